@@ -1,0 +1,190 @@
+/*
+ * skv.h -- C ABI of the ShadowKV sparse-KV decode step for AMD MI355X (gfx950).
+ *
+ * The method is the one described in "ShadowKV: KV Cache in Shadows for
+ * High-Throughput Long-Context LLM Inference":
+ *   - pre-fill (papercache deep notes, section A2, pre-fill algorithm; paper-graph-ui
+ *     summary, section 3.4 "Low-Rank Key Cache Compression via Online SVD" and
+ *     "Landmark Construction and Outlier Detection"): a rank-r SVD of the
+ *     pre-RoPE keys K ~ A x3 B with A shared by the KV heads, chunk-mean landmarks of
+ *     the post-RoPE keys, the O chunks with the lowest in-chunk minimum cosine to
+ *     their landmark kept exactly as a static outlier cache;
+ *   - decode (papercache deep notes, section A2, decode algorithm; paper-graph-ui
+ *     summary, section 3.4 "Decoding-Time KV Selection" and "Sparse KV
+ *     Reconstruction and Overlapping Strategy"): softmax(Q L^T / sqrt(d)) per query
+ *     head, maximum over each GQA group, top-K chunks per KV head, an index scan
+ *     against the previous step's chunks so only misses are rebuilt
+ *     (RoPE(Gather(A, I_miss) B)) and fetched, then exact attention over
+ *     [outliers; selected chunks; local window].
+ *
+ * Conventions shared by every entry point
+ *   - Every call returns an skv_status; SKV_OK is 0.  No C++ exception crosses
+ *     the ABI.  Arguments are validated before anything is enqueued; a call that
+ *     fails validation leaves the handle unchanged.  A HIP failure inside a call
+ *     poisons the handle: later calls on it return SKV_ERR_STATE until
+ *     skv_destroy.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major, with the
+ *     layouts given per argument.  "device" pointers are HIP device memory on the
+ *     current device; "pinned host" pointers come from hipHostMalloc.
+ *   - Query head hq uses KV head hq / G with G = n_q_heads / n_kv_heads.
+ *   - Streams are passed as void* holding a hipStream_t (NULL = default stream).
+ *   - A handle (one model layer) is not thread-safe; distinct handles are
+ *     independent.
+ */
+#ifndef SKV_H
+#define SKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKV_ABI_VERSION 1
+
+typedef int32_t skv_status;
+#define SKV_OK 0
+#define SKV_ERR_INVALID_ARG 1  /* null pointer, bad enum value, wrong pointer kind */
+#define SKV_ERR_SHAPE 2        /* sizes that violate the method's constraints     */
+#define SKV_ERR_UNSUPPORTED 3  /* valid for the method, not implemented here      */
+#define SKV_ERR_OOM 4          /* device or host allocation failed                */
+#define SKV_ERR_HIP 5          /* a HIP runtime call failed                       */
+#define SKV_ERR_STATE 6        /* handle poisoned by an earlier HIP failure       */
+#define SKV_ERR_INTERNAL 7     /* internal invariant broken (e.g. no convergence)  */
+
+/* Value placement (the value store V_CPU of the pages). */
+#define SKV_VALUES_DEVICE 0    /* values stay in HBM and are read by chunk id      */
+#define SKV_VALUES_HOST 1      /* values in pinned host memory, missed chunks are
+                                  gathered over PCIe on a side stream that overlaps
+                                  the key rebuild                                   */
+
+/*
+ * Shape and budget of one layer.
+ *   head_dim must be 128.  seq_len % chunk == 0, chunk in {4, 8, 16},
+ *   window % chunk == 0, G in {1, 2, 4, 8, 16}, rank % 16 == 0,
+ *   1 <= rank <= min(seq_len, n_kv_heads * head_dim), n_kv_heads * head_dim <= 2048,
+ *   n_cand = seq_len/chunk - n_outlier - window/chunk, 1 <= top_k <= n_cand, top_k <= 4096.
+ */
+typedef struct skv_config {
+  int32_t batch;           /* b                                                   */
+  int32_t n_q_heads;       /* H_q                                                 */
+  int32_t n_kv_heads;      /* H_kv                                                */
+  int32_t head_dim;        /* d (128)                                             */
+  int64_t seq_len;         /* S: context tokens held by the cache                 */
+  int32_t rank;            /* r: SVD rank of the pre-RoPE keys                    */
+  int32_t chunk;           /* C: tokens per chunk / landmark                      */
+  int32_t top_k;           /* K: chunks selected per KV head and step             */
+  int32_t n_outlier;       /* O: outlier chunks per KV head                       */
+  int32_t window;          /* W: last W context tokens kept exact (local window)  */
+  int32_t value_placement; /* SKV_VALUES_DEVICE or SKV_VALUES_HOST                */
+  double rope_theta;       /* RoPE base (rotate-half pairing (i, i + d/2))        */
+  int32_t temporal_cache;  /* 1: rebuild/fetch only chunks missed vs the previous
+                              step; 0: rebuild every selected chunk every step     */
+  int32_t reserved;        /* must be 0                                           */
+} skv_config;
+
+typedef struct skv_layer skv_layer;   /* opaque; owns all derived state */
+
+/* Temporal-cache counters (summed over the b * n_kv_heads pairs). */
+typedef struct skv_stats {
+  int64_t steps;          /* decode steps since build or the last reset             */
+  int64_t last_hits;      /* |I_t & I_{t-1}| of the last step                       */
+  int64_t last_misses;    /* chunks rebuilt (and, for host values, fetched) last step */
+  int64_t total_hits;     /* hits over steps 1.. since build/reset                  */
+  int64_t total_misses;   /* misses over steps 1.. since build/reset                */
+  double last_alpha;      /* last_hits / (pairs * top_k); 0 for the first step      */
+  double mean_alpha;      /* total_hits / (pairs * top_k * (steps - 1))             */
+  int64_t last_host_bytes;/* value bytes gathered from pinned host memory last step */
+} skv_stats;
+
+/*
+ * Host copies of the built state, for inspection and parity checks.  Any
+ * pointer may be NULL to skip that tensor.  Sizes (elements):
+ *   A          bf16 [b][S][r]
+ *   B          bf16 [b][H_kv][r][d]       (the per-head right factor)
+ *   landmarks  bf16 [b][H_kv][n_cand][d]  (candidate chunks, ascending chunk id)
+ *   cand_ids   int32 [b][H_kv][n_cand]    (chunk id of each landmark row)
+ *   outlier_ids int32 [b][H_kv][O]        (ascending)
+ *   k_outlier, v_outlier bf16 [b][H_kv][O*C][d]   (post-RoPE keys, values)
+ *   k_window,  v_window  bf16 [b][H_kv][W][d]
+ *   min_cos    float [b][H_kv][S/C]       (in-chunk minimum cosine, every chunk)
+ *   eigvals    double [b][r]              (largest eigenvalues of K_b^T K_b, i.e.
+ *                                          squared singular values, descending)
+ */
+typedef struct skv_state_host {
+  uint16_t* A;
+  uint16_t* B;
+  uint16_t* landmarks;
+  int32_t* cand_ids;
+  int32_t* outlier_ids;
+  uint16_t* k_outlier;
+  uint16_t* v_outlier;
+  uint16_t* k_window;
+  uint16_t* v_window;
+  float* min_cos;
+  double* eigvals;
+} skv_state_host;
+
+/*
+ * skv_build -- pre-fill of one layer (pre-fill algorithm of the papercache notes,
+ * section A2; paper-graph-ui summary, section 3.4).
+ *   k_pre : device, bf16 [b][S][H_kv*d]; row t holds the pre-RoPE keys of token
+ *           position t, heads concatenated.  Only read during the call.
+ *   v     : bf16 [b][H_kv][S][d]; device memory for SKV_VALUES_DEVICE, pinned host
+ *           memory for SKV_VALUES_HOST.  BORROWED: it must stay valid and unchanged
+ *           until skv_destroy (the value store is never copied whole).
+ *   stream: work is enqueued there; the call returns after it has completed
+ *           (host-synchronous).
+ *   out   : receives the new handle; untouched on failure.
+ * Computes post-RoPE keys (angles in float64), landmarks, per-chunk min-cosine,
+ * outliers among the non-window chunks (lowest min-cos, lower id on ties), the
+ * exact outlier and window K/V, and the rank-r factors from the top-r
+ * eigenvectors of K_b^T K_b (fp64 Gram on the GPU, subspace iteration with
+ * Rayleigh-Ritz in fp64), with each right singular vector's largest-magnitude
+ * entry made positive.  Stored state is bf16 (round-to-nearest-even).
+ * Errors: INVALID_ARG, SHAPE, UNSUPPORTED, OOM, HIP, INTERNAL (eigensolver did
+ * not converge).
+ */
+skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_t* v,
+                     void* stream, skv_layer** out);
+
+/*
+ * skv_decode_step -- one decode step of one layer (decode algorithm of the
+ * papercache notes, section A2; paper-graph-ui summary, section 3.4).
+ *   q         : device, bf16 [b][H_q][d], post-RoPE queries of one new token.
+ *   out       : device, float [b][H_q][d], attention output.
+ *   chunk_ids : device, int32 [b][H_kv][K]: the selected chunk ids, ascending.
+ *   stream    : every kernel is enqueued on it (plus an internal side stream
+ *               joined back into it for host values); no host synchronisation,
+ *               so the call can be captured in a HIP graph.  Outputs are valid
+ *               once the stream has completed.
+ * Selection uses fp32 scores; a chunk's score is max_g(logit_g/sqrt(d) - LSE_g),
+ * the log of the pages' max over the group of softmax probabilities; ties go to
+ * the lower chunk id.
+ * Errors: INVALID_ARG, STATE, HIP.
+ */
+skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t* chunk_ids,
+                           void* stream);
+
+/* Temporal-cache counters; synchronises with the last stream used. */
+skv_status skv_get_stats(const skv_layer* h, skv_stats* stats);
+
+/* Forget the previous selection: the next step rebuilds every selected chunk. */
+skv_status skv_reset_temporal_cache(skv_layer* h);
+
+/* Synchronous copy of the built state into caller-owned host buffers. */
+skv_status skv_export_state(const skv_layer* h, const skv_state_host* dst);
+
+/* Release everything the handle owns (never the borrowed value store). NULL is ok. */
+void skv_destroy(skv_layer* h);
+
+/* Static description of a status code. */
+const char* skv_status_string(skv_status s);
+
+/* SKV_ABI_VERSION of the loaded library. */
+int32_t skv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SKV_H */

@@ -1,0 +1,407 @@
+// Pre-fill (build) kernels for gfx950: post-RoPE keys, chunk-mean landmarks and
+// in-chunk minimum cosine, outlier choice, candidate compaction, exact outlier /
+// window caches, fp64 Gram matrices, fp64 products for the subspace iteration
+// and the projection A = K Psi.  The method's pre-fill is described in
+// "ShadowKV ..." (papercache deep notes, section A2, pre-fill algorithm; the
+// paper-graph-ui summary, section 3.4, "Landmark Construction and Outlier
+// Detection" and "Low-Rank Key Cache Compression via Online SVD").
+#include "skv_internal.h"
+#include "skv_select.h"
+
+namespace skv {
+
+// ---------------------------------------------------------------------------
+// RoPE + landmark + min-cos: one wave per (b, h, chunk); lane l holds dims l, l+64
+// (the rotate-half pair).  Landmark = mean of the C rotated keys (fp32), stored
+// bf16; min-cos uses the fp32 mean.
+
+template <int C>
+__global__ __launch_bounds__(256) void rope_landmark_kernel(const uint16_t* __restrict__ k_pre,
+                                                            int64_t S, int H, int n_c,
+                                                            const double* __restrict__ inv_freq,
+                                                            uint16_t* __restrict__ L_full,
+                                                            float* __restrict__ min_cos) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (j >= n_c) return;
+  const double f = inv_freq[lane];
+  float y1[C], y2[C];
+  float m1 = 0.f, m2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < C; i++) {
+    const int64_t pos = (int64_t)j * C + i;
+    const uint16_t* row = k_pre + ((int64_t)b * S + pos) * (int64_t)(H * kHeadDim) + h * kHeadDim;
+    const float x1 = bf16_to_f32(row[lane]), x2 = bf16_to_f32(row[lane + 64]);
+    float c, s;
+    rope_cs(pos, f, &c, &s);
+    y1[i] = x1 * c - x2 * s;
+    y2[i] = x2 * c + x1 * s;
+    m1 += y1[i];
+    m2 += y2[i];
+  }
+  m1 *= 1.0f / C;
+  m2 *= 1.0f / C;
+  const float mm = wave_sum(m1 * m1 + m2 * m2);
+  float mc = 3.0f;
+#pragma unroll
+  for (int i = 0; i < C; i++) {
+    const float dot = wave_sum(y1[i] * m1 + y2[i] * m2);
+    const float kk = wave_sum(y1[i] * y1[i] + y2[i] * y2[i]);
+    const float cs = dot / fmaxf(sqrtf(kk) * sqrtf(mm), 1e-8f);
+    mc = fminf(mc, cs);
+  }
+  const int64_t pr = (int64_t)b * H + h;
+  uint16_t* lrow = L_full + (pr * n_c + j) * kHeadDim;
+  lrow[lane] = f32_to_bf16(m1);
+  lrow[lane + 64] = f32_to_bf16(m2);
+  if (lane == 0) min_cos[pr * n_c + j] = mc;
+}
+
+hipError_t launch_rope_landmark(const uint16_t* k_pre, int b, int64_t S, int H, int C,
+                                const double* inv_freq, uint16_t* L_full, float* min_cos,
+                                hipStream_t st) {
+  const int n_c = (int)(S / C);
+  dim3 grid((n_c + 3) / 4, H, b);
+  switch (C) {
+    case 4: rope_landmark_kernel<4><<<grid, 256, 0, st>>>(k_pre, S, H, n_c, inv_freq, L_full, min_cos); break;
+    case 8: rope_landmark_kernel<8><<<grid, 256, 0, st>>>(k_pre, S, H, n_c, inv_freq, L_full, min_cos); break;
+    case 16: rope_landmark_kernel<16><<<grid, 256, 0, st>>>(k_pre, S, H, n_c, inv_freq, L_full, min_cos); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Outliers: per pair, the O eligible chunks with the lowest min-cos (lower id on
+// ties), ascending.  Key = order-preserving bits of -min_cos.
+
+__global__ __launch_bounds__(256) void outlier_kernel(const float* __restrict__ min_cos, int n_c,
+                                                      int n_elig, int O, uint32_t* __restrict__ keys,
+                                                      int32_t* __restrict__ outlier_ids) {
+  __shared__ int hist[2048];
+  __shared__ int sh[16];
+  const int p = blockIdx.x;
+  const float* mc = min_cos + (int64_t)p * n_c;
+  uint32_t* kp = keys + (int64_t)p * n_c;
+  for (int i = threadIdx.x; i < n_elig; i += 256) kp[i] = float_key(-mc[i]);
+  __syncthreads();
+  int32_t* out = outlier_ids + (int64_t)p * O;
+  block_topk<256>([&](int i) { return kp[i]; }, n_elig, O, hist, sh,
+                  [&](int pos, int i) { if (pos < O) out[pos] = i; });
+}
+
+hipError_t launch_outliers(const float* min_cos, int P, int n_c, int n_elig, int O,
+                           uint32_t* key_scratch, int32_t* outlier_ids, hipStream_t st) {
+  if (O == 0) return hipSuccess;
+  outlier_kernel<<<P, 256, 0, st>>>(min_cos, n_c, n_elig, O, key_scratch, outlier_ids);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Candidates: every eligible chunk that is not an outlier, in ascending order;
+// landmarks are compacted to those rows.  One wave per chunk.
+
+__global__ __launch_bounds__(256) void candidates_kernel(const uint16_t* __restrict__ L_full,
+                                                         const int32_t* __restrict__ outlier_ids,
+                                                         int n_c, int n_elig, int O,
+                                                         uint16_t* __restrict__ L,
+                                                         int32_t* __restrict__ cand_map) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int p = blockIdx.y;
+  if (j >= n_elig) return;
+  const int32_t* oid = outlier_ids + (int64_t)p * O;
+  // number of outliers below j (binary search over the ascending list)
+  int lo = 0, hi = O;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (oid[mid] < j) lo = mid + 1; else hi = mid;
+  }
+  if (lo < O && oid[lo] == j) return;
+  const int ci = j - lo;
+  const int n_cand = n_elig - O;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(L_full + ((int64_t)p * n_c + j) * kHeadDim);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(L + ((int64_t)p * n_cand + ci) * kHeadDim);
+  dst[lane] = src[lane];
+  if (lane == 0) cand_map[(int64_t)p * n_cand + ci] = j;
+}
+
+hipError_t launch_candidates(const uint16_t* L_full, const int32_t* outlier_ids, int P, int n_c,
+                             int n_elig, int O, uint16_t* L, int32_t* cand_map, hipStream_t st) {
+  dim3 grid((n_elig + 3) / 4, P);
+  candidates_kernel<<<grid, 256, 0, st>>>(L_full, outlier_ids, n_c, n_elig, O, L, cand_map);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Exact static caches: post-RoPE keys and values of the outlier chunks and of the
+// last W tokens.  One wave per (pair, token); `v` may be a mapped host pointer.
+
+__global__ __launch_bounds__(256) void static_gather_kernel(
+    const uint16_t* __restrict__ k_pre, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ outlier_ids, int64_t S, int H, int C, int O, int W,
+    const double* __restrict__ inv_freq, uint16_t* __restrict__ k_out, uint16_t* __restrict__ v_out,
+    uint16_t* __restrict__ k_win, uint16_t* __restrict__ v_win) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int p = blockIdx.y;
+  const int b = p / H, h = p % H;
+  const int n_tok = O * C + W;
+  if (t >= n_tok) return;
+  int64_t pos;
+  uint16_t *kd, *vd;
+  if (t < O * C) {
+    pos = (int64_t)outlier_ids[(int64_t)p * O + t / C] * C + (t % C);
+    kd = k_out + ((int64_t)p * O * C + t) * kHeadDim;
+    vd = v_out + ((int64_t)p * O * C + t) * kHeadDim;
+  } else {
+    const int w = t - O * C;
+    pos = S - W + w;
+    kd = k_win + ((int64_t)p * W + w) * kHeadDim;
+    vd = v_win + ((int64_t)p * W + w) * kHeadDim;
+  }
+  const uint16_t* row = k_pre + ((int64_t)b * S + pos) * (int64_t)(H * kHeadDim) + h * kHeadDim;
+  const float x1 = bf16_to_f32(row[lane]), x2 = bf16_to_f32(row[lane + 64]);
+  float c, s;
+  rope_cs(pos, inv_freq[lane], &c, &s);
+  kd[lane] = f32_to_bf16(x1 * c - x2 * s);
+  kd[lane + 64] = f32_to_bf16(x2 * c + x1 * s);
+  const uint32_t* vs = reinterpret_cast<const uint32_t*>(v + (((int64_t)b * H + h) * S + pos) * kHeadDim);
+  reinterpret_cast<uint32_t*>(vd)[lane] = vs[lane];
+}
+
+hipError_t launch_static_gather(const uint16_t* k_pre, const uint16_t* v, const int32_t* outlier_ids,
+                                int b, int64_t S, int H, int C, int O, int W, const double* inv_freq,
+                                uint16_t* k_out, uint16_t* v_out, uint16_t* k_win, uint16_t* v_win,
+                                hipStream_t st) {
+  const int n_tok = O * C + W;
+  if (n_tok == 0) return hipSuccess;
+  dim3 grid((n_tok + 3) / 4, b * H);
+  static_gather_kernel<<<grid, 256, 0, st>>>(k_pre, v, outlier_ids, S, H, C, O, W, inv_freq, k_out,
+                                             v_out, k_win, v_win);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Gram matrices G_b = K_b^T K_b in fp64 (bf16 products are exact; sums in fp64).
+// Upper-triangle 64x64 tiles, rows of K split into `nseg` segments whose partial
+// Grams are added in a fixed order afterwards (deterministic).
+
+constexpr int GT = 64, GK = 32;
+
+__global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ k_pre, int64_t S,
+                                                   int HD, int nseg, double* __restrict__ partial) {
+  __shared__ float ti[GK][GT + 4];
+  __shared__ float tj[GK][GT + 4];
+  const int nt = HD / GT;
+  int t = blockIdx.x, a = 0;
+  while (t >= nt - a) { t -= nt - a; a++; }
+  const int i0 = a * GT, j0 = (a + t) * GT;
+  const int seg = blockIdx.y, b = blockIdx.z;
+  const int64_t seg_len = (S + nseg - 1) / nseg;
+  const int64_t s0 = seg * seg_len, s1 = min(S, s0 + seg_len);
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  double acc[4][4] = {};
+  const uint16_t* kb = k_pre + (int64_t)b * S * HD;
+  for (int64_t s = s0; s < s1; s += GK) {
+    // load 32 rows x 64 cols for both column blocks (256 threads x 8 elements each)
+    for (int e = threadIdx.x; e < GK * GT / 8; e += 256) {
+      const int r = e / (GT / 8), c8 = (e % (GT / 8)) * 8;
+      const int64_t row = s + r;
+      u32x4 wi = {0, 0, 0, 0}, wj = {0, 0, 0, 0};
+      if (row < s1) {
+        wi = *reinterpret_cast<const u32x4*>(kb + row * HD + i0 + c8);
+        wj = *reinterpret_cast<const u32x4*>(kb + row * HD + j0 + c8);
+      }
+      float xi[8], xj[8];
+      unpack8(wi, xi);
+      unpack8(wj, xj);
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        ti[r][c8 + q] = xi[q];
+        tj[r][c8 + q] = xj[q];
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int r = 0; r < GK; r++) {
+      double x[4], y[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        x[q] = ti[r][ty * 4 + q];
+        y[q] = tj[r][tx * 4 + q];
+      }
+#pragma unroll
+      for (int p = 0; p < 4; p++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) acc[p][q] = fma(x[p], y[q], acc[p][q]);
+    }
+    __syncthreads();
+  }
+  double* out = partial + ((int64_t)b * nseg + seg) * HD * HD;
+#pragma unroll
+  for (int p = 0; p < 4; p++)
+#pragma unroll
+    for (int q = 0; q < 4; q++) out[(int64_t)(i0 + ty * 4 + p) * HD + j0 + tx * 4 + q] = acc[p][q];
+}
+
+// Sum the segments in order and mirror the upper triangle.
+__global__ void gram_reduce_kernel(const double* __restrict__ partial, int HD, int nseg,
+                                   double* __restrict__ gram) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (idx >= (int64_t)HD * HD) return;
+  const int i = (int)(idx / HD), j = (int)(idx % HD);
+  const int ti = i / GT, tj = j / GT;
+  const int64_t src = ti <= tj ? idx : (int64_t)j * HD + i;
+  double s = 0.0;
+  for (int g = 0; g < nseg; g++) s += partial[((int64_t)b * nseg + g) * HD * HD + src];
+  gram[(int64_t)b * HD * HD + idx] = s;
+}
+
+int gram_segments(int b, int64_t S, int HD) {
+  const int nt = HD / GT;
+  const int tiles = nt * (nt + 1) / 2 * b;
+  int nseg = (2048 + tiles - 1) / tiles;
+  const int64_t max_seg = (S + 255) / 256;
+  if (nseg > max_seg) nseg = (int)max_seg;
+  if (nseg < 1) nseg = 1;
+  if (nseg > 64) nseg = 64;
+  return nseg;
+}
+
+hipError_t launch_gram(const uint16_t* k_pre, int b, int64_t S, int HD, int nseg, double* partial,
+                       double* gram, hipStream_t st) {
+  const int nt = HD / GT;
+  dim3 grid(nt * (nt + 1) / 2, nseg, b);
+  gram_kernel<<<grid, 256, 0, st>>>(k_pre, S, HD, nseg, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2((unsigned)(((int64_t)HD * HD + 255) / 256), b);
+  gram_reduce_kernel<<<g2, 256, 0, st>>>(partial, HD, nseg, gram);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Batched fp64 C[bi] = A[bi] (M x K) * B[bi] (K x N), all row-major.
+
+__global__ __launch_bounds__(256) void gemm_f64_kernel(const double* __restrict__ A,
+                                                       const double* __restrict__ B,
+                                                       double* __restrict__ C, int M, int N, int K) {
+  __shared__ double ta[16][64 + 1];
+  __shared__ double tb[16][64 + 1];
+  const int bi = blockIdx.z;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  A += (int64_t)bi * M * K;
+  B += (int64_t)bi * K * N;
+  C += (int64_t)bi * M * N;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      const int kk = e / 64, mm = e % 64;
+      const int gm = m0 + mm, gk = k0 + kk, gn = n0 + mm;
+      ta[kk][mm] = (gm < M && gk < K) ? A[(int64_t)gm * K + gk] : 0.0;
+      tb[kk][mm] = (gk < K && gn < N) ? B[(int64_t)gk * N + gn] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; kk++) {
+      double x[4], y[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        x[q] = ta[kk][ty * 4 + q];
+        y[q] = tb[kk][tx * 4 + q];
+      }
+#pragma unroll
+      for (int p = 0; p < 4; p++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) acc[p][q] = fma(x[p], y[q], acc[p][q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int p = 0; p < 4; p++)
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int gm = m0 + ty * 4 + p, gn = n0 + tx * 4 + q;
+      if (gm < M && gn < N) C[(int64_t)gm * N + gn] = acc[p][q];
+    }
+}
+
+hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batch, int M, int N,
+                           int K, hipStream_t st) {
+  dim3 grid((N + 63) / 64, (M + 63) / 64, batch);
+  gemm_f64_kernel<<<grid, 256, 0, st>>>(A, B, C, M, N, K);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Projection A[b] = K_b Psi_b (S x HD times HD x r), fp32 accumulation, bf16 out.
+
+__global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict__ k_pre,
+                                                      const float* __restrict__ psi, int64_t S,
+                                                      int HD, int r, uint16_t* __restrict__ A) {
+  __shared__ float tk[32][64 + 1];   // [k][row]
+  __shared__ float tp[32][64 + 1];   // [k][col]
+  const int b = blockIdx.z;
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  const int n0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const uint16_t* kb = k_pre + (int64_t)b * S * HD;
+  const float* pb = psi + (int64_t)b * HD * r;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < HD; k0 += 32) {
+    // K tile: 64 rows x 32 k (8 elements per thread)
+    {
+      const int e = threadIdx.x;               // 256 = 64 rows x 4 groups of 8
+      const int rr = e >> 2, c8 = (e & 3) * 8;
+      const int64_t row = m0 + rr;
+      u32x4 w = {0, 0, 0, 0};
+      if (row < S) w = *reinterpret_cast<const u32x4*>(kb + row * HD + k0 + c8);
+      float x[8];
+      unpack8(w, x);
+#pragma unroll
+      for (int q = 0; q < 8; q++) tk[c8 + q][rr] = x[q];
+    }
+    for (int e = threadIdx.x; e < 32 * 64; e += 256) {
+      const int kk = e / 64, cc = e % 64;
+      tp[kk][cc] = (n0 + cc < r) ? pb[(int64_t)(k0 + kk) * r + n0 + cc] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; kk++) {
+      float x[4], y[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        x[q] = tk[kk][ty * 4 + q];
+        y[q] = tp[kk][tx * 4 + q];
+      }
+#pragma unroll
+      for (int p = 0; p < 4; p++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) acc[p][q] = fmaf(x[p], y[q], acc[p][q]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int p = 0; p < 4; p++) {
+    const int64_t row = m0 + ty * 4 + p;
+    if (row >= S) continue;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int col = n0 + tx * 4 + q;
+      if (col < r) A[((int64_t)b * S + row) * r + col] = f32_to_bf16(acc[p][q]);
+    }
+  }
+}
+
+hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_t S, int HD, int r,
+                          uint16_t* A, hipStream_t st) {
+  dim3 grid((unsigned)((S + 63) / 64), (r + 63) / 64, b);
+  project_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, A);
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -1,0 +1,530 @@
+// C ABI of the skv library: argument validation, handle lifecycle, the build
+// sequence (pre-fill) and the stream-ordered decode step.  No host
+// synchronisation inside skv_decode_step; the build is host-synchronous.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "skv_internal.h"
+
+using namespace skv;
+
+struct skv_layer {
+  skv_config cfg;
+  int G = 0, n_c = 0, n_win = 0, n_cand = 0, P = 0, HD = 0, U = 0;
+  int nb_score = 0, cpb = 0, n_split = 0, upw = 0, res_words = 0;
+  bool poisoned = false;
+  bool need_reset = false;
+  const uint16_t* v_dev = nullptr;   // device-visible address of the value store
+  void* pool = nullptr;
+  // carved from pool
+  uint16_t *A = nullptr, *Bt = nullptr, *L = nullptr, *k_out = nullptr, *v_out = nullptr,
+           *k_win = nullptr, *v_win = nullptr, *key_slots = nullptr, *val_slots = nullptr;
+  int32_t *cand_map = nullptr, *outlier_ids = nullptr, *slot_cand = nullptr, *slot_chunk = nullptr,
+          *miss_slot = nullptr, *miss_chunk = nullptr, *miss_cand = nullptr, *free_slot = nullptr,
+          *n_miss = nullptr, *hits_last = nullptr, *cnt_score = nullptr, *cnt_attn = nullptr;
+  uint32_t *resident = nullptr, *keys = nullptr;
+  long long *hits_total = nullptr, *miss_total = nullptr;
+  float *logits = nullptr, *lse_part = nullptr, *attn_part = nullptr, *min_cos = nullptr;
+  double* inv_freq = nullptr;
+  std::vector<double> eig;
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  hipStream_t last_stream = nullptr;
+  int64_t steps = 0;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+struct Carver {
+  size_t off = 0;
+  template <class T>
+  size_t take(size_t count) {
+    size_t o = (off + kAlign - 1) / kAlign * kAlign;
+    off = o + std::max<size_t>(count * sizeof(T), 1);
+    return o;
+  }
+};
+
+skv_status validate(const skv_config* c) {
+  if (!c) return SKV_ERR_INVALID_ARG;
+  if (c->reserved != 0) return SKV_ERR_INVALID_ARG;
+  if (c->value_placement != SKV_VALUES_DEVICE && c->value_placement != SKV_VALUES_HOST)
+    return SKV_ERR_INVALID_ARG;
+  if (c->temporal_cache != 0 && c->temporal_cache != 1) return SKV_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->seq_len < 1) return SKV_ERR_SHAPE;
+  if (c->head_dim != kHeadDim) return SKV_ERR_UNSUPPORTED;
+  if (c->n_q_heads % c->n_kv_heads != 0) return SKV_ERR_SHAPE;
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return SKV_ERR_UNSUPPORTED;
+  if (c->chunk != 4 && c->chunk != 8 && c->chunk != 16) return SKV_ERR_UNSUPPORTED;
+  if (c->seq_len % c->chunk != 0) return SKV_ERR_SHAPE;
+  if (c->seq_len / c->chunk > (int64_t)INT32_MAX / 64) return SKV_ERR_UNSUPPORTED;
+  if (c->window < 0 || c->window % c->chunk != 0 || c->window >= c->seq_len) return SKV_ERR_SHAPE;
+  if (c->n_outlier < 0) return SKV_ERR_SHAPE;
+  const int64_t n_c = c->seq_len / c->chunk;
+  const int64_t n_cand = n_c - c->n_outlier - c->window / c->chunk;
+  if (n_cand < 1) return SKV_ERR_SHAPE;
+  if (c->top_k < 1 || c->top_k > n_cand) return SKV_ERR_SHAPE;
+  if (c->top_k > kMaxTopK) return SKV_ERR_UNSUPPORTED;
+  const int64_t HD = (int64_t)c->n_kv_heads * c->head_dim;
+  if (HD > 2048) return SKV_ERR_UNSUPPORTED;
+  if (c->rank < 1 || c->rank > std::min<int64_t>(c->seq_len, HD)) return SKV_ERR_SHAPE;
+  if (c->rank % 16 != 0) return SKV_ERR_UNSUPPORTED;
+  if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta)) return SKV_ERR_SHAPE;
+  return SKV_OK;
+}
+
+// float64 -> bfloat16 bits, round to nearest even at the 8th significant bit.
+uint16_t f64_to_bf16(double x) {
+  uint64_t u;
+  std::memcpy(&u, &x, 8);
+  const uint64_t lsb = (u >> 45) & 1ull;
+  u += (1ull << 44) - 1ull + lsb;
+  u &= ~((1ull << 45) - 1ull);
+  double y;
+  std::memcpy(&y, &u, 8);
+  const float f = (float)y;   // exact: y has 8 significant bits
+  uint32_t b;
+  std::memcpy(&b, &f, 4);
+  return (uint16_t)(b >> 16);
+}
+
+bool is_device_ptr(const void* p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return at.type == hipMemoryTypeDevice;
+}
+
+const void* host_device_ptr(const void* p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (at.type != hipMemoryTypeHost) return nullptr;
+  void* dp = nullptr;
+  if (hipHostGetDevicePointer(&dp, const_cast<void*>(p), 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return dp;
+}
+
+void release(skv_layer* h) {
+  if (!h) return;
+  if (h->pool) (void)hipFree(h->pool);
+  if (h->side) (void)hipStreamDestroy(h->side);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  delete h;
+}
+
+DecodeArgs decode_args(skv_layer* h) {
+  const skv_config& c = h->cfg;
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.batch = c.batch;
+  a.n_kv = c.n_kv_heads;
+  a.group = h->G;
+  a.chunk = c.chunk;
+  a.top_k = c.top_k;
+  a.n_outlier = c.n_outlier;
+  a.n_win_units = h->n_win;
+  a.n_cand = h->n_cand;
+  a.seq_len = c.seq_len;
+  a.nb_score = h->nb_score;
+  a.cpb = h->cpb;
+  a.n_split = h->n_split;
+  a.upw = h->upw;
+  a.temporal = c.temporal_cache;
+  a.host_values = c.value_placement == SKV_VALUES_HOST;
+  a.scale = 1.0f / std::sqrt((float)c.head_dim);
+  a.inv_freq = h->inv_freq;
+  a.L = h->L;
+  a.cand_map = h->cand_map;
+  a.A = h->A;
+  a.Bt = h->Bt;
+  a.rank = c.rank;
+  a.k_out = h->k_out;
+  a.v_out = h->v_out;
+  a.k_win = h->k_win;
+  a.v_win = h->v_win;
+  a.v_store = h->v_dev;
+  a.key_slots = h->key_slots;
+  a.val_slots = h->val_slots;
+  a.slot_cand = h->slot_cand;
+  a.slot_chunk = h->slot_chunk;
+  a.resident = h->resident;
+  a.res_words = h->res_words;
+  a.miss_slot = h->miss_slot;
+  a.miss_chunk = h->miss_chunk;
+  a.miss_cand = h->miss_cand;
+  a.free_slot = h->free_slot;
+  a.n_miss = h->n_miss;
+  a.hits_last = h->hits_last;
+  a.hits_total = h->hits_total;
+  a.miss_total = h->miss_total;
+  a.logits = h->logits;
+  a.lse_part = h->lse_part;
+  a.keys = h->keys;
+  a.cnt_score = h->cnt_score;
+  a.cnt_attn = h->cnt_attn;
+  a.attn_part = h->attn_part;
+  return a;
+}
+
+#define HIP_TRY(expr)                  \
+  do {                                 \
+    hipError_t e_ = (expr);            \
+    if (e_ != hipSuccess) goto hip_fail; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t skv_abi_version(void) { return SKV_ABI_VERSION; }
+
+const char* skv_status_string(skv_status s) {
+  switch (s) {
+    case SKV_OK: return "ok";
+    case SKV_ERR_INVALID_ARG: return "invalid argument";
+    case SKV_ERR_SHAPE: return "shape violates the method's constraints";
+    case SKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SKV_ERR_OOM: return "out of memory";
+    case SKV_ERR_HIP: return "HIP runtime error";
+    case SKV_ERR_STATE: return "handle poisoned by an earlier HIP error";
+    case SKV_ERR_INTERNAL: return "internal error (eigensolver did not converge)";
+    default: return "unknown status";
+  }
+}
+
+skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_t* v, void* stream,
+                     skv_layer** out) {
+  skv_status st = validate(cfg);
+  if (st != SKV_OK) return st;
+  if (!k_pre || !v || !out) return SKV_ERR_INVALID_ARG;
+  if (!is_device_ptr(k_pre)) return SKV_ERR_INVALID_ARG;
+  const uint16_t* v_dev = nullptr;
+  if (cfg->value_placement == SKV_VALUES_DEVICE) {
+    if (!is_device_ptr(v)) return SKV_ERR_INVALID_ARG;
+    v_dev = v;
+  } else {
+    v_dev = static_cast<const uint16_t*>(host_device_ptr(v));
+    if (!v_dev) return SKV_ERR_INVALID_ARG;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  skv_layer* h = new (std::nothrow) skv_layer();
+  if (!h) return SKV_ERR_OOM;
+  h->cfg = *cfg;
+  const skv_config& c = *cfg;
+  const int b = c.batch, H = c.n_kv_heads, C = c.chunk, K = c.top_k, O = c.n_outlier, r = c.rank;
+  const int64_t S = c.seq_len;
+  h->G = c.n_q_heads / H;
+  h->n_c = (int)(S / C);
+  h->n_win = c.window / C;
+  h->n_cand = h->n_c - O - h->n_win;
+  h->P = b * H;
+  h->HD = H * kHeadDim;
+  h->U = O + K + h->n_win;
+  h->res_words = (h->n_cand + 31) / 32;
+  h->v_dev = v_dev;
+  const int P = h->P, G = h->G, n_c = h->n_c, n_cand = h->n_cand, HD = h->HD;
+  {
+    int nb = (2048 + P - 1) / P;
+    nb = std::max(1, std::min(nb, (n_cand + 63) / 64));
+    h->cpb = (n_cand + nb - 1) / nb;
+    h->nb_score = (n_cand + h->cpb - 1) / h->cpb;
+    int ns = (2048 + P - 1) / P;
+    ns = std::max(1, std::min(ns, h->U));
+    h->upw = (h->U + ns - 1) / ns;
+    h->n_split = (h->U + h->upw - 1) / h->upw;
+  }
+
+  // persistent state, one allocation
+  Carver cv;
+  const size_t oA = cv.take<uint16_t>((size_t)b * S * r);
+  const size_t oBt = cv.take<uint16_t>((size_t)b * HD * r);
+  const size_t oL = cv.take<uint16_t>((size_t)P * n_cand * kHeadDim);
+  const size_t oKo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
+  const size_t oVo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
+  const size_t oKw = cv.take<uint16_t>((size_t)P * c.window * kHeadDim);
+  const size_t oVw = cv.take<uint16_t>((size_t)P * c.window * kHeadDim);
+  const size_t oKs = cv.take<uint16_t>((size_t)P * K * C * kHeadDim);
+  const size_t oVs = cv.take<uint16_t>(c.value_placement == SKV_VALUES_HOST ? (size_t)P * K * C * kHeadDim : 0);
+  const size_t oCm = cv.take<int32_t>((size_t)P * n_cand);
+  const size_t oOi = cv.take<int32_t>((size_t)P * O);
+  const size_t oSc = cv.take<int32_t>((size_t)P * K);
+  const size_t oSch = cv.take<int32_t>((size_t)P * K);
+  const size_t oMs = cv.take<int32_t>((size_t)P * K);
+  const size_t oMch = cv.take<int32_t>((size_t)P * K);
+  const size_t oMca = cv.take<int32_t>((size_t)P * K);
+  const size_t oFs = cv.take<int32_t>((size_t)P * K);
+  const size_t oNm = cv.take<int32_t>(P);
+  const size_t oHl = cv.take<int32_t>(P);
+  const size_t oCs = cv.take<int32_t>(P);
+  const size_t oCa = cv.take<int32_t>(P);
+  const size_t oRes = cv.take<uint32_t>((size_t)P * h->res_words);
+  const size_t oKeys = cv.take<uint32_t>((size_t)P * n_c);
+  const size_t oHt = cv.take<long long>(P);
+  const size_t oMt = cv.take<long long>(P);
+  const size_t oLg = cv.take<float>((size_t)P * n_cand * G);
+  const size_t oLp = cv.take<float>((size_t)P * h->nb_score * G * 2);
+  const size_t oAp = cv.take<float>((size_t)P * h->n_split * G * (kHeadDim + 2));
+  const size_t oMc = cv.take<float>((size_t)P * n_c);
+  const size_t oIf = cv.take<double>(kHeadDim / 2);
+  const size_t pool_bytes = cv.off;
+
+  // build temporaries
+  const int nseg = gram_segments(b, S, HD);
+  uint16_t* L_full = nullptr;
+  double *gpart = nullptr, *gram = nullptr;
+  float* psi_f = nullptr;
+  std::vector<double> psi((size_t)b * HD * r);
+  std::vector<float> psi32((size_t)b * HD * r);
+  std::vector<uint16_t> bt16((size_t)b * HD * r);
+  std::vector<double> invf(kHeadDim / 2);
+  int rc;
+  hipError_t herr = hipSuccess;
+
+  if (hipMalloc(&h->pool, pool_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    h->pool = nullptr;
+    release(h);
+    return SKV_ERR_OOM;
+  }
+  if (hipMalloc(&L_full, (size_t)P * n_c * kHeadDim * 2) != hipSuccess ||
+      hipMalloc(&gpart, (size_t)b * nseg * HD * HD * 8) != hipSuccess ||
+      hipMalloc(&gram, (size_t)b * HD * HD * 8) != hipSuccess ||
+      hipMalloc(&psi_f, (size_t)b * HD * r * 4) != hipSuccess) {
+    (void)hipGetLastError();
+    if (L_full) (void)hipFree(L_full);
+    if (gpart) (void)hipFree(gpart);
+    if (gram) (void)hipFree(gram);
+    if (psi_f) (void)hipFree(psi_f);
+    release(h);
+    return SKV_ERR_OOM;
+  }
+  {
+    char* base = static_cast<char*>(h->pool);
+    h->A = (uint16_t*)(base + oA);
+    h->Bt = (uint16_t*)(base + oBt);
+    h->L = (uint16_t*)(base + oL);
+    h->k_out = (uint16_t*)(base + oKo);
+    h->v_out = (uint16_t*)(base + oVo);
+    h->k_win = (uint16_t*)(base + oKw);
+    h->v_win = (uint16_t*)(base + oVw);
+    h->key_slots = (uint16_t*)(base + oKs);
+    h->val_slots = c.value_placement == SKV_VALUES_HOST ? (uint16_t*)(base + oVs) : nullptr;
+    h->cand_map = (int32_t*)(base + oCm);
+    h->outlier_ids = (int32_t*)(base + oOi);
+    h->slot_cand = (int32_t*)(base + oSc);
+    h->slot_chunk = (int32_t*)(base + oSch);
+    h->miss_slot = (int32_t*)(base + oMs);
+    h->miss_chunk = (int32_t*)(base + oMch);
+    h->miss_cand = (int32_t*)(base + oMca);
+    h->free_slot = (int32_t*)(base + oFs);
+    h->n_miss = (int32_t*)(base + oNm);
+    h->hits_last = (int32_t*)(base + oHl);
+    h->cnt_score = (int32_t*)(base + oCs);
+    h->cnt_attn = (int32_t*)(base + oCa);
+    h->resident = (uint32_t*)(base + oRes);
+    h->keys = (uint32_t*)(base + oKeys);
+    h->hits_total = (long long*)(base + oHt);
+    h->miss_total = (long long*)(base + oMt);
+    h->logits = (float*)(base + oLg);
+    h->lse_part = (float*)(base + oLp);
+    h->attn_part = (float*)(base + oAp);
+    h->min_cos = (float*)(base + oMc);
+    h->inv_freq = (double*)(base + oIf);
+  }
+  for (int i = 0; i < kHeadDim / 2; i++) invf[i] = std::pow(c.rope_theta, -2.0 * i / kHeadDim);
+
+  HIP_TRY(hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
+  HIP_TRY(hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming));
+  HIP_TRY(hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming));
+  HIP_TRY(hipMemsetAsync(h->pool, 0, pool_bytes, s));
+  HIP_TRY(hipMemcpyAsync(h->inv_freq, invf.data(), invf.size() * 8, hipMemcpyHostToDevice, s));
+  // post-RoPE keys -> landmarks and min-cos; outliers; candidates; exact caches
+  HIP_TRY(launch_rope_landmark(k_pre, b, S, H, C, h->inv_freq, L_full, h->min_cos, s));
+  HIP_TRY(launch_outliers(h->min_cos, P, n_c, n_c - h->n_win, O, h->keys, h->outlier_ids, s));
+  HIP_TRY(launch_candidates(L_full, h->outlier_ids, P, n_c, n_c - h->n_win, O, h->L, h->cand_map, s));
+  HIP_TRY(launch_static_gather(k_pre, v_dev, h->outlier_ids, b, S, H, C, O, c.window, h->inv_freq,
+                               h->k_out, h->v_out, h->k_win, h->v_win, s));
+  // low-rank factors
+  HIP_TRY(launch_gram(k_pre, b, S, HD, nseg, gpart, gram, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  h->eig.resize((size_t)b * r);
+  rc = top_eigvecs(gram, b, HD, r, s, psi.data(), h->eig.data(), &herr);
+  if (rc == 2) goto hip_fail;
+  if (rc != 0) {
+    (void)hipFree(L_full);
+    (void)hipFree(gpart);
+    (void)hipFree(gram);
+    (void)hipFree(psi_f);
+    release(h);
+    return SKV_ERR_INTERNAL;
+  }
+  for (size_t i = 0; i < psi.size(); i++) {
+    psi32[i] = (float)psi[i];
+    bt16[i] = f64_to_bf16(psi[i]);
+  }
+  HIP_TRY(hipMemcpyAsync(psi_f, psi32.data(), psi32.size() * 4, hipMemcpyHostToDevice, s));
+  HIP_TRY(hipMemcpyAsync(h->Bt, bt16.data(), bt16.size() * 2, hipMemcpyHostToDevice, s));
+  HIP_TRY(launch_project(k_pre, psi_f, b, S, HD, r, h->A, s));
+  HIP_TRY(launch_reset_cache(decode_args(h), s));
+  HIP_TRY(hipStreamSynchronize(s));
+  (void)hipFree(L_full);
+  (void)hipFree(gpart);
+  (void)hipFree(gram);
+  (void)hipFree(psi_f);
+  h->last_stream = s;
+  *out = h;
+  return SKV_OK;
+
+hip_fail:
+  (void)hipGetLastError();
+  (void)hipStreamSynchronize(s);
+  (void)hipFree(L_full);
+  (void)hipFree(gpart);
+  (void)hipFree(gram);
+  (void)hipFree(psi_f);
+  release(h);
+  return SKV_ERR_HIP;
+}
+
+skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t* chunk_ids,
+                           void* stream) {
+  if (!h) return SKV_ERR_INVALID_ARG;
+  if (h->poisoned) return SKV_ERR_STATE;
+  if (!q || !out || !chunk_ids) return SKV_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeArgs a = decode_args(h);
+  a.q = q;
+  a.out = out;
+  a.chunk_ids = chunk_ids;
+  if (h->need_reset) {
+    HIP_TRY(launch_reset_cache(a, s));
+    h->need_reset = false;
+  }
+  HIP_TRY(launch_score_select(a, s));
+  if (a.host_values) {
+    HIP_TRY(hipEventRecord(h->ev_fork, s));
+    HIP_TRY(hipStreamWaitEvent(h->side, h->ev_fork, 0));
+    HIP_TRY(launch_value_gather(a, h->side));
+    HIP_TRY(hipEventRecord(h->ev_join, h->side));
+    HIP_TRY(launch_rebuild(a, s));
+    HIP_TRY(hipStreamWaitEvent(s, h->ev_join, 0));
+  } else {
+    HIP_TRY(launch_rebuild(a, s));
+  }
+  HIP_TRY(launch_attention(a, s));
+  h->steps++;
+  h->last_stream = s;
+  return SKV_OK;
+hip_fail:
+  (void)hipGetLastError();
+  h->poisoned = true;
+  return SKV_ERR_HIP;
+}
+
+skv_status skv_reset_temporal_cache(skv_layer* h) {
+  if (!h) return SKV_ERR_INVALID_ARG;
+  if (h->poisoned) return SKV_ERR_STATE;
+  h->need_reset = true;
+  h->steps = 0;
+  return SKV_OK;
+}
+
+skv_status skv_get_stats(const skv_layer* hc, skv_stats* out) {
+  if (!hc || !out) return SKV_ERR_INVALID_ARG;
+  skv_layer* h = const_cast<skv_layer*>(hc);
+  if (h->poisoned) return SKV_ERR_STATE;
+  std::memset(out, 0, sizeof(*out));
+  out->steps = h->steps;
+  if (h->need_reset) return SKV_OK;   // counters are cleared by the next step
+  const int P = h->P;
+  std::vector<int32_t> nm(P), hl(P);
+  std::vector<long long> ht(P), mt(P);
+  HIP_TRY(hipStreamSynchronize(h->last_stream));
+  HIP_TRY(hipStreamSynchronize(h->side));
+  HIP_TRY(hipMemcpy(nm.data(), h->n_miss, P * 4, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(hl.data(), h->hits_last, P * 4, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(ht.data(), h->hits_total, P * 8, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(mt.data(), h->miss_total, P * 8, hipMemcpyDeviceToHost));
+  if (h->steps > 0) {
+    for (int p = 0; p < P; p++) {
+      out->last_hits += hl[p];
+      out->last_misses += nm[p];
+      out->total_hits += ht[p];
+      out->total_misses += mt[p];
+    }
+    const double denom = (double)P * h->cfg.top_k;
+    out->last_alpha = h->steps > 1 ? out->last_hits / denom : 0.0;
+    out->mean_alpha = h->steps > 1 ? out->total_hits / (denom * (double)(h->steps - 1)) : 0.0;
+    if (h->cfg.value_placement == SKV_VALUES_HOST)
+      out->last_host_bytes = out->last_misses * (int64_t)h->cfg.chunk * kHeadDim * 2;
+  }
+  return SKV_OK;
+hip_fail:
+  (void)hipGetLastError();
+  h->poisoned = true;
+  return SKV_ERR_HIP;
+}
+
+skv_status skv_export_state(const skv_layer* hc, const skv_state_host* d) {
+  if (!hc || !d) return SKV_ERR_INVALID_ARG;
+  skv_layer* h = const_cast<skv_layer*>(hc);
+  if (h->poisoned) return SKV_ERR_STATE;
+  const skv_config& c = h->cfg;
+  const int b = c.batch, H = c.n_kv_heads, C = c.chunk, O = c.n_outlier, r = c.rank;
+  const int64_t S = c.seq_len;
+  const int P = h->P, HD = h->HD;
+  HIP_TRY(hipStreamSynchronize(h->last_stream));
+  if (d->A) HIP_TRY(hipMemcpy(d->A, h->A, (size_t)b * S * r * 2, hipMemcpyDeviceToHost));
+  if (d->B) {
+    std::vector<uint16_t> bt((size_t)b * HD * r);
+    HIP_TRY(hipMemcpy(bt.data(), h->Bt, bt.size() * 2, hipMemcpyDeviceToHost));
+    for (int bi = 0; bi < b; bi++)
+      for (int hh = 0; hh < H; hh++)
+        for (int k = 0; k < r; k++)
+          for (int dd = 0; dd < kHeadDim; dd++)
+            d->B[(((size_t)bi * H + hh) * r + k) * kHeadDim + dd] =
+                bt[((size_t)bi * HD + hh * kHeadDim + dd) * r + k];
+  }
+  if (d->landmarks) HIP_TRY(hipMemcpy(d->landmarks, h->L, (size_t)P * h->n_cand * kHeadDim * 2, hipMemcpyDeviceToHost));
+  if (d->cand_ids) HIP_TRY(hipMemcpy(d->cand_ids, h->cand_map, (size_t)P * h->n_cand * 4, hipMemcpyDeviceToHost));
+  if (d->outlier_ids && O) HIP_TRY(hipMemcpy(d->outlier_ids, h->outlier_ids, (size_t)P * O * 4, hipMemcpyDeviceToHost));
+  if (d->k_outlier && O) HIP_TRY(hipMemcpy(d->k_outlier, h->k_out, (size_t)P * O * C * kHeadDim * 2, hipMemcpyDeviceToHost));
+  if (d->v_outlier && O) HIP_TRY(hipMemcpy(d->v_outlier, h->v_out, (size_t)P * O * C * kHeadDim * 2, hipMemcpyDeviceToHost));
+  if (d->k_window && c.window) HIP_TRY(hipMemcpy(d->k_window, h->k_win, (size_t)P * c.window * kHeadDim * 2, hipMemcpyDeviceToHost));
+  if (d->v_window && c.window) HIP_TRY(hipMemcpy(d->v_window, h->v_win, (size_t)P * c.window * kHeadDim * 2, hipMemcpyDeviceToHost));
+  if (d->min_cos) HIP_TRY(hipMemcpy(d->min_cos, h->min_cos, (size_t)P * h->n_c * 4, hipMemcpyDeviceToHost));
+  if (d->eigvals) std::memcpy(d->eigvals, h->eig.data(), h->eig.size() * 8);
+  return SKV_OK;
+hip_fail:
+  (void)hipGetLastError();
+  h->poisoned = true;
+  return SKV_ERR_HIP;
+}
+
+void skv_destroy(skv_layer* h) {
+  if (!h) return;
+  (void)hipStreamSynchronize(h->last_stream);
+  if (h->side) (void)hipStreamSynchronize(h->side);
+  release(h);
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, RoPE angles,
+// wave64 cross-lane sums, order-preserving float keys, block scans.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bf16 bits, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Unpack 8 bf16 held in a 16-byte word into floats.
+__device__ __forceinline__ void unpack8(const u32x4 w, float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+
+// ---------------------------------------------------------------- RoPE
+
+// cos/sin of pos * inv_freq with the product and the reduction modulo 2*pi in
+// float64 (positions up to 2^20 lose nothing), sincos of the reduced angle in fp32.
+__device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq, float* c, float* s) {
+  const double two_pi_hi = 6.283185307179586;          // nearest double to 2*pi
+  const double two_pi_lo = 2.4492935982947064e-16;     // 2*pi - two_pi_hi
+  double a = (double)pos * inv_freq;
+  double n = rint(a * 0.15915494309189535);
+  double r = fma(-n, two_pi_hi, a);
+  r = fma(-n, two_pi_lo, r);
+  __sincosf((float)r, s, c);
+}
+
+// ---------------------------------------------------------------- cross-lane
+
+// DPP controls (gfx9 encoding).
+#define SKV_DPP_QP_XOR1 0xB1     // quad_perm [1,0,3,2]
+#define SKV_DPP_QP_XOR2 0x4E     // quad_perm [2,3,0,1]
+#define SKV_DPP_ROW_HALF_MIRROR 0x141
+#define SKV_DPP_ROW_MIRROR 0x140
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the total.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<SKV_DPP_QP_XOR1>(v);
+  v += dpp<SKV_DPP_QP_XOR2>(v);
+  v += dpp<SKV_DPP_ROW_HALF_MIRROR>(v);
+  v += dpp<SKV_DPP_ROW_MIRROR>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// ---------------------------------------------------------------- keys
+
+// Order-preserving map of a finite float to uint32 (larger float, larger key).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- block scan
+
+// Exclusive prefix sum over a block of NT threads (NT multiple of 64, <= 1024).
+// `tmp` needs NT/64 ints of LDS.  Returns the exclusive prefix, writes the total.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wid] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; w++) {
+    int t = tmp[w];
+    if (w < wid) base += t;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// Release/acquire helpers for the "last workgroup finishes" pattern.
+__device__ __forceinline__ int arrive_count(int* counter) {
+  __threadfence();
+  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace skv

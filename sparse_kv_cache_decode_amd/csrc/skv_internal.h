@@ -1,0 +1,98 @@
+// Internal declarations of the skv library: the layer handle and kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/skv.h"
+
+namespace skv {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxTopK = 4096;
+
+// Everything a decode step touches, by value into the kernels.
+struct DecodeArgs {
+  int batch, n_kv, group, chunk, top_k, n_outlier, n_win_units, n_cand;
+  int64_t seq_len;
+  int nb_score, cpb;          // score workgroups per pair, candidates per workgroup
+  int n_split, upw;           // attention workgroups per pair, units per workgroup
+  int temporal, host_values;
+  float scale;                // 1/sqrt(d)
+  const double* inv_freq;     // [64]
+  // inputs / state
+  const uint16_t* q;          // [b][Hq][d]
+  const uint16_t* L;          // [P][n_cand][d]
+  const int32_t* cand_map;    // [P][n_cand]
+  const uint16_t* A;          // [b][S][r]
+  const uint16_t* Bt;         // [b][Hkv*d][r]
+  int rank;
+  const uint16_t* k_out;      // [P][O*C][d]
+  const uint16_t* v_out;
+  const uint16_t* k_win;      // [P][W][d]
+  const uint16_t* v_win;
+  const uint16_t* v_store;    // [b][Hkv][S][d] (device pointer, may map host memory)
+  uint16_t* key_slots;        // [P][K][C][d]
+  uint16_t* val_slots;        // [P][K][C][d] (host placement only)
+  // temporal cache
+  int32_t* slot_cand;         // [P][K]
+  int32_t* slot_chunk;        // [P][K]
+  uint32_t* resident;         // [P][res_words] bitmap over candidate indices
+  int res_words;
+  int32_t* miss_slot;         // [P][K]
+  int32_t* miss_chunk;        // [P][K]
+  int32_t* miss_cand;         // [P][K]
+  int32_t* free_slot;         // [P][K]
+  int32_t* n_miss;            // [P]
+  int32_t* hits_last;         // [P]
+  long long* hits_total;      // [P]
+  long long* miss_total;      // [P]
+  // scratch
+  float* logits;              // [P][n_cand][G]
+  float* lse_part;            // [P][nb_score][G][2]
+  uint32_t* keys;             // [P][n_cand]
+  int32_t* cnt_score;         // [P]
+  int32_t* cnt_attn;          // [P]
+  float* attn_part;           // [P][n_split][G][d + 2]
+  // outputs
+  float* out;                 // [b][Hq][d]
+  int32_t* chunk_ids;         // [P][K]
+};
+
+// ---- build launchers (build_kernels.hip); all enqueue on `st`
+hipError_t launch_rope_landmark(const uint16_t* k_pre, int b, int64_t S, int H, int C,
+                                const double* inv_freq, uint16_t* L_full, float* min_cos,
+                                hipStream_t st);
+hipError_t launch_outliers(const float* min_cos, int P, int n_c, int n_elig, int O,
+                           uint32_t* key_scratch, int32_t* outlier_ids, hipStream_t st);
+hipError_t launch_candidates(const uint16_t* L_full, const int32_t* outlier_ids, int P, int n_c,
+                             int n_elig, int O, uint16_t* L, int32_t* cand_map, hipStream_t st);
+hipError_t launch_static_gather(const uint16_t* k_pre, const uint16_t* v, const int32_t* outlier_ids,
+                                int b, int64_t S, int H, int C, int O, int W, const double* inv_freq,
+                                uint16_t* k_out, uint16_t* v_out, uint16_t* k_win, uint16_t* v_win,
+                                hipStream_t st);
+hipError_t launch_gram(const uint16_t* k_pre, int b, int64_t S, int HD, int nseg, double* partial,
+                       double* gram, hipStream_t st);
+int gram_segments(int b, int64_t S, int HD);
+hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batch, int M, int N,
+                           int K, hipStream_t st);
+hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_t S, int HD, int r,
+                          uint16_t* A, hipStream_t st);
+
+// ---- decode launchers (decode_kernels.hip)
+hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_score_select(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);
+
+// ---- host eigensolver (eig_host.cpp)
+// Top-r eigenpairs of each symmetric n x n matrix gram[bi] (row-major fp64, on the
+// device), by block subspace iteration with Rayleigh-Ritz.  The products with the
+// Gram matrix run on the GPU (launch_gemm_f64); orthonormalisation and the small
+// eigenproblems run on the host in fp64.  psi receives [b][n][r] (columns =
+// eigenvectors, eigenvalues descending, largest-|.| entry positive), eig [b][r].
+// Returns 0 on success, 1 on non-convergence, 2 on a HIP error (err set).
+int top_eigvecs(const double* gram_dev, int b, int n, int r, hipStream_t st, double* psi,
+                double* eig, hipError_t* err);
+
+}  // namespace skv

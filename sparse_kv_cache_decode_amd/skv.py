@@ -1,0 +1,206 @@
+"""Thin ctypes binding of libskv.so (names as in include/skv.h).
+
+Argument marshalling only: torch tensors supply device / pinned-host pointers
+and streams; every step of the method runs in the library's HIP kernels.  The
+library is loaded on first use and its absence is an error (there is no
+fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so")
+_lib = None
+
+SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_SHAPE, SKV_ERR_UNSUPPORTED = 0, 1, 2, 3
+SKV_ERR_OOM, SKV_ERR_HIP, SKV_ERR_STATE, SKV_ERR_INTERNAL = 4, 5, 6, 7
+SKV_VALUES_DEVICE, SKV_VALUES_HOST = 0, 1
+
+EXPORTED = ["skv_build", "skv_decode_step", "skv_get_stats", "skv_reset_temporal_cache",
+            "skv_export_state", "skv_destroy", "skv_status_string", "skv_abi_version"]
+
+
+class SkvConfig(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("seq_len", ctypes.c_int64), ("rank", ctypes.c_int32), ("chunk", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("n_outlier", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("value_placement", ctypes.c_int32), ("rope_theta", ctypes.c_double),
+                ("temporal_cache", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class SkvStats(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int64), ("last_hits", ctypes.c_int64),
+                ("last_misses", ctypes.c_int64), ("total_hits", ctypes.c_int64),
+                ("total_misses", ctypes.c_int64), ("last_alpha", ctypes.c_double),
+                ("mean_alpha", ctypes.c_double), ("last_host_bytes", ctypes.c_int64)]
+
+
+class SkvStateHost(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ["A", "B", "landmarks", "cand_ids", "outlier_ids", "k_outlier", "v_outlier",
+                 "k_window", "v_window", "min_cos", "eigvals"]]
+
+
+class SkvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({skv_status_string(status)})")
+        self.status = status
+
+
+def lib():
+    """Load libskv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: run `python -m sparse_kv_cache_decode_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.skv_build.argtypes = [ctypes.POINTER(SkvConfig), vp, vp, vp, ctypes.POINTER(vp)]
+        L.skv_build.restype = i32
+        L.skv_decode_step.argtypes = [vp, vp, vp, vp, vp]
+        L.skv_decode_step.restype = i32
+        L.skv_get_stats.argtypes = [vp, ctypes.POINTER(SkvStats)]
+        L.skv_get_stats.restype = i32
+        L.skv_reset_temporal_cache.argtypes = [vp]
+        L.skv_reset_temporal_cache.restype = i32
+        L.skv_export_state.argtypes = [vp, ctypes.POINTER(SkvStateHost)]
+        L.skv_export_state.restype = i32
+        L.skv_destroy.argtypes = [vp]
+        L.skv_destroy.restype = None
+        L.skv_status_string.argtypes = [i32]
+        L.skv_status_string.restype = ctypes.c_char_p
+        L.skv_abi_version.argtypes = []
+        L.skv_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def skv_status_string(status: int) -> str:
+    return lib().skv_status_string(status).decode()
+
+
+def skv_abi_version() -> int:
+    return lib().skv_abi_version()
+
+
+def make_config(shape, value_placement: int = SKV_VALUES_DEVICE, temporal_cache: int = 1) -> SkvConfig:
+    """skv_config from any object with the ShadowKV shape fields."""
+    return SkvConfig(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                     shape.seq_len, shape.rank, shape.chunk, shape.top_k, shape.n_outlier,
+                     shape.window, value_placement, float(shape.rope_theta), temporal_cache, 0)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        assert t.is_contiguous()
+        return t.data_ptr()
+    return int(t)
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(fn, status):
+    if status != SKV_OK:
+        raise SkvError(fn, status)
+
+
+def skv_build(cfg: SkvConfig, k_pre, v, stream=None) -> int:
+    """Build one layer; returns the opaque handle (an int)."""
+    h = ctypes.c_void_p()
+    _check("skv_build", lib().skv_build(ctypes.byref(cfg), _ptr(k_pre), _ptr(v), _stream(stream),
+                                        ctypes.byref(h)))
+    return h.value
+
+
+def skv_decode_step(h: int, q, out, chunk_ids, stream=None) -> None:
+    _check("skv_decode_step", lib().skv_decode_step(h, _ptr(q), _ptr(out), _ptr(chunk_ids),
+                                                    _stream(stream)))
+
+
+def skv_get_stats(h: int) -> dict:
+    s = SkvStats()
+    _check("skv_get_stats", lib().skv_get_stats(h, ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in SkvStats._fields_}
+
+
+def skv_reset_temporal_cache(h: int) -> None:
+    _check("skv_reset_temporal_cache", lib().skv_reset_temporal_cache(h))
+
+
+def skv_destroy(h: int) -> None:
+    lib().skv_destroy(h)
+
+
+def skv_export_state(h: int, cfg: SkvConfig) -> dict:
+    """Copy the built state to host numpy arrays (bf16 as uint16 bit patterns)."""
+    b, H, d, C = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.chunk
+    S, r, O, W = cfg.seq_len, cfg.rank, cfg.n_outlier, cfg.window
+    n_c = S // C
+    n_cand = n_c - O - W // C
+    arrs = {
+        "A": np.zeros((b, S, r), np.uint16), "B": np.zeros((b, H, r, d), np.uint16),
+        "landmarks": np.zeros((b, H, n_cand, d), np.uint16),
+        "cand_ids": np.zeros((b, H, n_cand), np.int32),
+        "outlier_ids": np.zeros((b, H, O), np.int32),
+        "k_outlier": np.zeros((b, H, O * C, d), np.uint16),
+        "v_outlier": np.zeros((b, H, O * C, d), np.uint16),
+        "k_window": np.zeros((b, H, W, d), np.uint16), "v_window": np.zeros((b, H, W, d), np.uint16),
+        "min_cos": np.zeros((b, H, n_c), np.float32), "eigvals": np.zeros((b, r), np.float64),
+    }
+    st = SkvStateHost(**{k: v.ctypes.data if v.size else None for k, v in arrs.items()})
+    _check("skv_export_state", lib().skv_export_state(h, ctypes.byref(st)))
+    return arrs
+
+
+class Layer:
+    """Owning wrapper of one built layer."""
+
+    def __init__(self, shape, k_pre, v, value_placement=SKV_VALUES_DEVICE, temporal_cache=1,
+                 stream=None):
+        self.cfg = make_config(shape, value_placement, temporal_cache)
+        self.shape = shape
+        self.h = skv_build(self.cfg, k_pre, v, stream)
+        self._v = v   # the value store is borrowed by the library: keep it alive
+
+    def decode(self, q, out=None, chunk_ids=None, stream=None):
+        s = self.shape
+        dev = q.device
+        if out is None:
+            out = torch.empty((s.batch, s.n_q_heads, s.head_dim), dtype=torch.float32, device=dev)
+        if chunk_ids is None:
+            chunk_ids = torch.empty((s.batch, s.n_kv_heads, s.top_k), dtype=torch.int32, device=dev)
+        skv_decode_step(self.h, q, out, chunk_ids, stream)
+        return out, chunk_ids
+
+    def stats(self):
+        return skv_get_stats(self.h)
+
+    def reset(self):
+        skv_reset_temporal_cache(self.h)
+
+    def export(self):
+        return skv_export_state(self.h, self.cfg)
+
+    def close(self):
+        if self.h:
+            skv_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

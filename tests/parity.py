@@ -1,0 +1,95 @@
+"""Comparison rules between the GPU library and the CPU oracle.
+
+Bars (floating point from bf16 storage with fp32 accumulation):
+* selected chunk ids bit-exact, except chunks whose oracle score S2 lies within
+  1e-3 relative of the oracle's K-th score (near ties may swap);
+* attention outputs: max |err| <= 2e-2 and relative L2 <= 5e-3;
+* hit counts exact whenever the selections agree.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import shadowkv as O
+
+TIE_REL = 1e-3
+MAX_ABS = 2e-2
+REL_L2 = 5e-3
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> uint16 numpy bit patterns (CPU copy)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def check_ids(gpu_ids: np.ndarray, st: O.State, res: O.StepResult) -> int:
+    """Assert the tie rule per pair; returns how many pairs differ at all."""
+    cfg = st.cfg
+    K = cfg.top_k
+    differ = 0
+    for b in range(cfg.batch):
+        for h in range(cfg.n_kv_heads):
+            g = gpu_ids[b, h]
+            assert np.all(np.diff(g) > 0), f"pair ({b},{h}) ids not strictly ascending"
+            o = res.ids[b, h]
+            if np.array_equal(g, o):
+                continue
+            differ += 1
+            cand = st.cand[b, h]
+            pos = np.searchsorted(cand, g)
+            assert np.all(pos < len(cand)) and np.array_equal(cand[np.minimum(pos, len(cand) - 1)], g), \
+                f"pair ({b},{h}) selected a non-candidate chunk"
+            s2 = res.scores[b, h]
+            kth = np.sort(s2)[::-1][K - 1]
+            for c in set(g.tolist()) ^ set(o.tolist()):
+                sc = s2[np.searchsorted(cand, c)]
+                assert abs(sc - kth) <= TIE_REL * kth, \
+                    f"pair ({b},{h}) chunk {c}: score {sc} vs K-th {kth} is not a near tie"
+    return differ
+
+
+def check_out(gpu_out: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_L2):
+    err = np.abs(gpu_out.astype(np.float64) - ref)
+    rl2 = np.linalg.norm(gpu_out.astype(np.float64) - ref) / np.linalg.norm(ref)
+    assert err.max() <= max_abs, f"max |err| {err.max():.3e} > {max_abs}"
+    assert rl2 <= rel_l2, f"rel L2 {rl2:.3e} > {rel_l2}"
+    return float(err.max()), float(rl2)
+
+
+def bf16_close(gpu_bits: np.ndarray, ref: np.ndarray, slack: float) -> float:
+    """Worst excess of |gpu - ref| over one bf16 spacing at ref plus an absolute
+    slack (fp32 arithmetic on O(1) values can land on either side of a rounding
+    boundary, and cancellation makes tiny results inexact in absolute terms).
+    Returns max(|gpu - ref| - spacing(ref) - slack); <= 0 passes."""
+    g = O.bf16_bits_to_f64(gpu_bits)
+    _, e = np.frexp(ref)
+    spacing = np.where(ref == 0, 0.0, np.ldexp(1.0, e - 8))
+    return float(np.max(np.abs(g - ref) - spacing - slack))
+
+
+def check_build(gpu: dict, st: O.State):
+    """Build-state parity: outliers, candidates, landmarks, exact caches, factors."""
+    cfg = st.cfg
+    np.testing.assert_array_equal(gpu["outlier_ids"], st.outliers)
+    np.testing.assert_array_equal(gpu["cand_ids"], st.cand)
+    np.testing.assert_allclose(gpu["min_cos"], st.min_cos, atol=2e-5)
+    # fp32 RoPE of O(1) keys: absolute error well under 1e-5
+    assert bf16_close(gpu["landmarks"], st.L, 1e-5) <= 0
+    assert bf16_close(gpu["k_outlier"], st.K_out, 1e-5) <= 0
+    assert bf16_close(gpu["k_window"], st.K_win, 1e-5) <= 0
+    np.testing.assert_array_equal(O.bf16_bits_to_f64(gpu["v_outlier"]), st.V_out)
+    np.testing.assert_array_equal(O.bf16_bits_to_f64(gpu["v_window"]), st.V_win)
+    r = cfg.rank
+    np.testing.assert_allclose(gpu["eigvals"], st.sigma[:, :r] ** 2, rtol=1e-8)
+    A = O.bf16_bits_to_f64(gpu["A"])
+    B = O.bf16_bits_to_f64(gpu["B"])
+    # same gauge: the factors agree element by element up to bf16 rounding
+    assert bf16_close(gpu["B"], st.B, 1e-9) <= 0
+    rel = np.abs(A - st.A) / (np.abs(st.A) + 1e-3 * np.abs(st.A).max())
+    assert rel.max() <= 2 ** -7, f"A differs by {rel.max()}"
+    for b in range(cfg.batch):
+        for h in range(cfg.n_kv_heads):
+            pg = A[b] @ B[b, h]
+            po = st.A[b] @ st.B[b, h]
+            assert np.linalg.norm(pg - po) <= 1e-2 * np.linalg.norm(po)
