@@ -1,0 +1,248 @@
+"""Decode-step benchmark of the ShadowKV sparse-KV decode on one MI355X.
+
+python bench.py [--gpus 1] [--steps 60] [--warmup 4] [--shape llama3_8b_122k]
+
+One step = one ShadowKV decode step (landmark scoring + top-K + index scan, key
+rebuild of the misses, sparse attention) through every layer of the model
+shape, i.e. one new token for each of the `batch` sequences.  Inputs are the
+seeded synthetic caches of sparse_kv_cache_decode_amd.synth, already resident in
+HBM when the timed region starts; queries drift as AR(1) so the temporal cache
+sees hits.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+METRIC = "decode tokens/s at S=122K batch 8 (Llama-3.1-8B shape); % HBM roofline"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle, timed on the host cores, on a bounded sample
+
+
+def cpu_baseline_child(shape_name: str, seed: int, min_seconds: float):
+    """Child process: build the oracle for layer 0 / batch element 0, say 'ready',
+    wait for 'go' on stdin, then time oracle decode steps for >= min_seconds."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+
+    from oracle import shadowkv as O
+    from sparse_kv_cache_decode_amd import synth
+
+    shape = synth.SHAPES[shape_name].replace(batch=1)
+    t0 = time.time()
+    k, v = synth.layer_cache_np(shape, 0, seed)
+    q = synth.queries_np(shape, k, 0, 64, seed)
+    kb = k.view(torch.int16).numpy().view(np.uint16)
+    vb = v.view(torch.int16).numpy().view(np.uint16)
+    st = O.build(O.config_from(shape), kb, vb)
+    qb = q.view(torch.int16).numpy().view(np.uint16)
+    print(json.dumps({"ready": True, "prep_s": time.time() - t0}), flush=True)
+    sys.stdin.readline()
+    threads = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) \
+        if threadpoolctl.threadpool_info() else 1
+    prev, n, t_start = None, 0, time.perf_counter()
+    while True:
+        res = O.decode_step(st, qb[n % 64], prev)
+        prev = res.ids
+        n += 1
+        el = time.perf_counter() - t_start
+        if el >= min_seconds and n >= 4:
+            break
+    print(json.dumps({"steps": n, "seconds": el, "threads": threads,
+                      "affinity": len(os.sched_getaffinity(0))}), flush=True)
+
+
+def start_cpu_baseline(shape_name, seed, min_seconds):
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--shape", shape_name,
+           "--seed", str(seed), "--cpu-seconds", str(min_seconds)]
+    return subprocess.Popen(cmd, stdin=subprocess.PIPE, stdout=subprocess.PIPE, text=True, cwd=ROOT)
+
+
+# ----------------------------------------------------------------------------
+
+
+def algorithmic_bytes(shape, misses_per_layer_step: float) -> dict:
+    """Bytes the method must move per layer-step (HBM-resident values)."""
+    d, C, r = shape.head_dim, shape.chunk, shape.rank
+    P = shape.pairs
+    landmarks = P * shape.n_cand * d * 2
+    q_bytes = shape.batch * shape.n_q_heads * d * 2
+    out_bytes = shape.batch * shape.n_q_heads * d * 4
+    rebuild = misses_per_layer_step * C * (r * 2 + d * 2) + P * r * d * 2
+    attn = P * shape.tokens_attended * d * 2 * 2
+    return {"score": landmarks + q_bytes, "rebuild": rebuild, "attention": attn + out_bytes,
+            "total": landmarks + q_bytes + rebuild + attn + out_bytes}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--shape", default="llama3_8b_122k")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = model's)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
+    args = ap.parse_args()
+
+    if args.cpu_baseline_child:
+        cpu_baseline_child(args.shape, args.seed, args.cpu_seconds)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step shards by batch element with no communication; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    # the oracle child starts before this process touches the GPU
+    child = None if args.no_cpu_baseline else start_cpu_baseline(args.shape, args.seed, args.cpu_seconds)
+
+    import torch
+
+    from sparse_kv_cache_decode_amd import skv, synth
+
+    shape = synth.SHAPES[args.shape]
+    if args.layers:
+        shape = shape.replace(layers=args.layers)
+    L, W, K = shape.layers, args.warmup, args.steps
+    total = W + K
+    dev = torch.device("cuda")
+    torch.cuda.init()
+    skv.lib()
+    layers, qs = [], []
+    t0 = time.time()
+    for l in range(L):
+        k_pre, v = synth.layer_cache_torch(shape, l, args.seed, dev)
+        layers.append(skv.Layer(shape, k_pre, v))
+        qs.append(synth.queries_torch(shape, k_pre, l, total, args.seed))
+        del k_pre, v
+        if l % 4 == 3 or l == L - 1:
+            log(f"built layer {l + 1}/{L} ({time.time() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    out = torch.empty((shape.batch, shape.n_q_heads, shape.head_dim), dtype=torch.float32, device=dev)
+    ids = torch.empty((shape.batch, shape.n_kv_heads, shape.top_k), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for t in range(W):
+        for l in range(L):
+            layers[l].decode(qs[l][t], out, ids, stream)
+    torch.cuda.synchronize()
+    before = [ly.stats() for ly in layers]
+    for ly in layers:
+        skv.skv_set_timing(ly.h, K)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for t in range(W, W + K):
+        for l in range(L):
+            layers[l].decode(qs[l][t], out, ids, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    log(f"timed {K} steps x {L} layers: {ms_total:.2f} ms")
+
+    after = [ly.stats() for ly in layers]
+    phase_ms = {p: 0.0 for p in skv.PHASES}
+    for ly in layers:
+        ph, n = skv.skv_get_timing(ly.h)
+        assert n == K
+        for p in ph:
+            phase_ms[p] += ph[p]
+    launches = K * L
+    phase_avg_us = {p: 1000.0 * phase_ms[p] / launches for p in phase_ms}
+    misses = sum(a["total_misses"] - b["total_misses"] for a, b in zip(after, before)) / launches
+    hits = sum(a["total_hits"] - b["total_hits"] for a, b in zip(after, before)) / launches
+    alpha_timed = hits / (shape.pairs * shape.top_k)
+    alpha_all = sum(a["mean_alpha"] for a in after) / L
+    by = algorithmic_bytes(shape, misses)
+
+    ms_per_step = ms_total / K
+    tok_s = shape.batch * K / (ms_total / 1000.0)
+    layer_us = 1000.0 * ms_per_step / L
+    step_gbps = by["total"] / (layer_us * 1e-6) / 1e9
+    score_gbps = by["score"] / (phase_avg_us["score"] * 1e-6) / 1e9
+    # pages' equivalent bandwidth with the measured alpha (values in HBM: no PCIe term),
+    # and the dense-attention bytes per measured layer time
+    S, C, Kc, Oc = shape.seq_len, shape.chunk, shape.top_k, shape.n_outlier
+    bt_formula = 2 * S * HBM_PEAK_GBPS / (S / C + 2 * (Kc + Oc) * C) / 1000.0
+    dense_bytes = 2 * S * shape.head_dim * 2 * shape.pairs
+    bt_measured = dense_bytes / (layer_us * 1e-6) / 1e12
+
+    cpu = None
+    if child is not None:
+        line = child.stdout.readline()
+        ready = json.loads(line) if line else None
+        if ready:
+            child.stdin.write("go\n")
+            child.stdin.flush()
+            res = json.loads(child.stdout.readline())
+            child.wait(timeout=600)
+            t_step = res["seconds"] / res["steps"]     # one layer, one batch element
+            cpu = {"value": 1.0 / (L * t_step), "unit": "tokens/s", "cores": res["threads"],
+                   "kind": "oracle",
+                   "sample": f"layer 0, batch element 0 of {shape.name} ({shape.pairs // shape.batch} KV heads, "
+                             f"S={shape.seq_len}), {res['steps']} drifting decode steps in {res['seconds']:.1f}s "
+                             f"(float64 NumPy, {res['threads']} BLAS threads, {res['affinity']} cores in affinity); "
+                             f"tokens/s = batch / (batch * layers * t_step) = 1/(layers * t_step); build untimed"}
+        else:
+            log("cpu baseline child failed")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}: {L} layers, batch {shape.batch}, S={shape.seq_len}, "
+                               f"{shape.n_q_heads} q / {shape.n_kv_heads} KV heads, d={shape.head_dim}, "
+                               f"r={shape.rank}, C={shape.chunk}, K={shape.top_k}, O={shape.n_outlier}, "
+                               f"window {shape.window}, values in HBM, AR(1)-drifting queries",
+                   "global_batch": shape.batch, "seq_len": shape.seq_len, "layers": L,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "score_kernel (landmark GEMV)",
+                     "achieved": round(score_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(score_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "step_roofline": {"algorithmic_bytes_per_layer_step": int(by["total"]),
+                          "achieved_GBps": round(step_gbps, 1),
+                          "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
+        "phase_us_per_layer": {p: round(v, 2) for p, v in phase_avg_us.items()},
+        "layer_us": round(layer_us, 2),
+        "alpha": {"timed_steps": round(alpha_timed, 4), "steps_1_to_end": round(alpha_all, 4),
+                  "misses_per_layer_step": round(misses, 1)},
+        "equivalent_bandwidth_TBps": {"formula_values_in_hbm_at_8TBps": round(bt_formula, 1),
+                                      "dense_bytes_over_measured_time": round(bt_measured, 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    for ly in layers:
+        ly.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -175,6 +175,24 @@ skv_status skv_reset_temporal_cache(skv_layer* h);
 /* Synchronous copy of the built state into caller-owned host buffers. */
 skv_status skv_export_state(const skv_layer* h, const skv_state_host* dst);
 
+/*
+ * Per-phase device timing.  With capacity > 0 the next `capacity` decode steps
+ * record HIP events on the decode stream around each kernel (and on the side
+ * stream around the host value gather); capacity 0 stops recording.  The events
+ * add one marker per phase and no host synchronisation.
+ */
+#define SKV_PHASE_SCORE 0         /* landmark GEMV: logits + per-head LSE partials */
+#define SKV_PHASE_SELECT 1        /* LSE, chunk scores, top-K, index scan          */
+#define SKV_PHASE_REBUILD 2       /* key rebuild + RoPE of the missed chunks       */
+#define SKV_PHASE_VALUE_GATHER 3  /* host-value gather (side stream, overlapped)   */
+#define SKV_PHASE_ATTENTION 4     /* split-K attention + merge of the splits       */
+#define SKV_NUM_PHASES 5
+skv_status skv_set_timing(skv_layer* h, int32_t capacity);
+
+/* Sums of the recorded phase durations in milliseconds (phase_ms[SKV_NUM_PHASES])
+ * and the number of recorded steps; synchronises with the recorded streams. */
+skv_status skv_get_timing(const skv_layer* h, double* phase_ms, int64_t* steps);
+
 /* Release everything the handle owns (never the borrowed value store). NULL is ok. */
 void skv_destroy(skv_layer* h);
 

@@ -3,9 +3,9 @@
 // "Decoding-Time KV Selection via Landmark-Guided Approximate Attention" and
 // "Sparse KV Reconstruction and Overlapping Strategy").
 //
-//  score_select : landmark GEMV (one 256-B landmark row feeds the G heads of its
-//                 KV head), per-head log-sum-exp partials; the last workgroup of a
-//                 pair to finish combines the LSE, forms the chunk score
+//  score        : landmark GEMV (one 256-B landmark row feeds the G heads of its
+//                 KV head), fp32 logits and per-head log-sum-exp partials.
+//  select       : one workgroup per pair combines the LSE, forms the chunk score
 //                 max_g(l_g - LSE_g) (log of the group max of softmax
 //                 probabilities), selects the top-K chunks and runs the
 //                 temporal-cache index scan (hits, misses, slot assignment).
@@ -13,7 +13,10 @@
 //                 MFMA 16x16x32 tiles with the rotation fused into the epilogue.
 //  value_gather : missed chunks' values from pinned host memory (side stream).
 //  attention    : split-K flash-decode over [outliers; selected; window] with an
-//                 online softmax in fp32; the last workgroup of a pair merges.
+//                 online softmax in fp32, then a per-pair merge of the splits.
+// Workgroups never wait on one another inside a kernel: device-scope fences on
+// gfx950 write back and invalidate the whole L2, so every cross-workgroup
+// hand-off goes through a kernel boundary instead.
 #include "skv_internal.h"
 #include "skv_select.h"
 
@@ -66,15 +69,8 @@ __device__ __forceinline__ float pick(const float (&v)[G], int i) {
 constexpr int kScoreUnroll = 4;
 
 template <int G>
-__global__ __launch_bounds__(256) void score_select_kernel(DecodeArgs a) {
-  extern __shared__ int smem[];
-  int* hist = smem;                 // 2048
-  int* sh = smem + 2048;            // 16
-  float* red = reinterpret_cast<float*>(smem + 2064);   // 2 * 16 * 16 (m, s per wave/row/head)
-  int* sel = smem + 2064 + 512;     // top_k
-  __shared__ int is_last;
-  __shared__ float lse[16];
-
+__global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
+  __shared__ float red[2][16][16];   // (m, s) per (wave, row) and head
   const int p = blockIdx.y, blk = blockIdx.x;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ds = lane & 15, tg = lane >> 4;
@@ -126,27 +122,35 @@ __global__ __launch_bounds__(256) void score_select_kernel(DecodeArgs a) {
   }
   // per-workgroup (max, sum exp) of every head
   if (ds < G) {
-    red[(w * 4 + tg) * 16 + ds] = m_run;
-    red[256 + (w * 4 + tg) * 16 + ds] = s_run;
+    red[0][w * 4 + tg][ds] = m_run;
+    red[1][w * 4 + tg][ds] = s_run;
   }
   __syncthreads();
   if (threadIdx.x < G) {
     float M = kNegBig;
-    for (int k = 0; k < 16; k++) M = fmaxf(M, red[k * 16 + threadIdx.x]);
+    for (int k = 0; k < 16; k++) M = fmaxf(M, red[0][k][threadIdx.x]);
     float S = 0.f;
-    for (int k = 0; k < 16; k++) S += red[256 + k * 16 + threadIdx.x] * __expf(red[k * 16 + threadIdx.x] - M);
+    for (int k = 0; k < 16; k++) S += red[1][k][threadIdx.x] * __expf(red[0][k][threadIdx.x] - M);
     float* dst = a.lse_part + (((int64_t)p * a.nb_score + blk) * G + threadIdx.x) * 2;
     dst[0] = M;
     dst[1] = S;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (arrive_count(&a.cnt_score[p]) == a.nb_score - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  if (threadIdx.x == 0) a.cnt_score[p] = 0;
+}
 
-  // ---- last workgroup of the pair: log-sum-exp of every head over all candidates
+// One workgroup per pair: log-sum-exp of every head over all candidates, chunk
+// scores, top-K selection, then the temporal-cache index scan.
+constexpr int kSelThreads = 512;
+
+template <int G>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
+  extern __shared__ int smem[];
+  int* hist = smem;                 // 2048
+  int* sh = smem + 2048;            // 16
+  int* sel = smem + 2064;           // top_k
+  __shared__ float lse[16];
+  const int p = blockIdx.x;
+  const int n_cand = a.n_cand;
+  const float* lg = a.logits + (int64_t)p * n_cand * G;
   if (threadIdx.x < G) {
     const float* src = a.lse_part + (int64_t)p * a.nb_score * G * 2;
     float M = kNegBig;
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(DecodeArgs a) {
   }
   __syncthreads();
   uint32_t* kp = a.keys + (int64_t)p * n_cand;
-  for (int c = threadIdx.x; c < n_cand; c += 256) {
+  for (int c = threadIdx.x; c < n_cand; c += kSelThreads) {
     float best = -3.0e38f;
 #pragma unroll
     for (int g = 0; g < G; g++) best = fmaxf(best, lg[(int64_t)c * G + g] - lse[g]);
@@ -166,10 +170,10 @@ __global__ __launch_bounds__(256) void score_select_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const int K = a.top_k;
-  block_topk<256>([&](int i) { return kp[i]; }, n_cand, K, hist, sh,
-                  [&](int pos, int i) { if (pos < K) sel[pos] = i; });
+  block_topk<kSelThreads>([&](int i) { return kp[i]; }, n_cand, K, hist, sh,
+                          [&](int pos, int i) { if (pos < K) sel[pos] = i; });
   const int32_t* cmap = a.cand_map + (int64_t)p * n_cand;
-  for (int i = threadIdx.x; i < K; i += 256) a.chunk_ids[(int64_t)p * K + i] = cmap[sel[i]];
+  for (int i = threadIdx.x; i < K; i += kSelThreads) a.chunk_ids[(int64_t)p * K + i] = cmap[sel[i]];
 
   // ---- temporal-cache index scan against the chunks held by the slots
   int32_t* sc = a.slot_cand + (int64_t)p * K;
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(DecodeArgs a) {
   uint32_t* res = a.resident + (int64_t)p * a.res_words;
   const bool has_prev = a.temporal && sc[0] >= 0;
   int n_free = 0, n_miss = 0;
-  for (int t0 = 0; t0 < K; t0 += 256) {
+  for (int t0 = 0; t0 < K; t0 += kSelThreads) {
     const int s = t0 + threadIdx.x;
     int fr = 0, ms = 0, ci = -1;
     if (s < K) {
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(DecodeArgs a) {
       ms = !(has_prev && ((res[ci >> 5] >> (ci & 31)) & 1u));
     }
     int tot;
-    const int ex = block_exclusive_scan<256>(fr | (ms << 16), sh, &tot);
+    const int ex = block_exclusive_scan<kSelThreads>(fr | (ms << 16), sh, &tot);
     if (fr) a.free_slot[(int64_t)p * K + n_free + (ex & 0xffff)] = s;
     if (ms) a.miss_cand[(int64_t)p * K + n_miss + (ex >> 16)] = ci;
     n_free += tot & 0xffff;
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(DecodeArgs a) {
   }
   __syncthreads();
   // n_free == n_miss: every missed chunk takes the next evicted slot
-  for (int j = threadIdx.x; j < n_miss; j += 256) {
+  for (int j = threadIdx.x; j < n_miss; j += kSelThreads) {
     const int slot = a.free_slot[(int64_t)p * K + j];
     const int ci = a.miss_cand[(int64_t)p * K + j];
     const int old = sc[slot];
@@ -217,15 +221,28 @@ __global__ __launch_bounds__(256) void score_select_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_score_select(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_score(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.nb_score, a.batch * a.n_kv);
-  const size_t lds = (size_t)(2064 + 512 + a.top_k) * sizeof(int);
   switch (a.group) {
-    case 1: score_select_kernel<1><<<grid, 256, lds, st>>>(a); break;
-    case 2: score_select_kernel<2><<<grid, 256, lds, st>>>(a); break;
-    case 4: score_select_kernel<4><<<grid, 256, lds, st>>>(a); break;
-    case 8: score_select_kernel<8><<<grid, 256, lds, st>>>(a); break;
-    case 16: score_select_kernel<16><<<grid, 256, lds, st>>>(a); break;
+    case 1: score_kernel<1><<<grid, 256, 0, st>>>(a); break;
+    case 2: score_kernel<2><<<grid, 256, 0, st>>>(a); break;
+    case 4: score_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    case 8: score_kernel<8><<<grid, 256, 0, st>>>(a); break;
+    case 16: score_kernel<16><<<grid, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
+  const size_t lds = (size_t)(2064 + a.top_k) * sizeof(int);
+  const int P = a.batch * a.n_kv;
+  switch (a.group) {
+    case 1: select_kernel<1><<<P, kSelThreads, lds, st>>>(a); break;
+    case 2: select_kernel<2><<<P, kSelThreads, lds, st>>>(a); break;
+    case 4: select_kernel<4><<<P, kSelThreads, lds, st>>>(a); break;
+    case 8: select_kernel<8><<<P, kSelThreads, lds, st>>>(a); break;
+    case 16: select_kernel<16><<<P, kSelThreads, lds, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -414,7 +431,6 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   constexpr int TPR = C / 4;   // tokens of a unit per lane row
   __shared__ float wo[4][G][kHeadDim];
   __shared__ float wm[4][G], wl[4][G];
-  __shared__ int is_last;
   const int p = blockIdx.y, split = blockIdx.x;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ds = lane & 15, tg = lane >> 4;
@@ -547,12 +563,14 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
       part[g * (kHeadDim + 2) + kHeadDim + 1] = den;
     }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (arrive_count(&a.cnt_attn[p]) == a.n_split - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  if (threadIdx.x == 0) a.cnt_attn[p] = 0;
+}
+
+// Merge the split partials of one pair: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+template <int G>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+  const int p = blockIdx.x;
+  const int b = p / a.n_kv, h = p % a.n_kv;
+  const int hq = a.n_kv * G;
   const float* allp = a.attn_part + (int64_t)p * a.n_split * G * (kHeadDim + 2);
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
     const int g = idx / kHeadDim, dim = idx % kHeadDim;
@@ -578,6 +596,9 @@ static hipError_t launch_attn_g(const DecodeArgs& a, hipStream_t st) {
     case 16: attn_kernel<G, 16><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  combine_kernel<G><<<a.batch * a.n_kv, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

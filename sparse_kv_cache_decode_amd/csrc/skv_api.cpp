@@ -27,7 +27,7 @@ struct skv_layer {
            *k_win = nullptr, *v_win = nullptr, *key_slots = nullptr, *val_slots = nullptr;
   int32_t *cand_map = nullptr, *outlier_ids = nullptr, *slot_cand = nullptr, *slot_chunk = nullptr,
           *miss_slot = nullptr, *miss_chunk = nullptr, *miss_cand = nullptr, *free_slot = nullptr,
-          *n_miss = nullptr, *hits_last = nullptr, *cnt_score = nullptr, *cnt_attn = nullptr;
+          *n_miss = nullptr, *hits_last = nullptr;
   uint32_t *resident = nullptr, *keys = nullptr;
   long long *hits_total = nullptr, *miss_total = nullptr;
   float *logits = nullptr, *lse_part = nullptr, *attn_part = nullptr, *min_cos = nullptr;
@@ -37,11 +37,15 @@ struct skv_layer {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipStream_t last_stream = nullptr;
   int64_t steps = 0;
+  // per-phase timing: kEv events per recorded step
+  std::vector<hipEvent_t> tev;
+  int t_cap = 0, t_n = 0;
 };
 
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kEv = 7;   // score | select | rebuild | attention on the stream, gather on the side
 
 struct Carver {
   size_t off = 0;
@@ -121,8 +125,16 @@ const void* host_device_ptr(const void* p) {
   return dp;
 }
 
+void drop_timing(skv_layer* h) {
+  for (hipEvent_t e : h->tev)
+    if (e) (void)hipEventDestroy(e);
+  h->tev.clear();
+  h->t_cap = h->t_n = 0;
+}
+
 void release(skv_layer* h) {
   if (!h) return;
+  drop_timing(h);
   if (h->pool) (void)hipFree(h->pool);
   if (h->side) (void)hipStreamDestroy(h->side);
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
@@ -178,8 +190,6 @@ DecodeArgs decode_args(skv_layer* h) {
   a.logits = h->logits;
   a.lse_part = h->lse_part;
   a.keys = h->keys;
-  a.cnt_score = h->cnt_score;
-  a.cnt_attn = h->cnt_attn;
   a.attn_part = h->attn_part;
   return a;
 }
@@ -274,8 +284,6 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const size_t oFs = cv.take<int32_t>((size_t)P * K);
   const size_t oNm = cv.take<int32_t>(P);
   const size_t oHl = cv.take<int32_t>(P);
-  const size_t oCs = cv.take<int32_t>(P);
-  const size_t oCa = cv.take<int32_t>(P);
   const size_t oRes = cv.take<uint32_t>((size_t)P * h->res_words);
   const size_t oKeys = cv.take<uint32_t>((size_t)P * n_c);
   const size_t oHt = cv.take<long long>(P);
@@ -338,8 +346,6 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->free_slot = (int32_t*)(base + oFs);
     h->n_miss = (int32_t*)(base + oNm);
     h->hits_last = (int32_t*)(base + oHl);
-    h->cnt_score = (int32_t*)(base + oCs);
-    h->cnt_attn = (int32_t*)(base + oCa);
     h->resident = (uint32_t*)(base + oRes);
     h->keys = (uint32_t*)(base + oKeys);
     h->hits_total = (long long*)(base + oHt);
@@ -415,22 +421,37 @@ skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t*
   a.q = q;
   a.out = out;
   a.chunk_ids = chunk_ids;
-  if (h->need_reset) {
-    HIP_TRY(launch_reset_cache(a, s));
-    h->need_reset = false;
+  {
+    hipEvent_t* ev = h->t_n < h->t_cap ? &h->tev[(size_t)h->t_n * kEv] : nullptr;
+    if (h->need_reset) {
+      HIP_TRY(launch_reset_cache(a, s));
+      h->need_reset = false;
+    }
+    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+    HIP_TRY(launch_score(a, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
+    HIP_TRY(launch_select(a, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    if (a.host_values) {
+      HIP_TRY(hipEventRecord(h->ev_fork, s));
+      HIP_TRY(hipStreamWaitEvent(h->side, h->ev_fork, 0));
+      if (ev) HIP_TRY(hipEventRecord(ev[5], h->side));
+      HIP_TRY(launch_value_gather(a, h->side));
+      if (ev) HIP_TRY(hipEventRecord(ev[6], h->side));
+      HIP_TRY(hipEventRecord(h->ev_join, h->side));
+      HIP_TRY(launch_rebuild(a, s));
+      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+      HIP_TRY(hipStreamWaitEvent(s, h->ev_join, 0));
+    } else {
+      HIP_TRY(launch_rebuild(a, s));
+      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+    }
+    HIP_TRY(launch_attention(a, s));
+    if (ev) {
+      HIP_TRY(hipEventRecord(ev[4], s));
+      h->t_n++;
+    }
   }
-  HIP_TRY(launch_score_select(a, s));
-  if (a.host_values) {
-    HIP_TRY(hipEventRecord(h->ev_fork, s));
-    HIP_TRY(hipStreamWaitEvent(h->side, h->ev_fork, 0));
-    HIP_TRY(launch_value_gather(a, h->side));
-    HIP_TRY(hipEventRecord(h->ev_join, h->side));
-    HIP_TRY(launch_rebuild(a, s));
-    HIP_TRY(hipStreamWaitEvent(s, h->ev_join, 0));
-  } else {
-    HIP_TRY(launch_rebuild(a, s));
-  }
-  HIP_TRY(launch_attention(a, s));
   h->steps++;
   h->last_stream = s;
   return SKV_OK;
@@ -513,6 +534,57 @@ skv_status skv_export_state(const skv_layer* hc, const skv_state_host* d) {
   if (d->v_window && c.window) HIP_TRY(hipMemcpy(d->v_window, h->v_win, (size_t)P * c.window * kHeadDim * 2, hipMemcpyDeviceToHost));
   if (d->min_cos) HIP_TRY(hipMemcpy(d->min_cos, h->min_cos, (size_t)P * h->n_c * 4, hipMemcpyDeviceToHost));
   if (d->eigvals) std::memcpy(d->eigvals, h->eig.data(), h->eig.size() * 8);
+  return SKV_OK;
+hip_fail:
+  (void)hipGetLastError();
+  h->poisoned = true;
+  return SKV_ERR_HIP;
+}
+
+skv_status skv_set_timing(skv_layer* h, int32_t capacity) {
+  if (!h || capacity < 0) return SKV_ERR_INVALID_ARG;
+  if (h->poisoned) return SKV_ERR_STATE;
+  (void)hipStreamSynchronize(h->last_stream);
+  if (h->side) (void)hipStreamSynchronize(h->side);
+  drop_timing(h);
+  if (capacity == 0) return SKV_OK;
+  h->tev.assign((size_t)capacity * kEv, nullptr);
+  for (auto& e : h->tev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      (void)hipGetLastError();
+      drop_timing(h);
+      return SKV_ERR_OOM;
+    }
+  }
+  h->t_cap = capacity;
+  return SKV_OK;
+}
+
+skv_status skv_get_timing(const skv_layer* hc, double* phase_ms, int64_t* steps) {
+  if (!hc || !phase_ms || !steps) return SKV_ERR_INVALID_ARG;
+  skv_layer* h = const_cast<skv_layer*>(hc);
+  if (h->poisoned) return SKV_ERR_STATE;
+  for (int i = 0; i < SKV_NUM_PHASES; i++) phase_ms[i] = 0.0;
+  *steps = h->t_n;
+  const bool host = h->cfg.value_placement == SKV_VALUES_HOST;
+  for (int i = 0; i < h->t_n; i++) {
+    hipEvent_t* ev = &h->tev[(size_t)i * kEv];
+    float ms;
+    HIP_TRY(hipEventSynchronize(ev[4]));
+    HIP_TRY(hipEventElapsedTime(&ms, ev[0], ev[1]));
+    phase_ms[SKV_PHASE_SCORE] += ms;
+    HIP_TRY(hipEventElapsedTime(&ms, ev[1], ev[2]));
+    phase_ms[SKV_PHASE_SELECT] += ms;
+    HIP_TRY(hipEventElapsedTime(&ms, ev[2], ev[3]));
+    phase_ms[SKV_PHASE_REBUILD] += ms;
+    HIP_TRY(hipEventElapsedTime(&ms, ev[3], ev[4]));
+    phase_ms[SKV_PHASE_ATTENTION] += ms;
+    if (host) {
+      HIP_TRY(hipEventSynchronize(ev[6]));
+      HIP_TRY(hipEventElapsedTime(&ms, ev[5], ev[6]));
+      phase_ms[SKV_PHASE_VALUE_GATHER] += ms;
+    }
+  }
   return SKV_OK;
 hip_fail:
   (void)hipGetLastError();

@@ -123,10 +123,4 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
   return base + x - v;
 }
 
-// Release/acquire helpers for the "last workgroup finishes" pattern.
-__device__ __forceinline__ int arrive_count(int* counter) {
-  __threadfence();
-  return __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace skv

@@ -50,8 +50,6 @@ struct DecodeArgs {
   float* logits;              // [P][n_cand][G]
   float* lse_part;            // [P][nb_score][G][2]
   uint32_t* keys;             // [P][n_cand]
-  int32_t* cnt_score;         // [P]
-  int32_t* cnt_attn;          // [P]
   float* attn_part;           // [P][n_split][G][d + 2]
   // outputs
   float* out;                 // [b][Hq][d]
@@ -80,7 +78,8 @@ hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_
 
 // ---- decode launchers (decode_kernels.hip)
 hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st);
-hipError_t launch_score_select(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_score(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);

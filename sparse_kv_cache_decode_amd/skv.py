@@ -21,7 +21,9 @@ SKV_ERR_OOM, SKV_ERR_HIP, SKV_ERR_STATE, SKV_ERR_INTERNAL = 4, 5, 6, 7
 SKV_VALUES_DEVICE, SKV_VALUES_HOST = 0, 1
 
 EXPORTED = ["skv_build", "skv_decode_step", "skv_get_stats", "skv_reset_temporal_cache",
-            "skv_export_state", "skv_destroy", "skv_status_string", "skv_abi_version"]
+            "skv_export_state", "skv_set_timing", "skv_get_timing", "skv_destroy",
+            "skv_status_string", "skv_abi_version"]
+PHASES = ["score", "select", "rebuild", "value_gather", "attention"]
 
 
 class SkvConfig(ctypes.Structure):
@@ -70,6 +72,10 @@ def lib():
         L.skv_reset_temporal_cache.restype = i32
         L.skv_export_state.argtypes = [vp, ctypes.POINTER(SkvStateHost)]
         L.skv_export_state.restype = i32
+        L.skv_set_timing.argtypes = [vp, i32]
+        L.skv_set_timing.restype = i32
+        L.skv_get_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.skv_get_timing.restype = i32
         L.skv_destroy.argtypes = [vp]
         L.skv_destroy.restype = None
         L.skv_status_string.argtypes = [i32]
@@ -138,6 +144,18 @@ def skv_get_stats(h: int) -> dict:
 
 def skv_reset_temporal_cache(h: int) -> None:
     _check("skv_reset_temporal_cache", lib().skv_reset_temporal_cache(h))
+
+
+def skv_set_timing(h: int, capacity: int) -> None:
+    _check("skv_set_timing", lib().skv_set_timing(h, capacity))
+
+
+def skv_get_timing(h: int) -> tuple[dict, int]:
+    """({phase: summed ms}, recorded steps)."""
+    ms = (ctypes.c_double * len(PHASES))()
+    n = ctypes.c_int64()
+    _check("skv_get_timing", lib().skv_get_timing(h, ms, ctypes.byref(n)))
+    return {p: ms[i] for i, p in enumerate(PHASES)}, n.value
 
 
 def skv_destroy(h: int) -> None:
