@@ -288,6 +288,18 @@ class StepResult:
     hits: np.ndarray         # [b, H] |I_t & I_{t-1}| (0 without a previous step)
 
 
+def pair_output(st: State, q: np.ndarray, bi: int, h: int, sel: np.ndarray) -> np.ndarray:
+    """Exact attention of the G query heads of pair (bi, h) over
+    [outlier chunks; rebuilt keys of the chunks `sel`; local window]; q [H_q, d]."""
+    cfg = st.cfg
+    G, C = cfg.group, cfg.chunk
+    ks = rebuild_keys(st, bi, h, sel)
+    tok = (sel[:, None] * C + np.arange(C)).reshape(-1)
+    keys = np.concatenate([st.K_out[bi, h], ks, st.K_win[bi, h]])
+    vals = np.concatenate([st.V_out[bi, h], st.V[bi, h, tok], st.V_win[bi, h]])
+    return attend(q[h * G:(h + 1) * G], keys, vals)
+
+
 def decode_step(st: State, q, prev_ids: np.ndarray | None = None) -> StepResult:
     """One decode step for every (batch, KV head) pair.
 
@@ -308,11 +320,7 @@ def decode_step(st: State, q, prev_ids: np.ndarray | None = None) -> StepResult:
             scores[bi, h], ids[bi, h] = s2, sel
             if prev_ids is not None:
                 hits[bi, h] = len(np.intersect1d(sel, prev_ids[bi, h]))
-            ks = rebuild_keys(st, bi, h, sel)
-            tok = (sel[:, None] * C + np.arange(C)).reshape(-1)
-            keys = np.concatenate([st.K_out[bi, h], ks, st.K_win[bi, h]])
-            vals = np.concatenate([st.V_out[bi, h], st.V[bi, h, tok], st.V_win[bi, h]])
-            out[bi, h * G:(h + 1) * G] = attend(q[bi, h * G:(h + 1) * G], keys, vals)
+            out[bi, h * G:(h + 1) * G] = pair_output(st, q[bi], bi, h, sel)
     return StepResult(out, ids, scores, hits)
 
 

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void outlier_kernel(const float* __restrict__ 
                                                       int n_elig, int O, uint32_t* __restrict__ keys,
                                                       int32_t* __restrict__ outlier_ids) {
   __shared__ int hist[2048];
-  __shared__ int sh[16];
+  __shared__ int sh[32];
   const int p = blockIdx.x;
   const float* mc = min_cos + (int64_t)p * n_c;
   uint32_t* kp = keys + (int64_t)p * n_c;

@@ -3,17 +3,21 @@
 // "Decoding-Time KV Selection via Landmark-Guided Approximate Attention" and
 // "Sparse KV Reconstruction and Overlapping Strategy").
 //
-//  score        : landmark GEMV (one 256-B landmark row feeds the G heads of its
-//                 KV head), fp32 logits and per-head log-sum-exp partials.
-//  select       : one workgroup per pair combines the LSE, forms the chunk score
-//                 max_g(l_g - LSE_g) (log of the group max of softmax
-//                 probabilities), selects the top-K chunks and runs the
-//                 temporal-cache index scan (hits, misses, slot assignment).
+//  score        : landmark GEMV: every 256-B landmark row is read once and dotted
+//                 with the G query heads of its KV head; the d = 128 contraction
+//                 runs on MFMA 16x16x32 bf16 (16 landmarks x 16 head columns per
+//                 tile, fp32 accumulation) so the vector ALUs only run the softmax
+//                 epilogue.  Writes fp32 logits and per-head log-sum-exp partials.
+//  select       : one workgroup per (batch, KV head) pair combines the LSE, forms
+//                 the chunk score max_g(l_g - LSE_g) (log of the group max of the
+//                 softmax probabilities), selects the top-K chunks with a radix
+//                 select in LDS and runs the temporal-cache index scan (hits,
+//                 misses, slot assignment).
 //  rebuild      : keys of the missed chunks, RoPE(Gather(A, I_miss) B), as bf16
 //                 MFMA 16x16x32 tiles with the rotation fused into the epilogue.
 //  value_gather : missed chunks' values from pinned host memory (side stream).
 //  attention    : split-K flash-decode over [outliers; selected; window] with an
-//                 online softmax in fp32, then a per-pair merge of the splits.
+//                 online softmax in fp32, then a per-(pair, head) merge of splits.
 // Workgroups never wait on one another inside a kernel: device-scope fences on
 // gfx950 write back and invalidate the whole L2, so every cross-workgroup
 // hand-off goes through a kernel boundary instead.
@@ -47,83 +51,81 @@ hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Score + select + index scan.
+// Score.  Wave w of a workgroup takes kScoreTiles tiles of 16 landmarks per
+// iteration.  MFMA operands (16x16x32): A = landmarks, lane (row r = lane%16,
+// kq = lane/16) holds dims j*32 + kq*8 .. +7 of landmark r; B = q^T, lane
+// (col g = lane%16, kq) holds the same dims of head g (zero for g >= G).
+// Output lane (g, kq) holds landmarks kq*4 .. kq*4+3 of head g.
 
-__device__ __forceinline__ bool sorted_contains(const int* v, int n, int x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (v[mid] < x) lo = mid + 1; else hi = mid;
-  }
-  return lo < n && v[lo] == x;
-}
-
-template <int G>
-__device__ __forceinline__ float pick(const float (&v)[G], int i) {
-  float r = v[0];
-#pragma unroll
-  for (int g = 1; g < G; g++) r = (i == g) ? v[g] : r;
-  return r;
-}
-
-constexpr int kScoreUnroll = 4;
+constexpr int kScoreTiles = 4;
 
 template <int G>
 __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
-  __shared__ float red[2][16][16];   // (m, s) per (wave, row) and head
+  __shared__ float red[2][16][16];   // (m, s) per (wave, kq) and head
   const int p = blockIdx.y, blk = blockIdx.x;
   const int b = p / a.n_kv, h = p % a.n_kv;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ds = lane & 15, tg = lane >> 4;
-  const int n_cand = a.n_cand;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, kq = lane >> 4;
   const int hq = a.n_kv * G;
 
-  float qv[G][8];
+  bf16x8 bq[4];
 #pragma unroll
-  for (int g = 0; g < G; g++) {
-    const u32x4 wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + h * G + g) * kHeadDim + ds * 8);
-    unpack8(wq, qv[g]);
-#pragma unroll
-    for (int i = 0; i < 8; i++) qv[g][i] *= a.scale;
+  for (int j = 0; j < 4; j++) {
+    u32x4 wq = {0u, 0u, 0u, 0u};
+    if (col < G)
+      wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + h * G + col) * kHeadDim + j * 32 + kq * 8);
+    bq[j] = __builtin_bit_cast(bf16x8, wq);
   }
-  const int c0 = blk * a.cpb, c1 = min(n_cand, c0 + a.cpb);
-  const uint16_t* Lp = a.L + (int64_t)p * n_cand * kHeadDim;
-  float* lg = a.logits + (int64_t)p * n_cand * G;
+  const int c0 = blk * a.cpb, c1 = min(a.n_cand, c0 + a.cpb);
+  const uint16_t* Lp = a.L + (int64_t)p * a.n_cand * kHeadDim;
+  float* lg = a.logits + ((int64_t)p * G + (col < G ? col : 0)) * a.ncp;
   float m_run = kNegBig, s_run = 0.f;
 
-  for (int base = c0; base < c1; base += 16 * kScoreUnroll) {
-    u32x4 wl[kScoreUnroll];
+  for (int base = c0 + w * 16 * kScoreTiles; base < c1; base += 4 * 16 * kScoreTiles) {
+    u32x4 al[kScoreTiles][4];
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; u++) {
-      const int c = base + u * 16 + w * 4 + tg;
-      wl[u] = (u32x4){0u, 0u, 0u, 0u};
-      if (c < c1) wl[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Lp + (int64_t)c * kHeadDim + ds * 8));
+    for (int t = 0; t < kScoreTiles; t++) {
+      const int row = base + t * 16 + col;
+      const uint16_t* src = Lp + (int64_t)row * kHeadDim + kq * 8;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        al[t][j] = (u32x4){0u, 0u, 0u, 0u};
+        if (row < c1) al[t][j] = *reinterpret_cast<const u32x4*>(src + j * 32);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kScoreUnroll; u++) {
-      const int c = base + u * 16 + w * 4 + tg;
-      float x[8];
-      unpack8(wl[u], x);
-      float l[G];
+    for (int t = 0; t < kScoreTiles; t++) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g = 0; g < G; g++) {
-        float part = 0.f;
+      for (int j = 0; j < 4; j++)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al[t][j]), bq[j], acc, 0, 0, 0);
+      const int cb = base + t * 16 + kq * 4;
+      if (col < G && cb < c1) {
+        float v[4];
 #pragma unroll
-        for (int i = 0; i < 8; i++) part = fmaf(qv[g][i], x[i], part);
-        l[g] = row16_sum(part);
-      }
-      if (c < c1 && ds < G) {
-        const float v = pick<G>(l, ds);
-        lg[(int64_t)c * G + ds] = v;
-        const float mn = fmaxf(m_run, v);
-        s_run = s_run * __expf(m_run - mn) + __expf(v - mn);
+        for (int i = 0; i < 4; i++) v[i] = acc[i] * a.scale;
+        if (cb + 4 <= c1) {
+          *reinterpret_cast<f32x4*>(lg + cb) = (f32x4){v[0], v[1], v[2], v[3]};
+        } else {
+          for (int i = 0; i < 4 && cb + i < c1; i++) lg[cb + i] = v[i];
+        }
+        float mx = v[0];
+#pragma unroll
+        for (int i = 1; i < 4; i++)
+          if (cb + i < c1) mx = fmaxf(mx, v[i]);
+        const float mn = fmaxf(m_run, mx);
+        float add = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          if (cb + i < c1) add += __expf(v[i] - mn);
+        s_run = s_run * __expf(m_run - mn) + add;
         m_run = mn;
       }
     }
   }
-  // per-workgroup (max, sum exp) of every head
-  if (ds < G) {
-    red[0][w * 4 + tg][ds] = m_run;
-    red[1][w * 4 + tg][ds] = s_run;
+  if (col < G) {
+    red[0][w * 4 + kq][col] = m_run;
+    red[1][w * 4 + kq][col] = s_run;
   }
   __syncthreads();
   if (threadIdx.x < G) {
@@ -134,90 +136,6 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
     float* dst = a.lse_part + (((int64_t)p * a.nb_score + blk) * G + threadIdx.x) * 2;
     dst[0] = M;
     dst[1] = S;
-  }
-}
-
-// One workgroup per pair: log-sum-exp of every head over all candidates, chunk
-// scores, top-K selection, then the temporal-cache index scan.
-constexpr int kSelThreads = 512;
-
-template <int G>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
-  extern __shared__ int smem[];
-  int* hist = smem;                 // 2048
-  int* sh = smem + 2048;            // 16
-  int* sel = smem + 2064;           // top_k
-  __shared__ float lse[16];
-  const int p = blockIdx.x;
-  const int n_cand = a.n_cand;
-  const float* lg = a.logits + (int64_t)p * n_cand * G;
-  if (threadIdx.x < G) {
-    const float* src = a.lse_part + (int64_t)p * a.nb_score * G * 2;
-    float M = kNegBig;
-    for (int k = 0; k < a.nb_score; k++) M = fmaxf(M, src[(k * G + threadIdx.x) * 2]);
-    float S = 0.f;
-    for (int k = 0; k < a.nb_score; k++)
-      S += src[(k * G + threadIdx.x) * 2 + 1] * __expf(src[(k * G + threadIdx.x) * 2] - M);
-    lse[threadIdx.x] = M + __logf(S);
-  }
-  __syncthreads();
-  uint32_t* kp = a.keys + (int64_t)p * n_cand;
-  for (int c = threadIdx.x; c < n_cand; c += kSelThreads) {
-    float best = -3.0e38f;
-#pragma unroll
-    for (int g = 0; g < G; g++) best = fmaxf(best, lg[(int64_t)c * G + g] - lse[g]);
-    kp[c] = float_key(best);
-  }
-  __syncthreads();
-  const int K = a.top_k;
-  block_topk<kSelThreads>([&](int i) { return kp[i]; }, n_cand, K, hist, sh,
-                          [&](int pos, int i) { if (pos < K) sel[pos] = i; });
-  const int32_t* cmap = a.cand_map + (int64_t)p * n_cand;
-  for (int i = threadIdx.x; i < K; i += kSelThreads) a.chunk_ids[(int64_t)p * K + i] = cmap[sel[i]];
-
-  // ---- temporal-cache index scan against the chunks held by the slots
-  int32_t* sc = a.slot_cand + (int64_t)p * K;
-  int32_t* sch = a.slot_chunk + (int64_t)p * K;
-  uint32_t* res = a.resident + (int64_t)p * a.res_words;
-  const bool has_prev = a.temporal && sc[0] >= 0;
-  int n_free = 0, n_miss = 0;
-  for (int t0 = 0; t0 < K; t0 += kSelThreads) {
-    const int s = t0 + threadIdx.x;
-    int fr = 0, ms = 0, ci = -1;
-    if (s < K) {
-      const int old = sc[s];
-      fr = !(has_prev && old >= 0 && sorted_contains(sel, K, old));
-      ci = sel[s];
-      ms = !(has_prev && ((res[ci >> 5] >> (ci & 31)) & 1u));
-    }
-    int tot;
-    const int ex = block_exclusive_scan<kSelThreads>(fr | (ms << 16), sh, &tot);
-    if (fr) a.free_slot[(int64_t)p * K + n_free + (ex & 0xffff)] = s;
-    if (ms) a.miss_cand[(int64_t)p * K + n_miss + (ex >> 16)] = ci;
-    n_free += tot & 0xffff;
-    n_miss += tot >> 16;
-  }
-  __syncthreads();
-  // n_free == n_miss: every missed chunk takes the next evicted slot
-  for (int j = threadIdx.x; j < n_miss; j += kSelThreads) {
-    const int slot = a.free_slot[(int64_t)p * K + j];
-    const int ci = a.miss_cand[(int64_t)p * K + j];
-    const int old = sc[slot];
-    if (old >= 0) atomicAnd(&res[old >> 5], ~(1u << (old & 31)));
-    atomicOr(&res[ci >> 5], 1u << (ci & 31));
-    const int ch = cmap[ci];
-    sc[slot] = ci;
-    sch[slot] = ch;
-    a.miss_slot[(int64_t)p * K + j] = slot;
-    a.miss_chunk[(int64_t)p * K + j] = ch;
-  }
-  if (threadIdx.x == 0) {
-    a.n_miss[p] = n_miss;
-    a.hits_last[p] = has_prev ? K - n_miss : 0;
-    if (has_prev) {
-      a.hits_total[p] += K - n_miss;
-      a.miss_total[p] += n_miss;
-    }
   }
 }
 
@@ -234,18 +152,174 @@ hipError_t launch_score(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
-  const size_t lds = (size_t)(2064 + a.top_k) * sizeof(int);
+// ---------------------------------------------------------------------------
+// Select + index scan, one workgroup of kSelThreads per pair.  All per-pair state
+// the scan touches (slot map, resident bitmap, miss / free lists) is staged in LDS;
+// the chunk keys too when they fit (select_lds_bytes decides), else they go to the
+// global key scratch.  LDS layout (ints): hist[2048] | sh[32] | sel[K] | selch[K] |
+// freel[K] | missp[K] | scl[K] | resl[res_words] | keys[n_cand].
+
+constexpr int kSelThreads = 1024;
+
+__device__ __forceinline__ bool sorted_contains(const int* v, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (v[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo < n && v[lo] == x;
+}
+
+size_t select_lds_bytes(int top_k, int res_words, int n_cand, bool keys_in_lds) {
+  return (size_t)(2048 + 32 + 5 * top_k + res_words + (keys_in_lds ? n_cand : 0)) * sizeof(int);
+}
+
+bool select_keys_in_lds(int top_k, int res_words, int n_cand) {
+  return select_lds_bytes(top_k, res_words, n_cand, true) <= kSelLdsMax;
+}
+
+template <int G, bool LDS_KEYS>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
+  extern __shared__ int smem[];
+  const int K = a.top_k, n_cand = a.n_cand, RW = a.res_words;
+  int* hist = smem;
+  int* sh = smem + 2048;
+  int* sel = sh + 32;        // selected candidate indices, ascending
+  int* selch = sel + K;      // their chunk ids
+  int* freel = selch + K;    // evicted slots, ascending
+  int* missp = freel + K;    // positions in sel of the missed chunks, ascending
+  int* scl = missp + K;      // slot -> candidate index (copy of the pair's slot map)
+  uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);   // resident bitmap copy
+  uint32_t* lkeys = resl + RW;
+  __shared__ float lse[16];
+  const int p = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float* lg = a.logits + (int64_t)p * G * a.ncp;
+  int32_t* sc = a.slot_cand + (int64_t)p * K;
+  int32_t* sch = a.slot_chunk + (int64_t)p * K;
+  uint32_t* res = a.resident + (int64_t)p * RW;
+  for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
+  for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
+
+  // chunk keys: max_g(logit_g - LSE_g); the first round of logit loads is in flight
+  // while the LSE of every head is reduced from the score workgroups' partials
+  uint32_t* kp = LDS_KEYS ? lkeys : a.keys + (int64_t)p * n_cand;
+  constexpr int R = (64 / G) < 16 ? (64 / G) : 16;
+  for (int c0 = 0; c0 < n_cand; c0 += R * kSelThreads) {
+    float lv[R][G];
+#pragma unroll
+    for (int u = 0; u < R; u++) {
+      const int c = c0 + u * kSelThreads + threadIdx.x;
+#pragma unroll
+      for (int g = 0; g < G; g++) lv[u][g] = c < n_cand ? lg[(int64_t)g * a.ncp + c] : 0.f;
+    }
+    if (c0 == 0) {
+      if (w < G) {
+        const float* src = a.lse_part + (int64_t)p * a.nb_score * G * 2;
+        float M = kNegBig;
+        for (int k = lane; k < a.nb_score; k += 64) M = fmaxf(M, src[(k * G + w) * 2]);
+        M = wave_max(M);
+        float S = 0.f;
+        for (int k = lane; k < a.nb_score; k += 64) S += src[(k * G + w) * 2 + 1] * __expf(src[(k * G + w) * 2] - M);
+        S = wave_sum(S);
+        if (lane == 0) lse[w] = M + __logf(S);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < R; u++) {
+      const int c = c0 + u * kSelThreads + threadIdx.x;
+      float best = lv[u][0] - lse[0];
+#pragma unroll
+      for (int g = 1; g < G; g++) best = fmaxf(best, lv[u][g] - lse[g]);
+      if (c < n_cand) kp[c] = float_key(best);
+    }
+  }
+  __syncthreads();
+  block_topk<kSelThreads>([&](int i) { return kp[i]; }, n_cand, K, hist, sh,
+                          [&](int pos, int i) { if (pos < K) sel[pos] = i; });
+  const int32_t* cmap = a.cand_map + (int64_t)p * n_cand;
+  for (int i = threadIdx.x; i < K; i += kSelThreads) {
+    const int ch = cmap[sel[i]];
+    selch[i] = ch;
+    a.chunk_ids[(int64_t)p * K + i] = ch;
+  }
+
+  // ---- temporal-cache index scan against the chunks held by the slots
+  const bool has_prev = a.temporal && scl[0] >= 0;
+  int n_free = 0, n_miss = 0;
+  for (int t0 = 0; t0 < K; t0 += kSelThreads) {
+    const int s = t0 + threadIdx.x;
+    int fr = 0, ms = 0;
+    if (s < K) {
+      const int old = scl[s];
+      fr = !(has_prev && old >= 0 && sorted_contains(sel, K, old));
+      const int ci = sel[s];
+      ms = !(has_prev && ((resl[ci >> 5] >> (ci & 31)) & 1u));
+    }
+    int tot;
+    const int ex = block_exclusive_scan<kSelThreads>(fr | (ms << 16), sh, &tot);
+    if (fr) freel[n_free + (ex & 0xffff)] = s;
+    if (ms) missp[n_miss + (ex >> 16)] = s;
+    n_free += tot & 0xffff;
+    n_miss += tot >> 16;
+  }
+  __syncthreads();
+  // n_free == n_miss: every missed chunk takes the next evicted slot
+  for (int j = threadIdx.x; j < n_miss; j += kSelThreads) {
+    const int slot = freel[j];
+    const int ci = sel[missp[j]], ch = selch[missp[j]];
+    const int old = scl[slot];
+    if (old >= 0) atomicAnd(&resl[old >> 5], ~(1u << (old & 31)));
+    atomicOr(&resl[ci >> 5], 1u << (ci & 31));
+    sc[slot] = ci;
+    sch[slot] = ch;
+    a.miss_slot[(int64_t)p * K + j] = slot;
+    a.miss_chunk[(int64_t)p * K + j] = ch;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < RW; i += kSelThreads) res[i] = resl[i];
+  if (threadIdx.x == 0) {
+    a.n_miss[p] = n_miss;
+    a.hits_last[p] = has_prev ? K - n_miss : 0;
+    if (has_prev) {
+      a.hits_total[p] += K - n_miss;
+      a.miss_total[p] += n_miss;
+    }
+  }
+}
+
+template <int G>
+static hipError_t launch_select_g(const DecodeArgs& a, hipStream_t st) {
   const int P = a.batch * a.n_kv;
+  const bool lds_keys = select_keys_in_lds(a.top_k, a.res_words, a.n_cand);
+  const size_t lds = select_lds_bytes(a.top_k, a.res_words, a.n_cand, lds_keys);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<G, true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSelLdsMax);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<G, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kSelLdsMax);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  if (lds_keys)
+    select_kernel<G, true><<<P, kSelThreads, lds, st>>>(a);
+  else
+    select_kernel<G, false><<<P, kSelThreads, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
   switch (a.group) {
-    case 1: select_kernel<1><<<P, kSelThreads, lds, st>>>(a); break;
-    case 2: select_kernel<2><<<P, kSelThreads, lds, st>>>(a); break;
-    case 4: select_kernel<4><<<P, kSelThreads, lds, st>>>(a); break;
-    case 8: select_kernel<8><<<P, kSelThreads, lds, st>>>(a); break;
-    case 16: select_kernel<16><<<P, kSelThreads, lds, st>>>(a); break;
+    case 1: return launch_select_g<1>(a, st);
+    case 2: return launch_select_g<2>(a, st);
+    case 4: return launch_select_g<4>(a, st);
+    case 8: return launch_select_g<8>(a, st);
+    case 16: return launch_select_g<16>(a, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -253,7 +327,7 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
 // rows, N = d = 128 as 8 MFMA column tiles; B^T slices of 128 k staged in LDS.
 
 constexpr int kRebuildRows = 128;
-constexpr int kKSlice = 128;
+constexpr int kKSlice = 192;
 constexpr int kLdsW = kKSlice + 8;
 
 template <int C>
@@ -270,18 +344,16 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
   const int lr = lane & 15, lk = lane >> 4;
   const uint16_t* Bt = a.Bt + ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
 
+  __shared__ int mchunk[kRebuildRows / 4];
+  for (int i = threadIdx.x; i < MPB; i += 256) mchunk[i] = j0 + i < n ? a.miss_chunk[(int64_t)p * K + j0 + i] : -1;
+  __syncthreads();
   // A operand rows of this lane: row m = w*32 + mt*16 + lr
   const uint16_t* arow[2];
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     const int m = w * 32 + mt * 16 + lr;
-    const int jm = j0 + m / C;
-    arow[mt] = nullptr;
-    if (jm < n) {
-      const int ch = a.miss_chunk[(int64_t)p * K + jm];
-      const int64_t pos = (int64_t)ch * C + (m % C);
-      arow[mt] = a.A + ((int64_t)b * a.seq_len + pos) * r;
-    }
+    const int ch = mchunk[m / C];
+    arow[mt] = ch >= 0 ? a.A + ((int64_t)b * a.seq_len + (int64_t)ch * C + (m % C)) * r : nullptr;
   }
   f32x4 acc[2][8];
 #pragma unroll
@@ -291,6 +363,17 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
 
   for (int ks = 0; ks < r; ks += kKSlice) {
     const int kn = min(kKSlice, r - ks);
+    // this slice's A fragments are in flight while B^T is staged
+    u32x4 af[kKSlice / 32][2];
+#pragma unroll
+    for (int q = 0; q < kKSlice / 32; q++) {
+      const int kof = q * 32 + lk * 8;
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        af[q][mt] = (u32x4){0u, 0u, 0u, 0u};
+        if (kof < kn && arow[mt]) af[q][mt] = *reinterpret_cast<const u32x4*>(arow[mt] + ks + kof);
+      }
+    }
     __syncthreads();
     const int per_row = kn / 8;
     for (int e = threadIdx.x; e < 128 * per_row; e += 256) {
@@ -299,16 +382,11 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
           *reinterpret_cast<const u32x4*>(Bt + (int64_t)nr * r + ks + k8);
     }
     __syncthreads();
-    for (int kk = 0; kk < kn; kk += 32) {
-      const int kof = kk + lk * 8;
-      const bool kin = kof < kn;
-      bf16x8 af[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; mt++) {
-        u32x4 wv = {0u, 0u, 0u, 0u};
-        if (kin && arow[mt]) wv = *reinterpret_cast<const u32x4*>(arow[mt] + ks + kof);
-        af[mt] = __builtin_bit_cast(bf16x8, wv);
-      }
+    for (int q = 0; q < kKSlice / 32; q++) {
+      const int kof = q * 32 + lk * 8;
+      if (q * 32 >= kn) break;
+      const bool kin = kof < kn;
 #pragma unroll
       for (int nt = 0; nt < 8; nt++) {
         u32x4 wb = {0u, 0u, 0u, 0u};
@@ -316,28 +394,32 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
         const bf16x8 bfr = __builtin_bit_cast(bf16x8, wb);
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr, acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[q][mt]), bfr,
+                                                                acc[mt][nt], 0, 0, 0);
       }
     }
   }
   __syncthreads();
-  // epilogue: RoPE on (col, col + 64) pairs, stage bf16 rows in LDS
+  // epilogue: RoPE on (col, col + 64) pairs, stage bf16 rows in LDS.  A lane's four
+  // rows lk*4 .. lk*4+3 of a tile are consecutive positions of one chunk, so the
+  // float64 angle reduction runs once per (tile, column) and the rows add j * f.
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
+    const int m0 = w * 32 + mt * 16 + lk * 4;
+    const int ch = max(mchunk[m0 / C], 0);
+    const int64_t pos0 = (int64_t)ch * C + (m0 % C);
 #pragma unroll
-    for (int jj = 0; jj < 4; jj++) {
-      const int m = w * 32 + mt * 16 + lk * 4 + jj;
-      const int jm = j0 + m / C;
-      const int ch = jm < n ? a.miss_chunk[(int64_t)p * K + jm] : 0;
-      const int64_t pos = (int64_t)ch * C + (m % C);
+    for (int nt = 0; nt < 4; nt++) {
+      const int col = nt * 16 + lr;
+      const double f = a.inv_freq[col];
+      const float a0 = rope_angle(pos0, f), ff = (float)f;
 #pragma unroll
-      for (int nt = 0; nt < 4; nt++) {
-        const int col = nt * 16 + lr;
+      for (int jj = 0; jj < 4; jj++) {
         float c, s;
-        rope_cs(pos, a.inv_freq[col], &c, &s);
+        __sincosf(a0 + jj * ff, &s, &c);
         const float x1 = acc[mt][nt][jj], x2 = acc[mt][nt + 4][jj];
-        tile[m * kLdsW + col] = f32_to_bf16(x1 * c - x2 * s);
-        tile[m * kLdsW + col + 64] = f32_to_bf16(x2 * c + x1 * s);
+        tile[(m0 + jj) * kLdsW + col] = f32_to_bf16(x1 * c - x2 * s);
+        tile[(m0 + jj) * kLdsW + col + 64] = f32_to_bf16(x2 * c + x1 * s);
       }
     }
   }
@@ -398,10 +480,12 @@ hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Split-K flash-decode.  Work unit = one chunk of C tokens: unit u < O is an
 // outlier chunk, O <= u < O+K the chunk held by slot u-O, the rest the window.
-// Lane (ds, tg): dims 8*ds..8*ds+7 of the tokens tg, tg+4, ... of a unit.
+// Lane (ds, tg): dims 8*ds..8*ds+7 of tokens tg, tg+4, ... of a unit.  Wave w of
+// a workgroup takes units u0+w, u0+w+4, ...; two units are processed while the
+// next two are fetched.
 
 template <int C>
-__device__ __forceinline__ void unit_ptrs(const DecodeArgs& a, int p, int b, int h, int u,
+__device__ __forceinline__ void unit_ptrs(const DecodeArgs& a, int p, int b, int h, int u, int ch,
                                           const uint16_t** kp, const uint16_t** vp) {
   const int O = a.n_outlier, K = a.top_k;
   if (u < O) {
@@ -409,18 +493,12 @@ __device__ __forceinline__ void unit_ptrs(const DecodeArgs& a, int p, int b, int
     *kp = a.k_out + off;
     *vp = a.v_out + off;
   } else if (u < O + K) {
-    const int s = u - O;
-    const int64_t off = ((int64_t)p * K + s) * C * kHeadDim;
+    const int64_t off = ((int64_t)p * K + (u - O)) * C * kHeadDim;
     *kp = a.key_slots + off;
-    if (a.host_values) {
-      *vp = a.val_slots + off;
-    } else {
-      const int ch = max(a.slot_chunk[(int64_t)p * K + s], 0);
-      *vp = a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * C) * kHeadDim;
-    }
+    *vp = a.host_values ? a.val_slots + off
+                        : a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * C) * kHeadDim;
   } else {
-    const int wu = u - O - K;
-    const int64_t off = ((int64_t)p * a.n_win_units + wu) * C * kHeadDim;
+    const int64_t off = ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
     *kp = a.k_win + off;
     *vp = a.v_win + off;
   }
@@ -431,12 +509,18 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   constexpr int TPR = C / 4;   // tokens of a unit per lane row
   __shared__ float wo[4][G][kHeadDim];
   __shared__ float wm[4][G], wl[4][G];
+  __shared__ int uch[kMaxUnitsPerSplit];
   const int p = blockIdx.y, split = blockIdx.x;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ds = lane & 15, tg = lane >> 4;
   const int U = a.n_outlier + a.top_k + a.n_win_units;
   const int u0 = split * a.upw, u1 = min(U, u0 + a.upw);
   const int hq = a.n_kv * G;
+  // chunk ids of the selected units of this split (no dependent load in the loop)
+  for (int i = threadIdx.x; i < u1 - u0; i += 256) {
+    const int s = u0 + i - a.n_outlier;
+    uch[i] = (s >= 0 && s < a.top_k) ? max(a.slot_chunk[(int64_t)p * a.top_k + s], 0) : 0;
+  }
 
   float qv[G][8];
 #pragma unroll
@@ -454,41 +538,38 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; i++) o[g][i] = 0.f;
   }
-  u32x4 kw[TPR], vw[TPR];
-  int u = u0 + w;
-  auto load = [&](int uu, u32x4* kd, u32x4* vd) {
+  __syncthreads();
+  const int nu = (u1 - u0 > w) ? (u1 - u0 - w + 3) / 4 : 0;   // units of this wave
+  auto load = [&](int i, u32x4* kd, u32x4* vd) {
+    if (i >= nu) return;
+    const int li = w + 4 * i;
     const uint16_t *kp, *vp;
-    unit_ptrs<C>(a, p, b, h, uu, &kp, &vp);
+    unit_ptrs<C>(a, p, b, h, u0 + li, uch[li], &kp, &vp);
 #pragma unroll
-    for (int i = 0; i < TPR; i++) {
-      const int t = tg + 4 * i;
-      kd[i] = *reinterpret_cast<const u32x4*>(kp + t * kHeadDim + ds * 8);
-      vd[i] = *reinterpret_cast<const u32x4*>(vp + t * kHeadDim + ds * 8);
+    for (int t = 0; t < TPR; t++) {
+      kd[t] = *reinterpret_cast<const u32x4*>(kp + (tg + 4 * t) * kHeadDim + ds * 8);
+      vd[t] = *reinterpret_cast<const u32x4*>(vp + (tg + 4 * t) * kHeadDim + ds * 8);
     }
   };
-  if (u < u1) load(u, kw, vw);
-  while (u < u1) {
-    const int un = u + 4;
-    u32x4 nk[TPR], nv[TPR];
-    if (un < u1) load(un, nk, nv);
+  auto process = [&](const u32x4* kd, const u32x4* vd) {
     float s[TPR][G];
 #pragma unroll
-    for (int i = 0; i < TPR; i++) {
+    for (int t = 0; t < TPR; t++) {
       float x[8];
-      unpack8(kw[i], x);
+      unpack8(kd[t], x);
 #pragma unroll
       for (int g = 0; g < G; g++) {
         float part = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; k++) part = fmaf(qv[g][k], x[k], part);
-        s[i][g] = row16_sum(part);
+        s[t][g] = row16_sum(part);
       }
     }
 #pragma unroll
     for (int g = 0; g < G; g++) {
       float mx = s[0][g];
 #pragma unroll
-      for (int i = 1; i < TPR; i++) mx = fmaxf(mx, s[i][g]);
+      for (int t = 1; t < TPR; t++) mx = fmaxf(mx, s[t][g]);
       const float mn = fmaxf(m[g], mx);
       const float corr = exp2f(m[g] - mn);
       m[g] = mn;
@@ -497,23 +578,34 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
       for (int k = 0; k < 8; k++) o[g][k] *= corr;
     }
 #pragma unroll
-    for (int i = 0; i < TPR; i++) {
+    for (int t = 0; t < TPR; t++) {
       float y[8];
-      unpack8(vw[i], y);
+      unpack8(vd[t], y);
 #pragma unroll
       for (int g = 0; g < G; g++) {
-        const float pr = exp2f(s[i][g] - m[g]);
+        const float pr = exp2f(s[t][g] - m[g]);
         l[g] += pr;
 #pragma unroll
         for (int k = 0; k < 8; k++) o[g][k] = fmaf(pr, y[k], o[g][k]);
       }
     }
+  };
+  u32x4 k0[TPR], v0[TPR], k1[TPR], v1[TPR];
+  load(0, k0, v0);
+  load(1, k1, v1);
+  for (int i = 0; i < nu; i += 2) {
+    u32x4 nk0[TPR], nv0[TPR], nk1[TPR], nv1[TPR];
+    load(i + 2, nk0, nv0);
+    load(i + 3, nk1, nv1);
+    process(k0, v0);
+    if (i + 1 < nu) process(k1, v1);
 #pragma unroll
-    for (int i = 0; i < TPR; i++) {
-      kw[i] = nk[i];
-      vw[i] = nv[i];
+    for (int t = 0; t < TPR; t++) {
+      k0[t] = nk0[t];
+      v0[t] = nv0[t];
+      k1[t] = nk1[t];
+      v1[t] = nv1[t];
     }
-    u = un;
   }
   // merge the four token rows of the wave (lanes ds, ds+16, ds+32, ds+48)
 #pragma unroll
@@ -565,26 +657,43 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the split partials of one pair: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Merge the split partials of one (pair, head):
+// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 template <int G>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-  const int p = blockIdx.x;
+__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
+  __shared__ float cw[kMaxSplits];
+  __shared__ float den_sh;
+  const int g = blockIdx.x, p = blockIdx.y;
   const int b = p / a.n_kv, h = p % a.n_kv;
-  const int hq = a.n_kv * G;
-  const float* allp = a.attn_part + (int64_t)p * a.n_split * G * (kHeadDim + 2);
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
-    const int g = idx / kHeadDim, dim = idx % kHeadDim;
+  const int ns = a.n_split;
+  const int64_t stride = (int64_t)G * (kHeadDim + 2);
+  const float* base = a.attn_part + (int64_t)p * ns * stride + g * (kHeadDim + 2);
+  for (int s = threadIdx.x; s < ns; s += 128) cw[s] = base[s * stride + kHeadDim];
+  __syncthreads();
+  if (threadIdx.x < 64) {   // wave 0: split weights 2^(m_s - M) and the denominator
     float M = kNegBig;
-    for (int sp = 0; sp < a.n_split; sp++) M = fmaxf(M, allp[(sp * G + g) * (kHeadDim + 2) + kHeadDim]);
-    float num = 0.f, den = 0.f;
-    for (int sp = 0; sp < a.n_split; sp++) {
-      const float* ps = allp + (sp * G + g) * (kHeadDim + 2);
-      const float c = exp2f(ps[kHeadDim] - M);
-      num += ps[dim] * c;
-      den += ps[kHeadDim + 1] * c;
+    for (int s = threadIdx.x; s < ns; s += 64) M = fmaxf(M, cw[s]);
+    M = wave_max(M);
+    float den = 0.f;
+    for (int s = threadIdx.x; s < ns; s += 64) {
+      const float c = exp2f(cw[s] - M);
+      den += base[s * stride + kHeadDim + 1] * c;
+      cw[s] = c;
     }
-    a.out[((int64_t)b * hq + h * G + g) * kHeadDim + dim] = num / den;
+    den = wave_sum(den);
+    if (threadIdx.x == 0) den_sh = den;
   }
+  __syncthreads();
+  const int dim = threadIdx.x;
+  float num = 0.f;
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+    const float x0 = base[(s + 0) * stride + dim], x1 = base[(s + 1) * stride + dim];
+    const float x2 = base[(s + 2) * stride + dim], x3 = base[(s + 3) * stride + dim];
+    num += x0 * cw[s] + x1 * cw[s + 1] + x2 * cw[s + 2] + x3 * cw[s + 3];
+  }
+  for (; s < ns; s++) num += base[s * stride + dim] * cw[s];
+  a.out[((int64_t)b * a.n_kv * G + h * G + g) * kHeadDim + dim] = num / den_sh;
 }
 
 template <int G>
@@ -598,7 +707,7 @@ static hipError_t launch_attn_g(const DecodeArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<G><<<a.batch * a.n_kv, 256, 0, st>>>(a);
+  combine_kernel<G><<<dim3(G, a.batch * a.n_kv), 128, 0, st>>>(a);
   return hipGetLastError();
 }
 

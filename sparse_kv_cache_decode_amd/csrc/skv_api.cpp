@@ -17,7 +17,7 @@ using namespace skv;
 struct skv_layer {
   skv_config cfg;
   int G = 0, n_c = 0, n_win = 0, n_cand = 0, P = 0, HD = 0, U = 0;
-  int nb_score = 0, cpb = 0, n_split = 0, upw = 0, res_words = 0;
+  int nb_score = 0, cpb = 0, ncp = 0, n_split = 0, upw = 0, res_words = 0;
   bool poisoned = false;
   bool need_reset = false;
   const uint16_t* v_dev = nullptr;   // device-visible address of the value store
@@ -157,6 +157,7 @@ DecodeArgs decode_args(skv_layer* h) {
   a.seq_len = c.seq_len;
   a.nb_score = h->nb_score;
   a.cpb = h->cpb;
+  a.ncp = h->ncp;
   a.n_split = h->n_split;
   a.upw = h->upw;
   a.temporal = c.temporal_cache;
@@ -253,13 +254,17 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   h->v_dev = v_dev;
   const int P = h->P, G = h->G, n_c = h->n_c, n_cand = h->n_cand, HD = h->HD;
   {
-    int nb = (2048 + P - 1) / P;
-    nb = std::max(1, std::min(nb, (n_cand + 63) / 64));
-    h->cpb = (n_cand + nb - 1) / nb;
+    // score: 256 landmarks (4 waves x 4 tiles x 16) per workgroup, i.e. one
+    // 64 KB landmark block each; a larger grid beats longer per-workgroup loops
+    h->cpb = 256;
     h->nb_score = (n_cand + h->cpb - 1) / h->cpb;
+    h->ncp = (n_cand + 3) / 4 * 4;
+    // attention: ~2048 workgroups, units per workgroup a multiple of 8 (2 per wave)
     int ns = (2048 + P - 1) / P;
     ns = std::max(1, std::min(ns, h->U));
-    h->upw = (h->U + ns - 1) / ns;
+    h->upw = ((h->U + ns - 1) / ns + 7) / 8 * 8;
+    h->upw = std::min(h->upw, kMaxUnitsPerSplit);
+    if ((int64_t)h->upw * kMaxSplits < h->U) h->upw = kMaxUnitsPerSplit;
     h->n_split = (h->U + h->upw - 1) / h->upw;
   }
 
@@ -288,7 +293,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const size_t oKeys = cv.take<uint32_t>((size_t)P * n_c);
   const size_t oHt = cv.take<long long>(P);
   const size_t oMt = cv.take<long long>(P);
-  const size_t oLg = cv.take<float>((size_t)P * n_cand * G);
+  const size_t oLg = cv.take<float>((size_t)P * G * h->ncp);
   const size_t oLp = cv.take<float>((size_t)P * h->nb_score * G * 2);
   const size_t oAp = cv.take<float>((size_t)P * h->n_split * G * (kHeadDim + 2));
   const size_t oMc = cv.take<float>((size_t)P * n_c);

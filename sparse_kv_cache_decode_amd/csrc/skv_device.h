@@ -49,6 +49,16 @@ __device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq, float* c, 
   __sincosf((float)r, s, c);
 }
 
+// pos * inv_freq reduced to [-pi, pi] in float64, returned as float.
+__device__ __forceinline__ float rope_angle(int64_t pos, double inv_freq) {
+  const double two_pi_hi = 6.283185307179586;
+  const double two_pi_lo = 2.4492935982947064e-16;
+  double a = (double)pos * inv_freq;
+  double n = rint(a * 0.15915494309189535);
+  double r = fma(-n, two_pi_hi, a);
+  return (float)fma(-n, two_pi_lo, r);
+}
+
 // ---------------------------------------------------------------- cross-lane
 
 // DPP controls (gfx9 encoding).

@@ -9,12 +9,16 @@ namespace skv {
 
 constexpr int kHeadDim = 128;
 constexpr int kMaxTopK = 4096;
+constexpr int kSelLdsMax = 150 * 1024;   // dynamic LDS of the select kernel
+constexpr int kMaxUnitsPerSplit = 256;   // attention units (chunks) per workgroup
+constexpr int kMaxSplits = 1024;         // attention workgroups per pair
 
 // Everything a decode step touches, by value into the kernels.
 struct DecodeArgs {
   int batch, n_kv, group, chunk, top_k, n_outlier, n_win_units, n_cand;
   int64_t seq_len;
   int nb_score, cpb;          // score workgroups per pair, candidates per workgroup
+  int ncp;                    // logits row stride (n_cand rounded up to 4)
   int n_split, upw;           // attention workgroups per pair, units per workgroup
   int temporal, host_values;
   float scale;                // 1/sqrt(d)
@@ -47,7 +51,7 @@ struct DecodeArgs {
   long long* hits_total;      // [P]
   long long* miss_total;      // [P]
   // scratch
-  float* logits;              // [P][n_cand][G]
+  float* logits;              // [P][G][ncp]
   float* lse_part;            // [P][nb_score][G][2]
   uint32_t* keys;             // [P][n_cand]
   float* attn_part;           // [P][n_split][G][d + 2]
@@ -80,6 +84,8 @@ hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_
 hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_score(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
+size_t select_lds_bytes(int top_k, int res_words, int n_cand, bool keys_in_lds);
+bool select_keys_in_lds(int top_k, int res_words, int n_cand);
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);

@@ -3,8 +3,13 @@
 Bars (floating point from bf16 storage with fp32 accumulation):
 * selected chunk ids bit-exact, except chunks whose oracle score S2 lies within
   1e-3 relative of the oracle's K-th score (near ties may swap);
-* attention outputs: max |err| <= 2e-2 and relative L2 <= 5e-3;
-* hit counts exact whenever the selections agree.
+* attention outputs: max |err| <= 2e-2 and relative L2 <= 5e-3, against the
+  oracle's output for its own selection; for a pair whose selection swapped a
+  near tie (several selections are then correct), against the oracle's exact
+  attention over the selection the GPU made, once that selection has passed the
+  tie rule;
+* hit counts exact against the oracle whenever the selections agree, and always
+  equal to |I_t & I_{t-1}| of the GPU's own consecutive selections.
 """
 from __future__ import annotations
 
@@ -23,11 +28,11 @@ def bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def check_ids(gpu_ids: np.ndarray, st: O.State, res: O.StepResult) -> int:
-    """Assert the tie rule per pair; returns how many pairs differ at all."""
+def check_ids(gpu_ids: np.ndarray, st: O.State, res: O.StepResult) -> list:
+    """Assert the tie rule per pair; returns the pairs (b, h) whose ids differ."""
     cfg = st.cfg
     K = cfg.top_k
-    differ = 0
+    differ = []
     for b in range(cfg.batch):
         for h in range(cfg.n_kv_heads):
             g = gpu_ids[b, h]
@@ -35,7 +40,7 @@ def check_ids(gpu_ids: np.ndarray, st: O.State, res: O.StepResult) -> int:
             o = res.ids[b, h]
             if np.array_equal(g, o):
                 continue
-            differ += 1
+            differ.append((b, h))
             cand = st.cand[b, h]
             pos = np.searchsorted(cand, g)
             assert np.all(pos < len(cand)) and np.array_equal(cand[np.minimum(pos, len(cand) - 1)], g), \
@@ -47,6 +52,16 @@ def check_ids(gpu_ids: np.ndarray, st: O.State, res: O.StepResult) -> int:
                 assert abs(sc - kth) <= TIE_REL * kth, \
                     f"pair ({b},{h}) chunk {c}: score {sc} vs K-th {kth} is not a near tie"
     return differ
+
+
+def reference_out(st: O.State, q_bits, res: O.StepResult, gpu_ids: np.ndarray, differ: list):
+    """Oracle outputs, with tie-swapped pairs recomputed over the GPU's selection."""
+    ref = res.out.copy()
+    q = O.bf16_bits_to_f64(q_bits)
+    G = st.cfg.group
+    for b, h in differ:
+        ref[b, h * G:(h + 1) * G] = O.pair_output(st, q[b], b, h, gpu_ids[b, h].astype(np.int64))
+    return ref
 
 
 def check_out(gpu_out: np.ndarray, ref: np.ndarray, max_abs=MAX_ABS, rel_l2=REL_L2):
@@ -62,6 +77,8 @@ def bf16_close(gpu_bits: np.ndarray, ref: np.ndarray, slack: float) -> float:
     slack (fp32 arithmetic on O(1) values can land on either side of a rounding
     boundary, and cancellation makes tiny results inexact in absolute terms).
     Returns max(|gpu - ref| - spacing(ref) - slack); <= 0 passes."""
+    if ref.size == 0:
+        return -np.inf
     g = O.bf16_bits_to_f64(gpu_bits)
     _, e = np.frexp(ref)
     spacing = np.where(ref == 0, 0.0, np.ldexp(1.0, e - 8))
