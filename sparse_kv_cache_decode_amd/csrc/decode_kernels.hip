@@ -334,18 +334,47 @@ template <int C>
 __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kLdsW];
+  __shared__ int mchunk[kRebuildRows / 4], mslot[kRebuildRows / 4];
   const int p = blockIdx.y;
   const int j0 = blockIdx.x * MPB;
-  const int n = a.n_miss[p];
-  if (j0 >= n) return;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int K = a.top_k, r = a.rank;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lk = lane >> 4;
   const uint16_t* Bt = a.Bt + ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
-
-  __shared__ int mchunk[kRebuildRows / 4];
-  for (int i = threadIdx.x; i < MPB; i += 256) mchunk[i] = j0 + i < n ? a.miss_chunk[(int64_t)p * K + j0 + i] : -1;
+  const bool single_slice = r <= kKSlice;
+  // B^T of the pair does not depend on the misses: its loads go out with n_miss
+  u32x4 bpre[(128 * kKSlice / 8 + 255) / 256];
+  constexpr int kBPieces = (128 * kKSlice / 8 + 255) / 256;
+  const int per_row0 = min(r, kKSlice) / 8;
+  if (single_slice) {
+#pragma unroll
+    for (int q = 0; q < kBPieces; q++) {
+      const int e = threadIdx.x + q * 256;
+      bpre[q] = (u32x4){0u, 0u, 0u, 0u};
+      if (e < 128 * per_row0) {
+        const int nr = e / per_row0, k8 = (e % per_row0) * 8;
+        bpre[q] = *reinterpret_cast<const u32x4*>(Bt + (int64_t)nr * r + k8);
+      }
+    }
+  }
+  const int n = a.n_miss[p];
+  if (j0 >= n) return;
+  for (int i = threadIdx.x; i < MPB; i += 256) {
+    const bool ok = j0 + i < n;
+    mchunk[i] = ok ? a.miss_chunk[(int64_t)p * K + j0 + i] : -1;
+    mslot[i] = ok ? a.miss_slot[(int64_t)p * K + j0 + i] : -1;
+  }
+  if (single_slice) {
+#pragma unroll
+    for (int q = 0; q < kBPieces; q++) {
+      const int e = threadIdx.x + q * 256;
+      if (e < 128 * per_row0) {
+        const int nr = e / per_row0, k8 = (e % per_row0) * 8;
+        *reinterpret_cast<u32x4*>(&tile[nr * kLdsW + k8]) = bpre[q];
+      }
+    }
+  }
   __syncthreads();
   // A operand rows of this lane: row m = w*32 + mt*16 + lr
   const uint16_t* arow[2];
@@ -363,7 +392,6 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
 
   for (int ks = 0; ks < r; ks += kKSlice) {
     const int kn = min(kKSlice, r - ks);
-    // this slice's A fragments are in flight while B^T is staged
     u32x4 af[kKSlice / 32][2];
 #pragma unroll
     for (int q = 0; q < kKSlice / 32; q++) {
@@ -374,14 +402,16 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
         if (kof < kn && arow[mt]) af[q][mt] = *reinterpret_cast<const u32x4*>(arow[mt] + ks + kof);
       }
     }
-    __syncthreads();
-    const int per_row = kn / 8;
-    for (int e = threadIdx.x; e < 128 * per_row; e += 256) {
-      const int nr = e / per_row, k8 = (e % per_row) * 8;
-      *reinterpret_cast<u32x4*>(&tile[nr * kLdsW + k8]) =
-          *reinterpret_cast<const u32x4*>(Bt + (int64_t)nr * r + ks + k8);
+    if (!single_slice) {
+      __syncthreads();
+      const int per_row = kn / 8;
+      for (int e = threadIdx.x; e < 128 * per_row; e += 256) {
+        const int nr = e / per_row, k8 = (e % per_row) * 8;
+        *reinterpret_cast<u32x4*>(&tile[nr * kLdsW + k8]) =
+            *reinterpret_cast<const u32x4*>(Bt + (int64_t)nr * r + ks + k8);
+      }
+      __syncthreads();
     }
-    __syncthreads();
 #pragma unroll
     for (int q = 0; q < kKSlice / 32; q++) {
       const int kof = q * 32 + lk * 8;
@@ -426,9 +456,8 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
   __syncthreads();
   for (int e = threadIdx.x; e < kRebuildRows * 16; e += 256) {
     const int m = e >> 4, piece = e & 15;
-    const int jm = j0 + m / C;
-    if (jm >= n) continue;
-    const int slot = a.miss_slot[(int64_t)p * K + jm];
+    const int slot = mslot[m / C];
+    if (slot < 0) continue;
     uint16_t* dst = a.key_slots + (((int64_t)p * K + slot) * C + (m % C)) * kHeadDim + piece * 8;
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&tile[m * kLdsW + piece * 8]);
   }
@@ -480,55 +509,85 @@ hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Split-K flash-decode.  Work unit = one chunk of C tokens: unit u < O is an
 // outlier chunk, O <= u < O+K the chunk held by slot u-O, the rest the window.
-// Lane (ds, tg): dims 8*ds..8*ds+7 of tokens tg, tg+4, ... of a unit.  Wave w of
-// a workgroup takes units u0+w, u0+w+4, ...; two units are processed while the
-// next two are fetched.
+// Each wave owns up to NUW consecutive units and issues every K/V load of them
+// before computing (K first: key addresses need no chunk id), so a workgroup has
+// 4*NUW chunks in flight.  Lane (ds, tg) holds dims 8*ds..8*ds+7 of the tokens
+// tg, tg+4, ... of a unit; a logit is a 16-lane DPP sum, the softmax is online
+// in fp32 (base 2), and the four waves merge through LDS.
 
-template <int C>
-__device__ __forceinline__ void unit_ptrs(const DecodeArgs& a, int p, int b, int h, int u, int ch,
-                                          const uint16_t** kp, const uint16_t** vp) {
-  const int O = a.n_outlier, K = a.top_k;
-  if (u < O) {
-    const int64_t off = ((int64_t)p * O + u) * C * kHeadDim;
-    *kp = a.k_out + off;
-    *vp = a.v_out + off;
-  } else if (u < O + K) {
-    const int64_t off = ((int64_t)p * K + (u - O)) * C * kHeadDim;
-    *kp = a.key_slots + off;
-    *vp = a.host_values ? a.val_slots + off
-                        : a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * C) * kHeadDim;
-  } else {
-    const int64_t off = ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
-    *kp = a.k_win + off;
-    *vp = a.v_win + off;
-  }
+template <int G, int C>
+struct AttnShape {
+  static constexpr int TPR = C / 4;                        // tokens per lane row
+  static constexpr int LOADS = G <= 4 ? 32 : 16;           // 16-B K/V loads per lane
+  static constexpr int NUW = LOADS / (2 * TPR);            // units per wave
+};
+
+int attn_units_per_wave(int group, int chunk) {
+  const int loads = group <= 4 ? 32 : 16;
+  return loads / (2 * (chunk / 4));
 }
 
 template <int G, int C>
 __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
-  constexpr int TPR = C / 4;   // tokens of a unit per lane row
+  constexpr int TPR = AttnShape<G, C>::TPR;
+  constexpr int NUW = AttnShape<G, C>::NUW;
   __shared__ float wo[4][G][kHeadDim];
   __shared__ float wm[4][G], wl[4][G];
-  __shared__ int uch[kMaxUnitsPerSplit];
   const int p = blockIdx.y, split = blockIdx.x;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ds = lane & 15, tg = lane >> 4;
-  const int U = a.n_outlier + a.top_k + a.n_win_units;
-  const int u0 = split * a.upw, u1 = min(U, u0 + a.upw);
+  const int O = a.n_outlier, K = a.top_k;
+  const int U = O + K + a.n_win_units;
+  // this wave's units: [uw0, uw1), at most NUW
+  const int per_wave = (a.upw + 3) / 4;
+  const int uw0 = min(U, split * a.upw + w * per_wave);
+  const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
+  const int nu = uw1 - uw0;
   const int hq = a.n_kv * G;
-  // chunk ids of the selected units of this split (no dependent load in the loop)
-  for (int i = threadIdx.x; i < u1 - u0; i += 256) {
-    const int s = u0 + i - a.n_outlier;
-    uch[i] = (s >= 0 && s < a.top_k) ? max(a.slot_chunk[(int64_t)p * a.top_k + s], 0) : 0;
+
+  // chunk id of each selected unit, one per lane, broadcast below
+  int my_ch = 0;
+  if (lane < nu) {
+    const int s = uw0 + lane - O;
+    if (s >= 0 && s < K) my_ch = max(a.slot_chunk[(int64_t)p * K + s], 0);
+  }
+  u32x4 kb[NUW][TPR], vb[NUW][TPR];
+#pragma unroll
+  for (int i = 0; i < NUW; i++) {
+    if (i < nu) {
+      const int u = uw0 + i;
+      const uint16_t* kp;
+      if (u < O) kp = a.k_out + ((int64_t)p * O + u) * C * kHeadDim;
+      else if (u < O + K) kp = a.key_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim;
+      else kp = a.k_win + ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
+#pragma unroll
+      for (int t = 0; t < TPR; t++) kb[i][t] = *reinterpret_cast<const u32x4*>(kp + (tg + 4 * t) * kHeadDim + ds * 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NUW; i++) {
+    if (i < nu) {
+      const int u = uw0 + i;
+      const int ch = __shfl(my_ch, i);
+      const uint16_t* vp;
+      if (u < O) vp = a.v_out + ((int64_t)p * O + u) * C * kHeadDim;
+      else if (u < O + K)
+        vp = a.host_values ? a.val_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim
+                           : a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * C) * kHeadDim;
+      else vp = a.v_win + ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
+#pragma unroll
+      for (int t = 0; t < TPR; t++) vb[i][t] = *reinterpret_cast<const u32x4*>(vp + (tg + 4 * t) * kHeadDim + ds * 8);
+    }
   }
 
+  // q scaled by 1/sqrt(d) and log2 e (the softmax runs in base 2)
   float qv[G][8];
 #pragma unroll
   for (int g = 0; g < G; g++) {
     const u32x4 wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + h * G + g) * kHeadDim + ds * 8);
     unpack8(wq, qv[g]);
 #pragma unroll
-    for (int i = 0; i < 8; i++) qv[g][i] *= a.scale * kLog2e;
+    for (int k = 0; k < 8; k++) qv[g][k] *= a.scale * kLog2e;
   }
   float m[G], l[G], o[G][8];
 #pragma unroll
@@ -538,73 +597,48 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; i++) o[g][i] = 0.f;
   }
-  __syncthreads();
-  const int nu = (u1 - u0 > w) ? (u1 - u0 - w + 3) / 4 : 0;   // units of this wave
-  auto load = [&](int i, u32x4* kd, u32x4* vd) {
-    if (i >= nu) return;
-    const int li = w + 4 * i;
-    const uint16_t *kp, *vp;
-    unit_ptrs<C>(a, p, b, h, u0 + li, uch[li], &kp, &vp);
 #pragma unroll
-    for (int t = 0; t < TPR; t++) {
-      kd[t] = *reinterpret_cast<const u32x4*>(kp + (tg + 4 * t) * kHeadDim + ds * 8);
-      vd[t] = *reinterpret_cast<const u32x4*>(vp + (tg + 4 * t) * kHeadDim + ds * 8);
-    }
-  };
-  auto process = [&](const u32x4* kd, const u32x4* vd) {
-    float s[TPR][G];
+  for (int i = 0; i < NUW; i++) {
+    if (i < nu) {
+      float s[TPR][G];
 #pragma unroll
-    for (int t = 0; t < TPR; t++) {
-      float x[8];
-      unpack8(kd[t], x);
+      for (int t = 0; t < TPR; t++) {
+        float x[8];
+        unpack8(kb[i][t], x);
+#pragma unroll
+        for (int g = 0; g < G; g++) {
+          float part = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; k++) part = fmaf(qv[g][k], x[k], part);
+          s[t][g] = row16_sum(part);
+        }
+      }
+      // running max: the (l, o) rescale only runs where the max grew
 #pragma unroll
       for (int g = 0; g < G; g++) {
-        float part = 0.f;
+        float mx = s[0][g];
 #pragma unroll
-        for (int k = 0; k < 8; k++) part = fmaf(qv[g][k], x[k], part);
-        s[t][g] = row16_sum(part);
+        for (int t = 1; t < TPR; t++) mx = fmaxf(mx, s[t][g]);
+        if (mx > m[g]) {
+          const float corr = __builtin_amdgcn_exp2f(m[g] - mx);
+          m[g] = mx;
+          l[g] *= corr;
+#pragma unroll
+          for (int k = 0; k < 8; k++) o[g][k] *= corr;
+        }
       }
-    }
 #pragma unroll
-    for (int g = 0; g < G; g++) {
-      float mx = s[0][g];
+      for (int t = 0; t < TPR; t++) {
+        float y[8];
+        unpack8(vb[i][t], y);
 #pragma unroll
-      for (int t = 1; t < TPR; t++) mx = fmaxf(mx, s[t][g]);
-      const float mn = fmaxf(m[g], mx);
-      const float corr = exp2f(m[g] - mn);
-      m[g] = mn;
-      l[g] *= corr;
+        for (int g = 0; g < G; g++) {
+          const float pr = __builtin_amdgcn_exp2f(s[t][g] - m[g]);
+          l[g] += pr;
 #pragma unroll
-      for (int k = 0; k < 8; k++) o[g][k] *= corr;
-    }
-#pragma unroll
-    for (int t = 0; t < TPR; t++) {
-      float y[8];
-      unpack8(vd[t], y);
-#pragma unroll
-      for (int g = 0; g < G; g++) {
-        const float pr = exp2f(s[t][g] - m[g]);
-        l[g] += pr;
-#pragma unroll
-        for (int k = 0; k < 8; k++) o[g][k] = fmaf(pr, y[k], o[g][k]);
+          for (int k = 0; k < 8; k++) o[g][k] = fmaf(pr, y[k], o[g][k]);
+        }
       }
-    }
-  };
-  u32x4 k0[TPR], v0[TPR], k1[TPR], v1[TPR];
-  load(0, k0, v0);
-  load(1, k1, v1);
-  for (int i = 0; i < nu; i += 2) {
-    u32x4 nk0[TPR], nv0[TPR], nk1[TPR], nv1[TPR];
-    load(i + 2, nk0, nv0);
-    load(i + 3, nk1, nv1);
-    process(k0, v0);
-    if (i + 1 < nu) process(k1, v1);
-#pragma unroll
-    for (int t = 0; t < TPR; t++) {
-      k0[t] = nk0[t];
-      v0[t] = nv0[t];
-      k1[t] = nk1[t];
-      v1[t] = nv1[t];
     }
   }
   // merge the four token rows of the wave (lanes ds, ds+16, ds+32, ds+48)
@@ -614,7 +648,7 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
     for (int g = 0; g < G; g++) {
       const float mo = __shfl_xor(m[g], off), lo = __shfl_xor(l[g], off);
       const float mn = fmaxf(m[g], mo);
-      const float c1 = exp2f(m[g] - mn), c2 = exp2f(mo - mn);
+      const float c1 = __builtin_amdgcn_exp2f(m[g] - mn), c2 = __builtin_amdgcn_exp2f(mo - mn);
       l[g] = l[g] * c1 + lo * c2;
 #pragma unroll
       for (int k = 0; k < 8; k++) {
@@ -645,7 +679,7 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ww++) {
-      const float c = exp2f(wm[ww][g] - M);
+      const float c = __builtin_amdgcn_exp2f(wm[ww][g] - M);
       num += wo[ww][g][dim] * c;
       den += wl[ww][g] * c;
     }
@@ -676,7 +710,7 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
     M = wave_max(M);
     float den = 0.f;
     for (int s = threadIdx.x; s < ns; s += 64) {
-      const float c = exp2f(cw[s] - M);
+      const float c = __builtin_amdgcn_exp2f(cw[s] - M);
       den += base[s * stride + kHeadDim + 1] * c;
       cw[s] = c;
     }

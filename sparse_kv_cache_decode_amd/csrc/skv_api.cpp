@@ -259,12 +259,14 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->cpb = 256;
     h->nb_score = (n_cand + h->cpb - 1) / h->cpb;
     h->ncp = (n_cand + 3) / 4 * 4;
-    // attention: ~2048 workgroups, units per workgroup a multiple of 8 (2 per wave)
-    int ns = (2048 + P - 1) / P;
-    ns = std::max(1, std::min(ns, h->U));
-    h->upw = ((h->U + ns - 1) / ns + 7) / 8 * 8;
-    h->upw = std::min(h->upw, kMaxUnitsPerSplit);
-    if ((int64_t)h->upw * kMaxSplits < h->U) h->upw = kMaxUnitsPerSplit;
+    // attention: each wave owns at most attn_units_per_wave units (all loads issued
+    // at once); split so that there are about 8 waves per CU
+    const int nuw = attn_units_per_wave(G, C);
+    const int waves_target = 2048;
+    int upw_wave = (int)(((int64_t)P * h->U + waves_target - 1) / waves_target);
+    upw_wave = std::max(1, std::min(upw_wave, nuw));
+    h->upw = 4 * upw_wave;
+    if ((int64_t)h->upw * kMaxSplits < h->U) h->upw = 4 * nuw;
     h->n_split = (h->U + h->upw - 1) / h->upw;
   }
 

@@ -10,7 +10,6 @@ namespace skv {
 constexpr int kHeadDim = 128;
 constexpr int kMaxTopK = 4096;
 constexpr int kSelLdsMax = 150 * 1024;   // dynamic LDS of the select kernel
-constexpr int kMaxUnitsPerSplit = 256;   // attention units (chunks) per workgroup
 constexpr int kMaxSplits = 1024;         // attention workgroups per pair
 
 // Everything a decode step touches, by value into the kernels.
@@ -89,6 +88,7 @@ bool select_keys_in_lds(int top_k, int res_words, int n_cand);
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);
+int attn_units_per_wave(int group, int chunk);
 
 // ---- host eigensolver (eig_host.cpp)
 // Top-r eigenpairs of each symmetric n x n matrix gram[bi] (row-major fp64, on the
