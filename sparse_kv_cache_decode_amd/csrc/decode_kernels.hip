@@ -330,13 +330,30 @@ constexpr int kRebuildRows = 128;
 constexpr int kKSlice = 192;
 constexpr int kLdsW = kKSlice + 8;
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id.  With a pair
+// count divisible by 8, linear id L = 8*s + x runs on XCD x and serves pair
+// x + 8*(s / nbp), so every workgroup of a pair shares one L2 and the pair's B^T
+// comes from HBM once.
+__device__ __forceinline__ void xcd_pair_map(int nbp, int P, int* p, int* j) {
+  const int L = blockIdx.x;
+  if ((P & 7) == 0) {
+    const int x = L & 7, sl = L >> 3;
+    *p = x + 8 * (sl / nbp);
+    *j = sl % nbp;
+  } else {
+    *p = L / nbp;
+    *j = L % nbp;
+  }
+}
+
 template <int C>
 __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kLdsW];
   __shared__ int mchunk[kRebuildRows / 4], mslot[kRebuildRows / 4];
-  const int p = blockIdx.y;
-  const int j0 = blockIdx.x * MPB;
+  int p, jb;
+  xcd_pair_map((a.top_k + MPB - 1) / MPB, a.batch * a.n_kv, &p, &jb);
+  const int j0 = jb * MPB;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int K = a.top_k, r = a.rank;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -465,7 +482,7 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
 
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st) {
   const int mpb = kRebuildRows / a.chunk;
-  dim3 grid((a.top_k + mpb - 1) / mpb, a.batch * a.n_kv);
+  dim3 grid(((a.top_k + mpb - 1) / mpb) * a.batch * a.n_kv);
   switch (a.chunk) {
     case 4: rebuild_kernel<4><<<grid, 256, 0, st>>>(a); break;
     case 8: rebuild_kernel<8><<<grid, 256, 0, st>>>(a); break;
@@ -509,164 +526,183 @@ hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Split-K flash-decode.  Work unit = one chunk of C tokens: unit u < O is an
 // outlier chunk, O <= u < O+K the chunk held by slot u-O, the rest the window.
-// Each wave owns up to NUW consecutive units and issues every K/V load of them
-// before computing (K first: key addresses need no chunk id), so a workgroup has
-// 4*NUW chunks in flight.  Lane (ds, tg) holds dims 8*ds..8*ds+7 of the tokens
-// tg, tg+4, ... of a unit; a logit is a 16-lane DPP sum, the softmax is online
-// in fp32 (base 2), and the four waves merge through LDS.
+// Each wave owns up to NT*16 consecutive tokens (NT tiles of 16) and issues all
+// of their K/V loads before computing (keys first: key addresses need no chunk
+// id).  Per tile:
+//  * S = K q^T on MFMA 16x16x32 bf16: lane (row r, kq) feeds dims j*32+kq*8.. of
+//    token r; the output lane (head g = lane%16, kq) holds tokens kq*4..kq*4+3.
+//  * softmax in that layout, base 2: one running max and sum per head and wave;
+//    probabilities and the rescale factor go through a 1 KB per-wave LDS buffer.
+//  * P V on the vector ALUs: lane (ds, tg) accumulates dims 8*ds..8*ds+7 of the
+//    tokens tg, tg+4, tg+8, tg+12 for every head.
+// The four waves of a workgroup merge through LDS into one split partial.
 
 template <int G, int C>
 struct AttnShape {
-  static constexpr int TPR = C / 4;                        // tokens per lane row
-  static constexpr int LOADS = G <= 4 ? 32 : 16;           // 16-B K/V loads per lane
-  static constexpr int NUW = LOADS / (2 * TPR);            // units per wave
+  static constexpr int NT = G <= 4 ? 4 : 2;     // 16-token tiles per wave
+  static constexpr int NUW = NT * 16 / C;       // units per wave
 };
 
-int attn_units_per_wave(int group, int chunk) {
-  const int loads = group <= 4 ? 32 : 16;
-  return loads / (2 * (chunk / 4));
+int attn_units_per_wave(int group, int chunk) { return (group <= 4 ? 4 : 2) * 16 / chunk; }
+
+template <int C>
+__device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, int u) {
+  const int O = a.n_outlier, K = a.top_k;
+  if (u < O) return a.k_out + ((int64_t)p * O + u) * C * kHeadDim;
+  if (u < O + K) return a.key_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim;
+  return a.k_win + ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
+}
+
+template <int C>
+__device__ __forceinline__ const uint16_t* unit_value(const DecodeArgs& a, int p, int b, int h, int u,
+                                                      int ch) {
+  const int O = a.n_outlier, K = a.top_k;
+  if (u < O) return a.v_out + ((int64_t)p * O + u) * C * kHeadDim;
+  if (u < O + K)
+    return a.host_values ? a.val_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim
+                         : a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * C) * kHeadDim;
+  return a.v_win + ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
 }
 
 template <int G, int C>
 __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
-  constexpr int TPR = AttnShape<G, C>::TPR;
-  constexpr int NUW = AttnShape<G, C>::NUW;
+  constexpr int NT = AttnShape<G, C>::NT;
+  __shared__ __attribute__((aligned(16))) float pbuf[4][16 * 16];   // [wave][head][tg][t]
+  __shared__ float cbuf[4][16];                                     // [wave][head] rescale
   __shared__ float wo[4][G][kHeadDim];
   __shared__ float wm[4][G], wl[4][G];
   const int p = blockIdx.y, split = blockIdx.x;
   const int b = p / a.n_kv, h = p % a.n_kv;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, ds = lane & 15, tg = lane >> 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;   // (row|head|ds, kq|tg)
   const int O = a.n_outlier, K = a.top_k;
   const int U = O + K + a.n_win_units;
-  // this wave's units: [uw0, uw1), at most NUW
   const int per_wave = (a.upw + 3) / 4;
   const int uw0 = min(U, split * a.upw + w * per_wave);
   const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
-  const int nu = uw1 - uw0;
+  const int ntok = (uw1 - uw0) * C;
   const int hq = a.n_kv * G;
 
-  // chunk id of each selected unit, one per lane, broadcast below
+  // chunk id of each selected unit of the wave, one per lane
   int my_ch = 0;
-  if (lane < nu) {
-    const int s = uw0 + lane - O;
-    if (s >= 0 && s < K) my_ch = max(a.slot_chunk[(int64_t)p * K + s], 0);
+  if (lane < uw1 - uw0) {
+    const int sidx = uw0 + lane - O;
+    if (sidx >= 0 && sidx < K) my_ch = max(a.slot_chunk[(int64_t)p * K + sidx], 0);
   }
-  u32x4 kb[NUW][TPR], vb[NUW][TPR];
+  // keys, MFMA A layout: token tile*16 + lr, dims j*32 + lq*8
+  u32x4 kf[NT][4], vf[NT][4];
 #pragma unroll
-  for (int i = 0; i < NUW; i++) {
-    if (i < nu) {
-      const int u = uw0 + i;
-      const uint16_t* kp;
-      if (u < O) kp = a.k_out + ((int64_t)p * O + u) * C * kHeadDim;
-      else if (u < O + K) kp = a.key_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim;
-      else kp = a.k_win + ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
+  for (int t = 0; t < NT; t++) {
+    const int tau = t * 16 + lr;
 #pragma unroll
-      for (int t = 0; t < TPR; t++) kb[i][t] = *reinterpret_cast<const u32x4*>(kp + (tg + 4 * t) * kHeadDim + ds * 8);
+    for (int j = 0; j < 4; j++) kf[t][j] = (u32x4){0u, 0u, 0u, 0u};
+    if (tau < ntok) {
+      const uint16_t* kp = unit_key<C>(a, p, uw0 + tau / C) + (tau % C) * kHeadDim + lq * 8;
+#pragma unroll
+      for (int j = 0; j < 4; j++) kf[t][j] = *reinterpret_cast<const u32x4*>(kp + j * 32);
     }
   }
+  // values, PV layout: token tile*16 + lq + 4*i, dims lr*8
 #pragma unroll
-  for (int i = 0; i < NUW; i++) {
-    if (i < nu) {
-      const int u = uw0 + i;
-      const int ch = __shfl(my_ch, i);
-      const uint16_t* vp;
-      if (u < O) vp = a.v_out + ((int64_t)p * O + u) * C * kHeadDim;
-      else if (u < O + K)
-        vp = a.host_values ? a.val_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim
-                           : a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * C) * kHeadDim;
-      else vp = a.v_win + ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
+  for (int t = 0; t < NT; t++) {
 #pragma unroll
-      for (int t = 0; t < TPR; t++) vb[i][t] = *reinterpret_cast<const u32x4*>(vp + (tg + 4 * t) * kHeadDim + ds * 8);
-    }
-  }
-
-  // q scaled by 1/sqrt(d) and log2 e (the softmax runs in base 2)
-  float qv[G][8];
-#pragma unroll
-  for (int g = 0; g < G; g++) {
-    const u32x4 wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + h * G + g) * kHeadDim + ds * 8);
-    unpack8(wq, qv[g]);
-#pragma unroll
-    for (int k = 0; k < 8; k++) qv[g][k] *= a.scale * kLog2e;
-  }
-  float m[G], l[G], o[G][8];
-#pragma unroll
-  for (int g = 0; g < G; g++) {
-    m[g] = kNegBig;
-    l[g] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) o[g][i] = 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < NUW; i++) {
-    if (i < nu) {
-      float s[TPR][G];
-#pragma unroll
-      for (int t = 0; t < TPR; t++) {
-        float x[8];
-        unpack8(kb[i][t], x);
-#pragma unroll
-        for (int g = 0; g < G; g++) {
-          float part = 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; k++) part = fmaf(qv[g][k], x[k], part);
-          s[t][g] = row16_sum(part);
-        }
+    for (int i = 0; i < 4; i++) {
+      const int tau = t * 16 + lq + 4 * i;
+      const int ch = __shfl(my_ch, min(tau, ntok - 1 + (ntok == 0)) / C);
+      vf[t][i] = (u32x4){0u, 0u, 0u, 0u};
+      if (tau < ntok) {
+        const uint16_t* vp = unit_value<C>(a, p, b, h, uw0 + tau / C, ch) + (tau % C) * kHeadDim + lr * 8;
+        vf[t][i] = *reinterpret_cast<const u32x4*>(vp);
       }
-      // running max: the (l, o) rescale only runs where the max grew
+    }
+  }
+  // q^T, MFMA B layout: head lr, dims j*32 + lq*8 (zero for heads >= G)
+  bf16x8 bq[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    u32x4 wq = {0u, 0u, 0u, 0u};
+    if (lr < G) wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + h * G + lr) * kHeadDim + j * 32 + lq * 8);
+    bq[j] = __builtin_bit_cast(bf16x8, wq);
+  }
+  const float qscale = a.scale * kLog2e;
+  float m = kNegBig, l = 0.f;        // head lr (S layout)
+  float o[G][8];                     // PV layout
+#pragma unroll
+  for (int g = 0; g < G; g++)
+#pragma unroll
+    for (int k = 0; k < 8; k++) o[g][k] = 0.f;
+
+#pragma unroll
+  for (int t = 0; t < NT; t++) {
+    if (t * 16 < ntok) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[t][j]), bq[j], acc, 0, 0, 0);
+      float sv[4];
+      float tmax = kNegBig;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        sv[i] = (t * 16 + lq * 4 + i < ntok) ? acc[i] * qscale : kNegBig;
+        tmax = fmaxf(tmax, sv[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mn = fmaxf(m, tmax);
+      const float corr = __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float pv = __builtin_amdgcn_exp2f(sv[i] - mn);
+        psum += pv;
+        pbuf[w][lr * 16 + i * 4 + lq] = pv;
+      }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l = l * corr + psum;
+      if (lq == 0) cbuf[w][lr] = corr;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
 #pragma unroll
       for (int g = 0; g < G; g++) {
-        float mx = s[0][g];
+        const float cg = cbuf[w][g];
+        if (cg != 1.f) {
 #pragma unroll
-        for (int t = 1; t < TPR; t++) mx = fmaxf(mx, s[t][g]);
-        if (mx > m[g]) {
-          const float corr = __builtin_amdgcn_exp2f(m[g] - mx);
-          m[g] = mx;
-          l[g] *= corr;
-#pragma unroll
-          for (int k = 0; k < 8; k++) o[g][k] *= corr;
+          for (int k = 0; k < 8; k++) o[g][k] *= cg;
         }
       }
+      f32x4 pg[G];
 #pragma unroll
-      for (int t = 0; t < TPR; t++) {
+      for (int g = 0; g < G; g++) pg[g] = *reinterpret_cast<const f32x4*>(&pbuf[w][g * 16 + lq * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
         float y[8];
-        unpack8(vb[i][t], y);
+        unpack8(vf[t][i], y);
 #pragma unroll
-        for (int g = 0; g < G; g++) {
-          const float pr = __builtin_amdgcn_exp2f(s[t][g] - m[g]);
-          l[g] += pr;
+        for (int g = 0; g < G; g++)
 #pragma unroll
-          for (int k = 0; k < 8; k++) o[g][k] = fmaf(pr, y[k], o[g][k]);
-        }
+          for (int k = 0; k < 8; k++) o[g][k] = fmaf(pg[g][i], y[k], o[g][k]);
       }
+      __builtin_amdgcn_wave_barrier();
     }
   }
-  // merge the four token rows of the wave (lanes ds, ds+16, ds+32, ds+48)
+  // the four token rows share the wave's running max: plain sums
 #pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
+  for (int g = 0; g < G; g++)
 #pragma unroll
-    for (int g = 0; g < G; g++) {
-      const float mo = __shfl_xor(m[g], off), lo = __shfl_xor(l[g], off);
-      const float mn = fmaxf(m[g], mo);
-      const float c1 = __builtin_amdgcn_exp2f(m[g] - mn), c2 = __builtin_amdgcn_exp2f(mo - mn);
-      l[g] = l[g] * c1 + lo * c2;
-#pragma unroll
-      for (int k = 0; k < 8; k++) {
-        const float oo = __shfl_xor(o[g][k], off);
-        o[g][k] = o[g][k] * c1 + oo * c2;
-      }
-      m[g] = mn;
+    for (int k = 0; k < 8; k++) {
+      o[g][k] += __shfl_xor(o[g][k], 16);
+      o[g][k] += __shfl_xor(o[g][k], 32);
     }
-  }
-  if (tg == 0) {
+  if (lq == 0) {
 #pragma unroll
-    for (int g = 0; g < G; g++) {
+    for (int g = 0; g < G; g++)
 #pragma unroll
-      for (int k = 0; k < 8; k++) wo[w][g][ds * 8 + k] = o[g][k];
-      if (ds == 0) {
-        wm[w][g] = m[g];
-        wl[w][g] = l[g];
-      }
+      for (int k = 0; k < 8; k++) wo[w][g][lr * 8 + k] = o[g][k];
+    if (lr < G) {
+      wm[w][lr] = m;
+      wl[w][lr] = l;
     }
   }
   __syncthreads();
