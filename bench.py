@@ -12,6 +12,8 @@ sees hits.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
@@ -23,6 +25,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+CALIB_BYTES = 512 << 20         # bytes read (and written) once by the counter-calibration kernel
+CSRC = os.path.join(ROOT, "sparse_kv_cache_decode_amd", "csrc")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_kernel_llama3_8b_122k_hbm_traffic.md")
+SCORE_KERNEL = "skv::score_kernel<4>"
 METRIC = "decode tokens/s at S=122K batch 8 (Llama-3.1-8B shape); % HBM roofline"
 
 
@@ -75,6 +81,129 @@ def start_cpu_baseline(shape_name, seed, min_seconds):
 
 
 # ----------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, KiB per dispatch),
+# scaled by what the same counters read for a streaming kernel of known size.
+
+
+def kernel_source_digest() -> str:
+    """Digest of every native source: traffic figures taken from an older build
+    than the one being timed are not reported."""
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(CSRC)):
+        if n.endswith((".hip", ".h", ".cpp")):
+            h.update(n.encode())
+            with open(os.path.join(CSRC, n), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def calibration_copy():
+    """Elementwise float32 multiply over CALIB_BYTES: reads and writes each byte once.
+    Runs outside the timed region; only its counter readings are used."""
+    import torch
+    src = torch.full((CALIB_BYTES // 4,), 1.0, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+
+
+def _short_kernel_name(name: str) -> str:
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth, end = 0, len(name)
+    for i, ch in enumerate(name):        # cut the argument list, keep template arguments
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            end = i
+            break
+    return name[:end]
+
+
+def _counter_rows(path: str, counter: str) -> list:
+    """(dispatch id, short kernel name, value) of every dispatch, in dispatch order."""
+    rows = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                rows.append((int(row["Dispatch_Id"]), _short_kernel_name(row["Kernel_Name"]),
+                             float(row["Counter_Value"])))
+    return sorted(rows)
+
+
+def _means(rows: list) -> dict:
+    acc = {}
+    for _, k, v in rows:
+        s, n = acc.get(k, (0.0, 0))
+        acc[k] = (s + v, n + 1)
+    return {k: (s / n, n) for k, (s, n) in acc.items()}
+
+
+def _calibration(rows: list):
+    """The calibration kernel is the last three dispatches of the run."""
+    last = rows[-3:]
+    names = {k for _, k, _ in last}
+    assert len(last) == 3 and len(names) == 1 and "MulFunctor<float>" in next(iter(names)), names
+    return next(iter(names)), sum(v for _, _, v in last) / 3.0
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> str:
+    """Markdown summary (with a JSON block that bench.py reads back) of two
+    rocprofv3 --pmc runs of `command`, one with FETCH_SIZE and one with WRITE_SIZE."""
+    fr, wr = _counter_rows(fetch_csv, "FETCH_SIZE"), _counter_rows(write_csv, "WRITE_SIZE")
+    fetch, write = _means(fr), _means(wr)
+    calib, cf = _calibration(fr)
+    _, cw = _calibration(wr)
+    f_fac = CALIB_BYTES / (cf * 1024.0)
+    w_fac = CALIB_BYTES / (cw * 1024.0)
+    kernels = {}
+    for k in sorted(fetch):
+        if not k.startswith("skv::") or k not in write:
+            continue
+        fb, wb = fetch[k][0] * 1024.0 * f_fac, write[k][0] * 1024.0 * w_fac
+        kernels[k] = {"dispatches": fetch[k][1], "fetch_kib": round(fetch[k][0], 1),
+                      "write_kib": round(write[k][0], 1), "hbm_read_bytes": int(fb),
+                      "hbm_write_bytes": int(wb), "hbm_bytes_per_launch": int(fb + wb)}
+    blob = {"workload": "llama3_8b_122k", "kernel_source_digest": kernel_source_digest(),
+            "calibration_bytes": CALIB_BYTES, "fetch_factor": round(f_fac, 4),
+            "write_factor": round(w_fac, 4), "kernels": kernels}
+    lines = ["# HBM traffic per kernel launch: ShadowKV decode, Llama-3.1-8B shape (122 880 tokens, batch 8)",
+             "", "Commands (repo root on the GPU box, `export TMPDIR=/tmp` first):", "", "```"]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append(f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c.lower()} -o pmc -- {command}")
+    lines += ["```", "",
+              f"Scaling: the calibration kernel (`{calib}`, the run's last three dispatches) reads and "
+              f"writes {CALIB_BYTES} bytes; FETCH_SIZE reads {cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB for it, "
+              f"so bytes = KiB x 1024 x {f_fac:.4f} (reads) and x {w_fac:.4f} (writes).", "",
+              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |",
+              "|---|---|---|---|---|---|"]
+    for k, v in kernels.items():
+        lines.append(f"| `{k}` | {v['dispatches']} | {v['fetch_kib']} | {v['write_kib']} | "
+                     f"{v['hbm_read_bytes'] / 1e6:.1f} | {v['hbm_write_bytes'] / 1e6:.1f} |")
+    lines += ["", "Read back by bench.py (used only while the native sources hash to the digest):", "",
+              "```json", json.dumps(blob, indent=1), "```", ""]
+    return "\n".join(lines)
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when there is none for this workload or the sources have changed since."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if blob.get("workload") != workload or blob.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    k = blob.get("kernels", {}).get(kernel)
+    return k["hbm_bytes_per_launch"] if k else None
+
+
+# ----------------------------------------------------------------------------
 
 
 def algorithmic_bytes(shape, misses_per_layer_step: float) -> dict:
@@ -100,8 +229,16 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed region, run a known-size streaming kernel for counter scaling")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs (no GPU needed)")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters))
+        return 0
 
     if args.cpu_baseline_child:
         cpu_baseline_child(args.shape, args.seed, args.cpu_seconds)
@@ -226,7 +363,9 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "score_kernel (landmark GEMV)",
                      "achieved": round(score_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(score_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(score_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(shape.name, SCORE_KERNEL),
+                     "algorithmic_bytes": int(by["score"])},
         "step_roofline": {"algorithmic_bytes_per_layer_step": int(by["total"]),
                           "achieved_GBps": round(step_gbps, 1),
                           "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
@@ -238,6 +377,8 @@ def main():
                                       "dense_bytes_over_measured_time": round(bt_measured, 1)},
         "cpu_baseline": cpu,
     }
+    if args.calib_copy:
+        calibration_copy()
     print(json.dumps(rec), flush=True)
     for ly in layers:
         ly.close()
