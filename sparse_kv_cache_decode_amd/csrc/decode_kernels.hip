@@ -265,15 +265,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
     n_miss += tot >> 16;
   }
   __syncthreads();
-  // n_free == n_miss: every missed chunk takes the next evicted slot
-  for (int j = threadIdx.x; j < n_miss; j += kSelThreads) {
-    const int slot = freel[j];
-    const int ci = sel[missp[j]], ch = selch[missp[j]];
-    const int old = scl[slot];
-    if (old >= 0) atomicAnd(&resl[old >> 5], ~(1u << (old & 31)));
-    atomicOr(&resl[ci >> 5], 1u << (ci & 31));
-    sc[slot] = ci;
-    sch[slot] = ch;
+  // n_free == n_miss: every missed chunk takes the next evicted slot.  The miss
+  // list is written in full, -1 past n_miss, so its readers need not load n_miss.
+  for (int j = threadIdx.x; j < K; j += kSelThreads) {
+    int slot = -1, ch = -1;
+    if (j < n_miss) {
+      slot = freel[j];
+      const int ci = sel[missp[j]];
+      ch = selch[missp[j]];
+      const int old = scl[slot];
+      if (old >= 0) atomicAnd(&resl[old >> 5], ~(1u << (old & 31)));
+      atomicOr(&resl[ci >> 5], 1u << (ci & 31));
+      sc[slot] = ci;
+      sch[slot] = ch;
+    }
     a.miss_slot[(int64_t)p * K + j] = slot;
     a.miss_chunk[(int64_t)p * K + j] = ch;
   }
@@ -324,82 +329,139 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Key rebuild: 128 rows (MPB = 128/C missed chunks) per workgroup, 4 waves x 32
-// rows, N = d = 128 as 8 MFMA column tiles; B^T slices of 128 k staged in LDS.
+// rows, N = d = 128 as 8 MFMA column tiles, k in steps of 32.  Every k-step is
+// one load group per wave (two direct global->LDS loads of B^T, two A-row
+// fragment loads), all groups issued up front; the MFMAs of step q start as soon
+// as groups 0..q have landed, while the later groups are still in flight.
 
 constexpr int kRebuildRows = 128;
-constexpr int kKSlice = 192;
-constexpr int kLdsW = kKSlice + 8;
+constexpr int kMaxSteps = 5;                  // k-steps per staged slice (160 k)
+constexpr int kOutW = kHeadDim + 8;           // staged output row pitch (bf16)
+constexpr int kStepPieces = kRebuildRows * 4; // 16-byte pieces of B^T per k-step
 
-// Workgroups are dispatched to the 8 XCDs round-robin by linear id.  With a pair
-// count divisible by 8, linear id L = 8*s + x runs on XCD x and serves pair
-// x + 8*(s / nbp), so every workgroup of a pair shares one L2 and the pair's B^T
-// comes from HBM once.
-__device__ __forceinline__ void xcd_pair_map(int nbp, int P, int* p, int* j) {
-  const int L = blockIdx.x;
-  if ((P & 7) == 0) {
-    const int x = L & 7, sl = L >> 3;
-    *p = x + 8 * (sl / nbp);
-    *j = sl % nbp;
-  } else {
-    *p = L / nbp;
-    *j = L % nbp;
+// Piece c (0..3) of B^T row n within a k-step: XOR-swizzled so that the 16 rows
+// one MFMA operand read touches fall in 16 distinct LDS bank groups.
+__device__ __forceinline__ int bt_slot(int n, int c) { return n * 4 + (c ^ ((n >> 2) & 3)); }
+
+// s_waitcnt immediate: vector-memory count n, other counters left alone (gfx9 layout)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most g load groups of 4 vector-memory instructions are outstanding
+// (g is a constant once the k-step loop is unrolled).
+__device__ __forceinline__ void wait_load_groups(int g) {
+  switch (g) {
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(16)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(20)); break;
   }
 }
 
-template <int C>
-__global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
+// Four B^T operand pieces (column tiles H*4 .. H*4+3) of k-step Q, read from LDS
+// in one asm block that ends with lgkmcnt(0), so the values exist only once they
+// have arrived.  A read the compiler can see would make it wait for every direct
+// global->LDS load still in flight (all k-steps at once); this one is ordered by
+// the explicit waits and barrier in mfma_steps.
+template <int Q, int H>
+__device__ __forceinline__ void stage_reads(uint32_t addr, u32x4 (&bw)[4]) {
+  constexpr int T = 16 * 4 * 16;                              // column-tile stride
+  constexpr int O = Q * kStepPieces * 16 + H * 4 * T;         // step and half offset
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n"
+      "ds_read_b128 %1, %4 offset:%6\n"
+      "ds_read_b128 %2, %4 offset:%7\n"
+      "ds_read_b128 %3, %4 offset:%8\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(bw[0]), "=&v"(bw[1]), "=&v"(bw[2]), "=&v"(bw[3])
+      : "v"(addr), "i"(O), "i"(O + T), "i"(O + 2 * T), "i"(O + 3 * T));
+}
+
+template <int Q, int H>
+__device__ __forceinline__ void mfma_half(const u32x4 (&a)[2], bool kin, uint32_t baddr, f32x4 (&acc)[2][8]) {
+  u32x4 bw[4];
+  stage_reads<Q, H>(baddr, bw);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const bf16x8 bfr = __builtin_bit_cast(bf16x8, kin ? bw[i] : (u32x4){0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+      acc[mt][H * 4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt]), bfr,
+                                                                   acc[mt][H * 4 + i], 0, 0, 0);
+  }
+}
+
+// k-step Q of a slice: wait for load groups 0..Q of every wave, then 16 MFMAs.
+// A fragments are used as loaded (rows past the misses hold finite data and are
+// never stored); B^T pieces past kn are zeroed, which cancels the k-padding.
+template <int NSTEP, int Q>
+__device__ __forceinline__ void mfma_steps(const u32x4 (&af)[NSTEP][2], int kn, int lk, uint32_t baddr,
+                                           f32x4 (&acc)[2][8]) {
+  __builtin_amdgcn_sched_barrier(0);             // step Q-1's MFMAs stay ahead of this wait
+  wait_load_groups(NSTEP - 1 - Q);               // this wave's groups 0..Q have landed
+  __builtin_amdgcn_s_barrier();                  // ... and every other wave's
+  const bool kin = Q * 32 + lk * 8 < kn;
+  mfma_half<Q, 0>(af[Q], kin, baddr, acc);
+  mfma_half<Q, 1>(af[Q], kin, baddr, acc);
+  if constexpr (Q + 1 < NSTEP) mfma_steps<NSTEP, Q + 1>(af, kn, lk, baddr, acc);
+}
+
+template <int C, int NSTEP>
+__global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
-  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kLdsW];
-  __shared__ int mchunk[kRebuildRows / 4], mslot[kRebuildRows / 4];
-  int p, jb;
-  xcd_pair_map((a.top_k + MPB - 1) / MPB, a.batch * a.n_kv, &p, &jb);
-  const int j0 = jb * MPB;
+  constexpr int kStageBytes = NSTEP * kStepPieces * 16 > kRebuildRows * kOutW * 2
+                                  ? NSTEP * kStepPieces * 16 : kRebuildRows * kOutW * 2;
+  __shared__ u32x4 stage[kStageBytes / 16];
+  __shared__ int mchunk[MPB], mslot[MPB];
+  const int P = a.batch * a.n_kv;
+  // Tile-major order: workgroup L serves tile L / P of pair L % P, so the tiles
+  // that exist for every pair are dispatched first.  Workgroups go to the 8 XCDs
+  // round-robin by linear id; with P a multiple of 8 all tiles of a pair run on
+  // XCD p % 8 and share one L2 copy of the pair's B^T.
+  const int p = blockIdx.x % P, j0 = (blockIdx.x / P) * MPB;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int K = a.top_k, r = a.rank;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lk = lane >> 4;
-  const uint16_t* Bt = a.Bt + ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
-  const bool single_slice = r <= kKSlice;
-  // B^T of the pair does not depend on the misses: its loads go out with n_miss
-  u32x4 bpre[(128 * kKSlice / 8 + 255) / 256];
-  constexpr int kBPieces = (128 * kKSlice / 8 + 255) / 256;
-  const int per_row0 = min(r, kKSlice) / 8;
-  if (single_slice) {
+  double ffreq[4];
 #pragma unroll
-    for (int q = 0; q < kBPieces; q++) {
-      const int e = threadIdx.x + q * 256;
-      bpre[q] = (u32x4){0u, 0u, 0u, 0u};
-      if (e < 128 * per_row0) {
-        const int nr = e / per_row0, k8 = (e % per_row0) * 8;
-        bpre[q] = *reinterpret_cast<const u32x4*>(Bt + (int64_t)nr * r + k8);
-      }
-    }
-  }
-  const int n = a.n_miss[p];
-  if (j0 >= n) return;
+  for (int nt = 0; nt < 4; nt++) ffreq[nt] = a.inv_freq[nt * 16 + lr];
   for (int i = threadIdx.x; i < MPB; i += 256) {
-    const bool ok = j0 + i < n;
+    const bool ok = j0 + i < K;
     mchunk[i] = ok ? a.miss_chunk[(int64_t)p * K + j0 + i] : -1;
     mslot[i] = ok ? a.miss_slot[(int64_t)p * K + j0 + i] : -1;
   }
-  if (single_slice) {
-#pragma unroll
-    for (int q = 0; q < kBPieces; q++) {
-      const int e = threadIdx.x + q * 256;
-      if (e < 128 * per_row0) {
-        const int nr = e / per_row0, k8 = (e % per_row0) * 8;
-        *reinterpret_cast<u32x4*>(&tile[nr * kLdsW + k8]) = bpre[q];
-      }
-    }
-  }
   __syncthreads();
-  // A operand rows of this lane: row m = w*32 + mt*16 + lr
+  if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
+  const uint16_t* Bt = a.Bt + ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
+  const uint16_t* Ab = a.A + (int64_t)b * a.seq_len * r;
+  // A operand rows of this lane: row m = w*32 + mt*16 + lr (rows past the misses
+  // read row 0 of the batch element; their outputs are not stored)
   const uint16_t* arow[2];
+  int64_t pos0[2];   // position of this lane's first output row of each tile
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     const int m = w * 32 + mt * 16 + lr;
     const int ch = mchunk[m / C];
-    arow[mt] = ch >= 0 ? a.A + ((int64_t)b * a.seq_len + (int64_t)ch * C + (m % C)) * r : nullptr;
+    arow[mt] = ch >= 0 ? Ab + ((int64_t)ch * C + (m % C)) * r : Ab;
+    const int m0 = w * 32 + mt * 16 + lk * 4;
+    pos0[mt] = (int64_t)max(mchunk[m0 / C], 0) * C + (m0 % C);
+  }
+  // LDS byte address of this lane's B^T operand piece in k-step 0, column tile 0:
+  // row lr, piece lk swizzled; the swizzle depends on lr only, so every (step,
+  // column tile) is a constant offset from it.
+  const uint32_t baddr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) u32x4*)stage +
+                         (uint32_t)bt_slot(lr, lk) * 16u;
+  // RoPE angles: a lane's four output rows lk*4 .. lk*4+3 of a tile are
+  // consecutive positions of one chunk, so the float64 reduction runs once per
+  // (tile, column) and the rows add j * f.
+  float ang[2][4], ff[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; nt++) {
+    ff[nt] = (float)ffreq[nt];
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) ang[mt][nt] = rope_angle(pos0[mt], ffreq[nt]);
   }
   f32x4 acc[2][8];
 #pragma unroll
@@ -407,66 +469,47 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = 0; ks < r; ks += kKSlice) {
-    const int kn = min(kKSlice, r - ks);
-    u32x4 af[kKSlice / 32][2];
+  for (int ks = 0; ks < r; ks += NSTEP * 32) {
+    const int kn = min(NSTEP * 32, r - ks);
+    if (ks > 0) __syncthreads();                 // previous slice fully consumed
+    u32x4 af[NSTEP][2];
 #pragma unroll
-    for (int q = 0; q < kKSlice / 32; q++) {
-      const int kof = q * 32 + lk * 8;
+    for (int q = 0; q < NSTEP; q++) {
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int i = w * 2 + u;                 // instruction 0..7 of the step
+        const int e = i * 64 + lane;
+        const int n = e >> 2, c = (e & 3) ^ ((n >> 2) & 3);
+        const int kk = q * 32 + c * 8 < kn ? ks + q * 32 + c * 8 : ks;
+        __builtin_amdgcn_global_load_lds(Bt + (int64_t)n * r + kk,
+            (__attribute__((address_space(3))) void*)(stage + q * kStepPieces + i * 64), 16, 0, 0);
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; mt++) {
-        af[q][mt] = (u32x4){0u, 0u, 0u, 0u};
-        if (kof < kn && arow[mt]) af[q][mt] = *reinterpret_cast<const u32x4*>(arow[mt] + ks + kof);
+        const int kk = q * 32 + lk * 8 < kn ? ks + q * 32 + lk * 8 : ks;
+        af[q][mt] = *reinterpret_cast<const u32x4*>(arow[mt] + kk);
       }
+      __builtin_amdgcn_sched_barrier(0);         // keep the groups in issue order
     }
-    if (!single_slice) {
-      __syncthreads();
-      const int per_row = kn / 8;
-      for (int e = threadIdx.x; e < 128 * per_row; e += 256) {
-        const int nr = e / per_row, k8 = (e % per_row) * 8;
-        *reinterpret_cast<u32x4*>(&tile[nr * kLdsW + k8]) =
-            *reinterpret_cast<const u32x4*>(Bt + (int64_t)nr * r + ks + k8);
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int q = 0; q < kKSlice / 32; q++) {
-      const int kof = q * 32 + lk * 8;
-      if (q * 32 >= kn) break;
-      const bool kin = kof < kn;
-#pragma unroll
-      for (int nt = 0; nt < 8; nt++) {
-        u32x4 wb = {0u, 0u, 0u, 0u};
-        if (kin) wb = *reinterpret_cast<const u32x4*>(&tile[(nt * 16 + lr) * kLdsW + kof]);
-        const bf16x8 bfr = __builtin_bit_cast(bf16x8, wb);
-#pragma unroll
-        for (int mt = 0; mt < 2; mt++)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[q][mt]), bfr,
-                                                                acc[mt][nt], 0, 0, 0);
-      }
-    }
+    mfma_steps<NSTEP, 0>(af, kn, lk, baddr, acc);
   }
   __syncthreads();
-  // epilogue: RoPE on (col, col + 64) pairs, stage bf16 rows in LDS.  A lane's four
-  // rows lk*4 .. lk*4+3 of a tile are consecutive positions of one chunk, so the
-  // float64 angle reduction runs once per (tile, column) and the rows add j * f.
+  // epilogue: RoPE on (col, col + 64) pairs, bf16 rows staged in LDS
+  uint16_t* otile = reinterpret_cast<uint16_t*>(stage);
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     const int m0 = w * 32 + mt * 16 + lk * 4;
-    const int ch = max(mchunk[m0 / C], 0);
-    const int64_t pos0 = (int64_t)ch * C + (m0 % C);
 #pragma unroll
     for (int nt = 0; nt < 4; nt++) {
       const int col = nt * 16 + lr;
-      const double f = a.inv_freq[col];
-      const float a0 = rope_angle(pos0, f), ff = (float)f;
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         float c, s;
-        __sincosf(a0 + jj * ff, &s, &c);
+        __sincosf(ang[mt][nt] + jj * ff[nt], &s, &c);
         const float x1 = acc[mt][nt][jj], x2 = acc[mt][nt + 4][jj];
-        tile[(m0 + jj) * kLdsW + col] = f32_to_bf16(x1 * c - x2 * s);
-        tile[(m0 + jj) * kLdsW + col + 64] = f32_to_bf16(x2 * c + x1 * s);
+        const uint32_t pk = pack_bf16x2(x1 * c - x2 * s, x2 * c + x1 * s);
+        otile[(m0 + jj) * kOutW + col] = (uint16_t)pk;
+        otile[(m0 + jj) * kOutW + col + 64] = (uint16_t)(pk >> 16);
       }
     }
   }
@@ -476,20 +519,32 @@ __global__ __launch_bounds__(256) void rebuild_kernel(DecodeArgs a) {
     const int slot = mslot[m / C];
     if (slot < 0) continue;
     uint16_t* dst = a.key_slots + (((int64_t)p * K + slot) * C + (m % C)) * kHeadDim + piece * 8;
-    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&tile[m * kLdsW + piece * 8]);
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&otile[m * kOutW + piece * 8]);
   }
+}
+
+template <int C>
+static hipError_t launch_rebuild_c(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  switch (min(kMaxSteps, (a.rank + 31) / 32)) {
+    case 1: rebuild_kernel<C, 1><<<grid, 256, 0, st>>>(a); break;
+    case 2: rebuild_kernel<C, 2><<<grid, 256, 0, st>>>(a); break;
+    case 3: rebuild_kernel<C, 3><<<grid, 256, 0, st>>>(a); break;
+    case 4: rebuild_kernel<C, 4><<<grid, 256, 0, st>>>(a); break;
+    case 5: rebuild_kernel<C, 5><<<grid, 256, 0, st>>>(a); break;
+    default: rebuild_kernel<C, kMaxSteps><<<grid, 256, 0, st>>>(a); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st) {
   const int mpb = kRebuildRows / a.chunk;
   dim3 grid(((a.top_k + mpb - 1) / mpb) * a.batch * a.n_kv);
   switch (a.chunk) {
-    case 4: rebuild_kernel<4><<<grid, 256, 0, st>>>(a); break;
-    case 8: rebuild_kernel<8><<<grid, 256, 0, st>>>(a); break;
-    case 16: rebuild_kernel<16><<<grid, 256, 0, st>>>(a); break;
+    case 4: return launch_rebuild_c<4>(a, grid, st);
+    case 8: return launch_rebuild_c<8>(a, grid, st);
+    case 16: return launch_rebuild_c<16>(a, grid, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
