@@ -79,7 +79,7 @@ hipError_t launch_rope_landmark(const uint16_t* k_pre, int b, int64_t S, int H, 
 __global__ __launch_bounds__(256) void outlier_kernel(const float* __restrict__ min_cos, int n_c,
                                                       int n_elig, int O, uint32_t* __restrict__ keys,
                                                       int32_t* __restrict__ outlier_ids) {
-  __shared__ int hist[2048];
+  __shared__ int hist[2048 + kTopkSmall];
   __shared__ int sh[32];
   const int p = blockIdx.x;
   const float* mc = min_cos + (int64_t)p * n_c;

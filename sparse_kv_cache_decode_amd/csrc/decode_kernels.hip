@@ -21,6 +21,8 @@
 // Workgroups never wait on one another inside a kernel: device-scope fences on
 // gfx950 write back and invalidate the whole L2, so every cross-workgroup
 // hand-off goes through a kernel boundary instead.
+#include <algorithm>
+
 #include "skv_internal.h"
 #include "skv_select.h"
 
@@ -153,13 +155,27 @@ hipError_t launch_score(const DecodeArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Select + index scan, one workgroup of kSelThreads per pair.  All per-pair state
-// the scan touches (slot map, resident bitmap, miss / free lists) is staged in LDS;
-// the chunk keys too when they fit (select_lds_bytes decides), else they go to the
-// global key scratch.  LDS layout (ints): hist[2048] | sh[32] | sel[K] | selch[K] |
-// freel[K] | missp[K] | scl[K] | resl[res_words] | keys[n_cand].
+// Selection, workgroups of kSelThreads.  The chunk key of a candidate is
+// max_g(l_g - LSE_g), the log of the group max of the softmax probabilities,
+// with LSE_g combined from the score workgroups' partials; keys are compared as
+// order-preserving uint32.
+//  select_kernel, one workgroup per pair, up to 32K candidates: thread t forms
+//    the keys of candidates [t*PT, t*PT + PT) in registers straight from the
+//    logits, the top-K is found by a radix select whose histogram lives in LDS
+//    (ascending candidate order, ties to the lower index), then the temporal-
+//    cache index scan runs.  All per-pair state the scan touches (slot map,
+//    resident bitmap, miss / free lists) is staged in LDS.
+//  With more candidates they are cut into n_part parts whose top-K are taken
+//    by separate workgroups (part_topk_kernel, grid (n_part, P)); merged_select_
+//    kernel then selects from the merged part lists.  The pair's top-K is
+//    contained in that union: an element beaten by K others inside its part is
+//    beaten by them overall.
+// LDS layout of both per-pair kernels (ints): hist[2048 + kTopkSmall] | sh[32] |
+// sel[K] | selch[K] | freel[K] | missp[K] | scl[K] | resl[res_words], followed in
+// merged_select_kernel by keys[m] | idx[m] (m the merged length) when they fit.
 
 constexpr int kSelThreads = 1024;
+constexpr int kHist = 2048 + kTopkSmall;
 
 __device__ __forceinline__ bool sorted_contains(const int* v, int n, int x) {
   int lo = 0, hi = n;
@@ -170,82 +186,105 @@ __device__ __forceinline__ bool sorted_contains(const int* v, int n, int x) {
   return lo < n && v[lo] == x;
 }
 
-size_t select_lds_bytes(int top_k, int res_words, int n_cand, bool keys_in_lds) {
-  return (size_t)(2048 + 32 + 5 * top_k + res_words + (keys_in_lds ? n_cand : 0)) * sizeof(int);
+void select_partition(int n_cand, int top_k, int pairs, int* n_part, int* part_size) {
+  // one part up to kSelThreads * 32 candidates (the register-resident select);
+  // beyond, about one stage-1 workgroup per CU, parts at least 4K long (a part's
+  // top-K is at most a quarter of it) and a merged length of at most 16384
+  int np = 1;
+  if (n_cand > kSelThreads * 32) {
+    np = std::min({(256 + pairs - 1) / pairs, n_cand / (4 * top_k), 16384 / top_k, 64});
+    np = std::max(np, 2);
+  }
+  const int ps = (n_cand + np - 1) / np;
+  *part_size = ps;
+  *n_part = (n_cand + ps - 1) / ps;
 }
 
-bool select_keys_in_lds(int top_k, int res_words, int n_cand) {
-  return select_lds_bytes(top_k, res_words, n_cand, true) <= kSelLdsMax;
+static size_t part_lds_bytes(int part_size, bool keys_in_lds) {
+  return (size_t)(kHist + 32 + (keys_in_lds ? part_size : 0)) * sizeof(int);
 }
 
-template <int G, bool LDS_KEYS>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
-  extern __shared__ int smem[];
-  const int K = a.top_k, n_cand = a.n_cand, RW = a.res_words;
-  int* hist = smem;
-  int* sh = smem + 2048;
-  int* sel = sh + 32;        // selected candidate indices, ascending
-  int* selch = sel + K;      // their chunk ids
-  int* freel = selch + K;    // evicted slots, ascending
-  int* missp = freel + K;    // positions in sel of the missed chunks, ascending
-  int* scl = missp + K;      // slot -> candidate index (copy of the pair's slot map)
-  uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);   // resident bitmap copy
-  uint32_t* lkeys = resl + RW;
-  __shared__ float lse[16];
-  const int p = blockIdx.x;
+static int merged_len(const DecodeArgs& a) {
+  const int kp0 = std::min(a.top_k, a.part_size);
+  const int kpl = std::min(a.top_k, a.n_cand - (a.n_part - 1) * a.part_size);
+  return (a.n_part - 1) * kp0 + kpl;
+}
+
+static size_t select_lds_bytes(const DecodeArgs& a, bool merged_in_lds) {
+  return (size_t)(kHist + 32 + 5 * a.top_k + a.res_words + (merged_in_lds ? 2 * merged_len(a) : 0)) *
+         sizeof(int);
+}
+
+// LSE_g of the pair's G heads from the score workgroups' partials, by waves 0..G-1.
+template <int G>
+__device__ __forceinline__ void pair_lse(const DecodeArgs& a, int p, float* lse) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const float* lg = a.logits + (int64_t)p * G * a.ncp;
-  int32_t* sc = a.slot_cand + (int64_t)p * K;
-  int32_t* sch = a.slot_chunk + (int64_t)p * K;
-  uint32_t* res = a.resident + (int64_t)p * RW;
-  for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
-  for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
+  if (w < G) {
+    const float* src = a.lse_part + (int64_t)p * a.nb_score * G * 2;
+    float M = kNegBig;
+    for (int k = lane; k < a.nb_score; k += 64) M = fmaxf(M, src[(k * G + w) * 2]);
+    M = wave_max(M);
+    float S = 0.f;
+    for (int k = lane; k < a.nb_score; k += 64) S += src[(k * G + w) * 2 + 1] * __expf(src[(k * G + w) * 2] - M);
+    S = wave_sum(S);
+    if (lane == 0) lse[w] = M + __logf(S);
+  }
+}
 
-  // chunk keys: max_g(logit_g - LSE_g); the first round of logit loads is in flight
-  // while the LSE of every head is reduced from the score workgroups' partials
-  uint32_t* kp = LDS_KEYS ? lkeys : a.keys + (int64_t)p * n_cand;
+// Keys of candidates [c0, c0 + n) of pair p into kp[0, n); returns this thread's
+// min / max of them.  The first round of logit loads is in flight while the LSE
+// of every head is reduced.
+template <int G>
+__device__ __forceinline__ void chunk_keys(const DecodeArgs& a, int p, int c0, int n, uint32_t* kp,
+                                           float* lse, uint32_t& lo, uint32_t& hi) {
+  const float* lg = a.logits + (int64_t)p * G * a.ncp + c0;
   constexpr int R = (64 / G) < 16 ? (64 / G) : 16;
-  for (int c0 = 0; c0 < n_cand; c0 += R * kSelThreads) {
+  lo = 0xffffffffu;
+  hi = 0u;
+  for (int i0 = 0; i0 < n; i0 += R * kSelThreads) {
     float lv[R][G];
 #pragma unroll
     for (int u = 0; u < R; u++) {
-      const int c = c0 + u * kSelThreads + threadIdx.x;
+      const int i = i0 + u * kSelThreads + threadIdx.x;
 #pragma unroll
-      for (int g = 0; g < G; g++) lv[u][g] = c < n_cand ? lg[(int64_t)g * a.ncp + c] : 0.f;
+      for (int g = 0; g < G; g++) lv[u][g] = i < n ? lg[(int64_t)g * a.ncp + i] : 0.f;
     }
-    if (c0 == 0) {
-      if (w < G) {
-        const float* src = a.lse_part + (int64_t)p * a.nb_score * G * 2;
-        float M = kNegBig;
-        for (int k = lane; k < a.nb_score; k += 64) M = fmaxf(M, src[(k * G + w) * 2]);
-        M = wave_max(M);
-        float S = 0.f;
-        for (int k = lane; k < a.nb_score; k += 64) S += src[(k * G + w) * 2 + 1] * __expf(src[(k * G + w) * 2] - M);
-        S = wave_sum(S);
-        if (lane == 0) lse[w] = M + __logf(S);
-      }
+    if (i0 == 0) {
+      pair_lse<G>(a, p, lse);
       __syncthreads();
     }
 #pragma unroll
     for (int u = 0; u < R; u++) {
-      const int c = c0 + u * kSelThreads + threadIdx.x;
+      const int i = i0 + u * kSelThreads + threadIdx.x;
       float best = lv[u][0] - lse[0];
 #pragma unroll
       for (int g = 1; g < G; g++) best = fmaxf(best, lv[u][g] - lse[g]);
-      if (c < n_cand) kp[c] = float_key(best);
+      if (i < n) {
+        const uint32_t key = float_key(best);
+        kp[i] = key;
+        lo = min(lo, key);
+        hi = max(hi, key);
+      }
     }
   }
   __syncthreads();
-  block_topk<kSelThreads>([&](int i) { return kp[i]; }, n_cand, K, hist, sh,
-                          [&](int pos, int i) { if (pos < K) sel[pos] = i; });
-  const int32_t* cmap = a.cand_map + (int64_t)p * n_cand;
+}
+
+// Index scan of pair p against the chunks its slots hold, given the selection
+// sel[0, K) (ascending candidate indices): chunk ids out, hits / misses, slot
+// reassignment, miss list, counters.
+__device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* selch, int* freel, int* missp,
+                           int* scl, uint32_t* resl) {
+  const int K = a.top_k, RW = a.res_words;
+  int32_t* sc = a.slot_cand + (int64_t)p * K;
+  int32_t* sch = a.slot_chunk + (int64_t)p * K;
+  uint32_t* res = a.resident + (int64_t)p * RW;
+  const int32_t* cmap = a.cand_map + (int64_t)p * a.n_cand;
   for (int i = threadIdx.x; i < K; i += kSelThreads) {
     const int ch = cmap[sel[i]];
     selch[i] = ch;
     a.chunk_ids[(int64_t)p * K + i] = ch;
   }
-
-  // ---- temporal-cache index scan against the chunks held by the slots
   const bool has_prev = a.temporal && scl[0] >= 0;
   int n_free = 0, n_miss = 0;
   for (int t0 = 0; t0 < K; t0 += kSelThreads) {
@@ -294,25 +333,181 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
   }
 }
 
+template <int G, int PT>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
+  extern __shared__ int smem[];
+  const int K = a.top_k, RW = a.res_words, n = a.n_cand;
+  int* hist = smem;
+  int* sh = smem + kHist;
+  int* sel = sh + 32;        // selected candidate indices, ascending
+  int* selch = sel + K;      // their chunk ids
+  int* freel = selch + K;    // evicted slots, ascending
+  int* missp = freel + K;    // positions in sel of the missed chunks, ascending
+  int* scl = missp + K;      // slot -> candidate index (copy of the pair's slot map)
+  uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);   // resident bitmap copy
+  __shared__ float lse[16];
+  const int p = blockIdx.x;
+  // this thread's candidates [i0, i0 + nv); logits of GB heads in flight at once
+  const int i0 = threadIdx.x * PT;
+  const int nv = max(0, min(PT, n - i0));
+  const float* lg = a.logits + (int64_t)p * G * a.ncp + i0;
+  // all heads at once when their logits fit in 64 registers, else 32 at a time
+  constexpr int GB = G * PT <= 64 ? G : (32 / PT < 1 ? 1 : 32 / PT);
+  f32x4 lv[GB][PT / 4];
+  auto load_heads = [&](int g0) {
+#pragma unroll
+    for (int gb = 0; gb < GB; gb++)
+#pragma unroll
+      for (int j = 0; j < PT / 4; j++)
+        lv[gb][j] = i0 + 4 * j < a.ncp ? *reinterpret_cast<const f32x4*>(lg + (int64_t)(g0 + gb) * a.ncp + 4 * j)
+                                       : (f32x4){0.f, 0.f, 0.f, 0.f};
+  };
+  load_heads(0);
+  const int32_t* sc = a.slot_cand + (int64_t)p * K;
+  const uint32_t* res = a.resident + (int64_t)p * RW;
+  for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
+  for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
+  for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
+  pair_lse<G>(a, p, lse);
+  __syncthreads();
+  float best[PT];
+  auto fold_heads = [&](int g0) {
+#pragma unroll
+    for (int gb = 0; gb < GB; gb++) {
+      const float l = lse[g0 + gb];
+#pragma unroll
+      for (int j = 0; j < PT / 4; j++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const float v = lv[gb][j][c] - l;
+          best[4 * j + c] = (g0 + gb == 0) ? v : fmaxf(best[4 * j + c], v);
+        }
+    }
+  };
+  fold_heads(0);
+#pragma unroll 1
+  for (int g0 = GB; g0 < G; g0 += GB) {   // one group of heads in registers at a time
+    load_heads(g0);
+    fold_heads(g0);
+  }
+  uint32_t key[PT];
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int e = 0; e < PT; e++) {
+    key[e] = float_key(best[e]);
+    if (e < nv) {
+      lo = min(lo, key[e]);
+      hi = max(hi, key[e]);
+    }
+  }
+  block_range<kSelThreads>(lo, hi, sh);
+  block_topk_reg<kSelThreads, PT>(key, nv, K, lo, hi, hist, sh, true,
+                                  [&](int pos, int e) { sel[pos] = i0 + e; });
+  index_scan(a, p, sh, sel, selch, freel, missp, scl, resl);
+}
+
+template <int G, bool LDS_KEYS>
+__global__ __launch_bounds__(kSelThreads) void part_topk_kernel(DecodeArgs a) {
+  extern __shared__ int smem[];
+  int* hist = smem;
+  int* sh = smem + kHist;
+  uint32_t* lkeys = reinterpret_cast<uint32_t*>(sh + 32);
+  __shared__ float lse[16];
+  const int part = blockIdx.x, p = blockIdx.y;
+  const int K = a.top_k;
+  const int c0 = part * a.part_size, n = min(a.part_size, a.n_cand - c0);
+  uint32_t* kp = LDS_KEYS ? lkeys : a.keys + (int64_t)p * a.n_cand + c0;
+  uint32_t lo, hi;
+  chunk_keys<G>(a, p, c0, n, kp, lse, lo, hi);
+  block_range<kSelThreads>(lo, hi, sh);
+  uint32_t* ok = a.part_keys + ((int64_t)p * a.n_part + part) * K;
+  int32_t* oi = a.part_idx + ((int64_t)p * a.n_part + part) * K;
+  block_topk<kSelThreads>([&](int i) { return kp[i]; }, n, min(K, n), lo, hi, hist, sh,
+                          [&](int pos, int i) { ok[pos] = kp[i]; oi[pos] = c0 + i; });
+}
+
+template <bool IN_LDS>
+__global__ __launch_bounds__(kSelThreads) void merged_select_kernel(DecodeArgs a) {
+  extern __shared__ int smem[];
+  const int K = a.top_k, RW = a.res_words;
+  int* hist = smem;
+  int* sh = smem + kHist;
+  int* sel = sh + 32;
+  int* selch = sel + K;
+  int* freel = selch + K;
+  int* missp = freel + K;
+  int* scl = missp + K;
+  uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);
+  const int p = blockIdx.x;
+  const int32_t* sc = a.slot_cand + (int64_t)p * K;
+  const uint32_t* res = a.resident + (int64_t)p * RW;
+  for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
+  for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
+  // merged part lists: part j contributes min(K, its length) entries; every part
+  // but the last has the full length, so entry i is (i / kp0, i % kp0)
+  const int kp0 = min(K, a.part_size);
+  const int m = (a.n_part - 1) * kp0 + min(K, a.n_cand - (a.n_part - 1) * a.part_size);
+  const uint32_t* gk = a.part_keys + (int64_t)p * a.n_part * K;
+  const int32_t* gi = a.part_idx + (int64_t)p * a.n_part * K;
+  uint32_t* mkeys = resl + RW;
+  int* midx = reinterpret_cast<int*>(mkeys + m);
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = threadIdx.x; i < m; i += kSelThreads) {
+    const int off = (i / kp0) * K + i % kp0;
+    const uint32_t key = gk[off];
+    if (IN_LDS) {
+      mkeys[i] = key;
+      midx[i] = gi[off];
+    }
+    lo = min(lo, key);
+    hi = max(hi, key);
+  }
+  block_range<kSelThreads>(lo, hi, sh);
+  block_topk<kSelThreads>(
+      [&](int i) { return IN_LDS ? mkeys[i] : gk[(i / kp0) * K + i % kp0]; }, m, K, lo, hi, hist, sh,
+      [&](int pos, int i) { sel[pos] = IN_LDS ? midx[i] : gi[(i / kp0) * K + i % kp0]; });
+  index_scan(a, p, sh, sel, selch, freel, missp, scl, resl);
+}
+
+template <class F>
+static hipError_t allow_lds(F* kernel) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             kSelLdsMax);
+}
+
 template <int G>
 static hipError_t launch_select_g(const DecodeArgs& a, hipStream_t st) {
   const int P = a.batch * a.n_kv;
-  const bool lds_keys = select_keys_in_lds(a.top_k, a.res_words, a.n_cand);
-  const size_t lds = select_lds_bytes(a.top_k, a.res_words, a.n_cand, lds_keys);
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<G, true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSelLdsMax);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<G, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kSelLdsMax);
+    hipError_t e = allow_lds(&select_kernel<G, 16>);
+    if (e == hipSuccess) e = allow_lds(&select_kernel<G, 32>);
+    if (e == hipSuccess) e = allow_lds(&part_topk_kernel<G, true>);
+    if (e == hipSuccess) e = allow_lds(&part_topk_kernel<G, false>);
+    if (e == hipSuccess) e = allow_lds(&merged_select_kernel<true>);
+    if (e == hipSuccess) e = allow_lds(&merged_select_kernel<false>);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  if (lds_keys)
-    select_kernel<G, true><<<P, kSelThreads, lds, st>>>(a);
+  if (a.n_part == 1) {
+    const size_t lds = select_lds_bytes(a, false);
+    if (a.n_cand <= kSelThreads * 16)
+      select_kernel<G, 16><<<P, kSelThreads, lds, st>>>(a);
+    else
+      select_kernel<G, 32><<<P, kSelThreads, lds, st>>>(a);
+    return hipGetLastError();
+  }
+  const bool part_lds = part_lds_bytes(a.part_size, true) <= (size_t)kSelLdsMax;
+  const dim3 g1(a.n_part, P);
+  if (part_lds)
+    part_topk_kernel<G, true><<<g1, kSelThreads, part_lds_bytes(a.part_size, true), st>>>(a);
   else
-    select_kernel<G, false><<<P, kSelThreads, lds, st>>>(a);
+    part_topk_kernel<G, false><<<g1, kSelThreads, part_lds_bytes(a.part_size, false), st>>>(a);
+  const bool in_lds = select_lds_bytes(a, true) <= (size_t)kSelLdsMax;
+  if (in_lds)
+    merged_select_kernel<true><<<P, kSelThreads, select_lds_bytes(a, true), st>>>(a);
+  else
+    merged_select_kernel<false><<<P, kSelThreads, select_lds_bytes(a, false), st>>>(a);
   return hipGetLastError();
 }
 
@@ -592,13 +787,17 @@ hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st) {
 //    tokens tg, tg+4, tg+8, tg+12 for every head.
 // The four waves of a workgroup merge through LDS into one split partial.
 
+// 16-token tiles per wave: as many as the registers allow at two waves per SIMD,
+// so that the grid of a long-context step fits the chip's wave slots in one round
+constexpr int attn_tiles(int group) { return group <= 4 ? 5 : (group <= 8 ? 3 : 2); }
+
 template <int G, int C>
 struct AttnShape {
-  static constexpr int NT = G <= 4 ? 4 : 2;     // 16-token tiles per wave
+  static constexpr int NT = attn_tiles(G);
   static constexpr int NUW = NT * 16 / C;       // units per wave
 };
 
-int attn_units_per_wave(int group, int chunk) { return (group <= 4 ? 4 : 2) * 16 / chunk; }
+int attn_units_per_wave(int group, int chunk) { return attn_tiles(group) * 16 / chunk; }
 
 template <int C>
 __device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, int u) {

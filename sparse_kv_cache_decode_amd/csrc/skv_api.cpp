@@ -17,7 +17,7 @@ using namespace skv;
 struct skv_layer {
   skv_config cfg;
   int G = 0, n_c = 0, n_win = 0, n_cand = 0, P = 0, HD = 0, U = 0;
-  int nb_score = 0, cpb = 0, ncp = 0, n_split = 0, upw = 0, res_words = 0;
+  int nb_score = 0, cpb = 0, ncp = 0, n_split = 0, upw = 0, res_words = 0, n_part = 0, part_size = 0;
   bool poisoned = false;
   bool need_reset = false;
   const uint16_t* v_dev = nullptr;   // device-visible address of the value store
@@ -28,7 +28,8 @@ struct skv_layer {
   int32_t *cand_map = nullptr, *outlier_ids = nullptr, *slot_cand = nullptr, *slot_chunk = nullptr,
           *miss_slot = nullptr, *miss_chunk = nullptr, *miss_cand = nullptr, *free_slot = nullptr,
           *n_miss = nullptr, *hits_last = nullptr;
-  uint32_t *resident = nullptr, *keys = nullptr;
+  uint32_t *resident = nullptr, *keys = nullptr, *part_keys = nullptr;
+  int32_t* part_idx = nullptr;
   long long *hits_total = nullptr, *miss_total = nullptr;
   float *logits = nullptr, *lse_part = nullptr, *attn_part = nullptr, *min_cos = nullptr;
   double* inv_freq = nullptr;
@@ -191,6 +192,10 @@ DecodeArgs decode_args(skv_layer* h) {
   a.logits = h->logits;
   a.lse_part = h->lse_part;
   a.keys = h->keys;
+  a.n_part = h->n_part;
+  a.part_size = h->part_size;
+  a.part_keys = h->part_keys;
+  a.part_idx = h->part_idx;
   a.attn_part = h->attn_part;
   return a;
 }
@@ -268,6 +273,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->upw = 4 * upw_wave;
     if ((int64_t)h->upw * kMaxSplits < h->U) h->upw = 4 * nuw;
     h->n_split = (h->U + h->upw - 1) / h->upw;
+    select_partition(n_cand, K, P, &h->n_part, &h->part_size);
   }
 
   // persistent state, one allocation
@@ -293,6 +299,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const size_t oHl = cv.take<int32_t>(P);
   const size_t oRes = cv.take<uint32_t>((size_t)P * h->res_words);
   const size_t oKeys = cv.take<uint32_t>((size_t)P * n_c);
+  const size_t oPk = cv.take<uint32_t>((size_t)P * h->n_part * K);
+  const size_t oPi = cv.take<int32_t>((size_t)P * h->n_part * K);
   const size_t oHt = cv.take<long long>(P);
   const size_t oMt = cv.take<long long>(P);
   const size_t oLg = cv.take<float>((size_t)P * G * h->ncp);
@@ -355,6 +363,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->hits_last = (int32_t*)(base + oHl);
     h->resident = (uint32_t*)(base + oRes);
     h->keys = (uint32_t*)(base + oKeys);
+    h->part_keys = (uint32_t*)(base + oPk);
+    h->part_idx = (int32_t*)(base + oPi);
     h->hits_total = (long long*)(base + oHt);
     h->miss_total = (long long*)(base + oMt);
     h->logits = (float*)(base + oLg);

@@ -53,6 +53,9 @@ struct DecodeArgs {
   float* logits;              // [P][G][ncp]
   float* lse_part;            // [P][nb_score][G][2]
   uint32_t* keys;             // [P][n_cand]
+  int n_part, part_size;      // selection stage 1: candidate parts per pair and their size
+  uint32_t* part_keys;        // [P][n_part][K] each part's top-K keys, ascending candidate index
+  int32_t* part_idx;          // [P][n_part][K] their candidate indices
   float* attn_part;           // [P][n_split][G][d + 2]
   // outputs
   float* out;                 // [b][Hq][d]
@@ -83,8 +86,9 @@ hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_
 hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_score(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
-size_t select_lds_bytes(int top_k, int res_words, int n_cand, bool keys_in_lds);
-bool select_keys_in_lds(int top_k, int res_words, int n_cand);
+// Two-stage top-K: the candidates of a pair are cut into n_part parts whose
+// top-K are taken by separate workgroups (stage 1), then merged per pair (stage 2).
+void select_partition(int n_cand, int top_k, int pairs, int* n_part, int* part_size);
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);

@@ -124,3 +124,12 @@ def test_reset_and_identical_query():
     assert s["steps"] == 1 and s["last_hits"] == 0 and s["last_misses"] == shape.pairs * shape.top_k
     assert torch.equal(ids2, ids0) and torch.equal(out2, out0)
     layer.close()
+
+
+def test_split_selection_many_candidates():
+    # n_cand = 34816 - 3 - 4 = 34809 > 32768: the candidates are cut into parts
+    # whose top-K are merged (the path of the 1M-token workload)
+    s = _small(batch=1, n_q_heads=2, n_kv_heads=1, seq_len=278528, rank=16, latent_rank=16,
+               top_k=64, n_outlier=3)
+    assert s.n_cand > 32768
+    _run(s, steps=2)
