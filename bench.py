@@ -203,6 +203,24 @@ def measured_traffic(workload: str, kernel: str):
     return k["hbm_bytes_per_launch"] if k else None
 
 
+def measure_h2d_gbps(nbytes: int = 256 << 20, reps: int = 8) -> float:
+    """Pinned host -> device copy rate (the PCIe ceiling for host-resident values)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    rate = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return rate
+
+
 # ----------------------------------------------------------------------------
 
 
@@ -227,6 +245,12 @@ def main():
     ap.add_argument("--shape", default="llama3_8b_122k")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = model's)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--values", choices=["hbm", "host"], default="hbm",
+                    help="value store in HBM or in pinned host memory (gathered over PCIe)")
+    ap.add_argument("--queries", choices=["drift", "independent"], default="drift",
+                    help="AR(1)-drifting queries (temporal cache hits) or independent draws")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="chunk size C for the 1M-token shape (budget K and O follow C)")
     ap.add_argument("--phase-every", type=int, default=16,
                     help="record per-phase HIP events on every n-th layer of the timed region "
                          "(an event record between kernels costs a few microseconds)")
@@ -259,7 +283,10 @@ def main():
 
     from sparse_kv_cache_decode_amd import skv, synth
 
-    shape = synth.SHAPES[args.shape]
+    shape = synth.glm_chunk_variant(args.chunk) if args.chunk else synth.SHAPES[args.shape]
+    if args.chunk and not args.shape.startswith("glm4"):
+        print("--chunk applies to the 1M-token shape only", file=sys.stderr)
+        return 2
     if args.layers:
         shape = shape.replace(layers=args.layers)
     L, W, K = shape.layers, args.warmup, args.steps
@@ -269,10 +296,18 @@ def main():
     skv.lib()
     layers, qs = [], []
     t0 = time.time()
+    host = args.values == "host"
+    placement = skv.SKV_VALUES_HOST if host else skv.SKV_VALUES_DEVICE
+    pcie_peak = measure_h2d_gbps() if host else None     # before the value stores take pinned memory
     for l in range(L):
         k_pre, v = synth.layer_cache_torch(shape, l, args.seed, dev)
-        layers.append(skv.Layer(shape, k_pre, v))
-        qs.append(synth.queries_torch(shape, k_pre, l, total, args.seed))
+        if host:
+            vh = torch.empty(v.shape, dtype=v.dtype, pin_memory=True)
+            vh.copy_(v)
+            del v
+            v = vh
+        layers.append(skv.Layer(shape, k_pre, v, placement))
+        qs.append(synth.queries_torch(shape, k_pre, l, total, args.seed, mode=args.queries))
         del k_pre, v
         if l % 4 == 3 or l == L - 1:
             log(f"built layer {l + 1}/{L} ({time.time() - t0:.1f}s)")
@@ -324,6 +359,18 @@ def main():
     # and the dense-attention bytes per measured layer time
     S, C, Kc, Oc = shape.seq_len, shape.chunk, shape.top_k, shape.n_outlier
     bt_formula = 2 * S * HBM_PEAK_GBPS / (S / C + 2 * (Kc + Oc) * C) / 1000.0
+    pcie = None
+    if host:
+        host_bytes = misses * C * shape.head_dim * 2          # values of the missed chunks
+        gather_us = phase_avg_us["value_gather"]
+        pcie_gbps = host_bytes / (gather_us * 1e-6) / 1e9 if gather_us > 0 else None
+        # the pages' formula with the measured hit rate and PCIe rate
+        bt_formula = (2 * S * HBM_PEAK_GBPS / (S / C + 2 * (Kc + Oc) * C + (1 - alpha_timed) * Kc * C *
+                                               HBM_PEAK_GBPS / pcie_gbps) / 1000.0) if pcie_gbps else None
+        pcie = {"host_bytes_per_layer_step": int(host_bytes), "gather_us_per_layer": round(gather_us, 2),
+                "achieved_GBps": round(pcie_gbps, 2) if pcie_gbps else None,
+                "pinned_h2d_peak_GBps": round(pcie_peak, 2),
+                "frac_of_peak": round(pcie_gbps / pcie_peak, 4) if pcie_gbps else None}
     dense_bytes = 2 * S * shape.head_dim * 2 * shape.pairs
     bt_measured = dense_bytes / (layer_us * 1e-6) / 1e12
 
@@ -362,7 +409,8 @@ def main():
         "config": {"workload": f"{shape.name}: {L} layers, batch {shape.batch}, S={shape.seq_len}, "
                                f"{shape.n_q_heads} q / {shape.n_kv_heads} KV heads, d={shape.head_dim}, "
                                f"r={shape.rank}, C={shape.chunk}, K={shape.top_k}, O={shape.n_outlier}, "
-                               f"window {shape.window}, values in HBM, AR(1)-drifting queries",
+                               f"window {shape.window}, values in {'pinned host memory' if host else 'HBM'}, "
+                               f"{'AR(1)-drifting' if args.queries == 'drift' else 'independent'} queries",
                    "global_batch": shape.batch, "seq_len": shape.seq_len, "layers": L,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "score_kernel (landmark GEMV)",
@@ -378,8 +426,11 @@ def main():
         "layer_us": round(layer_us, 2),
         "alpha": {"timed_steps": round(alpha_timed, 4), "steps_1_to_end": round(alpha_all, 4),
                   "misses_per_layer_step": round(misses, 1)},
-        "equivalent_bandwidth_TBps": {"formula_values_in_hbm_at_8TBps": round(bt_formula, 1),
-                                      "dense_bytes_over_measured_time": round(bt_measured, 1)},
+        "equivalent_bandwidth_TBps": {
+            ("formula_measured_alpha_and_pcie" if host else "formula_values_in_hbm_at_8TBps"):
+                round(bt_formula, 2) if bt_formula else None,
+            "dense_bytes_over_measured_time": round(bt_measured, 1)},
+        "pcie": pcie,
         "cpu_baseline": cpu,
     }
     if args.calib_copy:

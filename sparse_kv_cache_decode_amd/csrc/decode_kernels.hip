@@ -159,15 +159,16 @@ hipError_t launch_score(const DecodeArgs& a, hipStream_t st) {
 // max_g(l_g - LSE_g), the log of the group max of the softmax probabilities,
 // with LSE_g combined from the score workgroups' partials; keys are compared as
 // order-preserving uint32.
-//  select_kernel, one workgroup per pair, up to 32K candidates: thread t forms
-//    the keys of candidates [t*PT, t*PT + PT) in registers straight from the
-//    logits, the top-K is found by a radix select whose histogram lives in LDS
+//  select_kernel, one workgroup per pair while the pair's logits are at most
+//    256 KB: thread t forms the keys of candidates [t*PT, t*PT + PT) in
+//    registers straight from the logits, the top-K is found by a radix select whose histogram lives in LDS
 //    (ascending candidate order, ties to the lower index), then the temporal-
 //    cache index scan runs.  All per-pair state the scan touches (slot map,
 //    resident bitmap, miss / free lists) is staged in LDS.
-//  With more candidates they are cut into n_part parts whose top-K are taken
-//    by separate workgroups (part_topk_kernel, grid (n_part, P)); merged_select_
-//    kernel then selects from the merged part lists.  The pair's top-K is
+//  With more logits per pair the candidates are cut into n_part parts whose
+//    top-K are taken the same way by separate workgroups (part_topk_kernel,
+//    grid (n_part, P)); merged_select_kernel then selects from the merged part
+//    lists.  The pair's top-K is
 //    contained in that union: an element beaten by K others inside its part is
 //    beaten by them overall.
 // LDS layout of both per-pair kernels (ints): hist[2048 + kTopkSmall] | sh[32] |
@@ -186,23 +187,24 @@ __device__ __forceinline__ bool sorted_contains(const int* v, int n, int x) {
   return lo < n && v[lo] == x;
 }
 
-void select_partition(int n_cand, int top_k, int pairs, int* n_part, int* part_size) {
-  // one part up to kSelThreads * 32 candidates (the register-resident select);
-  // beyond, about one stage-1 workgroup per CU, parts at least 4K long (a part's
-  // top-K is at most a quarter of it) and a merged length of at most 16384
+void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, int* part_size) {
+  // One workgroup per pair while its logits are at most 256 KB (one CU pulls that
+  // in about as fast as a second kernel launch would cost).  Beyond, about one
+  // stage-1 workgroup per CU, parts at least 4K long (a part's top-K is at most a
+  // quarter of it), at most 16K per part (register keys) and a merged length of
+  // at most 16384.
   int np = 1;
-  if (n_cand > kSelThreads * 32) {
+  if ((int64_t)group * n_cand > 65536 || n_cand > kSelThreads * 16) {
     np = std::min({(256 + pairs - 1) / pairs, n_cand / (4 * top_k), 16384 / top_k, 64});
-    np = std::max(np, 2);
+    np = std::max({np, 2, (n_cand + kSelThreads * 16 - 1) / (kSelThreads * 16)});
   }
-  const int ps = (n_cand + np - 1) / np;
+  const int ps = np == 1 ? n_cand : ((n_cand + np - 1) / np + 15) / 16 * 16;   // 16-B aligned parts
   *part_size = ps;
   *n_part = (n_cand + ps - 1) / ps;
 }
 
-static size_t part_lds_bytes(int part_size, bool keys_in_lds) {
-  return (size_t)(kHist + 32 + (keys_in_lds ? part_size : 0)) * sizeof(int);
-}
+// keys per thread of the register-resident selection for n candidates
+static int keys_per_thread(int n) { return n <= kSelThreads * 4 ? 4 : (n <= kSelThreads * 8 ? 8 : 16); }
 
 static int merged_len(const DecodeArgs& a) {
   const int kp0 = std::min(a.top_k, a.part_size);
@@ -229,45 +231,6 @@ __device__ __forceinline__ void pair_lse(const DecodeArgs& a, int p, float* lse)
     S = wave_sum(S);
     if (lane == 0) lse[w] = M + __logf(S);
   }
-}
-
-// Keys of candidates [c0, c0 + n) of pair p into kp[0, n); returns this thread's
-// min / max of them.  The first round of logit loads is in flight while the LSE
-// of every head is reduced.
-template <int G>
-__device__ __forceinline__ void chunk_keys(const DecodeArgs& a, int p, int c0, int n, uint32_t* kp,
-                                           float* lse, uint32_t& lo, uint32_t& hi) {
-  const float* lg = a.logits + (int64_t)p * G * a.ncp + c0;
-  constexpr int R = (64 / G) < 16 ? (64 / G) : 16;
-  lo = 0xffffffffu;
-  hi = 0u;
-  for (int i0 = 0; i0 < n; i0 += R * kSelThreads) {
-    float lv[R][G];
-#pragma unroll
-    for (int u = 0; u < R; u++) {
-      const int i = i0 + u * kSelThreads + threadIdx.x;
-#pragma unroll
-      for (int g = 0; g < G; g++) lv[u][g] = i < n ? lg[(int64_t)g * a.ncp + i] : 0.f;
-    }
-    if (i0 == 0) {
-      pair_lse<G>(a, p, lse);
-      __syncthreads();
-    }
-#pragma unroll
-    for (int u = 0; u < R; u++) {
-      const int i = i0 + u * kSelThreads + threadIdx.x;
-      float best = lv[u][0] - lse[0];
-#pragma unroll
-      for (int g = 1; g < G; g++) best = fmaxf(best, lv[u][g] - lse[g]);
-      if (i < n) {
-        const uint32_t key = float_key(best);
-        kp[i] = key;
-        lo = min(lo, key);
-        hi = max(hi, key);
-      }
-    }
-  }
-  __syncthreads();
 }
 
 // Index scan of pair p against the chunks its slots hold, given the selection
@@ -333,24 +296,18 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
   }
 }
 
-template <int G, int PT>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
-  extern __shared__ int smem[];
-  const int K = a.top_k, RW = a.res_words, n = a.n_cand;
-  int* hist = smem;
-  int* sh = smem + kHist;
-  int* sel = sh + 32;        // selected candidate indices, ascending
-  int* selch = sel + K;      // their chunk ids
-  int* freel = selch + K;    // evicted slots, ascending
-  int* missp = freel + K;    // positions in sel of the missed chunks, ascending
-  int* scl = missp + K;      // slot -> candidate index (copy of the pair's slot map)
-  uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);   // resident bitmap copy
-  __shared__ float lse[16];
-  const int p = blockIdx.x;
-  // this thread's candidates [i0, i0 + nv); logits of GB heads in flight at once
+// Keys of candidates [c0 + PT*t, c0 + PT*t + nv) of pair p for thread t, in
+// registers, with the thread's min / max; returns nv.  The G logits of those
+// candidates are loaded with 16-byte loads (GB heads in flight at once) before
+// the LSE of every head is reduced; `stage` issues the caller's other staging
+// work before the barrier, and hist[0, 2048) is cleared in the same window.
+template <int G, int PT, class Stage>
+__device__ __forceinline__ int reg_keys(const DecodeArgs& a, int p, int c0, int n, float* lse, int* hist,
+                                        uint32_t (&key)[PT], uint32_t& lo, uint32_t& hi, Stage stage) {
   const int i0 = threadIdx.x * PT;
   const int nv = max(0, min(PT, n - i0));
-  const float* lg = a.logits + (int64_t)p * G * a.ncp + i0;
+  const int cb = c0 + i0;                        // a multiple of 4: 16-byte aligned rows
+  const float* lg = a.logits + (int64_t)p * G * a.ncp + cb;
   // all heads at once when their logits fit in 64 registers, else 32 at a time
   constexpr int GB = G * PT <= 64 ? G : (32 / PT < 1 ? 1 : 32 / PT);
   f32x4 lv[GB][PT / 4];
@@ -359,14 +316,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
     for (int gb = 0; gb < GB; gb++)
 #pragma unroll
       for (int j = 0; j < PT / 4; j++)
-        lv[gb][j] = i0 + 4 * j < a.ncp ? *reinterpret_cast<const f32x4*>(lg + (int64_t)(g0 + gb) * a.ncp + 4 * j)
-                                       : (f32x4){0.f, 0.f, 0.f, 0.f};
+        lv[gb][j] = nv > 4 * j && cb + 4 * j < a.ncp
+                        ? *reinterpret_cast<const f32x4*>(lg + (int64_t)(g0 + gb) * a.ncp + 4 * j)
+                        : (f32x4){0.f, 0.f, 0.f, 0.f};
   };
   load_heads(0);
-  const int32_t* sc = a.slot_cand + (int64_t)p * K;
-  const uint32_t* res = a.resident + (int64_t)p * RW;
-  for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
-  for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
+  stage();
   for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
   pair_lse<G>(a, p, lse);
   __syncthreads();
@@ -390,8 +345,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
     load_heads(g0);
     fold_heads(g0);
   }
-  uint32_t key[PT];
-  uint32_t lo = 0xffffffffu, hi = 0u;
+  lo = 0xffffffffu;
+  hi = 0u;
 #pragma unroll
   for (int e = 0; e < PT; e++) {
     key[e] = float_key(best[e]);
@@ -400,30 +355,56 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
       hi = max(hi, key[e]);
     }
   }
+  return nv;
+}
+
+template <int G, int PT>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
+  extern __shared__ int smem[];
+  const int K = a.top_k, RW = a.res_words;
+  int* hist = smem;
+  int* sh = smem + kHist;
+  int* sel = sh + 32;        // selected candidate indices, ascending
+  int* selch = sel + K;      // their chunk ids
+  int* freel = selch + K;    // evicted slots, ascending
+  int* missp = freel + K;    // positions in sel of the missed chunks, ascending
+  int* scl = missp + K;      // slot -> candidate index (copy of the pair's slot map)
+  uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);   // resident bitmap copy
+  __shared__ float lse[16];
+  const int p = blockIdx.x;
+  const int32_t* sc = a.slot_cand + (int64_t)p * K;
+  const uint32_t* res = a.resident + (int64_t)p * RW;
+  uint32_t key[PT], lo, hi;
+  const int nv = reg_keys<G, PT>(a, p, 0, a.n_cand, lse, hist, key, lo, hi, [&] {
+    for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
+    for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
+  });
   block_range<kSelThreads>(lo, hi, sh);
+  const int i0 = threadIdx.x * PT;
   block_topk_reg<kSelThreads, PT>(key, nv, K, lo, hi, hist, sh, true,
                                   [&](int pos, int e) { sel[pos] = i0 + e; });
   index_scan(a, p, sh, sel, selch, freel, missp, scl, resl);
 }
 
-template <int G, bool LDS_KEYS>
+template <int G, int PT>
 __global__ __launch_bounds__(kSelThreads) void part_topk_kernel(DecodeArgs a) {
   extern __shared__ int smem[];
   int* hist = smem;
   int* sh = smem + kHist;
-  uint32_t* lkeys = reinterpret_cast<uint32_t*>(sh + 32);
   __shared__ float lse[16];
   const int part = blockIdx.x, p = blockIdx.y;
   const int K = a.top_k;
   const int c0 = part * a.part_size, n = min(a.part_size, a.n_cand - c0);
-  uint32_t* kp = LDS_KEYS ? lkeys : a.keys + (int64_t)p * a.n_cand + c0;
-  uint32_t lo, hi;
-  chunk_keys<G>(a, p, c0, n, kp, lse, lo, hi);
+  uint32_t key[PT], lo, hi;
+  const int nv = reg_keys<G, PT>(a, p, c0, n, lse, hist, key, lo, hi, [] {});
   block_range<kSelThreads>(lo, hi, sh);
   uint32_t* ok = a.part_keys + ((int64_t)p * a.n_part + part) * K;
   int32_t* oi = a.part_idx + ((int64_t)p * a.n_part + part) * K;
-  block_topk<kSelThreads>([&](int i) { return kp[i]; }, n, min(K, n), lo, hi, hist, sh,
-                          [&](int pos, int i) { ok[pos] = kp[i]; oi[pos] = c0 + i; });
+  const int ci = c0 + threadIdx.x * PT;
+  block_topk_reg<kSelThreads, PT>(key, nv, min(K, n), lo, hi, hist, sh, true, [&](int pos, int e) {
+    ok[pos] = key[e];
+    oi[pos] = ci + e;
+  });
 }
 
 template <bool IN_LDS>
@@ -475,40 +456,37 @@ static hipError_t allow_lds(F* kernel) {
                              kSelLdsMax);
 }
 
-template <int G>
-static hipError_t launch_select_g(const DecodeArgs& a, hipStream_t st) {
+template <int G, int PT>
+static hipError_t launch_select_pt(const DecodeArgs& a, hipStream_t st) {
   const int P = a.batch * a.n_kv;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = allow_lds(&select_kernel<G, 16>);
-    if (e == hipSuccess) e = allow_lds(&select_kernel<G, 32>);
-    if (e == hipSuccess) e = allow_lds(&part_topk_kernel<G, true>);
-    if (e == hipSuccess) e = allow_lds(&part_topk_kernel<G, false>);
+    hipError_t e = allow_lds(&select_kernel<G, PT>);
     if (e == hipSuccess) e = allow_lds(&merged_select_kernel<true>);
     if (e == hipSuccess) e = allow_lds(&merged_select_kernel<false>);
     if (e != hipSuccess) return e;
     attr = true;
   }
   if (a.n_part == 1) {
-    const size_t lds = select_lds_bytes(a, false);
-    if (a.n_cand <= kSelThreads * 16)
-      select_kernel<G, 16><<<P, kSelThreads, lds, st>>>(a);
-    else
-      select_kernel<G, 32><<<P, kSelThreads, lds, st>>>(a);
+    select_kernel<G, PT><<<P, kSelThreads, select_lds_bytes(a, false), st>>>(a);
     return hipGetLastError();
   }
-  const bool part_lds = part_lds_bytes(a.part_size, true) <= (size_t)kSelLdsMax;
-  const dim3 g1(a.n_part, P);
-  if (part_lds)
-    part_topk_kernel<G, true><<<g1, kSelThreads, part_lds_bytes(a.part_size, true), st>>>(a);
-  else
-    part_topk_kernel<G, false><<<g1, kSelThreads, part_lds_bytes(a.part_size, false), st>>>(a);
+  part_topk_kernel<G, PT><<<dim3(a.n_part, P), kSelThreads, (kHist + 32) * sizeof(int), st>>>(a);
   const bool in_lds = select_lds_bytes(a, true) <= (size_t)kSelLdsMax;
   if (in_lds)
     merged_select_kernel<true><<<P, kSelThreads, select_lds_bytes(a, true), st>>>(a);
   else
     merged_select_kernel<false><<<P, kSelThreads, select_lds_bytes(a, false), st>>>(a);
   return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_select_g(const DecodeArgs& a, hipStream_t st) {
+  switch (keys_per_thread(a.part_size)) {
+    case 4: return launch_select_pt<G, 4>(a, st);
+    case 8: return launch_select_pt<G, 8>(a, st);
+    default: return launch_select_pt<G, 16>(a, st);
+  }
 }
 
 hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {

@@ -273,7 +273,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->upw = 4 * upw_wave;
     if ((int64_t)h->upw * kMaxSplits < h->U) h->upw = 4 * nuw;
     h->n_split = (h->U + h->upw - 1) / h->upw;
-    select_partition(n_cand, K, P, &h->n_part, &h->part_size);
+    select_partition(n_cand, K, G, P, &h->n_part, &h->part_size);
   }
 
   // persistent state, one allocation

@@ -88,7 +88,7 @@ hipError_t launch_score(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
 // Two-stage top-K: the candidates of a pair are cut into n_part parts whose
 // top-K are taken by separate workgroups (stage 1), then merged per pair (stage 2).
-void select_partition(int n_cand, int top_k, int pairs, int* n_part, int* part_size);
+void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, int* part_size);
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);

@@ -133,3 +133,11 @@ def test_split_selection_many_candidates():
                top_k=64, n_outlier=3)
     assert s.n_cand > 32768
     _run(s, steps=2)
+
+
+def test_split_selection_group_of_eight():
+    # G * n_cand = 8 * 8674 > 65536 logits per pair: selection in parts of 592
+    s = _small(batch=1, n_q_heads=16, n_kv_heads=2, seq_len=69632, rank=32, latent_rank=32,
+               top_k=136, n_outlier=26)
+    assert s.group * s.n_cand > 65536
+    _run(s, steps=2)
