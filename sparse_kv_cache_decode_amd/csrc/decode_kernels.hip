@@ -70,14 +70,13 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
   const int col = lane & 15, kq = lane >> 4;
   const int hq = a.n_kv * G;
 
+  // Loads are unconditional (branch-free code keeps the compiler's wait counts
+  // exact): head columns past G repeat head G-1 and landmark rows past the block
+  // repeat its last row; neither output is used.
   bf16x8 bq[4];
+  const uint16_t* qp = a.q + ((int64_t)b * hq + h * G + min(col, G - 1)) * kHeadDim + kq * 8;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    u32x4 wq = {0u, 0u, 0u, 0u};
-    if (col < G)
-      wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + h * G + col) * kHeadDim + j * 32 + kq * 8);
-    bq[j] = __builtin_bit_cast(bf16x8, wq);
-  }
+  for (int j = 0; j < 4; j++) bq[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + j * 32));
   const int c0 = blk * a.cpb, c1 = min(a.n_cand, c0 + a.cpb);
   const uint16_t* Lp = a.L + (int64_t)p * a.n_cand * kHeadDim;
   float* lg = a.logits + ((int64_t)p * G + (col < G ? col : 0)) * a.ncp;
@@ -87,13 +86,10 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
     u32x4 al[kScoreTiles][4];
 #pragma unroll
     for (int t = 0; t < kScoreTiles; t++) {
-      const int row = base + t * 16 + col;
+      const int row = min(base + t * 16 + col, c1 - 1);
       const uint16_t* src = Lp + (int64_t)row * kHeadDim + kq * 8;
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        al[t][j] = (u32x4){0u, 0u, 0u, 0u};
-        if (row < c1) al[t][j] = *reinterpret_cast<const u32x4*>(src + j * 32);
-      }
+      for (int j = 0; j < 4; j++) al[t][j] = *reinterpret_cast<const u32x4*>(src + j * 32);
     }
 #pragma unroll
     for (int t = 0; t < kScoreTiles; t++) {
@@ -316,9 +312,8 @@ __device__ __forceinline__ int reg_keys(const DecodeArgs& a, int p, int c0, int 
     for (int gb = 0; gb < GB; gb++)
 #pragma unroll
       for (int j = 0; j < PT / 4; j++)
-        lv[gb][j] = nv > 4 * j && cb + 4 * j < a.ncp
-                        ? *reinterpret_cast<const f32x4*>(lg + (int64_t)(g0 + gb) * a.ncp + 4 * j)
-                        : (f32x4){0.f, 0.f, 0.f, 0.f};
+        lv[gb][j] = *reinterpret_cast<const f32x4*>(   // unconditional: entries past nv are unused
+            lg + (int64_t)(g0 + gb) * a.ncp + (min(cb + 4 * j, a.ncp - 4) - cb));
   };
   load_heads(0);
   stage();
@@ -821,40 +816,41 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
     const int sidx = uw0 + lane - O;
     if (sidx >= 0 && sidx < K) my_ch = max(a.slot_chunk[(int64_t)p * K + sidx], 0);
   }
-  // keys, MFMA A layout: token tile*16 + lr, dims j*32 + lq*8
-  u32x4 kf[NT][4], vf[NT][4];
-#pragma unroll
-  for (int t = 0; t < NT; t++) {
-    const int tau = t * 16 + lr;
-#pragma unroll
-    for (int j = 0; j < 4; j++) kf[t][j] = (u32x4){0u, 0u, 0u, 0u};
-    if (tau < ntok) {
-      const uint16_t* kp = unit_key<C>(a, p, uw0 + tau / C) + (tau % C) * kHeadDim + lq * 8;
-#pragma unroll
-      for (int j = 0; j < 4; j++) kf[t][j] = *reinterpret_cast<const u32x4*>(kp + j * 32);
-    }
-  }
-  // values, PV layout: token tile*16 + lq + 4*i, dims lr*8
-#pragma unroll
-  for (int t = 0; t < NT; t++) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int tau = t * 16 + lq + 4 * i;
-      const int ch = __shfl(my_ch, min(tau, ntok - 1 + (ntok == 0)) / C);
-      vf[t][i] = (u32x4){0u, 0u, 0u, 0u};
-      if (tau < ntok) {
-        const uint16_t* vp = unit_value<C>(a, p, b, h, uw0 + tau / C, ch) + (tau % C) * kHeadDim + lr * 8;
-        vf[t][i] = *reinterpret_cast<const u32x4*>(vp);
-      }
-    }
-  }
-  // q^T, MFMA B layout: head lr, dims j*32 + lq*8 (zero for heads >= G)
+  // q^T first (every tile needs it; vector-memory loads complete in issue order),
+  // MFMA B layout: head lr, dims j*32 + lq*8 (zero for heads >= G)
   bf16x8 bq[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     u32x4 wq = {0u, 0u, 0u, 0u};
     if (lr < G) wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + h * G + lr) * kHeadDim + j * 32 + lq * 8);
     bq[j] = __builtin_bit_cast(bf16x8, wq);
+  }
+  // then tile by tile, keys then values, so that tile 0 can start as soon as its
+  // own 8 loads are in.  Keys in MFMA A layout: token tile*16 + lr, dims j*32 + lq*8;
+  // values in PV layout: token tile*16 + lq + 4*i, dims lr*8.
+  // The loads are unconditional (branch-free code keeps the compiler's per-tile
+  // wait counts exact): tokens past the wave's range re-read its last token,
+  // whose scores are masked to -inf below, so they weigh 0.  A wave with no
+  // tokens reads unit 0 of the pair and masks everything.
+  const int tlast = max(ntok - 1, 0), ub = ntok > 0 ? uw0 : 0;
+  int vch[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; t++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) vch[t][i] = __shfl(my_ch, min(t * 16 + lq + 4 * i, tlast) / C);
+  u32x4 kf[NT][4], vf[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; t++) {
+    const int tk = min(t * 16 + lr, tlast);
+    const uint16_t* kp = unit_key<C>(a, p, ub + tk / C) + (tk % C) * kHeadDim + lq * 8;
+#pragma unroll
+    for (int j = 0; j < 4; j++) kf[t][j] = *reinterpret_cast<const u32x4*>(kp + j * 32);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int tv = min(t * 16 + lq + 4 * i, tlast);
+      vf[t][i] = *reinterpret_cast<const u32x4*>(unit_value<C>(a, p, b, h, ub + tv / C, vch[t][i]) +
+                                                 (tv % C) * kHeadDim + lr * 8);
+    }
   }
   const float qscale = a.scale * kLog2e;
   float m = kNegBig, l = 0.f;        // head lr (S layout)
