@@ -53,72 +53,77 @@ hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Score.  Wave w of a workgroup takes kScoreTiles tiles of 16 landmarks per
-// iteration.  MFMA operands (16x16x32): A = landmarks, lane (row r = lane%16,
+// Score.  A workgroup takes a block of kScoreRows candidate landmarks (32 KB).
+// The block is copied into LDS with direct global->LDS loads, each wave
+// instruction reading 1 KB of contiguous rows (full 128-byte lines; reading
+// the MFMA operand layout straight from memory touches only 64 bytes of a row
+// per instruction, and streamed about 5 % slower).  The 16-byte pieces of row r
+// sit at position piece ^ (r & 15), so the operand reads of 16 rows hit 16
+// distinct LDS bank groups.  Wave w then takes tiles w*2, w*2+1 of 16
+// landmarks.  MFMA operands (16x16x32): A = landmarks, lane (row r = lane%16,
 // kq = lane/16) holds dims j*32 + kq*8 .. +7 of landmark r; B = q^T, lane
-// (col g = lane%16, kq) holds the same dims of head g (zero for g >= G).
-// Output lane (g, kq) holds landmarks kq*4 .. kq*4+3 of head g.
-
-constexpr int kScoreTiles = 4;
+// (col g = lane%16, kq) holds the same dims of head g.  Output lane (g, kq)
+// holds landmarks kq*4 .. kq*4+3 of head g.
 
 template <int G>
 __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
+  __shared__ u32x4 stage[kScoreRows * 16];
   __shared__ float red[2][16][16];   // (m, s) per (wave, kq) and head
   const int p = blockIdx.y, blk = blockIdx.x;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = lane & 15, kq = lane >> 4;
   const int hq = a.n_kv * G;
-
-  // Loads are unconditional (branch-free code keeps the compiler's wait counts
-  // exact): head columns past G repeat head G-1 and landmark rows past the block
-  // repeat its last row; neither output is used.
+  const int c0 = blk * kScoreRows, c1 = min(a.n_cand, c0 + kScoreRows), nr = c1 - c0;
+  const uint16_t* Lp = a.L + ((int64_t)p * a.n_cand + c0) * kHeadDim;
+  // rows past a ragged block's end repeat its last row; their outputs are not used
+#pragma unroll
+  for (int i = w; i < kScoreRows / 4; i += 4) {
+    const int s = i * 64 + lane;
+    const int row = s >> 4, c = (s & 15) ^ (row & 15);
+    __builtin_amdgcn_global_load_lds(Lp + (int64_t)min(row, nr - 1) * kHeadDim + c * 8,
+                                     (__attribute__((address_space(3))) void*)(stage + i * 64), 16, 0, 0);
+  }
+  // head columns past G repeat head G-1; their outputs are not used
   bf16x8 bq[4];
   const uint16_t* qp = a.q + ((int64_t)b * hq + h * G + min(col, G - 1)) * kHeadDim + kq * 8;
 #pragma unroll
   for (int j = 0; j < 4; j++) bq[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + j * 32));
-  const int c0 = blk * a.cpb, c1 = min(a.n_cand, c0 + a.cpb);
-  const uint16_t* Lp = a.L + (int64_t)p * a.n_cand * kHeadDim;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   float* lg = a.logits + ((int64_t)p * G + (col < G ? col : 0)) * a.ncp;
   float m_run = kNegBig, s_run = 0.f;
-
-  for (int base = c0 + w * 16 * kScoreTiles; base < c1; base += 4 * 16 * kScoreTiles) {
-    u32x4 al[kScoreTiles][4];
+  constexpr int kTiles = kScoreRows / 64;   // 16-row tiles per wave
 #pragma unroll
-    for (int t = 0; t < kScoreTiles; t++) {
-      const int row = min(base + t * 16 + col, c1 - 1);
-      const uint16_t* src = Lp + (int64_t)row * kHeadDim + kq * 8;
+  for (int t = 0; t < kTiles; t++) {
+    const int row = w * (kScoreRows / 4) + t * 16 + col;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; j++) al[t][j] = *reinterpret_cast<const u32x4*>(src + j * 32);
+    for (int j = 0; j < 4; j++) {
+      const u32x4 av = stage[row * 16 + ((j * 4 + kq) ^ (row & 15))];
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bq[j], acc, 0, 0, 0);
     }
+    const int cb = c0 + w * (kScoreRows / 4) + t * 16 + kq * 4;
+    if (col < G && cb < c1) {
+      float v[4];
 #pragma unroll
-    for (int t = 0; t < kScoreTiles; t++) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, al[t][j]), bq[j], acc, 0, 0, 0);
-      const int cb = base + t * 16 + kq * 4;
-      if (col < G && cb < c1) {
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) v[i] = acc[i] * a.scale;
-        if (cb + 4 <= c1) {
-          *reinterpret_cast<f32x4*>(lg + cb) = (f32x4){v[0], v[1], v[2], v[3]};
-        } else {
-          for (int i = 0; i < 4 && cb + i < c1; i++) lg[cb + i] = v[i];
-        }
-        float mx = v[0];
-#pragma unroll
-        for (int i = 1; i < 4; i++)
-          if (cb + i < c1) mx = fmaxf(mx, v[i]);
-        const float mn = fmaxf(m_run, mx);
-        float add = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          if (cb + i < c1) add += __expf(v[i] - mn);
-        s_run = s_run * __expf(m_run - mn) + add;
-        m_run = mn;
+      for (int i = 0; i < 4; i++) v[i] = acc[i] * a.scale;
+      if (cb + 4 <= c1) {
+        *reinterpret_cast<f32x4*>(lg + cb) = (f32x4){v[0], v[1], v[2], v[3]};
+      } else {
+        for (int i = 0; i < 4 && cb + i < c1; i++) lg[cb + i] = v[i];
       }
+      float mx = v[0];
+#pragma unroll
+      for (int i = 1; i < 4; i++)
+        if (cb + i < c1) mx = fmaxf(mx, v[i]);
+      const float mn = fmaxf(m_run, mx);
+      float add = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (cb + i < c1) add += __expf(v[i] - mn);
+      s_run = s_run * __expf(m_run - mn) + add;
+      m_run = mn;
     }
   }
   if (col < G) {

@@ -259,9 +259,9 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   h->v_dev = v_dev;
   const int P = h->P, G = h->G, n_c = h->n_c, n_cand = h->n_cand, HD = h->HD;
   {
-    // score: 256 landmarks (4 waves x 4 tiles x 16) per workgroup, i.e. one
-    // 64 KB landmark block each; a larger grid beats longer per-workgroup loops
-    h->cpb = 256;
+    // score: kScoreRows landmarks (4 waves x 2 tiles x 16, a 32 KB block staged
+    // in LDS) per workgroup; a larger grid beats longer per-workgroup loops
+    h->cpb = kScoreRows;
     h->nb_score = (n_cand + h->cpb - 1) / h->cpb;
     h->ncp = (n_cand + 3) / 4 * 4;
     // attention: each wave owns at most attn_units_per_wave units (all loads issued

@@ -11,6 +11,7 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxTopK = 4096;
 constexpr int kSelLdsMax = 150 * 1024;   // dynamic LDS of the select kernel
 constexpr int kMaxSplits = 1024;         // attention workgroups per pair
+constexpr int kScoreRows = 128;          // candidate landmarks per score workgroup
 
 // Everything a decode step touches, by value into the kernels.
 struct DecodeArgs {
