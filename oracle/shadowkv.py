@@ -18,6 +18,10 @@ Sources (page titles as given on each page):
 * papercache deep notes of the same paper, section A2: Algorithm 1 (pre-fill)
   and Algorithm 2 (decode) pseudocode, the equivalent-bandwidth definition and
   its worked example; appendix A7 for the memory-savings example.
+* The paper-graph-ui summary, section 3.4 "Sparse KV Reconstruction and
+  Overlapping Strategy": the assembled cache ends with the generated tokens'
+  K_new, V_new; its ShadowKV+ paragraph keeps a generated pre-RoPE key k' as
+  k' Psi and reconstructs it as (k' Psi) Psi^T with the pre-fill's Psi.
 
 Readings taken where the pages are silent (each also listed in the design
 notes): rotate-half RoPE with inv_freq_i = theta^(-2i/d), angles in float64;
@@ -32,7 +36,12 @@ probabilities; ties in top-K prefer the lower chunk id, ties in the outlier
 test prefer the lower chunk id; selected ids are returned ascending; cosine
 with a zero vector is 0; stored state (A, B, landmarks, outlier and window
 keys, rebuilt keys) is rounded once to bfloat16 with round-to-nearest-even
-when ``storage_rounding`` is on.
+when ``storage_rounding`` is on.  Generated tokens: the t-th appended token
+(t = 0, 1, ...) sits at position seq_len + t; every decode step attends to all
+of them and they take no part in scoring or selection; exact mode keeps
+RoPE(k'); low-rank mode takes Psi^T to be the stored B of the batch element
+(heads concatenated), keeps a' = k' Psi and the key RoPE(a' Psi^T), both
+rounded like the rest of the stored state; values are kept as given.
 """
 from __future__ import annotations
 
@@ -197,6 +206,9 @@ class State:
     V_win: np.ndarray        # [b, H, W, d]
     V: np.ndarray            # [b, H, S, d] value store (V_CPU plus the rest)
     storage_rounding: bool = True
+    K_new: np.ndarray | None = None   # [b, H, T, d] post-RoPE keys of generated tokens
+    V_new: np.ndarray | None = None   # [b, H, T, d] their values
+    A_new: np.ndarray | None = None   # [b, T, r] low-rank states a' = k' Psi (low-rank mode)
 
     def keep(self, x):
         return round_bf16(x) if self.storage_rounding else x
@@ -236,6 +248,46 @@ def build(cfg: Config, k_pre, v, storage_rounding: bool = True) -> State:
     return State(cfg, np.stack(As), np.stack(Bs), np.stack(sigs), np.stack(Ls),
                  np.stack(cands), np.stack(outs), np.stack(mcs), np.stack(kos),
                  np.stack(vos), np.stack(kws), np.stack(vws), v, storage_rounding)
+
+
+def psi_t(st: State, bi: int) -> np.ndarray:
+    """Psi^T of batch element bi as stored: [r, H*d], the heads' B side by side."""
+    B = st.B[bi]                                   # [H, r, d]
+    return B.transpose(1, 0, 2).reshape(B.shape[1], -1)
+
+
+def append(st: State, k_new, v_new, lowrank: bool = False) -> None:
+    """Add one generated token per batch element (ShadowKV+ when ``lowrank``).
+
+    ``k_new``: [b, H*d] pre-RoPE key (heads concatenated), ``v_new``: [b, H, d];
+    bf16 bit patterns or floats.  The token's position is seq_len plus the
+    number of tokens appended before it.
+    """
+    cfg = st.cfg
+    k_new, v_new = _as_f64(k_new), _as_f64(v_new)
+    b, H, d = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    assert k_new.shape == (b, H * d) and v_new.shape == (b, H, d)
+    t = 0 if st.K_new is None else st.K_new.shape[2]
+    pos = np.array([cfg.seq_len + t])
+    keys = np.zeros((b, H, 1, d))
+    a_rows = np.zeros((b, 1, cfg.rank))
+    for bi in range(b):
+        k = k_new[bi]
+        if lowrank:
+            pt = psi_t(st, bi)                     # [r, H*d]
+            a_rows[bi, 0] = st.keep(k @ pt.T)      # a' = k' Psi
+            k = a_rows[bi, 0] @ pt                 # (k' Psi) Psi^T
+        for h in range(H):
+            keys[bi, h] = st.keep(apply_rope(k[h * d:(h + 1) * d][None], pos, cfg.rope_theta))
+    vals = v_new[:, :, None, :]
+    if st.K_new is None:
+        st.K_new, st.V_new = keys, vals
+        st.A_new = a_rows if lowrank else None
+    else:
+        st.K_new = np.concatenate([st.K_new, keys], axis=2)
+        st.V_new = np.concatenate([st.V_new, vals], axis=2)
+        if lowrank:
+            st.A_new = np.concatenate([st.A_new, a_rows], axis=1)
 
 
 def _as_f64(x):
@@ -290,13 +342,18 @@ class StepResult:
 
 def pair_output(st: State, q: np.ndarray, bi: int, h: int, sel: np.ndarray) -> np.ndarray:
     """Exact attention of the G query heads of pair (bi, h) over
-    [outlier chunks; rebuilt keys of the chunks `sel`; local window]; q [H_q, d]."""
+    [outlier chunks; rebuilt keys of the chunks `sel`; local window; generated
+    tokens]; q [H_q, d]."""
     cfg = st.cfg
     G, C = cfg.group, cfg.chunk
     ks = rebuild_keys(st, bi, h, sel)
     tok = (sel[:, None] * C + np.arange(C)).reshape(-1)
-    keys = np.concatenate([st.K_out[bi, h], ks, st.K_win[bi, h]])
-    vals = np.concatenate([st.V_out[bi, h], st.V[bi, h, tok], st.V_win[bi, h]])
+    keys = [st.K_out[bi, h], ks, st.K_win[bi, h]]
+    vals = [st.V_out[bi, h], st.V[bi, h, tok], st.V_win[bi, h]]
+    if st.K_new is not None:
+        keys.append(st.K_new[bi, h])
+        vals.append(st.V_new[bi, h])
+    keys, vals = np.concatenate(keys), np.concatenate(vals)
     return attend(q[h * G:(h + 1) * G], keys, vals)
 
 

@@ -20,6 +20,13 @@ a ``torch.Generator`` seeded from the same triple on the GPU):
   rotated to position ``j``.  Successive decode steps drift as AR(1):
   ``q_t = 0.9*q_{t-1} + sqrt(0.19)*fresh_t``; the "independent" mode draws
   every step afresh.
+* generated tokens (stream ``(l, b, 2)``, ``continuation_*``): the context's
+  latent process carried on, ``a_{S+t} = rho*a_{S+t-1} + sqrt(1-rho^2)*eps``,
+  the key ``a_{S+t} @ B_gen + noise*N(0,1)`` with the context's ``B_gen`` (so
+  new keys share the context's low-rank subspace), the value ``N(0,1)``.
+  ``queries_new_np`` (stream ``(l, b, 3)``) aims every q-head of a step at one
+  of the tokens generated so far instead (``j ~ U{0..n-1}`` at position S+j),
+  each step drawn afresh.
 
 Every tensor is rounded once to bfloat16 (round-to-nearest-even) and returned
 as ``torch.bfloat16``.  The rotation used to aim the queries is the synthetic
@@ -162,6 +169,25 @@ def layer_cache_np(s: Shape, layer: int, seed: int = 0):
     return torch.stack(ks), torch.stack(vs)
 
 
+def continuation_np(s: Shape, layer: int, n_tokens: int, seed: int = 0):
+    """Generated tokens after the context of ``layer_cache_np(s, layer, seed)``:
+    (k_new bf16 [n][b][H_kv*d], v_new bf16 [n][b][H_kv][d])."""
+    hd = s.n_kv_heads * s.head_dim
+    k_new = np.zeros((n_tokens, s.batch, hd))
+    v_new = np.zeros((n_tokens, s.batch, s.n_kv_heads, s.head_dim))
+    c = math.sqrt(1.0 - s.rho * s.rho)
+    for b in range(s.batch):
+        g = _rng(seed, layer, b, 0)                   # the context's draws, in order
+        a = _ar1_np(g.standard_normal((s.seq_len, s.latent_rank)), s.rho)[-1]
+        bm = g.standard_normal((s.latent_rank, hd)) / math.sqrt(s.latent_rank)
+        g2 = _rng(seed, layer, b, 2)
+        for t in range(n_tokens):
+            a = s.rho * a + c * g2.standard_normal(s.latent_rank)
+            k_new[t, b] = a @ bm + s.noise * g2.standard_normal(hd)
+            v_new[t, b] = g2.standard_normal((s.n_kv_heads, s.head_dim))
+    return _to_bf16(k_new), _to_bf16(v_new)
+
+
 def queries_np(s: Shape, k_pre: torch.Tensor, layer: int, steps: int, seed: int = 0,
                mode: str = "drift") -> torch.Tensor:
     """Queries bf16 [steps][b][H_q][d] aimed at random keys (see module doc)."""
@@ -183,6 +209,24 @@ def queries_np(s: Shape, k_pre: torch.Tensor, layer: int, steps: int, seed: int 
                 q = 0.9 * prev + math.sqrt(0.19) * fresh
             out[t, b] = q
             prev = q
+    return _to_bf16(out)
+
+
+def queries_new_np(s: Shape, k_new: torch.Tensor, n_avail: list, layer: int = 0,
+                   seed: int = 0) -> torch.Tensor:
+    """Queries bf16 [len(n_avail)][b][H_q][d] aimed at generated tokens: step t
+    picks its needles among the first n_avail[t] > 0 rows of k_new [n][b][H_kv*d]."""
+    d, G = s.head_dim, s.group
+    out = np.zeros((len(n_avail), s.batch, s.n_q_heads, d))
+    heads = np.arange(s.n_q_heads) // G
+    for b in range(s.batch):
+        g = _rng(seed, layer, b, 3)
+        kb = k_new[:, b].to(torch.float64).numpy().reshape(-1, s.n_kv_heads, d)
+        for t, n in enumerate(n_avail):
+            j = g.integers(0, n, size=s.n_q_heads)
+            z = g.standard_normal((s.n_q_heads, d))
+            pos = (s.seq_len + j).astype(np.float64)
+            out[t, b] = z + 4.0 * _rotate_np(kb[j, heads], pos, s.rope_theta)
     return _to_bf16(out)
 
 
@@ -239,6 +283,32 @@ def layer_cache_torch(s: Shape, layer: int, seed: int = 0, device="cuda",
             vh = torch.randn((s.seq_len, s.head_dim), generator=g, device=device)
             v[b, h].copy_(vh.to(torch.bfloat16))
     return k_pre, v
+
+
+def continuation_torch(s: Shape, layer: int, n_tokens: int, seed: int = 0, device="cuda"):
+    """Generated tokens after the context of ``layer_cache_torch(s, layer, seed)``,
+    drawn on ``device``: (k_new bf16 [n][b][H_kv*d], v_new bf16 [n][b][H_kv][d])."""
+    hd = s.n_kv_heads * s.head_dim
+    k_new = torch.empty((n_tokens, s.batch, hd), dtype=torch.bfloat16, device=device)
+    v_new = torch.empty((n_tokens, s.batch, s.n_kv_heads, s.head_dim), dtype=torch.bfloat16,
+                        device=device)
+    c = math.sqrt(1.0 - s.rho * s.rho)
+    for b in range(s.batch):
+        g = _tgen(seed, layer, b, 0, device)          # the context's draws, in order
+        eps = torch.randn((s.seq_len, s.latent_rank), generator=g, device=device,
+                          dtype=torch.float64)
+        a = _ar1_torch(eps, s.rho)[-1]
+        del eps
+        bm = torch.randn((s.latent_rank, hd), generator=g, device=device) / math.sqrt(s.latent_rank)
+        g2 = _tgen(seed, layer, b, 2, device)
+        for t in range(n_tokens):
+            a = s.rho * a + c * torch.randn(s.latent_rank, generator=g2, device=device,
+                                            dtype=torch.float64)
+            k = a.to(torch.float32) @ bm + s.noise * torch.randn(hd, generator=g2, device=device)
+            k_new[t, b] = k.to(torch.bfloat16)
+            v_new[t, b] = torch.randn((s.n_kv_heads, s.head_dim), generator=g2,
+                                      device=device).to(torch.bfloat16)
+    return k_new, v_new
 
 
 def _rotate_torch(x: torch.Tensor, pos: torch.Tensor, theta: float) -> torch.Tensor:

@@ -384,3 +384,80 @@ def test_storage_rounding_is_applied_to_stored_state():
     st0 = O.build(cfg, k, v, storage_rounding=False)
     assert not np.array_equal(st0.A, st.A)
     np.testing.assert_allclose(st0.A, st.A, rtol=2 ** -8)
+
+
+# ---------------------------------------------------------------- generated tokens
+
+@pytest.mark.parametrize("lowrank", [False, True])
+def test_appended_tokens_full_budget_equals_dense_attention(lowrank):
+    # full rank and every candidate selected: attention over the context and the
+    # generated tokens is plain dense attention over the grown sequence, the
+    # t-th generated token rotated at position seq_len + t (with a square
+    # orthogonal Psi the low-rank state loses nothing)
+    rng = np.random.default_rng(31)
+    cfg = small_cfg()
+    n_c = cfg.seq_len // cfg.chunk
+    cfg = small_cfg(top_k=n_c - 2 - 2, rank=cfg.n_kv_heads * cfg.head_dim)
+    hd, d, G, S = cfg.n_kv_heads * cfg.head_dim, cfg.head_dim, cfg.group, cfg.seq_len
+    T = 3
+    k = rng.standard_normal((1, S + T, hd))
+    v = rng.standard_normal((1, cfg.n_kv_heads, S + T, d))
+    st = O.build(cfg, k[:, :S], v[:, :, :S], storage_rounding=False)
+    for t in range(T):
+        O.append(st, k[:, S + t], v[:, :, S + t], lowrank=lowrank)
+    q = rng.standard_normal((1, cfg.n_q_heads, d)) * 3
+    res = O.decode_step(st, q)
+    pos = np.arange(S + T)
+    for hq in range(cfg.n_q_heads):
+        h = hq // G
+        kr = O.apply_rope(k[0, :, h * d:(h + 1) * d], pos, cfg.rope_theta)
+        s = kr @ q[0, hq] / math.sqrt(d)
+        p = np.exp(s - s.max()); p /= p.sum()
+        np.testing.assert_allclose(res.out[0, hq], p @ v[0, h], atol=1e-9)
+
+
+def test_lowrank_state_is_the_projection_on_the_context_subspace():
+    # the stored key of a generated token, rotated back, is k' projected on the
+    # top-r right singular subspace of the context keys (computed here from
+    # eigh of the Gram matrix), and a context key appended again gets exactly
+    # its row of A as low-rank state (A = K Psi)
+    rng = np.random.default_rng(32)
+    cfg = small_cfg(seq_len=128, rank=6)
+    hd, d, S = cfg.n_kv_heads * cfg.head_dim, cfg.head_dim, cfg.seq_len
+    k = lowrank_keys(rng, 1, S, hd, 10)
+    v = rng.standard_normal((1, cfg.n_kv_heads, S, d))
+    st = O.build(cfg, k, v, storage_rounding=False)
+    w, U = np.linalg.eigh(k[0].T @ k[0])
+    top = U[:, np.argsort(w)[::-1][:cfg.rank]]
+    proj = top @ top.T
+    knew = [rng.standard_normal(hd), k[0, 17]]
+    for kn in knew:
+        O.append(st, kn[None], rng.standard_normal((1, cfg.n_kv_heads, d)), lowrank=True)
+    for t, kn in enumerate(knew):
+        back = np.concatenate([O.apply_rope(st.K_new[0, h, t][None], np.array([-(S + t)]),
+                                            cfg.rope_theta)[0] for h in range(cfg.n_kv_heads)])
+        np.testing.assert_allclose(back, kn @ proj, atol=1e-9)
+        assert np.abs((kn - back) @ top).max() < 1e-9          # residual orthogonal to Psi
+    np.testing.assert_allclose(st.A_new[0, 1], st.A[0, 17], atol=1e-9)
+
+
+def test_appended_tokens_leave_selection_alone_and_are_rounded():
+    rng = np.random.default_rng(33)
+    cfg = small_cfg(seq_len=128, top_k=4)
+    hd, d = cfg.n_kv_heads * cfg.head_dim, cfg.head_dim
+    k = lowrank_keys(rng, 1, cfg.seq_len, hd, 8)
+    v = rng.standard_normal((1, cfg.n_kv_heads, cfg.seq_len, d))
+    q = rng.standard_normal((1, cfg.n_q_heads, d)) * 3
+    st = O.build(cfg, k, v)
+    before = O.decode_step(st, q)
+    for lowrank in (False, True):
+        st2 = O.build(cfg, k, v)
+        for _ in range(2):
+            O.append(st2, rng.standard_normal((1, hd)), rng.standard_normal((1, cfg.n_kv_heads, d)),
+                     lowrank=lowrank)
+        after = O.decode_step(st2, q)
+        np.testing.assert_array_equal(after.ids, before.ids)
+        assert not np.allclose(after.out, before.out)
+        for arr in [st2.K_new] + ([st2.A_new] if lowrank else []):
+            as32 = torch.tensor(arr, dtype=torch.float32)
+            np.testing.assert_array_equal(as32.to(torch.bfloat16).to(torch.float64).numpy(), arr)

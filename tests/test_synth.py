@@ -56,3 +56,30 @@ def test_budget_rule():
     assert synth.budget(1048576, 4) == (4096, 786)
     assert synth.budget(1048576, 16) == (1024, 197)
     assert synth.budget(8192, 8) == (16, 3)
+
+
+def test_continuation_shares_the_context_subspace():
+    s = _small()
+    k, _ = synth.layer_cache_np(s, 0)
+    kn, vn = synth.continuation_np(s, 0, 6)
+    assert kn.shape == (6, 2, 256) and vn.shape == (6, 2, 2, 128)
+    kn2, _ = synth.continuation_np(s, 0, 6)
+    assert torch.equal(kn, kn2)
+    for gen in ("np", "torch"):
+        if gen == "torch":
+            kt, _ = synth.layer_cache_torch(s, 0, 0, "cpu")
+            kn, vn = synth.continuation_torch(s, 0, 6, 0, "cpu")
+            kc = kt
+        else:
+            kc = k
+        for b in range(2):
+            kb = kc[b].double().numpy()
+            _, _, vt = np.linalg.svd(kb, full_matrices=False)
+            top = vt[:s.latent_rank].T
+            x = kn[:, b].double().numpy()
+            kept = np.linalg.norm(x @ top, axis=1) / np.linalg.norm(x, axis=1)
+            assert kept.min() > 0.97, (gen, kept)
+            # the latent process carries on: the first new key is close to the last context key
+            c0 = np.dot(x[0], kb[-1]) / (np.linalg.norm(x[0]) * np.linalg.norm(kb[-1]))
+            assert c0 > 0.6, (gen, c0)
+        assert abs(vn.double().std().item() - 1.0) < 0.1
