@@ -251,6 +251,9 @@ def main():
                     help="AR(1)-drifting queries (temporal cache hits) or independent draws")
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunk size C for the 1M-token shape (budget K and O follow C)")
+    ap.add_argument("--append", choices=["none", "exact", "lowrank"], default="none",
+                    help="append one generated token per layer before every decode step "
+                         "(exact keys, or ShadowKV+ low-rank states)")
     ap.add_argument("--phase-every", type=int, default=16,
                     help="record per-phase HIP events on every n-th layer of the timed region "
                          "(an event record between kernels costs a few microseconds)")
@@ -299,6 +302,8 @@ def main():
     host = args.values == "host"
     placement = skv.SKV_VALUES_HOST if host else skv.SKV_VALUES_DEVICE
     pcie_peak = measure_h2d_gbps() if host else None     # before the value stores take pinned memory
+    new_mode = {"exact": skv.SKV_NEW_EXACT, "lowrank": skv.SKV_NEW_LOWRANK}.get(args.append)
+    news = []
     for l in range(L):
         k_pre, v = synth.layer_cache_torch(shape, l, args.seed, dev)
         if host:
@@ -306,7 +311,11 @@ def main():
             vh.copy_(v)
             del v
             v = vh
-        layers.append(skv.Layer(shape, k_pre, v, placement))
+        if new_mode is None:
+            layers.append(skv.Layer(shape, k_pre, v, placement))
+        else:
+            layers.append(skv.Layer(shape, k_pre, v, placement, max_new_tokens=total, new_token_mode=new_mode))
+            news.append(synth.continuation_torch(shape, l, total, args.seed, dev))
         qs.append(synth.queries_torch(shape, k_pre, l, total, args.seed, mode=args.queries))
         del k_pre, v
         if l % 4 == 3 or l == L - 1:
@@ -316,9 +325,14 @@ def main():
     ids = torch.empty((shape.batch, shape.n_kv_heads, shape.top_k), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
-    for t in range(W):
+    def step(t):
         for l in range(L):
+            if news:
+                layers[l].append(news[l][0][t], news[l][1][t], stream)
             layers[l].decode(qs[l][t], out, ids, stream)
+
+    for t in range(W):
+        step(t)
     torch.cuda.synchronize()
     before = [ly.stats() for ly in layers]
     sampled = list(range(0, L, max(1, args.phase_every)))
@@ -328,8 +342,7 @@ def main():
     torch.cuda.synchronize()
     ev0.record(stream)
     for t in range(W, W + K):
-        for l in range(L):
-            layers[l].decode(qs[l][t], out, ids, stream)
+        step(t)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
@@ -410,7 +423,10 @@ def main():
                                f"{shape.n_q_heads} q / {shape.n_kv_heads} KV heads, d={shape.head_dim}, "
                                f"r={shape.rank}, C={shape.chunk}, K={shape.top_k}, O={shape.n_outlier}, "
                                f"window {shape.window}, values in {'pinned host memory' if host else 'HBM'}, "
-                               f"{'AR(1)-drifting' if args.queries == 'drift' else 'independent'} queries",
+                               f"{'AR(1)-drifting' if args.queries == 'drift' else 'independent'} queries"
+                               + ("" if new_mode is None else
+                                  f", one generated token appended per layer and step ({args.append} keys; "
+                                  f"{W + 1}..{W + K} generated tokens attended in the timed steps)"),
                    "global_batch": shape.batch, "seq_len": shape.seq_len, "layers": L,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "score_kernel (landmark GEMV)",

@@ -15,7 +15,13 @@
  *     head, maximum over each GQA group, top-K chunks per KV head, an index scan
  *     against the previous step's chunks so only misses are rebuilt
  *     (RoPE(Gather(A, I_miss) B)) and fetched, then exact attention over
- *     [outliers; selected chunks; local window].
+ *     [outliers; selected chunks; local window; generated tokens];
+ *   - generated tokens (paper-graph-ui summary, section 3.4 "Sparse KV
+ *     Reconstruction and Overlapping Strategy": the assembly
+ *     [K_outlier; RoPE(K_sparse); K_new] and the paragraph on the ShadowKV+
+ *     extension): appended one per step and always attended, either exact
+ *     (ShadowKV) or stored as their projection onto the pre-fill subspace and
+ *     reconstructed from it (ShadowKV+).
  *
  * Conventions shared by every entry point
  *   - Every call returns an skv_status; SKV_OK is 0.  No C++ exception crosses
@@ -25,7 +31,9 @@
  *     skv_destroy.
  *   - bf16 tensors are passed as uint16_t bit patterns, row-major, with the
  *     layouts given per argument.  "device" pointers are HIP device memory on the
- *     current device; "pinned host" pointers come from hipHostMalloc.
+ *     current device; "pinned host" pointers come from hipHostMalloc.  bf16 and
+ *     float tensors start on a 16-byte boundary, int32 ones on a 4-byte boundary
+ *     (every HIP allocation is 256-byte aligned); otherwise SKV_ERR_INVALID_ARG.
  *   - Query head hq uses KV head hq / G with G = n_q_heads / n_kv_heads.
  *   - Streams are passed as void* holding a hipStream_t (NULL = default stream).
  *   - A handle (one model layer) is not thread-safe; distinct handles are
@@ -40,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 1
+#define SKV_ABI_VERSION 2
 
 typedef int32_t skv_status;
 #define SKV_OK 0
@@ -58,12 +66,20 @@ typedef int32_t skv_status;
                                   gathered over PCIe on a side stream that overlaps
                                   the key rebuild                                   */
 
+/* How appended (generated) tokens keep their keys. */
+#define SKV_NEW_EXACT 0        /* post-RoPE key kept exactly (ShadowKV)             */
+#define SKV_NEW_LOWRANK 1      /* pre-RoPE key projected onto the pre-fill subspace,
+                                  a' = k' Psi (Psi^T = the stored B), kept as a' and
+                                  reconstructed as RoPE(a' Psi^T) (ShadowKV+)       */
+
 /*
  * Shape and budget of one layer.
  *   head_dim must be 128.  seq_len % chunk == 0, chunk in {4, 8, 16},
  *   window % chunk == 0, G in {1, 2, 4, 8, 16}, rank % 16 == 0,
  *   1 <= rank <= min(seq_len, n_kv_heads * head_dim), n_kv_heads * head_dim <= 2048,
  *   n_cand = seq_len/chunk - n_outlier - window/chunk, 1 <= top_k <= n_cand, top_k <= 4096.
+ *   max_new_tokens >= 0 is the capacity for appended tokens (skv_append_token);
+ *   new_token_mode is SKV_NEW_EXACT or SKV_NEW_LOWRANK.
  */
 typedef struct skv_config {
   int32_t batch;           /* b                                                   */
@@ -81,6 +97,8 @@ typedef struct skv_config {
   int32_t temporal_cache;  /* 1: rebuild/fetch only chunks missed vs the previous
                               step; 0: rebuild every selected chunk every step     */
   int32_t reserved;        /* must be 0                                           */
+  int32_t max_new_tokens;  /* capacity for generated tokens (0: none)             */
+  int32_t new_token_mode;  /* SKV_NEW_EXACT or SKV_NEW_LOWRANK                     */
 } skv_config;
 
 typedef struct skv_layer skv_layer;   /* opaque; owns all derived state */
@@ -95,6 +113,7 @@ typedef struct skv_stats {
   double last_alpha;      /* last_hits / (pairs * top_k); 0 for the first step      */
   double mean_alpha;      /* total_hits / (pairs * top_k * (steps - 1))             */
   int64_t last_host_bytes;/* value bytes gathered from pinned host memory last step */
+  int64_t new_tokens;     /* generated tokens appended since build                  */
 } skv_stats;
 
 /*
@@ -165,6 +184,26 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
  */
 skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t* chunk_ids,
                            void* stream);
+
+/*
+ * skv_append_token -- append one generated token to the layer (paper-graph-ui
+ * summary, section 3.4 "Sparse KV Reconstruction and Overlapping Strategy": the
+ * generated tokens' K_new, V_new are attended after the sparse set; its ShadowKV+
+ * paragraph: a new pre-RoPE key k' is kept as k' Psi and reconstructed as
+ * (k' Psi) Psi^T).
+ *   k_new : device, bf16 [b][H_kv*d], the new token's pre-RoPE keys, heads
+ *           concatenated; its position is seq_len + (tokens appended so far).
+ *   v_new : device, bf16 [b][H_kv][d], its values.
+ *   stream: enqueued, no host synchronisation.  Both inputs are only read by the
+ *           enqueued work (they may be reused once the stream has passed it).
+ * SKV_NEW_EXACT stores RoPE(k'); SKV_NEW_LOWRANK stores a' = k' Psi in bf16 (Psi^T
+ * being the stored bf16 B) and the key RoPE(a' Psi^T).  Every later decode step
+ * attends to all appended tokens.  The landmarks, outliers and the selection
+ * cover the pre-filled context only.
+ * Errors: INVALID_ARG (null pointer), SHAPE (capacity max_new_tokens reached),
+ * STATE, HIP.
+ */
+skv_status skv_append_token(skv_layer* h, const uint16_t* k_new, const uint16_t* v_new, void* stream);
 
 /* Temporal-cache counters; synchronises with the last stream used. */
 skv_status skv_get_stats(const skv_layer* h, skv_stats* stats);

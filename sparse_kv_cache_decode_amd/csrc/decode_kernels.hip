@@ -721,6 +721,139 @@ hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// Append one generated token (position S + t) for every batch element; one
+// workgroup per (batch element, KV head).  Exact: the key is RoPE(k').  Low rank
+// (paper-graph-ui summary, section 3.4, ShadowKV+): a' = k' Psi with Psi^T the
+// stored B (fp32 accumulation, rounded to bf16 and kept), then the key
+// RoPE(a' Psi^T).  Every low-rank workgroup of a batch element forms the whole
+// a' (the B_t rows of all heads, a few hundred KB that the heads share through
+// L2), so one launch needs no cross-workgroup step; 1024 threads keep about 20
+// row loads per thread, issued eight at a time.  Blocks of one batch element are
+// spaced `batch` apart, which puts them on one XCD when the batch is a multiple
+// of the XCD count.
+
+constexpr int kMaxHD = 2048;
+constexpr int kAppendThreads = 1024;
+
+// RoPE of head h's pre-RoPE key (x1 = dims [0, 64), x2 = [64, 128) via xk) and
+// the value copy; threads [0, 64) rotate, [64, 80) copy 16 bytes each.
+__device__ __forceinline__ void append_store(const DecodeArgs& a, const uint16_t* v_new, int b, int h, int t,
+                                             int tid, float x1, float x2) {
+  const int64_t row = ((int64_t)(b * a.n_kv + h) * a.max_new + t) * kHeadDim;
+  if (tid < kHeadDim / 2) {
+    float cs, sn;
+    rope_cs(a.seq_len + t, a.inv_freq[tid], &cs, &sn);
+    a.key_new[row + tid] = f32_to_bf16(x1 * cs - x2 * sn);
+    a.key_new[row + tid + kHeadDim / 2] = f32_to_bf16(x2 * cs + x1 * sn);
+  } else if (tid < kHeadDim / 2 + kHeadDim / 8) {
+    const int c = tid - kHeadDim / 2;
+    *reinterpret_cast<u32x4*>(a.val_new + row + c * 8) =
+        *reinterpret_cast<const u32x4*>(v_new + ((int64_t)b * a.n_kv + h) * kHeadDim + c * 8);
+  }
+}
+
+__global__ __launch_bounds__(128) void append_exact_kernel(DecodeArgs a, const uint16_t* k_new,
+                                                           const uint16_t* v_new, int t) {
+  const int b = blockIdx.x % a.batch, h = blockIdx.x / a.batch, tid = threadIdx.x;
+  const uint16_t* kp = k_new + (int64_t)b * a.n_kv * kHeadDim + h * kHeadDim;
+  const int dd = tid % (kHeadDim / 2);
+  append_store(a, v_new, b, h, t, tid, bf16_to_f32(kp[dd]), bf16_to_f32(kp[dd + kHeadDim / 2]));
+}
+
+__global__ __launch_bounds__(kAppendThreads) void append_lowrank_kernel(DecodeArgs a, const uint16_t* k_new,
+                                                                        const uint16_t* v_new, int t,
+                                                                        uint16_t* a_new) {
+  __shared__ float ks[kMaxHD];                  // k' of the batch element
+  __shared__ float red[kAppendThreads * 8];     // per-row-group partial a'
+  __shared__ float red2[kAppendThreads];        // second-level partials
+  __shared__ float ap[kMaxHD];                  // a', bf16-rounded
+  __shared__ float xs[kHeadDim];                // a' Psi^T for head h
+  const int b = blockIdx.x % a.batch, h = blockIdx.x / a.batch;
+  const int HD = a.n_kv * kHeadDim, r = a.rank, tid = threadIdx.x;
+  const uint16_t* kp = k_new + (int64_t)b * HD;
+  const uint16_t* Bt = a.Bt + (int64_t)b * HD * r;
+  for (int i = tid; i < HD; i += kAppendThreads) ks[i] = bf16_to_f32(kp[i]);
+  __syncthreads();
+  // a' = k' Psi: thread (row group g, column piece c) sums rows g, g + ng, ... of
+  // B_t over its 8 columns; rows past HD re-read the last row with weight 0
+  const int nch = r / 8, ng = kAppendThreads / nch;   // r <= 2048 keeps ng >= 4
+  const int c = tid % nch, g = tid / nch;
+  if (g < ng) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i0 = g; i0 < HD; i0 += 8 * ng) {
+      u32x4 w[8];
+#pragma unroll
+      for (int m = 0; m < 8; m++)
+        w[m] = *reinterpret_cast<const u32x4*>(Bt + (int64_t)min(i0 + m * ng, HD - 1) * r + c * 8);
+#pragma unroll
+      for (int m = 0; m < 8; m++) {
+        const int i = i0 + m * ng;
+        const float x = i < HD ? ks[min(i, HD - 1)] : 0.f;
+        float y[8];
+        unpack8(w[m], y);
+#pragma unroll
+        for (int k = 0; k < 8; k++) acc[k] = fmaf(x, y[k], acc[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) red[g * r + c * 8 + k] = acc[k];
+  }
+  __syncthreads();
+  // sum the ng groups: parts of them first, then the parts
+  const int parts = kAppendThreads / r;              // >= 1 (r <= 1024) or 0
+  if (parts > 0) {
+    if (tid < parts * r) {
+      const int j = tid % r, pt = tid / r;
+      float sum = 0.f;
+      for (int gg = pt; gg < ng; gg += parts) sum += red[gg * r + j];
+      red2[pt * r + j] = sum;
+    }
+    __syncthreads();
+  }
+  for (int j = tid; j < r; j += kAppendThreads) {
+    float sum = 0.f;
+    if (parts > 0)
+      for (int pt = 0; pt < parts; pt++) sum += red2[pt * r + j];
+    else
+      for (int gg = 0; gg < ng; gg++) sum += red[gg * r + j];
+    const uint16_t q = f32_to_bf16(sum);
+    ap[j] = bf16_to_f32(q);
+    if (h == 0) a_new[((int64_t)b * a.max_new + t) * r + j] = q;
+  }
+  __syncthreads();
+  // head h's pre-RoPE key: x_dd = a' . B_t[h d + dd], eight threads per dim
+  {
+    const int dd = tid >> 3, sub = tid & 7;
+    const uint16_t* row = Bt + (int64_t)(h * kHeadDim + dd) * r;
+    float sum = 0.f;
+    for (int c8 = sub; c8 < nch; c8 += 8) {
+      float y[8];
+      unpack8(*reinterpret_cast<const u32x4*>(row + c8 * 8), y);
+#pragma unroll
+      for (int k = 0; k < 8; k++) sum = fmaf(ap[c8 * 8 + k], y[k], sum);
+    }
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    sum += __shfl_xor(sum, 4);
+    if (sub == 0) xs[dd] = sum;
+  }
+  __syncthreads();
+  if (tid < kHeadDim) {
+    const int dd = tid % (kHeadDim / 2);
+    append_store(a, v_new, b, h, t, tid, xs[dd], xs[dd + kHeadDim / 2]);
+  }
+}
+
+hipError_t launch_append(const DecodeArgs& a, const uint16_t* k_new, const uint16_t* v_new, int t, bool lowrank,
+                         uint16_t* a_new, hipStream_t st) {
+  if (lowrank)
+    append_lowrank_kernel<<<a.batch * a.n_kv, kAppendThreads, 0, st>>>(a, k_new, v_new, t, a_new);
+  else
+    append_exact_kernel<<<a.batch * a.n_kv, 128, 0, st>>>(a, k_new, v_new, t);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Value gather from pinned host memory (zero-copy reads over PCIe).
 
 constexpr int kGatherMisses = 16;
@@ -779,10 +912,11 @@ int attn_units_per_wave(int group, int chunk) { return attn_tiles(group) * 16 / 
 
 template <int C>
 __device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, int u) {
-  const int O = a.n_outlier, K = a.top_k;
+  const int O = a.n_outlier, K = a.top_k, Wu = a.n_win_units;
   if (u < O) return a.k_out + ((int64_t)p * O + u) * C * kHeadDim;
   if (u < O + K) return a.key_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim;
-  return a.k_win + ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
+  if (u < O + K + Wu) return a.k_win + ((int64_t)p * Wu + (u - O - K)) * C * kHeadDim;
+  return a.key_new + ((int64_t)p * a.max_new + (int64_t)(u - O - K - Wu) * C) * kHeadDim;
 }
 
 template <int C>
@@ -793,7 +927,9 @@ __device__ __forceinline__ const uint16_t* unit_value(const DecodeArgs& a, int p
   if (u < O + K)
     return a.host_values ? a.val_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim
                          : a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * C) * kHeadDim;
-  return a.v_win + ((int64_t)p * a.n_win_units + (u - O - K)) * C * kHeadDim;
+  const int Wu = a.n_win_units;
+  if (u < O + K + Wu) return a.v_win + ((int64_t)p * Wu + (u - O - K)) * C * kHeadDim;
+  return a.val_new + ((int64_t)p * a.max_new + (int64_t)(u - O - K - Wu) * C) * kHeadDim;
 }
 
 template <int G, int C>
@@ -808,11 +944,14 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;   // (row|head|ds, kq|tg)
   const int O = a.n_outlier, K = a.top_k;
-  const int U = O + K + a.n_win_units;
+  // units: [outliers; selected slots; window; appended tokens (the last unit may
+  // be partly filled: tokens past n_new_tokens are masked like a wave's tail)]
+  const int U = O + K + a.n_win_units + a.n_new_units;
   const int per_wave = (a.upw + 3) / 4;
   const int uw0 = min(U, split * a.upw + w * per_wave);
   const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
-  const int ntok = (uw1 - uw0) * C;
+  const int valid = (O + K + a.n_win_units) * C + a.n_new_tokens;   // tokens in units [0, U)
+  const int ntok = max(0, min((uw1 - uw0) * C, valid - uw0 * C));
   const int hq = a.n_kv * G;
 
   // chunk id of each selected unit of the wave, one per lane

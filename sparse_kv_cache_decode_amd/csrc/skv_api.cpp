@@ -17,6 +17,7 @@ using namespace skv;
 struct skv_layer {
   skv_config cfg;
   int G = 0, n_c = 0, n_win = 0, n_cand = 0, P = 0, HD = 0, U = 0;
+  int n_new = 0;                     // generated tokens appended so far
   int nb_score = 0, cpb = 0, ncp = 0, n_split = 0, upw = 0, res_words = 0, n_part = 0, part_size = 0;
   bool poisoned = false;
   bool need_reset = false;
@@ -24,7 +25,8 @@ struct skv_layer {
   void* pool = nullptr;
   // carved from pool
   uint16_t *A = nullptr, *Bt = nullptr, *L = nullptr, *k_out = nullptr, *v_out = nullptr,
-           *k_win = nullptr, *v_win = nullptr, *key_slots = nullptr, *val_slots = nullptr;
+           *k_win = nullptr, *v_win = nullptr, *key_slots = nullptr, *val_slots = nullptr,
+           *key_new = nullptr, *val_new = nullptr, *a_new = nullptr;
   int32_t *cand_map = nullptr, *outlier_ids = nullptr, *slot_cand = nullptr, *slot_chunk = nullptr,
           *miss_slot = nullptr, *miss_chunk = nullptr, *miss_cand = nullptr, *free_slot = nullptr,
           *n_miss = nullptr, *hits_last = nullptr;
@@ -84,6 +86,13 @@ skv_status validate(const skv_config* c) {
   if (c->rank < 1 || c->rank > std::min<int64_t>(c->seq_len, HD)) return SKV_ERR_SHAPE;
   if (c->rank % 16 != 0) return SKV_ERR_UNSUPPORTED;
   if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta)) return SKV_ERR_SHAPE;
+  if (c->max_new_tokens < 0) return SKV_ERR_SHAPE;
+  if (c->new_token_mode != SKV_NEW_EXACT && c->new_token_mode != SKV_NEW_LOWRANK) return SKV_ERR_INVALID_ARG;
+  // attention splits: at most kMaxSplits per pair with every appended token present
+  const int64_t units = c->n_outlier + c->top_k + c->window / c->chunk +
+                        ((int64_t)c->max_new_tokens + c->chunk - 1) / c->chunk;
+  const int64_t per_wg = 4 * attn_units_per_wave(G, c->chunk);
+  if ((units + per_wg - 1) / per_wg > kMaxSplits) return SKV_ERR_UNSUPPORTED;
   return SKV_OK;
 }
 
@@ -101,6 +110,9 @@ uint16_t f64_to_bf16(double x) {
   std::memcpy(&b, &f, 4);
   return (uint16_t)(b >> 16);
 }
+
+// Kernels move bf16 and float data in 16-byte pieces.
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
 bool is_device_ptr(const void* p) {
   hipPointerAttribute_t at;
@@ -154,12 +166,17 @@ DecodeArgs decode_args(skv_layer* h) {
   a.top_k = c.top_k;
   a.n_outlier = c.n_outlier;
   a.n_win_units = h->n_win;
+  a.n_new_tokens = h->n_new;
+  a.n_new_units = (h->n_new + c.chunk - 1) / c.chunk;
+  a.max_new = c.max_new_tokens;
+  a.key_new = h->key_new;
+  a.val_new = h->val_new;
   a.n_cand = h->n_cand;
   a.seq_len = c.seq_len;
   a.nb_score = h->nb_score;
   a.cpb = h->cpb;
   a.ncp = h->ncp;
-  a.n_split = h->n_split;
+  a.n_split = (h->U + a.n_new_units + h->upw - 1) / h->upw;   // splits grow with appended tokens
   a.upw = h->upw;
   a.temporal = c.temporal_cache;
   a.host_values = c.value_placement == SKV_VALUES_HOST;
@@ -231,6 +248,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   skv_status st = validate(cfg);
   if (st != SKV_OK) return st;
   if (!k_pre || !v || !out) return SKV_ERR_INVALID_ARG;
+  if (!aligned(k_pre, 16) || !aligned(v, 16)) return SKV_ERR_INVALID_ARG;
   if (!is_device_ptr(k_pre)) return SKV_ERR_INVALID_ARG;
   const uint16_t* v_dev = nullptr;
   if (cfg->value_placement == SKV_VALUES_DEVICE) {
@@ -271,7 +289,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     int upw_wave = (int)(((int64_t)P * h->U + waves_target - 1) / waves_target);
     upw_wave = std::max(1, std::min(upw_wave, nuw));
     h->upw = 4 * upw_wave;
-    if ((int64_t)h->upw * kMaxSplits < h->U) h->upw = 4 * nuw;
+    const int64_t u_max = h->U + ((int64_t)c.max_new_tokens + C - 1) / C;   // with every appended token
+    if ((int64_t)h->upw * kMaxSplits < u_max) h->upw = 4 * nuw;
     h->n_split = (h->U + h->upw - 1) / h->upw;
     select_partition(n_cand, K, G, P, &h->n_part, &h->part_size);
   }
@@ -305,7 +324,11 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const size_t oMt = cv.take<long long>(P);
   const size_t oLg = cv.take<float>((size_t)P * G * h->ncp);
   const size_t oLp = cv.take<float>((size_t)P * h->nb_score * G * 2);
-  const size_t oAp = cv.take<float>((size_t)P * h->n_split * G * (kHeadDim + 2));
+  const int n_split_max = (h->U + (c.max_new_tokens + C - 1) / C + h->upw - 1) / h->upw;
+  const size_t oAp = cv.take<float>((size_t)P * n_split_max * G * (kHeadDim + 2));
+  const size_t oKn = cv.take<uint16_t>((size_t)P * c.max_new_tokens * kHeadDim);
+  const size_t oVn = cv.take<uint16_t>((size_t)P * c.max_new_tokens * kHeadDim);
+  const size_t oAn = cv.take<uint16_t>(c.new_token_mode == SKV_NEW_LOWRANK ? (size_t)b * c.max_new_tokens * r : 0);
   const size_t oMc = cv.take<float>((size_t)P * n_c);
   const size_t oIf = cv.take<double>(kHeadDim / 2);
   const size_t pool_bytes = cv.off;
@@ -370,6 +393,9 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->logits = (float*)(base + oLg);
     h->lse_part = (float*)(base + oLp);
     h->attn_part = (float*)(base + oAp);
+    h->key_new = (uint16_t*)(base + oKn);
+    h->val_new = (uint16_t*)(base + oVn);
+    h->a_new = c.new_token_mode == SKV_NEW_LOWRANK ? (uint16_t*)(base + oAn) : nullptr;
     h->min_cos = (float*)(base + oMc);
     h->inv_freq = (double*)(base + oIf);
   }
@@ -433,6 +459,7 @@ skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t*
   if (!h) return SKV_ERR_INVALID_ARG;
   if (h->poisoned) return SKV_ERR_STATE;
   if (!q || !out || !chunk_ids) return SKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(chunk_ids, 4)) return SKV_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   DecodeArgs a = decode_args(h);
   a.q = q;
@@ -478,6 +505,23 @@ hip_fail:
   return SKV_ERR_HIP;
 }
 
+skv_status skv_append_token(skv_layer* h, const uint16_t* k_new, const uint16_t* v_new, void* stream) {
+  if (!h || !k_new || !v_new) return SKV_ERR_INVALID_ARG;
+  if (h->poisoned) return SKV_ERR_STATE;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return SKV_ERR_INVALID_ARG;
+  if (h->n_new >= h->cfg.max_new_tokens) return SKV_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeArgs a = decode_args(h);
+  HIP_TRY(launch_append(a, k_new, v_new, h->n_new, h->cfg.new_token_mode == SKV_NEW_LOWRANK, h->a_new, s));
+  h->n_new++;
+  h->last_stream = s;
+  return SKV_OK;
+hip_fail:
+  (void)hipGetLastError();
+  h->poisoned = true;
+  return SKV_ERR_HIP;
+}
+
 skv_status skv_reset_temporal_cache(skv_layer* h) {
   if (!h) return SKV_ERR_INVALID_ARG;
   if (h->poisoned) return SKV_ERR_STATE;
@@ -492,6 +536,7 @@ skv_status skv_get_stats(const skv_layer* hc, skv_stats* out) {
   if (h->poisoned) return SKV_ERR_STATE;
   std::memset(out, 0, sizeof(*out));
   out->steps = h->steps;
+  out->new_tokens = h->n_new;
   if (h->need_reset) return SKV_OK;   // counters are cleared by the next step
   const int P = h->P;
   std::vector<int32_t> nm(P), hl(P);

@@ -16,6 +16,7 @@ constexpr int kScoreRows = 128;          // candidate landmarks per score workgr
 // Everything a decode step touches, by value into the kernels.
 struct DecodeArgs {
   int batch, n_kv, group, chunk, top_k, n_outlier, n_win_units, n_cand;
+  int n_new_tokens, n_new_units, max_new;   // appended tokens, their units, capacity
   int64_t seq_len;
   int nb_score, cpb;          // score workgroups per pair, candidates per workgroup
   int ncp;                    // logits row stride (n_cand rounded up to 4)
@@ -36,6 +37,8 @@ struct DecodeArgs {
   const uint16_t* v_win;
   const uint16_t* v_store;    // [b][Hkv][S][d] (device pointer, may map host memory)
   uint16_t* key_slots;        // [P][K][C][d]
+  uint16_t* key_new;          // [P][max_new][d] post-RoPE keys of appended tokens
+  uint16_t* val_new;          // [P][max_new][d] their values
   uint16_t* val_slots;        // [P][K][C][d] (host placement only)
   // temporal cache
   int32_t* slot_cand;         // [P][K]
@@ -91,6 +94,10 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
 // top-K are taken by separate workgroups (stage 1), then merged per pair (stage 2).
 void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, int* part_size);
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
+// Append token t (position S + t) of every batch element; lowrank: also store
+// a' = k' Psi in a_new [b][max_new][r].
+hipError_t launch_append(const DecodeArgs& a, const uint16_t* k_new, const uint16_t* v_new, int t, bool lowrank,
+                         uint16_t* a_new, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);
 int attn_units_per_wave(int group, int chunk);

@@ -19,8 +19,9 @@ _lib = None
 SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_SHAPE, SKV_ERR_UNSUPPORTED = 0, 1, 2, 3
 SKV_ERR_OOM, SKV_ERR_HIP, SKV_ERR_STATE, SKV_ERR_INTERNAL = 4, 5, 6, 7
 SKV_VALUES_DEVICE, SKV_VALUES_HOST = 0, 1
+SKV_NEW_EXACT, SKV_NEW_LOWRANK = 0, 1
 
-EXPORTED = ["skv_build", "skv_decode_step", "skv_get_stats", "skv_reset_temporal_cache",
+EXPORTED = ["skv_build", "skv_decode_step", "skv_append_token", "skv_get_stats", "skv_reset_temporal_cache",
             "skv_export_state", "skv_set_timing", "skv_get_timing", "skv_destroy",
             "skv_status_string", "skv_abi_version"]
 PHASES = ["score", "select", "rebuild", "value_gather", "attention"]
@@ -32,14 +33,16 @@ class SkvConfig(ctypes.Structure):
                 ("seq_len", ctypes.c_int64), ("rank", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_outlier", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("value_placement", ctypes.c_int32), ("rope_theta", ctypes.c_double),
-                ("temporal_cache", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("temporal_cache", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_new_tokens", ctypes.c_int32), ("new_token_mode", ctypes.c_int32)]
 
 
 class SkvStats(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int64), ("last_hits", ctypes.c_int64),
                 ("last_misses", ctypes.c_int64), ("total_hits", ctypes.c_int64),
                 ("total_misses", ctypes.c_int64), ("last_alpha", ctypes.c_double),
-                ("mean_alpha", ctypes.c_double), ("last_host_bytes", ctypes.c_int64)]
+                ("mean_alpha", ctypes.c_double), ("last_host_bytes", ctypes.c_int64),
+                ("new_tokens", ctypes.c_int64)]
 
 
 class SkvStateHost(ctypes.Structure):
@@ -66,6 +69,8 @@ def lib():
         L.skv_build.restype = i32
         L.skv_decode_step.argtypes = [vp, vp, vp, vp, vp]
         L.skv_decode_step.restype = i32
+        L.skv_append_token.argtypes = [vp, vp, vp, vp]
+        L.skv_append_token.restype = i32
         L.skv_get_stats.argtypes = [vp, ctypes.POINTER(SkvStats)]
         L.skv_get_stats.restype = i32
         L.skv_reset_temporal_cache.argtypes = [vp]
@@ -94,11 +99,13 @@ def skv_abi_version() -> int:
     return lib().skv_abi_version()
 
 
-def make_config(shape, value_placement: int = SKV_VALUES_DEVICE, temporal_cache: int = 1) -> SkvConfig:
+def make_config(shape, value_placement: int = SKV_VALUES_DEVICE, temporal_cache: int = 1,
+                max_new_tokens: int = 0, new_token_mode: int = SKV_NEW_EXACT) -> SkvConfig:
     """skv_config from any object with the ShadowKV shape fields."""
     return SkvConfig(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                      shape.seq_len, shape.rank, shape.chunk, shape.top_k, shape.n_outlier,
-                     shape.window, value_placement, float(shape.rope_theta), temporal_cache, 0)
+                     shape.window, value_placement, float(shape.rope_theta), temporal_cache, 0,
+                     max_new_tokens, new_token_mode)
 
 
 def _ptr(t) -> int | None:
@@ -134,6 +141,10 @@ def skv_build(cfg: SkvConfig, k_pre, v, stream=None) -> int:
 def skv_decode_step(h: int, q, out, chunk_ids, stream=None) -> None:
     _check("skv_decode_step", lib().skv_decode_step(h, _ptr(q), _ptr(out), _ptr(chunk_ids),
                                                     _stream(stream)))
+
+
+def skv_append_token(h: int, k_new, v_new, stream=None) -> None:
+    _check("skv_append_token", lib().skv_append_token(h, _ptr(k_new), _ptr(v_new), _stream(stream)))
 
 
 def skv_get_stats(h: int) -> dict:
@@ -187,8 +198,8 @@ class Layer:
     """Owning wrapper of one built layer."""
 
     def __init__(self, shape, k_pre, v, value_placement=SKV_VALUES_DEVICE, temporal_cache=1,
-                 stream=None):
-        self.cfg = make_config(shape, value_placement, temporal_cache)
+                 stream=None, max_new_tokens=0, new_token_mode=SKV_NEW_EXACT):
+        self.cfg = make_config(shape, value_placement, temporal_cache, max_new_tokens, new_token_mode)
         self.shape = shape
         self.h = skv_build(self.cfg, k_pre, v, stream)
         self._v = v   # the value store is borrowed by the library: keep it alive
@@ -202,6 +213,11 @@ class Layer:
             chunk_ids = torch.empty((s.batch, s.n_kv_heads, s.top_k), dtype=torch.int32, device=dev)
         skv_decode_step(self.h, q, out, chunk_ids, stream)
         return out, chunk_ids
+
+    def append(self, k_new, v_new, stream=None):
+        """Append one generated token per batch element: k_new pre-RoPE bf16
+        [b][H_kv*d], v_new bf16 [b][H_kv][d] (device)."""
+        skv_append_token(self.h, k_new, v_new, stream)
 
     def stats(self):
         return skv_get_stats(self.h)

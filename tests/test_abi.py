@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert skv.skv_abi_version() == 1
+    assert skv.skv_abi_version() == 2
     seen = set()
     for code in range(8):
         s = skv.skv_status_string(code)
@@ -71,6 +71,8 @@ def _cfg(**kw):
     (dict(temporal_cache=3), skv.SKV_ERR_INVALID_ARG),
     (dict(reserved=1), skv.SKV_ERR_INVALID_ARG),
     (dict(batch=0), skv.SKV_ERR_SHAPE),
+    (dict(max_new_tokens=-1), skv.SKV_ERR_SHAPE),
+    (dict(new_token_mode=2), skv.SKV_ERR_INVALID_ARG),
 ])
 def test_build_validation(kw, expect):
     st, h = _build_status(_cfg(**kw))
@@ -89,6 +91,7 @@ def test_build_null_arguments():
 def test_null_handle_calls():
     lib = skv.lib()
     assert lib.skv_decode_step(None, 1, 1, 1, None) == skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_append_token(None, 1, 1, None) == skv.SKV_ERR_INVALID_ARG
     assert lib.skv_get_stats(None, ctypes.byref(skv.SkvStats())) == skv.SKV_ERR_INVALID_ARG
     assert lib.skv_reset_temporal_cache(None) == skv.SKV_ERR_INVALID_ARG
     assert lib.skv_export_state(None, ctypes.byref(skv.SkvStateHost())) == skv.SKV_ERR_INVALID_ARG
@@ -111,7 +114,8 @@ int main(void) {
   printf("skv_config %zu\nskv_stats %zu\nskv_state_host %zu\n", sizeof(skv_config),
          sizeof(skv_stats), sizeof(skv_state_host));
   P(skv_config, seq_len) P(skv_config, rope_theta) P(skv_config, temporal_cache)
-  P(skv_config, reserved) P(skv_stats, last_alpha) P(skv_stats, last_host_bytes)
+  P(skv_config, reserved) P(skv_config, max_new_tokens) P(skv_config, new_token_mode)
+  P(skv_stats, last_alpha) P(skv_stats, last_host_bytes) P(skv_stats, new_tokens)
   P(skv_state_host, eigvals)
   return 0;
 }
@@ -130,6 +134,9 @@ int main(void) {
                               "skv_config.rope_theta": (skv.SkvConfig, "rope_theta"),
                               "skv_config.temporal_cache": (skv.SkvConfig, "temporal_cache"),
                               "skv_config.reserved": (skv.SkvConfig, "reserved"),
+                              "skv_config.max_new_tokens": (skv.SkvConfig, "max_new_tokens"),
+                              "skv_config.new_token_mode": (skv.SkvConfig, "new_token_mode"),
+                              "skv_stats.new_tokens": (skv.SkvStats, "new_tokens"),
                               "skv_stats.last_alpha": (skv.SkvStats, "last_alpha"),
                               "skv_stats.last_host_bytes": (skv.SkvStats, "last_host_bytes"),
                               "skv_state_host.eigvals": (skv.SkvStateHost, "eigvals")}.items():

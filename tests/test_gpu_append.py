@@ -1,0 +1,122 @@
+"""Generated tokens (skv_append_token) against the oracle: exact and low-rank
+(ShadowKV+) keys, appended between decode steps, attended after the sparse set.
+
+Both sides start from the same bf16 context and receive the same bf16 new
+tokens; the schedules leave the last unit of appended tokens partly filled and
+make the attention split grow between steps.  Once tokens have been appended,
+every other q-head aims at one of them (the rest at the context), so that the
+generated tokens carry most of those heads' attention weight."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import shadowkv as O
+from sparse_kv_cache_decode_amd import skv, synth
+from tests.parity import bits, check_build, check_ids, check_out, reference_out
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(**kw):
+    base = dict(name="small", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=8168,
+                rank=64, chunk=8, top_k=13, n_outlier=5, window=32, latent_rank=64)
+    base.update(kw)
+    return synth.Shape(**base)
+
+
+def _mixed_queries(shape, k, kn, schedule, seed):
+    q = synth.queries_np(shape, k, 0, len(schedule), seed)
+    avail = np.cumsum(schedule)
+    if avail.max() > 0:
+        qn = synth.queries_new_np(shape, kn, [max(int(n), 1) for n in avail], 0, seed)
+        for t, n in enumerate(avail):
+            if n > 0:
+                q[t, :, 1::2] = qn[t, :, 1::2]
+    return q
+
+
+def _run_append(shape, mode, schedule, max_new, seed=0):
+    lowrank = mode == skv.SKV_NEW_LOWRANK
+    print(f"[append] {shape.name} b={shape.batch} G={shape.group} C={shape.chunk} r={shape.rank} "
+          f"mode={'lowrank' if lowrank else 'exact'} schedule={schedule} max_new={max_new}", flush=True)
+    n_tok = sum(schedule)
+    k, v = synth.layer_cache_np(shape, 0, seed)
+    kn, vn = synth.continuation_np(shape, 0, n_tok, seed)
+    q = _mixed_queries(shape, k, kn, schedule, seed)
+    st = O.build(O.config_from(shape), bits(k), bits(v))
+    layer = skv.Layer(shape, k.cuda(), v.cuda(), max_new_tokens=max_new, new_token_mode=mode)
+    check_build(layer.export(), st)
+    knd, vnd = kn.cuda(), vn.cuda()
+    prev = None
+    used = 0
+    worst = (0.0, 0.0)
+    for step, n in enumerate(schedule):
+        for t in range(used, used + n):
+            layer.append(knd[t], vnd[t])
+            O.append(st, bits(kn[t]), bits(vn[t]), lowrank=lowrank)
+        used += n
+        out, ids = layer.decode(q[step].cuda())
+        torch.cuda.synchronize()
+        assert layer.stats()["new_tokens"] == used
+        res = O.decode_step(st, bits(q[step]), prev)
+        gids = ids.cpu().numpy()
+        differ = check_ids(gids, st, res)
+        e = check_out(out.cpu().numpy(), reference_out(st, bits(q[step]), res, gids, differ))
+        worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+        prev = res.ids
+    print(f"[append] ok: {used} tokens, max|err| {worst[0]:.2e} relL2 {worst[1]:.2e}", flush=True)
+    return layer, knd, vnd
+
+
+@pytest.mark.parametrize("mode", [skv.SKV_NEW_EXACT, skv.SKV_NEW_LOWRANK])
+def test_append_between_steps(mode):
+    # 0, 3, 10, 19 tokens: the first step has none, later ones end in a partial
+    # unit (C = 8), and 19 tokens add a third unit to the split count
+    layer, kn, vn = _run_append(_small(), mode, [0, 3, 7, 9], max_new=21)
+    layer.close()
+
+
+def test_append_capacity_is_enforced():
+    shape = _small(batch=1)
+    layer, kn, vn = _run_append(shape, skv.SKV_NEW_EXACT, [2, 1], max_new=3)
+    with pytest.raises(skv.SkvError) as e:
+        layer.append(kn[0], vn[0])
+    assert e.value.status == skv.SKV_ERR_SHAPE
+    assert layer.stats()["new_tokens"] == 3
+    layer.close()
+
+
+@pytest.mark.parametrize("mode", [skv.SKV_NEW_EXACT, skv.SKV_NEW_LOWRANK])
+def test_append_group_of_eight_chunk_sixteen(mode):
+    shape = _small(batch=1, n_q_heads=16, seq_len=8192, chunk=16, top_k=7, n_outlier=2,
+                   rank=96, latent_rank=96)
+    layer, _, _ = _run_append(shape, mode, [5, 12, 20], max_new=40)
+    layer.close()
+
+
+def test_append_lowrank_full_rank_one_kv_head():
+    # rank = H_kv * d: Psi is square (the low-rank state still goes through bf16)
+    shape = _small(batch=1, n_q_heads=4, n_kv_heads=1, seq_len=2048, rank=128, latent_rank=64,
+                   top_k=9, n_outlier=2)
+    layer, _, _ = _run_append(shape, skv.SKV_NEW_LOWRANK, [17, 1], max_new=18, seed=3)
+    layer.close()
+
+
+def test_misaligned_pointers_rejected_before_any_launch():
+    shape = _small(batch=1, seq_len=2048, top_k=9, n_outlier=2)
+    k, v = synth.layer_cache_np(shape, 0, 1)
+    kn, vn = synth.continuation_np(shape, 0, 1, 1)
+    layer = skv.Layer(shape, k.cuda(), v.cuda(), max_new_tokens=2)
+    lib = skv.lib()
+    q = torch.zeros((1, shape.n_q_heads * shape.head_dim + 8), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((1, shape.n_q_heads, shape.head_dim), device="cuda")
+    ids = torch.empty((1, shape.n_kv_heads, shape.top_k), dtype=torch.int32, device="cuda")
+    knd = torch.zeros(kn.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    vnd = vn.cuda()
+    assert lib.skv_decode_step(layer.h, q.data_ptr() + 2, out.data_ptr(), ids.data_ptr(), None) == \
+        skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_decode_step(layer.h, q.data_ptr(), out.data_ptr() + 4, ids.data_ptr(), None) == \
+        skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_append_token(layer.h, knd.data_ptr() + 2, vnd.data_ptr(), None) == skv.SKV_ERR_INVALID_ARG
+    assert layer.stats()["new_tokens"] == 0 and layer.stats()["steps"] == 0
+    layer.close()
