@@ -37,11 +37,16 @@ test prefer the lower chunk id; selected ids are returned ascending; cosine
 with a zero vector is 0; stored state (A, B, landmarks, outlier and window
 keys, rebuilt keys) is rounded once to bfloat16 with round-to-nearest-even
 when ``storage_rounding`` is on.  Generated tokens: the t-th appended token
-(t = 0, 1, ...) sits at position seq_len + t; every decode step attends to all
-of them and they take no part in scoring or selection; exact mode keeps
-RoPE(k'); low-rank mode takes Psi^T to be the stored B of the batch element
-(heads concatenated), keeps a' = k' Psi and the key RoPE(a' Psi^T), both
-rounded like the rest of the stored state; values are kept as given.
+(t = 0, 1, ...) sits at position seq_len + t and its value is kept as given.
+Exact mode (ShadowKV's assembly): every decode step attends to all of them
+with the exact key RoPE(k'), and they take no part in scoring or selection.
+Low-rank mode (ShadowKV+): a' = k' Psi, with Psi^T the stored B of the batch
+element (heads concatenated), is kept as the token's row of A; the last
+``window`` tokens of the completed chunks and the tokens of the chunk being
+filled stay exact (RoPE(k')); when a chunk completes, the oldest exact chunk
+leaves that region and joins the candidates (never the outliers) with the
+mean of its stored exact keys as landmark, and from then on is scored,
+selected and rebuilt from A like any context chunk.
 """
 from __future__ import annotations
 
@@ -206,9 +211,10 @@ class State:
     V_win: np.ndarray        # [b, H, W, d]
     V: np.ndarray            # [b, H, S, d] value store (V_CPU plus the rest)
     storage_rounding: bool = True
-    K_new: np.ndarray | None = None   # [b, H, T, d] post-RoPE keys of generated tokens
-    V_new: np.ndarray | None = None   # [b, H, T, d] their values
-    A_new: np.ndarray | None = None   # [b, T, r] low-rank states a' = k' Psi (low-rank mode)
+    K_new: np.ndarray | None = None   # exact mode: [b, H, T, d] post-RoPE keys of generated tokens
+    V_new: np.ndarray | None = None   # exact mode: [b, H, T, d] their values
+    n_new: int = 0                    # generated tokens appended so far
+    new_mode: str | None = None       # "exact" or "lowrank" once a token is appended
 
     def keep(self, x):
         return round_bf16(x) if self.storage_rounding else x
@@ -261,33 +267,42 @@ def append(st: State, k_new, v_new, lowrank: bool = False) -> None:
 
     ``k_new``: [b, H*d] pre-RoPE key (heads concatenated), ``v_new``: [b, H, d];
     bf16 bit patterns or floats.  The token's position is seq_len plus the
-    number of tokens appended before it.
+    number of tokens appended before it.  A state takes one mode for all its
+    appended tokens.
     """
     cfg = st.cfg
     k_new, v_new = _as_f64(k_new), _as_f64(v_new)
-    b, H, d = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    b, H, d, C = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.chunk
     assert k_new.shape == (b, H * d) and v_new.shape == (b, H, d)
-    t = 0 if st.K_new is None else st.K_new.shape[2]
+    mode = "lowrank" if lowrank else "exact"
+    assert st.new_mode in (None, mode), "one mode per state"
+    st.new_mode = mode
+    t = st.n_new
     pos = np.array([cfg.seq_len + t])
     keys = np.zeros((b, H, 1, d))
-    a_rows = np.zeros((b, 1, cfg.rank))
     for bi in range(b):
-        k = k_new[bi]
-        if lowrank:
-            pt = psi_t(st, bi)                     # [r, H*d]
-            a_rows[bi, 0] = st.keep(k @ pt.T)      # a' = k' Psi
-            k = a_rows[bi, 0] @ pt                 # (k' Psi) Psi^T
         for h in range(H):
-            keys[bi, h] = st.keep(apply_rope(k[h * d:(h + 1) * d][None], pos, cfg.rope_theta))
+            keys[bi, h] = st.keep(apply_rope(k_new[bi, h * d:(h + 1) * d][None], pos, cfg.rope_theta))
     vals = v_new[:, :, None, :]
-    if st.K_new is None:
-        st.K_new, st.V_new = keys, vals
-        st.A_new = a_rows if lowrank else None
-    else:
-        st.K_new = np.concatenate([st.K_new, keys], axis=2)
-        st.V_new = np.concatenate([st.V_new, vals], axis=2)
-        if lowrank:
-            st.A_new = np.concatenate([st.A_new, a_rows], axis=1)
+    st.n_new += 1
+    if not lowrank:
+        st.K_new = keys if st.K_new is None else np.concatenate([st.K_new, keys], axis=2)
+        st.V_new = vals if st.V_new is None else np.concatenate([st.V_new, vals], axis=2)
+        return
+    # the low-rank state joins A, the value joins the value store
+    a_rows = np.stack([st.keep(k_new[bi] @ psi_t(st, bi).T) for bi in range(b)])[:, None]
+    st.A = np.concatenate([st.A, a_rows], axis=1)
+    st.V = np.concatenate([st.V, vals], axis=2)
+    # the exact region grows by the new token; a completed chunk pushes the
+    # oldest exact chunk out to the candidates
+    st.K_win = np.concatenate([st.K_win, keys], axis=2)
+    st.V_win = np.concatenate([st.V_win, vals], axis=2)
+    if st.n_new % C == 0:
+        lm = st.keep(st.K_win[:, :, :C].mean(axis=2))             # [b, H, d]
+        chunk = (cfg.seq_len - cfg.window) // C + st.n_new // C - 1
+        st.L = np.concatenate([st.L, lm[:, :, None]], axis=2)
+        st.cand = np.concatenate([st.cand, np.full((b, H, 1), chunk, dtype=st.cand.dtype)], axis=2)
+        st.K_win, st.V_win = st.K_win[:, :, C:], st.V_win[:, :, C:]
 
 
 def _as_f64(x):
@@ -368,7 +383,7 @@ def decode_step(st: State, q, prev_ids: np.ndarray | None = None) -> StepResult:
     b, H, G, C, K = cfg.batch, cfg.n_kv_heads, cfg.group, cfg.chunk, cfg.top_k
     out = np.zeros((b, cfg.n_q_heads, cfg.head_dim))
     ids = np.zeros((b, H, K), dtype=np.int64)
-    scores = np.zeros((b, H, cfg.n_cand))
+    scores = np.zeros((b, H, st.cand.shape[2]))
     hits = np.zeros((b, H), dtype=np.int64)
     for bi in range(b):
         for h in range(H):

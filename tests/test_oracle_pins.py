@@ -5,6 +5,7 @@ form, a different routine (eigh of the Gram matrix, torch's bfloat16
 conversion, complex rotation), brute force in pure Python on tiny inputs, or a
 value the pages print (tests/golden/).
 """
+import dataclasses
 import itertools
 import json
 import math
@@ -417,10 +418,10 @@ def test_appended_tokens_full_budget_equals_dense_attention(lowrank):
 
 
 def test_lowrank_state_is_the_projection_on_the_context_subspace():
-    # the stored key of a generated token, rotated back, is k' projected on the
-    # top-r right singular subspace of the context keys (computed here from
+    # a generated token's row of A, mapped back through Psi^T, is k' projected on
+    # the top-r right singular subspace of the context keys (computed here from
     # eigh of the Gram matrix), and a context key appended again gets exactly
-    # its row of A as low-rank state (A = K Psi)
+    # its own row of A (A = K Psi)
     rng = np.random.default_rng(32)
     cfg = small_cfg(seq_len=128, rank=6)
     hd, d, S = cfg.n_kv_heads * cfg.head_dim, cfg.head_dim, cfg.seq_len
@@ -433,18 +434,19 @@ def test_lowrank_state_is_the_projection_on_the_context_subspace():
     knew = [rng.standard_normal(hd), k[0, 17]]
     for kn in knew:
         O.append(st, kn[None], rng.standard_normal((1, cfg.n_kv_heads, d)), lowrank=True)
+    psi_t = np.concatenate([st.B[0, h] for h in range(cfg.n_kv_heads)], axis=1)   # [r, H d]
     for t, kn in enumerate(knew):
-        back = np.concatenate([O.apply_rope(st.K_new[0, h, t][None], np.array([-(S + t)]),
-                                            cfg.rope_theta)[0] for h in range(cfg.n_kv_heads)])
+        back = st.A[0, S + t] @ psi_t
         np.testing.assert_allclose(back, kn @ proj, atol=1e-9)
         assert np.abs((kn - back) @ top).max() < 1e-9          # residual orthogonal to Psi
-    np.testing.assert_allclose(st.A_new[0, 1], st.A[0, 17], atol=1e-9)
+    np.testing.assert_allclose(st.A[0, S + 1], st.A[0, 17], atol=1e-9)
 
 
 def test_appended_tokens_leave_selection_alone_and_are_rounded():
+    # fewer tokens than a chunk: nothing joins the candidates yet
     rng = np.random.default_rng(33)
     cfg = small_cfg(seq_len=128, top_k=4)
-    hd, d = cfg.n_kv_heads * cfg.head_dim, cfg.head_dim
+    hd, d, S = cfg.n_kv_heads * cfg.head_dim, cfg.head_dim, cfg.seq_len
     k = lowrank_keys(rng, 1, cfg.seq_len, hd, 8)
     v = rng.standard_normal((1, cfg.n_kv_heads, cfg.seq_len, d))
     q = rng.standard_normal((1, cfg.n_q_heads, d)) * 3
@@ -452,12 +454,44 @@ def test_appended_tokens_leave_selection_alone_and_are_rounded():
     before = O.decode_step(st, q)
     for lowrank in (False, True):
         st2 = O.build(cfg, k, v)
-        for _ in range(2):
+        for _ in range(cfg.chunk - 1):
             O.append(st2, rng.standard_normal((1, hd)), rng.standard_normal((1, cfg.n_kv_heads, d)),
                      lowrank=lowrank)
         after = O.decode_step(st2, q)
         np.testing.assert_array_equal(after.ids, before.ids)
         assert not np.allclose(after.out, before.out)
-        for arr in [st2.K_new] + ([st2.A_new] if lowrank else []):
+        stored = [st2.A[:, S:], st2.K_win] if lowrank else [st2.K_new]
+        for arr in stored:
             as32 = torch.tensor(arr, dtype=torch.float32)
             np.testing.assert_array_equal(as32.to(torch.bfloat16).to(torch.float64).numpy(), arr)
+
+
+@pytest.mark.parametrize("window,n_new", [(8, 14), (8, 12), (0, 9)])
+def test_lowrank_folding_equals_a_build_on_the_grown_context(window, n_new):
+    # no outliers, full rank, no storage rounding: after n = m C + p appended
+    # tokens the ShadowKV+ state decodes exactly like a build on the first
+    # S + m C tokens of the grown sequence with the last p tokens appended in
+    # exact mode (folded landmarks, chunk ids, rolled window, A rows and values
+    # all have to line up)
+    rng = np.random.default_rng(34)
+    cfg = small_cfg(n_outlier=0, window=window, top_k=3)
+    cfg = small_cfg(n_outlier=0, window=window, top_k=3, rank=cfg.n_kv_heads * cfg.head_dim)
+    hd, d, S, C = cfg.n_kv_heads * cfg.head_dim, cfg.head_dim, cfg.seq_len, cfg.chunk
+    m, p = divmod(n_new, C)
+    k = lowrank_keys(rng, 1, S + n_new, hd, 8)
+    v = rng.standard_normal((1, cfg.n_kv_heads, S + n_new, d))
+    st = O.build(cfg, k[:, :S], v[:, :, :S], storage_rounding=False)
+    for t in range(n_new):
+        O.append(st, k[:, S + t], v[:, :, S + t], lowrank=True)
+    grown = dataclasses.replace(cfg, seq_len=S + m * C)
+    ref = O.build(grown, k[:, :S + m * C], v[:, :, :S + m * C], storage_rounding=False)
+    for t in range(p):
+        O.append(ref, k[:, S + m * C + t], v[:, :, S + m * C + t], lowrank=False)
+    np.testing.assert_array_equal(st.cand, ref.cand)
+    np.testing.assert_allclose(st.L, ref.L, atol=1e-12)
+    assert st.cand.shape[2] == cfg.n_cand + m
+    for _ in range(3):
+        q = rng.standard_normal((1, cfg.n_q_heads, d)) * 3
+        a, b = O.decode_step(st, q), O.decode_step(ref, q)
+        np.testing.assert_array_equal(a.ids, b.ids)
+        np.testing.assert_allclose(a.out, b.out, atol=1e-9)
