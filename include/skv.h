@@ -19,9 +19,10 @@
  *   - generated tokens (paper-graph-ui summary, section 3.4 "Sparse KV
  *     Reconstruction and Overlapping Strategy": the assembly
  *     [K_outlier; RoPE(K_sparse); K_new] and the paragraph on the ShadowKV+
- *     extension): appended one per step and always attended, either exact
- *     (ShadowKV) or stored as their projection onto the pre-fill subspace and
- *     reconstructed from it (ShadowKV+).
+ *     extension): appended one per step, either kept exact and always attended
+ *     (ShadowKV) or, once their chunk has left the local window, kept only as
+ *     their projection onto the pre-fill subspace and selected and
+ *     reconstructed like the context's chunks (ShadowKV+).
  *
  * Conventions shared by every entry point
  *   - Every call returns an skv_status; SKV_OK is 0.  No C++ exception crosses
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 2
+#define SKV_ABI_VERSION 3
 
 typedef int32_t skv_status;
 #define SKV_OK 0
@@ -68,9 +69,10 @@ typedef int32_t skv_status;
 
 /* How appended (generated) tokens keep their keys. */
 #define SKV_NEW_EXACT 0        /* post-RoPE key kept exactly (ShadowKV)             */
-#define SKV_NEW_LOWRANK 1      /* pre-RoPE key projected onto the pre-fill subspace,
-                                  a' = k' Psi (Psi^T = the stored B), kept as a' and
-                                  reconstructed as RoPE(a' Psi^T) (ShadowKV+)       */
+#define SKV_NEW_LOWRANK 1      /* ShadowKV+: a' = k' Psi (Psi^T = the stored B) joins
+                                  A; the token stays exact while it is in the local
+                                  window, then its chunk becomes a candidate that is
+                                  reconstructed as RoPE(a' Psi^T) when selected      */
 
 /*
  * Shape and budget of one layer.
@@ -121,7 +123,10 @@ typedef struct skv_stats {
  * pointer may be NULL to skip that tensor.  Sizes (elements):
  *   A          bf16 [b][S][r]
  *   B          bf16 [b][H_kv][r][d]       (the per-head right factor)
- *   landmarks  bf16 [b][H_kv][n_cand][d]  (candidate chunks, ascending chunk id)
+ *   landmarks  bf16 [b][H_kv][n_cand][d]  (candidate chunks of the pre-filled
+ *                                          context, ascending chunk id; chunks
+ *                                          folded in by skv_append_token are not
+ *                                          exported)
  *   cand_ids   int32 [b][H_kv][n_cand]    (chunk id of each landmark row)
  *   outlier_ids int32 [b][H_kv][O]        (ascending)
  *   k_outlier, v_outlier bf16 [b][H_kv][O*C][d]   (post-RoPE keys, values)
@@ -188,18 +193,27 @@ skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t*
 /*
  * skv_append_token -- append one generated token to the layer (paper-graph-ui
  * summary, section 3.4 "Sparse KV Reconstruction and Overlapping Strategy": the
- * generated tokens' K_new, V_new are attended after the sparse set; its ShadowKV+
+ * generated tokens' K_new, V_new close the assembled cache; its ShadowKV+
  * paragraph: a new pre-RoPE key k' is kept as k' Psi and reconstructed as
- * (k' Psi) Psi^T).
+ * (k' Psi) Psi^T when needed).
  *   k_new : device, bf16 [b][H_kv*d], the new token's pre-RoPE keys, heads
  *           concatenated; its position is seq_len + (tokens appended so far).
  *   v_new : device, bf16 [b][H_kv][d], its values.
  *   stream: enqueued, no host synchronisation.  Both inputs are only read by the
  *           enqueued work (they may be reused once the stream has passed it).
- * SKV_NEW_EXACT stores RoPE(k'); SKV_NEW_LOWRANK stores a' = k' Psi in bf16 (Psi^T
- * being the stored bf16 B) and the key RoPE(a' Psi^T).  Every later decode step
- * attends to all appended tokens.  The landmarks, outliers and the selection
- * cover the pre-filled context only.
+ * SKV_NEW_EXACT: the key RoPE(k') (bf16) and the value are kept, and every later
+ * decode step attends to all appended tokens after the local window; landmarks,
+ * outliers and the selection cover the pre-filled context only.
+ * SKV_NEW_LOWRANK (ShadowKV+): a' = k' Psi (fp32 accumulation over the stored
+ * bf16 Psi^T, rounded to bf16) becomes row seq_len + t of A, and RoPE(k') is kept
+ * exactly while the token is in the exact region: the last `window` tokens of the
+ * completed chunks plus the chunk being filled.  When an append completes a chunk,
+ * the oldest exact chunk leaves that region and becomes the last candidate of
+ * every pair (never an outlier): its landmark is the bf16 mean of its stored
+ * exact keys, its chunk id (seq_len - window)/chunk + (chunks completed so far)
+ * - 1; from the next decode step it is scored, selected, rebuilt from A and its
+ * values read (from the value store, or from the appended values) like a
+ * context chunk.
  * Errors: INVALID_ARG (null pointer), SHAPE (capacity max_new_tokens reached),
  * STATE, HIP.
  */

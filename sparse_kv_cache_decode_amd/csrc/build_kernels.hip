@@ -104,7 +104,7 @@ hipError_t launch_outliers(const float* min_cos, int P, int n_c, int n_elig, int
 
 __global__ __launch_bounds__(256) void candidates_kernel(const uint16_t* __restrict__ L_full,
                                                          const int32_t* __restrict__ outlier_ids,
-                                                         int n_c, int n_elig, int O,
+                                                         int n_c, int n_elig, int O, int stride,
                                                          uint16_t* __restrict__ L,
                                                          int32_t* __restrict__ cand_map) {
   const int lane = threadIdx.x & 63;
@@ -120,17 +120,16 @@ __global__ __launch_bounds__(256) void candidates_kernel(const uint16_t* __restr
   }
   if (lo < O && oid[lo] == j) return;
   const int ci = j - lo;
-  const int n_cand = n_elig - O;
   const uint32_t* src = reinterpret_cast<const uint32_t*>(L_full + ((int64_t)p * n_c + j) * kHeadDim);
-  uint32_t* dst = reinterpret_cast<uint32_t*>(L + ((int64_t)p * n_cand + ci) * kHeadDim);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(L + ((int64_t)p * stride + ci) * kHeadDim);
   dst[lane] = src[lane];
-  if (lane == 0) cand_map[(int64_t)p * n_cand + ci] = j;
+  if (lane == 0) cand_map[(int64_t)p * stride + ci] = j;
 }
 
 hipError_t launch_candidates(const uint16_t* L_full, const int32_t* outlier_ids, int P, int n_c,
-                             int n_elig, int O, uint16_t* L, int32_t* cand_map, hipStream_t st) {
+                             int n_elig, int O, int stride, uint16_t* L, int32_t* cand_map, hipStream_t st) {
   dim3 grid((n_elig + 3) / 4, P);
-  candidates_kernel<<<grid, 256, 0, st>>>(L_full, outlier_ids, n_c, n_elig, O, L, cand_map);
+  candidates_kernel<<<grid, 256, 0, st>>>(L_full, outlier_ids, n_c, n_elig, O, stride, L, cand_map);
   return hipGetLastError();
 }
 
@@ -342,7 +341,7 @@ hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batc
 
 __global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict__ k_pre,
                                                       const float* __restrict__ psi, int64_t S,
-                                                      int HD, int r, uint16_t* __restrict__ A) {
+                                                      int HD, int r, int64_t a_rows, uint16_t* __restrict__ A) {
   __shared__ float tk[32][64 + 1];   // [k][row]
   __shared__ float tp[32][64 + 1];   // [k][col]
   const int b = blockIdx.z;
@@ -392,15 +391,15 @@ __global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const int col = n0 + tx * 4 + q;
-      if (col < r) A[((int64_t)b * S + row) * r + col] = f32_to_bf16(acc[p][q]);
+      if (col < r) A[((int64_t)b * a_rows + row) * r + col] = f32_to_bf16(acc[p][q]);
     }
   }
 }
 
 hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_t S, int HD, int r,
-                          uint16_t* A, hipStream_t st) {
+                          int64_t a_rows, uint16_t* A, hipStream_t st) {
   dim3 grid((unsigned)((S + 63) / 64), (r + 63) / 64, b);
-  project_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, A);
+  project_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, a_rows, A);
   return hipGetLastError();
 }
 

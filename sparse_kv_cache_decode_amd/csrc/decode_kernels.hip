@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
   const int col = lane & 15, kq = lane >> 4;
   const int hq = a.n_kv * G;
   const int c0 = blk * kScoreRows, c1 = min(a.n_cand, c0 + kScoreRows), nr = c1 - c0;
-  const uint16_t* Lp = a.L + ((int64_t)p * a.n_cand + c0) * kHeadDim;
+  const uint16_t* Lp = a.L + ((int64_t)p * a.cand_stride + c0) * kHeadDim;
   // rows past a ragged block's end repeat its last row; their outputs are not used
 #pragma unroll
   for (int i = w; i < kScoreRows / 4; i += 4) {
@@ -243,7 +243,7 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
   int32_t* sc = a.slot_cand + (int64_t)p * K;
   int32_t* sch = a.slot_chunk + (int64_t)p * K;
   uint32_t* res = a.resident + (int64_t)p * RW;
-  const int32_t* cmap = a.cand_map + (int64_t)p * a.n_cand;
+  const int32_t* cmap = a.cand_map + (int64_t)p * a.cand_stride;
   for (int i = threadIdx.x; i < K; i += kSelThreads) {
     const int ch = cmap[sel[i]];
     selch[i] = ch;
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   __syncthreads();
   if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
   const uint16_t* Bt = a.Bt + ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
-  const uint16_t* Ab = a.A + (int64_t)b * a.seq_len * r;
+  const uint16_t* Ab = a.A + (int64_t)b * a.a_rows * r;
   // A operand rows of this lane: row m = w*32 + mt*16 + lr (rows past the misses
   // read row 0 of the batch element; their outputs are not stored)
   const uint16_t* arow[2];
@@ -721,26 +721,34 @@ hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Append one generated token (position S + t) for every batch element; one
-// workgroup per (batch element, KV head).  Exact: the key is RoPE(k').  Low rank
-// (paper-graph-ui summary, section 3.4, ShadowKV+): a' = k' Psi with Psi^T the
-// stored B (fp32 accumulation, rounded to bf16 and kept), then the key
-// RoPE(a' Psi^T).  Every low-rank workgroup of a batch element forms the whole
-// a' (the B_t rows of all heads, a few hundred KB that the heads share through
-// L2), so one launch needs no cross-workgroup step; 1024 threads keep about 20
-// row loads per thread, issued eight at a time.  Blocks of one batch element are
-// spaced `batch` apart, which puts them on one XCD when the batch is a multiple
-// of the XCD count.
+// Append one generated token (position S + t) for every batch element.
+//  append_exact_kernel, one workgroup per (batch element, KV head): the exact
+//    post-RoPE key RoPE(k') and the value into key_new / val_new.  In both modes
+//    an appended token is first held exactly (the summary's assembly keeps the
+//    recent tokens' K_new exact; ShadowKV+ keeps them there until their chunk
+//    leaves the local window).
+//  append_project_kernel, low rank only (paper-graph-ui summary, section 3.4,
+//    ShadowKV+ paragraph), one workgroup per batch element: a' = k' Psi with
+//    Psi^T the stored B (fp32 accumulation, rounded to bf16), written as row
+//    S + t of the batch element's A, from where the key rebuild reads it once
+//    the token's chunk has been folded into the candidates.  1024 threads keep
+//    about 20 row loads of B^T per thread, issued eight at a time.
+//  fold_kernel, low rank only, after the append that completes a chunk: the
+//    oldest exact chunk (combined index n_fold over [window units; appended
+//    units]) becomes the pair's last candidate, its landmark the bf16 mean of its
+//    stored exact keys and its chunk id n_c - W/C + n_fold.  Chunk ids of the
+//    candidates stay ascending.
 
 constexpr int kMaxHD = 2048;
 constexpr int kAppendThreads = 1024;
 
-// RoPE of head h's pre-RoPE key (x1 = dims [0, 64), x2 = [64, 128) via xk) and
-// the value copy; threads [0, 64) rotate, [64, 80) copy 16 bytes each.
-__device__ __forceinline__ void append_store(const DecodeArgs& a, const uint16_t* v_new, int b, int h, int t,
-                                             int tid, float x1, float x2) {
+__global__ __launch_bounds__(128) void append_exact_kernel(DecodeArgs a, const uint16_t* k_new,
+                                                           const uint16_t* v_new, int t) {
+  const int b = blockIdx.x % a.batch, h = blockIdx.x / a.batch, tid = threadIdx.x;
+  const uint16_t* kp = k_new + (int64_t)b * a.n_kv * kHeadDim + h * kHeadDim;
   const int64_t row = ((int64_t)(b * a.n_kv + h) * a.max_new + t) * kHeadDim;
   if (tid < kHeadDim / 2) {
+    const float x1 = bf16_to_f32(kp[tid]), x2 = bf16_to_f32(kp[tid + kHeadDim / 2]);
     float cs, sn;
     rope_cs(a.seq_len + t, a.inv_freq[tid], &cs, &sn);
     a.key_new[row + tid] = f32_to_bf16(x1 * cs - x2 * sn);
@@ -752,30 +760,19 @@ __device__ __forceinline__ void append_store(const DecodeArgs& a, const uint16_t
   }
 }
 
-__global__ __launch_bounds__(128) void append_exact_kernel(DecodeArgs a, const uint16_t* k_new,
-                                                           const uint16_t* v_new, int t) {
-  const int b = blockIdx.x % a.batch, h = blockIdx.x / a.batch, tid = threadIdx.x;
-  const uint16_t* kp = k_new + (int64_t)b * a.n_kv * kHeadDim + h * kHeadDim;
-  const int dd = tid % (kHeadDim / 2);
-  append_store(a, v_new, b, h, t, tid, bf16_to_f32(kp[dd]), bf16_to_f32(kp[dd + kHeadDim / 2]));
-}
-
-__global__ __launch_bounds__(kAppendThreads) void append_lowrank_kernel(DecodeArgs a, const uint16_t* k_new,
-                                                                        const uint16_t* v_new, int t,
-                                                                        uint16_t* a_new) {
+__global__ __launch_bounds__(kAppendThreads) void append_project_kernel(DecodeArgs a, const uint16_t* k_new,
+                                                                        int t, uint16_t* A) {
   __shared__ float ks[kMaxHD];                  // k' of the batch element
   __shared__ float red[kAppendThreads * 8];     // per-row-group partial a'
   __shared__ float red2[kAppendThreads];        // second-level partials
-  __shared__ float ap[kMaxHD];                  // a', bf16-rounded
-  __shared__ float xs[kHeadDim];                // a' Psi^T for head h
-  const int b = blockIdx.x % a.batch, h = blockIdx.x / a.batch;
+  const int b = blockIdx.x;
   const int HD = a.n_kv * kHeadDim, r = a.rank, tid = threadIdx.x;
   const uint16_t* kp = k_new + (int64_t)b * HD;
   const uint16_t* Bt = a.Bt + (int64_t)b * HD * r;
   for (int i = tid; i < HD; i += kAppendThreads) ks[i] = bf16_to_f32(kp[i]);
   __syncthreads();
-  // a' = k' Psi: thread (row group g, column piece c) sums rows g, g + ng, ... of
-  // B_t over its 8 columns; rows past HD re-read the last row with weight 0
+  // thread (row group g, column piece c) sums rows g, g + ng, ... of B^T over its
+  // 8 columns; rows past HD re-read the last row with weight 0
   const int nch = r / 8, ng = kAppendThreads / nch;   // r <= 2048 keeps ng >= 4
   const int c = tid % nch, g = tid / nch;
   if (g < ng) {
@@ -816,41 +813,39 @@ __global__ __launch_bounds__(kAppendThreads) void append_lowrank_kernel(DecodeAr
       for (int pt = 0; pt < parts; pt++) sum += red2[pt * r + j];
     else
       for (int gg = 0; gg < ng; gg++) sum += red[gg * r + j];
-    const uint16_t q = f32_to_bf16(sum);
-    ap[j] = bf16_to_f32(q);
-    if (h == 0) a_new[((int64_t)b * a.max_new + t) * r + j] = q;
-  }
-  __syncthreads();
-  // head h's pre-RoPE key: x_dd = a' . B_t[h d + dd], eight threads per dim
-  {
-    const int dd = tid >> 3, sub = tid & 7;
-    const uint16_t* row = Bt + (int64_t)(h * kHeadDim + dd) * r;
-    float sum = 0.f;
-    for (int c8 = sub; c8 < nch; c8 += 8) {
-      float y[8];
-      unpack8(*reinterpret_cast<const u32x4*>(row + c8 * 8), y);
-#pragma unroll
-      for (int k = 0; k < 8; k++) sum = fmaf(ap[c8 * 8 + k], y[k], sum);
-    }
-    sum += __shfl_xor(sum, 1);
-    sum += __shfl_xor(sum, 2);
-    sum += __shfl_xor(sum, 4);
-    if (sub == 0) xs[dd] = sum;
-  }
-  __syncthreads();
-  if (tid < kHeadDim) {
-    const int dd = tid % (kHeadDim / 2);
-    append_store(a, v_new, b, h, t, tid, xs[dd], xs[dd + kHeadDim / 2]);
+    A[((int64_t)b * a.a_rows + a.seq_len + t) * r + j] = f32_to_bf16(sum);
   }
 }
 
 hipError_t launch_append(const DecodeArgs& a, const uint16_t* k_new, const uint16_t* v_new, int t, bool lowrank,
-                         uint16_t* a_new, hipStream_t st) {
-  if (lowrank)
-    append_lowrank_kernel<<<a.batch * a.n_kv, kAppendThreads, 0, st>>>(a, k_new, v_new, t, a_new);
-  else
-    append_exact_kernel<<<a.batch * a.n_kv, 128, 0, st>>>(a, k_new, v_new, t);
+                         hipStream_t st) {
+  append_exact_kernel<<<a.batch * a.n_kv, 128, 0, st>>>(a, k_new, v_new, t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !lowrank) return e;
+  append_project_kernel<<<a.batch, kAppendThreads, 0, st>>>(a, k_new, t, const_cast<uint16_t*>(a.A));
   return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kHeadDim) void fold_kernel(DecodeArgs a, uint16_t* L, int32_t* cand_map) {
+  const int p = blockIdx.x, dim = threadIdx.x, C = a.chunk, Wu = a.n_win_units, x = a.n_fold;
+  const uint16_t* src = x < Wu ? a.k_win + ((int64_t)p * Wu + x) * C * kHeadDim
+                               : a.key_new + ((int64_t)p * a.max_new + (int64_t)(x - Wu) * C) * kHeadDim;
+  float sum = 0.f;
+  for (int i = 0; i < C; i++) sum += bf16_to_f32(src[i * kHeadDim + dim]);
+  L[((int64_t)p * a.cand_stride + a.n_cand) * kHeadDim + dim] = f32_to_bf16(sum * (1.0f / C));
+  if (dim == 0) cand_map[(int64_t)p * a.cand_stride + a.n_cand] = a.n_c - Wu + x;
+}
+
+hipError_t launch_fold(const DecodeArgs& a, hipStream_t st) {
+  fold_kernel<<<a.batch * a.n_kv, kHeadDim, 0, st>>>(a, const_cast<uint16_t*>(a.L), const_cast<int32_t*>(a.cand_map));
+  return hipGetLastError();
+}
+
+// Values of chunk ch of pair p: context chunks from the value store, chunks of
+// appended tokens (folded into the candidates in low-rank mode) from val_new.
+__device__ __forceinline__ const uint16_t* chunk_values(const DecodeArgs& a, int p, int b, int h, int ch) {
+  if (ch < a.n_c) return a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * a.chunk) * kHeadDim;
+  return a.val_new + ((int64_t)p * a.max_new + (int64_t)(ch - a.n_c) * a.chunk) * kHeadDim;
 }
 
 // ---------------------------------------------------------------------------
@@ -872,7 +867,7 @@ __global__ __launch_bounds__(256) void value_gather_kernel(DecodeArgs a) {
     const int piece = e % per_miss;
     const int slot = a.miss_slot[(int64_t)p * K + jm];
     const int ch = a.miss_chunk[(int64_t)p * K + jm];
-    const uint16_t* src = a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * C) * kHeadDim + piece * 8;
+    const uint16_t* src = chunk_values(a, p, b, h, ch) + piece * 8;
     uint16_t* dst = a.val_slots + ((int64_t)p * K + slot) * C * kHeadDim + piece * 8;
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
   }
@@ -915,8 +910,9 @@ __device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, 
   const int O = a.n_outlier, K = a.top_k, Wu = a.n_win_units;
   if (u < O) return a.k_out + ((int64_t)p * O + u) * C * kHeadDim;
   if (u < O + K) return a.key_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim;
-  if (u < O + K + Wu) return a.k_win + ((int64_t)p * Wu + (u - O - K)) * C * kHeadDim;
-  return a.key_new + ((int64_t)p * a.max_new + (int64_t)(u - O - K - Wu) * C) * kHeadDim;
+  const int x = u - O - K + a.n_fold;
+  if (x < Wu) return a.k_win + ((int64_t)p * Wu + x) * C * kHeadDim;
+  return a.key_new + ((int64_t)p * a.max_new + (int64_t)(x - Wu) * C) * kHeadDim;
 }
 
 template <int C>
@@ -925,11 +921,10 @@ __device__ __forceinline__ const uint16_t* unit_value(const DecodeArgs& a, int p
   const int O = a.n_outlier, K = a.top_k;
   if (u < O) return a.v_out + ((int64_t)p * O + u) * C * kHeadDim;
   if (u < O + K)
-    return a.host_values ? a.val_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim
-                         : a.v_store + (((int64_t)b * a.n_kv + h) * a.seq_len + (int64_t)ch * C) * kHeadDim;
-  const int Wu = a.n_win_units;
-  if (u < O + K + Wu) return a.v_win + ((int64_t)p * Wu + (u - O - K)) * C * kHeadDim;
-  return a.val_new + ((int64_t)p * a.max_new + (int64_t)(u - O - K - Wu) * C) * kHeadDim;
+    return a.host_values ? a.val_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim : chunk_values(a, p, b, h, ch);
+  const int Wu = a.n_win_units, x = u - O - K + a.n_fold;
+  if (x < Wu) return a.v_win + ((int64_t)p * Wu + x) * C * kHeadDim;
+  return a.val_new + ((int64_t)p * a.max_new + (int64_t)(x - Wu) * C) * kHeadDim;
 }
 
 template <int G, int C>
@@ -944,13 +939,14 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;   // (row|head|ds, kq|tg)
   const int O = a.n_outlier, K = a.top_k;
-  // units: [outliers; selected slots; window; appended tokens (the last unit may
-  // be partly filled: tokens past n_new_tokens are masked like a wave's tail)]
-  const int U = O + K + a.n_win_units + a.n_new_units;
+  // units: [outliers; selected slots; exact region], the exact region being the
+  // window units and appended units not yet folded into the candidates (its
+  // last unit may be partly filled: tokens past it are masked like a wave's tail)
+  const int U = O + K + a.n_win_units + a.n_new_units - a.n_fold;
   const int per_wave = (a.upw + 3) / 4;
   const int uw0 = min(U, split * a.upw + w * per_wave);
   const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
-  const int valid = (O + K + a.n_win_units) * C + a.n_new_tokens;   // tokens in units [0, U)
+  const int valid = (O + K + a.n_win_units - a.n_fold) * C + a.n_new_tokens;   // tokens in units [0, U)
   const int ntok = max(0, min((uw1 - uw0) * C, valid - uw0 * C));
   const int hq = a.n_kv * G;
 

@@ -16,9 +16,14 @@ using namespace skv;
 
 struct skv_layer {
   skv_config cfg;
-  int G = 0, n_c = 0, n_win = 0, n_cand = 0, P = 0, HD = 0, U = 0;
+  int G = 0, n_c = 0, n_win = 0, P = 0, HD = 0, U = 0;
+  int n_cand0 = 0;                   // candidates of the pre-filled context
+  int n_cand = 0;                    // candidates now (n_cand0 + n_fold)
+  int cand_cap = 0;                  // candidate rows per pair (n_cand0 + folds possible)
   int n_new = 0;                     // generated tokens appended so far
-  int nb_score = 0, cpb = 0, ncp = 0, n_split = 0, upw = 0, res_words = 0, n_part = 0, part_size = 0;
+  int n_fold = 0;                    // appended chunks folded into the candidates (low rank)
+  int64_t a_rows = 0;                // rows of A per batch element
+  int upw = 0, res_words = 0;
   bool poisoned = false;
   bool need_reset = false;
   const uint16_t* v_dev = nullptr;   // device-visible address of the value store
@@ -26,7 +31,7 @@ struct skv_layer {
   // carved from pool
   uint16_t *A = nullptr, *Bt = nullptr, *L = nullptr, *k_out = nullptr, *v_out = nullptr,
            *k_win = nullptr, *v_win = nullptr, *key_slots = nullptr, *val_slots = nullptr,
-           *key_new = nullptr, *val_new = nullptr, *a_new = nullptr;
+           *key_new = nullptr, *val_new = nullptr;
   int32_t *cand_map = nullptr, *outlier_ids = nullptr, *slot_cand = nullptr, *slot_chunk = nullptr,
           *miss_slot = nullptr, *miss_chunk = nullptr, *miss_cand = nullptr, *free_slot = nullptr,
           *n_miss = nullptr, *hits_last = nullptr;
@@ -169,14 +174,21 @@ DecodeArgs decode_args(skv_layer* h) {
   a.n_new_tokens = h->n_new;
   a.n_new_units = (h->n_new + c.chunk - 1) / c.chunk;
   a.max_new = c.max_new_tokens;
+  a.n_fold = h->n_fold;
   a.key_new = h->key_new;
   a.val_new = h->val_new;
   a.n_cand = h->n_cand;
+  a.cand_stride = h->cand_cap;
+  a.n_c = h->n_c;
   a.seq_len = c.seq_len;
-  a.nb_score = h->nb_score;
-  a.cpb = h->cpb;
-  a.ncp = h->ncp;
-  a.n_split = (h->U + a.n_new_units + h->upw - 1) / h->upw;   // splits grow with appended tokens
+  a.a_rows = h->a_rows;
+  // score: kScoreRows landmarks per workgroup (a larger grid beats longer
+  // per-workgroup loops); logits rows padded to 16 bytes
+  a.cpb = kScoreRows;
+  a.nb_score = (h->n_cand + kScoreRows - 1) / kScoreRows;
+  a.ncp = (h->n_cand + 3) / 4 * 4;
+  // attention splits grow with the exact region (window + appended, not folded)
+  a.n_split = (h->U + a.n_new_units - h->n_fold + h->upw - 1) / h->upw;
   a.upw = h->upw;
   a.temporal = c.temporal_cache;
   a.host_values = c.value_placement == SKV_VALUES_HOST;
@@ -209,8 +221,7 @@ DecodeArgs decode_args(skv_layer* h) {
   a.logits = h->logits;
   a.lse_part = h->lse_part;
   a.keys = h->keys;
-  a.n_part = h->n_part;
-  a.part_size = h->part_size;
+  select_partition(h->n_cand, c.top_k, h->G, h->P, &a.n_part, &a.part_size);
   a.part_keys = h->part_keys;
   a.part_idx = h->part_idx;
   a.attn_part = h->attn_part;
@@ -269,19 +280,26 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   h->G = c.n_q_heads / H;
   h->n_c = (int)(S / C);
   h->n_win = c.window / C;
-  h->n_cand = h->n_c - O - h->n_win;
+  const bool lowrank = c.new_token_mode == SKV_NEW_LOWRANK;
+  h->n_cand0 = h->n_cand = h->n_c - O - h->n_win;
+  // low rank: every completed chunk of appended tokens adds one candidate
+  h->cand_cap = h->n_cand0 + (lowrank ? c.max_new_tokens / C : 0);
+  h->a_rows = S + (lowrank ? c.max_new_tokens : 0);
   h->P = b * H;
   h->HD = H * kHeadDim;
   h->U = O + K + h->n_win;
-  h->res_words = (h->n_cand + 31) / 32;
+  h->res_words = (h->cand_cap + 31) / 32;
   h->v_dev = v_dev;
-  const int P = h->P, G = h->G, n_c = h->n_c, n_cand = h->n_cand, HD = h->HD;
+  const int P = h->P, G = h->G, n_c = h->n_c, cap = h->cand_cap, HD = h->HD;
+  // scratch sized for the largest candidate count the handle can reach
+  const int nb_cap = (cap + kScoreRows - 1) / kScoreRows, ncp_cap = (cap + 3) / 4 * 4;
+  int n_part_cap = 1;
+  for (int n = h->n_cand0; n <= cap; n++) {
+    int np, ps;
+    select_partition(n, K, G, P, &np, &ps);
+    n_part_cap = std::max(n_part_cap, np);
+  }
   {
-    // score: kScoreRows landmarks (4 waves x 2 tiles x 16, a 32 KB block staged
-    // in LDS) per workgroup; a larger grid beats longer per-workgroup loops
-    h->cpb = kScoreRows;
-    h->nb_score = (n_cand + h->cpb - 1) / h->cpb;
-    h->ncp = (n_cand + 3) / 4 * 4;
     // attention: each wave owns at most attn_units_per_wave units (all loads issued
     // at once); split so that there are about 8 waves per CU
     const int nuw = attn_units_per_wave(G, C);
@@ -291,22 +309,20 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->upw = 4 * upw_wave;
     const int64_t u_max = h->U + ((int64_t)c.max_new_tokens + C - 1) / C;   // with every appended token
     if ((int64_t)h->upw * kMaxSplits < u_max) h->upw = 4 * nuw;
-    h->n_split = (h->U + h->upw - 1) / h->upw;
-    select_partition(n_cand, K, G, P, &h->n_part, &h->part_size);
   }
 
   // persistent state, one allocation
   Carver cv;
-  const size_t oA = cv.take<uint16_t>((size_t)b * S * r);
+  const size_t oA = cv.take<uint16_t>((size_t)b * h->a_rows * r);
   const size_t oBt = cv.take<uint16_t>((size_t)b * HD * r);
-  const size_t oL = cv.take<uint16_t>((size_t)P * n_cand * kHeadDim);
+  const size_t oL = cv.take<uint16_t>((size_t)P * cap * kHeadDim);
   const size_t oKo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
   const size_t oVo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
   const size_t oKw = cv.take<uint16_t>((size_t)P * c.window * kHeadDim);
   const size_t oVw = cv.take<uint16_t>((size_t)P * c.window * kHeadDim);
   const size_t oKs = cv.take<uint16_t>((size_t)P * K * C * kHeadDim);
   const size_t oVs = cv.take<uint16_t>(c.value_placement == SKV_VALUES_HOST ? (size_t)P * K * C * kHeadDim : 0);
-  const size_t oCm = cv.take<int32_t>((size_t)P * n_cand);
+  const size_t oCm = cv.take<int32_t>((size_t)P * cap);
   const size_t oOi = cv.take<int32_t>((size_t)P * O);
   const size_t oSc = cv.take<int32_t>((size_t)P * K);
   const size_t oSch = cv.take<int32_t>((size_t)P * K);
@@ -318,17 +334,16 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const size_t oHl = cv.take<int32_t>(P);
   const size_t oRes = cv.take<uint32_t>((size_t)P * h->res_words);
   const size_t oKeys = cv.take<uint32_t>((size_t)P * n_c);
-  const size_t oPk = cv.take<uint32_t>((size_t)P * h->n_part * K);
-  const size_t oPi = cv.take<int32_t>((size_t)P * h->n_part * K);
+  const size_t oPk = cv.take<uint32_t>((size_t)P * n_part_cap * K);
+  const size_t oPi = cv.take<int32_t>((size_t)P * n_part_cap * K);
   const size_t oHt = cv.take<long long>(P);
   const size_t oMt = cv.take<long long>(P);
-  const size_t oLg = cv.take<float>((size_t)P * G * h->ncp);
-  const size_t oLp = cv.take<float>((size_t)P * h->nb_score * G * 2);
+  const size_t oLg = cv.take<float>((size_t)P * G * ncp_cap);
+  const size_t oLp = cv.take<float>((size_t)P * nb_cap * G * 2);
   const int n_split_max = (h->U + (c.max_new_tokens + C - 1) / C + h->upw - 1) / h->upw;
   const size_t oAp = cv.take<float>((size_t)P * n_split_max * G * (kHeadDim + 2));
   const size_t oKn = cv.take<uint16_t>((size_t)P * c.max_new_tokens * kHeadDim);
   const size_t oVn = cv.take<uint16_t>((size_t)P * c.max_new_tokens * kHeadDim);
-  const size_t oAn = cv.take<uint16_t>(c.new_token_mode == SKV_NEW_LOWRANK ? (size_t)b * c.max_new_tokens * r : 0);
   const size_t oMc = cv.take<float>((size_t)P * n_c);
   const size_t oIf = cv.take<double>(kHeadDim / 2);
   const size_t pool_bytes = cv.off;
@@ -395,7 +410,6 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->attn_part = (float*)(base + oAp);
     h->key_new = (uint16_t*)(base + oKn);
     h->val_new = (uint16_t*)(base + oVn);
-    h->a_new = c.new_token_mode == SKV_NEW_LOWRANK ? (uint16_t*)(base + oAn) : nullptr;
     h->min_cos = (float*)(base + oMc);
     h->inv_freq = (double*)(base + oIf);
   }
@@ -409,7 +423,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   // post-RoPE keys -> landmarks and min-cos; outliers; candidates; exact caches
   HIP_TRY(launch_rope_landmark(k_pre, b, S, H, C, h->inv_freq, L_full, h->min_cos, s));
   HIP_TRY(launch_outliers(h->min_cos, P, n_c, n_c - h->n_win, O, h->keys, h->outlier_ids, s));
-  HIP_TRY(launch_candidates(L_full, h->outlier_ids, P, n_c, n_c - h->n_win, O, h->L, h->cand_map, s));
+  HIP_TRY(launch_candidates(L_full, h->outlier_ids, P, n_c, n_c - h->n_win, O, cap, h->L, h->cand_map, s));
   HIP_TRY(launch_static_gather(k_pre, v_dev, h->outlier_ids, b, S, H, C, O, c.window, h->inv_freq,
                                h->k_out, h->v_out, h->k_win, h->v_win, s));
   // low-rank factors
@@ -432,7 +446,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   }
   HIP_TRY(hipMemcpyAsync(psi_f, psi32.data(), psi32.size() * 4, hipMemcpyHostToDevice, s));
   HIP_TRY(hipMemcpyAsync(h->Bt, bt16.data(), bt16.size() * 2, hipMemcpyHostToDevice, s));
-  HIP_TRY(launch_project(k_pre, psi_f, b, S, HD, r, h->A, s));
+  HIP_TRY(launch_project(k_pre, psi_f, b, S, HD, r, h->a_rows, h->A, s));
   HIP_TRY(launch_reset_cache(decode_args(h), s));
   HIP_TRY(hipStreamSynchronize(s));
   (void)hipFree(L_full);
@@ -511,10 +525,18 @@ skv_status skv_append_token(skv_layer* h, const uint16_t* k_new, const uint16_t*
   if (!aligned(k_new, 16) || !aligned(v_new, 16)) return SKV_ERR_INVALID_ARG;
   if (h->n_new >= h->cfg.max_new_tokens) return SKV_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  DecodeArgs a = decode_args(h);
-  HIP_TRY(launch_append(a, k_new, v_new, h->n_new, h->cfg.new_token_mode == SKV_NEW_LOWRANK, h->a_new, s));
-  h->n_new++;
-  h->last_stream = s;
+  {
+    const bool lowrank = h->cfg.new_token_mode == SKV_NEW_LOWRANK;
+    HIP_TRY(launch_append(decode_args(h), k_new, v_new, h->n_new, lowrank, s));
+    h->n_new++;
+    h->last_stream = s;
+    if (lowrank && h->n_new % h->cfg.chunk == 0) {
+      // the chunk just completed pushes the oldest exact chunk into the candidates
+      HIP_TRY(launch_fold(decode_args(h), s));
+      h->n_cand++;
+      h->n_fold++;
+    }
+  }
   return SKV_OK;
 hip_fail:
   (void)hipGetLastError();
@@ -576,7 +598,9 @@ skv_status skv_export_state(const skv_layer* hc, const skv_state_host* d) {
   const int64_t S = c.seq_len;
   const int P = h->P, HD = h->HD;
   HIP_TRY(hipStreamSynchronize(h->last_stream));
-  if (d->A) HIP_TRY(hipMemcpy(d->A, h->A, (size_t)b * S * r * 2, hipMemcpyDeviceToHost));
+  if (d->A)
+    HIP_TRY(hipMemcpy2D(d->A, (size_t)S * r * 2, h->A, (size_t)h->a_rows * r * 2, (size_t)S * r * 2, b,
+                        hipMemcpyDeviceToHost));
   if (d->B) {
     std::vector<uint16_t> bt((size_t)b * HD * r);
     HIP_TRY(hipMemcpy(bt.data(), h->Bt, bt.size() * 2, hipMemcpyDeviceToHost));
@@ -587,8 +611,12 @@ skv_status skv_export_state(const skv_layer* hc, const skv_state_host* d) {
             d->B[(((size_t)bi * H + hh) * r + k) * kHeadDim + dd] =
                 bt[((size_t)bi * HD + hh * kHeadDim + dd) * r + k];
   }
-  if (d->landmarks) HIP_TRY(hipMemcpy(d->landmarks, h->L, (size_t)P * h->n_cand * kHeadDim * 2, hipMemcpyDeviceToHost));
-  if (d->cand_ids) HIP_TRY(hipMemcpy(d->cand_ids, h->cand_map, (size_t)P * h->n_cand * 4, hipMemcpyDeviceToHost));
+  if (d->landmarks)
+    HIP_TRY(hipMemcpy2D(d->landmarks, (size_t)h->n_cand0 * kHeadDim * 2, h->L, (size_t)h->cand_cap * kHeadDim * 2,
+                        (size_t)h->n_cand0 * kHeadDim * 2, P, hipMemcpyDeviceToHost));
+  if (d->cand_ids)
+    HIP_TRY(hipMemcpy2D(d->cand_ids, (size_t)h->n_cand0 * 4, h->cand_map, (size_t)h->cand_cap * 4,
+                        (size_t)h->n_cand0 * 4, P, hipMemcpyDeviceToHost));
   if (d->outlier_ids && O) HIP_TRY(hipMemcpy(d->outlier_ids, h->outlier_ids, (size_t)P * O * 4, hipMemcpyDeviceToHost));
   if (d->k_outlier && O) HIP_TRY(hipMemcpy(d->k_outlier, h->k_out, (size_t)P * O * C * kHeadDim * 2, hipMemcpyDeviceToHost));
   if (d->v_outlier && O) HIP_TRY(hipMemcpy(d->v_outlier, h->v_out, (size_t)P * O * C * kHeadDim * 2, hipMemcpyDeviceToHost));

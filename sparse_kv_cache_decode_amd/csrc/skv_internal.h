@@ -16,8 +16,12 @@ constexpr int kScoreRows = 128;          // candidate landmarks per score workgr
 // Everything a decode step touches, by value into the kernels.
 struct DecodeArgs {
   int batch, n_kv, group, chunk, top_k, n_outlier, n_win_units, n_cand;
+  int cand_stride;            // rows per pair of L and cand_map (candidate capacity)
+  int n_c;                    // chunks of the pre-filled context (S / C)
   int n_new_tokens, n_new_units, max_new;   // appended tokens, their units, capacity
+  int n_fold;                 // appended chunks folded into the candidates (low-rank mode)
   int64_t seq_len;
+  int64_t a_rows;             // rows of A per batch element (S, plus max_new in low-rank mode)
   int nb_score, cpb;          // score workgroups per pair, candidates per workgroup
   int ncp;                    // logits row stride (n_cand rounded up to 4)
   int n_split, upw;           // attention workgroups per pair, units per workgroup
@@ -26,9 +30,9 @@ struct DecodeArgs {
   const double* inv_freq;     // [64]
   // inputs / state
   const uint16_t* q;          // [b][Hq][d]
-  const uint16_t* L;          // [P][n_cand][d]
-  const int32_t* cand_map;    // [P][n_cand]
-  const uint16_t* A;          // [b][S][r]
+  const uint16_t* L;          // [P][cand_stride][d], first n_cand rows in use
+  const int32_t* cand_map;    // [P][cand_stride]
+  const uint16_t* A;          // [b][a_rows][r]
   const uint16_t* Bt;         // [b][Hkv*d][r]
   int rank;
   const uint16_t* k_out;      // [P][O*C][d]
@@ -73,7 +77,7 @@ hipError_t launch_rope_landmark(const uint16_t* k_pre, int b, int64_t S, int H, 
 hipError_t launch_outliers(const float* min_cos, int P, int n_c, int n_elig, int O,
                            uint32_t* key_scratch, int32_t* outlier_ids, hipStream_t st);
 hipError_t launch_candidates(const uint16_t* L_full, const int32_t* outlier_ids, int P, int n_c,
-                             int n_elig, int O, uint16_t* L, int32_t* cand_map, hipStream_t st);
+                             int n_elig, int O, int stride, uint16_t* L, int32_t* cand_map, hipStream_t st);
 hipError_t launch_static_gather(const uint16_t* k_pre, const uint16_t* v, const int32_t* outlier_ids,
                                 int b, int64_t S, int H, int C, int O, int W, const double* inv_freq,
                                 uint16_t* k_out, uint16_t* v_out, uint16_t* k_win, uint16_t* v_win,
@@ -83,8 +87,9 @@ hipError_t launch_gram(const uint16_t* k_pre, int b, int64_t S, int HD, int nseg
 int gram_segments(int b, int64_t S, int HD);
 hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batch, int M, int N,
                            int K, hipStream_t st);
+// A[b] rows 0..S-1 of a [b][a_rows][r] array
 hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_t S, int HD, int r,
-                          uint16_t* A, hipStream_t st);
+                          int64_t a_rows, uint16_t* A, hipStream_t st);
 
 // ---- decode launchers (decode_kernels.hip)
 hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st);
@@ -94,10 +99,14 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
 // top-K are taken by separate workgroups (stage 1), then merged per pair (stage 2).
 void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, int* part_size);
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
-// Append token t (position S + t) of every batch element; lowrank: also store
-// a' = k' Psi in a_new [b][max_new][r].
+// Append token t (position S + t) of every batch element: exact post-RoPE key
+// and value into key_new / val_new; lowrank: also its row a' = k' Psi of A.
 hipError_t launch_append(const DecodeArgs& a, const uint16_t* k_new, const uint16_t* v_new, int t, bool lowrank,
-                         uint16_t* a_new, hipStream_t st);
+                         hipStream_t st);
+// Low-rank mode, after an append that completes a chunk: the oldest exact chunk
+// (combined window/appended index a.n_fold) becomes candidate a.n_cand of every
+// pair, its landmark the bf16 mean of its stored keys.
+hipError_t launch_fold(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);
 int attn_units_per_wave(int group, int chunk);

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert skv.skv_abi_version() == 2
+    assert skv.skv_abi_version() == 3
     seen = set()
     for code in range(8):
         s = skv.skv_status_string(code)

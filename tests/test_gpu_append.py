@@ -1,11 +1,16 @@
-"""Generated tokens (skv_append_token) against the oracle: exact and low-rank
-(ShadowKV+) keys, appended between decode steps, attended after the sparse set.
+"""Generated tokens (skv_append_token) against the oracle, appended between
+decode steps.  Exact mode: every appended token is attended after the local
+window.  Low-rank mode (ShadowKV+): a token stays exact while it is in the
+window region; each completed chunk pushes the oldest exact chunk into the
+candidates, which are then scored, selected and rebuilt from A (first the
+context's window chunks, then chunks of generated tokens).
 
 Both sides start from the same bf16 context and receive the same bf16 new
 tokens; the schedules leave the last unit of appended tokens partly filled and
 make the attention split grow between steps.  Once tokens have been appended,
 every other q-head aims at one of them (the rest at the context), so that the
-generated tokens carry most of those heads' attention weight."""
+generated tokens carry most of those heads' attention weight and folded chunks
+of generated tokens are selected."""
 import numpy as np
 import pytest
 import torch
@@ -35,19 +40,25 @@ def _mixed_queries(shape, k, kn, schedule, seed):
     return q
 
 
-def _run_append(shape, mode, schedule, max_new, seed=0):
+def _run_append(shape, mode, schedule, max_new, seed=0, placement=skv.SKV_VALUES_DEVICE):
     lowrank = mode == skv.SKV_NEW_LOWRANK
     print(f"[append] {shape.name} b={shape.batch} G={shape.group} C={shape.chunk} r={shape.rank} "
-          f"mode={'lowrank' if lowrank else 'exact'} schedule={schedule} max_new={max_new}", flush=True)
+          f"W={shape.window} mode={'lowrank' if lowrank else 'exact'} schedule={schedule} "
+          f"max_new={max_new} placement={placement}", flush=True)
     n_tok = sum(schedule)
     k, v = synth.layer_cache_np(shape, 0, seed)
     kn, vn = synth.continuation_np(shape, 0, n_tok, seed)
     q = _mixed_queries(shape, k, kn, schedule, seed)
     st = O.build(O.config_from(shape), bits(k), bits(v))
-    layer = skv.Layer(shape, k.cuda(), v.cuda(), max_new_tokens=max_new, new_token_mode=mode)
+    if placement == skv.SKV_VALUES_HOST:
+        vd = torch.empty(v.shape, dtype=v.dtype, pin_memory=True)
+        vd.copy_(v)
+    else:
+        vd = v.cuda()
+    layer = skv.Layer(shape, k.cuda(), vd, placement, max_new_tokens=max_new, new_token_mode=mode)
     check_build(layer.export(), st)
     knd, vnd = kn.cuda(), vn.cuda()
-    prev = None
+    prev, prev_differ = None, False
     used = 0
     worst = (0.0, 0.0)
     for step, n in enumerate(schedule):
@@ -63,8 +74,14 @@ def _run_append(shape, mode, schedule, max_new, seed=0):
         differ = check_ids(gids, st, res)
         e = check_out(out.cpu().numpy(), reference_out(st, bits(q[step]), res, gids, differ))
         worst = (max(worst[0], e[0]), max(worst[1], e[1]))
-        prev = res.ids
-    print(f"[append] ok: {used} tokens, max|err| {worst[0]:.2e} relL2 {worst[1]:.2e}", flush=True)
+        if not differ and not prev_differ and prev is not None:
+            assert int(layer.stats()["last_hits"]) == int(res.hits.sum())
+        prev, prev_differ = res.ids, bool(differ)
+        folded_new = int(np.sum(gids >= shape.n_chunks))
+    if lowrank:
+        assert st.cand.shape[2] == shape.n_cand + used // shape.chunk
+    print(f"[append] ok: {used} tokens, max|err| {worst[0]:.2e} relL2 {worst[1]:.2e}, "
+          f"selected chunks of generated tokens at the last step: {folded_new}", flush=True)
     return layer, knd, vnd
 
 
@@ -119,4 +136,24 @@ def test_misaligned_pointers_rejected_before_any_launch():
         skv.SKV_ERR_INVALID_ARG
     assert lib.skv_append_token(layer.h, knd.data_ptr() + 2, vnd.data_ptr(), None) == skv.SKV_ERR_INVALID_ARG
     assert layer.stats()["new_tokens"] == 0 and layer.stats()["steps"] == 0
+    layer.close()
+
+
+def test_lowrank_folds_generated_chunks():
+    # W = 16, C = 8: after 44 tokens five chunks have left the exact region, the
+    # two window chunks of the context and three chunks of generated tokens,
+    # whose keys are then rebuilt from their rows of A and whose values come from
+    # the appended values
+    shape = _small(window=16)
+    layer, _, _ = _run_append(shape, skv.SKV_NEW_LOWRANK, [0, 9, 20, 15], max_new=48)
+    layer.close()
+
+
+def test_lowrank_no_window_host_values():
+    # W = 0: the exact region is the chunk being filled; values of the context in
+    # pinned host memory (gathered on the side stream), generated chunks' values
+    # from the device
+    shape = _small(window=0, batch=1, n_q_heads=8)
+    layer, _, _ = _run_append(shape, skv.SKV_NEW_LOWRANK, [4, 8, 13, 1], max_new=26,
+                              placement=skv.SKV_VALUES_HOST)
     layer.close()
