@@ -254,6 +254,10 @@ def main():
     ap.add_argument("--append", choices=["none", "exact", "lowrank"], default="none",
                     help="append one generated token per layer before every decode step "
                          "(exact keys, or ShadowKV+ low-rank states)")
+    ap.add_argument("--graph", choices=["on", "off"], default="off",
+                    help="replay each timed step (all layers) as one captured HIP graph; off: launch eagerly")
+    ap.add_argument("--phase-steps", type=int, default=16,
+                    help="eager steps after the timed region that record per-phase events on sampled layers")
     ap.add_argument("--phase-every", type=int, default=16,
                     help="record per-phase HIP events on every n-th layer of the timed region "
                          "(an event record between kernels costs a few microseconds)")
@@ -293,7 +297,8 @@ def main():
     if args.layers:
         shape = shape.replace(layers=args.layers)
     L, W, K = shape.layers, args.warmup, args.steps
-    total = W + K
+    PH = max(1, args.phase_steps)
+    total = W + K + PH            # warm-up, timed and phase-timing steps
     dev = torch.device("cuda")
     torch.cuda.init()
     skv.lib()
@@ -320,47 +325,68 @@ def main():
         del k_pre, v
         if l % 4 == 3 or l == L - 1:
             log(f"built layer {l + 1}/{L} ({time.time() - t0:.1f}s)")
+    # queries step-major, so that one step's queries of every layer are one block
+    qall = torch.stack([torch.stack([qs[l][t] for l in range(L)]) for t in range(total)])
+    del qs
     torch.cuda.synchronize()
     out = torch.empty((shape.batch, shape.n_q_heads, shape.head_dim), dtype=torch.float32, device=dev)
     ids = torch.empty((shape.batch, shape.n_kv_heads, shape.top_k), dtype=torch.int32, device=dev)
+    qbuf = torch.empty_like(qall[0])
     stream = torch.cuda.current_stream()
 
-    def step(t):
+    def step_layers(q, t, st):
         for l in range(L):
             if news:
-                layers[l].append(news[l][0][t], news[l][1][t], stream)
-            layers[l].decode(qs[l][t], out, ids, stream)
+                layers[l].append(news[l][0][t], news[l][1][t], st)
+            layers[l].decode(q[l], out, ids, st)
 
     for t in range(W):
-        step(t)
+        step_layers(qall[t], t, stream)
     torch.cuda.synchronize()
+    graph = None
+    if args.graph == "on" and not news:
+        # the step reads its queries from qbuf; capture launches nothing
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_layers(qbuf, 0, None)
+        torch.cuda.synchronize()
     before = [ly.stats() for ly in layers]
-    sampled = list(range(0, L, max(1, args.phase_every)))
-    for l in sampled:
-        skv.skv_set_timing(layers[l].h, K)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
     for t in range(W, W + K):
-        step(t)
+        if graph is not None:
+            qbuf.copy_(qall[t])
+            graph.replay()
+        else:
+            step_layers(qall[t], t, stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
-    log(f"timed {K} steps x {L} layers: {ms_total:.2f} ms")
-
+    log(f"timed {K} steps x {L} layers: {ms_total:.2f} ms ({'graph replay' if graph else 'eager launches'})")
     after = [ly.stats() for ly in layers]
+
+    # per-phase device timing: eager steps after the timed region, events on the
+    # sampled layers (which then run their phases back to back, as one pair group)
+    sampled = list(range(0, L, max(1, args.phase_every)))
+    for l in sampled:
+        skv.skv_set_timing(layers[l].h, PH)
+    for t in range(W + K, total):
+        step_layers(qall[t], t, stream)
+    torch.cuda.synchronize()
     phase_ms = {p: 0.0 for p in skv.PHASES}
     for l in sampled:
         ph, n = skv.skv_get_timing(layers[l].h)
-        assert n == K
+        assert n == PH
         for p in ph:
             phase_ms[p] += ph[p]
     launches = K * L
-    phase_avg_us = {p: 1000.0 * phase_ms[p] / (K * len(sampled)) for p in phase_ms}
+    phase_avg_us = {p: 1000.0 * phase_ms[p] / (PH * len(sampled)) for p in phase_ms}
     misses = sum(a["total_misses"] - b["total_misses"] for a, b in zip(after, before)) / launches
     hits = sum(a["total_hits"] - b["total_hits"] for a, b in zip(after, before)) / launches
     alpha_timed = hits / (shape.pairs * shape.top_k)
-    alpha_all = sum(a["mean_alpha"] for a in after) / L
+    # hits over steps 1.. of the warm-up and timed steps (device counters)
+    alpha_all = sum(a["total_hits"] for a in after) / (L * shape.pairs * shape.top_k * (W + K - 1))
     by = algorithmic_bytes(shape, misses)
 
     ms_per_step = ms_total / K
@@ -438,7 +464,9 @@ def main():
                           "achieved_GBps": round(step_gbps, 1),
                           "frac": round(step_gbps / HBM_PEAK_GBPS, 4)},
         "phase_us_per_layer": {p: round(v, 2) for p, v in phase_avg_us.items()},
-        "phase_timing": f"HIP events around each phase on the decode stream, layers {sampled} of every timed step",
+        "phase_timing": f"HIP events around each phase on the decode stream, layers {sampled}, {PH} eager steps "
+                        f"after the timed region",
+        "launch": "one captured HIP graph per step (all layers), replayed" if graph is not None else "eager launches",
         "layer_us": round(layer_us, 2),
         "alpha": {"timed_steps": round(alpha_timed, 4), "steps_1_to_end": round(alpha_all, 4),
                   "misses_per_layer_step": round(misses, 1)},

@@ -588,11 +588,14 @@ __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   __shared__ u32x4 stage[kStageBytes / 16];
   __shared__ int mchunk[MPB], mslot[MPB];
   const int P = a.batch * a.n_kv;
-  // Tile-major order: workgroup L serves tile L / P of pair L % P, so the tiles
-  // that exist for every pair are dispatched first.  Workgroups go to the 8 XCDs
-  // round-robin by linear id; with P a multiple of 8 all tiles of a pair run on
-  // XCD p % 8 and share one L2 copy of the pair's B^T.
-  const int p = blockIdx.x % P, j0 = (blockIdx.x / P) * MPB;
+  // Workgroup L serves pair L % P and tile T - 1 - L / P of its T tiles:
+  // a pair's misses form a prefix of its list, so the empty tiles (all of them
+  // past the misses) are dispatched first and leave at once, and the tiles with
+  // work start right after them instead of waiting behind them for a slot.
+  // Workgroups go to the 8 XCDs round-robin by linear id; with P a multiple of 8
+  // all tiles of a pair run on one XCD and share one L2 copy of the pair's B^T.
+  const int n_tiles = (a.top_k + MPB - 1) / MPB;
+  const int p = blockIdx.x % P, j0 = (n_tiles - 1 - (int)(blockIdx.x / P)) * MPB;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int K = a.top_k, r = a.rank;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -934,7 +937,10 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   __shared__ float cbuf[4][16];                                     // [wave][head] rescale
   __shared__ float wo[4][G][kHeadDim];
   __shared__ float wm[4][G], wl[4][G];
-  const int p = blockIdx.y, split = blockIdx.x;
+  // pairs fastest: workgroups go to the 8 XCDs round-robin by linear id, so each
+  // XCD gets whole pairs (all splits of pairs p = x mod 8) and equal work even
+  // when the last split of a pair is short
+  const int p = blockIdx.x, split = blockIdx.y;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;   // (row|head|ds, kq|tg)
@@ -1136,7 +1142,7 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
 
 template <int G>
 static hipError_t launch_attn_g(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.n_split, a.batch * a.n_kv);
+  dim3 grid(a.batch * a.n_kv, a.n_split);
   switch (a.chunk) {
     case 4: attn_kernel<G, 4><<<grid, 256, 0, st>>>(a); break;
     case 8: attn_kernel<G, 8><<<grid, 256, 0, st>>>(a); break;

@@ -7,12 +7,48 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "skv_internal.h"
 
 using namespace skv;
+
+namespace {
+
+// The side stream the handles of one device share for the host-value gather
+// (default priority, created once and kept until the process ends), so that the
+// number of streams, and of hardware queues in use, stays fixed however many
+// layers are built.
+struct DeviceStreams {
+  hipStream_t side = nullptr;
+};
+
+std::mutex g_streams_mu;
+std::vector<DeviceStreams*> g_streams;   // by device ordinal
+
+hipError_t device_streams(DeviceStreams** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_streams_mu);
+  if ((int)g_streams.size() <= dev) g_streams.resize(dev + 1, nullptr);
+  if (!g_streams[dev]) {
+    DeviceStreams* ds = new (std::nothrow) DeviceStreams();
+    if (!ds) return hipErrorOutOfMemory;
+    e = hipStreamCreateWithFlags(&ds->side, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      delete ds;
+      return e;
+    }
+    g_streams[dev] = ds;
+  }
+  *out = g_streams[dev];
+  return hipSuccess;
+}
+
+}  // namespace
 
 struct skv_layer {
   skv_config cfg;
@@ -41,7 +77,7 @@ struct skv_layer {
   float *logits = nullptr, *lse_part = nullptr, *attn_part = nullptr, *min_cos = nullptr;
   double* inv_freq = nullptr;
   std::vector<double> eig;
-  hipStream_t side = nullptr;
+  hipStream_t side = nullptr;        // the device's shared side stream: host-value gather
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipStream_t last_stream = nullptr;
   int64_t steps = 0;
@@ -154,9 +190,9 @@ void release(skv_layer* h) {
   if (!h) return;
   drop_timing(h);
   if (h->pool) (void)hipFree(h->pool);
-  if (h->side) (void)hipStreamDestroy(h->side);
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+
   delete h;
 }
 
@@ -415,7 +451,11 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   }
   for (int i = 0; i < kHeadDim / 2; i++) invf[i] = std::pow(c.rope_theta, -2.0 * i / kHeadDim);
 
-  HIP_TRY(hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking));
+  {
+    DeviceStreams* ds = nullptr;
+    HIP_TRY(device_streams(&ds));
+    h->side = ds->side;
+  }
   HIP_TRY(hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming));
   HIP_TRY(hipMemsetAsync(h->pool, 0, pool_bytes, s));

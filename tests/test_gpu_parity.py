@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(shape, steps, placement=skv.SKV_VALUES_DEVICE, temporal=1, seed=0, mode="drift",
-         check_state=True):
+         check_state=True, keep=False):
     print(f"[parity] {shape.name} b={shape.batch} S={shape.seq_len} G={shape.group} "
           f"C={shape.chunk} K={shape.top_k} O={shape.n_outlier} r={shape.rank} "
           f"placement={placement} temporal={temporal} steps={steps}", flush=True)
@@ -53,7 +53,8 @@ def _run(shape, steps, placement=skv.SKV_VALUES_DEVICE, temporal=1, seed=0, mode
         prev, prev_gpu, prev_differ = res.ids, gids, bool(differ)
     print(f"[parity] ok: max|err| {worst[0]:.2e} relL2 {worst[1]:.2e} alpha {layer.stats()['mean_alpha']:.3f}"
           f" near-tie swaps {swaps}", flush=True)
-    layer.close()
+    if not keep:
+        layer.close()
     return layer
 
 
@@ -141,3 +142,4 @@ def test_split_selection_group_of_eight():
                top_k=136, n_outlier=26)
     assert s.group * s.n_cand > 65536
     _run(s, steps=2)
+
