@@ -174,7 +174,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> str:
     lines = ["# HBM traffic per kernel launch: ShadowKV decode, Llama-3.1-8B shape (122 880 tokens, batch 8)",
              "", "Commands (repo root on the GPU box, `export TMPDIR=/tmp` first):", "", "```"]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        lines.append(f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc_{c.lower()} -o pmc -- {command}")
+        lines.append(f"rocprofv3 --pmc {c} --output-format csv -d /tmp/pmc_{c.lower()} -o pmc -- {command}")
     lines += ["```", "",
               f"Scaling: the calibration kernel (`{calib}`, the run's last three dispatches) reads and "
               f"writes {CALIB_BYTES} bytes; FETCH_SIZE reads {cf:.0f} KiB and WRITE_SIZE {cw:.0f} KiB for it, "
@@ -187,6 +187,37 @@ def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> str:
     lines += ["", "Read back by bench.py (used only while the native sources hash to the digest):", "",
               "```json", json.dumps(blob, indent=1), "```", ""]
     return "\n".join(lines)
+
+
+def summarize_trace(stats_csv: str, command: str) -> str:
+    """Markdown table of the library's kernels from a rocprofv3 kernel_stats.csv,
+    with the score kernel's rate at its algorithmic bytes per launch."""
+    rows = []
+    with open(stats_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            name = _short_kernel_name(row["Name"])
+            if name.startswith("skv::"):
+                rows.append((name, int(row["Calls"]), float(row["AverageNs"]) / 1e3, float(row["MinNs"]) / 1e3,
+                             float(row["MaxNs"]) / 1e3, float(row["TotalDurationNs"]) / 1e6))
+    rows.sort(key=lambda r: -r[5])
+    lines = ["# Kernel timing: ShadowKV decode, Llama-3.1-8B shape (122 880 tokens, batch 8, 32 layers)", "",
+             "Command (repo root on the GPU box, `export TMPDIR=/tmp` first):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/prof_bench -o bench -- {command}",
+             "```", "",
+             "Per-kernel summary from `bench_kernel_stats.csv` (library kernels only). The build kernels run "
+             "once per layer; the decode kernels once per layer and step (warm-up, timed and phase-timing steps).",
+             "", "| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    for n, c, a, lo, hi, t in rows:
+        lines.append(f"| `{n}` | {c} | {a:.2f} | {lo:.2f} | {hi:.2f} | {t:.1f} |")
+    score = [r for r in rows if r[0] == SCORE_KERNEL]
+    if score:
+        from sparse_kv_cache_decode_amd import synth
+        shape = synth.SHAPES["llama3_8b_122k"]
+        by = algorithmic_bytes(shape, 0.0)["score"]
+        lines += ["", f"Score kernel: {by} algorithmic bytes per launch / {score[0][2]:.2f} us average = "
+                      f"{by / (score[0][2] * 1e-6) / 1e9:.0f} GB/s ({by / (score[0][2] * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} "
+                      f"of {HBM_PEAK_GBPS / 1000:.0f} TB/s)."]
+    return "\n".join(lines) + "\n"
 
 
 def measured_traffic(workload: str, kernel: str):
@@ -259,7 +290,7 @@ def main():
     ap.add_argument("--phase-steps", type=int, default=16,
                     help="eager steps after the timed region that record per-phase events on sampled layers")
     ap.add_argument("--phase-every", type=int, default=16,
-                    help="record per-phase HIP events on every n-th layer of the timed region "
+                    help="record per-phase HIP events on every n-th layer during the phase-timing steps "
                          "(an event record between kernels costs a few microseconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -267,11 +298,16 @@ def main():
                     help="after the timed region, run a known-size streaming kernel for counter scaling")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="print the traffic summary of two rocprofv3 --pmc runs (no GPU needed)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"),
+                    help="print the per-kernel summary of a rocprofv3 --kernel-trace --stats run (no GPU needed)")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
 
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters))
+        return 0
+    if args.summarize_trace:
+        print(summarize_trace(*args.summarize_trace))
         return 0
 
     if args.cpu_baseline_child:
@@ -279,7 +315,7 @@ def main():
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode step shards by batch element with no communication; see the design notes)",
+              "(the decode step shards by batch element with no communication)",
               file=sys.stderr)
         return 2
 

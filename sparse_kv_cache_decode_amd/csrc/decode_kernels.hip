@@ -580,22 +580,22 @@ __device__ __forceinline__ void mfma_steps(const u32x4 (&af)[NSTEP][2], int kn, 
   if constexpr (Q + 1 < NSTEP) mfma_steps<NSTEP, Q + 1>(af, kn, lk, baddr, acc);
 }
 
+// Staging buffer of one rebuild tile: B^T pieces of NSTEP k-steps, later the
+// tile's bf16 output rows.
+template <int NSTEP>
+constexpr int rebuild_stage_bytes() {
+  return NSTEP * kStepPieces * 16 > kRebuildRows * kOutW * 2 ? NSTEP * kStepPieces * 16 : kRebuildRows * kOutW * 2;
+}
+
+// One tile of kRebuildRows rows of pair p: the keys of the missed chunks
+// mchunk[0, 128/C) (-1: none), rotated, stored as bf16 into their slots mslot[].
+// Called by all 256 threads of a workgroup with mchunk / mslot in LDS (written
+// before a barrier) and `stage` an LDS buffer of rebuild_stage_bytes<NSTEP>().
+// Returns once the stores are issued; the caller orders them against later
+// readers.
 template <int C, int NSTEP>
-__global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
-  constexpr int MPB = kRebuildRows / C;
-  constexpr int kStageBytes = NSTEP * kStepPieces * 16 > kRebuildRows * kOutW * 2
-                                  ? NSTEP * kStepPieces * 16 : kRebuildRows * kOutW * 2;
-  __shared__ u32x4 stage[kStageBytes / 16];
-  __shared__ int mchunk[MPB], mslot[MPB];
-  const int P = a.batch * a.n_kv;
-  // Workgroup L serves pair L % P and tile T - 1 - L / P of its T tiles:
-  // a pair's misses form a prefix of its list, so the empty tiles (all of them
-  // past the misses) are dispatched first and leave at once, and the tiles with
-  // work start right after them instead of waiting behind them for a slot.
-  // Workgroups go to the 8 XCDs round-robin by linear id; with P a multiple of 8
-  // all tiles of a pair run on one XCD and share one L2 copy of the pair's B^T.
-  const int n_tiles = (a.top_k + MPB - 1) / MPB;
-  const int p = blockIdx.x % P, j0 = (n_tiles - 1 - (int)(blockIdx.x / P)) * MPB;
+__device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const int* mchunk, const int* mslot,
+                                             u32x4* stage) {
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int K = a.top_k, r = a.rank;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -603,13 +603,6 @@ __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   double ffreq[4];
 #pragma unroll
   for (int nt = 0; nt < 4; nt++) ffreq[nt] = a.inv_freq[nt * 16 + lr];
-  for (int i = threadIdx.x; i < MPB; i += 256) {
-    const bool ok = j0 + i < K;
-    mchunk[i] = ok ? a.miss_chunk[(int64_t)p * K + j0 + i] : -1;
-    mslot[i] = ok ? a.miss_slot[(int64_t)p * K + j0 + i] : -1;
-  }
-  __syncthreads();
-  if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
   const uint16_t* Bt = a.Bt + ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
   const uint16_t* Ab = a.A + (int64_t)b * a.a_rows * r;
   // A operand rows of this lane: row m = w*32 + mt*16 + lr (rows past the misses
@@ -697,6 +690,31 @@ __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
     uint16_t* dst = a.key_slots + (((int64_t)p * K + slot) * C + (m % C)) * kHeadDim + piece * 8;
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&otile[m * kOutW + piece * 8]);
   }
+}
+
+template <int C, int NSTEP>
+__global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
+  constexpr int MPB = kRebuildRows / C;
+  __shared__ u32x4 stage[rebuild_stage_bytes<NSTEP>() / 16];
+  __shared__ int mchunk[MPB], mslot[MPB];
+  const int P = a.batch * a.n_kv;
+  // Workgroup L serves pair L % P and tile T - 1 - L / P of its T tiles:
+  // a pair's misses form a prefix of its list, so the empty tiles (all of them
+  // past the misses) are dispatched first and leave at once, and the tiles with
+  // work start right after them instead of waiting behind them for a slot.
+  // Workgroups go to the 8 XCDs round-robin by linear id; with P a multiple of 8
+  // all tiles of a pair run on one XCD and share one L2 copy of the pair's B^T.
+  const int n_tiles = (a.top_k + MPB - 1) / MPB;
+  const int p = blockIdx.x % P, j0 = (n_tiles - 1 - (int)(blockIdx.x / P)) * MPB;
+  const int K = a.top_k;
+  for (int i = threadIdx.x; i < MPB; i += 256) {
+    const bool ok = j0 + i < K;
+    mchunk[i] = ok ? a.miss_chunk[(int64_t)p * K + j0 + i] : -1;
+    mslot[i] = ok ? a.miss_slot[(int64_t)p * K + j0 + i] : -1;
+  }
+  __syncthreads();
+  if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
+  rebuild_tile<C, NSTEP>(a, p, mchunk, mslot, stage);
 }
 
 template <int C>
@@ -955,6 +973,7 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   const int valid = (O + K + a.n_win_units - a.n_fold) * C + a.n_new_tokens;   // tokens in units [0, U)
   const int ntok = max(0, min((uw1 - uw0) * C, valid - uw0 * C));
   const int hq = a.n_kv * G;
+
 
   // chunk id of each selected unit of the wave, one per lane
   int my_ch = 0;
