@@ -191,12 +191,12 @@ __device__ __forceinline__ bool sorted_contains(const int* v, int n, int x) {
 void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, int* part_size) {
   // One workgroup per pair while its logits are at most 256 KB (one CU pulls that
   // in about as fast as a second kernel launch would cost).  Beyond, about one
-  // stage-1 workgroup per CU, parts at least 4K long (a part's top-K is at most a
-  // quarter of it), at most 16K per part (register keys) and a merged length of
-  // at most 16384.
+  // stage-1 workgroup per CU, parts at least 2K long (a part's top-K keeps at most
+  // half of it) and at most 16K (register keys); the part lists are then merged
+  // in a tree (merge_groups).
   int np = 1;
   if ((int64_t)group * n_cand > 65536 || n_cand > kSelThreads * 16) {
-    np = std::min({(256 + pairs - 1) / pairs, n_cand / (4 * top_k), 16384 / top_k, 64});
+    np = std::min({(256 + pairs - 1) / pairs, n_cand / (2 * top_k), 64});
     np = std::max({np, 2, (n_cand + kSelThreads * 16 - 1) / (kSelThreads * 16)});
   }
   const int ps = np == 1 ? n_cand : ((n_cand + np - 1) / np + 15) / 16 * 16;   // 16-B aligned parts
@@ -207,29 +207,44 @@ void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, 
 // keys per thread of the register-resident selection for n candidates
 static int keys_per_thread(int n) { return n <= kSelThreads * 4 ? 4 : (n <= kSelThreads * 8 ? 8 : 16); }
 
-static int merged_len(const DecodeArgs& a) {
-  const int kp0 = std::min(a.top_k, a.part_size);
-  const int kpl = std::min(a.top_k, a.n_cand - (a.n_part - 1) * a.part_size);
-  return (a.n_part - 1) * kp0 + kpl;
+// Lists merged by one workgroup of the merge tree: their entries (at most K each)
+// fit 16 per thread in registers.
+int merge_groups(int top_k) { return std::max(2, kSelThreads * 16 / top_k); }
+
+static size_t select_lds_bytes(const DecodeArgs& a) {
+  return (size_t)(kHist + 32 + 5 * a.top_k + a.res_words) * sizeof(int);
 }
 
-static size_t select_lds_bytes(const DecodeArgs& a, bool merged_in_lds) {
-  return (size_t)(kHist + 32 + 5 * a.top_k + a.res_words + (merged_in_lds ? 2 * merged_len(a) : 0)) *
-         sizeof(int);
-}
-
-// LSE_g of the pair's G heads from the score workgroups' partials, by waves 0..G-1.
+// LSE_g of the pair's G heads from the score workgroups' (max, sum) partials, by
+// waves 0..G-1: one pass, each lane folding its blocks into a running (max, sum)
+// with four independent 8-byte loads in flight, then a butterfly over the wave.
 template <int G>
 __device__ __forceinline__ void pair_lse(const DecodeArgs& a, int p, float* lse) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (w < G) {
     const float* src = a.lse_part + (int64_t)p * a.nb_score * G * 2;
-    float M = kNegBig;
-    for (int k = lane; k < a.nb_score; k += 64) M = fmaxf(M, src[(k * G + w) * 2]);
-    M = wave_max(M);
-    float S = 0.f;
-    for (int k = lane; k < a.nb_score; k += 64) S += src[(k * G + w) * 2 + 1] * __expf(src[(k * G + w) * 2] - M);
-    S = wave_sum(S);
+    float M = kNegBig, S = 0.f;
+    for (int k0 = lane; k0 < a.nb_score; k0 += 4 * 64) {
+      float2 ms[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int k = k0 + u * 64;
+        ms[u] = k < a.nb_score ? *reinterpret_cast<const float2*>(src + (k * G + w) * 2) : make_float2(kNegBig, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const float Mn = fmaxf(M, ms[u].x);
+        S = S * __expf(M - Mn) + ms[u].y * __expf(ms[u].x - Mn);
+        M = Mn;
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float Mo = __shfl_xor(M, o), So = __shfl_xor(S, o);
+      const float Mn = fmaxf(M, Mo);
+      S = S * __expf(M - Mn) + So * __expf(Mo - Mn);
+      M = Mn;
+    }
     if (lane == 0) lse[w] = M + __logf(S);
   }
 }
@@ -309,8 +324,9 @@ __device__ __forceinline__ int reg_keys(const DecodeArgs& a, int p, int c0, int 
   const int nv = max(0, min(PT, n - i0));
   const int cb = c0 + i0;                        // a multiple of 4: 16-byte aligned rows
   const float* lg = a.logits + (int64_t)p * G * a.ncp + cb;
-  // all heads at once when their logits fit in 64 registers, else 32 at a time
-  constexpr int GB = G * PT <= 64 ? G : (32 / PT < 1 ? 1 : 32 / PT);
+  // all heads at once when their logits fit in 64 registers, else groups of 64
+  // logits (32 at 16 keys per thread, which hold more registers themselves)
+  constexpr int GB = G * PT <= 64 ? G : (PT <= 8 ? 64 : 32) / PT;
   f32x4 lv[GB][PT / 4];
   auto load_heads = [&](int g0) {
 #pragma unroll
@@ -407,9 +423,90 @@ __global__ __launch_bounds__(kSelThreads) void part_topk_kernel(DecodeArgs a) {
   });
 }
 
-template <bool IN_LDS>
-__global__ __launch_bounds__(kSelThreads) void merged_select_kernel(DecodeArgs a) {
+// Lists of (key, candidate index) per pair, each in ascending candidate order and
+// covering consecutive candidate ranges in list order: list j of pair p starts at
+// element p * pair_stride + j * K; every list but the last holds len0 entries, all
+// lists of a pair m entries.  Entry i of a pair is entry i % len0 of list i / len0.
+struct ListSet {
+  const uint32_t* keys;
+  const int32_t* idx;
+  int64_t pair_stride;
+  int len0, n_lists, m;
+};
+
+// Entries [e0, e0 + n) of pair p's lists, thread t holding [e0 + t*PT, e0 + t*PT + PT)
+// in registers (n <= kSelThreads * PT; entries past n re-read entry n - 1 and are
+// not counted), with the thread's key range; returns the thread's count.
+template <int PT>
+__device__ __forceinline__ int load_entries(const ListSet& ls, int K, int p, int e0, int n, uint32_t (&key)[PT],
+                                            int (&idx)[PT], uint32_t& lo, uint32_t& hi) {
+  const int i0 = threadIdx.x * PT, nv = max(0, min(PT, n - i0));
+  const uint32_t* gk = ls.keys + (int64_t)p * ls.pair_stride;
+  const int32_t* gi = ls.idx + (int64_t)p * ls.pair_stride;
+  if (ls.len0 % PT == 0 && K % 4 == 0 && e0 % PT == 0 && nv == PT) {
+    // the PT entries lie in one list, 16-byte aligned: PT / 4 loads of each
+    const int i = e0 + i0, off = (i / ls.len0) * K + i % ls.len0;
+#pragma unroll
+    for (int j = 0; j < PT / 4; j++) {
+      const u32x4 kw = *reinterpret_cast<const u32x4*>(gk + off + 4 * j);
+      const u32x4 iw = *reinterpret_cast<const u32x4*>(gi + off + 4 * j);
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        key[4 * j + c] = kw[c];
+        idx[4 * j + c] = (int)iw[c];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PT; e++) {
+      const int i = e0 + min(i0 + e, n - 1);
+      const int off = (i / ls.len0) * K + i % ls.len0;
+      key[e] = gk[off];
+      idx[e] = gi[off];
+    }
+  }
+  lo = 0xffffffffu;
+  hi = 0u;
+#pragma unroll
+  for (int e = 0; e < PT; e++) {
+    if (e < nv) {
+      lo = min(lo, key[e]);
+      hi = max(hi, key[e]);
+    }
+  }
+  return nv;
+}
+
+// One level of the merge tree: workgroup (gi, p) takes lists [gi*grp, gi*grp + grp)
+// of pair p and writes their top-K (in ascending candidate order, so ties still
+// go to the lower candidate) as list gi of `out` (pair stride out_stride).  The
+// pair's top-K is contained in the union of the groups' top-K.
+__global__ __launch_bounds__(kSelThreads) void merge_level_kernel(DecodeArgs a, ListSet ls, int grp,
+                                                                  uint32_t* out_keys, int32_t* out_idx,
+                                                                  int64_t out_stride) {
+  __shared__ int hist[kHist];
+  __shared__ int sh[32];
+  constexpr int PT = 16;
+  const int gi = blockIdx.x, p = blockIdx.y, K = a.top_k;
+  const int e0 = gi * grp * ls.len0, n = min(ls.m - e0, grp * ls.len0);
+  uint32_t key[PT], lo, hi;
+  int idx[PT];
+  const int nv = load_entries<PT>(ls, K, p, e0, n, key, idx, lo, hi);
+  for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
+  block_range<kSelThreads>(lo, hi, sh);   // its barriers also publish the cleared histogram
+  uint32_t* ok = out_keys + (int64_t)p * out_stride + (int64_t)gi * K;
+  int32_t* oi = out_idx + (int64_t)p * out_stride + (int64_t)gi * K;
+  block_topk_reg<kSelThreads, PT>(key, nv, min(K, n), lo, hi, hist, sh, true, [&](int pos, int e) {
+    ok[pos] = key[e];
+    oi[pos] = idx[e];
+  });
+}
+
+// Last level: the top-K of all of pair p's lists (at most kSelThreads * 16 entries,
+// in registers), then the temporal-cache index scan.
+__global__ __launch_bounds__(kSelThreads) void merged_select_kernel(DecodeArgs a, ListSet ls) {
   extern __shared__ int smem[];
+  constexpr int PT = 16;
   const int K = a.top_k, RW = a.res_words;
   int* hist = smem;
   int* sh = smem + kHist;
@@ -420,33 +517,16 @@ __global__ __launch_bounds__(kSelThreads) void merged_select_kernel(DecodeArgs a
   int* scl = missp + K;
   uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);
   const int p = blockIdx.x;
+  uint32_t key[PT], lo, hi;
+  int idx[PT];
+  const int nv = load_entries<PT>(ls, K, p, 0, ls.m, key, idx, lo, hi);
   const int32_t* sc = a.slot_cand + (int64_t)p * K;
   const uint32_t* res = a.resident + (int64_t)p * RW;
   for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
   for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
-  // merged part lists: part j contributes min(K, its length) entries; every part
-  // but the last has the full length, so entry i is (i / kp0, i % kp0)
-  const int kp0 = min(K, a.part_size);
-  const int m = (a.n_part - 1) * kp0 + min(K, a.n_cand - (a.n_part - 1) * a.part_size);
-  const uint32_t* gk = a.part_keys + (int64_t)p * a.n_part * K;
-  const int32_t* gi = a.part_idx + (int64_t)p * a.n_part * K;
-  uint32_t* mkeys = resl + RW;
-  int* midx = reinterpret_cast<int*>(mkeys + m);
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int i = threadIdx.x; i < m; i += kSelThreads) {
-    const int off = (i / kp0) * K + i % kp0;
-    const uint32_t key = gk[off];
-    if (IN_LDS) {
-      mkeys[i] = key;
-      midx[i] = gi[off];
-    }
-    lo = min(lo, key);
-    hi = max(hi, key);
-  }
-  block_range<kSelThreads>(lo, hi, sh);
-  block_topk<kSelThreads>(
-      [&](int i) { return IN_LDS ? mkeys[i] : gk[(i / kp0) * K + i % kp0]; }, m, K, lo, hi, hist, sh,
-      [&](int pos, int i) { sel[pos] = IN_LDS ? midx[i] : gi[(i / kp0) * K + i % kp0]; });
+  for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
+  block_range<kSelThreads>(lo, hi, sh);   // its barriers also publish the cleared histogram
+  block_topk_reg<kSelThreads, PT>(key, nv, K, lo, hi, hist, sh, true, [&](int pos, int e) { sel[pos] = idx[e]; });
   index_scan(a, p, sh, sel, selch, freel, missp, scl, resl);
 }
 
@@ -458,25 +538,40 @@ static hipError_t allow_lds(F* kernel) {
 
 template <int G, int PT>
 static hipError_t launch_select_pt(const DecodeArgs& a, hipStream_t st) {
-  const int P = a.batch * a.n_kv;
+  const int P = a.batch * a.n_kv, K = a.top_k;
   static bool attr = false;
   if (!attr) {
     hipError_t e = allow_lds(&select_kernel<G, PT>);
-    if (e == hipSuccess) e = allow_lds(&merged_select_kernel<true>);
-    if (e == hipSuccess) e = allow_lds(&merged_select_kernel<false>);
+    if (e == hipSuccess) e = allow_lds(&merged_select_kernel);
     if (e != hipSuccess) return e;
     attr = true;
   }
   if (a.n_part == 1) {
-    select_kernel<G, PT><<<P, kSelThreads, select_lds_bytes(a, false), st>>>(a);
+    select_kernel<G, PT><<<P, kSelThreads, select_lds_bytes(a), st>>>(a);
     return hipGetLastError();
   }
   part_topk_kernel<G, PT><<<dim3(a.n_part, P), kSelThreads, (kHist + 32) * sizeof(int), st>>>(a);
-  const bool in_lds = select_lds_bytes(a, true) <= (size_t)kSelLdsMax;
-  if (in_lds)
-    merged_select_kernel<true><<<P, kSelThreads, select_lds_bytes(a, true), st>>>(a);
-  else
-    merged_select_kernel<false><<<P, kSelThreads, select_lds_bytes(a, false), st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // merge tree: the part lists, then each level's lists alternately in the merge
+  // buffers and back in the part buffers, until one workgroup holds them all
+  const int len0 = std::min(K, a.part_size);
+  ListSet ls{a.part_keys, a.part_idx, (int64_t)a.n_part * K, len0, a.n_part,
+             (a.n_part - 1) * len0 + std::min(K, a.n_cand - (a.n_part - 1) * a.part_size)};
+  const int grp = merge_groups(K);
+  bool to_merge = true;
+  while (ls.n_lists > grp) {
+    const int n_out = (ls.n_lists + grp - 1) / grp;
+    uint32_t* ok = to_merge ? a.merge_keys : a.part_keys;
+    int32_t* oi = to_merge ? a.merge_idx : a.part_idx;
+    const int64_t out_stride = (int64_t)n_out * K;
+    merge_level_kernel<<<dim3(n_out, P), kSelThreads, 0, st>>>(a, ls, grp, ok, oi, out_stride);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int last = ls.m - (n_out - 1) * grp * ls.len0;   // entries of the last group
+    ls = ListSet{ok, oi, out_stride, K, n_out, (n_out - 1) * K + std::min(K, last)};
+    to_merge = !to_merge;
+  }
+  merged_select_kernel<<<P, kSelThreads, select_lds_bytes(a), st>>>(a, ls);
   return hipGetLastError();
 }
 
@@ -914,17 +1009,27 @@ hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st) {
 //    tokens tg, tg+4, tg+8, tg+12 for every head.
 // The four waves of a workgroup merge through LDS into one split partial.
 
+// Query heads per workgroup: a KV head's group of G query heads is split into
+// head groups of at most kAttnHeads, each its own workgroup over the same
+// tokens, so that the P V accumulators (8 registers per head) leave room for
+// two waves per SIMD.  The head groups of a (pair, split) are dispatched P
+// workgroups apart, i.e. on the same XCD with P a multiple of 8, so the second
+// one mostly reads its keys and values from L2.
+constexpr int kAttnHeads = 8;
+constexpr int attn_group_heads(int group) { return group < kAttnHeads ? group : kAttnHeads; }
+int attn_head_groups(int group) { return group / attn_group_heads(group); }
+
 // 16-token tiles per wave: as many as the registers allow at two waves per SIMD,
 // so that the grid of a long-context step fits the chip's wave slots in one round
-constexpr int attn_tiles(int group) { return group <= 4 ? 5 : (group <= 8 ? 3 : 2); }
+constexpr int attn_tiles(int heads) { return heads <= 4 ? 5 : (heads <= 8 ? 4 : 2); }
 
-template <int G, int C>
+template <int GW, int C>
 struct AttnShape {
-  static constexpr int NT = attn_tiles(G);
+  static constexpr int NT = attn_tiles(GW);
   static constexpr int NUW = NT * 16 / C;       // units per wave
 };
 
-int attn_units_per_wave(int group, int chunk) { return attn_tiles(group) * 16 / chunk; }
+int attn_units_per_wave(int group, int chunk) { return attn_tiles(attn_group_heads(group)) * 16 / chunk; }
 
 template <int C>
 __device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, int u) {
@@ -948,17 +1053,17 @@ __device__ __forceinline__ const uint16_t* unit_value(const DecodeArgs& a, int p
   return a.val_new + ((int64_t)p * a.max_new + (int64_t)(x - Wu) * C) * kHeadDim;
 }
 
-template <int G, int C>
+template <int GW, int C>
 __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
-  constexpr int NT = AttnShape<G, C>::NT;
+  constexpr int NT = AttnShape<GW, C>::NT;
   __shared__ __attribute__((aligned(16))) float pbuf[4][16 * 16];   // [wave][head][tg][t]
   __shared__ float cbuf[4][16];                                     // [wave][head] rescale
-  __shared__ float wo[4][G][kHeadDim];
-  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wo[4][GW][kHeadDim];
+  __shared__ float wm[4][GW], wl[4][GW];
   // pairs fastest: workgroups go to the 8 XCDs round-robin by linear id, so each
   // XCD gets whole pairs (all splits of pairs p = x mod 8) and equal work even
   // when the last split of a pair is short
-  const int p = blockIdx.x, split = blockIdx.y;
+  const int p = blockIdx.x, hg = blockIdx.y, split = blockIdx.z;   // hg: head group
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;   // (row|head|ds, kq|tg)
@@ -972,7 +1077,7 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
   const int valid = (O + K + a.n_win_units - a.n_fold) * C + a.n_new_tokens;   // tokens in units [0, U)
   const int ntok = max(0, min((uw1 - uw0) * C, valid - uw0 * C));
-  const int hq = a.n_kv * G;
+  const int G = a.group, hq = a.n_kv * G, hq0 = h * G + hg * GW;   // first query head of the group
 
 
   // chunk id of each selected unit of the wave, one per lane
@@ -982,12 +1087,12 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
     if (sidx >= 0 && sidx < K) my_ch = max(a.slot_chunk[(int64_t)p * K + sidx], 0);
   }
   // q^T first (every tile needs it; vector-memory loads complete in issue order),
-  // MFMA B layout: head lr, dims j*32 + lq*8 (zero for heads >= G)
+  // MFMA B layout: head lr, dims j*32 + lq*8 (zero for heads >= GW)
   bf16x8 bq[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     u32x4 wq = {0u, 0u, 0u, 0u};
-    if (lr < G) wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + h * G + lr) * kHeadDim + j * 32 + lq * 8);
+    if (lr < GW) wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + hq0 + lr) * kHeadDim + j * 32 + lq * 8);
     bq[j] = __builtin_bit_cast(bf16x8, wq);
   }
   // then tile by tile, keys then values, so that tile 0 can start as soon as its
@@ -1019,9 +1124,9 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   }
   const float qscale = a.scale * kLog2e;
   float m = kNegBig, l = 0.f;        // head lr (S layout)
-  float o[G][8];                     // PV layout
+  float o[GW][8];                    // PV layout
 #pragma unroll
-  for (int g = 0; g < G; g++)
+  for (int g = 0; g < GW; g++)
 #pragma unroll
     for (int k = 0; k < 8; k++) o[g][k] = 0.f;
 
@@ -1058,22 +1163,22 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
 #pragma unroll
-      for (int g = 0; g < G; g++) {
+      for (int g = 0; g < GW; g++) {
         const float cg = cbuf[w][g];
         if (cg != 1.f) {
 #pragma unroll
           for (int k = 0; k < 8; k++) o[g][k] *= cg;
         }
       }
-      f32x4 pg[G];
+      f32x4 pg[GW];
 #pragma unroll
-      for (int g = 0; g < G; g++) pg[g] = *reinterpret_cast<const f32x4*>(&pbuf[w][g * 16 + lq * 4]);
+      for (int g = 0; g < GW; g++) pg[g] = *reinterpret_cast<const f32x4*>(&pbuf[w][g * 16 + lq * 4]);
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         float y[8];
         unpack8(vf[t][i], y);
 #pragma unroll
-        for (int g = 0; g < G; g++)
+        for (int g = 0; g < GW; g++)
 #pragma unroll
           for (int k = 0; k < 8; k++) o[g][k] = fmaf(pg[g][i], y[k], o[g][k]);
       }
@@ -1082,7 +1187,7 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   }
   // the four token rows share the wave's running max: plain sums
 #pragma unroll
-  for (int g = 0; g < G; g++)
+  for (int g = 0; g < GW; g++)
 #pragma unroll
     for (int k = 0; k < 8; k++) {
       o[g][k] += __shfl_xor(o[g][k], 16);
@@ -1090,17 +1195,17 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
     }
   if (lq == 0) {
 #pragma unroll
-    for (int g = 0; g < G; g++)
+    for (int g = 0; g < GW; g++)
 #pragma unroll
       for (int k = 0; k < 8; k++) wo[w][g][lr * 8 + k] = o[g][k];
-    if (lr < G) {
+    if (lr < GW) {
       wm[w][lr] = m;
       wl[w][lr] = l;
     }
   }
   __syncthreads();
-  float* part = a.attn_part + ((int64_t)p * a.n_split + split) * G * (kHeadDim + 2);
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
+  float* part = a.attn_part + (((int64_t)p * a.n_split + split) * G + hg * GW) * kPartStride;
+  for (int idx = threadIdx.x; idx < GW * kHeadDim; idx += 256) {
     const int g = idx / kHeadDim, dim = idx % kHeadDim;
     float M = kNegBig;
 #pragma unroll
@@ -1112,26 +1217,33 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
       num += wo[ww][g][dim] * c;
       den += wl[ww][g] * c;
     }
-    part[g * (kHeadDim + 2) + dim] = num;
+    part[g * kPartStride + dim] = num;
     if (dim == 0) {
-      part[g * (kHeadDim + 2) + kHeadDim] = M;
-      part[g * (kHeadDim + 2) + kHeadDim + 1] = den;
+      part[g * kPartStride + kHeadDim] = M;
+      part[g * kPartStride + kHeadDim + 1] = den;
     }
   }
 }
 
 // Merge the split partials of one (pair, head):
 // out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// 512 threads: 32 lanes cover one partial row (4 dims each, 16-byte loads) and
+// the 16 row groups take every 16th split, then sum their rows through LDS, so a
+// long split list is read 16 rows at a time.
+constexpr int kCombineThreads = 512;
+constexpr int kCombineGroups = kCombineThreads / (kHeadDim / 4);
+
 template <int G>
-__global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) {
   __shared__ float cw[kMaxSplits];
+  __shared__ __attribute__((aligned(16))) float rows[kCombineGroups][kHeadDim];
   __shared__ float den_sh;
   const int g = blockIdx.x, p = blockIdx.y;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int ns = a.n_split;
-  const int64_t stride = (int64_t)G * (kHeadDim + 2);
-  const float* base = a.attn_part + (int64_t)p * ns * stride + g * (kHeadDim + 2);
-  for (int s = threadIdx.x; s < ns; s += 128) cw[s] = base[s * stride + kHeadDim];
+  const int64_t stride = (int64_t)G * kPartStride;
+  const float* base = a.attn_part + (int64_t)p * ns * stride + g * kPartStride;
+  for (int s = threadIdx.x; s < ns; s += kCombineThreads) cw[s] = base[s * stride + kHeadDim];
   __syncthreads();
   if (threadIdx.x < 64) {   // wave 0: split weights 2^(m_s - M) and the denominator
     float M = kNegBig;
@@ -1147,30 +1259,38 @@ __global__ __launch_bounds__(128) void combine_kernel(DecodeArgs a) {
     if (threadIdx.x == 0) den_sh = den;
   }
   __syncthreads();
-  const int dim = threadIdx.x;
-  float num = 0.f;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-    const float x0 = base[(s + 0) * stride + dim], x1 = base[(s + 1) * stride + dim];
-    const float x2 = base[(s + 2) * stride + dim], x3 = base[(s + 3) * stride + dim];
-    num += x0 * cw[s] + x1 * cw[s + 1] + x2 * cw[s + 2] + x3 * cw[s + 3];
+  const int c4 = threadIdx.x % (kHeadDim / 4), grp = threadIdx.x / (kHeadDim / 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = grp; s < ns; s += kCombineGroups) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(base + s * stride + c4 * 4);
+    const float c = cw[s];
+#pragma unroll
+    for (int k = 0; k < 4; k++) acc[k] = fmaf(x[k], c, acc[k]);
   }
-  for (; s < ns; s++) num += base[s * stride + dim] * cw[s];
-  a.out[((int64_t)b * a.n_kv * G + h * G + g) * kHeadDim + dim] = num / den_sh;
+  *reinterpret_cast<f32x4*>(&rows[grp][c4 * 4]) = acc;
+  __syncthreads();
+  if (threadIdx.x < kHeadDim) {
+    const int dim = threadIdx.x;
+    float num = 0.f;
+#pragma unroll
+    for (int r = 0; r < kCombineGroups; r++) num += rows[r][dim];
+    a.out[((int64_t)b * a.n_kv * G + h * G + g) * kHeadDim + dim] = num / den_sh;
+  }
 }
 
 template <int G>
 static hipError_t launch_attn_g(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.batch * a.n_kv, a.n_split);
+  constexpr int GW = attn_group_heads(G);
+  dim3 grid(a.batch * a.n_kv, G / GW, a.n_split);
   switch (a.chunk) {
-    case 4: attn_kernel<G, 4><<<grid, 256, 0, st>>>(a); break;
-    case 8: attn_kernel<G, 8><<<grid, 256, 0, st>>>(a); break;
-    case 16: attn_kernel<G, 16><<<grid, 256, 0, st>>>(a); break;
+    case 4: attn_kernel<GW, 4><<<grid, 256, 0, st>>>(a); break;
+    case 8: attn_kernel<GW, 8><<<grid, 256, 0, st>>>(a); break;
+    case 16: attn_kernel<GW, 16><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<G><<<dim3(G, a.batch * a.n_kv), 128, 0, st>>>(a);
+  combine_kernel<G><<<dim3(G, a.batch * a.n_kv), kCombineThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

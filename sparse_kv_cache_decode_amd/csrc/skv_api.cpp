@@ -71,8 +71,8 @@ struct skv_layer {
   int32_t *cand_map = nullptr, *outlier_ids = nullptr, *slot_cand = nullptr, *slot_chunk = nullptr,
           *miss_slot = nullptr, *miss_chunk = nullptr, *miss_cand = nullptr, *free_slot = nullptr,
           *n_miss = nullptr, *hits_last = nullptr;
-  uint32_t *resident = nullptr, *keys = nullptr, *part_keys = nullptr;
-  int32_t* part_idx = nullptr;
+  uint32_t *resident = nullptr, *keys = nullptr, *part_keys = nullptr, *merge_keys = nullptr;
+  int32_t *part_idx = nullptr, *merge_idx = nullptr;
   long long *hits_total = nullptr, *miss_total = nullptr;
   float *logits = nullptr, *lse_part = nullptr, *attn_part = nullptr, *min_cos = nullptr;
   double* inv_freq = nullptr;
@@ -260,6 +260,8 @@ DecodeArgs decode_args(skv_layer* h) {
   select_partition(h->n_cand, c.top_k, h->G, h->P, &a.n_part, &a.part_size);
   a.part_keys = h->part_keys;
   a.part_idx = h->part_idx;
+  a.merge_keys = h->merge_keys;
+  a.merge_idx = h->merge_idx;
   a.attn_part = h->attn_part;
   return a;
 }
@@ -340,7 +342,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     // at once); split so that there are about 8 waves per CU
     const int nuw = attn_units_per_wave(G, C);
     const int waves_target = 2048;
-    int upw_wave = (int)(((int64_t)P * h->U + waves_target - 1) / waves_target);
+    const int64_t wave_units = (int64_t)attn_head_groups(G) * P * h->U;   // every head group reads every unit
+    int upw_wave = (int)((wave_units + waves_target - 1) / waves_target);
     upw_wave = std::max(1, std::min(upw_wave, nuw));
     h->upw = 4 * upw_wave;
     const int64_t u_max = h->U + ((int64_t)c.max_new_tokens + C - 1) / C;   // with every appended token
@@ -372,12 +375,15 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const size_t oKeys = cv.take<uint32_t>((size_t)P * n_c);
   const size_t oPk = cv.take<uint32_t>((size_t)P * n_part_cap * K);
   const size_t oPi = cv.take<int32_t>((size_t)P * n_part_cap * K);
+  const int n_merge_cap = n_part_cap > 1 ? (n_part_cap + 1) / 2 : 0;   // first tree level's lists
+  const size_t oMk = cv.take<uint32_t>((size_t)P * n_merge_cap * K);
+  const size_t oMi = cv.take<int32_t>((size_t)P * n_merge_cap * K);
   const size_t oHt = cv.take<long long>(P);
   const size_t oMt = cv.take<long long>(P);
   const size_t oLg = cv.take<float>((size_t)P * G * ncp_cap);
   const size_t oLp = cv.take<float>((size_t)P * nb_cap * G * 2);
   const int n_split_max = (h->U + (c.max_new_tokens + C - 1) / C + h->upw - 1) / h->upw;
-  const size_t oAp = cv.take<float>((size_t)P * n_split_max * G * (kHeadDim + 2));
+  const size_t oAp = cv.take<float>((size_t)P * n_split_max * G * kPartStride);
   const size_t oKn = cv.take<uint16_t>((size_t)P * c.max_new_tokens * kHeadDim);
   const size_t oVn = cv.take<uint16_t>((size_t)P * c.max_new_tokens * kHeadDim);
   const size_t oMc = cv.take<float>((size_t)P * n_c);
@@ -439,6 +445,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->keys = (uint32_t*)(base + oKeys);
     h->part_keys = (uint32_t*)(base + oPk);
     h->part_idx = (int32_t*)(base + oPi);
+    h->merge_keys = (uint32_t*)(base + oMk);
+    h->merge_idx = (int32_t*)(base + oMi);
     h->hits_total = (long long*)(base + oHt);
     h->miss_total = (long long*)(base + oMt);
     h->logits = (float*)(base + oLg);

@@ -12,6 +12,7 @@ constexpr int kMaxTopK = 4096;
 constexpr int kSelLdsMax = 150 * 1024;   // dynamic LDS of the select kernel
 constexpr int kMaxSplits = 1024;         // attention workgroups per pair
 constexpr int kScoreRows = 128;          // candidate landmarks per score workgroup
+constexpr int kPartStride = kHeadDim + 4; // floats per attention partial row: o[d], m, l, 2 pad (16-B rows)
 
 // Everything a decode step touches, by value into the kernels.
 struct DecodeArgs {
@@ -64,7 +65,9 @@ struct DecodeArgs {
   int n_part, part_size;      // selection stage 1: candidate parts per pair and their size
   uint32_t* part_keys;        // [P][n_part][K] each part's top-K keys, ascending candidate index
   int32_t* part_idx;          // [P][n_part][K] their candidate indices
-  float* attn_part;           // [P][n_split][G][d + 2]
+  uint32_t* merge_keys;       // [P][<= n_part / 2][K] lists of a merge-tree level
+  int32_t* merge_idx;
+  float* attn_part;           // [P][n_split][G][kPartStride]
   // outputs
   float* out;                 // [b][Hq][d]
   int32_t* chunk_ids;         // [P][K]
@@ -98,6 +101,7 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
 // Two-stage top-K: the candidates of a pair are cut into n_part parts whose
 // top-K are taken by separate workgroups (stage 1), then merged per pair (stage 2).
 void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, int* part_size);
+int merge_groups(int top_k);   // part lists merged per workgroup of the merge tree
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
 // Append token t (position S + t) of every batch element: exact post-RoPE key
 // and value into key_new / val_new; lowrank: also its row a' = k' Psi of A.
@@ -110,6 +114,7 @@ hipError_t launch_fold(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);
 int attn_units_per_wave(int group, int chunk);
+int attn_head_groups(int group);   // attention workgroups per (pair, split): query-head groups
 
 // ---- host eigensolver (eig_host.cpp)
 // Top-r eigenpairs of each symmetric n x n matrix gram[bi] (row-major fp64, on the
