@@ -198,6 +198,12 @@ void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, 
   if ((int64_t)group * n_cand > 65536 || n_cand > kSelThreads * 16) {
     np = std::min({(256 + pairs - 1) / pairs, n_cand / (2 * top_k), 64});
     np = std::max({np, 2, (n_cand + kSelThreads * 16 - 1) / (kSelThreads * 16)});
+    // a part just past 4 or 8 keys per thread would double every thread's
+    // registers and loads: take a few more, smaller parts instead
+    for (int tier : {kSelThreads * 4, kSelThreads * 8}) {
+      const int ps = (n_cand + np - 1) / np;
+      if (ps > tier && ps <= tier + tier / 8) np = (n_cand + tier - 1) / tier;
+    }
   }
   const int ps = np == 1 ? n_cand : ((n_cand + np - 1) / np + 15) / 16 * 16;   // 16-B aligned parts
   *part_size = ps;

@@ -147,7 +147,7 @@ def test_split_selection_group_of_eight():
 
 def test_merge_tree_one_level():
     # K = 2048 of 49145 candidates, 16 q heads on one KV head (the 1M-token shape's
-    # G and K): 11 parts; 8 part lists fit one merge workgroup, so one tree level
+    # G and K): 12 parts; 8 part lists fit one merge workgroup, so one tree level
     # merges them into 2 lists before the final selection
     s = _small(batch=1, n_q_heads=16, n_kv_heads=1, seq_len=393216, rank=16, latent_rank=16,
                top_k=2048, n_outlier=3)
@@ -156,8 +156,8 @@ def test_merge_tree_one_level():
 
 
 def test_merge_tree_two_levels():
-    # K = 4096 (the largest budget) at C = 4: 17 parts, 4 lists per merge
-    # workgroup: two tree levels (17 -> 5 -> 2 lists), then the final selection
+    # K = 4096 (the largest budget) at C = 4: 18 parts, 4 lists per merge
+    # workgroup: two tree levels (18 -> 5 -> 2 lists), then the final selection
     s = _small(batch=1, n_q_heads=4, n_kv_heads=1, seq_len=557104, chunk=4, rank=16, latent_rank=16,
                top_k=4096, n_outlier=3)
     assert s.n_cand == 139265
