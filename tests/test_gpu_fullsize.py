@@ -1,12 +1,18 @@
-"""Full-size parity on the Llama-3.1-8B workload (one layer: batch 8, 122 880
-tokens, 32 q / 8 KV heads, r = 160, C = 8, K = 240, O = 46, window 32), with the
-library in the launch configuration the benchmark times.
+"""Full-size parity on the benchmarked workloads, one layer each, with the
+library in the launch configuration the benchmark times:
+* Llama-3.1-8B shape: batch 8, 122 880 tokens, 32 q / 8 KV heads, r = 160,
+  C = 8, K = 240, O = 46, window 32 (one selection workgroup per KV head);
+* Yi-9B-200K shape: batch 8, 204 800 tokens, 32 q / 4 KV heads, r = 96,
+  K = 400 (selection in parts, one merge);
+* GLM-4-9B-1M shape: batch 4, 1 048 576 tokens, 32 q / 2 KV heads, r = 48,
+  K = 2048 (selection in 32 parts and a merge tree; attention in two head
+  groups of 8).
 
 The oracle cannot afford the whole batch in float64, so it builds and decodes
-sampled batch elements (the first and the last) from the very same bf16 bits
-the GPU consumed; every pair of the batch is checked through properties that
-hold at any size (ascending candidate ids, hit counts equal to the set algebra
-of the GPU's own consecutive selections)."""
+sampled batch elements from the very same bf16 bits the GPU consumed; every
+pair of the batch is checked through properties that hold at any size
+(ascending candidate ids, hit counts equal to the set algebra of the GPU's own
+consecutive selections)."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +23,6 @@ from tests.parity import bits, check_build, check_ids, check_out, reference_out
 
 pytestmark = pytest.mark.gpu
 
-SAMPLED = (0, 7)
 STEPS = 3
 
 
@@ -26,8 +31,10 @@ def _slice_state(ex: dict, b: int) -> dict:
 
 
 @pytest.mark.timeout(900)
-def test_llama3_8b_122k_one_layer_sampled():
-    shape = synth.SHAPES["llama3_8b_122k"]
+@pytest.mark.parametrize("name,sampled", [("llama3_8b_122k", (0, 7)), ("yi_9b_200k", (0,)),
+                                          ("glm4_9b_1m", (3,))])
+def test_one_layer_sampled(name, sampled):
+    shape = synth.SHAPES[name]
     print(f"[fullsize] {shape}", flush=True)
     k, v = synth.layer_cache_torch(shape, 0, 0, "cuda")
     q = synth.queries_torch(shape, k, 0, STEPS, 0)
@@ -65,7 +72,7 @@ def test_llama3_8b_122k_one_layer_sampled():
     # oracle on sampled batch elements, from the same input bits
     one = shape.replace(batch=1)
     qb = [bits(q[t]) for t in range(STEPS)]
-    for b in SAMPLED:
+    for b in sampled:
         print(f"[fullsize] oracle build, batch element {b}", flush=True)
         st = O.build(O.config_from(one), bits(k[b:b + 1]), bits(v[b:b + 1]))
         check_build(_slice_state(ex, b), st)
