@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import glob
 import hashlib
 import json
 import math
@@ -27,8 +28,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 CALIB_BYTES = 512 << 20         # bytes read (and written) once by the counter-calibration kernel
 CSRC = os.path.join(ROOT, "sparse_kv_cache_decode_amd", "csrc")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_kernel_llama3_8b_122k_hbm_traffic.md")
-SCORE_KERNEL = "skv::score_kernel<4>"
+PROFILES = os.path.join(ROOT, "profiles")
+SCORE_KERNELS = {"bf16": "skv::score_kernel<4>", "e5m2": "skv::score_fp8_kernel<4>"}
+LANDMARK_BYTES = {"bf16": 2, "e5m2": 1}
 METRIC = "decode tokens/s at S=122K batch 8 (Llama-3.1-8B shape); % HBM roofline"
 
 
@@ -209,29 +211,33 @@ def summarize_trace(stats_csv: str, command: str) -> str:
              "", "| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
     for n, c, a, lo, hi, t in rows:
         lines.append(f"| `{n}` | {c} | {a:.2f} | {lo:.2f} | {hi:.2f} | {t:.1f} |")
-    score = [r for r in rows if r[0] == SCORE_KERNEL]
-    if score:
-        from sparse_kv_cache_decode_amd import synth
-        shape = synth.SHAPES["llama3_8b_122k"]
-        by = algorithmic_bytes(shape, 0.0)["score"]
-        lines += ["", f"Score kernel: {by} algorithmic bytes per launch / {score[0][2]:.2f} us average = "
-                      f"{by / (score[0][2] * 1e-6) / 1e9:.0f} GB/s ({by / (score[0][2] * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} "
-                      f"of {HBM_PEAK_GBPS / 1000:.0f} TB/s)."]
+    for fmt, kname in SCORE_KERNELS.items():
+        score = [r for r in rows if r[0] == kname]
+        if score:
+            from sparse_kv_cache_decode_amd import synth
+            shape = synth.SHAPES["llama3_8b_122k"].replace(landmark_format=fmt)
+            by = algorithmic_bytes(shape, 0.0)["score"]
+            lines += ["", f"Score kernel ({fmt} landmarks): {by} algorithmic bytes per launch / {score[0][2]:.2f} us "
+                          f"average = {by / (score[0][2] * 1e-6) / 1e9:.0f} GB/s "
+                          f"({by / (score[0][2] * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of {HBM_PEAK_GBPS / 1000:.0f} TB/s)."]
     return "\n".join(lines) + "\n"
 
 
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None
     when there is none for this workload or the sources have changed since."""
-    try:
-        text = open(TRAFFIC_SUMMARY).read()
-        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-    except (OSError, IndexError, ValueError):
-        return None
-    if blob.get("workload") != workload or blob.get("kernel_source_digest") != kernel_source_digest():
-        return None
-    k = blob.get("kernels", {}).get(kernel)
-    return k["hbm_bytes_per_launch"] if k else None
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*_hbm_traffic.md"))):
+        try:
+            text = open(path).read()
+            blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        except (OSError, IndexError, ValueError):
+            continue
+        if blob.get("workload") != workload or blob.get("kernel_source_digest") != kernel_source_digest():
+            continue
+        k = blob.get("kernels", {}).get(kernel)
+        if k:
+            return k["hbm_bytes_per_launch"]
+    return None
 
 
 def measure_h2d_gbps(nbytes: int = 256 << 20, reps: int = 8) -> float:
@@ -259,7 +265,7 @@ def algorithmic_bytes(shape, misses_per_layer_step: float) -> dict:
     """Bytes the method must move per layer-step (HBM-resident values)."""
     d, C, r = shape.head_dim, shape.chunk, shape.rank
     P = shape.pairs
-    landmarks = P * shape.n_cand * d * 2
+    landmarks = P * shape.n_cand * d * LANDMARK_BYTES[shape.landmark_format]
     q_bytes = shape.batch * shape.n_q_heads * d * 2
     out_bytes = shape.batch * shape.n_q_heads * d * 4
     rebuild = misses_per_layer_step * C * (r * 2 + d * 2) + P * r * d * 2
@@ -285,6 +291,8 @@ def main():
     ap.add_argument("--append", choices=["none", "exact", "lowrank"], default="none",
                     help="append one generated token per layer before every decode step "
                          "(exact keys, or ShadowKV+ low-rank states)")
+    ap.add_argument("--landmarks", choices=["bf16", "e5m2"], default="bf16",
+                    help="landmark storage: bf16 (the pages' precision) or FP8 E5M2 (their precision study)")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
                     help="replay each timed step (all layers) as one captured HIP graph; off: launch eagerly")
     ap.add_argument("--phase-steps", type=int, default=16,
@@ -332,6 +340,8 @@ def main():
         return 2
     if args.layers:
         shape = shape.replace(layers=args.layers)
+    if args.landmarks != "bf16":
+        shape = shape.replace(landmark_format=args.landmarks)
     L, W, K = shape.layers, args.warmup, args.steps
     PH = max(1, args.phase_steps)
     total = W + K + PH            # warm-up, timed and phase-timing steps
@@ -479,22 +489,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if shape.landmark_format == "bf16" else "bf16, e5m2 landmarks (fp16 MFMA scoring)",
         "data": "synthetic",
         "config": {"workload": f"{shape.name}: {L} layers, batch {shape.batch}, S={shape.seq_len}, "
                                f"{shape.n_q_heads} q / {shape.n_kv_heads} KV heads, d={shape.head_dim}, "
                                f"r={shape.rank}, C={shape.chunk}, K={shape.top_k}, O={shape.n_outlier}, "
-                               f"window {shape.window}, values in {'pinned host memory' if host else 'HBM'}, "
+                               f"window {shape.window}, {shape.landmark_format} landmarks, "
+                               f"values in {'pinned host memory' if host else 'HBM'}, "
                                f"{'AR(1)-drifting' if args.queries == 'drift' else 'independent'} queries"
                                + ("" if new_mode is None else
                                   f", one generated token appended per layer and step ({args.append} keys; "
                                   f"{W + 1}..{W + K} generated tokens attended in the timed steps)"),
                    "global_batch": shape.batch, "seq_len": shape.seq_len, "layers": L,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "score_kernel (landmark GEMV)",
+        "roofline": {"bound": "hbm", "kernel": f"{SCORE_KERNELS[shape.landmark_format]} (landmark GEMV)",
                      "achieved": round(score_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(score_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(shape.name, SCORE_KERNEL),
+                     "traffic": measured_traffic(shape.name, SCORE_KERNELS[shape.landmark_format]),
                      "algorithmic_bytes": int(by["score"])},
         "step_roofline": {"algorithmic_bytes_per_layer_step": int(by["total"]),
                           "achieved_GBps": round(step_gbps, 1),

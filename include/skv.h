@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 3
+#define SKV_ABI_VERSION 4
 
 typedef int32_t skv_status;
 #define SKV_OK 0
@@ -66,6 +66,16 @@ typedef int32_t skv_status;
 #define SKV_VALUES_HOST 1      /* values in pinned host memory, missed chunks are
                                   gathered over PCIe on a side stream that overlaps
                                   the key rebuild                                   */
+
+/* Storage format of the landmarks (chunk means). */
+#define SKV_LANDMARKS_BF16 0      /* bfloat16, 256 bytes per landmark                 */
+#define SKV_LANDMARKS_FP8_E5M2 1  /* FP8 E5M2 (1 sign, 5 exponent bits with bias 15, 2
+                                     mantissa bits, the torch.float8_e5m2 format),
+                                     128 bytes per landmark: the fp32 chunk mean is
+                                     rounded once to nearest even; scoring widens it
+                                     to fp16 exactly and multiplies it with q in fp16
+                                     (q's bf16 values are exact there while they lie
+                                     in fp16's normal range, |q| <= 65504)         */
 
 /* How appended (generated) tokens keep their keys. */
 #define SKV_NEW_EXACT 0        /* post-RoPE key kept exactly (ShadowKV)             */
@@ -98,7 +108,7 @@ typedef struct skv_config {
   double rope_theta;       /* RoPE base (rotate-half pairing (i, i + d/2))        */
   int32_t temporal_cache;  /* 1: rebuild/fetch only chunks missed vs the previous
                               step; 0: rebuild every selected chunk every step     */
-  int32_t reserved;        /* must be 0                                           */
+  int32_t landmark_format; /* SKV_LANDMARKS_BF16 or SKV_LANDMARKS_FP8_E5M2        */
   int32_t max_new_tokens;  /* capacity for generated tokens (0: none)             */
   int32_t new_token_mode;  /* SKV_NEW_EXACT or SKV_NEW_LOWRANK                     */
 } skv_config;
@@ -123,7 +133,8 @@ typedef struct skv_stats {
  * pointer may be NULL to skip that tensor.  Sizes (elements):
  *   A          bf16 [b][S][r]
  *   B          bf16 [b][H_kv][r][d]       (the per-head right factor)
- *   landmarks  bf16 [b][H_kv][n_cand][d]  (candidate chunks of the pre-filled
+ *   landmarks  bf16 [b][H_kv][n_cand][d]  (bf16 values also with FP8 storage, which
+ *                                          they hold exactly; candidate chunks of the pre-filled
  *                                          context, ascending chunk id; chunks
  *                                          folded in by skv_append_token are not
  *                                          exported)

@@ -36,7 +36,9 @@ probabilities; ties in top-K prefer the lower chunk id, ties in the outlier
 test prefer the lower chunk id; selected ids are returned ascending; cosine
 with a zero vector is 0; stored state (A, B, landmarks, outlier and window
 keys, rebuilt keys) is rounded once to bfloat16 with round-to-nearest-even
-when ``storage_rounding`` is on.  Generated tokens: the t-th appended token
+when ``storage_rounding`` is on; with ``landmark_format = "e5m2"`` the
+landmarks are rounded instead to FP8 E5M2 (the torch.float8_e5m2 precision of
+the summary's precision-sensitivity paragraph, section 5).  Generated tokens: the t-th appended token
 (t = 0, 1, ...) sits at position seq_len + t and its value is kept as given.
 Exact mode (ShadowKV's assembly): every decode step attends to all of them
 with the exact key RoPE(k'), and they take no part in scoring or selection.
@@ -76,6 +78,20 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     m, e = np.frexp(x)              # x = m * 2^e, 0.5 <= |m| < 1
     r = np.rint(m * 256.0) / 256.0  # 8 significant bits, ties to even
     return np.ldexp(r, e)
+
+
+def round_e5m2(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest FP8 E5M2 value (ties to even), as
+    float64: 1 sign, 5 exponent bits with bias 15, 2 mantissa bits, so normal
+    values keep 3 significant bits from 2^-14 up to 57344, and below 2^-14 the
+    values are multiples of 2^-16.  Magnitudes that round past 57344 become inf."""
+    x = np.asarray(x, dtype=np.float64)
+    assert np.all(np.isfinite(x))
+    m, e = np.frexp(x)                                  # x = m * 2^e, 0.5 <= |m| < 1
+    normal = np.ldexp(np.rint(m * 8.0) / 8.0, e)        # 3 significant bits
+    sub = np.rint(x * 2.0 ** 16) / 2.0 ** 16            # fixed spacing 2^-16
+    r = np.where(np.abs(x) >= 2.0 ** -14, normal, sub)
+    return np.where(np.abs(r) > 57344.0, np.copysign(np.inf, x), r)
 
 
 # ----------------------------------------------------------------------------
@@ -170,6 +186,7 @@ class Config:
     n_outlier: int
     window: int
     rope_theta: float = 500000.0
+    landmark_format: str = "bf16"    # storage of the landmarks: "bf16" or "e5m2" (FP8)
 
     @property
     def group(self):
@@ -192,7 +209,7 @@ def config_from(shape) -> Config:
     """Take the ShadowKV fields from any object carrying them."""
     return Config(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                   shape.seq_len, shape.rank, shape.chunk, shape.top_k, shape.n_outlier,
-                  shape.window, shape.rope_theta)
+                  shape.window, shape.rope_theta, getattr(shape, "landmark_format", "bf16"))
 
 
 @dataclasses.dataclass
@@ -219,6 +236,11 @@ class State:
     def keep(self, x):
         return round_bf16(x) if self.storage_rounding else x
 
+    def keep_landmark(self, x):
+        if not self.storage_rounding:
+            return x
+        return round_e5m2(x) if self.cfg.landmark_format == "e5m2" else round_bf16(x)
+
 
 def build(cfg: Config, k_pre, v, storage_rounding: bool = True) -> State:
     """Algorithm 1 for every batch element.
@@ -233,6 +255,7 @@ def build(cfg: Config, k_pre, v, storage_rounding: bool = True) -> State:
     assert S % C == 0 and cfg.window % C == 0 and 1 <= cfg.top_k <= cfg.n_cand
     n_c, n_elig = cfg.n_chunks, cfg.n_chunks - cfg.n_win_chunks
     rnd = round_bf16 if storage_rounding else (lambda x: x)
+    rnd_l = (round_e5m2 if cfg.landmark_format == "e5m2" else round_bf16) if storage_rounding else (lambda x: x)
     pos = np.arange(S)
 
     As, Bs, sigs, Ls, cands, outs, mcs, kos, vos, kws, vws = ([] for _ in range(11))
@@ -244,7 +267,7 @@ def build(cfg: Config, k_pre, v, storage_rounding: bool = True) -> State:
         mc = chunk_min_cos(kr, lm, C)              # [H, n_c]
         o_ids = np.stack([pick_outliers(mc[h], cfg.n_outlier, n_elig) for h in range(H)])
         cand = np.stack([np.setdiff1d(np.arange(n_elig), o_ids[h]) for h in range(H)])
-        Ls.append(rnd(np.stack([lm[h, cand[h]] for h in range(H)])))
+        Ls.append(rnd_l(np.stack([lm[h, cand[h]] for h in range(H)])))
         tok = (o_ids[:, :, None] * C + np.arange(C)).reshape(H, -1)
         kos.append(rnd(np.stack([kr[h, tok[h]] for h in range(H)])))
         vos.append(np.stack([v[bi, h, tok[h]] for h in range(H)]))
@@ -298,7 +321,7 @@ def append(st: State, k_new, v_new, lowrank: bool = False) -> None:
     st.K_win = np.concatenate([st.K_win, keys], axis=2)
     st.V_win = np.concatenate([st.V_win, vals], axis=2)
     if st.n_new % C == 0:
-        lm = st.keep(st.K_win[:, :, :C].mean(axis=2))             # [b, H, d]
+        lm = st.keep_landmark(st.K_win[:, :, :C].mean(axis=2))    # [b, H, d]
         chunk = (cfg.seq_len - cfg.window) // C + st.n_new // C - 1
         st.L = np.concatenate([st.L, lm[:, :, None]], axis=2)
         st.cand = np.concatenate([st.cand, np.full((b, H, 1), chunk, dtype=st.cand.dtype)], axis=2)

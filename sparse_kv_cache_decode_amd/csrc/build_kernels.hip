@@ -12,14 +12,15 @@ namespace skv {
 
 // ---------------------------------------------------------------------------
 // RoPE + landmark + min-cos: one wave per (b, h, chunk); lane l holds dims l, l+64
-// (the rotate-half pair).  Landmark = mean of the C rotated keys (fp32), stored
-// bf16; min-cos uses the fp32 mean.
+// (the rotate-half pair).  Landmark = mean of the C rotated keys (fp32), rounded
+// once to its storage format (bf16, or FP8 E5M2 with fp8); min-cos uses the fp32
+// mean.
 
 template <int C>
 __global__ __launch_bounds__(256) void rope_landmark_kernel(const uint16_t* __restrict__ k_pre,
                                                             int64_t S, int H, int n_c,
-                                                            const double* __restrict__ inv_freq,
-                                                            uint16_t* __restrict__ L_full,
+                                                            const double* __restrict__ inv_freq, bool fp8,
+                                                            void* __restrict__ L_full,
                                                             float* __restrict__ min_cos) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -52,21 +53,27 @@ __global__ __launch_bounds__(256) void rope_landmark_kernel(const uint16_t* __re
     mc = fminf(mc, cs);
   }
   const int64_t pr = (int64_t)b * H + h;
-  uint16_t* lrow = L_full + (pr * n_c + j) * kHeadDim;
-  lrow[lane] = f32_to_bf16(m1);
-  lrow[lane + 64] = f32_to_bf16(m2);
+  if (fp8) {
+    uint8_t* lrow = static_cast<uint8_t*>(L_full) + (pr * n_c + j) * kHeadDim;
+    lrow[lane] = f32_to_e5m2(m1);
+    lrow[lane + 64] = f32_to_e5m2(m2);
+  } else {
+    uint16_t* lrow = static_cast<uint16_t*>(L_full) + (pr * n_c + j) * kHeadDim;
+    lrow[lane] = f32_to_bf16(m1);
+    lrow[lane + 64] = f32_to_bf16(m2);
+  }
   if (lane == 0) min_cos[pr * n_c + j] = mc;
 }
 
 hipError_t launch_rope_landmark(const uint16_t* k_pre, int b, int64_t S, int H, int C,
-                                const double* inv_freq, uint16_t* L_full, float* min_cos,
+                                const double* inv_freq, bool fp8, void* L_full, float* min_cos,
                                 hipStream_t st) {
   const int n_c = (int)(S / C);
   dim3 grid((n_c + 3) / 4, H, b);
   switch (C) {
-    case 4: rope_landmark_kernel<4><<<grid, 256, 0, st>>>(k_pre, S, H, n_c, inv_freq, L_full, min_cos); break;
-    case 8: rope_landmark_kernel<8><<<grid, 256, 0, st>>>(k_pre, S, H, n_c, inv_freq, L_full, min_cos); break;
-    case 16: rope_landmark_kernel<16><<<grid, 256, 0, st>>>(k_pre, S, H, n_c, inv_freq, L_full, min_cos); break;
+    case 4: rope_landmark_kernel<4><<<grid, 256, 0, st>>>(k_pre, S, H, n_c, inv_freq, fp8, L_full, min_cos); break;
+    case 8: rope_landmark_kernel<8><<<grid, 256, 0, st>>>(k_pre, S, H, n_c, inv_freq, fp8, L_full, min_cos); break;
+    case 16: rope_landmark_kernel<16><<<grid, 256, 0, st>>>(k_pre, S, H, n_c, inv_freq, fp8, L_full, min_cos); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -102,10 +109,10 @@ hipError_t launch_outliers(const float* min_cos, int P, int n_c, int n_elig, int
 // Candidates: every eligible chunk that is not an outlier, in ascending order;
 // landmarks are compacted to those rows.  One wave per chunk.
 
-__global__ __launch_bounds__(256) void candidates_kernel(const uint16_t* __restrict__ L_full,
+__global__ __launch_bounds__(256) void candidates_kernel(const uint32_t* __restrict__ L_full,
                                                          const int32_t* __restrict__ outlier_ids,
-                                                         int n_c, int n_elig, int O, int stride,
-                                                         uint16_t* __restrict__ L,
+                                                         int n_c, int n_elig, int O, int stride, int row_words,
+                                                         uint32_t* __restrict__ L,
                                                          int32_t* __restrict__ cand_map) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -120,16 +127,18 @@ __global__ __launch_bounds__(256) void candidates_kernel(const uint16_t* __restr
   }
   if (lo < O && oid[lo] == j) return;
   const int ci = j - lo;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(L_full + ((int64_t)p * n_c + j) * kHeadDim);
-  uint32_t* dst = reinterpret_cast<uint32_t*>(L + ((int64_t)p * stride + ci) * kHeadDim);
-  dst[lane] = src[lane];
+  const uint32_t* src = L_full + ((int64_t)p * n_c + j) * row_words;
+  uint32_t* dst = L + ((int64_t)p * stride + ci) * row_words;
+  if (lane < row_words) dst[lane] = src[lane];
   if (lane == 0) cand_map[(int64_t)p * stride + ci] = j;
 }
 
-hipError_t launch_candidates(const uint16_t* L_full, const int32_t* outlier_ids, int P, int n_c,
-                             int n_elig, int O, int stride, uint16_t* L, int32_t* cand_map, hipStream_t st) {
+hipError_t launch_candidates(const void* L_full, const int32_t* outlier_ids, int P, int n_c,
+                             int n_elig, int O, int stride, int row_bytes, void* L, int32_t* cand_map,
+                             hipStream_t st) {
   dim3 grid((n_elig + 3) / 4, P);
-  candidates_kernel<<<grid, 256, 0, st>>>(L_full, outlier_ids, n_c, n_elig, O, stride, L, cand_map);
+  candidates_kernel<<<grid, 256, 0, st>>>(static_cast<const uint32_t*>(L_full), outlier_ids, n_c, n_elig, O,
+                                          stride, row_bytes / 4, static_cast<uint32_t*>(L), cand_map);
   return hipGetLastError();
 }
 

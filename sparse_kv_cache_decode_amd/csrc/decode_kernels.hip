@@ -53,6 +53,55 @@ hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// Score epilogue, shared by both landmark formats: one 16-landmark tile's MFMA
+// output (lane (head col, kq) holds landmarks cb .. cb+3 of head col) scaled to
+// logits, stored, and folded into the lane's running (max, sum) of exp.
+template <int G>
+__device__ __forceinline__ void score_tile_out(const DecodeArgs& a, float* lg, int col, int cb, int c1, f32x4 acc,
+                                               float& m_run, float& s_run) {
+  if (col < G && cb < c1) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = acc[i] * a.scale;
+    if (cb + 4 <= c1) {
+      *reinterpret_cast<f32x4*>(lg + cb) = (f32x4){v[0], v[1], v[2], v[3]};
+    } else {
+      for (int i = 0; i < 4 && cb + i < c1; i++) lg[cb + i] = v[i];
+    }
+    float mx = v[0];
+#pragma unroll
+    for (int i = 1; i < 4; i++)
+      if (cb + i < c1) mx = fmaxf(mx, v[i]);
+    const float mn = fmaxf(m_run, mx);
+    float add = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if (cb + i < c1) add += __expf(v[i] - mn);
+    s_run = s_run * __expf(m_run - mn) + add;
+    m_run = mn;
+  }
+}
+
+// The workgroup's per-head (max, sum) partial from its 16 lanes per head.
+template <int G>
+__device__ __forceinline__ void score_lse_out(const DecodeArgs& a, int p, int blk, int w, int col, int kq,
+                                              float m_run, float s_run, float (&red)[2][16][16]) {
+  if (col < G) {
+    red[0][w * 4 + kq][col] = m_run;
+    red[1][w * 4 + kq][col] = s_run;
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    float M = kNegBig;
+    for (int k = 0; k < 16; k++) M = fmaxf(M, red[0][k][threadIdx.x]);
+    float S = 0.f;
+    for (int k = 0; k < 16; k++) S += red[1][k][threadIdx.x] * __expf(red[0][k][threadIdx.x] - M);
+    float* dst = a.lse_part + (((int64_t)p * a.nb_score + blk) * G + threadIdx.x) * 2;
+    dst[0] = M;
+    dst[1] = S;
+  }
+}
+
 // Score.  A workgroup takes a block of kScoreRows candidate landmarks (32 KB).
 // The block is copied into LDS with direct global->LDS loads, each wave
 // instruction reading 1 KB of contiguous rows (full 128-byte lines; reading
@@ -103,53 +152,79 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
       const u32x4 av = stage[row * 16 + ((j * 4 + kq) ^ (row & 15))];
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bq[j], acc, 0, 0, 0);
     }
-    const int cb = c0 + w * (kScoreRows / 4) + t * 16 + kq * 4;
-    if (col < G && cb < c1) {
-      float v[4];
+    score_tile_out<G>(a, lg, col, c0 + w * (kScoreRows / 4) + t * 16 + kq * 4, c1, acc, m_run, s_run);
+  }
+  score_lse_out<G>(a, p, blk, w, col, kq, m_run, s_run, red);
+}
+
+// Score over FP8 (E5M2) landmarks: 128-byte rows, kScoreRows8 per workgroup (the
+// same 32 KB block).  Lane (row r, kq) loads dims kq*32 .. kq*32+31 of its row
+// with two 16-byte loads per tile, all tiles' loads issued first; MFMA j
+// (16x16x32 fp16) takes dims kq*32 + j*8 .. +7, and q's operand follows the same
+// assignment (a dot product does not depend on the order of the dims).  An E5M2
+// byte is the high byte of the fp16 with the same value, so widening is a shift;
+// q's bf16 values convert to fp16 exactly in fp16's normal range.
+
+__device__ __forceinline__ u32x4 e5m2x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  return (u32x4){((lo & 0xffu) << 8) | ((lo & 0xff00u) << 16), ((lo >> 8) & 0xff00u) | (lo & 0xff000000u),
+                 ((hi & 0xffu) << 8) | ((hi & 0xff00u) << 16), ((hi >> 8) & 0xff00u) | (hi & 0xff000000u)};
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void score_fp8_kernel(DecodeArgs a) {
+  __shared__ float red[2][16][16];   // (m, s) per (wave, kq) and head
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const int p = blockIdx.y, blk = blockIdx.x;
+  const int b = p / a.n_kv, h = p % a.n_kv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = lane & 15, kq = lane >> 4;
+  const int hq = a.n_kv * G;
+  const int c0 = blk * kScoreRows8, c1 = min(a.n_cand, c0 + kScoreRows8), nr = c1 - c0;
+  const uint8_t* Lp = reinterpret_cast<const uint8_t*>(a.L) + ((int64_t)p * a.cand_stride + c0) * kHeadDim;
+  constexpr int kTiles = kScoreRows8 / 64;   // 16-row tiles per wave
+  // rows past a ragged block's end repeat its last row; their outputs are not used
+  u32x4 lf[kTiles][2];
 #pragma unroll
-      for (int i = 0; i < 4; i++) v[i] = acc[i] * a.scale;
-      if (cb + 4 <= c1) {
-        *reinterpret_cast<f32x4*>(lg + cb) = (f32x4){v[0], v[1], v[2], v[3]};
-      } else {
-        for (int i = 0; i < 4 && cb + i < c1; i++) lg[cb + i] = v[i];
-      }
-      float mx = v[0];
+  for (int t = 0; t < kTiles; t++) {
+    const uint8_t* rp = Lp + (int64_t)min(w * (kScoreRows8 / 4) + t * 16 + col, nr - 1) * kHeadDim + kq * 32;
+    lf[t][0] = *reinterpret_cast<const u32x4*>(rp);
+    lf[t][1] = *reinterpret_cast<const u32x4*>(rp + 16);
+  }
+  // head columns past G repeat head G-1; their outputs are not used
+  f16x8 bq[4];
+  const uint16_t* qp = a.q + ((int64_t)b * hq + h * G + min(col, G - 1)) * kHeadDim + kq * 32;
 #pragma unroll
-      for (int i = 1; i < 4; i++)
-        if (cb + i < c1) mx = fmaxf(mx, v[i]);
-      const float mn = fmaxf(m_run, mx);
-      float add = 0.f;
+  for (int j = 0; j < 4; j++) {
+    float x[8];
+    unpack8(*reinterpret_cast<const u32x4*>(qp + j * 8), x);
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-        if (cb + i < c1) add += __expf(v[i] - mn);
-      s_run = s_run * __expf(m_run - mn) + add;
-      m_run = mn;
+    for (int k = 0; k < 8; k++) bq[j][k] = (_Float16)x[k];
+  }
+  float* lg = a.logits + ((int64_t)p * G + (col < G ? col : 0)) * a.ncp;
+  float m_run = kNegBig, s_run = 0.f;
+#pragma unroll
+  for (int t = 0; t < kTiles; t++) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const u32x4 half = lf[t][j / 2];
+      const u32x4 av = e5m2x8_to_f16x8(half[(j % 2) * 2], half[(j % 2) * 2 + 1]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), bq[j], acc, 0, 0, 0);
     }
+    score_tile_out<G>(a, lg, col, c0 + w * (kScoreRows8 / 4) + t * 16 + kq * 4, c1, acc, m_run, s_run);
   }
-  if (col < G) {
-    red[0][w * 4 + kq][col] = m_run;
-    red[1][w * 4 + kq][col] = s_run;
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float M = kNegBig;
-    for (int k = 0; k < 16; k++) M = fmaxf(M, red[0][k][threadIdx.x]);
-    float S = 0.f;
-    for (int k = 0; k < 16; k++) S += red[1][k][threadIdx.x] * __expf(red[0][k][threadIdx.x] - M);
-    float* dst = a.lse_part + (((int64_t)p * a.nb_score + blk) * G + threadIdx.x) * 2;
-    dst[0] = M;
-    dst[1] = S;
-  }
+  score_lse_out<G>(a, p, blk, w, col, kq, m_run, s_run, red);
 }
 
 hipError_t launch_score(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.nb_score, a.batch * a.n_kv);
+  const bool fp8 = a.landmark_format == SKV_LANDMARKS_FP8_E5M2;
   switch (a.group) {
-    case 1: score_kernel<1><<<grid, 256, 0, st>>>(a); break;
-    case 2: score_kernel<2><<<grid, 256, 0, st>>>(a); break;
-    case 4: score_kernel<4><<<grid, 256, 0, st>>>(a); break;
-    case 8: score_kernel<8><<<grid, 256, 0, st>>>(a); break;
-    case 16: score_kernel<16><<<grid, 256, 0, st>>>(a); break;
+    case 1: fp8 ? score_fp8_kernel<1><<<grid, 256, 0, st>>>(a) : score_kernel<1><<<grid, 256, 0, st>>>(a); break;
+    case 2: fp8 ? score_fp8_kernel<2><<<grid, 256, 0, st>>>(a) : score_kernel<2><<<grid, 256, 0, st>>>(a); break;
+    case 4: fp8 ? score_fp8_kernel<4><<<grid, 256, 0, st>>>(a) : score_kernel<4><<<grid, 256, 0, st>>>(a); break;
+    case 8: fp8 ? score_fp8_kernel<8><<<grid, 256, 0, st>>>(a) : score_kernel<8><<<grid, 256, 0, st>>>(a); break;
+    case 16: fp8 ? score_fp8_kernel<16><<<grid, 256, 0, st>>>(a) : score_kernel<16><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -857,8 +932,9 @@ hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st) {
 //    about 20 row loads of B^T per thread, issued eight at a time.
 //  fold_kernel, low rank only, after the append that completes a chunk: the
 //    oldest exact chunk (combined index n_fold over [window units; appended
-//    units]) becomes the pair's last candidate, its landmark the bf16 mean of its
-//    stored exact keys and its chunk id n_c - W/C + n_fold.  Chunk ids of the
+//    units]) becomes the pair's last candidate, its landmark the mean of its
+//    stored exact keys (rounded once to the landmark format) and its chunk id
+//    n_c - W/C + n_fold.  Chunk ids of the
 //    candidates stay ascending.
 
 constexpr int kMaxHD = 2048;
@@ -954,7 +1030,11 @@ __global__ __launch_bounds__(kHeadDim) void fold_kernel(DecodeArgs a, uint16_t* 
                                : a.key_new + ((int64_t)p * a.max_new + (int64_t)(x - Wu) * C) * kHeadDim;
   float sum = 0.f;
   for (int i = 0; i < C; i++) sum += bf16_to_f32(src[i * kHeadDim + dim]);
-  L[((int64_t)p * a.cand_stride + a.n_cand) * kHeadDim + dim] = f32_to_bf16(sum * (1.0f / C));
+  const int64_t at = ((int64_t)p * a.cand_stride + a.n_cand) * kHeadDim + dim;
+  if (a.landmark_format == SKV_LANDMARKS_FP8_E5M2)
+    reinterpret_cast<uint8_t*>(L)[at] = f32_to_e5m2(sum * (1.0f / C));
+  else
+    L[at] = f32_to_bf16(sum * (1.0f / C));
   if (dim == 0) cand_map[(int64_t)p * a.cand_stride + a.n_cand] = a.n_c - Wu + x;
 }
 

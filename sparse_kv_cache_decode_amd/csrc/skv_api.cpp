@@ -101,9 +101,23 @@ struct Carver {
   }
 };
 
+// FP8 E5M2 byte -> bf16 bits (exact: 2 mantissa bits, exponents inside bf16's).
+uint16_t e5m2_to_bf16(uint8_t v) {
+  const int e = (v >> 2) & 31, m = v & 3;
+  float x;
+  if (e == 31) x = m ? NAN : INFINITY;
+  else if (e == 0) x = std::ldexp((float)m, -16);
+  else x = std::ldexp(1.0f + m * 0.25f, e - 15);
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  u = (u >> 16) | ((uint32_t)(v & 0x80) << 8);
+  return (uint16_t)u;
+}
+
 skv_status validate(const skv_config* c) {
   if (!c) return SKV_ERR_INVALID_ARG;
-  if (c->reserved != 0) return SKV_ERR_INVALID_ARG;
+  if (c->landmark_format != SKV_LANDMARKS_BF16 && c->landmark_format != SKV_LANDMARKS_FP8_E5M2)
+    return SKV_ERR_INVALID_ARG;
   if (c->value_placement != SKV_VALUES_DEVICE && c->value_placement != SKV_VALUES_HOST)
     return SKV_ERR_INVALID_ARG;
   if (c->temporal_cache != 0 && c->temporal_cache != 1) return SKV_ERR_INVALID_ARG;
@@ -218,10 +232,12 @@ DecodeArgs decode_args(skv_layer* h) {
   a.n_c = h->n_c;
   a.seq_len = c.seq_len;
   a.a_rows = h->a_rows;
-  // score: kScoreRows landmarks per workgroup (a larger grid beats longer
-  // per-workgroup loops); logits rows padded to 16 bytes
-  a.cpb = kScoreRows;
-  a.nb_score = (h->n_cand + kScoreRows - 1) / kScoreRows;
+  // score: a 32 KB block of landmarks per workgroup (kScoreRows bf16 rows or
+  // kScoreRows8 FP8 rows; a larger grid beats longer per-workgroup loops);
+  // logits rows padded to 16 bytes
+  a.landmark_format = c.landmark_format;
+  a.cpb = c.landmark_format == SKV_LANDMARKS_FP8_E5M2 ? kScoreRows8 : kScoreRows;
+  a.nb_score = (h->n_cand + a.cpb - 1) / a.cpb;
   a.ncp = (h->n_cand + 3) / 4 * 4;
   // attention splits grow with the exact region (window + appended, not folded)
   a.n_split = (h->U + a.n_new_units - h->n_fold + h->upw - 1) / h->upw;
@@ -329,8 +345,11 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   h->res_words = (h->cand_cap + 31) / 32;
   h->v_dev = v_dev;
   const int P = h->P, G = h->G, n_c = h->n_c, cap = h->cand_cap, HD = h->HD;
-  // scratch sized for the largest candidate count the handle can reach
+  // scratch sized for the largest candidate count the handle can reach (the
+  // bf16 score block is the smaller one, so its count bounds both formats)
   const int nb_cap = (cap + kScoreRows - 1) / kScoreRows, ncp_cap = (cap + 3) / 4 * 4;
+  const bool fp8 = c.landmark_format == SKV_LANDMARKS_FP8_E5M2;
+  const int lrow = fp8 ? kHeadDim : kHeadDim * 2;   // bytes per landmark
   int n_part_cap = 1;
   for (int n = h->n_cand0; n <= cap; n++) {
     int np, ps;
@@ -354,7 +373,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   Carver cv;
   const size_t oA = cv.take<uint16_t>((size_t)b * h->a_rows * r);
   const size_t oBt = cv.take<uint16_t>((size_t)b * HD * r);
-  const size_t oL = cv.take<uint16_t>((size_t)P * cap * kHeadDim);
+  const size_t oL = cv.take<uint8_t>((size_t)P * cap * lrow);
   const size_t oKo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
   const size_t oVo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
   const size_t oKw = cv.take<uint16_t>((size_t)P * c.window * kHeadDim);
@@ -392,7 +411,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
 
   // build temporaries
   const int nseg = gram_segments(b, S, HD);
-  uint16_t* L_full = nullptr;
+  void* L_full = nullptr;
   double *gpart = nullptr, *gram = nullptr;
   float* psi_f = nullptr;
   std::vector<double> psi((size_t)b * HD * r);
@@ -408,7 +427,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     release(h);
     return SKV_ERR_OOM;
   }
-  if (hipMalloc(&L_full, (size_t)P * n_c * kHeadDim * 2) != hipSuccess ||
+  if (hipMalloc(&L_full, (size_t)P * n_c * lrow) != hipSuccess ||
       hipMalloc(&gpart, (size_t)b * nseg * HD * HD * 8) != hipSuccess ||
       hipMalloc(&gram, (size_t)b * HD * HD * 8) != hipSuccess ||
       hipMalloc(&psi_f, (size_t)b * HD * r * 4) != hipSuccess) {
@@ -469,9 +488,9 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   HIP_TRY(hipMemsetAsync(h->pool, 0, pool_bytes, s));
   HIP_TRY(hipMemcpyAsync(h->inv_freq, invf.data(), invf.size() * 8, hipMemcpyHostToDevice, s));
   // post-RoPE keys -> landmarks and min-cos; outliers; candidates; exact caches
-  HIP_TRY(launch_rope_landmark(k_pre, b, S, H, C, h->inv_freq, L_full, h->min_cos, s));
+  HIP_TRY(launch_rope_landmark(k_pre, b, S, H, C, h->inv_freq, fp8, L_full, h->min_cos, s));
   HIP_TRY(launch_outliers(h->min_cos, P, n_c, n_c - h->n_win, O, h->keys, h->outlier_ids, s));
-  HIP_TRY(launch_candidates(L_full, h->outlier_ids, P, n_c, n_c - h->n_win, O, cap, h->L, h->cand_map, s));
+  HIP_TRY(launch_candidates(L_full, h->outlier_ids, P, n_c, n_c - h->n_win, O, cap, lrow, h->L, h->cand_map, s));
   HIP_TRY(launch_static_gather(k_pre, v_dev, h->outlier_ids, b, S, H, C, O, c.window, h->inv_freq,
                                h->k_out, h->v_out, h->k_win, h->v_win, s));
   // low-rank factors
@@ -659,9 +678,16 @@ skv_status skv_export_state(const skv_layer* hc, const skv_state_host* d) {
             d->B[(((size_t)bi * H + hh) * r + k) * kHeadDim + dd] =
                 bt[((size_t)bi * HD + hh * kHeadDim + dd) * r + k];
   }
-  if (d->landmarks)
+  if (d->landmarks && c.landmark_format == SKV_LANDMARKS_FP8_E5M2) {
+    // FP8 bytes widened to bf16 (every E5M2 value is a bf16 value)
+    std::vector<uint8_t> l8((size_t)P * h->n_cand0 * kHeadDim);
+    HIP_TRY(hipMemcpy2D(l8.data(), (size_t)h->n_cand0 * kHeadDim, h->L, (size_t)h->cand_cap * kHeadDim,
+                        (size_t)h->n_cand0 * kHeadDim, P, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < l8.size(); i++) d->landmarks[i] = e5m2_to_bf16(l8[i]);
+  } else if (d->landmarks) {
     HIP_TRY(hipMemcpy2D(d->landmarks, (size_t)h->n_cand0 * kHeadDim * 2, h->L, (size_t)h->cand_cap * kHeadDim * 2,
                         (size_t)h->n_cand0 * kHeadDim * 2, P, hipMemcpyDeviceToHost));
+  }
   if (d->cand_ids)
     HIP_TRY(hipMemcpy2D(d->cand_ids, (size_t)h->n_cand0 * 4, h->cand_map, (size_t)h->cand_cap * 4,
                         (size_t)h->n_cand0 * 4, P, hipMemcpyDeviceToHost));

@@ -25,6 +25,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// float -> FP8 E5M2 byte (1 sign, 5 exponent bits with bias 15, 2 mantissa bits),
+// round to nearest, ties to even; below 2^-14 the values are multiples of 2^-16;
+// magnitudes that round past 57344 give inf.  Inputs are finite.
+__device__ __forceinline__ uint8_t f32_to_e5m2(float f) {
+  const uint32_t sign = (__float_as_uint(f) >> 24) & 0x80u;
+  const float x = fabsf(f);
+  if (x < 0x1p-14f) return (uint8_t)(sign | (uint32_t)rintf(x * 65536.0f));   // 4 -> smallest normal
+  uint32_t v = __float_as_uint(x);
+  v += 0xfffffu + ((v >> 21) & 1u);              // round the 21 dropped mantissa bits
+  const int e = (int)(v >> 23) - 127 + 15;
+  if (e >= 31) return (uint8_t)(sign | 0x7cu);   // inf
+  return (uint8_t)(sign | ((uint32_t)e << 2) | ((v >> 21) & 3u));
+}
+
 // Unpack 8 bf16 held in a 16-byte word into floats.
 __device__ __forceinline__ void unpack8(const u32x4 w, float* x) {
 #pragma unroll

@@ -11,7 +11,8 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxTopK = 4096;
 constexpr int kSelLdsMax = 150 * 1024;   // dynamic LDS of the select kernel
 constexpr int kMaxSplits = 1024;         // attention workgroups per pair
-constexpr int kScoreRows = 128;          // candidate landmarks per score workgroup
+constexpr int kScoreRows = 128;          // candidate landmarks per score workgroup (bf16)
+constexpr int kScoreRows8 = 256;         // the same for FP8 landmarks (the same 32 KB)
 constexpr int kPartStride = kHeadDim + 4; // floats per attention partial row: o[d], m, l, 2 pad (16-B rows)
 
 // Everything a decode step touches, by value into the kernels.
@@ -19,6 +20,7 @@ struct DecodeArgs {
   int batch, n_kv, group, chunk, top_k, n_outlier, n_win_units, n_cand;
   int cand_stride;            // rows per pair of L and cand_map (candidate capacity)
   int n_c;                    // chunks of the pre-filled context (S / C)
+  int landmark_format;        // SKV_LANDMARKS_BF16 or SKV_LANDMARKS_FP8_E5M2
   int n_new_tokens, n_new_units, max_new;   // appended tokens, their units, capacity
   int n_fold;                 // appended chunks folded into the candidates (low-rank mode)
   int64_t seq_len;
@@ -31,7 +33,7 @@ struct DecodeArgs {
   const double* inv_freq;     // [64]
   // inputs / state
   const uint16_t* q;          // [b][Hq][d]
-  const uint16_t* L;          // [P][cand_stride][d], first n_cand rows in use
+  const uint16_t* L;          // [P][cand_stride][d] bf16 (bytes for FP8), first n_cand rows in use
   const int32_t* cand_map;    // [P][cand_stride]
   const uint16_t* A;          // [b][a_rows][r]
   const uint16_t* Bt;         // [b][Hkv*d][r]
@@ -74,13 +76,16 @@ struct DecodeArgs {
 };
 
 // ---- build launchers (build_kernels.hip); all enqueue on `st`
+// L_full: [P][n_c][d] bf16, or bytes with fp8 (FP8 E5M2)
 hipError_t launch_rope_landmark(const uint16_t* k_pre, int b, int64_t S, int H, int C,
-                                const double* inv_freq, uint16_t* L_full, float* min_cos,
+                                const double* inv_freq, bool fp8, void* L_full, float* min_cos,
                                 hipStream_t st);
 hipError_t launch_outliers(const float* min_cos, int P, int n_c, int n_elig, int O,
                            uint32_t* key_scratch, int32_t* outlier_ids, hipStream_t st);
-hipError_t launch_candidates(const uint16_t* L_full, const int32_t* outlier_ids, int P, int n_c,
-                             int n_elig, int O, int stride, uint16_t* L, int32_t* cand_map, hipStream_t st);
+// rows of row_bytes (256 bf16, 128 FP8)
+hipError_t launch_candidates(const void* L_full, const int32_t* outlier_ids, int P, int n_c,
+                             int n_elig, int O, int stride, int row_bytes, void* L, int32_t* cand_map,
+                             hipStream_t st);
 hipError_t launch_static_gather(const uint16_t* k_pre, const uint16_t* v, const int32_t* outlier_ids,
                                 int b, int64_t S, int H, int C, int O, int W, const double* inv_freq,
                                 uint16_t* k_out, uint16_t* v_out, uint16_t* k_win, uint16_t* v_win,

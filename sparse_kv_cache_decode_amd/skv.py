@@ -20,6 +20,8 @@ SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_SHAPE, SKV_ERR_UNSUPPORTED = 0, 1, 2, 3
 SKV_ERR_OOM, SKV_ERR_HIP, SKV_ERR_STATE, SKV_ERR_INTERNAL = 4, 5, 6, 7
 SKV_VALUES_DEVICE, SKV_VALUES_HOST = 0, 1
 SKV_NEW_EXACT, SKV_NEW_LOWRANK = 0, 1
+SKV_LANDMARKS_BF16, SKV_LANDMARKS_FP8_E5M2 = 0, 1
+LANDMARK_FORMATS = {"bf16": SKV_LANDMARKS_BF16, "e5m2": SKV_LANDMARKS_FP8_E5M2}
 
 EXPORTED = ["skv_build", "skv_decode_step", "skv_append_token", "skv_get_stats", "skv_reset_temporal_cache",
             "skv_export_state", "skv_set_timing", "skv_get_timing", "skv_destroy",
@@ -33,7 +35,7 @@ class SkvConfig(ctypes.Structure):
                 ("seq_len", ctypes.c_int64), ("rank", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_outlier", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("value_placement", ctypes.c_int32), ("rope_theta", ctypes.c_double),
-                ("temporal_cache", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("temporal_cache", ctypes.c_int32), ("landmark_format", ctypes.c_int32),
                 ("max_new_tokens", ctypes.c_int32), ("new_token_mode", ctypes.c_int32)]
 
 
@@ -101,10 +103,12 @@ def skv_abi_version() -> int:
 
 def make_config(shape, value_placement: int = SKV_VALUES_DEVICE, temporal_cache: int = 1,
                 max_new_tokens: int = 0, new_token_mode: int = SKV_NEW_EXACT) -> SkvConfig:
-    """skv_config from any object with the ShadowKV shape fields."""
+    """skv_config from any object with the ShadowKV shape fields (landmark
+    storage from its optional ``landmark_format``: "bf16" or "e5m2")."""
+    fmt = LANDMARK_FORMATS[getattr(shape, "landmark_format", "bf16")]
     return SkvConfig(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                      shape.seq_len, shape.rank, shape.chunk, shape.top_k, shape.n_outlier,
-                     shape.window, value_placement, float(shape.rope_theta), temporal_cache, 0,
+                     shape.window, value_placement, float(shape.rope_theta), temporal_cache, fmt,
                      max_new_tokens, new_token_mode)
 
 

@@ -64,6 +64,7 @@ class Shape:
     rope_theta: float = 500000.0
     rho: float = 0.95
     noise: float = 0.05
+    landmark_format: str = "bf16"   # landmark storage: "bf16" or "e5m2" (FP8)
 
     @property
     def group(self) -> int:

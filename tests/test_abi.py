@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert skv.skv_abi_version() == 3
+    assert skv.skv_abi_version() == 4
     seen = set()
     for code in range(8):
         s = skv.skv_status_string(code)
@@ -69,7 +69,7 @@ def _cfg(**kw):
     (dict(rope_theta=0.0), skv.SKV_ERR_SHAPE),
     (dict(value_placement=2), skv.SKV_ERR_INVALID_ARG),
     (dict(temporal_cache=3), skv.SKV_ERR_INVALID_ARG),
-    (dict(reserved=1), skv.SKV_ERR_INVALID_ARG),
+    (dict(landmark_format=2), skv.SKV_ERR_INVALID_ARG),
     (dict(batch=0), skv.SKV_ERR_SHAPE),
     (dict(max_new_tokens=-1), skv.SKV_ERR_SHAPE),
     (dict(new_token_mode=2), skv.SKV_ERR_INVALID_ARG),
@@ -114,7 +114,7 @@ int main(void) {
   printf("skv_config %zu\nskv_stats %zu\nskv_state_host %zu\n", sizeof(skv_config),
          sizeof(skv_stats), sizeof(skv_state_host));
   P(skv_config, seq_len) P(skv_config, rope_theta) P(skv_config, temporal_cache)
-  P(skv_config, reserved) P(skv_config, max_new_tokens) P(skv_config, new_token_mode)
+  P(skv_config, landmark_format) P(skv_config, max_new_tokens) P(skv_config, new_token_mode)
   P(skv_stats, last_alpha) P(skv_stats, last_host_bytes) P(skv_stats, new_tokens)
   P(skv_state_host, eigvals)
   return 0;
@@ -133,7 +133,7 @@ int main(void) {
     for key, (cls, field) in {"skv_config.seq_len": (skv.SkvConfig, "seq_len"),
                               "skv_config.rope_theta": (skv.SkvConfig, "rope_theta"),
                               "skv_config.temporal_cache": (skv.SkvConfig, "temporal_cache"),
-                              "skv_config.reserved": (skv.SkvConfig, "reserved"),
+                              "skv_config.landmark_format": (skv.SkvConfig, "landmark_format"),
                               "skv_config.max_new_tokens": (skv.SkvConfig, "max_new_tokens"),
                               "skv_config.new_token_mode": (skv.SkvConfig, "new_token_mode"),
                               "skv_stats.new_tokens": (skv.SkvStats, "new_tokens"),

@@ -1,0 +1,46 @@
+"""FP8 (E5M2) landmark storage against the oracle, which rounds its fp64 chunk
+means with the same format (ShadowKV paper, Appendix A.4 precision study,
+Tables 9 and 10; the format is torch.float8_e5m2).  Build: every landmark the
+oracle's value or one E5M2 spacing away; decode: the usual bars with the oracle
+scoring the landmarks the GPU built (the rule and its reason are in
+tests/parity.py)."""
+import pytest
+
+from sparse_kv_cache_decode_amd import skv, synth
+from tests.test_gpu_append import _run_append
+from tests.test_gpu_parity import _run, _small
+
+pytestmark = pytest.mark.gpu
+
+
+def test_fp8_tiny_8k_end_to_end():
+    _run(synth.SHAPES["tiny_8k"].replace(landmark_format="e5m2"), steps=4)
+
+
+def test_fp8_ragged_blocks_two_batches():
+    # n_cand = 1012 = 3 * 256 + 244: the last 256-landmark block is ragged
+    _run(_small(landmark_format="e5m2"), steps=3)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (32, 4), (32, 2)])
+def test_fp8_group_sizes(hq, hkv):
+    _run(_small(n_q_heads=hq, n_kv_heads=hkv, batch=1, seq_len=4096, top_k=9, n_outlier=2,
+                rank=48, latent_rank=48, landmark_format="e5m2"), steps=2)
+
+
+def test_fp8_chunk_four_host_values():
+    _run(_small(chunk=4, window=32, landmark_format="e5m2"), steps=2, placement=skv.SKV_VALUES_HOST)
+
+
+def test_fp8_split_selection():
+    # 34809 candidates: selection in parts and a merge, scores from 136 FP8 blocks
+    s = _small(batch=1, n_q_heads=2, n_kv_heads=1, seq_len=278528, rank=16, latent_rank=16,
+               top_k=64, n_outlier=3, landmark_format="e5m2")
+    _run(s, steps=2)
+
+
+def test_fp8_lowrank_folds_generated_chunks():
+    # folded chunks get E5M2 landmarks too (the mean of their stored exact keys)
+    layer, _, _ = _run_append(_small(window=16, landmark_format="e5m2"), skv.SKV_NEW_LOWRANK,
+                              [0, 9, 20, 15], max_new=48)
+    layer.close()

@@ -19,7 +19,7 @@ import torch
 
 from oracle import shadowkv as O
 from sparse_kv_cache_decode_amd import skv, synth
-from tests.parity import bits, check_build, check_ids, check_out, reference_out
+from tests.parity import adopt_landmarks, bits, check_build, check_ids, check_out, reference_out
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,7 @@ def test_one_layer_sampled(name, sampled):
         print(f"[fullsize] oracle build, batch element {b}", flush=True)
         st = O.build(O.config_from(one), bits(k[b:b + 1]), bits(v[b:b + 1]))
         check_build(_slice_state(ex, b), st)
+        adopt_landmarks(st, _slice_state(ex, b))
         prev = None
         worst = (0.0, 0.0)
         for t in range(STEPS):

@@ -6,7 +6,7 @@ import torch
 
 from oracle import shadowkv as O
 from sparse_kv_cache_decode_amd import skv, synth
-from tests.parity import bits, check_build, check_ids, check_out, reference_out
+from tests.parity import adopt_landmarks, bits, check_build, check_ids, check_out, reference_out
 
 pytestmark = pytest.mark.gpu
 
@@ -15,7 +15,8 @@ def _run(shape, steps, placement=skv.SKV_VALUES_DEVICE, temporal=1, seed=0, mode
          check_state=True, keep=False):
     print(f"[parity] {shape.name} b={shape.batch} S={shape.seq_len} G={shape.group} "
           f"C={shape.chunk} K={shape.top_k} O={shape.n_outlier} r={shape.rank} "
-          f"placement={placement} temporal={temporal} steps={steps}", flush=True)
+          f"landmarks={shape.landmark_format} placement={placement} temporal={temporal} steps={steps}",
+          flush=True)
     k, v = synth.layer_cache_np(shape, 0, seed)
     q = synth.queries_np(shape, k, 0, steps, seed, mode=mode)
     st = O.build(O.config_from(shape), bits(k), bits(v))
@@ -27,8 +28,11 @@ def _run(shape, steps, placement=skv.SKV_VALUES_DEVICE, temporal=1, seed=0, mode
         vd = v.cuda()
     layer = skv.Layer(shape, kd, vd, placement, temporal)
     del kd
-    if check_state:
-        check_build(layer.export(), st)
+    if check_state or shape.landmark_format != "bf16":
+        ex = layer.export()
+        if check_state:
+            check_build(ex, st)
+        adopt_landmarks(st, ex)
     prev, prev_gpu, prev_differ = None, None, True
     worst = (0.0, 0.0)
     swaps = 0

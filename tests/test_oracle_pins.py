@@ -58,6 +58,27 @@ def test_bf16_bits_decode_matches_torch():
     np.testing.assert_array_equal(O.bf16_bits_to_f64(bits), t.to(torch.float64).numpy())
 
 
+def test_round_e5m2_matches_torch_float8_e5m2():
+    # normal and subnormal magnitudes (2^-18 .. 2^15); torch's conversion is
+    # from float32, so the inputs are float32 values
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(40000) * np.exp2(rng.uniform(-18, 15, 40000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_e5m2(x.astype(np.float64)), ref)
+
+
+def test_round_e5m2_hand_cases():
+    r = lambda v: float(O.round_e5m2(np.array([v]))[0])
+    assert r(1.0 + 2 ** -3) == 1.0                  # halfway between 1 and 1.25: even (1.0)
+    assert r(1.0 + 3 * 2 ** -3) == 1.5              # halfway between 1.25 and 1.5: even (1.5)
+    assert r(-1.3) == -1.25
+    assert r(2 ** -14) == 2 ** -14                  # smallest normal
+    assert r(3 * 2 ** -17) == 2 * 2 ** -16          # subnormal spacing 2^-16, tie to even
+    assert r(57344.0) == 57344.0 and r(-61439.0) == -57344.0
+    assert r(61440.0) == np.inf                     # halfway past the largest: rounds up, overflows
+    assert r(0.0) == 0.0
+
+
 # ---------------------------------------------------------------- RoPE
 
 def test_rope_closed_forms():
