@@ -10,13 +10,17 @@ Bars (floating point from bf16 storage with fp32 accumulation):
   tie rule;
 * hit counts exact against the oracle whenever the selections agree, and always
   equal to |I_t & I_{t-1}| of the GPU's own consecutive selections;
-* FP8 (E5M2) landmarks: each value equal to the oracle's or one E5M2 spacing
-  away (the GPU rounds an fp32 mean of fp32-rotated keys, the oracle an fp64
-  one, so a mean that falls near a rounding boundary may go either way), with
-  at most 1 in 1000 values differing.  With 2 mantissa bits, one such value
-  moves a landmark's score by up to 1/8 of one of its 128 terms, which can
-  exceed the near-tie margin; decode parity therefore runs the oracle on the
-  landmarks the GPU built (adopt_landmarks), once they have passed this bar.
+* landmarks: each value equal to the oracle's or one spacing of the storage
+  format away (bf16, or E5M2 with FP8 storage), with at most 1 in 1000 values
+  differing: the GPU rounds an fp32 mean of fp32-rotated keys, the oracle an
+  fp64 one, so a mean that falls near a rounding boundary may go either way.
+  One such bf16 value moves a landmark's logit by up to 2^-8 of one of its 128
+  terms (1/8 of it for E5M2), which exceeds the near-tie margin at the K-th
+  score (seen: 1.3e-3 at K = 60 of 8178 candidates); decode parity therefore
+  runs the oracle on the landmarks the GPU built (adopt_landmarks), once they
+  have passed this bar, and the tie margin then covers the fp32 arithmetic of
+  the decode step alone (logit error at most 128 * 2^-24 * sum|q_d L_d| / sqrt(d),
+  about 2e-4 at the workloads' magnitudes).
 """
 from __future__ import annotations
 
@@ -28,7 +32,7 @@ from oracle import shadowkv as O
 TIE_REL = 1e-3
 MAX_ABS = 2e-2
 REL_L2 = 5e-3
-E5M2_DIFF_FRACTION = 1e-3
+LANDMARK_DIFF_FRACTION = 1e-3
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -108,10 +112,8 @@ def e5m2_close(gpu_bits: np.ndarray, ref: np.ndarray) -> tuple[float, float]:
 
 
 def adopt_landmarks(st: O.State, gpu: dict) -> None:
-    """FP8 storage: run the oracle's decode on the landmarks the GPU built (see
-    the module docstring); a no-op for bf16 storage."""
-    if st.cfg.landmark_format == "e5m2":
-        st.L = O.bf16_bits_to_f64(gpu["landmarks"]).reshape(st.L.shape)
+    """Run the oracle's decode on the landmarks the GPU built (module docstring)."""
+    st.L = O.bf16_bits_to_f64(gpu["landmarks"]).reshape(st.L.shape)
 
 
 def check_build(gpu: dict, st: O.State):
@@ -124,9 +126,12 @@ def check_build(gpu: dict, st: O.State):
     if cfg.landmark_format == "e5m2":
         excess, frac = e5m2_close(gpu["landmarks"], st.L)
         assert excess <= 0, f"FP8 landmark off by more than one spacing ({excess})"
-        assert frac <= E5M2_DIFF_FRACTION, f"{frac:.2e} of the FP8 landmarks differ"
+        assert frac <= LANDMARK_DIFF_FRACTION, f"{frac:.2e} of the FP8 landmarks differ"
     else:
         assert bf16_close(gpu["landmarks"], st.L, 1e-5) <= 0
+        if st.L.size:
+            frac = float(np.mean(O.bf16_bits_to_f64(gpu["landmarks"]) != st.L))
+            assert frac <= LANDMARK_DIFF_FRACTION, f"{frac:.2e} of the bf16 landmarks differ"
     assert bf16_close(gpu["k_outlier"], st.K_out, 1e-5) <= 0
     assert bf16_close(gpu["k_window"], st.K_win, 1e-5) <= 0
     np.testing.assert_array_equal(O.bf16_bits_to_f64(gpu["v_outlier"]), st.V_out)
