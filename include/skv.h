@@ -67,7 +67,10 @@ typedef int32_t skv_status;
                                   gathered over PCIe on a side stream that overlaps
                                   the key rebuild                                   */
 
-/* Storage format of the landmarks (chunk means). */
+/* Storage format of the landmarks (chunk means).  FP8 follows the precision
+ * study of the paper-graph-ui summary of ShadowKV (section 5, Tables 9 and 10),
+ * which runs the method in torch.float8_e5m2; here only the landmarks, the
+ * stream that dominates a decode step's bytes, take that format. */
 #define SKV_LANDMARKS_BF16 0      /* bfloat16, 256 bytes per landmark                 */
 #define SKV_LANDMARKS_FP8_E5M2 1  /* FP8 E5M2 (1 sign, 5 exponent bits with bias 15, 2
                                      mantissa bits, the torch.float8_e5m2 format),

@@ -1,6 +1,7 @@
 """FP8 (E5M2) landmark storage against the oracle, which rounds its fp64 chunk
-means with the same format (ShadowKV paper, Appendix A.4 precision study,
-Tables 9 and 10; the format is torch.float8_e5m2).  Build: every landmark the
+means with the same format (the precision-sensitivity study in section 5 of the
+paper-graph-ui summary of ShadowKV, Tables 9 and 10, runs the method in
+torch.float8_e5m2).  Build: every landmark the
 oracle's value or one E5M2 spacing away; decode: the usual bars with the oracle
 scoring the landmarks the GPU built (the rule and its reason are in
 tests/parity.py)."""
