@@ -30,7 +30,7 @@ CALIB_BYTES = 512 << 20         # bytes read (and written) once by the counter-c
 CSRC = os.path.join(ROOT, "sparse_kv_cache_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 SCORE_KERNELS = {"bf16": "skv::score_kernel<4>", "e5m2": "skv::score_fp8_kernel<4>"}
-LANDMARK_BYTES = {"bf16": 2, "e5m2": 1}
+FORMAT_BYTES = {"bf16": 2, "e5m2": 1}
 METRIC = "decode tokens/s at S=122K batch 8 (Llama-3.1-8B shape); % HBM roofline"
 
 
@@ -265,10 +265,10 @@ def algorithmic_bytes(shape, misses_per_layer_step: float) -> dict:
     """Bytes the method must move per layer-step (HBM-resident values)."""
     d, C, r = shape.head_dim, shape.chunk, shape.rank
     P = shape.pairs
-    landmarks = P * shape.n_cand * d * LANDMARK_BYTES[shape.landmark_format]
+    landmarks = P * shape.n_cand * d * FORMAT_BYTES[shape.landmark_format]
     q_bytes = shape.batch * shape.n_q_heads * d * 2
     out_bytes = shape.batch * shape.n_q_heads * d * 4
-    rebuild = misses_per_layer_step * C * (r * 2 + d * 2) + P * r * d * 2
+    rebuild = misses_per_layer_step * C * (r * FORMAT_BYTES[shape.a_format] + d * 2) + P * r * d * 2
     attn = P * shape.tokens_attended * d * 2 * 2
     return {"score": landmarks + q_bytes, "rebuild": rebuild, "attention": attn + out_bytes,
             "total": landmarks + q_bytes + rebuild + attn + out_bytes}
@@ -293,6 +293,8 @@ def main():
                          "(exact keys, or ShadowKV+ low-rank states)")
     ap.add_argument("--landmarks", choices=["bf16", "e5m2"], default="bf16",
                     help="landmark storage: bf16 (the pages' precision) or FP8 E5M2 (their precision study)")
+    ap.add_argument("--a-format", choices=["bf16", "e5m2"], default="bf16",
+                    help="storage of the rows of A: bf16 (the pages' precision) or FP8 E5M2")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
                     help="replay each timed step (all layers) as one captured HIP graph; off: launch eagerly")
     ap.add_argument("--phase-steps", type=int, default=16,
@@ -340,8 +342,8 @@ def main():
         return 2
     if args.layers:
         shape = shape.replace(layers=args.layers)
-    if args.landmarks != "bf16":
-        shape = shape.replace(landmark_format=args.landmarks)
+    if args.landmarks != "bf16" or args.a_format != "bf16":
+        shape = shape.replace(landmark_format=args.landmarks, a_format=args.a_format)
     L, W, K = shape.layers, args.warmup, args.steps
     PH = max(1, args.phase_steps)
     total = W + K + PH            # warm-up, timed and phase-timing steps
@@ -489,12 +491,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if shape.landmark_format == "bf16" else "bf16, e5m2 landmarks (fp16 MFMA scoring)",
+        "dtype": "bf16" + ("" if shape.landmark_format == "bf16" else ", e5m2 landmarks (fp16 MFMA scoring)")
+                 + ("" if shape.a_format == "bf16" else ", e5m2 rows of A (widened to bf16 for the rebuild)"),
         "data": "synthetic",
         "config": {"workload": f"{shape.name}: {L} layers, batch {shape.batch}, S={shape.seq_len}, "
                                f"{shape.n_q_heads} q / {shape.n_kv_heads} KV heads, d={shape.head_dim}, "
                                f"r={shape.rank}, C={shape.chunk}, K={shape.top_k}, O={shape.n_outlier}, "
                                f"window {shape.window}, {shape.landmark_format} landmarks, "
+                               f"{shape.a_format} A, "
                                f"values in {'pinned host memory' if host else 'HBM'}, "
                                f"{'AR(1)-drifting' if args.queries == 'drift' else 'independent'} queries"
                                + ("" if new_mode is None else

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 4
+#define SKV_ABI_VERSION 5
 
 typedef int32_t skv_status;
 #define SKV_OK 0
@@ -67,18 +67,22 @@ typedef int32_t skv_status;
                                   gathered over PCIe on a side stream that overlaps
                                   the key rebuild                                   */
 
-/* Storage format of the landmarks (chunk means).  FP8 follows the precision
- * study of the paper-graph-ui summary of ShadowKV (section 5, Tables 9 and 10),
- * which runs the method in torch.float8_e5m2; here only the landmarks, the
- * stream that dominates a decode step's bytes, take that format. */
-#define SKV_LANDMARKS_BF16 0      /* bfloat16, 256 bytes per landmark                 */
-#define SKV_LANDMARKS_FP8_E5M2 1  /* FP8 E5M2 (1 sign, 5 exponent bits with bias 15, 2
-                                     mantissa bits, the torch.float8_e5m2 format),
-                                     128 bytes per landmark: the fp32 chunk mean is
-                                     rounded once to nearest even; scoring widens it
-                                     to fp16 exactly and multiplies it with q in fp16
-                                     (q's bf16 values are exact there while they lie
-                                     in fp16's normal range, |q| <= 65504)         */
+/* Storage formats of the landmarks (chunk means) and of the rows of A.  FP8
+ * follows the precision study of the paper-graph-ui summary of ShadowKV
+ * (section 5, Tables 9 and 10), which runs the method in torch.float8_e5m2.
+ * Here it applies to the two large stores: the landmarks (the stream that
+ * dominates a decode step's bytes) and A (S x r per batch element).  B stays
+ * bfloat16: it is about 1/100 of A's size and enters every rebuilt key (the
+ * summary's section 7 expects A to tolerate lower precision than B). */
+#define SKV_FORMAT_BF16 0      /* bfloat16                                           */
+#define SKV_FORMAT_FP8_E5M2 1  /* FP8 E5M2 (1 sign, 5 exponent bits with bias 15, 2
+                                  mantissa bits, the torch.float8_e5m2 format), each
+                                  value rounded once to nearest even from fp32.
+                                  Landmarks (128 bytes each) are widened to fp16
+                                  exactly and scored with q in fp16 (q's bf16 values
+                                  are exact there in fp16's normal range,
+                                  |q| <= 65504); rows of A (r bytes each) are widened
+                                  to bf16 exactly for the key rebuild              */
 
 /* How appended (generated) tokens keep their keys. */
 #define SKV_NEW_EXACT 0        /* post-RoPE key kept exactly (ShadowKV)             */
@@ -111,9 +115,12 @@ typedef struct skv_config {
   double rope_theta;       /* RoPE base (rotate-half pairing (i, i + d/2))        */
   int32_t temporal_cache;  /* 1: rebuild/fetch only chunks missed vs the previous
                               step; 0: rebuild every selected chunk every step     */
-  int32_t landmark_format; /* SKV_LANDMARKS_BF16 or SKV_LANDMARKS_FP8_E5M2        */
+  int32_t landmark_format; /* SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2              */
   int32_t max_new_tokens;  /* capacity for generated tokens (0: none)             */
   int32_t new_token_mode;  /* SKV_NEW_EXACT or SKV_NEW_LOWRANK                     */
+  int32_t a_format;        /* SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2 (rows of A,
+                              also those appended in SKV_NEW_LOWRANK mode)        */
+  int32_t reserved;        /* must be 0                                           */
 } skv_config;
 
 typedef struct skv_layer skv_layer;   /* opaque; owns all derived state */
@@ -134,7 +141,7 @@ typedef struct skv_stats {
 /*
  * Host copies of the built state, for inspection and parity checks.  Any
  * pointer may be NULL to skip that tensor.  Sizes (elements):
- *   A          bf16 [b][S][r]
+ *   A          bf16 [b][S][r]             (bf16 values also with FP8 storage)
  *   B          bf16 [b][H_kv][r][d]       (the per-head right factor)
  *   landmarks  bf16 [b][H_kv][n_cand][d]  (bf16 values also with FP8 storage, which
  *                                          they hold exactly; candidate chunks of the pre-filled

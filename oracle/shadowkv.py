@@ -38,7 +38,11 @@ with a zero vector is 0; stored state (A, B, landmarks, outlier and window
 keys, rebuilt keys) is rounded once to bfloat16 with round-to-nearest-even
 when ``storage_rounding`` is on; with ``landmark_format = "e5m2"`` the
 landmarks are rounded instead to FP8 E5M2 (the torch.float8_e5m2 precision of
-the summary's precision-sensitivity paragraph, section 5).  Generated tokens: the t-th appended token
+the summary's precision-sensitivity paragraph, section 5), and with
+``a_format = "e5m2"`` the rows of A likewise (context rows and the rows of
+generated tokens); B stays bfloat16 (the summary's section 7 expects A, whose
+rows are each used once per selection, to tolerate lower precision than B,
+which enters every rebuilt key).  Generated tokens: the t-th appended token
 (t = 0, 1, ...) sits at position seq_len + t and its value is kept as given.
 Exact mode (ShadowKV's assembly): every decode step attends to all of them
 with the exact key RoPE(k'), and they take no part in scoring or selection.
@@ -187,6 +191,7 @@ class Config:
     window: int
     rope_theta: float = 500000.0
     landmark_format: str = "bf16"    # storage of the landmarks: "bf16" or "e5m2" (FP8)
+    a_format: str = "bf16"           # storage of the rows of A: "bf16" or "e5m2" (FP8)
 
     @property
     def group(self):
@@ -209,7 +214,8 @@ def config_from(shape) -> Config:
     """Take the ShadowKV fields from any object carrying them."""
     return Config(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                   shape.seq_len, shape.rank, shape.chunk, shape.top_k, shape.n_outlier,
-                  shape.window, shape.rope_theta, getattr(shape, "landmark_format", "bf16"))
+                  shape.window, shape.rope_theta, getattr(shape, "landmark_format", "bf16"),
+                  getattr(shape, "a_format", "bf16"))
 
 
 @dataclasses.dataclass
@@ -236,6 +242,11 @@ class State:
     def keep(self, x):
         return round_bf16(x) if self.storage_rounding else x
 
+    def keep_a(self, x):
+        if not self.storage_rounding:
+            return x
+        return round_e5m2(x) if self.cfg.a_format == "e5m2" else round_bf16(x)
+
     def keep_landmark(self, x):
         if not self.storage_rounding:
             return x
@@ -256,12 +267,13 @@ def build(cfg: Config, k_pre, v, storage_rounding: bool = True) -> State:
     n_c, n_elig = cfg.n_chunks, cfg.n_chunks - cfg.n_win_chunks
     rnd = round_bf16 if storage_rounding else (lambda x: x)
     rnd_l = (round_e5m2 if cfg.landmark_format == "e5m2" else round_bf16) if storage_rounding else (lambda x: x)
+    rnd_a = (round_e5m2 if cfg.a_format == "e5m2" else round_bf16) if storage_rounding else (lambda x: x)
     pos = np.arange(S)
 
     As, Bs, sigs, Ls, cands, outs, mcs, kos, vos, kws, vws = ([] for _ in range(11))
     for bi in range(b):
         a, bm, sig = truncated_svd(k_pre[bi], cfg.rank, H)
-        As.append(rnd(a)); Bs.append(rnd(bm)); sigs.append(sig)
+        As.append(rnd_a(a)); Bs.append(rnd(bm)); sigs.append(sig)
         kr = apply_rope(k_pre[bi].reshape(S, H, d).transpose(1, 0, 2), pos, cfg.rope_theta)
         lm = landmarks(kr, C)                      # [H, n_c, d]
         mc = chunk_min_cos(kr, lm, C)              # [H, n_c]
@@ -313,7 +325,7 @@ def append(st: State, k_new, v_new, lowrank: bool = False) -> None:
         st.V_new = vals if st.V_new is None else np.concatenate([st.V_new, vals], axis=2)
         return
     # the low-rank state joins A, the value joins the value store
-    a_rows = np.stack([st.keep(k_new[bi] @ psi_t(st, bi).T) for bi in range(b)])[:, None]
+    a_rows = np.stack([st.keep_a(k_new[bi] @ psi_t(st, bi).T) for bi in range(b)])[:, None]
     st.A = np.concatenate([st.A, a_rows], axis=1)
     st.V = np.concatenate([st.V, vals], axis=2)
     # the exact region grows by the new token; a completed chunk pushes the

@@ -346,11 +346,13 @@ hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batc
 }
 
 // ---------------------------------------------------------------------------
-// Projection A[b] = K_b Psi_b (S x HD times HD x r), fp32 accumulation, bf16 out.
+// Projection A[b] = K_b Psi_b (S x HD times HD x r), fp32 accumulation, bf16 out
+// (FP8 E5M2 bytes with fp8).
 
 __global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict__ k_pre,
                                                       const float* __restrict__ psi, int64_t S,
-                                                      int HD, int r, int64_t a_rows, uint16_t* __restrict__ A) {
+                                                      int HD, int r, int64_t a_rows, bool fp8,
+                                                      void* __restrict__ A) {
   __shared__ float tk[32][64 + 1];   // [k][row]
   __shared__ float tp[32][64 + 1];   // [k][col]
   const int b = blockIdx.z;
@@ -400,15 +402,20 @@ __global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const int col = n0 + tx * 4 + q;
-      if (col < r) A[((int64_t)b * a_rows + row) * r + col] = f32_to_bf16(acc[p][q]);
+      if (col >= r) continue;
+      const int64_t at = ((int64_t)b * a_rows + row) * r + col;
+      if (fp8)
+        static_cast<uint8_t*>(A)[at] = f32_to_e5m2(acc[p][q]);
+      else
+        static_cast<uint16_t*>(A)[at] = f32_to_bf16(acc[p][q]);
     }
   }
 }
 
 hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_t S, int HD, int r,
-                          int64_t a_rows, uint16_t* A, hipStream_t st) {
+                          int64_t a_rows, bool fp8, void* A, hipStream_t st) {
   dim3 grid((unsigned)((S + 63) / 64), (r + 63) / 64, b);
-  project_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, a_rows, A);
+  project_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, a_rows, fp8, A);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@
 // gfx950 write back and invalidate the whole L2, so every cross-workgroup
 // hand-off goes through a kernel boundary instead.
 #include <algorithm>
+#include <type_traits>
 
 #include "skv_internal.h"
 #include "skv_select.h"
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(DecodeArgs a) {
 
 hipError_t launch_score(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.nb_score, a.batch * a.n_kv);
-  const bool fp8 = a.landmark_format == SKV_LANDMARKS_FP8_E5M2;
+  const bool fp8 = a.landmark_format == SKV_FORMAT_FP8_E5M2;
   switch (a.group) {
     case 1: fp8 ? score_fp8_kernel<1><<<grid, 256, 0, st>>>(a) : score_kernel<1><<<grid, 256, 0, st>>>(a); break;
     case 2: fp8 ? score_fp8_kernel<2><<<grid, 256, 0, st>>>(a) : score_kernel<2><<<grid, 256, 0, st>>>(a); break;
@@ -727,16 +728,43 @@ __device__ __forceinline__ void stage_reads(uint32_t addr, u32x4 (&bw)[4]) {
       : "v"(addr), "i"(O), "i"(O + T), "i"(O + 2 * T), "i"(O + 3 * T));
 }
 
-template <int Q, int H>
-__device__ __forceinline__ void mfma_half(const u32x4 (&a)[2], bool kin, uint32_t baddr, f32x4 (&acc)[2][8]) {
+// 8 FP8 E5M2 values (bytes of lo, then hi) -> 8 bf16, exactly: the byte is the
+// high byte of the equal fp16, widened to fp32 and cut to its high half.
+__device__ __forceinline__ u32x4 e5m2x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const u32x4 h = e5m2x8_to_f16x8(lo, hi);
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float f0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(h[i] & 0xffffu));
+    const float f1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(h[i] >> 16));
+    o[i] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+  }
+  return o;
+}
+
+// An A fragment as the MFMA takes it: 8 bf16 as loaded, or widened from 8 FP8
+// bytes.  The empty volatile asm pins the widening after the explicit load waits
+// (without it the compiler hoists it next to the loads and waits for all of them).
+__device__ __forceinline__ u32x4 a_operand(const u32x4& v) { return v; }
+__device__ __forceinline__ u32x4 a_operand(const uint2& v) {
+  uint32_t lo = v.x, hi = v.y;
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  return e5m2x8_to_bf16x8(lo, hi);
+}
+
+template <int Q, int H, class AF>
+__device__ __forceinline__ void mfma_half(const AF (&a)[2], bool kin, uint32_t baddr, f32x4 (&acc)[2][8]) {
   u32x4 bw[4];
   stage_reads<Q, H>(baddr, bw);
+  u32x4 av[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) av[mt] = a_operand(a[mt]);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const bf16x8 bfr = __builtin_bit_cast(bf16x8, kin ? bw[i] : (u32x4){0u, 0u, 0u, 0u});
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
-      acc[mt][H * 4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt]), bfr,
+      acc[mt][H * 4 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[mt]), bfr,
                                                                    acc[mt][H * 4 + i], 0, 0, 0);
   }
 }
@@ -744,16 +772,17 @@ __device__ __forceinline__ void mfma_half(const u32x4 (&a)[2], bool kin, uint32_
 // k-step Q of a slice: wait for load groups 0..Q of every wave, then 16 MFMAs.
 // A fragments are used as loaded (rows past the misses hold finite data and are
 // never stored); B^T pieces past kn are zeroed, which cancels the k-padding.
-template <int NSTEP, int Q>
-__device__ __forceinline__ void mfma_steps(const u32x4 (&af)[NSTEP][2], int kn, int lk, uint32_t baddr,
+template <int NSTEP, int Q, class AF>
+__device__ __forceinline__ void mfma_steps(const AF (&af)[NSTEP][2], int kn, int lk, uint32_t baddr,
                                            f32x4 (&acc)[2][8]) {
   __builtin_amdgcn_sched_barrier(0);             // step Q-1's MFMAs stay ahead of this wait
   wait_load_groups(NSTEP - 1 - Q);               // this wave's groups 0..Q have landed
   __builtin_amdgcn_s_barrier();                  // ... and every other wave's
+  __builtin_amdgcn_sched_barrier(0);             // nothing that reads them moves above the waits
   const bool kin = Q * 32 + lk * 8 < kn;
   mfma_half<Q, 0>(af[Q], kin, baddr, acc);
   mfma_half<Q, 1>(af[Q], kin, baddr, acc);
-  if constexpr (Q + 1 < NSTEP) mfma_steps<NSTEP, Q + 1>(af, kn, lk, baddr, acc);
+  if constexpr (Q + 1 < NSTEP) mfma_steps<NSTEP, Q + 1, AF>(af, kn, lk, baddr, acc);
 }
 
 // Staging buffer of one rebuild tile: B^T pieces of NSTEP k-steps, later the
@@ -769,7 +798,8 @@ constexpr int rebuild_stage_bytes() {
 // before a barrier) and `stage` an LDS buffer of rebuild_stage_bytes<NSTEP>().
 // Returns once the stores are issued; the caller orders them against later
 // readers.
-template <int C, int NSTEP>
+// A8: rows of A stored as FP8 E5M2 (r bytes per row) instead of bf16.
+template <int C, int NSTEP, bool A8>
 __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const int* mchunk, const int* mslot,
                                              u32x4* stage) {
   const int b = p / a.n_kv, h = p % a.n_kv;
@@ -780,16 +810,16 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
 #pragma unroll
   for (int nt = 0; nt < 4; nt++) ffreq[nt] = a.inv_freq[nt * 16 + lr];
   const uint16_t* Bt = a.Bt + ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
-  const uint16_t* Ab = a.A + (int64_t)b * a.a_rows * r;
+  const int64_t Ab = (int64_t)b * a.a_rows * r;   // element offset of the batch element's A
   // A operand rows of this lane: row m = w*32 + mt*16 + lr (rows past the misses
   // read row 0 of the batch element; their outputs are not stored)
-  const uint16_t* arow[2];
+  int64_t arow[2];
   int64_t pos0[2];   // position of this lane's first output row of each tile
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     const int m = w * 32 + mt * 16 + lr;
     const int ch = mchunk[m / C];
-    arow[mt] = ch >= 0 ? Ab + ((int64_t)ch * C + (m % C)) * r : Ab;
+    arow[mt] = ch >= 0 ? Ab + ((int64_t)ch * C + (m % C)) * r : Ab;   // element offsets
     const int m0 = w * 32 + mt * 16 + lk * 4;
     pos0[mt] = (int64_t)max(mchunk[m0 / C], 0) * C + (m0 % C);
   }
@@ -817,7 +847,8 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
   for (int ks = 0; ks < r; ks += NSTEP * 32) {
     const int kn = min(NSTEP * 32, r - ks);
     if (ks > 0) __syncthreads();                 // previous slice fully consumed
-    u32x4 af[NSTEP][2];
+    using AFrag = typename std::conditional<A8, uint2, u32x4>::type;
+    AFrag af[NSTEP][2];
 #pragma unroll
     for (int q = 0; q < NSTEP; q++) {
 #pragma unroll
@@ -832,11 +863,14 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
 #pragma unroll
       for (int mt = 0; mt < 2; mt++) {
         const int kk = q * 32 + lk * 8 < kn ? ks + q * 32 + lk * 8 : ks;
-        af[q][mt] = *reinterpret_cast<const u32x4*>(arow[mt] + kk);
+        if constexpr (A8)
+          af[q][mt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.A) + arow[mt] + kk);
+        else
+          af[q][mt] = *reinterpret_cast<const u32x4*>(a.A + arow[mt] + kk);
       }
       __builtin_amdgcn_sched_barrier(0);         // keep the groups in issue order
     }
-    mfma_steps<NSTEP, 0>(af, kn, lk, baddr, acc);
+    mfma_steps<NSTEP, 0, AFrag>(af, kn, lk, baddr, acc);
   }
   __syncthreads();
   // epilogue: RoPE on (col, col + 64) pairs, bf16 rows staged in LDS
@@ -868,7 +902,7 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
   }
 }
 
-template <int C, int NSTEP>
+template <int C, int NSTEP, bool A8>
 __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
   __shared__ u32x4 stage[rebuild_stage_bytes<NSTEP>() / 16];
@@ -890,31 +924,37 @@ __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
-  rebuild_tile<C, NSTEP>(a, p, mchunk, mslot, stage);
+  rebuild_tile<C, NSTEP, A8>(a, p, mchunk, mslot, stage);
 }
 
-template <int C>
+template <int C, bool A8>
 static hipError_t launch_rebuild_c(const DecodeArgs& a, dim3 grid, hipStream_t st) {
   switch (min(kMaxSteps, (a.rank + 31) / 32)) {
-    case 1: rebuild_kernel<C, 1><<<grid, 256, 0, st>>>(a); break;
-    case 2: rebuild_kernel<C, 2><<<grid, 256, 0, st>>>(a); break;
-    case 3: rebuild_kernel<C, 3><<<grid, 256, 0, st>>>(a); break;
-    case 4: rebuild_kernel<C, 4><<<grid, 256, 0, st>>>(a); break;
-    case 5: rebuild_kernel<C, 5><<<grid, 256, 0, st>>>(a); break;
-    default: rebuild_kernel<C, kMaxSteps><<<grid, 256, 0, st>>>(a); break;
+    case 1: rebuild_kernel<C, 1, A8><<<grid, 256, 0, st>>>(a); break;
+    case 2: rebuild_kernel<C, 2, A8><<<grid, 256, 0, st>>>(a); break;
+    case 3: rebuild_kernel<C, 3, A8><<<grid, 256, 0, st>>>(a); break;
+    case 4: rebuild_kernel<C, 4, A8><<<grid, 256, 0, st>>>(a); break;
+    case 5: rebuild_kernel<C, 5, A8><<<grid, 256, 0, st>>>(a); break;
+    default: rebuild_kernel<C, kMaxSteps, A8><<<grid, 256, 0, st>>>(a); break;
   }
   return hipGetLastError();
+}
+
+template <bool A8>
+static hipError_t launch_rebuild_a(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.chunk) {
+    case 4: return launch_rebuild_c<4, A8>(a, grid, st);
+    case 8: return launch_rebuild_c<8, A8>(a, grid, st);
+    case 16: return launch_rebuild_c<16, A8>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st) {
   const int mpb = kRebuildRows / a.chunk;
   dim3 grid(((a.top_k + mpb - 1) / mpb) * a.batch * a.n_kv);
-  switch (a.chunk) {
-    case 4: return launch_rebuild_c<4>(a, grid, st);
-    case 8: return launch_rebuild_c<8>(a, grid, st);
-    case 16: return launch_rebuild_c<16>(a, grid, st);
-    default: return hipErrorInvalidValue;
-  }
+  return a.a_format == SKV_FORMAT_FP8_E5M2 ? launch_rebuild_a<true>(a, grid, st)
+                                            : launch_rebuild_a<false>(a, grid, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1011,7 +1051,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_project_kernel(DecodeAr
       for (int pt = 0; pt < parts; pt++) sum += red2[pt * r + j];
     else
       for (int gg = 0; gg < ng; gg++) sum += red[gg * r + j];
-    A[((int64_t)b * a.a_rows + a.seq_len + t) * r + j] = f32_to_bf16(sum);
+    const int64_t at = ((int64_t)b * a.a_rows + a.seq_len + t) * r + j;
+    if (a.a_format == SKV_FORMAT_FP8_E5M2)
+      reinterpret_cast<uint8_t*>(A)[at] = f32_to_e5m2(sum);
+    else
+      A[at] = f32_to_bf16(sum);
   }
 }
 
@@ -1031,7 +1075,7 @@ __global__ __launch_bounds__(kHeadDim) void fold_kernel(DecodeArgs a, uint16_t* 
   float sum = 0.f;
   for (int i = 0; i < C; i++) sum += bf16_to_f32(src[i * kHeadDim + dim]);
   const int64_t at = ((int64_t)p * a.cand_stride + a.n_cand) * kHeadDim + dim;
-  if (a.landmark_format == SKV_LANDMARKS_FP8_E5M2)
+  if (a.landmark_format == SKV_FORMAT_FP8_E5M2)
     reinterpret_cast<uint8_t*>(L)[at] = f32_to_e5m2(sum * (1.0f / C));
   else
     L[at] = f32_to_bf16(sum * (1.0f / C));

@@ -116,8 +116,10 @@ uint16_t e5m2_to_bf16(uint8_t v) {
 
 skv_status validate(const skv_config* c) {
   if (!c) return SKV_ERR_INVALID_ARG;
-  if (c->landmark_format != SKV_LANDMARKS_BF16 && c->landmark_format != SKV_LANDMARKS_FP8_E5M2)
+  if (c->landmark_format != SKV_FORMAT_BF16 && c->landmark_format != SKV_FORMAT_FP8_E5M2)
     return SKV_ERR_INVALID_ARG;
+  if (c->a_format != SKV_FORMAT_BF16 && c->a_format != SKV_FORMAT_FP8_E5M2) return SKV_ERR_INVALID_ARG;
+  if (c->reserved != 0) return SKV_ERR_INVALID_ARG;
   if (c->value_placement != SKV_VALUES_DEVICE && c->value_placement != SKV_VALUES_HOST)
     return SKV_ERR_INVALID_ARG;
   if (c->temporal_cache != 0 && c->temporal_cache != 1) return SKV_ERR_INVALID_ARG;
@@ -236,7 +238,8 @@ DecodeArgs decode_args(skv_layer* h) {
   // kScoreRows8 FP8 rows; a larger grid beats longer per-workgroup loops);
   // logits rows padded to 16 bytes
   a.landmark_format = c.landmark_format;
-  a.cpb = c.landmark_format == SKV_LANDMARKS_FP8_E5M2 ? kScoreRows8 : kScoreRows;
+  a.a_format = c.a_format;
+  a.cpb = c.landmark_format == SKV_FORMAT_FP8_E5M2 ? kScoreRows8 : kScoreRows;
   a.nb_score = (h->n_cand + a.cpb - 1) / a.cpb;
   a.ncp = (h->n_cand + 3) / 4 * 4;
   // attention splits grow with the exact region (window + appended, not folded)
@@ -348,7 +351,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   // scratch sized for the largest candidate count the handle can reach (the
   // bf16 score block is the smaller one, so its count bounds both formats)
   const int nb_cap = (cap + kScoreRows - 1) / kScoreRows, ncp_cap = (cap + 3) / 4 * 4;
-  const bool fp8 = c.landmark_format == SKV_LANDMARKS_FP8_E5M2;
+  const bool fp8 = c.landmark_format == SKV_FORMAT_FP8_E5M2;
   const int lrow = fp8 ? kHeadDim : kHeadDim * 2;   // bytes per landmark
   int n_part_cap = 1;
   for (int n = h->n_cand0; n <= cap; n++) {
@@ -371,7 +374,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
 
   // persistent state, one allocation
   Carver cv;
-  const size_t oA = cv.take<uint16_t>((size_t)b * h->a_rows * r);
+  const bool a8 = c.a_format == SKV_FORMAT_FP8_E5M2;
+  const size_t oA = cv.take<uint8_t>((size_t)b * h->a_rows * r * (a8 ? 1 : 2));
   const size_t oBt = cv.take<uint16_t>((size_t)b * HD * r);
   const size_t oL = cv.take<uint8_t>((size_t)P * cap * lrow);
   const size_t oKo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
@@ -513,7 +517,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   }
   HIP_TRY(hipMemcpyAsync(psi_f, psi32.data(), psi32.size() * 4, hipMemcpyHostToDevice, s));
   HIP_TRY(hipMemcpyAsync(h->Bt, bt16.data(), bt16.size() * 2, hipMemcpyHostToDevice, s));
-  HIP_TRY(launch_project(k_pre, psi_f, b, S, HD, r, h->a_rows, h->A, s));
+  HIP_TRY(launch_project(k_pre, psi_f, b, S, HD, r, h->a_rows, a8, h->A, s));
   HIP_TRY(launch_reset_cache(decode_args(h), s));
   HIP_TRY(hipStreamSynchronize(s));
   (void)hipFree(L_full);
@@ -665,7 +669,12 @@ skv_status skv_export_state(const skv_layer* hc, const skv_state_host* d) {
   const int64_t S = c.seq_len;
   const int P = h->P, HD = h->HD;
   HIP_TRY(hipStreamSynchronize(h->last_stream));
-  if (d->A)
+  if (d->A && c.a_format == SKV_FORMAT_FP8_E5M2) {
+    std::vector<uint8_t> a8((size_t)b * S * r);
+    HIP_TRY(hipMemcpy2D(a8.data(), (size_t)S * r, h->A, (size_t)h->a_rows * r, (size_t)S * r, b,
+                        hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < a8.size(); i++) d->A[i] = e5m2_to_bf16(a8[i]);
+  } else if (d->A)
     HIP_TRY(hipMemcpy2D(d->A, (size_t)S * r * 2, h->A, (size_t)h->a_rows * r * 2, (size_t)S * r * 2, b,
                         hipMemcpyDeviceToHost));
   if (d->B) {
@@ -678,7 +687,7 @@ skv_status skv_export_state(const skv_layer* hc, const skv_state_host* d) {
             d->B[(((size_t)bi * H + hh) * r + k) * kHeadDim + dd] =
                 bt[((size_t)bi * HD + hh * kHeadDim + dd) * r + k];
   }
-  if (d->landmarks && c.landmark_format == SKV_LANDMARKS_FP8_E5M2) {
+  if (d->landmarks && c.landmark_format == SKV_FORMAT_FP8_E5M2) {
     // FP8 bytes widened to bf16 (every E5M2 value is a bf16 value)
     std::vector<uint8_t> l8((size_t)P * h->n_cand0 * kHeadDim);
     HIP_TRY(hipMemcpy2D(l8.data(), (size_t)h->n_cand0 * kHeadDim, h->L, (size_t)h->cand_cap * kHeadDim,

@@ -20,7 +20,8 @@ struct DecodeArgs {
   int batch, n_kv, group, chunk, top_k, n_outlier, n_win_units, n_cand;
   int cand_stride;            // rows per pair of L and cand_map (candidate capacity)
   int n_c;                    // chunks of the pre-filled context (S / C)
-  int landmark_format;        // SKV_LANDMARKS_BF16 or SKV_LANDMARKS_FP8_E5M2
+  int landmark_format;        // SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2
+  int a_format;               // the same for the rows of A
   int n_new_tokens, n_new_units, max_new;   // appended tokens, their units, capacity
   int n_fold;                 // appended chunks folded into the candidates (low-rank mode)
   int64_t seq_len;
@@ -35,7 +36,7 @@ struct DecodeArgs {
   const uint16_t* q;          // [b][Hq][d]
   const uint16_t* L;          // [P][cand_stride][d] bf16 (bytes for FP8), first n_cand rows in use
   const int32_t* cand_map;    // [P][cand_stride]
-  const uint16_t* A;          // [b][a_rows][r]
+  const uint16_t* A;          // [b][a_rows][r] bf16 (bytes for FP8)
   const uint16_t* Bt;         // [b][Hkv*d][r]
   int rank;
   const uint16_t* k_out;      // [P][O*C][d]
@@ -96,8 +97,9 @@ int gram_segments(int b, int64_t S, int HD);
 hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batch, int M, int N,
                            int K, hipStream_t st);
 // A[b] rows 0..S-1 of a [b][a_rows][r] array
+// A: [b][a_rows][r] bf16, or bytes with fp8 (FP8 E5M2)
 hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_t S, int HD, int r,
-                          int64_t a_rows, uint16_t* A, hipStream_t st);
+                          int64_t a_rows, bool fp8, void* A, hipStream_t st);
 
 // ---- decode launchers (decode_kernels.hip)
 hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st);

@@ -20,8 +20,8 @@ SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_SHAPE, SKV_ERR_UNSUPPORTED = 0, 1, 2, 3
 SKV_ERR_OOM, SKV_ERR_HIP, SKV_ERR_STATE, SKV_ERR_INTERNAL = 4, 5, 6, 7
 SKV_VALUES_DEVICE, SKV_VALUES_HOST = 0, 1
 SKV_NEW_EXACT, SKV_NEW_LOWRANK = 0, 1
-SKV_LANDMARKS_BF16, SKV_LANDMARKS_FP8_E5M2 = 0, 1
-LANDMARK_FORMATS = {"bf16": SKV_LANDMARKS_BF16, "e5m2": SKV_LANDMARKS_FP8_E5M2}
+SKV_FORMAT_BF16, SKV_FORMAT_FP8_E5M2 = 0, 1
+FORMATS = {"bf16": SKV_FORMAT_BF16, "e5m2": SKV_FORMAT_FP8_E5M2}
 
 EXPORTED = ["skv_build", "skv_decode_step", "skv_append_token", "skv_get_stats", "skv_reset_temporal_cache",
             "skv_export_state", "skv_set_timing", "skv_get_timing", "skv_destroy",
@@ -36,7 +36,8 @@ class SkvConfig(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("n_outlier", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("value_placement", ctypes.c_int32), ("rope_theta", ctypes.c_double),
                 ("temporal_cache", ctypes.c_int32), ("landmark_format", ctypes.c_int32),
-                ("max_new_tokens", ctypes.c_int32), ("new_token_mode", ctypes.c_int32)]
+                ("max_new_tokens", ctypes.c_int32), ("new_token_mode", ctypes.c_int32),
+                ("a_format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SkvStats(ctypes.Structure):
@@ -103,13 +104,15 @@ def skv_abi_version() -> int:
 
 def make_config(shape, value_placement: int = SKV_VALUES_DEVICE, temporal_cache: int = 1,
                 max_new_tokens: int = 0, new_token_mode: int = SKV_NEW_EXACT) -> SkvConfig:
-    """skv_config from any object with the ShadowKV shape fields (landmark
-    storage from its optional ``landmark_format``: "bf16" or "e5m2")."""
-    fmt = LANDMARK_FORMATS[getattr(shape, "landmark_format", "bf16")]
+    """skv_config from any object with the ShadowKV shape fields (storage of
+    the landmarks and of A from its optional ``landmark_format`` and
+    ``a_format``: "bf16" or "e5m2")."""
+    lfmt = FORMATS[getattr(shape, "landmark_format", "bf16")]
+    afmt = FORMATS[getattr(shape, "a_format", "bf16")]
     return SkvConfig(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                      shape.seq_len, shape.rank, shape.chunk, shape.top_k, shape.n_outlier,
-                     shape.window, value_placement, float(shape.rope_theta), temporal_cache, fmt,
-                     max_new_tokens, new_token_mode)
+                     shape.window, value_placement, float(shape.rope_theta), temporal_cache, lfmt,
+                     max_new_tokens, new_token_mode, afmt, 0)
 
 
 def _ptr(t) -> int | None:

@@ -45,3 +45,30 @@ def test_fp8_lowrank_folds_generated_chunks():
     layer, _, _ = _run_append(_small(window=16, landmark_format="e5m2"), skv.SKV_NEW_LOWRANK,
                               [0, 9, 20, 15], max_new=48)
     layer.close()
+
+
+def test_fp8_a_tiny_8k_both_formats():
+    # landmarks and A both FP8 (the key rebuild widens A's bytes to bf16)
+    _run(synth.SHAPES["tiny_8k"].replace(landmark_format="e5m2", a_format="e5m2"), steps=4)
+
+
+def test_fp8_a_only_ragged_two_batches():
+    _run(_small(a_format="e5m2"), steps=3)
+
+
+@pytest.mark.parametrize("chunk", [4, 16])
+def test_fp8_a_chunk_sizes_host_values(chunk):
+    _run(_small(chunk=chunk, seq_len=8192, top_k=8192 // (64 * chunk), n_outlier=3,
+                landmark_format="e5m2", a_format="e5m2"), steps=2, placement=skv.SKV_VALUES_HOST)
+
+
+def test_fp8_a_group_of_sixteen_small_rank():
+    _run(_small(n_q_heads=32, n_kv_heads=2, batch=1, seq_len=4096, top_k=9, n_outlier=2,
+                rank=16, latent_rank=16, landmark_format="e5m2", a_format="e5m2"), steps=2)
+
+
+def test_fp8_a_lowrank_appended_rows():
+    # the rows of A of generated tokens are FP8 too; folded chunks are rebuilt from them
+    layer, _, _ = _run_append(_small(window=16, landmark_format="e5m2", a_format="e5m2"),
+                              skv.SKV_NEW_LOWRANK, [0, 9, 20, 15], max_new=48)
+    layer.close()

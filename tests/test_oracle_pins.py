@@ -408,6 +408,32 @@ def test_storage_rounding_is_applied_to_stored_state():
     np.testing.assert_allclose(st0.A, st.A, rtol=2 ** -8)
 
 
+def test_fp8_formats_round_landmarks_and_a_only():
+    # FP8 landmarks and A: exactly the E5M2 rounding of the unrounded build's
+    # values; B and the exact keys stay bf16; a decode step rebuilds its keys
+    # from the rounded A (its outputs differ from the bf16 build's)
+    rng = np.random.default_rng(19)
+    cfg = small_cfg()
+    hd = cfg.n_kv_heads * cfg.head_dim
+    k = lowrank_keys(rng, 1, cfg.seq_len, hd, 8)
+    v = rng.standard_normal((1, cfg.n_kv_heads, cfg.seq_len, cfg.head_dim))
+    q = rng.standard_normal((1, cfg.n_q_heads, cfg.head_dim))
+    st0 = O.build(cfg, k, v, storage_rounding=False)
+    st = O.build(dataclasses.replace(cfg, landmark_format="e5m2", a_format="e5m2"), k, v)
+    np.testing.assert_array_equal(st.L, O.round_e5m2(st0.L))
+    np.testing.assert_array_equal(st.A, O.round_e5m2(st0.A))
+    np.testing.assert_array_equal(st.B, O.round_bf16(st0.B))
+    np.testing.assert_array_equal(st.K_out, O.round_bf16(st0.K_out))
+    assert np.abs(st.A - st0.A).max() > 2 ** -6 * np.abs(st0.A).max()   # a coarse grid indeed
+    bf = O.build(cfg, k, v)
+    r8, rb = O.decode_step(st, q), O.decode_step(bf, q)
+    assert not np.array_equal(r8.out, rb.out)
+    # the appended rows of A take the same format
+    kn = rng.standard_normal((1, hd))
+    O.append(st, kn, rng.standard_normal((1, cfg.n_kv_heads, cfg.head_dim)), lowrank=True)
+    np.testing.assert_array_equal(st.A[:, -1], O.round_e5m2(kn[0] @ O.psi_t(st, 0).T)[None])
+
+
 # ---------------------------------------------------------------- generated tokens
 
 @pytest.mark.parametrize("lowrank", [False, True])
