@@ -192,66 +192,90 @@ hipError_t launch_static_gather(const uint16_t* k_pre, const uint16_t* v, const 
 }
 
 // ---------------------------------------------------------------------------
-// Gram matrices G_b = K_b^T K_b in fp64 (bf16 products are exact; sums in fp64).
-// Upper-triangle 64x64 tiles, rows of K split into `nseg` segments whose partial
-// Grams are added in a fixed order afterwards (deterministic).
+// Gram matrices G_b = K_b^T K_b on MFMA.  A bf16 x bf16 product is exact in
+// fp32; every v_mfma_f32_32x32x8_bf16 sums the products of 8 rows into fp32 from
+// zero, and its result is added to fp64 accumulators at once, so each fp32
+// rounding touches a sum of 8 terms only (relative error of the eigenvalues
+// about 1e-9 against an fp64 Gram).  Upper-triangle 128 x 128 tiles; a
+// workgroup's 4 waves own its 64 x 64 quadrants (2 x 2 MFMA tiles each).  Rows of
+// K are split into `nseg` segments whose partial Grams are added in a fixed
+// order afterwards (deterministic).
 
-constexpr int GT = 64, GK = 32;
+constexpr int GM = 128;          // output tile edge
+constexpr int GR = 64;           // rows of K staged per step
+constexpr int GP = GR + 4;       // LDS pitch (bf16) of one staged column: 136 B
 
-__global__ __launch_bounds__(256) void gram_kernel(const uint16_t* __restrict__ k_pre, int64_t S,
-                                                   int HD, int nseg, double* __restrict__ partial) {
-  __shared__ float ti[GK][GT + 4];
-  __shared__ float tj[GK][GT + 4];
-  const int nt = HD / GT;
+__global__ __launch_bounds__(256, 2) void gram_kernel(const uint16_t* __restrict__ k_pre, int64_t S, int HD,
+                                                      int nseg, double* __restrict__ partial) {
+  typedef short bf16x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  // staged rows, transposed: column c (0..127 the i-block, 128..255 the j-block)
+  // holds its GR rows contiguously, so an MFMA operand (4 consecutive rows of one
+  // column) is one 8-byte read; the 136-B pitch spreads 32 columns over all banks
+  __shared__ __attribute__((aligned(16))) uint16_t st[2 * GM * GP];
+  const int nt = HD / GM;
   int t = blockIdx.x, a = 0;
   while (t >= nt - a) { t -= nt - a; a++; }
-  const int i0 = a * GT, j0 = (a + t) * GT;
+  const int i0 = a * GM, j0 = (a + t) * GM;
   const int seg = blockIdx.y, b = blockIdx.z;
   const int64_t seg_len = (S + nseg - 1) / nseg;
   const int64_t s0 = seg * seg_len, s1 = min(S, s0 + seg_len);
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  double acc[4][4] = {};
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wi = w >> 1, wj = w & 1;             // the wave's quadrant
+  const int lc = lane & 31, lk = lane >> 5;      // operand column, k group (rows 4lk .. 4lk+3)
   const uint16_t* kb = k_pre + (int64_t)b * S * HD;
-  for (int64_t s = s0; s < s1; s += GK) {
-    // load 32 rows x 64 cols for both column blocks (256 threads x 8 elements each)
-    for (int e = threadIdx.x; e < GK * GT / 8; e += 256) {
-      const int r = e / (GT / 8), c8 = (e % (GT / 8)) * 8;
-      const int64_t row = s + r;
-      u32x4 wi = {0, 0, 0, 0}, wj = {0, 0, 0, 0};
-      if (row < s1) {
-        wi = *reinterpret_cast<const u32x4*>(kb + row * HD + i0 + c8);
-        wj = *reinterpret_cast<const u32x4*>(kb + row * HD + j0 + c8);
-      }
-      float xi[8], xj[8];
-      unpack8(wi, xi);
-      unpack8(wj, xj);
+  double acc[2][2][16];
 #pragma unroll
-      for (int q = 0; q < 8; q++) {
-        ti[r][c8 + q] = xi[q];
-        tj[r][c8 + q] = xj[q];
-      }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int r = 0; r < GK; r++) {
-      double x[4], y[4];
+  for (int mi = 0; mi < 2; mi++)
+#pragma unroll
+    for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+      for (int x = 0; x < 16; x++) acc[mi][nj][x] = 0.0;
+  for (int64_t s = s0; s < s1; s += GR) {
+    __syncthreads();                             // the previous step's reads are done
+    for (int e = threadIdx.x; e < GR * 32; e += 256) {
+      const int row = e >> 5, c0 = (e & 31) * 8;
+      const int gcol = c0 < GM ? i0 + c0 : j0 + c0 - GM;
+      u32x4 v = {0u, 0u, 0u, 0u};                // rows past the segment add nothing
+      if (s + row < s1) v = *reinterpret_cast<const u32x4*>(kb + (s + row) * HD + gcol);
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        x[q] = ti[r][ty * 4 + q];
-        y[q] = tj[r][tx * 4 + q];
+        st[(c0 + 2 * q) * GP + row] = (uint16_t)(v[q] & 0xffffu);
+        st[(c0 + 2 * q + 1) * GP + row] = (uint16_t)(v[q] >> 16);
       }
-#pragma unroll
-      for (int p = 0; p < 4; p++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) acc[p][q] = fma(x[p], y[q], acc[p][q]);
     }
     __syncthreads();
+#pragma unroll 2
+    for (int ks = 0; ks < GR / 8; ks++) {
+      bf16x4 af[2], bfr[2];
+#pragma unroll
+      for (int m = 0; m < 2; m++) {
+        af[m] = *reinterpret_cast<const bf16x4*>(&st[(wi * 64 + m * 32 + lc) * GP + ks * 8 + lk * 4]);
+        bfr[m] = *reinterpret_cast<const bf16x4*>(&st[(GM + wj * 64 + m * 32 + lc) * GP + ks * 8 + lk * 4]);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; mi++)
+#pragma unroll
+        for (int nj = 0; nj < 2; nj++) {
+          const f32x16 zero = {};
+          const f32x16 c = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(af[mi], bfr[nj], zero, 0, 0, 0);
+#pragma unroll
+          for (int x = 0; x < 16; x++) acc[mi][nj][x] += (double)c[x];
+        }
+    }
   }
+  // output lane (column lc of the 32 x 32 tile) holds rows 8(x/4) + 4lk + x%4
   double* out = partial + ((int64_t)b * nseg + seg) * HD * HD;
 #pragma unroll
-  for (int p = 0; p < 4; p++)
+  for (int mi = 0; mi < 2; mi++)
 #pragma unroll
-    for (int q = 0; q < 4; q++) out[(int64_t)(i0 + ty * 4 + p) * HD + j0 + tx * 4 + q] = acc[p][q];
+    for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+      for (int x = 0; x < 16; x++) {
+        const int row = i0 + wi * 64 + mi * 32 + 8 * (x >> 2) + 4 * lk + (x & 3);
+        const int col = j0 + wj * 64 + nj * 32 + lc;
+        out[(int64_t)row * HD + col] = acc[mi][nj][x];
+      }
 }
 
 // Sum the segments in order and mirror the upper triangle.
@@ -261,7 +285,7 @@ __global__ void gram_reduce_kernel(const double* __restrict__ partial, int HD, i
   const int b = blockIdx.y;
   if (idx >= (int64_t)HD * HD) return;
   const int i = (int)(idx / HD), j = (int)(idx % HD);
-  const int ti = i / GT, tj = j / GT;
+  const int ti = i / GM, tj = j / GM;
   const int64_t src = ti <= tj ? idx : (int64_t)j * HD + i;
   double s = 0.0;
   for (int g = 0; g < nseg; g++) s += partial[((int64_t)b * nseg + g) * HD * HD + src];
@@ -269,10 +293,10 @@ __global__ void gram_reduce_kernel(const double* __restrict__ partial, int HD, i
 }
 
 int gram_segments(int b, int64_t S, int HD) {
-  const int nt = HD / GT;
+  const int nt = HD / GM;
   const int tiles = nt * (nt + 1) / 2 * b;
-  int nseg = (2048 + tiles - 1) / tiles;
-  const int64_t max_seg = (S + 255) / 256;
+  int nseg = (1024 + tiles - 1) / tiles;        // about 1024 workgroups
+  const int64_t max_seg = (S + 4 * GR - 1) / (4 * GR);   // at least 4 staging steps each
   if (nseg > max_seg) nseg = (int)max_seg;
   if (nseg < 1) nseg = 1;
   if (nseg > 64) nseg = 64;
@@ -281,7 +305,7 @@ int gram_segments(int b, int64_t S, int HD) {
 
 hipError_t launch_gram(const uint16_t* k_pre, int b, int64_t S, int HD, int nseg, double* partial,
                        double* gram, hipStream_t st) {
-  const int nt = HD / GT;
+  const int nt = HD / GM;
   dim3 grid(nt * (nt + 1) / 2, nseg, b);
   gram_kernel<<<grid, 256, 0, st>>>(k_pre, S, HD, nseg, partial);
   hipError_t e = hipGetLastError();
@@ -292,8 +316,10 @@ hipError_t launch_gram(const uint16_t* k_pre, int b, int64_t S, int HD, int nseg
 }
 
 // ---------------------------------------------------------------------------
-// Batched fp64 C[bi] = A[bi] (M x K) * B[bi] (K x N), all row-major.
+// Batched fp64 C[bi] = op(A[bi]) * B[bi], all row-major: op(A) = A (M x K), or
+// with TA the transpose of a K x M array.
 
+template <bool TA>
 __global__ __launch_bounds__(256) void gemm_f64_kernel(const double* __restrict__ A,
                                                        const double* __restrict__ B,
                                                        double* __restrict__ C, int M, int N, int K) {
@@ -310,7 +336,7 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(const double* __restrict_
     for (int e = threadIdx.x; e < 16 * 64; e += 256) {
       const int kk = e / 64, mm = e % 64;
       const int gm = m0 + mm, gk = k0 + kk, gn = n0 + mm;
-      ta[kk][mm] = (gm < M && gk < K) ? A[(int64_t)gm * K + gk] : 0.0;
+      ta[kk][mm] = (gm < M && gk < K) ? A[TA ? (int64_t)gk * M + gm : (int64_t)gm * K + gk] : 0.0;
       tb[kk][mm] = (gk < K && gn < N) ? B[(int64_t)gk * N + gn] : 0.0;
     }
     __syncthreads();
@@ -341,7 +367,14 @@ __global__ __launch_bounds__(256) void gemm_f64_kernel(const double* __restrict_
 hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batch, int M, int N,
                            int K, hipStream_t st) {
   dim3 grid((N + 63) / 64, (M + 63) / 64, batch);
-  gemm_f64_kernel<<<grid, 256, 0, st>>>(A, B, C, M, N, K);
+  gemm_f64_kernel<false><<<grid, 256, 0, st>>>(A, B, C, M, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f64_tn(const double* A, const double* B, double* C, int batch, int M, int N,
+                              int K, hipStream_t st) {
+  dim3 grid((N + 63) / 64, (M + 63) / 64, batch);
+  gemm_f64_kernel<true><<<grid, 256, 0, st>>>(A, B, C, M, N, K);
   return hipGetLastError();
 }
 

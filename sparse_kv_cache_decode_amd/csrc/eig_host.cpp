@@ -4,13 +4,18 @@
 //
 // Method: block subspace iteration with Rayleigh-Ritz (Golub & Van Loan,
 // "Matrix Computations", orthogonal iteration and the Rayleigh-Ritz procedure).
-// Y = G Q runs on the GPU (fp64); the orthonormalisation (modified Gram-Schmidt,
-// applied twice) and the small p x p eigenproblems (cyclic Jacobi) run on the host
-// in fp64, one thread per batch element.  Converged when every wanted Ritz pair
-// has residual ||G u - theta u|| <= 1e-11 * theta_max.
+// Every n x p product runs on the GPU in fp64: Y = G Q, the Gram matrices of the
+// blocks and the products with p x p factors.  The blocks are orthonormalised by
+// Cholesky QR applied twice (W = X^T X = R^T R on the host, X <- X R^-1 on the
+// GPU), falling back to modified Gram-Schmidt on the host if a factor breaks
+// down; the p x p Rayleigh-Ritz eigenproblem is solved on the host by Householder
+// tridiagonalisation and the implicit symmetric QR algorithm with Wilkinson
+// shifts (ibid., 8.3), one thread per batch element.  Converged when every wanted
+// Ritz pair has residual ||G u - theta u|| <= 1e-11 * theta_max.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -61,103 +66,127 @@ void orthonormalise(double* q, int n, int p) {
     for (int j = 0; j < p; j++) q[(size_t)i * p + j] = c[(size_t)j * n + i];
 }
 
-// Cyclic Jacobi for a symmetric p x p matrix h (row-major, destroyed): eigenvalues
-// in w, eigenvectors as columns of v.
-void jacobi_eig(std::vector<double>& h, int p, std::vector<double>& w, std::vector<double>& v) {
+// Eigen-decomposition of a symmetric p x p matrix (row-major `a`, destroyed):
+// Householder reduction to tridiagonal form with the reflections accumulated in
+// v, then implicit QR sweeps with Wilkinson shifts on the tridiagonal (d, e),
+// each sweep a chain of plane rotations in planes (k, k+1) that chases the bulge
+// down the block, accumulated into v as well.  Eigenvalues in w (unsorted),
+// eigenvectors as the columns of v (row-major).  False if a block does not
+// converge within 50 p sweeps.
+bool sym_eig(std::vector<double>& a, int p, std::vector<double>& w, std::vector<double>& v) {
+  auto A = [&](int i, int j) -> double& { return a[(size_t)i * p + j]; };
   v.assign((size_t)p * p, 0.0);
   for (int i = 0; i < p; i++) v[(size_t)i * p + i] = 1.0;
-  auto A = [&](int i, int j) -> double& { return h[(size_t)i * p + j]; };
-  for (int sweep = 0; sweep < 100; sweep++) {
-    double off = 0.0, tot = 0.0;
-    for (int i = 0; i < p; i++)
-      for (int j = 0; j < p; j++) {
-        const double x = A(i, j) * A(i, j);
-        tot += x;
-        if (i != j) off += x;
-      }
-    if (off <= 1e-30 * tot) break;
-    for (int a = 0; a < p - 1; a++)
-      for (int b = a + 1; b < p; b++) {
-        const double apq = A(a, b);
-        if (std::fabs(apq) < 1e-300) continue;
-        const double tau = (A(b, b) - A(a, a)) / (2.0 * apq);
-        const double t = (tau >= 0 ? 1.0 : -1.0) / (std::fabs(tau) + std::sqrt(1.0 + tau * tau));
-        const double c = 1.0 / std::sqrt(1.0 + t * t), s = t * c;
-        for (int k = 0; k < p; k++) {   // columns a, b
-          const double x = A(k, a), y = A(k, b);
-          A(k, a) = c * x - s * y;
-          A(k, b) = s * x + c * y;
-        }
-        for (int k = 0; k < p; k++) {   // rows a, b
-          const double x = A(a, k), y = A(b, k);
-          A(a, k) = c * x - s * y;
-          A(b, k) = s * x + c * y;
-        }
-        for (int k = 0; k < p; k++) {
-          double* vr = &v[(size_t)k * p];
-          const double x = vr[a], y = vr[b];
-          vr[a] = c * x - s * y;
-          vr[b] = s * x + c * y;
-        }
-      }
+  std::vector<double> hv(p), u(p), wv(p);
+  for (int k = 0; k + 2 < p; k++) {
+    // reflection H = I - beta hv hv^T that maps column k below the diagonal onto
+    // its first entry
+    const int m = p - k - 1;
+    double nx = 0.0;
+    for (int i = 0; i < m; i++) nx += A(k + 1 + i, k) * A(k + 1 + i, k);
+    nx = std::sqrt(nx);
+    if (nx == 0.0) continue;
+    const double alpha = A(k + 1, k) > 0 ? -nx : nx;
+    for (int i = 0; i < m; i++) hv[i] = A(k + 1 + i, k);
+    hv[0] -= alpha;
+    double vn = 0.0;
+    for (int i = 0; i < m; i++) vn += hv[i] * hv[i];
+    if (vn == 0.0) continue;
+    const double beta = 2.0 / vn;
+    // trailing block: H A22 H = A22 - hv w^T - w hv^T with w = u - (beta/2)(u.hv) hv, u = beta A22 hv
+    for (int i = 0; i < m; i++) {
+      double t = 0.0;
+      for (int j = 0; j < m; j++) t += A(k + 1 + i, k + 1 + j) * hv[j];
+      u[i] = beta * t;
+    }
+    double uv = 0.0;
+    for (int i = 0; i < m; i++) uv += u[i] * hv[i];
+    for (int i = 0; i < m; i++) wv[i] = u[i] - 0.5 * beta * uv * hv[i];
+    for (int i = 0; i < m; i++)
+      for (int j = 0; j < m; j++) A(k + 1 + i, k + 1 + j) -= hv[i] * wv[j] + wv[i] * hv[j];
+    A(k + 1, k) = A(k, k + 1) = alpha;
+    for (int i = 1; i < m; i++) A(k + 1 + i, k) = A(k, k + 1 + i) = 0.0;
+    for (int row = 0; row < p; row++) {   // v <- v H
+      double* vr = &v[(size_t)row * p + k + 1];
+      double t = 0.0;
+      for (int j = 0; j < m; j++) t += vr[j] * hv[j];
+      t *= beta;
+      for (int j = 0; j < m; j++) vr[j] -= t * hv[j];
+    }
   }
-  w.resize(p);
-  for (int i = 0; i < p; i++) w[i] = A(i, i);
+  std::vector<double> d(p), e(p, 0.0);
+  for (int i = 0; i < p; i++) d[i] = A(i, i);
+  for (int i = 0; i + 1 < p; i++) e[i] = A(i, i + 1);
+  auto negligible = [&](int i) {
+    return std::fabs(e[i]) <= DBL_EPSILON * (std::fabs(d[i]) + std::fabs(d[i + 1]));
+  };
+  int hi = p - 1, sweeps = 0;
+  while (hi > 0) {
+    if (negligible(hi - 1)) {   // d[hi] has converged
+      e[hi - 1] = 0.0;
+      hi--;
+      continue;
+    }
+    if (++sweeps > 50 * p) return false;
+    int lo = hi - 1;            // the unreduced block [lo, hi]
+    while (lo > 0 && !negligible(lo - 1)) lo--;
+    // Wilkinson shift: the eigenvalue of the trailing 2x2 block closer to d[hi]
+    const double dd = 0.5 * (d[hi - 1] - d[hi]), b2 = e[hi - 1] * e[hi - 1];
+    const double mu = d[hi] - b2 / (dd + std::copysign(std::sqrt(dd * dd + b2), dd));
+    // rotation k acts on rows/columns (k, k+1) as [c s; -s c]; (x, z) is the pair
+    // it annihilates: the shifted first column for k = lo, else (e[k-1], bulge)
+    double x = d[lo] - mu, z = e[lo];
+    for (int k = lo; k < hi; k++) {
+      const double rr = std::hypot(x, z);
+      const double c = rr == 0.0 ? 1.0 : x / rr, sn = rr == 0.0 ? 0.0 : z / rr;
+      if (k > lo) e[k - 1] = rr;
+      const double a0 = d[k], a1 = d[k + 1], bb = e[k];
+      d[k] = c * c * a0 + 2.0 * c * sn * bb + sn * sn * a1;
+      d[k + 1] = sn * sn * a0 - 2.0 * c * sn * bb + c * c * a1;
+      e[k] = c * sn * (a1 - a0) + (c * c - sn * sn) * bb;
+      if (k + 1 < hi) {          // the rotation pushes a bulge to (k, k+2)
+        z = sn * e[k + 1];
+        e[k + 1] *= c;
+        x = e[k];
+      }
+      for (int row = 0; row < p; row++) {
+        double* vr = &v[(size_t)row * p];
+        const double y0 = vr[k], y1 = vr[k + 1];
+        vr[k] = c * y0 + sn * y1;
+        vr[k + 1] = -sn * y0 + c * y1;
+      }
+    }
+  }
+  w = d;
+  return true;
 }
 
-// Rayleigh-Ritz on span(q) with y = G q: fills u (n x p Ritz vectors, descending
-// Ritz values theta) and returns the largest relative residual among the first r.
-double rayleigh_ritz(const double* q, const double* y, int n, int p, int r, double* u,
-                     std::vector<double>& theta) {
-  std::vector<double> h((size_t)p * p, 0.0);
-  for (int i = 0; i < n; i++) {
-    const double* qi = q + (size_t)i * p;
-    const double* yi = y + (size_t)i * p;
-    for (int a = 0; a < p; a++) {
-      const double x = qi[a];
-      double* ha = &h[(size_t)a * p];
-      for (int b = 0; b < p; b++) ha[b] += x * yi[b];
+// W = R^T R (R upper triangular, W symmetric p x p); rinv = R^-1 (row-major).
+// False if a pivot is not clearly positive (X too close to rank deficient).
+bool chol_inverse(const double* W, int p, double* rinv) {
+  std::vector<double> R((size_t)p * p, 0.0);
+  for (int j = 0; j < p; j++) {
+    double s = W[(size_t)j * p + j];
+    for (int k = 0; k < j; k++) s -= R[(size_t)k * p + j] * R[(size_t)k * p + j];
+    if (!(s > 1e-14 * W[(size_t)j * p + j]) || !(s > 0.0)) return false;
+    const double rjj = std::sqrt(s);
+    R[(size_t)j * p + j] = rjj;
+    for (int i = j + 1; i < p; i++) {
+      double t = W[(size_t)j * p + i];
+      for (int k = 0; k < j; k++) t -= R[(size_t)k * p + j] * R[(size_t)k * p + i];
+      R[(size_t)j * p + i] = t / rjj;
     }
   }
-  for (int a = 0; a < p; a++)
-    for (int b = a + 1; b < p; b++) {
-      const double m = 0.5 * (h[(size_t)a * p + b] + h[(size_t)b * p + a]);
-      h[(size_t)a * p + b] = h[(size_t)b * p + a] = m;
-    }
-  std::vector<double> w, v;
-  jacobi_eig(h, p, w, v);
-  std::vector<int> ord(p);
-  for (int i = 0; i < p; i++) ord[i] = i;
-  std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) { return w[a] > w[b]; });
-  theta.resize(p);
-  for (int j = 0; j < p; j++) theta[j] = w[ord[j]];
-  // u = q V_sorted, yv = y V_sorted; residual of column j = ||yv_j - theta_j u_j||
-  std::vector<double> res(p, 0.0);
-  std::vector<double> urow(p), yrow(p);
-  for (int i = 0; i < n; i++) {
-    const double* qi = q + (size_t)i * p;
-    const double* yi = y + (size_t)i * p;
-    std::fill(urow.begin(), urow.end(), 0.0);
-    std::fill(yrow.begin(), yrow.end(), 0.0);
-    for (int a = 0; a < p; a++) {
-      const double xq = qi[a], xy = yi[a];
-      const double* va = &v[(size_t)a * p];
-      for (int j = 0; j < p; j++) {
-        const double vv = va[ord[j]];
-        urow[j] += xq * vv;
-        yrow[j] += xy * vv;
-      }
-    }
-    for (int j = 0; j < p; j++) {
-      u[(size_t)i * p + j] = urow[j];
-      const double e = yrow[j] - theta[j] * urow[j];
-      res[j] += e * e;
+  std::fill(rinv, rinv + (size_t)p * p, 0.0);
+  for (int j = 0; j < p; j++) {   // column j of R^-1 by back substitution
+    rinv[(size_t)j * p + j] = 1.0 / R[(size_t)j * p + j];
+    for (int i = j - 1; i >= 0; i--) {
+      double t = 0.0;
+      for (int k = i + 1; k <= j; k++) t += R[(size_t)i * p + k] * rinv[(size_t)k * p + j];
+      rinv[(size_t)i * p + j] = -t / R[(size_t)i * p + i];
     }
   }
-  const double scale = std::max(std::fabs(theta[0]), 1e-300);
-  double worst = 0.0;
-  for (int j = 0; j < r; j++) worst = std::max(worst, std::sqrt(res[j]) / scale);
-  return worst;
+  return true;
 }
 
 }  // namespace
@@ -166,18 +195,13 @@ int top_eigvecs(const double* gram_dev, int b, int n, int r, hipStream_t st, dou
                 double* eig, hipError_t* err) {
   *err = hipSuccess;
   const int p = std::min(n, r + std::max(16, r / 4));
-  const size_t blk = (size_t)n * p;
-  std::vector<double> q(blk * b), y(blk * b), u(blk * b);
-  for (int bi = 0; bi < b; bi++) {
-    start_block(&q[blk * bi], n, p, 0x5eedull + (uint64_t)bi);
-  }
-  double* dq = nullptr;
-  double* dy = nullptr;
-  if ((*err = hipMalloc(&dq, blk * b * sizeof(double))) != hipSuccess) return 2;
-  if ((*err = hipMalloc(&dy, blk * b * sizeof(double))) != hipSuccess) {
-    hipFree(dq);
-    return 2;
-  }
+  const size_t blk = (size_t)n * p, sq = (size_t)p * p;
+  std::vector<double> hq(blk * b), hy(blk * b), hs(sq * b), hv(sq * b), ufinal(blk * b);
+  std::vector<std::vector<double>> theta(b);
+  std::vector<char> done(b, 0);
+  double* dev = nullptr;   // q, y, t, u (n x p blocks), s (p x p blocks)
+  if ((*err = hipMalloc(&dev, (4 * blk + sq) * b * sizeof(double))) != hipSuccess) return 2;
+  double *dq = dev, *dy = dq + blk * b, *dt = dy + blk * b, *du = dt + blk * b, *ds = du + blk * b;
   const int nthreads = std::max(1, std::min(b, (int)std::thread::hardware_concurrency()));
   auto parallel = [&](auto fn) {
     std::vector<std::thread> th;
@@ -187,59 +211,119 @@ int top_eigvecs(const double* gram_dev, int b, int n, int r, hipStream_t st, dou
       });
     for (auto& x : th) x.join();
   };
-  auto multiply = [&]() -> bool {   // y = G q for every batch element
-    if ((*err = hipMemcpyAsync(dq, q.data(), blk * b * sizeof(double), hipMemcpyHostToDevice, st)) != hipSuccess) return false;
-    if ((*err = launch_gemm_f64(gram_dev, dq, dy, b, n, p, n, st)) != hipSuccess) return false;
-    if ((*err = hipMemcpyAsync(y.data(), dy, blk * b * sizeof(double), hipMemcpyDeviceToHost, st)) != hipSuccess) return false;
-    return (*err = hipStreamSynchronize(st)) == hipSuccess;
+  auto copy = [&](void* dst, const void* src, size_t doubles, hipMemcpyKind kind) {
+    return (*err = hipMemcpyAsync(dst, src, doubles * sizeof(double), kind, st)) == hipSuccess;
   };
-  parallel([&](int bi) { orthonormalise(&q[blk * bi], n, p); });
-  std::vector<std::vector<double>> theta(b);
-  std::vector<char> done(b, 0);
-  int status = 1;
+  auto sync = [&] { return (*err = hipStreamSynchronize(st)) == hipSuccess; };
+  auto ok = [&](hipError_t e) { return (*err = e) == hipSuccess; };
+  // orthonormalise the columns of every block of x (device) in place
+  auto orth = [&](double* x) -> bool {
+    for (int pass = 0; pass < 2; pass++) {
+      if (!ok(launch_gemm_f64_tn(x, x, ds, b, p, p, n, st)) || !copy(hs.data(), ds, sq * b, hipMemcpyDeviceToHost) ||
+          !sync())
+        return false;
+      std::vector<char> bad(b, 0);
+      parallel([&](int bi) { bad[bi] = !chol_inverse(&hs[sq * bi], p, &hv[sq * bi]); });
+      if (std::find(bad.begin(), bad.end(), 1) != bad.end()) {
+        // a block too close to rank deficient for Cholesky QR: Gram-Schmidt on the host
+        if (!copy(hq.data(), x, blk * b, hipMemcpyDeviceToHost) || !sync()) return false;
+        parallel([&](int bi) { orthonormalise(&hq[blk * bi], n, p); });
+        return copy(x, hq.data(), blk * b, hipMemcpyHostToDevice) && sync();
+      }
+      if (!copy(ds, hv.data(), sq * b, hipMemcpyHostToDevice) || !ok(launch_gemm_f64(x, ds, dt, b, n, p, p, st)) ||
+          !copy(x, dt, blk * b, hipMemcpyDeviceToDevice))
+        return false;
+    }
+    return true;
+  };
+  for (int bi = 0; bi < b; bi++) start_block(&hq[blk * bi], n, p, 0x5eedull + (uint64_t)bi);
+  int status = 2;
   const bool square = (p == n);   // q spans everything: one Rayleigh-Ritz is exact
-  for (int round = 0; round < 60; round++) {
-    const int iters = square ? 0 : 3;
-    bool ok = true;
-    for (int it = 0; it < iters && ok; it++) {
-      ok = multiply();
-      if (ok) parallel([&](int bi) {
-          if (done[bi]) return;
-          std::memcpy(&q[blk * bi], &y[blk * bi], blk * sizeof(double));
-          orthonormalise(&q[blk * bi], n, p);
-        });
-    }
-    if (!ok || !multiply()) {
-      status = 2;
-      break;
-    }
-    std::vector<double> worst(b, 0.0);
-    parallel([&](int bi) {
-      if (done[bi]) return;
-      worst[bi] = rayleigh_ritz(&q[blk * bi], &y[blk * bi], n, p, r, &u[blk * bi], theta[bi]);
-    });
-    bool all = true;
-    for (int bi = 0; bi < b; bi++) {
-      if (done[bi]) continue;
-      if (worst[bi] <= 1e-11 || square) {
-        done[bi] = 1;
-      } else {
-        all = false;
-        // restart from the Ritz vectors (already orthonormal)
-        std::memcpy(&q[blk * bi], &u[blk * bi], blk * sizeof(double));
+  if (copy(dq, hq.data(), blk * b, hipMemcpyHostToDevice) && orth(dq)) {
+    status = 1;
+    for (int round = 0; round < 60; round++) {
+      bool good = true;
+      for (int it = 0; it < (square ? 0 : 3) && good; it++)
+        good = ok(launch_gemm_f64(gram_dev, dq, dy, b, n, p, n, st)) &&
+               copy(dq, dy, blk * b, hipMemcpyDeviceToDevice) && orth(dq);
+      // Rayleigh-Ritz: H = Q^T G Q, H = V diag(theta) V^T, U = Q V, residuals G U - U diag(theta)
+      good = good && ok(launch_gemm_f64(gram_dev, dq, dy, b, n, p, n, st)) &&
+             ok(launch_gemm_f64_tn(dq, dy, ds, b, p, p, n, st)) &&
+             copy(hs.data(), ds, sq * b, hipMemcpyDeviceToHost) && sync();
+      if (!good) {
+        status = 2;
+        break;
+      }
+      std::vector<char> failed(b, 0);
+      parallel([&](int bi) {
+        double* h = &hs[sq * bi];
+        double* vs = &hv[sq * bi];
+        if (done[bi]) {   // keep the block (identity); its results are not used
+          std::fill(vs, vs + sq, 0.0);
+          for (int i = 0; i < p; i++) vs[(size_t)i * p + i] = 1.0;
+          return;
+        }
+        std::vector<double> hm(h, h + sq), w, v;
+        for (int i = 0; i < p; i++)
+          for (int j = i + 1; j < p; j++) hm[(size_t)i * p + j] = hm[(size_t)j * p + i] =
+                                              0.5 * (h[(size_t)i * p + j] + h[(size_t)j * p + i]);
+        if (!sym_eig(hm, p, w, v)) {
+          failed[bi] = 1;
+          return;
+        }
+        std::vector<int> ord(p);
+        for (int i = 0; i < p; i++) ord[i] = i;
+        std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return w[x] > w[y]; });
+        theta[bi].resize(p);
+        for (int j = 0; j < p; j++) {
+          theta[bi][j] = w[ord[j]];
+          for (int i = 0; i < p; i++) vs[(size_t)i * p + j] = v[(size_t)i * p + ord[j]];
+        }
+      });
+      if (std::find(failed.begin(), failed.end(), 1) != failed.end()) break;   // status 1
+      good = copy(ds, hv.data(), sq * b, hipMemcpyHostToDevice) && ok(launch_gemm_f64(dq, ds, du, b, n, p, p, st)) &&
+             ok(launch_gemm_f64(dy, ds, dt, b, n, p, p, st)) &&
+             copy(hq.data(), du, blk * b, hipMemcpyDeviceToHost) &&
+             copy(hy.data(), dt, blk * b, hipMemcpyDeviceToHost) && sync();
+      if (!good) {
+        status = 2;
+        break;
+      }
+      parallel([&](int bi) {
+        if (done[bi]) return;
+        const double* u = &hq[blk * bi];
+        const double* yv = &hy[blk * bi];
+        std::vector<double> res(r, 0.0);
+        for (int i = 0; i < n; i++)
+          for (int j = 0; j < r; j++) {
+            const double e = yv[(size_t)i * p + j] - theta[bi][j] * u[(size_t)i * p + j];
+            res[j] += e * e;
+          }
+        const double scale = std::max(std::fabs(theta[bi][0]), 1e-300);
+        double worst = 0.0;
+        for (int j = 0; j < r; j++) worst = std::max(worst, std::sqrt(res[j]) / scale);
+        if (worst <= 1e-11 || square) {
+          done[bi] = 1;
+          std::memcpy(&ufinal[blk * bi], u, blk * sizeof(double));
+        }
+      });
+      if (std::find(done.begin(), done.end(), 0) == done.end()) {
+        status = 0;
+        break;
+      }
+      // restart from the Ritz vectors (orthonormal)
+      if (!copy(dq, du, blk * b, hipMemcpyDeviceToDevice)) {
+        status = 2;
+        break;
       }
     }
-    if (all) {
-      status = 0;
-      break;
-    }
   }
-  hipFree(dq);
-  hipFree(dy);
+  (void)hipStreamSynchronize(st);
+  (void)hipFree(dev);
   if (status != 0) return status;
   // first r Ritz vectors, sign gauge: largest-|.| entry positive (lowest index on ties)
   for (int bi = 0; bi < b; bi++) {
-    const double* ub = &u[blk * bi];
+    const double* ub = &ufinal[blk * bi];
     double* pb = psi + (size_t)bi * n * r;
     for (int j = 0; j < r; j++) {
       int arg = 0;

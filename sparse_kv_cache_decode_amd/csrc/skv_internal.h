@@ -96,6 +96,9 @@ hipError_t launch_gram(const uint16_t* k_pre, int b, int64_t S, int HD, int nseg
 int gram_segments(int b, int64_t S, int HD);
 hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batch, int M, int N,
                            int K, hipStream_t st);
+// C[bi] (M x N) = A[bi]^T B[bi] with A[bi] stored K x M, B[bi] K x N
+hipError_t launch_gemm_f64_tn(const double* A, const double* B, double* C, int batch, int M, int N,
+                              int K, hipStream_t st);
 // A[b] rows 0..S-1 of a [b][a_rows][r] array
 // A: [b][a_rows][r] bf16, or bytes with fp8 (FP8 E5M2)
 hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_t S, int HD, int r,
@@ -125,9 +128,9 @@ int attn_head_groups(int group);   // attention workgroups per (pair, split): qu
 
 // ---- host eigensolver (eig_host.cpp)
 // Top-r eigenpairs of each symmetric n x n matrix gram[bi] (row-major fp64, on the
-// device), by block subspace iteration with Rayleigh-Ritz.  The products with the
-// Gram matrix run on the GPU (launch_gemm_f64); orthonormalisation and the small
-// eigenproblems run on the host in fp64.  psi receives [b][n][r] (columns =
+// device), by block subspace iteration with Rayleigh-Ritz.  Every n x p product
+// runs on the GPU in fp64 (launch_gemm_f64 / _tn); the host does the p x p work
+// (Cholesky factors, the Rayleigh-Ritz eigenproblem).  psi receives [b][n][r] (columns =
 // eigenvectors, eigenvalues descending, largest-|.| entry positive), eig [b][r].
 // Returns 0 on success, 1 on non-convergence, 2 on a HIP error (err set).
 int top_eigvecs(const double* gram_dev, int b, int n, int r, hipStream_t st, double* psi,

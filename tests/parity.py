@@ -146,19 +146,43 @@ def check_build(gpu: dict, st: O.State):
     np.testing.assert_array_equal(O.bf16_bits_to_f64(gpu["v_outlier"]), st.V_out)
     np.testing.assert_array_equal(O.bf16_bits_to_f64(gpu["v_window"]), st.V_win)
     r = cfg.rank
-    np.testing.assert_allclose(gpu["eigvals"], st.sigma[:, :r] ** 2, rtol=1e-8)
+    # the GPU's Gram adds fp32 sums of 8 exact bf16 products in fp64: its error is
+    # about 1e-9 of the largest entries, and by Weyl's theorem no eigenvalue moves
+    # by more than the error's spectral norm, so the bar is relative to lambda_max
+    lam = st.sigma[:, :r] ** 2
+    np.testing.assert_allclose(gpu["eigvals"], lam, rtol=1e-8, atol=1e-8 * float(lam.max()))
     A = O.bf16_bits_to_f64(gpu["A"])
     B = O.bf16_bits_to_f64(gpu["B"])
-    # same gauge: the factors agree element by element up to bf16 rounding
-    assert bf16_close(gpu["B"], st.B, 1e-9) <= 0
-    if cfg.a_format == "e5m2":
-        # fp32 projection error on top of the rounding: well under 1e-5 of max|A|
-        excess, frac = e5m2_close(gpu["A"], st.A, 1e-5 * np.abs(st.A).max())
-        assert excess <= 0, f"FP8 A off by more than one spacing ({excess})"
-        assert frac <= LANDMARK_DIFF_FRACTION, f"{frac:.2e} of the FP8 A values differ"
-    else:
-        rel = np.abs(A - st.A) / (np.abs(st.A) + 1e-3 * np.abs(st.A).max())
-        assert rel.max() <= 2 ** -7, f"A differs by {rel.max()}"
+    # Same gauge: the factors agree column by column up to rounding where the
+    # singular vector is well determined.  Davis-Kahan bounds the perturbation of
+    # eigenvector j by ||dG|| / gap_j (gap to the neighbouring eigenvalues of the
+    # full spectrum); with ||dG|| <= 1e-8 lambda_max (the bar above) a column is
+    # compared element by element where that bound is below 1e-4, with the bound
+    # as extra absolute slack.  Columns inside a cluster of nearly equal
+    # eigenvalues are determined only as a subspace: the A B products below cover
+    # them.
+    for bi in range(cfg.batch):
+        lam_all = st.sigma[bi] ** 2
+        gap = np.full(r, np.inf)
+        gap[1:] = np.minimum(gap[1:], lam_all[:r - 1] - lam_all[1:r])
+        nxt = min(r, len(lam_all) - 1)
+        gap[:nxt] = np.minimum(gap[:nxt], lam_all[:nxt] - lam_all[1:nxt + 1])
+        dk = 1e-8 * lam_all[0] / np.maximum(gap, 1e-300)
+        well = dk < 1e-4
+        gb, ob = B[bi][:, well], st.B[bi][:, well]                    # [H, n_well, d]
+        _, e = np.frexp(ob)
+        spacing = np.where(ob == 0, 0.0, np.ldexp(1.0, e - 8))
+        excess = np.abs(gb - ob) - spacing - 1e-9 - dk[well][None, :, None]
+        assert excess.size == 0 or excess.max() <= 0, f"B differs beyond rounding ({excess.max()})"
+        if cfg.a_format == "e5m2":
+            # fp32 projection error on top of the rounding: well under 1e-5 of max|A|
+            excess, frac = e5m2_close(gpu["A"][bi][:, well], st.A[bi][:, well], 1e-5 * np.abs(st.A[bi]).max())
+            assert excess <= 0, f"FP8 A off by more than one spacing ({excess})"
+            assert frac <= LANDMARK_DIFF_FRACTION, f"{frac:.2e} of the FP8 A values differ"
+        else:
+            ga, oa = A[bi][:, well], st.A[bi][:, well]
+            rel = np.abs(ga - oa) / (np.abs(oa) + 1e-3 * np.abs(st.A[bi]).max())
+            assert rel.size == 0 or rel.max() <= 2 ** -7, f"A differs by {rel.max()}"
     for b in range(cfg.batch):
         for h in range(cfg.n_kv_heads):
             pg = A[b] @ B[b, h]
