@@ -357,6 +357,7 @@ def main():
     pcie_peak = measure_h2d_gbps() if host else None     # before the value stores take pinned memory
     new_mode = {"exact": skv.SKV_NEW_EXACT, "lowrank": skv.SKV_NEW_LOWRANK}.get(args.append)
     news = []
+    build_s = []       # wall time of each layer's skv_build (pre-fill factorisation and caches)
     for l in range(L):
         k_pre, v = synth.layer_cache_torch(shape, l, args.seed, dev)
         if host:
@@ -364,10 +365,15 @@ def main():
             vh.copy_(v)
             del v
             v = vh
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
         if new_mode is None:
             layers.append(skv.Layer(shape, k_pre, v, placement))
         else:
             layers.append(skv.Layer(shape, k_pre, v, placement, max_new_tokens=total, new_token_mode=new_mode))
+        torch.cuda.synchronize()
+        build_s.append(time.perf_counter() - tb)
+        if new_mode is not None:
             news.append(synth.continuation_torch(shape, l, total, args.seed, dev))
         qs.append(synth.queries_torch(shape, k_pre, l, total, args.seed, mode=args.queries))
         del k_pre, v
@@ -519,6 +525,10 @@ def main():
                         f"after the timed region",
         "launch": "one captured HIP graph per step (all layers), replayed" if graph is not None else "eager launches",
         "layer_us": round(layer_us, 2),
+        "build_ms_per_layer": {"mean": round(1000.0 * sum(build_s[1:] or build_s) / len(build_s[1:] or build_s), 1),
+                               "first": round(1000.0 * build_s[0], 1),
+                               "note": "skv_build wall time per layer (not part of the timed decode steps); "
+                                       "mean over layers after the first"},
         "alpha": {"timed_steps": round(alpha_timed, 4), "steps_1_to_end": round(alpha_all, 4),
                   "misses_per_layer_step": round(misses, 1)},
         "equivalent_bandwidth_TBps": {

@@ -68,15 +68,16 @@ void orthonormalise(double* q, int n, int p) {
 
 // Eigen-decomposition of a symmetric p x p matrix (row-major `a`, destroyed):
 // Householder reduction to tridiagonal form with the reflections accumulated in
-// v, then implicit QR sweeps with Wilkinson shifts on the tridiagonal (d, e),
+// vt, then implicit QR sweeps with Wilkinson shifts on the tridiagonal (d, e),
 // each sweep a chain of plane rotations in planes (k, k+1) that chases the bulge
-// down the block, accumulated into v as well.  Eigenvalues in w (unsorted),
-// eigenvectors as the columns of v (row-major).  False if a block does not
-// converge within 50 p sweeps.
-bool sym_eig(std::vector<double>& a, int p, std::vector<double>& w, std::vector<double>& v) {
+// down the block, accumulated into vt as well.  Eigenvalues in w (unsorted),
+// eigenvectors as the rows of vt (row-major, so that a rotation touches two
+// contiguous rows).  False if a block does not converge within 50 p sweeps.
+bool sym_eig(std::vector<double>& a, int p, std::vector<double>& w, std::vector<double>& vt) {
   auto A = [&](int i, int j) -> double& { return a[(size_t)i * p + j]; };
-  v.assign((size_t)p * p, 0.0);
-  for (int i = 0; i < p; i++) v[(size_t)i * p + i] = 1.0;
+  vt.assign((size_t)p * p, 0.0);
+  for (int i = 0; i < p; i++) vt[(size_t)i * p + i] = 1.0;
+  std::vector<double> tv(p);
   std::vector<double> hv(p), u(p), wv(p);
   for (int k = 0; k + 2 < p; k++) {
     // reflection H = I - beta hv hv^T that maps column k below the diagonal onto
@@ -106,12 +107,16 @@ bool sym_eig(std::vector<double>& a, int p, std::vector<double>& w, std::vector<
       for (int j = 0; j < m; j++) A(k + 1 + i, k + 1 + j) -= hv[i] * wv[j] + wv[i] * hv[j];
     A(k + 1, k) = A(k, k + 1) = alpha;
     for (int i = 1; i < m; i++) A(k + 1 + i, k) = A(k, k + 1 + i) = 0.0;
-    for (int row = 0; row < p; row++) {   // v <- v H
-      double* vr = &v[(size_t)row * p + k + 1];
-      double t = 0.0;
-      for (int j = 0; j < m; j++) t += vr[j] * hv[j];
-      t *= beta;
-      for (int j = 0; j < m; j++) vr[j] -= t * hv[j];
+    // V <- V H, i.e. rows k+1.. of vt: vt_j -= beta hv_j (sum_i hv_i vt_i)
+    std::fill(tv.begin(), tv.end(), 0.0);
+    for (int j = 0; j < m; j++) {
+      const double* row = &vt[(size_t)(k + 1 + j) * p];
+      for (int c = 0; c < p; c++) tv[c] += hv[j] * row[c];
+    }
+    for (int j = 0; j < m; j++) {
+      double* row = &vt[(size_t)(k + 1 + j) * p];
+      const double f = beta * hv[j];
+      for (int c = 0; c < p; c++) row[c] -= f * tv[c];
     }
   }
   std::vector<double> d(p), e(p, 0.0);
@@ -149,11 +154,12 @@ bool sym_eig(std::vector<double>& a, int p, std::vector<double>& w, std::vector<
         e[k + 1] *= c;
         x = e[k];
       }
-      for (int row = 0; row < p; row++) {
-        double* vr = &v[(size_t)row * p];
-        const double y0 = vr[k], y1 = vr[k + 1];
-        vr[k] = c * y0 + sn * y1;
-        vr[k + 1] = -sn * y0 + c * y1;
+      double* r0 = &vt[(size_t)k * p];
+      double* r1 = &vt[(size_t)(k + 1) * p];
+      for (int col = 0; col < p; col++) {
+        const double y0 = r0[col], y1 = r1[col];
+        r0[col] = c * y0 + sn * y1;
+        r1[col] = -sn * y0 + c * y1;
       }
     }
   }
@@ -277,7 +283,7 @@ int top_eigvecs(const double* gram_dev, int b, int n, int r, hipStream_t st, dou
         theta[bi].resize(p);
         for (int j = 0; j < p; j++) {
           theta[bi][j] = w[ord[j]];
-          for (int i = 0; i < p; i++) vs[(size_t)i * p + j] = v[(size_t)i * p + ord[j]];
+          for (int i = 0; i < p; i++) vs[(size_t)i * p + j] = v[(size_t)ord[j] * p + i];
         }
       });
       if (std::find(failed.begin(), failed.end(), 1) != failed.end()) break;   // status 1
