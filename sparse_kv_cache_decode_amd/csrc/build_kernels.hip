@@ -379,76 +379,99 @@ hipError_t launch_gemm_f64_tn(const double* A, const double* B, double* C, int b
 }
 
 // ---------------------------------------------------------------------------
-// Projection A[b] = K_b Psi_b (S x HD times HD x r), fp32 accumulation, bf16 out
-// (FP8 E5M2 bytes with fp8).
+// Projection A[b] = K_b Psi_b (S x HD times HD x r) on MFMA 16x16x32 bf16.  Psi
+// comes split in two bf16 parts, hi = bf16(Psi) and lo = bf16(Psi - hi), so
+// K Psi = K hi + K lo up to about 2^-16 of Psi (K is exact in bf16); fp32
+// accumulation; bf16 out, or FP8 E5M2 bytes with fp8.  A workgroup takes 64 rows
+// and up to kProjTiles 16-column tiles; wave w owns rows w*16 .. w*16+15.  MFMA
+// operands: lane (row lc, kq) holds dims kq*8 .. +7 of its K row; lane (column lc,
+// kq) the same dims of its Psi^T row; output lane (column lc, kq) holds rows
+// kq*4 .. kq*4+3.
+
+constexpr int kProjTiles = 10;   // 160 columns: every rank up to 160 in one pass over K
+
+// double -> bf16 bits, one rounding to nearest even at the 8th significant bit
+// (the double is cut to 8 significant bits first, which float holds exactly).
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  u += (1ull << 44) - 1ull + ((u >> 45) & 1ull);
+  u &= ~((1ull << 45) - 1ull);
+  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+}
+
+__global__ void split_psi_kernel(const double* __restrict__ psi, int b, int HD, int r,
+                                 uint16_t* __restrict__ bt, uint16_t* __restrict__ psi_t) {
+  const int64_t n = (int64_t)b * HD * r;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int j = (int)(idx % r);
+  const int64_t bi = idx / ((int64_t)HD * r);
+  const int i = (int)((idx / r) % HD);
+  const double x = psi[idx];
+  const uint16_t hi = f64_to_bf16_rne(x);
+  bt[idx] = hi;
+  const int64_t dst = (bi * r + j) * HD + i;
+  psi_t[dst] = hi;
+  psi_t[n + dst] = f64_to_bf16_rne(x - (double)__uint_as_float((uint32_t)hi << 16));
+}
+
+hipError_t launch_split_psi(const double* psi, int b, int HD, int r, uint16_t* bt, uint16_t* psi_t,
+                            hipStream_t st) {
+  const int64_t n = (int64_t)b * HD * r;
+  split_psi_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(psi, b, HD, r, bt, psi_t);
+  return hipGetLastError();
+}
 
 __global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict__ k_pre,
-                                                      const float* __restrict__ psi, int64_t S,
+                                                      const uint16_t* __restrict__ psi_t, int nb, int64_t S,
                                                       int HD, int r, int64_t a_rows, bool fp8,
                                                       void* __restrict__ A) {
-  __shared__ float tk[32][64 + 1];   // [k][row]
-  __shared__ float tp[32][64 + 1];   // [k][col]
   const int b = blockIdx.z;
-  const int64_t m0 = (int64_t)blockIdx.x * 64;
-  const int n0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const uint16_t* kb = k_pre + (int64_t)b * S * HD;
-  const float* pb = psi + (int64_t)b * HD * r;
-  float acc[4][4] = {};
+  const int64_t row0 = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16;
+  const int n0 = blockIdx.y * kProjTiles * 16;
+  const int lane = threadIdx.x & 63, lc = lane & 15, kq = lane >> 4;
+  const int nt = min(kProjTiles, (r - n0) / 16);
+  // rows past S re-read row S-1; their outputs are not stored
+  const uint16_t* kp = k_pre + ((int64_t)b * S + min(row0 + lc, S - 1)) * HD + kq * 8;
+  const uint16_t* hi = psi_t + ((int64_t)b * r + n0 + lc) * HD + kq * 8;
+  const uint16_t* lo = hi + (int64_t)nb * r * HD;
+  f32x4 acc[kProjTiles];
+#pragma unroll
+  for (int t = 0; t < kProjTiles; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < HD; k0 += 32) {
-    // K tile: 64 rows x 32 k (8 elements per thread)
-    {
-      const int e = threadIdx.x;               // 256 = 64 rows x 4 groups of 8
-      const int rr = e >> 2, c8 = (e & 3) * 8;
-      const int64_t row = m0 + rr;
-      u32x4 w = {0, 0, 0, 0};
-      if (row < S) w = *reinterpret_cast<const u32x4*>(kb + row * HD + k0 + c8);
-      float x[8];
-      unpack8(w, x);
+    const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + k0));
 #pragma unroll
-      for (int q = 0; q < 8; q++) tk[c8 + q][rr] = x[q];
-    }
-    for (int e = threadIdx.x; e < 32 * 64; e += 256) {
-      const int kk = e / 64, cc = e % 64;
-      tp[kk][cc] = (n0 + cc < r) ? pb[(int64_t)(k0 + kk) * r + n0 + cc] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; kk++) {
-      float x[4], y[4];
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        x[q] = tk[kk][ty * 4 + q];
-        y[q] = tp[kk][tx * 4 + q];
+    for (int t = 0; t < kProjTiles; t++) {
+      if (t < nt) {
+        const int64_t o = (int64_t)t * 16 * HD + k0;
+        const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(hi + o));
+        const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lo + o));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[t], 0, 0, 0);
       }
-#pragma unroll
-      for (int p = 0; p < 4; p++)
-#pragma unroll
-        for (int q = 0; q < 4; q++) acc[p][q] = fmaf(x[p], y[q], acc[p][q]);
     }
-    __syncthreads();
   }
 #pragma unroll
-  for (int p = 0; p < 4; p++) {
-    const int64_t row = m0 + ty * 4 + p;
-    if (row >= S) continue;
+  for (int t = 0; t < kProjTiles; t++) {
+    if (t >= nt) continue;
+    const int col = n0 + t * 16 + lc;
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const int col = n0 + tx * 4 + q;
-      if (col >= r) continue;
+    for (int i = 0; i < 4; i++) {
+      const int64_t row = row0 + kq * 4 + i;
+      if (row >= S) continue;
       const int64_t at = ((int64_t)b * a_rows + row) * r + col;
       if (fp8)
-        static_cast<uint8_t*>(A)[at] = f32_to_e5m2(acc[p][q]);
+        static_cast<uint8_t*>(A)[at] = f32_to_e5m2(acc[t][i]);
       else
-        static_cast<uint16_t*>(A)[at] = f32_to_bf16(acc[p][q]);
+        static_cast<uint16_t*>(A)[at] = f32_to_bf16(acc[t][i]);
     }
   }
 }
 
-hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_t S, int HD, int r,
+hipError_t launch_project(const uint16_t* k_pre, const uint16_t* psi_t, int b, int64_t S, int HD, int r,
                           int64_t a_rows, bool fp8, void* A, hipStream_t st) {
-  dim3 grid((unsigned)((S + 63) / 64), (r + 63) / 64, b);
-  project_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, a_rows, fp8, A);
+  dim3 grid((unsigned)((S + 63) / 64), (r + kProjTiles * 16 - 1) / (kProjTiles * 16), b);
+  project_kernel<<<grid, 256, 0, st>>>(k_pre, psi_t, b, S, HD, r, a_rows, fp8, A);
   return hipGetLastError();
 }
 

@@ -6,9 +6,11 @@
 // "Matrix Computations", orthogonal iteration and the Rayleigh-Ritz procedure).
 // Every n x p product runs on the GPU in fp64: Y = G Q, the Gram matrices of the
 // blocks and the products with p x p factors.  The blocks are orthonormalised by
-// Cholesky QR applied twice (W = X^T X = R^T R on the host, X <- X R^-1 on the
-// GPU), falling back to modified Gram-Schmidt on the host if a factor breaks
-// down; the p x p Rayleigh-Ritz eigenproblem is solved on the host by Householder
+// Cholesky QR (W = X^T X = R^T R on the host, X <- X R^-1 on the GPU), once
+// between power steps and twice before each Rayleigh-Ritz step (a block that
+// is orthonormal only to about kappa^2 eps still spans the right subspace for
+// the next power step), falling back to modified Gram-Schmidt on the host if a
+// factor breaks down; the p x p Rayleigh-Ritz eigenproblem is solved on the host by Householder
 // tridiagonalisation and the implicit symmetric QR algorithm with Wilkinson
 // shifts (ibid., 8.3), one thread per batch element.  Converged when every wanted
 // Ritz pair has residual ||G u - theta u|| <= 1e-11 * theta_max.
@@ -223,8 +225,8 @@ int top_eigvecs(const double* gram_dev, int b, int n, int r, hipStream_t st, dou
   auto sync = [&] { return (*err = hipStreamSynchronize(st)) == hipSuccess; };
   auto ok = [&](hipError_t e) { return (*err = e) == hipSuccess; };
   // orthonormalise the columns of every block of x (device) in place
-  auto orth = [&](double* x) -> bool {
-    for (int pass = 0; pass < 2; pass++) {
+  auto orth = [&](double* x, int passes) -> bool {
+    for (int pass = 0; pass < passes; pass++) {
       if (!ok(launch_gemm_f64_tn(x, x, ds, b, p, p, n, st)) || !copy(hs.data(), ds, sq * b, hipMemcpyDeviceToHost) ||
           !sync())
         return false;
@@ -245,13 +247,13 @@ int top_eigvecs(const double* gram_dev, int b, int n, int r, hipStream_t st, dou
   for (int bi = 0; bi < b; bi++) start_block(&hq[blk * bi], n, p, 0x5eedull + (uint64_t)bi);
   int status = 2;
   const bool square = (p == n);   // q spans everything: one Rayleigh-Ritz is exact
-  if (copy(dq, hq.data(), blk * b, hipMemcpyHostToDevice) && orth(dq)) {
+  if (copy(dq, hq.data(), blk * b, hipMemcpyHostToDevice) && orth(dq, 2)) {
     status = 1;
     for (int round = 0; round < 60; round++) {
       bool good = true;
       for (int it = 0; it < (square ? 0 : 3) && good; it++)
         good = ok(launch_gemm_f64(gram_dev, dq, dy, b, n, p, n, st)) &&
-               copy(dq, dy, blk * b, hipMemcpyDeviceToDevice) && orth(dq);
+               copy(dq, dy, blk * b, hipMemcpyDeviceToDevice) && orth(dq, it == 2 ? 2 : 1);
       // Rayleigh-Ritz: H = Q^T G Q, H = V diag(theta) V^T, U = Q V, residuals G U - U diag(theta)
       good = good && ok(launch_gemm_f64(gram_dev, dq, dy, b, n, p, n, st)) &&
              ok(launch_gemm_f64_tn(dq, dy, ds, b, p, p, n, st)) &&

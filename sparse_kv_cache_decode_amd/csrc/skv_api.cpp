@@ -153,21 +153,6 @@ skv_status validate(const skv_config* c) {
   return SKV_OK;
 }
 
-// float64 -> bfloat16 bits, round to nearest even at the 8th significant bit.
-uint16_t f64_to_bf16(double x) {
-  uint64_t u;
-  std::memcpy(&u, &x, 8);
-  const uint64_t lsb = (u >> 45) & 1ull;
-  u += (1ull << 44) - 1ull + lsb;
-  u &= ~((1ull << 45) - 1ull);
-  double y;
-  std::memcpy(&y, &u, 8);
-  const float f = (float)y;   // exact: y has 8 significant bits
-  uint32_t b;
-  std::memcpy(&b, &f, 4);
-  return (uint16_t)(b >> 16);
-}
-
 // Kernels move bf16 and float data in 16-byte pieces.
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
@@ -417,10 +402,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const int nseg = gram_segments(b, S, HD);
   void* L_full = nullptr;
   double *gpart = nullptr, *gram = nullptr;
-  float* psi_f = nullptr;
+  uint16_t* psi_f = nullptr;   // Psi^T as bf16 hi and lo parts
   std::vector<double> psi((size_t)b * HD * r);
-  std::vector<float> psi32((size_t)b * HD * r);
-  std::vector<uint16_t> bt16((size_t)b * HD * r);
   std::vector<double> invf(kHeadDim / 2);
   int rc;
   hipError_t herr = hipSuccess;
@@ -434,7 +417,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   if (hipMalloc(&L_full, (size_t)P * n_c * lrow) != hipSuccess ||
       hipMalloc(&gpart, (size_t)b * nseg * HD * HD * 8) != hipSuccess ||
       hipMalloc(&gram, (size_t)b * HD * HD * 8) != hipSuccess ||
-      hipMalloc(&psi_f, (size_t)b * HD * r * 4) != hipSuccess) {
+      hipMalloc(&psi_f, (size_t)2 * b * HD * r * 2) != hipSuccess) {
     (void)hipGetLastError();
     if (L_full) (void)hipFree(L_full);
     if (gpart) (void)hipFree(gpart);
@@ -511,12 +494,10 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     release(h);
     return SKV_ERR_INTERNAL;
   }
-  for (size_t i = 0; i < psi.size(); i++) {
-    psi32[i] = (float)psi[i];
-    bt16[i] = f64_to_bf16(psi[i]);
-  }
-  HIP_TRY(hipMemcpyAsync(psi_f, psi32.data(), psi32.size() * 4, hipMemcpyHostToDevice, s));
-  HIP_TRY(hipMemcpyAsync(h->Bt, bt16.data(), bt16.size() * 2, hipMemcpyHostToDevice, s));
+  // Psi in fp64 through the (now free) Gram partials buffer, b*nseg*HD*HD >= b*HD*r
+  // doubles; B^T and the projection's hi/lo parts are rounded from it on the GPU
+  HIP_TRY(hipMemcpyAsync(gpart, psi.data(), psi.size() * 8, hipMemcpyHostToDevice, s));
+  HIP_TRY(launch_split_psi(gpart, b, HD, r, h->Bt, psi_f, s));
   HIP_TRY(launch_project(k_pre, psi_f, b, S, HD, r, h->a_rows, a8, h->A, s));
   HIP_TRY(launch_reset_cache(decode_args(h), s));
   HIP_TRY(hipStreamSynchronize(s));

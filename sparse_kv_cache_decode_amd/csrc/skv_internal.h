@@ -100,8 +100,13 @@ hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batc
 hipError_t launch_gemm_f64_tn(const double* A, const double* B, double* C, int batch, int M, int N,
                               int K, hipStream_t st);
 // A[b] rows 0..S-1 of a [b][a_rows][r] array
-// A: [b][a_rows][r] bf16, or bytes with fp8 (FP8 E5M2)
-hipError_t launch_project(const uint16_t* k_pre, const float* psi, int b, int64_t S, int HD, int r,
+// psi [b][HD][r] fp64 -> bt = bf16(psi) (same layout) and psi_t = Psi^T as bf16 hi
+// [b][r][HD] followed by bf16 lo = bf16(psi - hi) [b][r][HD]; round to nearest even
+hipError_t launch_split_psi(const double* psi, int b, int HD, int r, uint16_t* bt, uint16_t* psi_t,
+                            hipStream_t st);
+// A: [b][a_rows][r] bf16, or bytes with fp8 (FP8 E5M2); psi_t: Psi^T split into
+// bf16 hi [b][r][HD] followed by bf16 lo [b][r][HD]
+hipError_t launch_project(const uint16_t* k_pre, const uint16_t* psi_t, int b, int64_t S, int HD, int r,
                           int64_t a_rows, bool fp8, void* A, hipStream_t st);
 
 // ---- decode launchers (decode_kernels.hip)
