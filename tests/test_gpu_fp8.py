@@ -72,3 +72,15 @@ def test_fp8_a_lowrank_appended_rows():
     layer, _, _ = _run_append(_small(window=16, landmark_format="e5m2", a_format="e5m2"),
                               skv.SKV_NEW_LOWRANK, [0, 9, 20, 15], max_new=48)
     layer.close()
+
+
+def test_fp8_full_budget_no_outliers_no_window():
+    # K = n_cand = 256, one FP8 score block exactly; every chunk selected
+    s = _small(seq_len=2048, n_outlier=0, window=0, top_k=256, batch=1, landmark_format="e5m2",
+               a_format="e5m2")
+    assert s.n_cand == 256
+    _run(s, steps=2)
+
+
+def test_fp8_budget_of_one_temporal_cache_off():
+    _run(_small(top_k=1, batch=1, landmark_format="e5m2", a_format="e5m2"), steps=3, temporal=0)

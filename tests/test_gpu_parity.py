@@ -173,3 +173,12 @@ def test_eight_kv_heads_small_budget():
     # landmark value sits a bf16 rounding boundary away; on the GPU's landmarks
     # the selections agree
     _run(_small(batch=2, n_q_heads=32, n_kv_heads=8, seq_len=65536, top_k=60, n_outlier=10), steps=3)
+
+
+def test_rank_deficient_prefill():
+    # S = 64 tokens of 2 KV heads (n = 256) at r = 64: the Gram matrix has rank 64,
+    # below the eigensolver's block of p = 80 columns, so Cholesky QR breaks down
+    # after the first product and the blocks go through Gram-Schmidt on the host
+    s = _small(batch=1, n_q_heads=4, n_kv_heads=2, seq_len=64, rank=64, latent_rank=64, top_k=2,
+               n_outlier=1, window=0)
+    _run(s, steps=3)
