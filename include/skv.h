@@ -98,7 +98,9 @@ typedef int32_t skv_status;
  *   1 <= rank <= min(seq_len, n_kv_heads * head_dim), n_kv_heads * head_dim <= 2048,
  *   n_cand = seq_len/chunk - n_outlier - window/chunk, 1 <= top_k <= n_cand, top_k <= 4096.
  *   max_new_tokens >= 0 is the capacity for appended tokens (skv_append_token);
- *   new_token_mode is SKV_NEW_EXACT or SKV_NEW_LOWRANK.
+ *   new_token_mode is SKV_NEW_EXACT or SKV_NEW_LOWRANK; landmark_format and a_format
+ *   are SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2; reserved is 0.  An unknown enum
+ *   value or a non-zero reserved field gives SKV_ERR_INVALID_ARG.
  */
 typedef struct skv_config {
   int32_t batch;           /* b                                                   */
