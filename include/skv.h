@@ -208,7 +208,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
  * Selection uses fp32 scores; a chunk's score is max_g(logit_g/sqrt(d) - LSE_g),
  * the log of the pages' max over the group of softmax probabilities; ties go to
  * the lower chunk id.
- * Errors: INVALID_ARG, STATE, HIP.
+ * Errors: INVALID_ARG (null, misaligned or non-device pointer; checked before
+ * any launch), STATE, HIP.
  */
 skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t* chunk_ids,
                            void* stream);
@@ -228,17 +229,17 @@ skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t*
  * decode step attends to all appended tokens after the local window; landmarks,
  * outliers and the selection cover the pre-filled context only.
  * SKV_NEW_LOWRANK (ShadowKV+): a' = k' Psi (fp32 accumulation over the stored
- * bf16 Psi^T, rounded to bf16) becomes row seq_len + t of A, and RoPE(k') is kept
+ * bf16 Psi^T, rounded to the format of A) becomes row seq_len + t of A, and RoPE(k') is kept
  * exactly while the token is in the exact region: the last `window` tokens of the
  * completed chunks plus the chunk being filled.  When an append completes a chunk,
  * the oldest exact chunk leaves that region and becomes the last candidate of
- * every pair (never an outlier): its landmark is the bf16 mean of its stored
- * exact keys, its chunk id (seq_len - window)/chunk + (chunks completed so far)
+ * every pair (never an outlier): its landmark is the mean of its stored exact
+ * keys rounded to the landmark format, its chunk id (seq_len - window)/chunk + (chunks completed so far)
  * - 1; from the next decode step it is scored, selected, rebuilt from A and its
  * values read (from the value store, or from the appended values) like a
  * context chunk.
- * Errors: INVALID_ARG (null pointer), SHAPE (capacity max_new_tokens reached),
- * STATE, HIP.
+ * Errors: INVALID_ARG (null, misaligned or non-device pointer), SHAPE (capacity
+ * max_new_tokens reached), STATE, HIP.
  */
 skv_status skv_append_token(skv_layer* h, const uint16_t* k_new, const uint16_t* v_new, void* stream);
 

@@ -526,6 +526,8 @@ skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t*
   if (h->poisoned) return SKV_ERR_STATE;
   if (!q || !out || !chunk_ids) return SKV_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(chunk_ids, 4)) return SKV_ERR_INVALID_ARG;
+  // a host pointer here would fault the kernels: refuse it before any launch
+  if (!is_device_ptr(q) || !is_device_ptr(out) || !is_device_ptr(chunk_ids)) return SKV_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   DecodeArgs a = decode_args(h);
   a.q = q;
@@ -575,6 +577,7 @@ skv_status skv_append_token(skv_layer* h, const uint16_t* k_new, const uint16_t*
   if (!h || !k_new || !v_new) return SKV_ERR_INVALID_ARG;
   if (h->poisoned) return SKV_ERR_STATE;
   if (!aligned(k_new, 16) || !aligned(v_new, 16)) return SKV_ERR_INVALID_ARG;
+  if (!is_device_ptr(k_new) || !is_device_ptr(v_new)) return SKV_ERR_INVALID_ARG;
   if (h->n_new >= h->cfg.max_new_tokens) return SKV_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   {

@@ -121,7 +121,7 @@ def test_append_lowrank_full_rank_one_kv_head():
     layer.close()
 
 
-def test_misaligned_pointers_rejected_before_any_launch():
+def test_misaligned_or_host_pointers_rejected_before_any_launch():
     shape = _small(batch=1, seq_len=2048, top_k=9, n_outlier=2)
     k, v = synth.layer_cache_np(shape, 0, 1)
     kn, vn = synth.continuation_np(shape, 0, 1, 1)
@@ -137,6 +137,19 @@ def test_misaligned_pointers_rejected_before_any_launch():
     assert lib.skv_decode_step(layer.h, q.data_ptr(), out.data_ptr() + 4, ids.data_ptr(), None) == \
         skv.SKV_ERR_INVALID_ARG
     assert lib.skv_append_token(layer.h, knd.data_ptr() + 2, vnd.data_ptr(), None) == skv.SKV_ERR_INVALID_ARG
+    # aligned host (pageable) memory is refused too, before any launch
+    qh = torch.zeros((1, shape.n_q_heads, shape.head_dim), dtype=torch.bfloat16)
+    outh = torch.empty((1, shape.n_q_heads, shape.head_dim))
+    idsh = torch.empty((1, shape.n_kv_heads, shape.top_k), dtype=torch.int32)
+    assert qh.data_ptr() % 16 == 0 and outh.data_ptr() % 16 == 0
+    assert lib.skv_decode_step(layer.h, qh.data_ptr(), out.data_ptr(), ids.data_ptr(), None) == \
+        skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_decode_step(layer.h, q.data_ptr(), outh.data_ptr(), ids.data_ptr(), None) == \
+        skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_decode_step(layer.h, q.data_ptr(), out.data_ptr(), idsh.data_ptr(), None) == \
+        skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_append_token(layer.h, kn.data_ptr(), vnd.data_ptr(), None) == skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_append_token(layer.h, knd.data_ptr(), vn.data_ptr(), None) == skv.SKV_ERR_INVALID_ARG
     assert layer.stats()["new_tokens"] == 0 and layer.stats()["steps"] == 0
     layer.close()
 
