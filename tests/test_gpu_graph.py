@@ -3,7 +3,7 @@ replay, exactly what eager calls give on a twin layer built from the same
 inputs (same kernels, same work: bitwise equal), with eager work and
 synchronisations between the replays; with values in HBM and in pinned host
 memory (the gather's side stream forked from and joined back into the
-capturing stream)."""
+capturing stream), and with FP8 landmarks and A."""
 import pytest
 import torch
 
@@ -14,11 +14,13 @@ from oracle import shadowkv as O
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("placement", [skv.SKV_VALUES_DEVICE, skv.SKV_VALUES_HOST])
-def test_graph_replays_match_eager(placement):
+@pytest.mark.parametrize("placement,fmt", [(skv.SKV_VALUES_DEVICE, "bf16"), (skv.SKV_VALUES_HOST, "bf16"),
+                                           (skv.SKV_VALUES_DEVICE, "e5m2")])
+def test_graph_replays_match_eager(placement, fmt):
     shape = synth.Shape("graph", batch=8, n_q_heads=16, n_kv_heads=4, head_dim=128, seq_len=4096,
-                        rank=64, chunk=8, top_k=8, n_outlier=2, window=32, latent_rank=64)
-    print(f"[graph] pairs={shape.pairs} placement={placement}", flush=True)
+                        rank=64, chunk=8, top_k=8, n_outlier=2, window=32, latent_rank=64,
+                        landmark_format=fmt, a_format=fmt)
+    print(f"[graph] pairs={shape.pairs} placement={placement} storage={fmt}", flush=True)
     steps = 6
     k, v = synth.layer_cache_np(shape, 0, 0)
     q = synth.queries_np(shape, k, 0, steps, 0)
