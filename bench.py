@@ -268,7 +268,8 @@ def algorithmic_bytes(shape, misses_per_layer_step: float) -> dict:
     landmarks = P * shape.n_cand * d * FORMAT_BYTES[shape.landmark_format]
     q_bytes = shape.batch * shape.n_q_heads * d * 2
     out_bytes = shape.batch * shape.n_q_heads * d * 4
-    rebuild = misses_per_layer_step * C * (r * FORMAT_BYTES[shape.a_format] + d * 2) + P * r * d * 2
+    rebuild = misses_per_layer_step * C * (r * FORMAT_BYTES[shape.a_format] + d * 2) + \
+        P * r * d * FORMAT_BYTES[shape.b_format]
     attn = P * shape.tokens_attended * d * 2 * 2
     return {"score": landmarks + q_bytes, "rebuild": rebuild, "attention": attn + out_bytes,
             "total": landmarks + q_bytes + rebuild + attn + out_bytes}
@@ -295,6 +296,8 @@ def main():
                     help="landmark storage: bf16 (the pages' precision) or FP8 E5M2 (their precision study)")
     ap.add_argument("--a-format", choices=["bf16", "e5m2"], default="bf16",
                     help="storage of the rows of A: bf16 (the pages' precision) or FP8 E5M2")
+    ap.add_argument("--b-format", choices=["bf16", "e5m2"], default="bf16",
+                    help="storage of B (Psi^T): bf16 (the pages' precision) or FP8 E5M2")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
                     help="replay each timed step (all layers) as one captured HIP graph; off: launch eagerly")
     ap.add_argument("--phase-steps", type=int, default=16,
@@ -342,8 +345,8 @@ def main():
         return 2
     if args.layers:
         shape = shape.replace(layers=args.layers)
-    if args.landmarks != "bf16" or args.a_format != "bf16":
-        shape = shape.replace(landmark_format=args.landmarks, a_format=args.a_format)
+    if args.landmarks != "bf16" or args.a_format != "bf16" or args.b_format != "bf16":
+        shape = shape.replace(landmark_format=args.landmarks, a_format=args.a_format, b_format=args.b_format)
     L, W, K = shape.layers, args.warmup, args.steps
     PH = max(1, args.phase_steps)
     total = W + K + PH            # warm-up, timed and phase-timing steps
@@ -498,13 +501,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" + ("" if shape.landmark_format == "bf16" else ", e5m2 landmarks (fp16 MFMA scoring)")
-                 + ("" if shape.a_format == "bf16" else ", e5m2 rows of A (widened to bf16 for the rebuild)"),
+                 + ("" if shape.a_format == "bf16" else ", e5m2 rows of A (widened to bf16 for the rebuild)")
+                 + ("" if shape.b_format == "bf16" else ", e5m2 B (widened to bf16 for the rebuild)"),
         "data": "synthetic",
         "config": {"workload": f"{shape.name}: {L} layers, batch {shape.batch}, S={shape.seq_len}, "
                                f"{shape.n_q_heads} q / {shape.n_kv_heads} KV heads, d={shape.head_dim}, "
                                f"r={shape.rank}, C={shape.chunk}, K={shape.top_k}, O={shape.n_outlier}, "
                                f"window {shape.window}, {shape.landmark_format} landmarks, "
-                               f"{shape.a_format} A, "
+                               f"{shape.a_format} A, {shape.b_format} B, "
                                f"values in {'pinned host memory' if host else 'HBM'}, "
                                f"{'AR(1)-drifting' if args.queries == 'drift' else 'independent'} queries"
                                + ("" if new_mode is None else

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 5
+#define SKV_ABI_VERSION 6
 
 typedef int32_t skv_status;
 #define SKV_OK 0
@@ -67,13 +67,13 @@ typedef int32_t skv_status;
                                   gathered over PCIe on a side stream that overlaps
                                   the key rebuild                                   */
 
-/* Storage formats of the landmarks (chunk means) and of the rows of A.  FP8
- * follows the precision study of the paper-graph-ui summary of ShadowKV
+/* Storage formats of the landmarks (chunk means), of the rows of A and of B.
+ * FP8 follows the precision study of the paper-graph-ui summary of ShadowKV
  * (section 5, Tables 9 and 10), which runs the method in torch.float8_e5m2.
- * Here it applies to the two large stores: the landmarks (the stream that
- * dominates a decode step's bytes) and A (S x r per batch element).  B stays
- * bfloat16: it is about 1/100 of A's size and enters every rebuilt key (the
- * summary's section 7 expects A to tolerate lower precision than B). */
+ * The landmarks are the stream that dominates a decode step's bytes and A the
+ * largest store (S x r per batch element); B is about 1/100 of A's size and
+ * enters every rebuilt key (the summary's section 7 expects it to need more
+ * precision than A), so each format is chosen on its own. */
 #define SKV_FORMAT_BF16 0      /* bfloat16                                           */
 #define SKV_FORMAT_FP8_E5M2 1  /* FP8 E5M2 (1 sign, 5 exponent bits with bias 15, 2
                                   mantissa bits, the torch.float8_e5m2 format), each
@@ -81,8 +81,9 @@ typedef int32_t skv_status;
                                   Landmarks (128 bytes each) are widened to fp16
                                   exactly and scored with q in fp16 (q's bf16 values
                                   are exact there in fp16's normal range,
-                                  |q| <= 65504); rows of A (r bytes each) are widened
-                                  to bf16 exactly for the key rebuild              */
+                                  |q| <= 65504); rows of A (r bytes each) and B are
+                                  widened to bf16 exactly for the key rebuild and
+                                  the low-rank append                              */
 
 /* How appended (generated) tokens keep their keys. */
 #define SKV_NEW_EXACT 0        /* post-RoPE key kept exactly (ShadowKV)             */
@@ -98,9 +99,9 @@ typedef int32_t skv_status;
  *   1 <= rank <= min(seq_len, n_kv_heads * head_dim), n_kv_heads * head_dim <= 2048,
  *   n_cand = seq_len/chunk - n_outlier - window/chunk, 1 <= top_k <= n_cand, top_k <= 4096.
  *   max_new_tokens >= 0 is the capacity for appended tokens (skv_append_token);
- *   new_token_mode is SKV_NEW_EXACT or SKV_NEW_LOWRANK; landmark_format and a_format
- *   are SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2; reserved is 0.  An unknown enum
- *   value or a non-zero reserved field gives SKV_ERR_INVALID_ARG.
+ *   new_token_mode is SKV_NEW_EXACT or SKV_NEW_LOWRANK; landmark_format, a_format
+ *   and b_format are SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2.  An unknown enum value
+ *   gives SKV_ERR_INVALID_ARG.
  */
 typedef struct skv_config {
   int32_t batch;           /* b                                                   */
@@ -122,7 +123,7 @@ typedef struct skv_config {
   int32_t new_token_mode;  /* SKV_NEW_EXACT or SKV_NEW_LOWRANK                     */
   int32_t a_format;        /* SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2 (rows of A,
                               also those appended in SKV_NEW_LOWRANK mode)        */
-  int32_t reserved;        /* must be 0                                           */
+  int32_t b_format;        /* SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2 (B = Psi^T)   */
 } skv_config;
 
 typedef struct skv_layer skv_layer;   /* opaque; owns all derived state */
@@ -144,7 +145,8 @@ typedef struct skv_stats {
  * Host copies of the built state, for inspection and parity checks.  Any
  * pointer may be NULL to skip that tensor.  Sizes (elements):
  *   A          bf16 [b][S][r]             (bf16 values also with FP8 storage)
- *   B          bf16 [b][H_kv][r][d]       (the per-head right factor)
+ *   B          bf16 [b][H_kv][r][d]       (the per-head right factor; bf16 values
+ *                                          also with FP8 storage)
  *   landmarks  bf16 [b][H_kv][n_cand][d]  (bf16 values also with FP8 storage, which
  *                                          they hold exactly; candidate chunks of the pre-filled
  *                                          context, ascending chunk id; chunks

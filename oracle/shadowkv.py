@@ -40,9 +40,9 @@ when ``storage_rounding`` is on; with ``landmark_format = "e5m2"`` the
 landmarks are rounded instead to FP8 E5M2 (the torch.float8_e5m2 precision of
 the summary's precision-sensitivity paragraph, section 5), and with
 ``a_format = "e5m2"`` the rows of A likewise (context rows and the rows of
-generated tokens); B stays bfloat16 (the summary's section 7 expects A, whose
-rows are each used once per selection, to tolerate lower precision than B,
-which enters every rebuilt key).  Generated tokens: the t-th appended token
+generated tokens), and with ``b_format = "e5m2"`` B (bfloat16 by default: the
+summary's section 7 expects A, whose rows are each used once per selection, to
+tolerate lower precision than B, which enters every rebuilt key).  Generated tokens: the t-th appended token
 (t = 0, 1, ...) sits at position seq_len + t and its value is kept as given.
 Exact mode (ShadowKV's assembly): every decode step attends to all of them
 with the exact key RoPE(k'), and they take no part in scoring or selection.
@@ -192,6 +192,7 @@ class Config:
     rope_theta: float = 500000.0
     landmark_format: str = "bf16"    # storage of the landmarks: "bf16" or "e5m2" (FP8)
     a_format: str = "bf16"           # storage of the rows of A: "bf16" or "e5m2" (FP8)
+    b_format: str = "bf16"           # storage of B: "bf16" or "e5m2" (FP8)
 
     @property
     def group(self):
@@ -215,7 +216,7 @@ def config_from(shape) -> Config:
     return Config(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                   shape.seq_len, shape.rank, shape.chunk, shape.top_k, shape.n_outlier,
                   shape.window, shape.rope_theta, getattr(shape, "landmark_format", "bf16"),
-                  getattr(shape, "a_format", "bf16"))
+                  getattr(shape, "a_format", "bf16"), getattr(shape, "b_format", "bf16"))
 
 
 @dataclasses.dataclass
@@ -268,12 +269,13 @@ def build(cfg: Config, k_pre, v, storage_rounding: bool = True) -> State:
     rnd = round_bf16 if storage_rounding else (lambda x: x)
     rnd_l = (round_e5m2 if cfg.landmark_format == "e5m2" else round_bf16) if storage_rounding else (lambda x: x)
     rnd_a = (round_e5m2 if cfg.a_format == "e5m2" else round_bf16) if storage_rounding else (lambda x: x)
+    rnd_b = (round_e5m2 if cfg.b_format == "e5m2" else round_bf16) if storage_rounding else (lambda x: x)
     pos = np.arange(S)
 
     As, Bs, sigs, Ls, cands, outs, mcs, kos, vos, kws, vws = ([] for _ in range(11))
     for bi in range(b):
         a, bm, sig = truncated_svd(k_pre[bi], cfg.rank, H)
-        As.append(rnd_a(a)); Bs.append(rnd(bm)); sigs.append(sig)
+        As.append(rnd_a(a)); Bs.append(rnd_b(bm)); sigs.append(sig)
         kr = apply_rope(k_pre[bi].reshape(S, H, d).transpose(1, 0, 2), pos, cfg.rope_theta)
         lm = landmarks(kr, C)                      # [H, n_c, d]
         mc = chunk_min_cos(kr, lm, C)              # [H, n_c]

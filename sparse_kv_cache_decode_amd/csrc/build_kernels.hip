@@ -399,8 +399,21 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
   return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
 }
 
-__global__ void split_psi_kernel(const double* __restrict__ psi, int b, int HD, int r,
-                                 uint16_t* __restrict__ bt, uint16_t* __restrict__ psi_t) {
+// double -> FP8 E5M2 byte, one rounding to nearest even (2 mantissa bits kept;
+// below 2^-14 the grid is 2^-16; past 57344 the result is inf).
+__device__ __forceinline__ uint8_t f64_to_e5m2_rne(double x) {
+  const uint32_t sign = (uint32_t)((uint64_t)__double_as_longlong(x) >> 56) & 0x80u;
+  const double ax = fabs(x);
+  if (ax < 0x1p-14) return (uint8_t)(sign | (uint32_t)rint(ax * 65536.0));
+  uint64_t v = (uint64_t)__double_as_longlong(ax);
+  v += (1ull << 49) - 1ull + ((v >> 50) & 1ull);
+  const int e = (int)(v >> 52) - 1023 + 15;
+  if (e >= 31) return (uint8_t)(sign | 0x7cu);
+  return (uint8_t)(sign | ((uint32_t)e << 2) | (uint32_t)((v >> 50) & 3ull));
+}
+
+__global__ void split_psi_kernel(const double* __restrict__ psi, int b, int HD, int r, bool b8,
+                                 void* __restrict__ bt, uint16_t* __restrict__ psi_t) {
   const int64_t n = (int64_t)b * HD * r;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
@@ -409,16 +422,19 @@ __global__ void split_psi_kernel(const double* __restrict__ psi, int b, int HD, 
   const int i = (int)((idx / r) % HD);
   const double x = psi[idx];
   const uint16_t hi = f64_to_bf16_rne(x);
-  bt[idx] = hi;
+  if (b8)
+    static_cast<uint8_t*>(bt)[idx] = f64_to_e5m2_rne(x);
+  else
+    static_cast<uint16_t*>(bt)[idx] = hi;
   const int64_t dst = (bi * r + j) * HD + i;
   psi_t[dst] = hi;
   psi_t[n + dst] = f64_to_bf16_rne(x - (double)__uint_as_float((uint32_t)hi << 16));
 }
 
-hipError_t launch_split_psi(const double* psi, int b, int HD, int r, uint16_t* bt, uint16_t* psi_t,
+hipError_t launch_split_psi(const double* psi, int b, int HD, int r, bool b8, void* bt, uint16_t* psi_t,
                             hipStream_t st) {
   const int64_t n = (int64_t)b * HD * r;
-  split_psi_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(psi, b, HD, r, bt, psi_t);
+  split_psi_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(psi, b, HD, r, b8, bt, psi_t);
   return hipGetLastError();
 }
 

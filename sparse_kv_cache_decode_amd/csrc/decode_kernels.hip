@@ -798,8 +798,12 @@ constexpr int rebuild_stage_bytes() {
 // before a barrier) and `stage` an LDS buffer of rebuild_stage_bytes<NSTEP>().
 // Returns once the stores are issued; the caller orders them against later
 // readers.
-// A8: rows of A stored as FP8 E5M2 (r bytes per row) instead of bf16.
-template <int C, int NSTEP, bool A8>
+// A8: rows of A stored as FP8 E5M2 (r bytes per row) instead of bf16.  B8: B^T
+// stored as FP8 E5M2; its operand fragments (8 bytes per lane and column tile,
+// 20 KB per pair at r = 160, read by every wave from L2) are then loaded straight
+// into registers and widened to bf16, with one k-step per iteration, instead of
+// the staged direct-to-LDS slices of the bf16 path.
+template <int C, int NSTEP, bool A8, bool B8>
 __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const int* mchunk, const int* mslot,
                                              u32x4* stage) {
   const int b = p / a.n_kv, h = p % a.n_kv;
@@ -844,6 +848,36 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+  if constexpr (B8) {
+    const uint8_t* Bt8 = reinterpret_cast<const uint8_t*>(a.Bt) +
+                         ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
+    for (int ks = 0; ks < r; ks += 32) {
+      // lanes whose k-group lies past r (r % 32 == 16) read group 0 and zero B
+      const bool kin = ks + lk * 8 < r;
+      const int kk = kin ? ks + lk * 8 : ks;
+      u32x4 av[2], bw[8];
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        if constexpr (A8) {
+          const uint2 w8 = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.A) + arow[mt] + kk);
+          av[mt] = e5m2x8_to_bf16x8(w8.x, w8.y);
+        } else {
+          av[mt] = *reinterpret_cast<const u32x4*>(a.A + arow[mt] + kk);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; t++) {
+        const uint2 w8 = *reinterpret_cast<const uint2*>(Bt8 + (int64_t)(t * 16 + lr) * r + kk);
+        bw[t] = kin ? e5m2x8_to_bf16x8(w8.x, w8.y) : (u32x4){0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int t = 0; t < 8; t++)
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++)
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[mt]),
+                                                               __builtin_bit_cast(bf16x8, bw[t]), acc[mt][t], 0, 0, 0);
+    }
+  } else {
   for (int ks = 0; ks < r; ks += NSTEP * 32) {
     const int kn = min(NSTEP * 32, r - ks);
     if (ks > 0) __syncthreads();                 // previous slice fully consumed
@@ -871,6 +905,7 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
       __builtin_amdgcn_sched_barrier(0);         // keep the groups in issue order
     }
     mfma_steps<NSTEP, 0, AFrag>(af, kn, lk, baddr, acc);
+  }
   }
   __syncthreads();
   // epilogue: RoPE on (col, col + 64) pairs, bf16 rows staged in LDS
@@ -902,7 +937,7 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
   }
 }
 
-template <int C, int NSTEP, bool A8>
+template <int C, int NSTEP, bool A8, bool B8>
 __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
   __shared__ u32x4 stage[rebuild_stage_bytes<NSTEP>() / 16];
@@ -924,18 +959,22 @@ __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
-  rebuild_tile<C, NSTEP, A8>(a, p, mchunk, mslot, stage);
+  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, mslot, stage);
 }
 
 template <int C, bool A8>
 static hipError_t launch_rebuild_c(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  if (a.b_format == SKV_FORMAT_FP8_E5M2) {
+    rebuild_kernel<C, 1, A8, true><<<grid, 256, 0, st>>>(a);   // one k-step per iteration
+    return hipGetLastError();
+  }
   switch (min(kMaxSteps, (a.rank + 31) / 32)) {
-    case 1: rebuild_kernel<C, 1, A8><<<grid, 256, 0, st>>>(a); break;
-    case 2: rebuild_kernel<C, 2, A8><<<grid, 256, 0, st>>>(a); break;
-    case 3: rebuild_kernel<C, 3, A8><<<grid, 256, 0, st>>>(a); break;
-    case 4: rebuild_kernel<C, 4, A8><<<grid, 256, 0, st>>>(a); break;
-    case 5: rebuild_kernel<C, 5, A8><<<grid, 256, 0, st>>>(a); break;
-    default: rebuild_kernel<C, kMaxSteps, A8><<<grid, 256, 0, st>>>(a); break;
+    case 1: rebuild_kernel<C, 1, A8, false><<<grid, 256, 0, st>>>(a); break;
+    case 2: rebuild_kernel<C, 2, A8, false><<<grid, 256, 0, st>>>(a); break;
+    case 3: rebuild_kernel<C, 3, A8, false><<<grid, 256, 0, st>>>(a); break;
+    case 4: rebuild_kernel<C, 4, A8, false><<<grid, 256, 0, st>>>(a); break;
+    case 5: rebuild_kernel<C, 5, A8, false><<<grid, 256, 0, st>>>(a); break;
+    default: rebuild_kernel<C, kMaxSteps, A8, false><<<grid, 256, 0, st>>>(a); break;
   }
   return hipGetLastError();
 }
@@ -1006,7 +1045,10 @@ __global__ __launch_bounds__(kAppendThreads) void append_project_kernel(DecodeAr
   const int b = blockIdx.x;
   const int HD = a.n_kv * kHeadDim, r = a.rank, tid = threadIdx.x;
   const uint16_t* kp = k_new + (int64_t)b * HD;
-  const uint16_t* Bt = a.Bt + (int64_t)b * HD * r;
+  const bool b8 = a.b_format == SKV_FORMAT_FP8_E5M2;
+  // B^T of the batch element: bf16, or FP8 bytes (element offsets the same)
+  const uint16_t* Bt = b8 ? reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.Bt) + (int64_t)b * HD * r)
+                          : a.Bt + (int64_t)b * HD * r;
   for (int i = tid; i < HD; i += kAppendThreads) ks[i] = bf16_to_f32(kp[i]);
   __syncthreads();
   // thread (row group g, column piece c) sums rows g, g + ng, ... of B^T over its
@@ -1018,8 +1060,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_project_kernel(DecodeAr
     for (int i0 = g; i0 < HD; i0 += 8 * ng) {
       u32x4 w[8];
 #pragma unroll
-      for (int m = 0; m < 8; m++)
-        w[m] = *reinterpret_cast<const u32x4*>(Bt + (int64_t)min(i0 + m * ng, HD - 1) * r + c * 8);
+      for (int m = 0; m < 8; m++) {
+        const int64_t at = (int64_t)min(i0 + m * ng, HD - 1) * r + c * 8;
+        if (b8) {
+          const uint2 w8 = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(Bt) + at);
+          w[m] = e5m2x8_to_bf16x8(w8.x, w8.y);
+        } else {
+          w[m] = *reinterpret_cast<const u32x4*>(Bt + at);
+        }
+      }
 #pragma unroll
       for (int m = 0; m < 8; m++) {
         const int i = i0 + m * ng;

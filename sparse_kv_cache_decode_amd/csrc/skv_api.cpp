@@ -119,7 +119,7 @@ skv_status validate(const skv_config* c) {
   if (c->landmark_format != SKV_FORMAT_BF16 && c->landmark_format != SKV_FORMAT_FP8_E5M2)
     return SKV_ERR_INVALID_ARG;
   if (c->a_format != SKV_FORMAT_BF16 && c->a_format != SKV_FORMAT_FP8_E5M2) return SKV_ERR_INVALID_ARG;
-  if (c->reserved != 0) return SKV_ERR_INVALID_ARG;
+  if (c->b_format != SKV_FORMAT_BF16 && c->b_format != SKV_FORMAT_FP8_E5M2) return SKV_ERR_INVALID_ARG;
   if (c->value_placement != SKV_VALUES_DEVICE && c->value_placement != SKV_VALUES_HOST)
     return SKV_ERR_INVALID_ARG;
   if (c->temporal_cache != 0 && c->temporal_cache != 1) return SKV_ERR_INVALID_ARG;
@@ -224,6 +224,7 @@ DecodeArgs decode_args(skv_layer* h) {
   // logits rows padded to 16 bytes
   a.landmark_format = c.landmark_format;
   a.a_format = c.a_format;
+  a.b_format = c.b_format;
   a.cpb = c.landmark_format == SKV_FORMAT_FP8_E5M2 ? kScoreRows8 : kScoreRows;
   a.nb_score = (h->n_cand + a.cpb - 1) / a.cpb;
   a.ncp = (h->n_cand + 3) / 4 * 4;
@@ -361,7 +362,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   Carver cv;
   const bool a8 = c.a_format == SKV_FORMAT_FP8_E5M2;
   const size_t oA = cv.take<uint8_t>((size_t)b * h->a_rows * r * (a8 ? 1 : 2));
-  const size_t oBt = cv.take<uint16_t>((size_t)b * HD * r);
+  const bool b8 = c.b_format == SKV_FORMAT_FP8_E5M2;
+  const size_t oBt = cv.take<uint8_t>((size_t)b * HD * r * (b8 ? 1 : 2));
   const size_t oL = cv.take<uint8_t>((size_t)P * cap * lrow);
   const size_t oKo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
   const size_t oVo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
@@ -497,7 +499,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   // Psi in fp64 through the (now free) Gram partials buffer, b*nseg*HD*HD >= b*HD*r
   // doubles; B^T and the projection's hi/lo parts are rounded from it on the GPU
   HIP_TRY(hipMemcpyAsync(gpart, psi.data(), psi.size() * 8, hipMemcpyHostToDevice, s));
-  HIP_TRY(launch_split_psi(gpart, b, HD, r, h->Bt, psi_f, s));
+  HIP_TRY(launch_split_psi(gpart, b, HD, r, b8, h->Bt, psi_f, s));
   HIP_TRY(launch_project(k_pre, psi_f, b, S, HD, r, h->a_rows, a8, h->A, s));
   HIP_TRY(launch_reset_cache(decode_args(h), s));
   HIP_TRY(hipStreamSynchronize(s));
@@ -663,7 +665,13 @@ skv_status skv_export_state(const skv_layer* hc, const skv_state_host* d) {
                         hipMemcpyDeviceToHost));
   if (d->B) {
     std::vector<uint16_t> bt((size_t)b * HD * r);
-    HIP_TRY(hipMemcpy(bt.data(), h->Bt, bt.size() * 2, hipMemcpyDeviceToHost));
+    if (c.b_format == SKV_FORMAT_FP8_E5M2) {   // FP8 bytes widened to bf16
+      std::vector<uint8_t> b8((size_t)b * HD * r);
+      HIP_TRY(hipMemcpy(b8.data(), h->Bt, b8.size(), hipMemcpyDeviceToHost));
+      for (size_t i = 0; i < b8.size(); i++) bt[i] = e5m2_to_bf16(b8[i]);
+    } else {
+      HIP_TRY(hipMemcpy(bt.data(), h->Bt, bt.size() * 2, hipMemcpyDeviceToHost));
+    }
     for (int bi = 0; bi < b; bi++)
       for (int hh = 0; hh < H; hh++)
         for (int k = 0; k < r; k++)

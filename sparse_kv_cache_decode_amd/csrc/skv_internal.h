@@ -22,6 +22,7 @@ struct DecodeArgs {
   int n_c;                    // chunks of the pre-filled context (S / C)
   int landmark_format;        // SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2
   int a_format;               // the same for the rows of A
+  int b_format;               // the same for B^T
   int n_new_tokens, n_new_units, max_new;   // appended tokens, their units, capacity
   int n_fold;                 // appended chunks folded into the candidates (low-rank mode)
   int64_t seq_len;
@@ -37,7 +38,7 @@ struct DecodeArgs {
   const uint16_t* L;          // [P][cand_stride][d] bf16 (bytes for FP8), first n_cand rows in use
   const int32_t* cand_map;    // [P][cand_stride]
   const uint16_t* A;          // [b][a_rows][r] bf16 (bytes for FP8)
-  const uint16_t* Bt;         // [b][Hkv*d][r]
+  const uint16_t* Bt;         // [b][HD][r] bf16 (bytes for FP8)         // [b][Hkv*d][r]
   int rank;
   const uint16_t* k_out;      // [P][O*C][d]
   const uint16_t* v_out;
@@ -100,9 +101,10 @@ hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batc
 hipError_t launch_gemm_f64_tn(const double* A, const double* B, double* C, int batch, int M, int N,
                               int K, hipStream_t st);
 // A[b] rows 0..S-1 of a [b][a_rows][r] array
-// psi [b][HD][r] fp64 -> bt = bf16(psi) (same layout) and psi_t = Psi^T as bf16 hi
-// [b][r][HD] followed by bf16 lo = bf16(psi - hi) [b][r][HD]; round to nearest even
-hipError_t launch_split_psi(const double* psi, int b, int HD, int r, uint16_t* bt, uint16_t* psi_t,
+// psi [b][HD][r] fp64 -> bt = bf16(psi), or FP8 E5M2 bytes with b8 (same layout), and
+// psi_t = Psi^T as bf16 hi [b][r][HD] followed by bf16 lo = bf16(psi - hi) [b][r][HD];
+// every rounding to nearest even, once, from the fp64 value
+hipError_t launch_split_psi(const double* psi, int b, int HD, int r, bool b8, void* bt, uint16_t* psi_t,
                             hipStream_t st);
 // A: [b][a_rows][r] bf16, or bytes with fp8 (FP8 E5M2); psi_t: Psi^T split into
 // bf16 hi [b][r][HD] followed by bf16 lo [b][r][HD]

@@ -37,7 +37,7 @@ class SkvConfig(ctypes.Structure):
                 ("value_placement", ctypes.c_int32), ("rope_theta", ctypes.c_double),
                 ("temporal_cache", ctypes.c_int32), ("landmark_format", ctypes.c_int32),
                 ("max_new_tokens", ctypes.c_int32), ("new_token_mode", ctypes.c_int32),
-                ("a_format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("a_format", ctypes.c_int32), ("b_format", ctypes.c_int32)]
 
 
 class SkvStats(ctypes.Structure):
@@ -105,14 +105,15 @@ def skv_abi_version() -> int:
 def make_config(shape, value_placement: int = SKV_VALUES_DEVICE, temporal_cache: int = 1,
                 max_new_tokens: int = 0, new_token_mode: int = SKV_NEW_EXACT) -> SkvConfig:
     """skv_config from any object with the ShadowKV shape fields (storage of
-    the landmarks and of A from its optional ``landmark_format`` and
-    ``a_format``: "bf16" or "e5m2")."""
+    the landmarks, of A and of B from its optional ``landmark_format``,
+    ``a_format`` and ``b_format``: "bf16" or "e5m2")."""
     lfmt = FORMATS[getattr(shape, "landmark_format", "bf16")]
     afmt = FORMATS[getattr(shape, "a_format", "bf16")]
+    bfmt = FORMATS[getattr(shape, "b_format", "bf16")]
     return SkvConfig(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                      shape.seq_len, shape.rank, shape.chunk, shape.top_k, shape.n_outlier,
                      shape.window, value_placement, float(shape.rope_theta), temporal_cache, lfmt,
-                     max_new_tokens, new_token_mode, afmt, 0)
+                     max_new_tokens, new_token_mode, afmt, bfmt)
 
 
 def _ptr(t) -> int | None:

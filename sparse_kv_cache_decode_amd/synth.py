@@ -66,6 +66,7 @@ class Shape:
     noise: float = 0.05
     landmark_format: str = "bf16"   # landmark storage: "bf16" or "e5m2" (FP8)
     a_format: str = "bf16"          # storage of the rows of A: "bf16" or "e5m2" (FP8)
+    b_format: str = "bf16"          # storage of B: "bf16" or "e5m2" (FP8)
 
     @property
     def group(self) -> int:

@@ -21,6 +21,8 @@ Bars (floating point from bf16 storage with fp32 accumulation):
   have passed this bar, and the tie margin then covers the fp32 arithmetic of
   the decode step alone (logit error at most 128 * 2^-24 * sum|q_d L_d| / sqrt(d),
   about 2e-4 at the workloads' magnitudes);
+* B: each well-determined column within one spacing of its storage format
+  (bf16, or E5M2 with FP8 storage) of the oracle's;
 * rows of A: within 2^-7 relative of the oracle's (bf16; both sides round the
   same product, the GPU's from an fp32 projection K Psi, the oracle's from its
   fp64 U_r Sigma_r); with FP8 storage each value the oracle's or one E5M2
@@ -171,7 +173,10 @@ def check_build(gpu: dict, st: O.State):
         well = dk < 1e-4
         gb, ob = B[bi][:, well], st.B[bi][:, well]                    # [H, n_well, d]
         _, e = np.frexp(ob)
-        spacing = np.where(ob == 0, 0.0, np.ldexp(1.0, e - 8))
+        if cfg.b_format == "e5m2":
+            spacing = np.where(np.abs(ob) < 2.0 ** -14, 2.0 ** -16, np.ldexp(1.0, e - 3))
+        else:
+            spacing = np.where(ob == 0, 0.0, np.ldexp(1.0, e - 8))
         excess = np.abs(gb - ob) - spacing - 1e-9 - dk[well][None, :, None]
         assert excess.size == 0 or excess.max() <= 0, f"B differs beyond rounding ({excess.max()})"
         if cfg.a_format == "e5m2":

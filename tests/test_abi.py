@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert skv.skv_abi_version() == 5
+    assert skv.skv_abi_version() == 6
     seen = set()
     for code in range(8):
         s = skv.skv_status_string(code)
@@ -71,7 +71,7 @@ def _cfg(**kw):
     (dict(temporal_cache=3), skv.SKV_ERR_INVALID_ARG),
     (dict(landmark_format=2), skv.SKV_ERR_INVALID_ARG),
     (dict(a_format=-1), skv.SKV_ERR_INVALID_ARG),
-    (dict(reserved=1), skv.SKV_ERR_INVALID_ARG),
+    (dict(b_format=7), skv.SKV_ERR_INVALID_ARG),
     (dict(batch=0), skv.SKV_ERR_SHAPE),
     (dict(max_new_tokens=-1), skv.SKV_ERR_SHAPE),
     (dict(new_token_mode=2), skv.SKV_ERR_INVALID_ARG),
@@ -117,7 +117,7 @@ int main(void) {
          sizeof(skv_stats), sizeof(skv_state_host));
   P(skv_config, seq_len) P(skv_config, rope_theta) P(skv_config, temporal_cache)
   P(skv_config, landmark_format) P(skv_config, max_new_tokens) P(skv_config, new_token_mode)
-  P(skv_config, a_format) P(skv_config, reserved)
+  P(skv_config, a_format) P(skv_config, b_format)
   P(skv_stats, last_alpha) P(skv_stats, last_host_bytes) P(skv_stats, new_tokens)
   P(skv_state_host, eigvals)
   return 0;
@@ -140,7 +140,7 @@ int main(void) {
                               "skv_config.max_new_tokens": (skv.SkvConfig, "max_new_tokens"),
                               "skv_config.new_token_mode": (skv.SkvConfig, "new_token_mode"),
                               "skv_config.a_format": (skv.SkvConfig, "a_format"),
-                              "skv_config.reserved": (skv.SkvConfig, "reserved"),
+                              "skv_config.b_format": (skv.SkvConfig, "b_format"),
                               "skv_stats.new_tokens": (skv.SkvStats, "new_tokens"),
                               "skv_stats.last_alpha": (skv.SkvStats, "last_alpha"),
                               "skv_stats.last_host_bytes": (skv.SkvStats, "last_host_bytes"),

@@ -84,3 +84,27 @@ def test_fp8_full_budget_no_outliers_no_window():
 
 def test_fp8_budget_of_one_temporal_cache_off():
     _run(_small(top_k=1, batch=1, landmark_format="e5m2", a_format="e5m2"), steps=3, temporal=0)
+
+
+def test_fp8_all_stores_tiny_8k():
+    # landmarks, A and B in FP8: the key rebuild reads B^T fragments as bytes
+    _run(synth.SHAPES["tiny_8k"].replace(landmark_format="e5m2", a_format="e5m2", b_format="e5m2"), steps=4)
+
+
+@pytest.mark.parametrize("chunk", [4, 16])
+def test_fp8_b_only_chunk_sizes_host_values(chunk):
+    _run(_small(chunk=chunk, seq_len=8192, top_k=8192 // (64 * chunk), n_outlier=3, b_format="e5m2"),
+         steps=2, placement=skv.SKV_VALUES_HOST)
+
+
+def test_fp8_all_stores_rank_sixteen():
+    # r = 16: the last (only) k-step is half empty, the upper k-groups read zeros
+    _run(_small(n_q_heads=32, n_kv_heads=2, batch=1, seq_len=4096, top_k=9, n_outlier=2, rank=16,
+                latent_rank=16, landmark_format="e5m2", a_format="e5m2", b_format="e5m2"), steps=2)
+
+
+def test_fp8_b_lowrank_appended_rows():
+    # the appended rows of A are projected with the FP8 B
+    layer, _, _ = _run_append(_small(window=16, b_format="e5m2"), skv.SKV_NEW_LOWRANK, [0, 9, 20, 15],
+                              max_new=48)
+    layer.close()

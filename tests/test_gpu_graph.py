@@ -3,7 +3,7 @@ replay, exactly what eager calls give on a twin layer built from the same
 inputs (same kernels, same work: bitwise equal), with eager work and
 synchronisations between the replays; with values in HBM and in pinned host
 memory (the gather's side stream forked from and joined back into the
-capturing stream), and with FP8 landmarks and A."""
+capturing stream), and with FP8 landmarks, A and B."""
 import pytest
 import torch
 
@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 def test_graph_replays_match_eager(placement, fmt):
     shape = synth.Shape("graph", batch=8, n_q_heads=16, n_kv_heads=4, head_dim=128, seq_len=4096,
                         rank=64, chunk=8, top_k=8, n_outlier=2, window=32, latent_rank=64,
-                        landmark_format=fmt, a_format=fmt)
+                        landmark_format=fmt, a_format=fmt, b_format=fmt)
     print(f"[graph] pairs={shape.pairs} placement={placement} storage={fmt}", flush=True)
     steps = 6
     k, v = synth.layer_cache_np(shape, 0, 0)

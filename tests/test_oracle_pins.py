@@ -408,10 +408,11 @@ def test_storage_rounding_is_applied_to_stored_state():
     np.testing.assert_allclose(st0.A, st.A, rtol=2 ** -8)
 
 
-def test_fp8_formats_round_landmarks_and_a_only():
+def test_fp8_formats_round_landmarks_a_and_b():
     # FP8 landmarks and A: exactly the E5M2 rounding of the unrounded build's
-    # values; B and the exact keys stay bf16; a decode step rebuilds its keys
-    # from the rounded A (its outputs differ from the bf16 build's)
+    # values; B (unless asked for) and the exact keys stay bf16; a decode step
+    # rebuilds its keys from the rounded A (its outputs differ from the bf16
+    # build's)
     rng = np.random.default_rng(19)
     cfg = small_cfg()
     hd = cfg.n_kv_heads * cfg.head_dim
@@ -428,6 +429,15 @@ def test_fp8_formats_round_landmarks_and_a_only():
     bf = O.build(cfg, k, v)
     r8, rb = O.decode_step(st, q), O.decode_step(bf, q)
     assert not np.array_equal(r8.out, rb.out)
+    # FP8 B as well: B is the E5M2 rounding, and the appended rows of A are
+    # projected with that B
+    st_b = O.build(dataclasses.replace(cfg, b_format="e5m2"), k, v)
+    np.testing.assert_array_equal(st_b.B, O.round_e5m2(st0.B))
+    np.testing.assert_array_equal(st_b.A, O.round_bf16(st0.A))
+    kb = rng.standard_normal((1, hd))
+    O.append(st_b, kb, rng.standard_normal((1, cfg.n_kv_heads, cfg.head_dim)), lowrank=True)
+    np.testing.assert_array_equal(st_b.A[:, -1], O.round_bf16(kb[0] @ O.psi_t(st_b, 0).T)[None])
+    assert np.array_equal(O.psi_t(st_b, 0), O.round_e5m2(O.psi_t(st_b, 0)))
     # the appended rows of A take the same format
     kn = rng.standard_normal((1, hd))
     O.append(st, kn, rng.standard_normal((1, cfg.n_kv_heads, cfg.head_dim)), lowrank=True)
