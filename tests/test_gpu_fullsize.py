@@ -7,7 +7,7 @@ library in the launch configuration the benchmark times:
 * GLM-4-9B-1M shape: batch 4, 1 048 576 tokens, 32 q / 2 KV heads, r = 48,
   K = 2048 (selection in 32 parts and a merge tree; attention in two head
   groups of 8);
-* the Llama-3.1-8B shape again with FP8 (E5M2) landmarks and rows of A.
+* the Llama-3.1-8B shape again with FP8 (E5M2) landmarks, rows of A and B.
 
 The oracle cannot afford the whole batch in float64, so it builds and decodes
 sampled batch elements from the very same bf16 bits the GPU consumed; every
@@ -35,7 +35,7 @@ def _slice_state(ex: dict, b: int) -> dict:
 @pytest.mark.parametrize("name,sampled,fmt", [("llama3_8b_122k", (0, 7), "bf16"), ("yi_9b_200k", (0,), "bf16"),
                                               ("glm4_9b_1m", (3,), "bf16"), ("llama3_8b_122k", (5,), "e5m2")])
 def test_one_layer_sampled(name, sampled, fmt):
-    shape = synth.SHAPES[name].replace(landmark_format=fmt, a_format=fmt)
+    shape = synth.SHAPES[name].replace(landmark_format=fmt, a_format=fmt, b_format=fmt)
     print(f"[fullsize] {shape}", flush=True)
     k, v = synth.layer_cache_torch(shape, 0, 0, "cuda")
     q = synth.queries_torch(shape, k, 0, STEPS, 0)
