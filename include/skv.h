@@ -208,8 +208,9 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
  *               so the call can be captured in a HIP graph.  Outputs are valid
  *               once the stream has completed.
  * Selection uses fp32 scores; a chunk's score is max_g(logit_g/sqrt(d) - LSE_g),
- * the log of the pages' max over the group of softmax probabilities; ties go to
- * the lower chunk id.
+ * the log of the pages' max over the group of softmax probabilities, compared as
+ * the fp32 value score - 1 (scores within one fp32 spacing of it, about 1e-7,
+ * tie); ties go to the lower chunk id.
  * Errors: INVALID_ARG (null, misaligned or non-device pointer; checked before
  * any launch), STATE, HIP.
  */

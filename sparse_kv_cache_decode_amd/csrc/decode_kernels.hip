@@ -408,6 +408,12 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
 // candidates are loaded with 16-byte loads (GB heads in flight at once) before
 // the LSE of every head is reduced; `stage` issues the caller's other staging
 // work before the barrier, and hist[0, 2048) is cleared in the same window.
+// The key is the order-preserving uint32 of score - 1 (score = the log of the
+// group max of probabilities, <= 0): in [-1, -30] fp32 values are spaced nearly
+// evenly, so the radix select's first 11-bit digit over the key range resolves
+// the top of the distribution.  On the score itself a pair with one dominant
+// chunk (score 0) stretched the range over every tiny negative value, and its
+// selection took three digit passes instead of one (11.5 against 6.3 us).
 template <int G, int PT, class Stage>
 __device__ __forceinline__ int reg_keys(const DecodeArgs& a, int p, int c0, int n, float* lse, int* hist,
                                         uint32_t (&key)[PT], uint32_t& lo, uint32_t& hi, Stage stage) {
@@ -456,7 +462,7 @@ __device__ __forceinline__ int reg_keys(const DecodeArgs& a, int p, int c0, int 
   hi = 0u;
 #pragma unroll
   for (int e = 0; e < PT; e++) {
-    key[e] = float_key(best[e]);
+    key[e] = float_key(best[e] - 1.0f);
     if (e < nv) {
       lo = min(lo, key[e]);
       hi = max(hi, key[e]);
