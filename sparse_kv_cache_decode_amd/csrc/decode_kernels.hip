@@ -1191,39 +1191,27 @@ hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Split-K flash-decode.  Work unit = one chunk of C tokens: unit u < O is an
-// outlier chunk, O <= u < O+K the chunk held by slot u-O, the rest the window.
-// Each wave owns up to NT*16 consecutive tokens (NT tiles of 16) and issues all
-// of their K/V loads before computing (keys first: key addresses need no chunk
-// id).  Per tile:
-//  * S = K q^T on MFMA 16x16x32 bf16: lane (row r, kq) feeds dims j*32+kq*8.. of
-//    token r; the output lane (head g = lane%16, kq) holds tokens kq*4..kq*4+3.
-//  * softmax in that layout, base 2: one running max and sum per head and wave;
-//    probabilities and the rescale factor go through a 1 KB per-wave LDS buffer.
-//  * P V on the vector ALUs: lane (ds, tg) accumulates dims 8*ds..8*ds+7 of the
-//    tokens tg, tg+4, tg+8, tg+12 for every head.
+// outlier chunk, O <= u < O+K the chunk held by slot u-O, the rest the window
+// and the appended tokens.  One workgroup per (pair, split) serves all G <= 16
+// query heads of its KV head, so every key and value is read once.  Each wave
+// owns up to NT*16 consecutive tokens (NT tiles of 16) and issues all of their
+// K/V loads before computing.  Per tile, both products run on MFMA:
+//  * S = K q^T (16x16x32 bf16): lane (row r, kq) feeds dims j*32+kq*8.. of token
+//    r; the output lane (head n = lane%16, kq) holds tokens 4kq..4kq+3.
+//  * softmax in that layout, base 2: one running max and sum per head.
+//  * O^T += V^T P (16x16x16 bf16).  The scores' output layout is already the
+//    B operand (tokens 4kq..4kq+3 of head n), so P stays in registers; it goes
+//    in as bf16 hi + lo parts, which keeps 16 bits of every weight.  The A
+//    operand (four tokens of one dim per lane) comes from the value loads by a
+//    4x4 dword transpose within each lane quad and one byte permute.
 // The four waves of a workgroup merge through LDS into one split partial.
 
-// Query heads per workgroup: a KV head's group of G query heads is split into
-// head groups of at most kAttnHeads, each its own workgroup over the same
-// tokens, so that the P V accumulators (8 registers per head) leave room for
-// two waves per SIMD.  The head groups of a (pair, split) are dispatched P
-// workgroups apart, i.e. on the same XCD with P a multiple of 8, so the second
-// one mostly reads its keys and values from L2.
-constexpr int kAttnHeads = 8;
-constexpr int attn_group_heads(int group) { return group < kAttnHeads ? group : kAttnHeads; }
-int attn_head_groups(int group) { return group / attn_group_heads(group); }
+// 16-token tiles per wave: two keep three waves per SIMD and give the chip
+// several waves per SIMD slot even at short contexts
+constexpr int kAttnTiles = 2;
+constexpr int kAttnMaxHeads = 16;   // query heads per KV head (the MFMA's N)
 
-// 16-token tiles per wave: as many as the registers allow at two waves per SIMD,
-// so that the grid of a long-context step fits the chip's wave slots in one round
-constexpr int attn_tiles(int heads) { return heads <= 4 ? 5 : (heads <= 8 ? 4 : 2); }
-
-template <int GW, int C>
-struct AttnShape {
-  static constexpr int NT = attn_tiles(GW);
-  static constexpr int NUW = NT * 16 / C;       // units per wave
-};
-
-int attn_units_per_wave(int group, int chunk) { return attn_tiles(attn_group_heads(group)) * 16 / chunk; }
+int attn_units_per_wave(int group, int chunk) { return kAttnTiles * 16 / chunk; }
 
 template <int C>
 __device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, int u) {
@@ -1247,20 +1235,41 @@ __device__ __forceinline__ const uint16_t* unit_value(const DecodeArgs& a, int p
   return a.val_new + ((int64_t)p * a.max_new + (int64_t)(x - Wu) * C) * kHeadDim;
 }
 
-template <int GW, int C>
+// Lane j of each quad holds dword w = element (j, w) of a 4x4 block; afterwards
+// it holds element (w, j).  Two rounds of 2x2 swaps: lanes one apart exchange
+// dwords one apart, then lanes two apart exchange dwords two apart.
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 x, int lane) {
+  const bool odd = lane & 1, hi = lane & 2;
+  constexpr int kSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+  constexpr int kSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+  uint32_t r = __builtin_amdgcn_mov_dpp((int)(odd ? x[0] : x[1]), kSwap1, 0xF, 0xF, false);
+  x[0] = odd ? r : x[0];
+  x[1] = odd ? x[1] : r;
+  r = __builtin_amdgcn_mov_dpp((int)(odd ? x[2] : x[3]), kSwap1, 0xF, 0xF, false);
+  x[2] = odd ? r : x[2];
+  x[3] = odd ? x[3] : r;
+  r = __builtin_amdgcn_mov_dpp((int)(hi ? x[0] : x[2]), kSwap2, 0xF, 0xF, false);
+  x[0] = hi ? r : x[0];
+  x[2] = hi ? x[2] : r;
+  r = __builtin_amdgcn_mov_dpp((int)(hi ? x[1] : x[3]), kSwap2, 0xF, 0xF, false);
+  x[1] = hi ? r : x[1];
+  x[3] = hi ? x[3] : r;
+  return x;
+}
+
+template <int NT, int C>
 __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
-  constexpr int NT = AttnShape<GW, C>::NT;
-  __shared__ __attribute__((aligned(16))) float pbuf[4][16 * 16];   // [wave][head][tg][t]
-  __shared__ float cbuf[4][16];                                     // [wave][head] rescale
-  __shared__ float wo[4][GW][kHeadDim];
-  __shared__ float wm[4][GW], wl[4][GW];
+  typedef short bf16x4 __attribute__((ext_vector_type(4)));
+  constexpr uint32_t kLoHalves = 0x05040100u, kHiHalves = 0x07060302u;   // v_perm selectors
+  __shared__ __attribute__((aligned(16))) float wo[4][kAttnMaxHeads][kHeadDim];
+  __shared__ float wm[4][kAttnMaxHeads], wl[4][kAttnMaxHeads];
   // pairs fastest: workgroups go to the 8 XCDs round-robin by linear id, so each
   // XCD gets whole pairs (all splits of pairs p = x mod 8) and equal work even
   // when the last split of a pair is short
-  const int p = blockIdx.x, hg = blockIdx.y, split = blockIdx.z;   // hg: head group
+  const int p = blockIdx.x, split = blockIdx.y;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int lr = lane & 15, lq = lane >> 4;   // (row|head|ds, kq|tg)
+  const int lr = lane & 15, lq = lane >> 4;   // (row|head|dim, kq)
   const int O = a.n_outlier, K = a.top_k;
   // units: [outliers; selected slots; exact region], the exact region being the
   // window units and appended units not yet folded into the candidates (its
@@ -1271,8 +1280,7 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
   const int valid = (O + K + a.n_win_units - a.n_fold) * C + a.n_new_tokens;   // tokens in units [0, U)
   const int ntok = max(0, min((uw1 - uw0) * C, valid - uw0 * C));
-  const int G = a.group, hq = a.n_kv * G, hq0 = h * G + hg * GW;   // first query head of the group
-
+  const int G = a.group, hq = a.n_kv * G, hq0 = h * G;   // first query head of the pair
 
   // chunk id of each selected unit of the wave, one per lane
   int my_ch = 0;
@@ -1281,27 +1289,27 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
     if (sidx >= 0 && sidx < K) my_ch = max(a.slot_chunk[(int64_t)p * K + sidx], 0);
   }
   // q^T first (every tile needs it; vector-memory loads complete in issue order),
-  // MFMA B layout: head lr, dims j*32 + lq*8 (zero for heads >= GW)
+  // MFMA B layout: head lr, dims j*32 + lq*8 (zero for heads >= G)
   bf16x8 bq[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     u32x4 wq = {0u, 0u, 0u, 0u};
-    if (lr < GW) wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + hq0 + lr) * kHeadDim + j * 32 + lq * 8);
+    if (lr < G) wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + hq0 + lr) * kHeadDim + j * 32 + lq * 8);
     bq[j] = __builtin_bit_cast(bf16x8, wq);
   }
   // then tile by tile, keys then values, so that tile 0 can start as soon as its
-  // own 8 loads are in.  Keys in MFMA A layout: token tile*16 + lr, dims j*32 + lq*8;
-  // values in PV layout: token tile*16 + lq + 4*i, dims lr*8.
+  // own 8 loads are in.  Keys in MFMA A layout: token tile*16 + lr, dims
+  // j*32 + lq*8.  Values: lane (lr = 4q + jj, lq) reads token tile*16 + 4lq + jj,
+  // dims c*32 + 8q .. +8 for c = 0..3; the quad transpose then leaves it dims
+  // c*32 + 2lr and c*32 + 2lr + 1 of tokens 4lq .. 4lq+3.
   // The loads are unconditional (branch-free code keeps the compiler's per-tile
   // wait counts exact): tokens past the wave's range re-read its last token,
   // whose scores are masked to -inf below, so they weigh 0.  A wave with no
   // tokens reads unit 0 of the pair and masks everything.
   const int tlast = max(ntok - 1, 0), ub = ntok > 0 ? uw0 : 0;
-  int vch[NT][4];
+  int vch[NT];
 #pragma unroll
-  for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) vch[t][i] = __shfl(my_ch, min(t * 16 + lq + 4 * i, tlast) / C);
+  for (int t = 0; t < NT; t++) vch[t] = __shfl(my_ch, min(t * 16 + 4 * lq + (lr & 3), tlast) / C);
   u32x4 kf[NT][4], vf[NT][4];
 #pragma unroll
   for (int t = 0; t < NT; t++) {
@@ -1309,20 +1317,19 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
     const uint16_t* kp = unit_key<C>(a, p, ub + tk / C) + (tk % C) * kHeadDim + lq * 8;
 #pragma unroll
     for (int j = 0; j < 4; j++) kf[t][j] = *reinterpret_cast<const u32x4*>(kp + j * 32);
+    const int tv = min(t * 16 + 4 * lq + (lr & 3), tlast);
+    const uint16_t* vp = unit_value<C>(a, p, b, h, ub + tv / C, vch[t]) + (tv % C) * kHeadDim + (lr >> 2) * 8;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int tv = min(t * 16 + lq + 4 * i, tlast);
-      vf[t][i] = *reinterpret_cast<const u32x4*>(unit_value<C>(a, p, b, h, ub + tv / C, vch[t][i]) +
-                                                 (tv % C) * kHeadDim + lr * 8);
-    }
+    for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
   }
   const float qscale = a.scale * kLog2e;
-  float m = kNegBig, l = 0.f;        // head lr (S layout)
-  float o[GW][8];                    // PV layout
+  float m = kNegBig, l = 0.f;   // head lr
+  // o[c][e][i]: head lr, dim c*32 + 8lq + 2i + e
+  f32x4 o[4][2];
 #pragma unroll
-  for (int g = 0; g < GW; g++)
+  for (int c = 0; c < 4; c++)
 #pragma unroll
-    for (int k = 0; k < 8; k++) o[g][k] = 0.f;
+    for (int e = 0; e < 2; e++) o[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int t = 0; t < NT; t++) {
@@ -1343,63 +1350,54 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
       const float mn = fmaxf(m, tmax);
       const float corr = __builtin_amdgcn_exp2f(m - mn);
       m = mn;
+      uint32_t ph[4], pl[4];
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const float pv = __builtin_amdgcn_exp2f(sv[i] - mn);
         psum += pv;
-        pbuf[w][lr * 16 + i * 4 + lq] = pv;
+        ph[i] = __builtin_bit_cast(uint32_t, pv);
+        pl[i] = __builtin_bit_cast(uint32_t, pv - __builtin_bit_cast(float, ph[i] & 0xffff0000u));
       }
       psum += __shfl_xor(psum, 16);
       psum += __shfl_xor(psum, 32);
       l = l * corr + psum;
-      if (lq == 0) cbuf[w][lr] = corr;
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
+      // weights of tokens 4lq..4lq+3 for head lr, truncated to bf16: hi, then the remainder
+      const bf16x4 bh = __builtin_bit_cast(bf16x4, (uint32_t __attribute__((ext_vector_type(2)))){
+          __builtin_amdgcn_perm(ph[1], ph[0], kHiHalves), __builtin_amdgcn_perm(ph[3], ph[2], kHiHalves)});
+      const bf16x4 bl = __builtin_bit_cast(bf16x4, (uint32_t __attribute__((ext_vector_type(2)))){
+          __builtin_amdgcn_perm(pl[1], pl[0], kHiHalves), __builtin_amdgcn_perm(pl[3], pl[2], kHiHalves)});
 #pragma unroll
-      for (int g = 0; g < GW; g++) {
-        const float cg = cbuf[w][g];
-        if (cg != 1.f) {
+      for (int c = 0; c < 4; c++) {
+        const u32x4 x = quad_transpose(vf[t][c], lane);   // x[i]: dims (c*32 + 2lr, +1) of token 4lq + i
+        const bf16x4 ve = __builtin_bit_cast(bf16x4, (uint32_t __attribute__((ext_vector_type(2)))){
+            __builtin_amdgcn_perm(x[1], x[0], kLoHalves), __builtin_amdgcn_perm(x[3], x[2], kLoHalves)});
+        const bf16x4 vo = __builtin_bit_cast(bf16x4, (uint32_t __attribute__((ext_vector_type(2)))){
+            __builtin_amdgcn_perm(x[1], x[0], kHiHalves), __builtin_amdgcn_perm(x[3], x[2], kHiHalves)});
 #pragma unroll
-          for (int k = 0; k < 8; k++) o[g][k] *= cg;
-        }
+        for (int e = 0; e < 2; e++) o[c][e] *= corr;
+        o[c][0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ve, bh, o[c][0], 0, 0, 0);
+        o[c][0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ve, bl, o[c][0], 0, 0, 0);
+        o[c][1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vo, bh, o[c][1], 0, 0, 0);
+        o[c][1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vo, bl, o[c][1], 0, 0, 0);
       }
-      f32x4 pg[GW];
-#pragma unroll
-      for (int g = 0; g < GW; g++) pg[g] = *reinterpret_cast<const f32x4*>(&pbuf[w][g * 16 + lq * 4]);
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        float y[8];
-        unpack8(vf[t][i], y);
-#pragma unroll
-        for (int g = 0; g < GW; g++)
-#pragma unroll
-          for (int k = 0; k < 8; k++) o[g][k] = fmaf(pg[g][i], y[k], o[g][k]);
-      }
-      __builtin_amdgcn_wave_barrier();
     }
   }
-  // the four token rows share the wave's running max: plain sums
+  if (lr < G) {
 #pragma unroll
-  for (int g = 0; g < GW; g++)
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      o[g][k] += __shfl_xor(o[g][k], 16);
-      o[g][k] += __shfl_xor(o[g][k], 32);
+    for (int c = 0; c < 4; c++) {
+      float* dst = &wo[w][lr][c * 32 + 8 * lq];
+      *reinterpret_cast<f32x4*>(dst) = f32x4{o[c][0][0], o[c][1][0], o[c][0][1], o[c][1][1]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[c][0][2], o[c][1][2], o[c][0][3], o[c][1][3]};
     }
-  if (lq == 0) {
-#pragma unroll
-    for (int g = 0; g < GW; g++)
-#pragma unroll
-      for (int k = 0; k < 8; k++) wo[w][g][lr * 8 + k] = o[g][k];
-    if (lr < GW) {
+    if (lq == 0) {
       wm[w][lr] = m;
       wl[w][lr] = l;
     }
   }
   __syncthreads();
-  float* part = a.attn_part + (((int64_t)p * a.n_split + split) * G + hg * GW) * kPartStride;
-  for (int idx = threadIdx.x; idx < GW * kHeadDim; idx += 256) {
+  float* part = a.attn_part + ((int64_t)p * a.n_split + split) * G * kPartStride;
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
     const int g = idx / kHeadDim, dim = idx % kHeadDim;
     float M = kNegBig;
 #pragma unroll
@@ -1473,28 +1471,28 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
 }
 
 template <int G>
-static hipError_t launch_attn_g(const DecodeArgs& a, hipStream_t st) {
-  constexpr int GW = attn_group_heads(G);
-  dim3 grid(a.batch * a.n_kv, G / GW, a.n_split);
-  switch (a.chunk) {
-    case 4: attn_kernel<GW, 4><<<grid, 256, 0, st>>>(a); break;
-    case 8: attn_kernel<GW, 8><<<grid, 256, 0, st>>>(a); break;
-    case 16: attn_kernel<GW, 16><<<grid, 256, 0, st>>>(a); break;
-    default: return hipErrorInvalidValue;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+static hipError_t launch_combine_g(const DecodeArgs& a, hipStream_t st) {
   combine_kernel<G><<<dim3(G, a.batch * a.n_kv), kCombineThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st) {
+  if (a.group < 1 || a.group > kAttnMaxHeads) return hipErrorInvalidValue;
+  const dim3 grid(a.batch * a.n_kv, a.n_split);
+  switch (a.chunk) {
+    case 4: attn_kernel<kAttnTiles, 4><<<grid, 256, 0, st>>>(a); break;
+    case 8: attn_kernel<kAttnTiles, 8><<<grid, 256, 0, st>>>(a); break;
+    case 16: attn_kernel<kAttnTiles, 16><<<grid, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   switch (a.group) {
-    case 1: return launch_attn_g<1>(a, st);
-    case 2: return launch_attn_g<2>(a, st);
-    case 4: return launch_attn_g<4>(a, st);
-    case 8: return launch_attn_g<8>(a, st);
-    case 16: return launch_attn_g<16>(a, st);
+    case 1: return launch_combine_g<1>(a, st);
+    case 2: return launch_combine_g<2>(a, st);
+    case 4: return launch_combine_g<4>(a, st);
+    case 8: return launch_combine_g<8>(a, st);
+    case 16: return launch_combine_g<16>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -350,7 +350,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     // at once); split so that there are about 8 waves per CU
     const int nuw = attn_units_per_wave(G, C);
     const int waves_target = 2048;
-    const int64_t wave_units = (int64_t)attn_head_groups(G) * P * h->U;   // every head group reads every unit
+    const int64_t wave_units = (int64_t)P * h->U;
     int upw_wave = (int)((wave_units + waves_target - 1) / waves_target);
     upw_wave = std::max(1, std::min(upw_wave, nuw));
     h->upw = 4 * upw_wave;

@@ -10,7 +10,7 @@ namespace skv {
 constexpr int kHeadDim = 128;
 constexpr int kMaxTopK = 4096;
 constexpr int kSelLdsMax = 150 * 1024;   // dynamic LDS of the select kernel
-constexpr int kMaxSplits = 1024;         // attention workgroups per pair
+constexpr int kMaxSplits = 4096;         // attention workgroups per pair
 constexpr int kScoreRows = 128;          // candidate landmarks per score workgroup (bf16)
 constexpr int kScoreRows8 = 256;         // the same for FP8 landmarks (the same 32 KB)
 constexpr int kPartStride = kHeadDim + 4; // floats per attention partial row: o[d], m, l, 2 pad (16-B rows)
@@ -131,7 +131,6 @@ hipError_t launch_fold(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);
 int attn_units_per_wave(int group, int chunk);
-int attn_head_groups(int group);   // attention workgroups per (pair, split): query-head groups
 
 // ---- host eigensolver (eig_host.cpp)
 // Top-r eigenpairs of each symmetric n x n matrix gram[bi] (row-major fp64, on the
