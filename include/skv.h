@@ -210,7 +210,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
  * Selection uses fp32 scores; a chunk's score is max_g(logit_g/sqrt(d) - LSE_g),
  * the log of the pages' max over the group of softmax probabilities, compared as
  * the fp32 value score - 1 (scores within one fp32 spacing of it, about 1e-7,
- * tie); ties go to the lower chunk id.
+ * tie); ties go to the lower chunk id.  The attention accumulates in fp32 with
+ * the softmax weights carried at 16 bits of precision (bf16 hi + lo parts).
  * Errors: INVALID_ARG (null, misaligned or non-device pointer; checked before
  * any launch), STATE, HIP.
  */
