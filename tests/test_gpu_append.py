@@ -17,7 +17,7 @@ import torch
 
 from oracle import shadowkv as O
 from sparse_kv_cache_decode_amd import skv, synth
-from tests.parity import adopt_landmarks, bits, check_build, check_ids, check_out, reference_out
+from tests.parity import adopt_gpu_state, bits, check_build, check_ids, check_out, reference_out
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,7 @@ def _run_append(shape, mode, schedule, max_new, seed=0, placement=skv.SKV_VALUES
     layer = skv.Layer(shape, k.cuda(), vd, placement, max_new_tokens=max_new, new_token_mode=mode)
     ex = layer.export()
     check_build(ex, st)
-    adopt_landmarks(st, ex)
+    adopt_gpu_state(st, ex)
     knd, vnd = kn.cuda(), vn.cuda()
     prev, prev_differ = None, False
     used = 0

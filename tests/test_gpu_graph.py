@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from sparse_kv_cache_decode_amd import skv, synth
-from tests.parity import adopt_landmarks, bits, check_ids, check_out, reference_out
+from tests.parity import adopt_gpu_state, bits, check_ids, check_out, reference_out
 from oracle import shadowkv as O
 
 pytestmark = pytest.mark.gpu
@@ -43,7 +43,7 @@ def test_graph_replays_match_eager(placement, fmt):
     with torch.cuda.graph(g):
         graphed.decode(qbuf, out_g, ids_g)
     st = O.build(O.config_from(shape), bits(k), bits(v))
-    adopt_landmarks(st, eager.export())
+    adopt_gpu_state(st, eager.export())
     prev = O.decode_step(st, bits(q[0])).ids
     for t in range(1, steps):
         qbuf.copy_(q[t].cuda())

@@ -6,7 +6,8 @@ import torch
 
 from oracle import shadowkv as O
 from sparse_kv_cache_decode_amd import skv, synth
-from tests.parity import adopt_landmarks, bits, check_build, check_ids, check_out, reference_out
+from tests.parity import (DECODE_MAX_ABS, DECODE_REL_L2, adopt_gpu_state, bits, check_build, check_ids,
+                          check_out, reference_out)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +32,7 @@ def _run(shape, steps, placement=skv.SKV_VALUES_DEVICE, temporal=1, seed=0, mode
     ex = layer.export()
     if check_state:
         check_build(ex, st)
-    adopt_landmarks(st, ex)
+    adopt_gpu_state(st, ex)
     prev, prev_gpu, prev_differ = None, None, True
     worst = (0.0, 0.0)
     swaps = 0
@@ -42,7 +43,8 @@ def _run(shape, steps, placement=skv.SKV_VALUES_DEVICE, temporal=1, seed=0, mode
         gids = ids.cpu().numpy()
         differ = check_ids(gids, st, res)
         swaps += len(differ)
-        e = check_out(out.cpu().numpy(), reference_out(st, bits(q[t]), res, gids, differ))
+        e = check_out(out.cpu().numpy(), reference_out(st, bits(q[t]), res, gids, differ), DECODE_MAX_ABS,
+                      DECODE_REL_L2)
         worst = (max(worst[0], e[0]), max(worst[1], e[1]))
         s = layer.stats()
         if t == 0 or not temporal:
