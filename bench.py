@@ -29,7 +29,12 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 CALIB_BYTES = 512 << 20         # bytes read (and written) once by the counter-calibration kernel
 CSRC = os.path.join(ROOT, "sparse_kv_cache_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
-SCORE_KERNELS = {"bf16": "skv::score_kernel<4>", "e5m2": "skv::score_fp8_kernel<4>"}
+SCORE_KERNELS = {"bf16": "skv::score_kernel<{G}>", "e5m2": "skv::score_fp8_kernel<{G}>"}
+
+
+def score_kernel_name(shape) -> str:
+    """The score kernel the library launches for this shape (templated on G)."""
+    return SCORE_KERNELS[shape.landmark_format].format(G=shape.group)
 FORMAT_BYTES = {"bf16": 2, "e5m2": 1}
 METRIC = "decode tokens/s at S=122K batch 8 (Llama-3.1-8B shape); % HBM roofline"
 
@@ -191,9 +196,12 @@ def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> str:
     return "\n".join(lines)
 
 
-def summarize_trace(stats_csv: str, command: str) -> str:
+def summarize_trace(stats_csv: str, command: str, shape=None) -> str:
     """Markdown table of the library's kernels from a rocprofv3 kernel_stats.csv,
-    with the score kernel's rate at its algorithmic bytes per launch."""
+    with the score kernel's rate at its algorithmic bytes per launch for `shape`
+    (default: the Llama-3.1-8B shape)."""
+    from sparse_kv_cache_decode_amd import synth
+    shape = shape or synth.SHAPES["llama3_8b_122k"]
     rows = []
     with open(stats_csv, newline="") as f:
         for row in csv.DictReader(f):
@@ -202,7 +210,8 @@ def summarize_trace(stats_csv: str, command: str) -> str:
                 rows.append((name, int(row["Calls"]), float(row["AverageNs"]) / 1e3, float(row["MinNs"]) / 1e3,
                              float(row["MaxNs"]) / 1e3, float(row["TotalDurationNs"]) / 1e6))
     rows.sort(key=lambda r: -r[5])
-    lines = ["# Kernel timing: ShadowKV decode, Llama-3.1-8B shape (122 880 tokens, batch 8, 32 layers)", "",
+    lines = [f"# Kernel timing: ShadowKV decode, {shape.name} (S = {shape.seq_len}, batch {shape.batch}, "
+             f"G = {shape.group}, C = {shape.chunk}, K = {shape.top_k}, {shape.layers} layers)", "",
              "Command (repo root on the GPU box, `export TMPDIR=/tmp` first):", "", "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/prof_bench -o bench -- {command}",
              "```", "",
@@ -211,12 +220,11 @@ def summarize_trace(stats_csv: str, command: str) -> str:
              "", "| kernel | calls | avg us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
     for n, c, a, lo, hi, t in rows:
         lines.append(f"| `{n}` | {c} | {a:.2f} | {lo:.2f} | {hi:.2f} | {t:.1f} |")
-    for fmt, kname in SCORE_KERNELS.items():
-        score = [r for r in rows if r[0] == kname]
+    for fmt in SCORE_KERNELS:
+        fshape = shape.replace(landmark_format=fmt)
+        score = [r for r in rows if r[0] == score_kernel_name(fshape)]
         if score:
-            from sparse_kv_cache_decode_amd import synth
-            shape = synth.SHAPES["llama3_8b_122k"].replace(landmark_format=fmt)
-            by = algorithmic_bytes(shape, 0.0)["score"]
+            by = algorithmic_bytes(fshape, 0.0)["score"]
             lines += ["", f"Score kernel ({fmt} landmarks): {by} algorithmic bytes per launch / {score[0][2]:.2f} us "
                           f"average = {by / (score[0][2] * 1e-6) / 1e9:.0f} GB/s "
                           f"({by / (score[0][2] * 1e-6) / 1e9 / HBM_PEAK_GBPS:.3f} of {HBM_PEAK_GBPS / 1000:.0f} TB/s)."]
@@ -320,7 +328,9 @@ def main():
         print(summarize_counters(*args.summarize_counters))
         return 0
     if args.summarize_trace:
-        print(summarize_trace(*args.summarize_trace))
+        from sparse_kv_cache_decode_amd import synth
+        tshape = synth.glm_chunk_variant(args.chunk) if args.chunk else synth.SHAPES[args.shape]
+        print(summarize_trace(*args.summarize_trace, tshape.replace(layers=args.layers or tshape.layers)))
         return 0
 
     if args.cpu_baseline_child:
@@ -516,10 +526,10 @@ def main():
                                   f"{W + 1}..{W + K} generated tokens attended in the timed steps)"),
                    "global_batch": shape.batch, "seq_len": shape.seq_len, "layers": L,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": f"{SCORE_KERNELS[shape.landmark_format]} (landmark GEMV)",
+        "roofline": {"bound": "hbm", "kernel": f"{score_kernel_name(shape)} (landmark GEMV)",
                      "achieved": round(score_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(score_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(shape.name, SCORE_KERNELS[shape.landmark_format]),
+                     "traffic": measured_traffic(shape.name, score_kernel_name(shape)),
                      "algorithmic_bytes": int(by["score"])},
         "step_roofline": {"algorithmic_bytes_per_layer_step": int(by["total"]),
                           "achieved_GBps": round(step_gbps, 1),

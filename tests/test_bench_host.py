@@ -103,3 +103,20 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_score_kernel_follows_the_group_size():
+    s = synth.SHAPES["glm4_9b_1m"]
+    assert bench.score_kernel_name(s) == "skv::score_kernel<16>"
+    assert bench.score_kernel_name(s.replace(landmark_format="e5m2")) == "skv::score_fp8_kernel<16>"
+    assert bench.score_kernel_name(synth.SHAPES["llama3_8b_122k"]) == "skv::score_kernel<4>"
+    with tempfile.TemporaryDirectory() as d:
+        p = os.path.join(d, "stats.csv")
+        with open(p, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs", "MaxNs"])
+            w.writeheader()
+            w.writerow({"Name": "void skv::score_kernel<16>(skv::DecodeArgs)", "Calls": 1, "TotalDurationNs": 60000,
+                        "AverageNs": 60000, "MinNs": 60000, "MaxNs": 60000})
+        text = bench.summarize_trace(p, "python3 bench.py --shape glm4_9b_1m", s)
+        by = bench.algorithmic_bytes(s, 0.0)["score"]
+        assert "glm4_9b_1m" in text and f"{by} algorithmic bytes per launch / 60.00 us" in text
