@@ -148,7 +148,7 @@ skv_status validate(const skv_config* c) {
   // attention splits: at most kMaxSplits per pair with every appended token present
   const int64_t units = c->n_outlier + c->top_k + c->window / c->chunk +
                         ((int64_t)c->max_new_tokens + c->chunk - 1) / c->chunk;
-  const int64_t per_wg = 4 * attn_units_per_wave(G, c->chunk);
+  const int64_t per_wg = 4 * attn_units_per_wave(c->chunk);
   if ((units + per_wg - 1) / per_wg > kMaxSplits) return SKV_ERR_UNSUPPORTED;
   return SKV_OK;
 }
@@ -348,7 +348,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   {
     // attention: each wave owns at most attn_units_per_wave units (all loads issued
     // at once); split so that there are about 8 waves per CU
-    const int nuw = attn_units_per_wave(G, C);
+    const int nuw = attn_units_per_wave(C);
     const int waves_target = 2048;
     const int64_t wave_units = (int64_t)P * h->U;
     int upw_wave = (int)((wave_units + waves_target - 1) / waves_target);

@@ -130,7 +130,7 @@ hipError_t launch_append(const DecodeArgs& a, const uint16_t* k_new, const uint1
 hipError_t launch_fold(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);
-int attn_units_per_wave(int group, int chunk);
+int attn_units_per_wave(int chunk);   // 16-token tiles per wave * 16 / C
 
 // ---- host eigensolver (eig_host.cpp)
 // Top-r eigenpairs of each symmetric n x n matrix gram[bi] (row-major fp64, on the
