@@ -12,9 +12,11 @@ namespace skv {
 
 // ---------------------------------------------------------------------------
 // RoPE + landmark + min-cos: one wave per (b, h, chunk); lane l holds dims l, l+64
-// (the rotate-half pair).  Landmark = mean of the C rotated keys (fp32), rounded
-// once to its storage format (bf16, or FP8 E5M2 with fp8); min-cos uses the fp32
-// mean.
+// (the rotate-half pair).  The rotation, the chunk mean and the cosines run in
+// float64, and the landmark is rounded once from the float64 mean to its storage
+// format (bf16, or FP8 E5M2 with fp8): the stored landmark is then the rounding of
+// the exact chunk mean up to float64 error, which only a mean within ~1e-15 of a
+// rounding boundary could change.
 
 template <int C>
 __global__ __launch_bounds__(256) void rope_landmark_kernel(const uint16_t* __restrict__ k_pre,
@@ -27,42 +29,42 @@ __global__ __launch_bounds__(256) void rope_landmark_kernel(const uint16_t* __re
   const int h = blockIdx.y, b = blockIdx.z;
   if (j >= n_c) return;
   const double f = inv_freq[lane];
-  float y1[C], y2[C];
-  float m1 = 0.f, m2 = 0.f;
+  double y1[C], y2[C];
+  double m1 = 0.0, m2 = 0.0;
 #pragma unroll
   for (int i = 0; i < C; i++) {
     const int64_t pos = (int64_t)j * C + i;
     const uint16_t* row = k_pre + ((int64_t)b * S + pos) * (int64_t)(H * kHeadDim) + h * kHeadDim;
-    const float x1 = bf16_to_f32(row[lane]), x2 = bf16_to_f32(row[lane + 64]);
-    float c, s;
-    rope_cs(pos, f, &c, &s);
+    const double x1 = bf16_to_f32(row[lane]), x2 = bf16_to_f32(row[lane + 64]);
+    double c, s;
+    rope_cs64(pos, f, &c, &s);
     y1[i] = x1 * c - x2 * s;
     y2[i] = x2 * c + x1 * s;
     m1 += y1[i];
     m2 += y2[i];
   }
-  m1 *= 1.0f / C;
-  m2 *= 1.0f / C;
-  const float mm = wave_sum(m1 * m1 + m2 * m2);
-  float mc = 3.0f;
+  m1 *= 1.0 / C;
+  m2 *= 1.0 / C;
+  const double mm = wave_sum64(m1 * m1 + m2 * m2);
+  double mc = 3.0;
 #pragma unroll
   for (int i = 0; i < C; i++) {
-    const float dot = wave_sum(y1[i] * m1 + y2[i] * m2);
-    const float kk = wave_sum(y1[i] * y1[i] + y2[i] * y2[i]);
-    const float cs = dot / fmaxf(sqrtf(kk) * sqrtf(mm), 1e-8f);
-    mc = fminf(mc, cs);
+    const double dot = wave_sum64(y1[i] * m1 + y2[i] * m2);
+    const double kk = wave_sum64(y1[i] * y1[i] + y2[i] * y2[i]);
+    const double cs = dot / fmax(sqrt(kk) * sqrt(mm), 1e-8);
+    mc = fmin(mc, cs);
   }
   const int64_t pr = (int64_t)b * H + h;
   if (fp8) {
     uint8_t* lrow = static_cast<uint8_t*>(L_full) + (pr * n_c + j) * kHeadDim;
-    lrow[lane] = f32_to_e5m2(m1);
-    lrow[lane + 64] = f32_to_e5m2(m2);
+    lrow[lane] = f64_to_e5m2_rne(m1);
+    lrow[lane + 64] = f64_to_e5m2_rne(m2);
   } else {
     uint16_t* lrow = static_cast<uint16_t*>(L_full) + (pr * n_c + j) * kHeadDim;
-    lrow[lane] = f32_to_bf16(m1);
-    lrow[lane + 64] = f32_to_bf16(m2);
+    lrow[lane] = f64_to_bf16_rne(m1);
+    lrow[lane + 64] = f64_to_bf16_rne(m2);
   }
-  if (lane == 0) min_cos[pr * n_c + j] = mc;
+  if (lane == 0) min_cos[pr * n_c + j] = (float)mc;
 }
 
 hipError_t launch_rope_landmark(const uint16_t* k_pre, int b, int64_t S, int H, int C,
@@ -143,8 +145,9 @@ hipError_t launch_candidates(const void* L_full, const int32_t* outlier_ids, int
 }
 
 // ---------------------------------------------------------------------------
-// Exact static caches: post-RoPE keys and values of the outlier chunks and of the
-// last W tokens.  One wave per (pair, token); `v` may be a mapped host pointer.
+// Exact static caches: post-RoPE keys (rotated in float64, rounded once to bf16)
+// and values of the outlier chunks and of the last W tokens.  One wave per
+// (pair, token); `v` may be a mapped host pointer.
 
 __global__ __launch_bounds__(256) void static_gather_kernel(
     const uint16_t* __restrict__ k_pre, const uint16_t* __restrict__ v,
@@ -170,11 +173,11 @@ __global__ __launch_bounds__(256) void static_gather_kernel(
     vd = v_win + ((int64_t)p * W + w) * kHeadDim;
   }
   const uint16_t* row = k_pre + ((int64_t)b * S + pos) * (int64_t)(H * kHeadDim) + h * kHeadDim;
-  const float x1 = bf16_to_f32(row[lane]), x2 = bf16_to_f32(row[lane + 64]);
-  float c, s;
-  rope_cs(pos, inv_freq[lane], &c, &s);
-  kd[lane] = f32_to_bf16(x1 * c - x2 * s);
-  kd[lane + 64] = f32_to_bf16(x2 * c + x1 * s);
+  const double x1 = bf16_to_f32(row[lane]), x2 = bf16_to_f32(row[lane + 64]);
+  double c, s;
+  rope_cs64(pos, inv_freq[lane], &c, &s);   // rotated in float64, rounded once
+  kd[lane] = f64_to_bf16_rne(x1 * c - x2 * s);
+  kd[lane + 64] = f64_to_bf16_rne(x2 * c + x1 * s);
   const uint32_t* vs = reinterpret_cast<const uint32_t*>(v + (((int64_t)b * H + h) * S + pos) * kHeadDim);
   reinterpret_cast<uint32_t*>(vd)[lane] = vs[lane];
 }
@@ -379,115 +382,90 @@ hipError_t launch_gemm_f64_tn(const double* A, const double* B, double* C, int b
 }
 
 // ---------------------------------------------------------------------------
-// Projection A[b] = K_b Psi_b (S x HD times HD x r) on MFMA 16x16x32 bf16.  Psi
-// comes split in two bf16 parts, hi = bf16(Psi) and lo = bf16(Psi - hi), so
-// K Psi = K hi + K lo up to about 2^-16 of Psi (K is exact in bf16); fp32
-// accumulation; bf16 out, or FP8 E5M2 bytes with fp8.  A workgroup takes 64 rows
-// and up to kProjTiles 16-column tiles; wave w owns rows w*16 .. w*16+15.  MFMA
-// operands: lane (row lc, kq) holds dims kq*8 .. +7 of its K row; lane (column lc,
-// kq) the same dims of its Psi^T row; output lane (column lc, kq) holds rows
-// kq*4 .. kq*4+3.
+// B^T: psi [b][HD][r] (float64) rounded once to bf16, or to FP8 E5M2 bytes with b8,
+// in the same layout.
 
-constexpr int kProjTiles = 10;   // 160 columns: every rank up to 160 in one pass over K
-
-// double -> bf16 bits, one rounding to nearest even at the 8th significant bit
-// (the double is cut to 8 significant bits first, which float holds exactly).
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
-  uint64_t u = (uint64_t)__double_as_longlong(x);
-  u += (1ull << 44) - 1ull + ((u >> 45) & 1ull);
-  u &= ~((1ull << 45) - 1ull);
-  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
-}
-
-// double -> FP8 E5M2 byte, one rounding to nearest even (2 mantissa bits kept;
-// below 2^-14 the grid is 2^-16; past 57344 the result is inf).
-__device__ __forceinline__ uint8_t f64_to_e5m2_rne(double x) {
-  const uint32_t sign = (uint32_t)((uint64_t)__double_as_longlong(x) >> 56) & 0x80u;
-  const double ax = fabs(x);
-  if (ax < 0x1p-14) return (uint8_t)(sign | (uint32_t)rint(ax * 65536.0));
-  uint64_t v = (uint64_t)__double_as_longlong(ax);
-  v += (1ull << 49) - 1ull + ((v >> 50) & 1ull);
-  const int e = (int)(v >> 52) - 1023 + 15;
-  if (e >= 31) return (uint8_t)(sign | 0x7cu);
-  return (uint8_t)(sign | ((uint32_t)e << 2) | (uint32_t)((v >> 50) & 3ull));
-}
-
-__global__ void split_psi_kernel(const double* __restrict__ psi, int b, int HD, int r, bool b8,
-                                 void* __restrict__ bt, uint16_t* __restrict__ psi_t) {
-  const int64_t n = (int64_t)b * HD * r;
+__global__ void round_psi_kernel(const double* __restrict__ psi, int64_t n, bool b8, void* __restrict__ bt) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n) return;
-  const int j = (int)(idx % r);
-  const int64_t bi = idx / ((int64_t)HD * r);
-  const int i = (int)((idx / r) % HD);
-  const double x = psi[idx];
-  const uint16_t hi = f64_to_bf16_rne(x);
   if (b8)
-    static_cast<uint8_t*>(bt)[idx] = f64_to_e5m2_rne(x);
+    static_cast<uint8_t*>(bt)[idx] = f64_to_e5m2_rne(psi[idx]);
   else
-    static_cast<uint16_t*>(bt)[idx] = hi;
-  const int64_t dst = (bi * r + j) * HD + i;
-  psi_t[dst] = hi;
-  psi_t[n + dst] = f64_to_bf16_rne(x - (double)__uint_as_float((uint32_t)hi << 16));
+    static_cast<uint16_t*>(bt)[idx] = f64_to_bf16_rne(psi[idx]);
 }
 
-hipError_t launch_split_psi(const double* psi, int b, int HD, int r, bool b8, void* bt, uint16_t* psi_t,
-                            hipStream_t st) {
+hipError_t launch_round_psi(const double* psi, int b, int HD, int r, bool b8, void* bt, hipStream_t st) {
   const int64_t n = (int64_t)b * HD * r;
-  split_psi_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(psi, b, HD, r, b8, bt, psi_t);
+  round_psi_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(psi, n, b8, bt);
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void project_kernel(const uint16_t* __restrict__ k_pre,
-                                                      const uint16_t* __restrict__ psi_t, int nb, int64_t S,
-                                                      int HD, int r, int64_t a_rows, bool fp8,
-                                                      void* __restrict__ A) {
+// ---------------------------------------------------------------------------
+// Projection A[b] = K_b Psi_b (S x HD times HD x r) in float64: K's bf16 values are
+// exact in float64, Psi is the eigensolver's float64 basis, and every product is
+// accumulated with float64 FMAs, so the stored A is the rounding (once, to bf16 or
+// FP8 E5M2) of K Psi up to float64 error.  Tiles of 64 rows x 64 columns, k-steps
+// of 16 staged in LDS; each of the 256 threads owns 4 x 4 outputs.  The build is
+// untimed; at b = 8, S = 122 880, HD = 1024, r = 160 this is about 0.4 TFLOP.
+
+__global__ __launch_bounds__(256) void project_f64_kernel(const uint16_t* __restrict__ k_pre,
+                                                          const double* __restrict__ psi, int64_t S, int HD,
+                                                          int r, int64_t a_rows, bool fp8, void* __restrict__ A) {
+  __shared__ double ta[16][64 + 1];   // K tile, [k][row]
+  __shared__ double tb[16][64 + 1];   // Psi tile, [k][column]
   const int b = blockIdx.z;
-  const int64_t row0 = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16;
-  const int n0 = blockIdx.y * kProjTiles * 16;
-  const int lane = threadIdx.x & 63, lc = lane & 15, kq = lane >> 4;
-  const int nt = min(kProjTiles, (r - n0) / 16);
-  // rows past S re-read row S-1; their outputs are not stored
-  const uint16_t* kp = k_pre + ((int64_t)b * S + min(row0 + lc, S - 1)) * HD + kq * 8;
-  const uint16_t* hi = psi_t + ((int64_t)b * r + n0 + lc) * HD + kq * 8;
-  const uint16_t* lo = hi + (int64_t)nb * r * HD;
-  f32x4 acc[kProjTiles];
-#pragma unroll
-  for (int t = 0; t < kProjTiles; t++) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < HD; k0 += 32) {
-    const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + k0));
-#pragma unroll
-    for (int t = 0; t < kProjTiles; t++) {
-      if (t < nt) {
-        const int64_t o = (int64_t)t * 16 * HD + k0;
-        const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(hi + o));
-        const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lo + o));
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, acc[t], 0, 0, 0);
-      }
+  const int64_t m0 = (int64_t)blockIdx.y * 64;
+  const int n0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const uint16_t* kb = k_pre + (int64_t)b * S * HD;
+  const double* pb = psi + (int64_t)b * HD * r;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < HD; k0 += 16) {   // HD is a multiple of 128
+    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+      const int mm = e >> 4, kk = e & 15;          // 16 consecutive k of one row of K
+      const int64_t gm = m0 + mm;
+      ta[kk][mm] = gm < S ? (double)bf16_to_f32(kb[gm * HD + k0 + kk]) : 0.0;
+      const int kp = e >> 6, nn = e & 63;          // 64 consecutive columns of one row of Psi
+      const int gn = n0 + nn;
+      tb[kp][nn] = gn < r ? pb[(int64_t)(k0 + kp) * r + gn] : 0.0;
     }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; kk++) {
+      double x[4], y[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        x[i] = ta[kk][ty * 4 + i];
+        y[i] = tb[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = fma(x[i], y[j], acc[i][j]);
+    }
+    __syncthreads();
   }
 #pragma unroll
-  for (int t = 0; t < kProjTiles; t++) {
-    if (t >= nt) continue;
-    const int col = n0 + t * 16 + lc;
+  for (int i = 0; i < 4; i++) {
+    const int64_t row = m0 + ty * 4 + i;
+    if (row >= S) continue;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int64_t row = row0 + kq * 4 + i;
-      if (row >= S) continue;
+    for (int j = 0; j < 4; j++) {
+      const int col = n0 + tx * 4 + j;
+      if (col >= r) continue;
       const int64_t at = ((int64_t)b * a_rows + row) * r + col;
       if (fp8)
-        static_cast<uint8_t*>(A)[at] = f32_to_e5m2(acc[t][i]);
+        static_cast<uint8_t*>(A)[at] = f64_to_e5m2_rne(acc[i][j]);
       else
-        static_cast<uint16_t*>(A)[at] = f32_to_bf16(acc[t][i]);
+        static_cast<uint16_t*>(A)[at] = f64_to_bf16_rne(acc[i][j]);
     }
   }
 }
 
-hipError_t launch_project(const uint16_t* k_pre, const uint16_t* psi_t, int b, int64_t S, int HD, int r,
+hipError_t launch_project(const uint16_t* k_pre, const double* psi, int b, int64_t S, int HD, int r,
                           int64_t a_rows, bool fp8, void* A, hipStream_t st) {
-  dim3 grid((unsigned)((S + 63) / 64), (r + kProjTiles * 16 - 1) / (kProjTiles * 16), b);
-  project_kernel<<<grid, 256, 0, st>>>(k_pre, psi_t, b, S, HD, r, a_rows, fp8, A);
+  dim3 grid((r + 63) / 64, (unsigned)((S + 63) / 64), b);
+  project_f64_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, a_rows, fp8, A);
   return hipGetLastError();
 }
 

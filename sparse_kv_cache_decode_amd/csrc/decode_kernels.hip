@@ -1020,10 +1020,11 @@ hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st) {
 //    leaves the local window).
 //  append_project_kernel, low rank only (paper-graph-ui summary, section 3.4,
 //    ShadowKV+ paragraph), one workgroup per batch element: a' = k' Psi with
-//    Psi^T the stored B (fp32 accumulation, rounded to bf16), written as row
-//    S + t of the batch element's A, from where the key rebuild reads it once
-//    the token's chunk has been folded into the candidates.  1024 threads keep
-//    about 20 row loads of B^T per thread, issued eight at a time.
+//    Psi^T the stored B (float64 accumulation of the exact bf16 products,
+//    rounded once to the format of A), written as row S + t of the batch
+//    element's A, from where the key rebuild reads it once the token's chunk
+//    has been folded into the candidates.  1024 threads keep about 20 row loads
+//    of B^T per thread, issued eight at a time.
 //  fold_kernel, low rank only, after the append that completes a chunk: the
 //    oldest exact chunk (combined index n_fold over [window units; appended
 //    units]) becomes the pair's last candidate, its landmark the mean of its
@@ -1039,12 +1040,12 @@ __global__ __launch_bounds__(128) void append_exact_kernel(DecodeArgs a, const u
   const int b = blockIdx.x % a.batch, h = blockIdx.x / a.batch, tid = threadIdx.x;
   const uint16_t* kp = k_new + (int64_t)b * a.n_kv * kHeadDim + h * kHeadDim;
   const int64_t row = ((int64_t)(b * a.n_kv + h) * a.max_new + t) * kHeadDim;
-  if (tid < kHeadDim / 2) {
-    const float x1 = bf16_to_f32(kp[tid]), x2 = bf16_to_f32(kp[tid + kHeadDim / 2]);
-    float cs, sn;
-    rope_cs(a.seq_len + t, a.inv_freq[tid], &cs, &sn);
-    a.key_new[row + tid] = f32_to_bf16(x1 * cs - x2 * sn);
-    a.key_new[row + tid + kHeadDim / 2] = f32_to_bf16(x2 * cs + x1 * sn);
+  if (tid < kHeadDim / 2) {   // rotated in float64, rounded once to bf16
+    const double x1 = bf16_to_f32(kp[tid]), x2 = bf16_to_f32(kp[tid + kHeadDim / 2]);
+    double cs, sn;
+    rope_cs64(a.seq_len + t, a.inv_freq[tid], &cs, &sn);
+    a.key_new[row + tid] = f64_to_bf16_rne(x1 * cs - x2 * sn);
+    a.key_new[row + tid + kHeadDim / 2] = f64_to_bf16_rne(x2 * cs + x1 * sn);
   } else if (tid < kHeadDim / 2 + kHeadDim / 8) {
     const int c = tid - kHeadDim / 2;
     *reinterpret_cast<u32x4*>(a.val_new + row + c * 8) =
@@ -1055,8 +1056,8 @@ __global__ __launch_bounds__(128) void append_exact_kernel(DecodeArgs a, const u
 __global__ __launch_bounds__(kAppendThreads) void append_project_kernel(DecodeArgs a, const uint16_t* k_new,
                                                                         int t, uint16_t* A) {
   __shared__ float ks[kMaxHD];                  // k' of the batch element
-  __shared__ float red[kAppendThreads * 8];     // per-row-group partial a'
-  __shared__ float red2[kAppendThreads];        // second-level partials
+  __shared__ double red[kAppendThreads * 4];    // per-row-group partials, half of the columns at a time
+  __shared__ double red2[kAppendThreads];       // second-level partials
   const int b = blockIdx.x;
   const int HD = a.n_kv * kHeadDim, r = a.rank, tid = threadIdx.x;
   const uint16_t* kp = k_new + (int64_t)b * HD;
@@ -1067,11 +1068,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_project_kernel(DecodeAr
   for (int i = tid; i < HD; i += kAppendThreads) ks[i] = bf16_to_f32(kp[i]);
   __syncthreads();
   // thread (row group g, column piece c) sums rows g, g + ng, ... of B^T over its
-  // 8 columns; rows past HD re-read the last row with weight 0
+  // 8 columns in float64 (every bf16 product is exact there); rows past HD
+  // re-read the last row with weight 0
   const int nch = r / 8, ng = kAppendThreads / nch;   // r <= 2048 keeps ng >= 4
   const int c = tid % nch, g = tid / nch;
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   if (g < ng) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int i0 = g; i0 < HD; i0 += 8 * ng) {
       u32x4 w[8];
 #pragma unroll
@@ -1087,39 +1089,42 @@ __global__ __launch_bounds__(kAppendThreads) void append_project_kernel(DecodeAr
 #pragma unroll
       for (int m = 0; m < 8; m++) {
         const int i = i0 + m * ng;
-        const float x = i < HD ? ks[min(i, HD - 1)] : 0.f;
+        const double x = i < HD ? (double)ks[min(i, HD - 1)] : 0.0;
         float y[8];
         unpack8(w[m], y);
 #pragma unroll
-        for (int k = 0; k < 8; k++) acc[k] = fmaf(x, y[k], acc[k]);
+        for (int k = 0; k < 8; k++) acc[k] = fma(x, (double)y[k], acc[k]);
       }
     }
-#pragma unroll
-    for (int k = 0; k < 8; k++) red[g * r + c * 8 + k] = acc[k];
   }
-  __syncthreads();
-  // sum the ng groups: parts of them first, then the parts
-  const int parts = kAppendThreads / r;              // >= 1 (r <= 1024) or 0
-  if (parts > 0) {
-    if (tid < parts * r) {
-      const int j = tid % r, pt = tid / r;
-      float sum = 0.f;
-      for (int gg = pt; gg < ng; gg += parts) sum += red[gg * r + j];
-      red2[pt * r + j] = sum;
+  // sum the ng groups, four of each thread's eight columns per round: parts of
+  // the groups first, then the parts.  Column j = 8c + 4hf + k sits at index
+  // jj = 4c + k of the round's r/2 columns.
+  const int R2 = r / 2, parts = kAppendThreads / R2;   // r <= 2048 keeps parts >= 1
+  for (int hf = 0; hf < 2; hf++) {
+    if (g < ng) {
+#pragma unroll
+      for (int k = 0; k < 4; k++) red[g * R2 + c * 4 + k] = acc[hf * 4 + k];
     }
     __syncthreads();
-  }
-  for (int j = tid; j < r; j += kAppendThreads) {
-    float sum = 0.f;
-    if (parts > 0)
-      for (int pt = 0; pt < parts; pt++) sum += red2[pt * r + j];
-    else
-      for (int gg = 0; gg < ng; gg++) sum += red[gg * r + j];
-    const int64_t at = ((int64_t)b * a.a_rows + a.seq_len + t) * r + j;
-    if (a.a_format == SKV_FORMAT_FP8_E5M2)
-      reinterpret_cast<uint8_t*>(A)[at] = f32_to_e5m2(sum);
-    else
-      A[at] = f32_to_bf16(sum);
+    if (tid < parts * R2) {
+      const int jj = tid % R2, pt = tid / R2;
+      double sum = 0.0;
+      for (int gg = pt; gg < ng; gg += parts) sum += red[gg * R2 + jj];
+      red2[pt * R2 + jj] = sum;
+    }
+    __syncthreads();
+    for (int jj = tid; jj < R2; jj += kAppendThreads) {
+      double sum = 0.0;
+      for (int pt = 0; pt < parts; pt++) sum += red2[pt * R2 + jj];
+      const int j = (jj >> 2) * 8 + hf * 4 + (jj & 3);
+      const int64_t at = ((int64_t)b * a.a_rows + a.seq_len + t) * r + j;
+      if (a.a_format == SKV_FORMAT_FP8_E5M2)
+        reinterpret_cast<uint8_t*>(A)[at] = f64_to_e5m2_rne(sum);
+      else
+        A[at] = f64_to_bf16_rne(sum);
+    }
+    __syncthreads();   // red and red2 are rewritten by the next round
   }
 }
 

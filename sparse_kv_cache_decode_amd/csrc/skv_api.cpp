@@ -71,10 +71,13 @@ struct skv_layer {
   int32_t *cand_map = nullptr, *outlier_ids = nullptr, *slot_cand = nullptr, *slot_chunk = nullptr,
           *miss_slot = nullptr, *miss_chunk = nullptr, *miss_cand = nullptr, *free_slot = nullptr,
           *n_miss = nullptr, *hits_last = nullptr;
-  uint32_t *resident = nullptr, *keys = nullptr, *part_keys = nullptr, *merge_keys = nullptr;
-  int32_t *part_idx = nullptr, *merge_idx = nullptr;
+  uint32_t *resident = nullptr, *keys = nullptr;
   long long *hits_total = nullptr, *miss_total = nullptr;
-  float *logits = nullptr, *lse_part = nullptr, *attn_part = nullptr, *min_cos = nullptr;
+  float* min_cos = nullptr;
+  // per-step transient scratch (logits, LSE partials, selection lists, attention
+  // partials): the handle's own region of the pool, laid out by `xs_layout`
+  TransientLayout xs_layout;
+  char* xs = nullptr;
   double* inv_freq = nullptr;
   std::vector<double> eig;
   hipStream_t side = nullptr;        // the device's shared side stream: host-value gather
@@ -259,15 +262,9 @@ DecodeArgs decode_args(skv_layer* h) {
   a.hits_last = h->hits_last;
   a.hits_total = h->hits_total;
   a.miss_total = h->miss_total;
-  a.logits = h->logits;
-  a.lse_part = h->lse_part;
   a.keys = h->keys;
   select_partition(h->n_cand, c.top_k, h->G, h->P, &a.n_part, &a.part_size);
-  a.part_keys = h->part_keys;
-  a.part_idx = h->part_idx;
-  a.merge_keys = h->merge_keys;
-  a.merge_idx = h->merge_idx;
-  a.attn_part = h->attn_part;
+  apply_transient(a, h->xs_layout, h->xs);
   return a;
 }
 
@@ -278,6 +275,66 @@ DecodeArgs decode_args(skv_layer* h) {
   } while (0)
 
 }  // namespace
+
+namespace skv {
+
+size_t transient_bytes(const skv_layer* h) { return h->xs_layout.bytes; }
+
+skv_status decode_enqueue(skv_layer* h, const uint16_t* q, float* out, int32_t* chunk_ids, void* stream,
+                          char* xs) {
+  if (!h) return SKV_ERR_INVALID_ARG;
+  if (h->poisoned) return SKV_ERR_STATE;
+  if (!q || !out || !chunk_ids) return SKV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(chunk_ids, 4)) return SKV_ERR_INVALID_ARG;
+  // a host pointer here would fault the kernels: refuse it before any launch
+  if (!is_device_ptr(q) || !is_device_ptr(out) || !is_device_ptr(chunk_ids)) return SKV_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DecodeArgs a = decode_args(h);
+  apply_transient(a, h->xs_layout, xs);
+  a.q = q;
+  a.out = out;
+  a.chunk_ids = chunk_ids;
+  {
+    hipEvent_t* ev = h->t_n < h->t_cap ? &h->tev[(size_t)h->t_n * kEv] : nullptr;
+    if (h->need_reset) {
+      HIP_TRY(launch_reset_cache(a, s));
+      h->need_reset = false;
+    }
+    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+    HIP_TRY(launch_score(a, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
+    HIP_TRY(launch_select(a, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    if (a.host_values) {
+      HIP_TRY(hipEventRecord(h->ev_fork, s));
+      HIP_TRY(hipStreamWaitEvent(h->side, h->ev_fork, 0));
+      if (ev) HIP_TRY(hipEventRecord(ev[5], h->side));
+      HIP_TRY(launch_value_gather(a, h->side));
+      if (ev) HIP_TRY(hipEventRecord(ev[6], h->side));
+      HIP_TRY(hipEventRecord(h->ev_join, h->side));
+      HIP_TRY(launch_rebuild(a, s));
+      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+      HIP_TRY(hipStreamWaitEvent(s, h->ev_join, 0));
+    } else {
+      HIP_TRY(launch_rebuild(a, s));
+      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+    }
+    HIP_TRY(launch_attention(a, s));
+    if (ev) {
+      HIP_TRY(hipEventRecord(ev[4], s));
+      h->t_n++;
+    }
+  }
+  h->steps++;
+  h->last_stream = s;
+  return SKV_OK;
+hip_fail:
+  (void)hipGetLastError();
+  h->poisoned = true;
+  return SKV_ERR_HIP;
+}
+
+}  // namespace skv
 
 extern "C" {
 
@@ -383,17 +440,24 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const size_t oHl = cv.take<int32_t>(P);
   const size_t oRes = cv.take<uint32_t>((size_t)P * h->res_words);
   const size_t oKeys = cv.take<uint32_t>((size_t)P * n_c);
-  const size_t oPk = cv.take<uint32_t>((size_t)P * n_part_cap * K);
-  const size_t oPi = cv.take<int32_t>((size_t)P * n_part_cap * K);
-  const int n_merge_cap = n_part_cap > 1 ? (n_part_cap + 1) / 2 : 0;   // first tree level's lists
-  const size_t oMk = cv.take<uint32_t>((size_t)P * n_merge_cap * K);
-  const size_t oMi = cv.take<int32_t>((size_t)P * n_merge_cap * K);
   const size_t oHt = cv.take<long long>(P);
   const size_t oMt = cv.take<long long>(P);
-  const size_t oLg = cv.take<float>((size_t)P * G * ncp_cap);
-  const size_t oLp = cv.take<float>((size_t)P * nb_cap * G * 2);
-  const int n_split_max = (h->U + (c.max_new_tokens + C - 1) / C + h->upw - 1) / h->upw;
-  const size_t oAp = cv.take<float>((size_t)P * n_split_max * G * kPartStride);
+  {
+    // transient scratch, laid out from offset 0 so that any 256-byte aligned base serves
+    Carver tc;
+    TransientLayout& t = h->xs_layout;
+    t.part_keys = tc.take<uint32_t>((size_t)P * n_part_cap * K);
+    t.part_idx = tc.take<int32_t>((size_t)P * n_part_cap * K);
+    const int n_merge_cap = n_part_cap > 1 ? (n_part_cap + 1) / 2 : 0;   // first tree level's lists
+    t.merge_keys = tc.take<uint32_t>((size_t)P * n_merge_cap * K);
+    t.merge_idx = tc.take<int32_t>((size_t)P * n_merge_cap * K);
+    t.logits = tc.take<float>((size_t)P * G * ncp_cap);
+    t.lse_part = tc.take<float>((size_t)P * nb_cap * G * 2);
+    const int n_split_max = (h->U + (c.max_new_tokens + C - 1) / C + h->upw - 1) / h->upw;
+    t.attn_part = tc.take<float>((size_t)P * n_split_max * G * kPartStride);
+    t.bytes = (tc.off + kAlign - 1) / kAlign * kAlign;
+  }
+  const size_t oXs = cv.take<uint8_t>(h->xs_layout.bytes);
   const size_t oKn = cv.take<uint16_t>((size_t)P * c.max_new_tokens * kHeadDim);
   const size_t oVn = cv.take<uint16_t>((size_t)P * c.max_new_tokens * kHeadDim);
   const size_t oMc = cv.take<float>((size_t)P * n_c);
@@ -404,7 +468,6 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const int nseg = gram_segments(b, S, HD);
   void* L_full = nullptr;
   double *gpart = nullptr, *gram = nullptr;
-  uint16_t* psi_f = nullptr;   // Psi^T as bf16 hi and lo parts
   std::vector<double> psi((size_t)b * HD * r);
   std::vector<double> invf(kHeadDim / 2);
   int rc;
@@ -418,13 +481,11 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   }
   if (hipMalloc(&L_full, (size_t)P * n_c * lrow) != hipSuccess ||
       hipMalloc(&gpart, (size_t)b * nseg * HD * HD * 8) != hipSuccess ||
-      hipMalloc(&gram, (size_t)b * HD * HD * 8) != hipSuccess ||
-      hipMalloc(&psi_f, (size_t)2 * b * HD * r * 2) != hipSuccess) {
+      hipMalloc(&gram, (size_t)b * HD * HD * 8) != hipSuccess) {
     (void)hipGetLastError();
     if (L_full) (void)hipFree(L_full);
     if (gpart) (void)hipFree(gpart);
     if (gram) (void)hipFree(gram);
-    if (psi_f) (void)hipFree(psi_f);
     release(h);
     return SKV_ERR_OOM;
   }
@@ -451,15 +512,9 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->hits_last = (int32_t*)(base + oHl);
     h->resident = (uint32_t*)(base + oRes);
     h->keys = (uint32_t*)(base + oKeys);
-    h->part_keys = (uint32_t*)(base + oPk);
-    h->part_idx = (int32_t*)(base + oPi);
-    h->merge_keys = (uint32_t*)(base + oMk);
-    h->merge_idx = (int32_t*)(base + oMi);
     h->hits_total = (long long*)(base + oHt);
     h->miss_total = (long long*)(base + oMt);
-    h->logits = (float*)(base + oLg);
-    h->lse_part = (float*)(base + oLp);
-    h->attn_part = (float*)(base + oAp);
+    h->xs = base + oXs;
     h->key_new = (uint16_t*)(base + oKn);
     h->val_new = (uint16_t*)(base + oVn);
     h->min_cos = (float*)(base + oMc);
@@ -492,21 +547,19 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     (void)hipFree(L_full);
     (void)hipFree(gpart);
     (void)hipFree(gram);
-    (void)hipFree(psi_f);
     release(h);
     return SKV_ERR_INTERNAL;
   }
   // Psi in fp64 through the (now free) Gram partials buffer, b*nseg*HD*HD >= b*HD*r
-  // doubles; B^T and the projection's hi/lo parts are rounded from it on the GPU
+  // doubles; B^T is rounded from it and A = K Psi projected from it in float64
   HIP_TRY(hipMemcpyAsync(gpart, psi.data(), psi.size() * 8, hipMemcpyHostToDevice, s));
-  HIP_TRY(launch_split_psi(gpart, b, HD, r, b8, h->Bt, psi_f, s));
-  HIP_TRY(launch_project(k_pre, psi_f, b, S, HD, r, h->a_rows, a8, h->A, s));
+  HIP_TRY(launch_round_psi(gpart, b, HD, r, b8, h->Bt, s));
+  HIP_TRY(launch_project(k_pre, gpart, b, S, HD, r, h->a_rows, a8, h->A, s));
   HIP_TRY(launch_reset_cache(decode_args(h), s));
   HIP_TRY(hipStreamSynchronize(s));
   (void)hipFree(L_full);
   (void)hipFree(gpart);
   (void)hipFree(gram);
-  (void)hipFree(psi_f);
   h->last_stream = s;
   *out = h;
   return SKV_OK;
@@ -517,7 +570,6 @@ hip_fail:
   (void)hipFree(L_full);
   (void)hipFree(gpart);
   (void)hipFree(gram);
-  (void)hipFree(psi_f);
   release(h);
   return SKV_ERR_HIP;
 }
@@ -525,54 +577,7 @@ hip_fail:
 skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t* chunk_ids,
                            void* stream) {
   if (!h) return SKV_ERR_INVALID_ARG;
-  if (h->poisoned) return SKV_ERR_STATE;
-  if (!q || !out || !chunk_ids) return SKV_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(chunk_ids, 4)) return SKV_ERR_INVALID_ARG;
-  // a host pointer here would fault the kernels: refuse it before any launch
-  if (!is_device_ptr(q) || !is_device_ptr(out) || !is_device_ptr(chunk_ids)) return SKV_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  DecodeArgs a = decode_args(h);
-  a.q = q;
-  a.out = out;
-  a.chunk_ids = chunk_ids;
-  {
-    hipEvent_t* ev = h->t_n < h->t_cap ? &h->tev[(size_t)h->t_n * kEv] : nullptr;
-    if (h->need_reset) {
-      HIP_TRY(launch_reset_cache(a, s));
-      h->need_reset = false;
-    }
-    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
-    HIP_TRY(launch_score(a, s));
-    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
-    HIP_TRY(launch_select(a, s));
-    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
-    if (a.host_values) {
-      HIP_TRY(hipEventRecord(h->ev_fork, s));
-      HIP_TRY(hipStreamWaitEvent(h->side, h->ev_fork, 0));
-      if (ev) HIP_TRY(hipEventRecord(ev[5], h->side));
-      HIP_TRY(launch_value_gather(a, h->side));
-      if (ev) HIP_TRY(hipEventRecord(ev[6], h->side));
-      HIP_TRY(hipEventRecord(h->ev_join, h->side));
-      HIP_TRY(launch_rebuild(a, s));
-      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
-      HIP_TRY(hipStreamWaitEvent(s, h->ev_join, 0));
-    } else {
-      HIP_TRY(launch_rebuild(a, s));
-      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
-    }
-    HIP_TRY(launch_attention(a, s));
-    if (ev) {
-      HIP_TRY(hipEventRecord(ev[4], s));
-      h->t_n++;
-    }
-  }
-  h->steps++;
-  h->last_stream = s;
-  return SKV_OK;
-hip_fail:
-  (void)hipGetLastError();
-  h->poisoned = true;
-  return SKV_ERR_HIP;
+  return skv::decode_enqueue(h, q, out, chunk_ids, stream, h->xs);
 }
 
 skv_status skv_append_token(skv_layer* h, const uint16_t* k_new, const uint16_t* v_new, void* stream) {

@@ -39,6 +39,28 @@ __device__ __forceinline__ uint8_t f32_to_e5m2(float f) {
   return (uint8_t)(sign | ((uint32_t)e << 2) | ((v >> 21) & 3u));
 }
 
+// double -> bf16 bits, one rounding to nearest even at the 8th significant bit
+// (the double is cut to 8 significant bits first, which float holds exactly).
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  u += (1ull << 44) - 1ull + ((u >> 45) & 1ull);
+  u &= ~((1ull << 45) - 1ull);
+  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+}
+
+// double -> FP8 E5M2 byte, one rounding to nearest even (2 mantissa bits kept;
+// below 2^-14 the grid is 2^-16; past 57344 the result is inf).
+__device__ __forceinline__ uint8_t f64_to_e5m2_rne(double x) {
+  const uint32_t sign = (uint32_t)((uint64_t)__double_as_longlong(x) >> 56) & 0x80u;
+  const double ax = fabs(x);
+  if (ax < 0x1p-14) return (uint8_t)(sign | (uint32_t)rint(ax * 65536.0));
+  uint64_t v = (uint64_t)__double_as_longlong(ax);
+  v += (1ull << 49) - 1ull + ((v >> 50) & 1ull);
+  const int e = (int)(v >> 52) - 1023 + 15;
+  if (e >= 31) return (uint8_t)(sign | 0x7cu);
+  return (uint8_t)(sign | ((uint32_t)e << 2) | (uint32_t)((v >> 50) & 3ull));
+}
+
 // Unpack 8 bf16 held in a 16-byte word into floats.
 __device__ __forceinline__ void unpack8(const u32x4 w, float* x) {
 #pragma unroll
@@ -50,16 +72,19 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* x) {
 
 // ---------------------------------------------------------------- RoPE
 
-// cos/sin of pos * inv_freq with the product and the reduction modulo 2*pi in
-// float64 (positions up to 2^20 lose nothing), sincos of the reduced angle in fp32.
-__device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq, float* c, float* s) {
-  const double two_pi_hi = 6.283185307179586;          // nearest double to 2*pi
-  const double two_pi_lo = 2.4492935982947064e-16;     // 2*pi - two_pi_hi
+// cos/sin of pos * inv_freq entirely in float64: the product and the reduction
+// modulo 2*pi (positions up to 2^20 lose nothing), then the float64 sincos of the
+// reduced angle.  Used where a rotated key is
+// rounded once to its storage format (landmarks, exact outlier / window keys,
+// exact generated keys), so that the rounding sees the float64 value.
+__device__ __forceinline__ void rope_cs64(int64_t pos, double inv_freq, double* c, double* s) {
+  const double two_pi_hi = 6.283185307179586;
+  const double two_pi_lo = 2.4492935982947064e-16;
   double a = (double)pos * inv_freq;
   double n = rint(a * 0.15915494309189535);
   double r = fma(-n, two_pi_hi, a);
   r = fma(-n, two_pi_lo, r);
-  __sincosf((float)r, s, c);
+  sincos(r, s, c);
 }
 
 // pos * inv_freq reduced to [-pi, pi] in float64, returned as float.
@@ -98,6 +123,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ double wave_sum64(double v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {

@@ -77,6 +77,32 @@ struct DecodeArgs {
   int32_t* chunk_ids;         // [P][K]
 };
 
+// Byte offsets of a decode step's transient scratch from a 256-byte aligned base
+// (nothing in it has to start at zero: every step writes each part before it
+// reads it).  Computed at build for the handle's largest candidate count.
+struct TransientLayout {
+  size_t logits = 0, lse_part = 0, part_keys = 0, part_idx = 0, merge_keys = 0, merge_idx = 0,
+         attn_part = 0, bytes = 0;
+};
+
+inline void apply_transient(DecodeArgs& a, const TransientLayout& t, char* base) {
+  a.logits = reinterpret_cast<float*>(base + t.logits);
+  a.lse_part = reinterpret_cast<float*>(base + t.lse_part);
+  a.part_keys = reinterpret_cast<uint32_t*>(base + t.part_keys);
+  a.part_idx = reinterpret_cast<int32_t*>(base + t.part_idx);
+  a.merge_keys = reinterpret_cast<uint32_t*>(base + t.merge_keys);
+  a.merge_idx = reinterpret_cast<int32_t*>(base + t.merge_idx);
+  a.attn_part = reinterpret_cast<float*>(base + t.attn_part);
+}
+
+// One decode step of `h` (validation, then every launch on `stream`), with the
+// transient scratch at `xs`: a 256-byte aligned device region of at least
+// transient_bytes(h) bytes.  skv_decode_step passes the handle's own region, the
+// no-allocation entry point the library's static device array.
+skv_status decode_enqueue(skv_layer* h, const uint16_t* q, float* out, int32_t* chunk_ids, void* stream,
+                          char* xs);
+size_t transient_bytes(const skv_layer* h);
+
 // ---- build launchers (build_kernels.hip); all enqueue on `st`
 // L_full: [P][n_c][d] bf16, or bytes with fp8 (FP8 E5M2)
 hipError_t launch_rope_landmark(const uint16_t* k_pre, int b, int64_t S, int H, int C,
@@ -100,15 +126,12 @@ hipError_t launch_gemm_f64(const double* A, const double* B, double* C, int batc
 // C[bi] (M x N) = A[bi]^T B[bi] with A[bi] stored K x M, B[bi] K x N
 hipError_t launch_gemm_f64_tn(const double* A, const double* B, double* C, int batch, int M, int N,
                               int K, hipStream_t st);
-// A[b] rows 0..S-1 of a [b][a_rows][r] array
-// psi [b][HD][r] fp64 -> bt = bf16(psi), or FP8 E5M2 bytes with b8 (same layout), and
-// psi_t = Psi^T as bf16 hi [b][r][HD] followed by bf16 lo = bf16(psi - hi) [b][r][HD];
-// every rounding to nearest even, once, from the fp64 value
-hipError_t launch_split_psi(const double* psi, int b, int HD, int r, bool b8, void* bt, uint16_t* psi_t,
-                            hipStream_t st);
-// A: [b][a_rows][r] bf16, or bytes with fp8 (FP8 E5M2); psi_t: Psi^T split into
-// bf16 hi [b][r][HD] followed by bf16 lo [b][r][HD]
-hipError_t launch_project(const uint16_t* k_pre, const uint16_t* psi_t, int b, int64_t S, int HD, int r,
+// psi [b][HD][r] fp64 -> bt = bf16(psi), or FP8 E5M2 bytes with b8 (same layout),
+// each value rounded once to nearest even from the fp64 value
+hipError_t launch_round_psi(const double* psi, int b, int HD, int r, bool b8, void* bt, hipStream_t st);
+// Rows 0..S-1 of A [b][a_rows][r] = K_b Psi_b in float64, each rounded once to
+// bf16, or FP8 E5M2 bytes with fp8; psi [b][HD][r] float64
+hipError_t launch_project(const uint16_t* k_pre, const double* psi, int b, int64_t S, int HD, int r,
                           int64_t a_rows, bool fp8, void* A, hipStream_t st);
 
 // ---- decode launchers (decode_kernels.hip)

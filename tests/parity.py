@@ -10,33 +10,22 @@ Bars (floating point from bf16 storage with fp32 accumulation):
   tie rule;
 * hit counts exact against the oracle whenever the selections agree, and always
   equal to |I_t & I_{t-1}| of the GPU's own consecutive selections;
-* landmarks: each value equal to the oracle's or one spacing of the storage
-  format away (bf16, or E5M2 with FP8 storage), with at most 1 in 1000 values
-  differing: the GPU rounds an fp32 mean of fp32-rotated keys, the oracle an
-  fp64 one, so a mean that falls near a rounding boundary may go either way.
-  One such bf16 value moves a landmark's logit by up to 2^-8 of one of its 128
-  terms (1/8 of it for E5M2), which exceeds the near-tie margin at the K-th
-  score (seen: 1.3e-3 at K = 60 of 8178 candidates); decode parity therefore
-  runs the oracle on the landmarks the GPU built (adopt_gpu_state), once they
-  have passed this bar, and the tie margin then covers the fp32 arithmetic of
-  the decode step alone (logit error at most 128 * 2^-24 * sum|q_d L_d| / sqrt(d),
-  about 2e-4 at the workloads' magnitudes);
-* B: each well-determined column within one spacing of its storage format
-  (bf16, or E5M2 with FP8 storage) of the oracle's;
-* rows of A: within 2^-7 relative of the oracle's (bf16; both sides round the
-  same product, the GPU's from an fp32 projection K Psi, the oracle's from its
-  fp64 U_r Sigma_r); with FP8 storage each value the oracle's or one E5M2
-  spacing away, at most 1 in 1000 differing;
-* A B per head within 1e-2 relative Frobenius of the oracle's: singular
-  vectors of nearly equal singular values are fixed only as a subspace, so the
-  two factorizations may differ by a rotation inside it, and every rounding
-  flip of A moves a rebuilt key by up to 2^-8 (1/8 with FP8) of one of its r
-  terms.  Rebuilt keys built from the two factorizations then differ by more
-  than the decode step's own arithmetic (output errors up to ~7e-3 were seen),
-  so decode parity runs the oracle on the A and B the GPU built, as on its
-  landmarks (adopt_gpu_state), once they have passed these bars.  The oracle
-  then rebuilds keys in fp64 from the same bf16 (or E5M2) factors and rounds
-  them, and the output comparison measures the decode path alone.
+* build state (check_build): outlier and candidate ids exact; every landmark
+  value and every exact outlier / window key equal to the oracle's rounding (the
+  GPU rotates and averages in float64 and rounds once, as the oracle does); B
+  and the rows of A equal to the oracle's rounding except where the GPU's
+  eigenvector basis (subspace iteration on a Gram matrix with fp32 sums of 8
+  exact products) and LAPACK's SVD differ near a rounding boundary: those
+  values are one spacing of the storage format away and at most 1 in 10 000
+  of them differ (seen: a few in a million); columns of nearly equal singular
+  values are fixed only as a subspace and are covered by A B per head within
+  1e-2 relative Frobenius.
+
+Two protocols use these bars.  End to end (test_gpu_end_to_end.py and the
+64-step full-size case), the oracle decodes on its own build.  On the GPU's
+state (adopt_gpu_state: the oracle decodes on the exported landmarks, A and B),
+the comparison measures the decode arithmetic alone and is held to the tighter
+DECODE_* bars.
 """
 from __future__ import annotations
 
@@ -57,6 +46,7 @@ REL_L2 = 5e-3
 DECODE_MAX_ABS = 2e-3
 DECODE_REL_L2 = 2e-4
 LANDMARK_DIFF_FRACTION = 1e-3
+FACTOR_DIFF_FRACTION = 1e-4
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
@@ -143,13 +133,25 @@ def adopt_gpu_state(st: O.State, gpu: dict) -> None:
     st.B = O.bf16_bits_to_f64(gpu["B"]).reshape(st.B.shape)
 
 
-def check_build(gpu: dict, st: O.State):
-    """Build-state parity: outliers, candidates, landmarks, exact caches, factors."""
+def check_build(gpu: dict, st: O.State, exact_landmarks: bool = True):
+    """Build-state parity: outliers, candidates, landmarks, exact caches, factors.
+
+    The GPU rotates, averages and takes cosines in float64 and rounds each stored
+    value once, so with ``exact_landmarks`` every landmark value and every exact
+    outlier / window key must equal the oracle's rounding (a float64 mean within
+    ~1e-15 of a rounding boundary could still go either way; none is expected at
+    these sizes)."""
     cfg = st.cfg
     np.testing.assert_array_equal(gpu["outlier_ids"], st.outliers)
     np.testing.assert_array_equal(gpu["cand_ids"], st.cand)
-    np.testing.assert_allclose(gpu["min_cos"], st.min_cos, atol=2e-5)
-    # fp32 RoPE of O(1) keys: absolute error well under 1e-5
+    # min-cos is computed in float64 and exported as float32
+    np.testing.assert_allclose(gpu["min_cos"], st.min_cos, rtol=0, atol=1e-6)
+    if exact_landmarks:
+        lm = O.bf16_bits_to_f64(gpu["landmarks"]).reshape(st.L.shape)
+        nd = int(np.sum(lm != st.L))
+        assert nd == 0, f"{nd} landmark values differ from the oracle's rounding"
+        np.testing.assert_array_equal(O.bf16_bits_to_f64(gpu["k_outlier"]).reshape(st.K_out.shape), st.K_out)
+        np.testing.assert_array_equal(O.bf16_bits_to_f64(gpu["k_window"]).reshape(st.K_win.shape), st.K_win)
     if cfg.landmark_format == "e5m2":
         excess, frac = e5m2_close(gpu["landmarks"], st.L)
         assert excess <= 0, f"FP8 landmark off by more than one spacing ({excess})"
@@ -195,15 +197,21 @@ def check_build(gpu: dict, st: O.State):
             spacing = np.where(ob == 0, 0.0, np.ldexp(1.0, e - 8))
         excess = np.abs(gb - ob) - spacing - 1e-9 - dk[well][None, :, None]
         assert excess.size == 0 or excess.max() <= 0, f"B differs beyond rounding ({excess.max()})"
+        # A = K Psi in float64 on both sides, rounded once: equal but for values
+        # within the two bases' difference of a rounding boundary
         if cfg.a_format == "e5m2":
-            # fp32 projection error on top of the rounding: well under 1e-5 of max|A|
-            excess, frac = e5m2_close(gpu["A"][bi][:, well], st.A[bi][:, well], 1e-5 * np.abs(st.A[bi]).max())
+            excess, frac = e5m2_close(gpu["A"][bi][:, well], st.A[bi][:, well], 1e-9 * np.abs(st.A[bi]).max())
             assert excess <= 0, f"FP8 A off by more than one spacing ({excess})"
-            assert frac <= LANDMARK_DIFF_FRACTION, f"{frac:.2e} of the FP8 A values differ"
         else:
             ga, oa = A[bi][:, well], st.A[bi][:, well]
-            rel = np.abs(ga - oa) / (np.abs(oa) + 1e-3 * np.abs(st.A[bi]).max())
-            assert rel.size == 0 or rel.max() <= 2 ** -7, f"A differs by {rel.max()}"
+            _, e = np.frexp(oa)
+            excess = np.abs(ga - oa) - np.where(oa == 0, 0.0, np.ldexp(1.0, e - 8)) - 1e-9 * np.abs(st.A[bi]).max()
+            assert excess.size == 0 or excess.max() <= 0, f"A differs beyond one spacing ({excess.max()})"
+            frac = float(np.mean(ga != oa)) if ga.size else 0.0
+        assert frac <= FACTOR_DIFF_FRACTION, f"{frac:.2e} of the values of A differ"
+        if gb.size:
+            fb = float(np.mean(gb != ob))
+            assert fb <= FACTOR_DIFF_FRACTION, f"{fb:.2e} of the values of B differ"
     for b in range(cfg.batch):
         for h in range(cfg.n_kv_heads):
             pg = A[b] @ B[b, h]

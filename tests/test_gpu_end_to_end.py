@@ -1,0 +1,74 @@
+"""End-to-end parity: the GPU's own build and decode against the oracle's own
+build and decode of the same seeded bf16 inputs.  Nothing the GPU computed is
+handed to the oracle: the oracle factorises, builds landmarks and outliers, and
+decodes by itself, in float64.
+
+Bars (the spec rule): selected chunk ids bit-exact except chunks whose
+oracle score lies within 1e-3 relative of the K-th score; outputs within
+max |err| <= 2e-2 and relative L2 <= 5e-3; build state as check_build states it,
+with every landmark value and every exact outlier / window key equal to the
+oracle's rounding (the build rotates and averages in float64 and rounds once).
+
+The decode-only comparisons on the GPU's exported state (test_gpu_parity.py,
+test_gpu_fullsize.py) keep the tighter bars of the decode arithmetic alone."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import shadowkv as O
+from sparse_kv_cache_decode_amd import skv, synth
+from tests.parity import MAX_ABS, REL_L2, bits, check_build, check_ids, check_out, reference_out
+
+pytestmark = pytest.mark.gpu
+
+
+def run_end_to_end(shape, steps, seed=0, placement=skv.SKV_VALUES_DEVICE):
+    print(f"[e2e] {shape.name} b={shape.batch} S={shape.seq_len} G={shape.group} C={shape.chunk} "
+          f"K={shape.top_k} O={shape.n_outlier} r={shape.rank} steps={steps}", flush=True)
+    k, v = synth.layer_cache_np(shape, 0, seed)
+    q = synth.queries_np(shape, k, 0, steps, seed)
+    st = O.build(O.config_from(shape), bits(k), bits(v))
+    vd = v.cuda()
+    if placement == skv.SKV_VALUES_HOST:
+        vd = torch.empty(v.shape, dtype=v.dtype, pin_memory=True)
+        vd.copy_(v)
+    layer = skv.Layer(shape, k.cuda(), vd, placement)
+    ex = layer.export()
+    check_build(ex, st, exact_landmarks=True)
+    fa = float(np.mean(O.bf16_bits_to_f64(ex["A"]).reshape(st.A.shape) != st.A))
+    fb = float(np.mean(O.bf16_bits_to_f64(ex["B"]).reshape(st.B.shape) != st.B))
+    print(f"[e2e] factor values that differ from the oracle's: A {fa:.2e}, B {fb:.2e}", flush=True)
+    prev = None
+    worst = (0.0, 0.0)
+    swaps = 0
+    for t in range(steps):
+        out, ids = layer.decode(q[t].cuda())
+        torch.cuda.synchronize()
+        res = O.decode_step(st, bits(q[t]), prev)
+        gids = ids.cpu().numpy()
+        differ = check_ids(gids, st, res)
+        swaps += len(differ)
+        e = check_out(out.cpu().numpy(), reference_out(st, bits(q[t]), res, gids, differ), MAX_ABS, REL_L2)
+        worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+        prev = res.ids
+    print(f"[e2e] ok: max|err| {worst[0]:.2e} relL2 {worst[1]:.2e} near-tie swaps {swaps}", flush=True)
+    layer.close()
+    return worst
+
+
+def test_end_to_end_tiny_8k():
+    run_end_to_end(synth.SHAPES["tiny_8k"], steps=4)
+
+
+def test_end_to_end_eight_kv_heads_small_budget():
+    # 8178 candidates, K = 60, 32 q / 8 KV heads: the case whose 60th and 61st
+    # chunks swapped when the build rounded fp32 chunk means
+    s = synth.Shape(name="small", batch=2, n_q_heads=32, n_kv_heads=8, head_dim=128, seq_len=65536,
+                    rank=64, chunk=8, top_k=60, n_outlier=10, window=32, latent_rank=64)
+    run_end_to_end(s, steps=3)
+
+
+def test_end_to_end_host_values_ragged():
+    s = synth.Shape(name="small", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=8168,
+                    rank=64, chunk=8, top_k=13, n_outlier=5, window=32, latent_rank=64)
+    run_end_to_end(s, steps=3, placement=skv.SKV_VALUES_HOST)

@@ -91,3 +91,63 @@ def test_one_layer_sampled(name, sampled, fmt):
             prev = res.ids
         print(f"[fullsize] batch element {b}: max|err| {worst[0]:.2e} relL2 {worst[1]:.2e}", flush=True)
     layer.close()
+
+
+@pytest.mark.timeout(900)
+def test_llama_64_drifting_steps():
+    """The Llama-3.1-8B shape's 64 drifting decode steps on one layer: every pair
+    through the properties, batch element 0 against the oracle end to end (its
+    own build) and on the GPU's exported factors (decode arithmetic alone)."""
+    import copy
+
+    from tests.parity import MAX_ABS, REL_L2
+    shape = synth.SHAPES["llama3_8b_122k"]
+    steps = shape.steps
+    print(f"[fullsize] {steps} steps of {shape}", flush=True)
+    k, v = synth.layer_cache_torch(shape, 0, 0, "cuda")
+    q = synth.queries_torch(shape, k, 0, steps, 0)
+    layer = skv.Layer(shape, k, v)
+    ex = layer.export()
+    outs, idss, hits = [], [], []
+    for t in range(steps):
+        out, ids = layer.decode(q[t])
+        torch.cuda.synchronize()
+        outs.append(out[0:1].cpu().numpy())
+        idss.append(ids.cpu().numpy())
+        hits.append(layer.stats()["last_hits"])
+        assert torch.isfinite(out).all()
+    layer.close()
+    for t in range(1, steps):
+        own = sum(len(np.intersect1d(idss[t][b, h], idss[t - 1][b, h]))
+                  for b in range(shape.batch) for h in range(shape.n_kv_heads))
+        assert hits[t] == own, t
+        assert np.all(np.diff(idss[t], axis=-1) > 0)
+    print(f"[fullsize] GPU done; mean alpha {np.mean(hits[1:]) / (shape.pairs * shape.top_k):.3f}", flush=True)
+    one = shape.replace(batch=1)
+    qb = [bits(q[t])[0:1] for t in range(steps)]
+    st = O.build(O.config_from(one), bits(k[0:1]), bits(v[0:1]))
+    del k, v
+    check_build(_slice_state(ex, 0), st)
+    sl = _slice_state(ex, 0)
+    print(f"[fullsize] factor values that differ from the oracle's: "
+          f"A {np.mean(O.bf16_bits_to_f64(sl['A']).reshape(st.A.shape) != st.A):.2e}, "
+          f"B {np.mean(O.bf16_bits_to_f64(sl['B']).reshape(st.B.shape) != st.B):.2e}", flush=True)
+    for label, state, bars in (("end to end", st, (MAX_ABS, REL_L2)),
+                               ("GPU factors", None, (DECODE_MAX_ABS, DECODE_REL_L2))):
+        if state is None:
+            state = copy.deepcopy(st)
+            adopt_gpu_state(state, _slice_state(ex, 0))
+        prev, worst, swaps = None, (0.0, 0.0), 0
+        for t in range(steps):
+            res = O.decode_step(state, qb[t], prev)
+            gids = idss[t][0:1]
+            differ = check_ids(gids, state, res)
+            swaps += len(differ)
+            e = check_out(outs[t], reference_out(state, qb[t], res, gids, differ), *bars)
+            worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+            if not differ and t > 0 and np.array_equal(idss[t - 1][0:1], prev):
+                assert int(res.hits.sum()) == sum(len(np.intersect1d(gids[0, h], prev[0, h]))
+                                                  for h in range(shape.n_kv_heads))
+            prev = res.ids
+        print(f"[fullsize] element 0, {label}: max|err| {worst[0]:.2e} relL2 {worst[1]:.2e} "
+              f"near-tie swaps {swaps}", flush=True)
