@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 6
+#define SKV_ABI_VERSION 7
 
 typedef int32_t skv_status;
 #define SKV_OK 0
@@ -60,6 +60,8 @@ typedef int32_t skv_status;
 #define SKV_ERR_HIP 5          /* a HIP runtime call failed                       */
 #define SKV_ERR_STATE 6        /* handle poisoned by an earlier HIP failure       */
 #define SKV_ERR_INTERNAL 7     /* internal invariant broken (e.g. no convergence)  */
+#define SKV_ERR_SCRATCH 8      /* a decode step's transient scratch exceeds the
+                                  static array of skv_decode_step_noalloc          */
 
 /* Value placement (the value store V_CPU of the pages). */
 #define SKV_VALUES_DEVICE 0    /* values stay in HBM and are read by chunk id      */
@@ -246,6 +248,28 @@ skv_status skv_decode_step(skv_layer* h, const uint16_t* q, float* out, int32_t*
  * max_new_tokens reached), STATE, HIP.
  */
 skv_status skv_append_token(skv_layer* h, const uint16_t* k_new, const uint16_t* v_new, void* stream);
+
+/*
+ * skv_decode_step_noalloc -- for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same step, arguments, outputs and errors as skv_decode_step,
+ * but the step's transient scratch (logits, log-sum-exp partials, selection
+ * lists, attention partials) lives in a static device array of the library,
+ * SKV_NOALLOC_SCRATCH_BYTES per device, held until the process ends, instead of
+ * the handle's own region.  The call allocates nothing.
+ *   - A handle whose transient scratch is larger gives SKV_ERR_SCRATCH before
+ *     anything is enqueued (the transient scratch is about
+ *     4 * b * n_q_heads * (n_cand + 4) bytes of logits plus lists and attention
+ *     partials: 18 MB for a layer of batch 8, 32 query heads, 15 310 candidates).
+ *   - Every call on one device uses that device's one array: calls whose work
+ *     overlaps on a device (other streams, other threads) race on it and must be
+ *     ordered by the caller.  Nothing in the array needs clearing between calls.
+ *   - Errors: as skv_decode_step, plus SCRATCH; HIP if the array's address
+ *     cannot be looked up.
+ */
+#define SKV_NOALLOC_SCRATCH_BYTES (64 << 20)
+skv_status skv_decode_step_noalloc(skv_layer* h, const uint16_t* q, float* out, int32_t* chunk_ids,
+                                   void* stream);
 
 /* Temporal-cache counters; synchronises with the last stream used. */
 skv_status skv_get_stats(const skv_layer* h, skv_stats* stats);

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libskv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["skv_api.cpp", "eig_host.cpp", "build_kernels.hip", "decode_kernels.hip"]
+SOURCES = ["skv_api.cpp", "eig_host.cpp", "build_kernels.hip", "decode_kernels.hip", "skv_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

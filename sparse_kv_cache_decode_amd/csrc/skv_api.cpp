@@ -350,6 +350,7 @@ const char* skv_status_string(skv_status s) {
     case SKV_ERR_HIP: return "HIP runtime error";
     case SKV_ERR_STATE: return "handle poisoned by an earlier HIP error";
     case SKV_ERR_INTERNAL: return "internal error (eigensolver did not converge)";
+    case SKV_ERR_SCRATCH: return "transient scratch larger than the static array of skv_decode_step_noalloc";
     default: return "unknown status";
   }
 }

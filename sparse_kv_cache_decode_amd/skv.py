@@ -17,13 +17,14 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libskv.so"
 _lib = None
 
 SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_SHAPE, SKV_ERR_UNSUPPORTED = 0, 1, 2, 3
-SKV_ERR_OOM, SKV_ERR_HIP, SKV_ERR_STATE, SKV_ERR_INTERNAL = 4, 5, 6, 7
+SKV_ERR_OOM, SKV_ERR_HIP, SKV_ERR_STATE, SKV_ERR_INTERNAL, SKV_ERR_SCRATCH = 4, 5, 6, 7, 8
+SKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 SKV_VALUES_DEVICE, SKV_VALUES_HOST = 0, 1
 SKV_NEW_EXACT, SKV_NEW_LOWRANK = 0, 1
 SKV_FORMAT_BF16, SKV_FORMAT_FP8_E5M2 = 0, 1
 FORMATS = {"bf16": SKV_FORMAT_BF16, "e5m2": SKV_FORMAT_FP8_E5M2}
 
-EXPORTED = ["skv_build", "skv_decode_step", "skv_append_token", "skv_get_stats", "skv_reset_temporal_cache",
+EXPORTED = ["skv_build", "skv_decode_step", "skv_decode_step_noalloc", "skv_append_token", "skv_get_stats", "skv_reset_temporal_cache",
             "skv_export_state", "skv_set_timing", "skv_get_timing", "skv_destroy",
             "skv_status_string", "skv_abi_version"]
 PHASES = ["score", "select", "rebuild", "value_gather", "attention"]
@@ -72,6 +73,8 @@ def lib():
         L.skv_build.restype = i32
         L.skv_decode_step.argtypes = [vp, vp, vp, vp, vp]
         L.skv_decode_step.restype = i32
+        L.skv_decode_step_noalloc.argtypes = [vp, vp, vp, vp, vp]
+        L.skv_decode_step_noalloc.restype = i32
         L.skv_append_token.argtypes = [vp, vp, vp, vp]
         L.skv_append_token.restype = i32
         L.skv_get_stats.argtypes = [vp, ctypes.POINTER(SkvStats)]
@@ -149,6 +152,11 @@ def skv_build(cfg: SkvConfig, k_pre, v, stream=None) -> int:
 def skv_decode_step(h: int, q, out, chunk_ids, stream=None) -> None:
     _check("skv_decode_step", lib().skv_decode_step(h, _ptr(q), _ptr(out), _ptr(chunk_ids),
                                                     _stream(stream)))
+
+
+def skv_decode_step_noalloc(h: int, q, out, chunk_ids, stream=None) -> None:
+    _check("skv_decode_step_noalloc", lib().skv_decode_step_noalloc(h, _ptr(q), _ptr(out), _ptr(chunk_ids),
+                                                                    _stream(stream)))
 
 
 def skv_append_token(h: int, k_new, v_new, stream=None) -> None:

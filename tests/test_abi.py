@@ -30,9 +30,9 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert skv.skv_abi_version() == 6
+    assert skv.skv_abi_version() == 7
     seen = set()
-    for code in range(8):
+    for code in range(9):
         s = skv.skv_status_string(code)
         assert s and s not in seen
         seen.add(s)
@@ -93,12 +93,19 @@ def test_build_null_arguments():
 def test_null_handle_calls():
     lib = skv.lib()
     assert lib.skv_decode_step(None, 1, 1, 1, None) == skv.SKV_ERR_INVALID_ARG
+    assert lib.skv_decode_step_noalloc(None, 1, 1, 1, None) == skv.SKV_ERR_INVALID_ARG
     assert lib.skv_append_token(None, 1, 1, None) == skv.SKV_ERR_INVALID_ARG
     assert lib.skv_get_stats(None, ctypes.byref(skv.SkvStats())) == skv.SKV_ERR_INVALID_ARG
     assert lib.skv_reset_temporal_cache(None) == skv.SKV_ERR_INVALID_ARG
     assert lib.skv_export_state(None, ctypes.byref(skv.SkvStateHost())) == skv.SKV_ERR_INVALID_ARG
     assert lib.skv_set_timing(None, 4) == skv.SKV_ERR_INVALID_ARG
     lib.skv_destroy(None)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SKV_NOALLOC_SCRATCH_BYTES \((\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == skv.SKV_NOALLOC_SCRATCH_BYTES
 
 
 def test_host_pointer_rejected_without_device_memory():
