@@ -306,6 +306,9 @@ def main():
                     help="storage of the rows of A: bf16 (the pages' precision) or FP8 E5M2")
     ap.add_argument("--b-format", choices=["bf16", "e5m2"], default="bf16",
                     help="storage of B (Psi^T): bf16 (the pages' precision) or FP8 E5M2")
+    ap.add_argument("--rebuild", choices=["auto", "fused", "separate"], default="auto",
+                    help="missed chunks rebuilt and attended in one launch with the rest of the attention "
+                         "(fused; auto with values in HBM) or rebuilt by their own launch before it (separate)")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
                     help="replay each timed step (all layers) as one captured HIP graph; off: launch eagerly")
     ap.add_argument("--phase-steps", type=int, default=16,
@@ -380,10 +383,12 @@ def main():
             v = vh
         torch.cuda.synchronize()
         tb = time.perf_counter()
+        rb = skv.REBUILD_MODES[args.rebuild]
         if new_mode is None:
-            layers.append(skv.Layer(shape, k_pre, v, placement))
+            layers.append(skv.Layer(shape, k_pre, v, placement, rebuild_mode=rb))
         else:
-            layers.append(skv.Layer(shape, k_pre, v, placement, max_new_tokens=total, new_token_mode=new_mode))
+            layers.append(skv.Layer(shape, k_pre, v, placement, max_new_tokens=total, new_token_mode=new_mode,
+                                    rebuild_mode=rb))
         torch.cuda.synchronize()
         build_s.append(time.perf_counter() - tb)
         if new_mode is not None:
@@ -538,6 +543,7 @@ def main():
         "phase_timing": f"HIP events around each phase on the decode stream, layers {sampled}, {PH} eager steps "
                         f"after the timed region",
         "launch": "one captured HIP graph per step (all layers), replayed" if graph is not None else "eager launches",
+        "rebuild": "fused" if (args.rebuild == "fused" or (args.rebuild == "auto" and not host)) else "separate",
         "layer_us": round(layer_us, 2),
         "build_ms_per_layer": {"mean": round(1000.0 * sum(build_s[1:] or build_s) / len(build_s[1:] or build_s), 1),
                                "first": round(1000.0 * build_s[0], 1),

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SKV_ABI_VERSION 7
+#define SKV_ABI_VERSION 8
 
 typedef int32_t skv_status;
 #define SKV_OK 0
@@ -94,6 +94,27 @@ typedef int32_t skv_status;
                                   window, then its chunk becomes a candidate that is
                                   reconstructed as RoPE(a' Psi^T) when selected      */
 
+/* How a decode step meets the chunks that missed the temporal cache (the summary's
+ * "Sparse KV Reconstruction and Overlapping Strategy", section 3.4: the key
+ * reconstruction of the selected chunks overlapped with the rest of the step). */
+#define SKV_REBUILD_AUTO 0     /* FUSED with values in HBM, SEPARATE with host values  */
+#define SKV_REBUILD_FUSED 1    /* one launch: each tile of missed chunks is rebuilt and
+                                  attended from on-chip memory by one workgroup (and
+                                  stored to the key slots for later hits, with the
+                                  temporal cache on), while the other workgroups of
+                                  the launch attend to the outliers, the slots that
+                                  hit and the window; values in HBM only            */
+#define SKV_REBUILD_SEPARATE 2 /* a rebuild launch refreshes the missed key slots, then
+                                  an attention launch reads every slot               */
+
+/* How the top-K of the chunk scores is found (the same chunks either way). */
+#define SKV_SELECT_AUTO 0      /* two levels where they fit: the largest score of every
+                                  16-chunk tile first (from per-tile maxima of the
+                                  logits), the K-th largest of those as a threshold,
+                                  then the top-K among the chunks of the tiles that
+                                  reach it; a full pass otherwise                    */
+#define SKV_SELECT_FULL 1      /* a pass over every candidate's score                */
+
 /*
  * Shape and budget of one layer.
  *   head_dim must be 128.  seq_len % chunk == 0, chunk in {4, 8, 16},
@@ -102,8 +123,9 @@ typedef int32_t skv_status;
  *   n_cand = seq_len/chunk - n_outlier - window/chunk, 1 <= top_k <= n_cand, top_k <= 4096.
  *   max_new_tokens >= 0 is the capacity for appended tokens (skv_append_token);
  *   new_token_mode is SKV_NEW_EXACT or SKV_NEW_LOWRANK; landmark_format, a_format
- *   and b_format are SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2.  An unknown enum value
- *   gives SKV_ERR_INVALID_ARG.
+ *   and b_format are SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2; rebuild_mode is one of
+ *   the SKV_REBUILD_* values, select_mode one of the SKV_SELECT_* values.  An unknown
+ *   enum value gives SKV_ERR_INVALID_ARG.
  */
 typedef struct skv_config {
   int32_t batch;           /* b                                                   */
@@ -126,6 +148,9 @@ typedef struct skv_config {
   int32_t a_format;        /* SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2 (rows of A,
                               also those appended in SKV_NEW_LOWRANK mode)        */
   int32_t b_format;        /* SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2 (B = Psi^T)   */
+  int32_t rebuild_mode;    /* SKV_REBUILD_AUTO, _FUSED or _SEPARATE; FUSED with
+                              SKV_VALUES_HOST gives SKV_ERR_UNSUPPORTED             */
+  int32_t select_mode;     /* SKV_SELECT_AUTO or SKV_SELECT_FULL                   */
 } skv_config;
 
 typedef struct skv_layer skv_layer;   /* opaque; owns all derived state */
@@ -288,9 +313,13 @@ skv_status skv_export_state(const skv_layer* h, const skv_state_host* dst);
  */
 #define SKV_PHASE_SCORE 0         /* landmark GEMV: logits + per-head LSE partials */
 #define SKV_PHASE_SELECT 1        /* LSE, chunk scores, top-K, index scan          */
-#define SKV_PHASE_REBUILD 2       /* key rebuild + RoPE of the missed chunks       */
+#define SKV_PHASE_REBUILD 2       /* key rebuild + RoPE of the missed chunks; with
+                                     the fused rebuild, the whole fused launch
+                                     (rebuild and attention of the misses, and
+                                     the attention over everything else)          */
 #define SKV_PHASE_VALUE_GATHER 3  /* host-value gather (side stream, overlapped)   */
-#define SKV_PHASE_ATTENTION 4     /* split-K attention + merge of the splits       */
+#define SKV_PHASE_ATTENTION 4     /* split-K attention + merge of the partials; with
+                                     the fused rebuild, the merge alone           */
 #define SKV_NUM_PHASES 5
 skv_status skv_set_timing(skv_layer* h, int32_t capacity);
 

@@ -56,23 +56,26 @@ hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Score epilogue, shared by both landmark formats: one 16-landmark tile's MFMA
 // output (lane (head col, kq) holds landmarks cb .. cb+3 of head col) scaled to
-// logits, stored, and folded into the lane's running (max, sum) of exp.
+// logits, stored, folded into the lane's running (max, sum) of exp, and the
+// tile's largest logit of each head stored for the two-level selection (tile
+// (cb - 4kq) / 16 of the pair; a tile past the candidates writes nothing).
+// Called by every lane of the wave.
 template <int G>
-__device__ __forceinline__ void score_tile_out(const DecodeArgs& a, float* lg, int col, int cb, int c1, f32x4 acc,
-                                               float& m_run, float& s_run) {
-  if (col < G && cb < c1) {
-    float v[4];
+__device__ __forceinline__ void score_tile_out(const DecodeArgs& a, float* lg, float* tmax, int col, int kq, int cb,
+                                               int c1, f32x4 acc, float& m_run, float& s_run) {
+  float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) v[i] = acc[i] * a.scale;
+  for (int i = 0; i < 4; i++) v[i] = acc[i] * a.scale;
+  float mx = kNegBig;
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    if (cb + i < c1) mx = fmaxf(mx, v[i]);
+  if (col < G && cb < c1) {
     if (cb + 4 <= c1) {
       *reinterpret_cast<f32x4*>(lg + cb) = (f32x4){v[0], v[1], v[2], v[3]};
     } else {
       for (int i = 0; i < 4 && cb + i < c1; i++) lg[cb + i] = v[i];
     }
-    float mx = v[0];
-#pragma unroll
-    for (int i = 1; i < 4; i++)
-      if (cb + i < c1) mx = fmaxf(mx, v[i]);
     const float mn = fmaxf(m_run, mx);
     float add = 0.f;
 #pragma unroll
@@ -81,6 +84,11 @@ __device__ __forceinline__ void score_tile_out(const DecodeArgs& a, float* lg, i
     s_run = s_run * __expf(m_run - mn) + add;
     m_run = mn;
   }
+  // the tile's maximum of head col: lanes col, col + 16, col + 32, col + 48
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const int tb = cb - 4 * kq;   // first candidate of the tile
+  if (kq == 0 && col < G && tb < c1) tmax[(tb >> 4) * G + col] = mx;
 }
 
 // The workgroup's per-head (max, sum) partial from its 16 lanes per head.
@@ -151,6 +159,7 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   float* lg = a.logits + ((int64_t)p * G + (col < G ? col : 0)) * a.ncp;
+  float* tmax = a.tile_max + (int64_t)p * a.n_ctiles * G;
   float m_run = kNegBig, s_run = 0.f;
   constexpr int kTiles = kScoreRows / 64;   // 16-row tiles per wave
 #pragma unroll
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
       const u32x4 av = stage[row * 16 + ((j * 4 + kq) ^ (row & 15))];
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bq[j], acc, 0, 0, 0);
     }
-    score_tile_out<G>(a, lg, col, c0 + w * (kScoreRows / 4) + t * 16 + kq * 4, c1, acc, m_run, s_run);
+    score_tile_out<G>(a, lg, tmax, col, kq, c0 + w * (kScoreRows / 4) + t * 16 + kq * 4, c1, acc, m_run, s_run);
   }
   score_lse_out<G>(a, p, blk, w, col, kq, m_run, s_run, red);
 }
@@ -211,6 +220,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(DecodeArgs a) {
     for (int k = 0; k < 8; k++) bq[j][k] = (_Float16)x[k];
   }
   float* lg = a.logits + ((int64_t)p * G + (col < G ? col : 0)) * a.ncp;
+  float* tmax = a.tile_max + (int64_t)p * a.n_ctiles * G;
   float m_run = kNegBig, s_run = 0.f;
 #pragma unroll
   for (int t = 0; t < kTiles; t++) {
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(DecodeArgs a) {
       const u32x4 av = e5m2x8_to_f16x8(half[(j % 2) * 2], half[(j % 2) * 2 + 1]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), bq[j], acc, 0, 0, 0);
     }
-    score_tile_out<G>(a, lg, col, c0 + w * (kScoreRows8 / 4) + t * 16 + kq * 4, c1, acc, m_run, s_run);
+    score_tile_out<G>(a, lg, tmax, col, kq, c0 + w * (kScoreRows8 / 4) + t * 16 + kq * 4, c1, acc, m_run, s_run);
   }
   score_lse_out<G>(a, p, blk, w, col, kq, m_run, s_run, red);
 }
@@ -342,7 +352,7 @@ __device__ __forceinline__ void pair_lse(const DecodeArgs& a, int p, float* lse)
 
 // Index scan of pair p against the chunks its slots hold, given the selection
 // sel[0, K) (ascending candidate indices): chunk ids out, hits / misses, slot
-// reassignment, miss list, counters.
+// reassignment, miss list, list of the slots that hit, counters.
 __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* selch, int* freel, int* missp,
                            int* scl, uint32_t* resl) {
   const int K = a.top_k, RW = a.res_words;
@@ -370,6 +380,8 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
     const int ex = block_exclusive_scan<kSelThreads>(fr | (ms << 16), sh, &tot);
     if (fr) freel[n_free + (ex & 0xffff)] = s;
     if (ms) missp[n_miss + (ex >> 16)] = s;
+    // a slot that keeps its chunk is a hit: listed in ascending slot order
+    if (s < K && !fr) a.hit_slot[(int64_t)p * K + s - n_free - (ex & 0xffff)] = s;
     n_free += tot & 0xffff;
     n_miss += tot >> 16;
   }
@@ -494,7 +506,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
   });
   block_range<kSelThreads>(lo, hi, sh);
   const int i0 = threadIdx.x * PT;
-  block_topk_reg<kSelThreads, PT>(key, nv, K, lo, hi, hist, sh, true,
+  block_topk_reg<kSelThreads, PT>(key, prefix_mask(nv), K, lo, hi, hist, sh, true,
                                   [&](int pos, int e) { sel[pos] = i0 + e; });
   index_scan(a, p, sh, sel, selch, freel, missp, scl, resl);
 }
@@ -514,7 +526,7 @@ __global__ __launch_bounds__(kSelThreads) void part_topk_kernel(DecodeArgs a) {
   uint32_t* ok = a.part_keys + ((int64_t)p * a.n_part + part) * K;
   int32_t* oi = a.part_idx + ((int64_t)p * a.n_part + part) * K;
   const int ci = c0 + threadIdx.x * PT;
-  block_topk_reg<kSelThreads, PT>(key, nv, min(K, n), lo, hi, hist, sh, true, [&](int pos, int e) {
+  block_topk_reg<kSelThreads, PT>(key, prefix_mask(nv), min(K, n), lo, hi, hist, sh, true, [&](int pos, int e) {
     ok[pos] = key[e];
     oi[pos] = ci + e;
   });
@@ -593,7 +605,7 @@ __global__ __launch_bounds__(kSelThreads) void merge_level_kernel(DecodeArgs a, 
   block_range<kSelThreads>(lo, hi, sh);   // its barriers also publish the cleared histogram
   uint32_t* ok = out_keys + (int64_t)p * out_stride + (int64_t)gi * K;
   int32_t* oi = out_idx + (int64_t)p * out_stride + (int64_t)gi * K;
-  block_topk_reg<kSelThreads, PT>(key, nv, min(K, n), lo, hi, hist, sh, true, [&](int pos, int e) {
+  block_topk_reg<kSelThreads, PT>(key, prefix_mask(nv), min(K, n), lo, hi, hist, sh, true, [&](int pos, int e) {
     ok[pos] = key[e];
     oi[pos] = idx[e];
   });
@@ -623,7 +635,7 @@ __global__ __launch_bounds__(kSelThreads) void merged_select_kernel(DecodeArgs a
   for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
   for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
   block_range<kSelThreads>(lo, hi, sh);   // its barriers also publish the cleared histogram
-  block_topk_reg<kSelThreads, PT>(key, nv, K, lo, hi, hist, sh, true, [&](int pos, int e) { sel[pos] = idx[e]; });
+  block_topk_reg<kSelThreads, PT>(key, prefix_mask(nv), K, lo, hi, hist, sh, true, [&](int pos, int e) { sel[pos] = idx[e]; });
   index_scan(a, p, sh, sel, selch, freel, missp, scl, resl);
 }
 
@@ -631,6 +643,240 @@ template <class F>
 static hipError_t allow_lds(F* kernel) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                              kSelLdsMax);
+}
+
+// ---------------------------------------------------------------------------
+// Two-level selection, one workgroup per pair.  The key of a 16-candidate tile
+// is the largest key in it, and it follows from the score kernel's per-tile
+// maxima of each head's logits: max_g(M_g - LSE_g) is the same fp32 arithmetic
+// as each candidate's max_g(l_g - LSE_g) applied to the tile's largest logits,
+// and every later step (- 1, the order-preserving map) is monotone.
+//  1. beta = the K-th largest tile key.  K tiles each hold a candidate whose key
+//     is >= beta, so the pair's K-th largest key is >= beta: every selected
+//     candidate has key >= beta and lies in a tile whose key is >= beta ("hot").
+//  2. The candidates of the hot tiles (4 per item, items in ascending candidate
+//     order) form the keys; those below beta are left out, which changes
+//     nothing, since every candidate left out is smaller than every selected one
+//     (ties included).  The top-K among them is the pair's top-K, with ties to
+//     the lower candidate index as over all candidates.
+// With K above the tile count every tile is hot and no key is left out.  The
+// tile maxima of a pair are about 1/16 of its logits and the hot tiles' logits
+// about K/n_tiles of them, so the selection reads a small fraction of what a
+// full pass over the logits reads (at the Llama-3.1-8B shape 15 KB + 61 KB of
+// 245 KB per pair; about 400 keys pass beta).  If the hot tiles outnumber the
+// register budget (IPT items of 4 candidates per thread; only with many equal
+// tile keys), the second level runs over them from memory instead.
+// LDS layout (ints): hist[2048 + kTopkSmall] | sh[32] | sel[K] | selch[K] |
+// freel[K] | missp[K] | scl[K] | resl[res_words] | hot tile list[n_ctiles].
+
+// key of candidate c (< n_cand) of pair p from its G logits
+template <int G>
+__device__ __forceinline__ uint32_t cand_key(const DecodeArgs& a, int p, int c, const float* lse) {
+  const float* lg = a.logits + (int64_t)p * G * a.ncp + c;
+  float best = lg[0] - lse[0];
+#pragma unroll
+  for (int g = 1; g < G; g++) best = fmaxf(best, lg[(int64_t)g * a.ncp] - lse[g]);
+  return float_key(best - 1.0f);
+}
+
+template <int G, int TPT, int IPT>
+__global__ __launch_bounds__(kSelThreads) void select2_kernel(DecodeArgs a) {
+  extern __shared__ int smem[];
+  const int K = a.top_k, RW = a.res_words, NT = a.n_ctiles, n = a.n_cand;
+  int* hist = smem;
+  int* sh = smem + kHist;
+  int* sel = sh + 32;        // selected candidate indices, ascending
+  int* selch = sel + K;      // their chunk ids
+  int* freel = selch + K;    // evicted slots, ascending
+  int* missp = freel + K;    // positions in sel of the missed chunks, ascending
+  int* scl = missp + K;      // slot -> candidate index (copy of the pair's slot map)
+  uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);   // resident bitmap copy
+  int* hot = reinterpret_cast<int*>(resl + RW);            // hot tiles, ascending
+  __shared__ float lse[16];
+  const int p = blockIdx.x;
+  // ---- level 1: tile keys of tiles [t*TPT, t*TPT + TPT); their maxima are
+  // loaded before the LSE is reduced when they fit in 32 registers, else after
+  const int t0 = threadIdx.x * TPT;
+  const int ntv = max(0, min(TPT, NT - t0));   // this thread's tiles
+  const float* tm = a.tile_max + (int64_t)p * NT * G;
+  constexpr bool kPrefetch = TPT * G <= 32;
+  float mg[kPrefetch ? TPT : 1][G];
+  auto load_tile = [&](int e, float (&m)[G]) {
+    const int tile = min(t0 + e, NT - 1);   // past the tiles: re-read the last, not counted
+    if constexpr (G % 4 == 0) {
+#pragma unroll
+      for (int g = 0; g < G; g += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(tm + (int64_t)tile * G + g);
+#pragma unroll
+        for (int j = 0; j < 4; j++) m[g + j] = v[j];
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; g++) m[g] = tm[(int64_t)tile * G + g];
+    }
+  };
+  if constexpr (kPrefetch) {
+#pragma unroll
+    for (int e = 0; e < TPT; e++) load_tile(e, mg[e]);
+  }
+  {
+    const int32_t* sc = a.slot_cand + (int64_t)p * K;
+    const uint32_t* res = a.resident + (int64_t)p * RW;
+    for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
+    for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
+  }
+  for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
+  pair_lse<G>(a, p, lse);
+  __syncthreads();
+  uint32_t tk[TPT];
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int e = 0; e < TPT; e++) {
+    float m1[G];
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int g = 0; g < G; g++) m1[g] = mg[e][g];
+    } else {
+      load_tile(e, m1);
+    }
+    float best = m1[0] - lse[0];
+#pragma unroll
+    for (int g = 1; g < G; g++) best = fmaxf(best, m1[g] - lse[g]);
+    tk[e] = float_key(best - 1.0f);
+    if (e < ntv) {
+      lo = min(lo, tk[e]);
+      hi = max(hi, tk[e]);
+    }
+  }
+  block_range<kSelThreads>(lo, hi, sh);
+  uint32_t beta = 0u;   // every key passes when K exceeds the tile count
+  if (K <= NT) {
+    int kk;
+    beta = block_kth_reg<kSelThreads, TPT>(tk, prefix_mask(ntv), K, lo, hi, hist, sh, true, &kk);
+  }
+  // hot tiles, compacted in ascending order
+  int nh = 0;
+#pragma unroll
+  for (int e = 0; e < TPT; e++) nh += (e < ntv && tk[e] >= beta);
+  int n_hot;
+  int off = block_exclusive_scan<kSelThreads>(nh, sh, &n_hot);
+#pragma unroll
+  for (int e = 0; e < TPT; e++)
+    if (e < ntv && tk[e] >= beta) hot[off++] = t0 + e;
+  for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  // ---- level 2: the candidates of the hot tiles, items of 4 candidates
+  const int n_items = n_hot * 4;
+  if (n_items <= kSelThreads * IPT) {
+    const int i0 = threadIdx.x * IPT;
+    uint32_t key[IPT * 4];
+    uint64_t vmask = 0;
+#pragma unroll
+    for (int it = 0; it < IPT; it++) {
+      const int item = min(i0 + it, n_items - 1);
+      const int cb = hot[item >> 2] * 16 + (item & 3) * 4;
+      const int cl = min(cb, a.ncp - 4);     // past the candidates: re-read the last row's end, not counted
+      // the G heads in groups of (at most) 4 loads
+      constexpr int GB = G < 4 ? G : 4;
+      float best[4];
+#pragma unroll
+      for (int g0 = 0; g0 < G; g0 += GB) {
+        f32x4 lv[GB];
+#pragma unroll
+        for (int g = 0; g < GB; g++)
+          lv[g] = *reinterpret_cast<const f32x4*>(a.logits + ((int64_t)p * G + g0 + g) * a.ncp + cl);
+#pragma unroll
+        for (int g = 0; g < GB; g++)
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            const float v = lv[g][c] - lse[g0 + g];
+            best[c] = (g0 + g == 0) ? v : fmaxf(best[c], v);
+          }
+      }
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const uint32_t kv = float_key(best[c] - 1.0f);
+        key[it * 4 + c] = kv;
+        if (i0 + it < n_items && cb + c < n && kv >= beta) vmask |= 1ull << (it * 4 + c);
+      }
+    }
+    lo = 0xffffffffu;
+    hi = 0u;
+#pragma unroll
+    for (int e = 0; e < IPT * 4; e++) {
+      if ((vmask >> e) & 1) {
+        lo = min(lo, key[e]);
+        hi = max(hi, key[e]);
+      }
+    }
+    block_range<kSelThreads>(lo, hi, sh);
+    block_topk_reg<kSelThreads, IPT * 4>(key, vmask, K, lo, hi, hist, sh, true, [&](int pos, int e) {
+      const int item = i0 + e / 4;
+      sel[pos] = hot[item >> 2] * 16 + (item & 3) * 4 + (e & 3);
+    });
+  } else {
+    // many equal tile keys: the hot tiles' candidates from memory (candidates
+    // past n_cand get key 0, below every real key, and are never taken)
+    const int m = n_hot * 16;
+    block_topk<kSelThreads>(
+        [&](int i) {
+          const int c = hot[i >> 4] * 16 + (i & 15);
+          return c < n ? cand_key<G>(a, p, c, lse) : 0u;
+        },
+        m, K, hist, sh, [&](int pos, int i) { sel[pos] = hot[i >> 4] * 16 + (i & 15); });
+  }
+  index_scan(a, p, sh, sel, selch, freel, missp, scl, resl);
+}
+
+static size_t select2_lds_bytes(const DecodeArgs& a) {
+  return (size_t)(kHist + 32 + 5 * a.top_k + a.res_words + a.n_ctiles_cap) * sizeof(int);
+}
+
+// Tiles and level-2 items per thread of the two-level selection, or 0 when it
+// does not apply (more than 16K tiles per pair, or its LDS would not fit).
+int select2_shape(int n_ctiles_cap, int top_k, int res_words, int* tpt, int* ipt) {
+  const int t = (n_ctiles_cap + kSelThreads - 1) / kSelThreads;
+  if (t > 16) return 0;
+  if ((size_t)(kHist + 32 + 5 * top_k + res_words + n_ctiles_cap) * sizeof(int) > (size_t)kSelLdsMax) return 0;
+  *tpt = t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 16;
+  // hot tiles are about K (more only on equal tile keys): room for 1.25 K, at
+  // most 8 items (32 keys) per thread, past which the registers spill
+  const int need = (5 * top_k + kSelThreads - 1) / kSelThreads;   // 4 items per tile
+  *ipt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+  return 1;
+}
+
+template <int G, int TPT, int IPT>
+static hipError_t launch_select2_i(const DecodeArgs& a, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = allow_lds(&select2_kernel<G, TPT, IPT>);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  select2_kernel<G, TPT, IPT><<<a.batch * a.n_kv, kSelThreads, select2_lds_bytes(a), st>>>(a);
+  return hipGetLastError();
+}
+
+template <int G, int TPT>
+static hipError_t launch_select2_t(const DecodeArgs& a, hipStream_t st) {
+  switch (a.sel_ipt) {
+    case 1: return launch_select2_i<G, TPT, 1>(a, st);
+    case 2: return launch_select2_i<G, TPT, 2>(a, st);
+    case 4: return launch_select2_i<G, TPT, 4>(a, st);
+    default: return launch_select2_i<G, TPT, 8>(a, st);
+  }
+}
+
+template <int G>
+static hipError_t launch_select2_g(const DecodeArgs& a, hipStream_t st) {
+  switch (a.sel_tpt) {
+    case 1: return launch_select2_t<G, 1>(a, st);
+    case 2: return launch_select2_t<G, 2>(a, st);
+    case 4: return launch_select2_t<G, 4>(a, st);
+    case 8: return launch_select2_t<G, 8>(a, st);
+    default: return launch_select2_t<G, 16>(a, st);
+  }
 }
 
 template <int G, int PT>
@@ -682,6 +928,16 @@ static hipError_t launch_select_g(const DecodeArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
+  if (a.sel_two_level) {
+    switch (a.group) {
+      case 1: return launch_select2_g<1>(a, st);
+      case 2: return launch_select2_g<2>(a, st);
+      case 4: return launch_select2_g<4>(a, st);
+      case 8: return launch_select2_g<8>(a, st);
+      case 16: return launch_select2_g<16>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.group) {
     case 1: return launch_select_g<1>(a, st);
     case 2: return launch_select_g<2>(a, st);
@@ -699,7 +955,6 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st) {
 // fragment loads), all groups issued up front; the MFMAs of step q start as soon
 // as groups 0..q have landed, while the later groups are still in flight.
 
-constexpr int kRebuildRows = 128;
 constexpr int kMaxSteps = 5;                  // k-steps per staged slice (160 k)
 constexpr int kOutW = kHeadDim + 8;           // staged output row pitch (bf16)
 constexpr int kStepPieces = kRebuildRows * 4; // 16-byte pieces of B^T per k-step
@@ -808,21 +1063,20 @@ constexpr int rebuild_stage_bytes() {
 }
 
 // One tile of kRebuildRows rows of pair p: the keys of the missed chunks
-// mchunk[0, 128/C) (-1: none), rotated, stored as bf16 into their slots mslot[].
-// Called by all 256 threads of a workgroup with mchunk / mslot in LDS (written
-// before a barrier) and `stage` an LDS buffer of rebuild_stage_bytes<NSTEP>().
-// Returns once the stores are issued; the caller orders them against later
-// readers.
+// mchunk[0, 128/C) (-1: none), rotated and rounded to bf16, left in `stage` as
+// rows of kOutW bf16 (row m = token m % C of miss m / C); store_tile writes them
+// into their slots.  Called by all 256 threads of a workgroup with mchunk in LDS
+// (written before a barrier) and `stage` an LDS buffer of
+// rebuild_stage_bytes<NSTEP>(); returns after a barrier, with the rows in place.
 // A8: rows of A stored as FP8 E5M2 (r bytes per row) instead of bf16.  B8: B^T
 // stored as FP8 E5M2; its operand fragments (8 bytes per lane and column tile,
 // 20 KB per pair at r = 160, read by every wave from L2) are then loaded straight
 // into registers and widened to bf16, with one k-step per iteration, instead of
 // the staged direct-to-LDS slices of the bf16 path.
 template <int C, int NSTEP, bool A8, bool B8>
-__device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const int* mchunk, const int* mslot,
-                                             u32x4* stage) {
+__device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const int* mchunk, u32x4* stage) {
   const int b = p / a.n_kv, h = p % a.n_kv;
-  const int K = a.top_k, r = a.rank;
+  const int r = a.rank;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lk = lane >> 4;
   double ffreq[4];
@@ -943,11 +1197,18 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
     }
   }
   __syncthreads();
+}
+
+// The rebuilt rows of a tile (in LDS, as rebuild_tile left them) into the key
+// slots mslot[] of their chunks (-1: none).  The caller orders the stores against
+// later readers.
+template <int C>
+__device__ __forceinline__ void store_tile(const DecodeArgs& a, int p, const int* mslot, const uint16_t* otile) {
   for (int e = threadIdx.x; e < kRebuildRows * 16; e += 256) {
     const int m = e >> 4, piece = e & 15;
     const int slot = mslot[m / C];
     if (slot < 0) continue;
-    uint16_t* dst = a.key_slots + (((int64_t)p * K + slot) * C + (m % C)) * kHeadDim + piece * 8;
+    uint16_t* dst = a.key_slots + (((int64_t)p * a.top_k + slot) * C + (m % C)) * kHeadDim + piece * 8;
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&otile[m * kOutW + piece * 8]);
   }
 }
@@ -974,7 +1235,8 @@ __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
-  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, mslot, stage);
+  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage);
+  store_tile<C>(a, p, mslot, reinterpret_cast<const uint16_t*>(stage));
 }
 
 template <int C, bool A8>
@@ -1196,11 +1458,12 @@ hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Split-K flash-decode.  Work unit = one chunk of C tokens: unit u < O is an
-// outlier chunk, O <= u < O+K the chunk held by slot u-O, the rest the window
-// and the appended tokens.  One workgroup per (pair, split) serves all G <= 16
-// query heads of its KV head, so every key and value is read once.  Each wave
-// owns up to NT*16 consecutive tokens (NT tiles of 16) and issues all of their
-// K/V loads before computing.  Per tile, both products run on MFMA:
+// outlier chunk, the next ns units are selected chunks held in key slots, the
+// rest the window and the appended tokens.  One workgroup per (pair, split)
+// serves all G <= 16 query heads of its KV head, so every key and value is read
+// once.  Each wave owns up to NT*16 consecutive tokens (NT tiles of 16) and
+// issues all of their K/V loads before computing.  Per tile, both products run
+// on MFMA:
 //  * S = K q^T (16x16x32 bf16): lane (row r, kq) feeds dims j*32+kq*8.. of token
 //    r; the output lane (head n = lane%16, kq) holds tokens 4kq..4kq+3.
 //  * softmax in that layout, base 2: one running max and sum per head.
@@ -1209,7 +1472,19 @@ hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st) {
 //    in as bf16 hi + lo parts, which keeps 16 bits of every weight.  The A
 //    operand (four tokens of one dim per lane) comes from the value loads by a
 //    4x4 dword transpose within each lane quad and one byte permute.
-// The four waves of a workgroup merge through LDS into one split partial.
+// The four waves of a workgroup merge through LDS into one partial (m, l, o).
+//
+// Two ways to meet the missed chunks (rebuild_fused):
+//  * separate: rebuild_kernel refreshes the missed slots first, then every slot
+//    is an attention unit (ns = K);
+//  * fused (the summary's reconstruction overlapped with the fetch, section 3.4
+//    "Sparse KV Reconstruction and Overlapping Strategy", as one launch): the
+//    workgroup that rebuilds a tile of missed chunks attends to those keys
+//    straight from LDS (and stores them to their slots for later hits), while
+//    the attention workgroups of the same launch take the outliers, the slots
+//    that hit (ns = K - misses, listed by the selection) and the exact region.
+//    One partial per split and one per tile of misses; combine_kernel merges
+//    the ones that hold tokens.
 
 // 16-token tiles per wave.  Two measured fastest (17.6 us per launch at
 // b = 8, S = 122 880, G = 4 against 17.9 with three and 20.6 with four; at
@@ -1221,24 +1496,32 @@ constexpr int kAttnMaxHeads = 16;   // query heads per KV head (the MFMA's N)
 
 int attn_units_per_wave(int chunk) { return kAttnTiles * 16 / chunk; }
 
+// Selected-chunk units of pair p: every slot (separate rebuild), or the slots
+// that hit (fused rebuild: the misses are attended where they are rebuilt).
+__device__ __forceinline__ int slot_units(const DecodeArgs& a, int p) {
+  return a.rebuild_fused ? a.top_k - a.n_miss[p] : a.top_k;
+}
+
+// Key / value rows of unit u of pair p; ns selected-chunk units, `slot` and `ch`
+// the slot and chunk id of u when it is one of them.
 template <int C>
-__device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, int u) {
+__device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, int u, int ns, int slot) {
   const int O = a.n_outlier, K = a.top_k, Wu = a.n_win_units;
   if (u < O) return a.k_out + ((int64_t)p * O + u) * C * kHeadDim;
-  if (u < O + K) return a.key_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim;
-  const int x = u - O - K + a.n_fold;
+  if (u < O + ns) return a.key_slots + ((int64_t)p * K + slot) * C * kHeadDim;
+  const int x = u - O - ns + a.n_fold;
   if (x < Wu) return a.k_win + ((int64_t)p * Wu + x) * C * kHeadDim;
   return a.key_new + ((int64_t)p * a.max_new + (int64_t)(x - Wu) * C) * kHeadDim;
 }
 
 template <int C>
-__device__ __forceinline__ const uint16_t* unit_value(const DecodeArgs& a, int p, int b, int h, int u,
-                                                      int ch) {
+__device__ __forceinline__ const uint16_t* unit_value(const DecodeArgs& a, int p, int b, int h, int u, int ns,
+                                                      int slot, int ch) {
   const int O = a.n_outlier, K = a.top_k;
   if (u < O) return a.v_out + ((int64_t)p * O + u) * C * kHeadDim;
-  if (u < O + K)
-    return a.host_values ? a.val_slots + ((int64_t)p * K + (u - O)) * C * kHeadDim : chunk_values(a, p, b, h, ch);
-  const int Wu = a.n_win_units, x = u - O - K + a.n_fold;
+  if (u < O + ns)
+    return a.host_values ? a.val_slots + ((int64_t)p * K + slot) * C * kHeadDim : chunk_values(a, p, b, h, ch);
+  const int Wu = a.n_win_units, x = u - O - ns + a.n_fold;
   if (x < Wu) return a.v_win + ((int64_t)p * Wu + x) * C * kHeadDim;
   return a.val_new + ((int64_t)p * a.max_new + (int64_t)(x - Wu) * C) * kHeadDim;
 }
@@ -1265,80 +1548,37 @@ __device__ __forceinline__ u32x4 quad_transpose(u32x4 x, int lane) {
   return x;
 }
 
-template <int NT, int C>
-__global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
-  typedef short bf16x4 __attribute__((ext_vector_type(4)));
-  constexpr uint32_t kLoHalves = 0x05040100u, kHiHalves = 0x07060302u;   // v_perm selectors
-  __shared__ __attribute__((aligned(16))) float wo[4][kAttnMaxHeads][kHeadDim];
-  __shared__ float wm[4][kAttnMaxHeads], wl[4][kAttnMaxHeads];
-  // pairs fastest: workgroups go to the 8 XCDs round-robin by linear id, so each
-  // XCD gets whole pairs (all splits of pairs p = x mod 8) and equal work even
-  // when the last split of a pair is short
-  const int p = blockIdx.x, split = blockIdx.y;
-  const int b = p / a.n_kv, h = p % a.n_kv;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int lr = lane & 15, lq = lane >> 4;   // (row|head|dim, kq)
-  const int O = a.n_outlier, K = a.top_k;
-  // units: [outliers; selected slots; exact region], the exact region being the
-  // window units and appended units not yet folded into the candidates (its
-  // last unit may be partly filled: tokens past it are masked like a wave's tail)
-  const int U = O + K + a.n_win_units + a.n_new_units - a.n_fold;
-  const int per_wave = (a.upw + 3) / 4;
-  const int uw0 = min(U, split * a.upw + w * per_wave);
-  const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
-  const int valid = (O + K + a.n_win_units - a.n_fold) * C + a.n_new_tokens;   // tokens in units [0, U)
-  const int ntok = max(0, min((uw1 - uw0) * C, valid - uw0 * C));
-  const int G = a.group, hq = a.n_kv * G, hq0 = h * G;   // first query head of the pair
-
-  // chunk id of each selected unit of the wave, one per lane
-  int my_ch = 0;
-  if (lane < uw1 - uw0) {
-    const int sidx = uw0 + lane - O;
-    if (sidx >= 0 && sidx < K) my_ch = max(a.slot_chunk[(int64_t)p * K + sidx], 0);
-  }
-  // q^T first (every tile needs it; vector-memory loads complete in issue order),
-  // MFMA B layout: head lr, dims j*32 + lq*8 (zero for heads >= G)
-  bf16x8 bq[4];
+// q^T of pair p in the MFMA B layout: head lr, dims j*32 + lq*8 (zero for heads >= G).
+__device__ __forceinline__ void load_q(const DecodeArgs& a, int p, int lr, int lq, bf16x8 (&bq)[4]) {
+  const int b = p / a.n_kv, h = p % a.n_kv, G = a.group;
+  const int64_t row = (int64_t)b * a.n_kv * G + h * G + lr;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
     u32x4 wq = {0u, 0u, 0u, 0u};
-    if (lr < G) wq = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * hq + hq0 + lr) * kHeadDim + j * 32 + lq * 8);
+    if (lr < G) wq = *reinterpret_cast<const u32x4*>(a.q + row * kHeadDim + j * 32 + lq * 8);
     bq[j] = __builtin_bit_cast(bf16x8, wq);
   }
-  // then tile by tile, keys then values, so that tile 0 can start as soon as its
-  // own 8 loads are in.  Keys in MFMA A layout: token tile*16 + lr, dims
-  // j*32 + lq*8.  Values: lane (lr = 4q + jj, lq) reads token tile*16 + 4lq + jj,
-  // dims c*32 + 8q .. +8 for c = 0..3; the quad transpose then leaves it dims
-  // c*32 + 2lr and c*32 + 2lr + 1 of tokens 4lq .. 4lq+3.
-  // The loads are unconditional (branch-free code keeps the compiler's per-tile
-  // wait counts exact): tokens past the wave's range re-read its last token,
-  // whose scores are masked to -inf below, so they weigh 0.  A wave with no
-  // tokens reads unit 0 of the pair and masks everything.
-  const int tlast = max(ntok - 1, 0), ub = ntok > 0 ? uw0 : 0;
-  int vch[NT];
-#pragma unroll
-  for (int t = 0; t < NT; t++) vch[t] = __shfl(my_ch, min(t * 16 + 4 * lq + (lr & 3), tlast) / C);
-  u32x4 kf[NT][4], vf[NT][4];
-#pragma unroll
-  for (int t = 0; t < NT; t++) {
-    const int tk = min(t * 16 + lr, tlast);
-    const uint16_t* kp = unit_key<C>(a, p, ub + tk / C) + (tk % C) * kHeadDim + lq * 8;
-#pragma unroll
-    for (int j = 0; j < 4; j++) kf[t][j] = *reinterpret_cast<const u32x4*>(kp + j * 32);
-    const int tv = min(t * 16 + 4 * lq + (lr & 3), tlast);
-    const uint16_t* vp = unit_value<C>(a, p, b, h, ub + tv / C, vch[t]) + (tv % C) * kHeadDim + (lr >> 2) * 8;
-#pragma unroll
-    for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
-  }
-  const float qscale = a.scale * kLog2e;
-  float m = kNegBig, l = 0.f;   // head lr
-  // o[c][e][i]: head lr, dim c*32 + 8lq + 2i + e
-  f32x4 o[4][2];
-#pragma unroll
-  for (int c = 0; c < 4; c++)
-#pragma unroll
-    for (int e = 0; e < 2; e++) o[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
 
+// Merge buffers of one workgroup's four waves (fp32 partial o per wave and head,
+// and the running max / sum).
+struct AttnMerge {
+  float wo[4][kAttnMaxHeads][kHeadDim];
+  float wm[4][kAttnMaxHeads], wl[4][kAttnMaxHeads];
+};
+
+// Online-softmax attention of one wave over NT tiles of 16 tokens, ntok of them
+// valid (the rest weigh 0): keys kf in the MFMA A layout (token t*16 + lr, dims
+// j*32 + lq*8), values vf as loaded (token t*16 + 4lq + lr%4, dims c*32 + 8(lr/4)).
+// Accumulates the running max m and sum l of head lr and o[c][e][i] = head lr,
+// dim c*32 + 8lq + 2i + e.
+template <int NT>
+__device__ __forceinline__ void wave_attend(const u32x4 (&kf)[NT][4], const u32x4 (&vf)[NT][4], const bf16x8 (&bq)[4],
+                                            int ntok, float qscale, int lane, float& m, float& l,
+                                            f32x4 (&o)[4][2]) {
+  typedef short bf16x4 __attribute__((ext_vector_type(4)));
+  constexpr uint32_t kLoHalves = 0x05040100u, kHiHalves = 0x07060302u;   // v_perm selectors
+  const int lq = (lane & 63) >> 4;
 #pragma unroll
   for (int t = 0; t < NT; t++) {
     if (t * 16 < ntok) {
@@ -1391,31 +1631,39 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
       }
     }
   }
+}
+
+// The four waves' (m, l, o) through LDS into one partial row per head at `part`
+// (G rows of kPartStride: o[d], m, l).  Called by all 256 threads; `mg` may alias
+// memory the waves have finished reading before the call.
+__device__ __forceinline__ void merge_waves(int G, int lane, float m, float l, const f32x4 (&o)[4][2],
+                                            AttnMerge& mg, float* part) {
+  const int w = threadIdx.x >> 6, lr = lane & 15, lq = lane >> 4;
+  __syncthreads();   // the waves are done with what `mg` may alias
   if (lr < G) {
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      float* dst = &wo[w][lr][c * 32 + 8 * lq];
+      float* dst = &mg.wo[w][lr][c * 32 + 8 * lq];
       *reinterpret_cast<f32x4*>(dst) = f32x4{o[c][0][0], o[c][1][0], o[c][0][1], o[c][1][1]};
       *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[c][0][2], o[c][1][2], o[c][0][3], o[c][1][3]};
     }
     if (lq == 0) {
-      wm[w][lr] = m;
-      wl[w][lr] = l;
+      mg.wm[w][lr] = m;
+      mg.wl[w][lr] = l;
     }
   }
   __syncthreads();
-  float* part = a.attn_part + ((int64_t)p * a.n_split + split) * G * kPartStride;
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += 256) {
     const int g = idx / kHeadDim, dim = idx % kHeadDim;
     float M = kNegBig;
 #pragma unroll
-    for (int ww = 0; ww < 4; ww++) M = fmaxf(M, wm[ww][g]);
+    for (int ww = 0; ww < 4; ww++) M = fmaxf(M, mg.wm[ww][g]);
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int ww = 0; ww < 4; ww++) {
-      const float c = __builtin_amdgcn_exp2f(wm[ww][g] - M);
-      num += wo[ww][g][dim] * c;
-      den += wl[ww][g] * c;
+      const float c = __builtin_amdgcn_exp2f(mg.wm[ww][g] - M);
+      num += mg.wo[ww][g][dim] * c;
+      den += mg.wl[ww][g] * c;
     }
     part[g * kPartStride + dim] = num;
     if (dim == 0) {
@@ -1425,34 +1673,118 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the split partials of one (pair, head):
-// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Attention workgroup (pair p, split): units [split*upw, split*upw + upw) of the
+// pair's [outliers; selected-chunk units; exact region] (the exact region being
+// the window units and appended units not yet folded into the candidates; its
+// last unit may be partly filled: tokens past it are masked like a wave's tail).
+// A split past the pair's units writes nothing (the merge skips it).
+template <int NT, int C>
+__device__ __forceinline__ void attend_split(const DecodeArgs& a, int p, int split, AttnMerge& mg) {
+  const int b = p / a.n_kv, h = p % a.n_kv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;   // (row|head|dim, kq)
+  const int O = a.n_outlier, K = a.top_k;
+  const int ns = slot_units(a, p);
+  const int U = O + ns + a.n_win_units + a.n_new_units - a.n_fold;
+  if (split * a.upw >= U) return;            // workgroup-uniform
+  const int per_wave = (a.upw + 3) / 4;
+  const int uw0 = min(U, split * a.upw + w * per_wave);
+  const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
+  const int valid = (O + ns + a.n_win_units - a.n_fold) * C + a.n_new_tokens;   // tokens in units [0, U)
+  const int ntok = max(0, min((uw1 - uw0) * C, valid - uw0 * C));
+
+  float m = kNegBig, l = 0.f;   // head lr
+  f32x4 o[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; c++)
+#pragma unroll
+    for (int e = 0; e < 2; e++) o[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (ntok > 0) {   // wave-uniform
+    // slot and chunk id of each selected-chunk unit of the wave, one per lane
+    int my_slot = 0, my_ch = 0;
+    if (lane < uw1 - uw0) {
+      const int sidx = uw0 + lane - O;
+      if (sidx >= 0 && sidx < ns) {
+        my_slot = a.rebuild_fused ? a.hit_slot[(int64_t)p * K + sidx] : sidx;
+        my_ch = max(a.slot_chunk[(int64_t)p * K + my_slot], 0);
+      }
+    }
+    // q first (every tile needs it; vector-memory loads complete in issue order),
+    // then tile by tile, keys then values, so that tile 0 can start as soon as its
+    // own loads are in.  Values: lane (lr = 4q + jj, lq) reads token tile*16 + 4lq
+    // + jj, dims c*32 + 8q .. +8 for c = 0..3; the quad transpose then leaves it
+    // dims c*32 + 2lr and c*32 + 2lr + 1 of tokens 4lq .. 4lq+3.  The loads are
+    // unconditional (branch-free code keeps the compiler's per-tile wait counts
+    // exact): tokens past the wave's range re-read its last token, whose scores
+    // are masked to -inf, so they weigh 0.
+    bf16x8 bq[4];
+    load_q(a, p, lr, lq, bq);
+    const int tlast = ntok - 1;
+    u32x4 kf[NT][4], vf[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      const int tk = min(t * 16 + lr, tlast);
+      const int ks = __shfl(my_slot, tk / C);
+      const uint16_t* kp = unit_key<C>(a, p, uw0 + tk / C, ns, ks) + (tk % C) * kHeadDim + lq * 8;
+#pragma unroll
+      for (int j = 0; j < 4; j++) kf[t][j] = *reinterpret_cast<const u32x4*>(kp + j * 32);
+      const int tv = min(t * 16 + 4 * lq + (lr & 3), tlast);
+      const int vs = __shfl(my_slot, tv / C), vc = __shfl(my_ch, tv / C);
+      const uint16_t* vp = unit_value<C>(a, p, b, h, uw0 + tv / C, ns, vs, vc) + (tv % C) * kHeadDim + (lr >> 2) * 8;
+#pragma unroll
+      for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
+    }
+    wave_attend<NT>(kf, vf, bq, ntok, a.scale * kLog2e, lane, m, l, o);
+  }
+  merge_waves(a.group, lane, m, l, o, mg, a.attn_part + ((int64_t)p * a.n_part_att + split) * a.group * kPartStride);
+}
+
+template <int NT, int C>
+__global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) AttnMerge mg;
+  // pairs fastest: workgroups go to the 8 XCDs round-robin by linear id, so each
+  // XCD gets whole pairs (all splits of pairs p = x mod 8) and equal work even
+  // when the last split of a pair is short
+  attend_split<NT, C>(a, blockIdx.x, blockIdx.y, mg);
+}
+
+// Merge the partials of one (pair, head) that hold tokens: the attention splits
+// [0, ns) and, with the fused rebuild, the tiles of misses [0, nt) (partials
+// n_split + t):  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 // 512 threads: 32 lanes cover one partial row (4 dims each, 16-byte loads) and
-// the 16 row groups take every 16th split, then sum their rows through LDS, so a
-// long split list is read 16 rows at a time.
+// the 16 row groups take every 16th partial, then sum their rows through LDS, so
+// a long list is read 16 rows at a time.
 constexpr int kCombineThreads = 512;
 constexpr int kCombineGroups = kCombineThreads / (kHeadDim / 4);
 
 template <int G>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) {
-  __shared__ float cw[kMaxSplits];
+  __shared__ float cw[kMaxPartials];
   __shared__ __attribute__((aligned(16))) float rows[kCombineGroups][kHeadDim];
   __shared__ float den_sh;
   const int g = blockIdx.x, p = blockIdx.y;
   const int b = p / a.n_kv, h = p % a.n_kv;
-  const int ns = a.n_split;
+  int ns = a.n_split, nt = 0;
+  if (a.rebuild_fused) {
+    const int nm = a.n_miss[p];
+    const int units = a.n_outlier + (a.top_k - nm) + a.n_win_units + a.n_new_units - a.n_fold;
+    ns = (units + a.upw - 1) / a.upw;
+    nt = (nm + kRebuildRows / a.chunk - 1) / (kRebuildRows / a.chunk);
+  }
+  const int n = ns + nt;
   const int64_t stride = (int64_t)G * kPartStride;
-  const float* base = a.attn_part + (int64_t)p * ns * stride + g * kPartStride;
-  for (int s = threadIdx.x; s < ns; s += kCombineThreads) cw[s] = base[s * stride + kHeadDim];
+  const float* base = a.attn_part + (int64_t)p * a.n_part_att * stride + g * kPartStride;
+  auto row = [&](int s) { return base + (int64_t)(s < ns ? s : a.n_split + (s - ns)) * stride; };
+  for (int s = threadIdx.x; s < n; s += kCombineThreads) cw[s] = row(s)[kHeadDim];
   __syncthreads();
-  if (threadIdx.x < 64) {   // wave 0: split weights 2^(m_s - M) and the denominator
+  if (threadIdx.x < 64) {   // wave 0: partial weights 2^(m_s - M) and the denominator
     float M = kNegBig;
-    for (int s = threadIdx.x; s < ns; s += 64) M = fmaxf(M, cw[s]);
+    for (int s = threadIdx.x; s < n; s += 64) M = fmaxf(M, cw[s]);
     M = wave_max(M);
     float den = 0.f;
-    for (int s = threadIdx.x; s < ns; s += 64) {
+    for (int s = threadIdx.x; s < n; s += 64) {
       const float c = __builtin_amdgcn_exp2f(cw[s] - M);
-      den += base[s * stride + kHeadDim + 1] * c;
+      den += row(s)[kHeadDim + 1] * c;
       cw[s] = c;
     }
     den = wave_sum(den);
@@ -1461,8 +1793,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
   __syncthreads();
   const int c4 = threadIdx.x % (kHeadDim / 4), grp = threadIdx.x / (kHeadDim / 4);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = grp; s < ns; s += kCombineGroups) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(base + s * stride + c4 * 4);
+  for (int s = grp; s < n; s += kCombineGroups) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(row(s) + c4 * 4);
     const float c = cw[s];
 #pragma unroll
     for (int k = 0; k < 4; k++) acc[k] = fmaf(x[k], c, acc[k]);
@@ -1484,6 +1816,17 @@ static hipError_t launch_combine_g(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
+  switch (a.group) {
+    case 1: return launch_combine_g<1>(a, st);
+    case 2: return launch_combine_g<2>(a, st);
+    case 4: return launch_combine_g<4>(a, st);
+    case 8: return launch_combine_g<8>(a, st);
+    case 16: return launch_combine_g<16>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st) {
   if (a.group < 1 || a.group > kAttnMaxHeads) return hipErrorInvalidValue;
   const dim3 grid(a.batch * a.n_kv, a.n_split);
@@ -1493,16 +1836,139 @@ hipError_t launch_attention(const DecodeArgs& a, hipStream_t st) {
     case 16: attn_kernel<kAttnTiles, 16><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  switch (a.group) {
-    case 1: return launch_combine_g<1>(a, st);
-    case 2: return launch_combine_g<2>(a, st);
-    case 4: return launch_combine_g<4>(a, st);
-    case 8: return launch_combine_g<8>(a, st);
-    case 16: return launch_combine_g<16>(a, st);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused tail of a decode step: one launch whose first P * n_tiles workgroups
+// each rebuild one tile of a pair's missed chunks (rebuild_tile), store the keys
+// to their slots (when the temporal cache keeps them) and attend to them from
+// LDS, with the tile's values loaded from the value store before the rebuild
+// starts, and whose other P * n_split workgroups attend to the outliers, the
+// slots that hit and the exact region (attend_split).  Miss tiles go first, the
+// empty ones (past a pair's misses) first of all, so the tiles with work start
+// at once and the attention workgroups fill in behind them.
+// Two workgroups per CU (the rebuild's registers plus the tile's values).
+
+// Attention of a miss tile: its n_rows rebuilt keys in LDS (rows of kOutW bf16),
+// values vf loaded by this wave (rows w*32 + t*16 + 4lq + lr%4, clamped to the
+// wave's last row), q in bq; one partial at `part`.
+template <int C>
+__device__ __forceinline__ void attend_tile(const DecodeArgs& a, int n_rows, const uint16_t* otile,
+                                            const u32x4 (&vf)[2][4], const bf16x8 (&bq)[4], float* part,
+                                            AttnMerge& mg) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int ntok = max(0, min(32, n_rows - w * 32));
+  float m = kNegBig, l = 0.f;
+  f32x4 o[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; c++)
+#pragma unroll
+    for (int e = 0; e < 2; e++) o[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (ntok > 0) {   // wave-uniform
+    u32x4 kf[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const int row = w * 32 + min(t * 16 + lr, ntok - 1);
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        kf[t][j] = *reinterpret_cast<const u32x4*>(otile + row * kOutW + j * 32 + lq * 8);
+    }
+    wave_attend<2>(kf, vf, bq, ntok, a.scale * kLog2e, lane, m, l, o);
+  }
+  merge_waves(a.group, lane, m, l, o, mg, part);
+}
+
+template <int C, int NSTEP, bool A8, bool B8>
+__global__ __launch_bounds__(256, 2) void tail_kernel(DecodeArgs a) {
+  constexpr int MPB = kRebuildRows / C;
+  constexpr int kStage = rebuild_stage_bytes<NSTEP>() > (int)sizeof(AttnMerge) ? rebuild_stage_bytes<NSTEP>()
+                                                                                : (int)sizeof(AttnMerge);
+  __shared__ u32x4 stage[kStage / 16];
+  __shared__ int mchunk[MPB], mslot[MPB];
+  AttnMerge& mg = *reinterpret_cast<AttnMerge*>(stage);   // used once the stage is read
+  const int P = a.batch * a.n_kv;
+  const int n_tiles = (a.top_k + MPB - 1) / MPB;
+  const int bid = blockIdx.x;
+  if (bid >= P * n_tiles) {
+    const int x = bid - P * n_tiles;
+    attend_split<kAttnTiles, C>(a, x % P, x / P, mg);
+    return;
+  }
+  // miss tile T of pair p: misses [T*MPB, T*MPB + MPB) of the pair's list
+  const int p = bid % P, T = n_tiles - 1 - bid / P;
+  const int j0 = T * MPB, K = a.top_k;
+  for (int i = threadIdx.x; i < MPB; i += 256) {
+    const bool ok = j0 + i < K;
+    mchunk[i] = ok ? a.miss_chunk[(int64_t)p * K + j0 + i] : -1;
+    mslot[i] = ok ? a.miss_slot[(int64_t)p * K + j0 + i] : -1;
+  }
+  __syncthreads();
+  if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
+  int nmiss = 0;               // misses in this tile (a prefix of mchunk)
+  for (int i = 0; i < MPB; i++) nmiss += mchunk[i] >= 0;
+  const int n_rows = nmiss * C;
+  const int b = p / a.n_kv, h = p % a.n_kv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  // q and this wave's values first: they arrive while the keys are rebuilt
+  bf16x8 bq[4];
+  load_q(a, p, lr, lq, bq);
+  u32x4 vf[2][4];
+  const int ntok = max(0, min(32, n_rows - w * 32));
+  if (ntok > 0) {   // wave-uniform
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const int row = w * 32 + min(t * 16 + 4 * lq + (lr & 3), ntok - 1);
+      const uint16_t* vp = chunk_values(a, p, b, h, mchunk[row / C]) + (row % C) * kHeadDim + (lr >> 2) * 8;
+#pragma unroll
+      for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) vf[t][c] = (u32x4){0u, 0u, 0u, 0u};
+  }
+  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage);
+  const uint16_t* otile = reinterpret_cast<const uint16_t*>(stage);
+  if (a.temporal) store_tile<C>(a, p, mslot, otile);   // kept for the next steps' hits
+  attend_tile<C>(a, n_rows, otile, vf, bq,
+                 a.attn_part + ((int64_t)p * a.n_part_att + a.n_split + T) * a.group * kPartStride, mg);
+}
+
+template <int C, bool A8>
+static hipError_t launch_tail_c(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  if (a.b_format == SKV_FORMAT_FP8_E5M2) {
+    tail_kernel<C, 1, A8, true><<<grid, 256, 0, st>>>(a);   // one k-step per iteration
+    return hipGetLastError();
+  }
+  switch (min(kMaxSteps, (a.rank + 31) / 32)) {
+    case 1: tail_kernel<C, 1, A8, false><<<grid, 256, 0, st>>>(a); break;
+    case 2: tail_kernel<C, 2, A8, false><<<grid, 256, 0, st>>>(a); break;
+    case 3: tail_kernel<C, 3, A8, false><<<grid, 256, 0, st>>>(a); break;
+    case 4: tail_kernel<C, 4, A8, false><<<grid, 256, 0, st>>>(a); break;
+    default: tail_kernel<C, kMaxSteps, A8, false><<<grid, 256, 0, st>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+template <bool A8>
+static hipError_t launch_tail_a(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.chunk) {
+    case 4: return launch_tail_c<4, A8>(a, grid, st);
+    case 8: return launch_tail_c<8, A8>(a, grid, st);
+    case 16: return launch_tail_c<16, A8>(a, grid, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_tail(const DecodeArgs& a, bool with_splits, hipStream_t st) {
+  if (a.group < 1 || a.group > kAttnMaxHeads) return hipErrorInvalidValue;
+  const int P = a.batch * a.n_kv, mpb = kRebuildRows / a.chunk;
+  const dim3 grid(P * ((a.top_k + mpb - 1) / mpb) + (with_splits ? P * a.n_split : 0));
+  return a.a_format == SKV_FORMAT_FP8_E5M2 ? launch_tail_a<true>(a, grid, st) : launch_tail_a<false>(a, grid, st);
 }
 
 }  // namespace skv

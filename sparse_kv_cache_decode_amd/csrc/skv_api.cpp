@@ -60,6 +60,8 @@ struct skv_layer {
   int n_fold = 0;                    // appended chunks folded into the candidates (low rank)
   int64_t a_rows = 0;                // rows of A per batch element
   int upw = 0, res_words = 0;
+  int n_part_att = 0;                // attention partial rows per pair
+  bool fused = false;                // misses rebuilt and attended in one launch (tail_kernel)
   bool poisoned = false;
   bool need_reset = false;
   const uint16_t* v_dev = nullptr;   // device-visible address of the value store
@@ -70,6 +72,7 @@ struct skv_layer {
            *key_new = nullptr, *val_new = nullptr;
   int32_t *cand_map = nullptr, *outlier_ids = nullptr, *slot_cand = nullptr, *slot_chunk = nullptr,
           *miss_slot = nullptr, *miss_chunk = nullptr, *miss_cand = nullptr, *free_slot = nullptr,
+          *hit_slot = nullptr,
           *n_miss = nullptr, *hits_last = nullptr;
   uint32_t *resident = nullptr, *keys = nullptr;
   long long *hits_total = nullptr, *miss_total = nullptr;
@@ -148,6 +151,11 @@ skv_status validate(const skv_config* c) {
   if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta)) return SKV_ERR_SHAPE;
   if (c->max_new_tokens < 0) return SKV_ERR_SHAPE;
   if (c->new_token_mode != SKV_NEW_EXACT && c->new_token_mode != SKV_NEW_LOWRANK) return SKV_ERR_INVALID_ARG;
+  if (c->rebuild_mode != SKV_REBUILD_AUTO && c->rebuild_mode != SKV_REBUILD_FUSED &&
+      c->rebuild_mode != SKV_REBUILD_SEPARATE)
+    return SKV_ERR_INVALID_ARG;
+  if (c->rebuild_mode == SKV_REBUILD_FUSED && c->value_placement == SKV_VALUES_HOST) return SKV_ERR_UNSUPPORTED;
+  if (c->select_mode != SKV_SELECT_AUTO && c->select_mode != SKV_SELECT_FULL) return SKV_ERR_INVALID_ARG;
   // attention splits: at most kMaxSplits per pair with every appended token present
   const int64_t units = c->n_outlier + c->top_k + c->window / c->chunk +
                         ((int64_t)c->max_new_tokens + c->chunk - 1) / c->chunk;
@@ -234,6 +242,8 @@ DecodeArgs decode_args(skv_layer* h) {
   // attention splits grow with the exact region (window + appended, not folded)
   a.n_split = (h->U + a.n_new_units - h->n_fold + h->upw - 1) / h->upw;
   a.upw = h->upw;
+  a.n_part_att = h->n_part_att;
+  a.rebuild_fused = h->fused ? 1 : 0;
   a.temporal = c.temporal_cache;
   a.host_values = c.value_placement == SKV_VALUES_HOST;
   a.scale = 1.0f / std::sqrt((float)c.head_dim);
@@ -258,12 +268,17 @@ DecodeArgs decode_args(skv_layer* h) {
   a.miss_chunk = h->miss_chunk;
   a.miss_cand = h->miss_cand;
   a.free_slot = h->free_slot;
+  a.hit_slot = h->hit_slot;
   a.n_miss = h->n_miss;
   a.hits_last = h->hits_last;
   a.hits_total = h->hits_total;
   a.miss_total = h->miss_total;
   a.keys = h->keys;
   select_partition(h->n_cand, c.top_k, h->G, h->P, &a.n_part, &a.part_size);
+  a.n_ctiles = (h->n_cand + 15) / 16;
+  a.n_ctiles_cap = (h->cand_cap + 15) / 16;
+  a.sel_two_level = c.select_mode != SKV_SELECT_FULL &&
+                    select2_shape(a.n_ctiles_cap, c.top_k, h->res_words, &a.sel_tpt, &a.sel_ipt);
   apply_transient(a, h->xs_layout, h->xs);
   return a;
 }
@@ -305,6 +320,18 @@ skv_status decode_enqueue(skv_layer* h, const uint16_t* q, float* out, int32_t* 
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
     HIP_TRY(launch_select(a, s));
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    if (h->fused) {
+      HIP_TRY(launch_tail(a, true, s));
+      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+      HIP_TRY(launch_combine(a, s));
+      if (ev) {
+        HIP_TRY(hipEventRecord(ev[4], s));
+        h->t_n++;
+      }
+      h->steps++;
+      h->last_stream = s;
+      return SKV_OK;
+    }
     if (a.host_values) {
       HIP_TRY(hipEventRecord(h->ev_fork, s));
       HIP_TRY(hipStreamWaitEvent(h->side, h->ev_fork, 0));
@@ -320,6 +347,7 @@ skv_status decode_enqueue(skv_layer* h, const uint16_t* q, float* out, int32_t* 
       if (ev) HIP_TRY(hipEventRecord(ev[3], s));
     }
     HIP_TRY(launch_attention(a, s));
+    HIP_TRY(launch_combine(a, s));
     if (ev) {
       HIP_TRY(hipEventRecord(ev[4], s));
       h->t_n++;
@@ -390,6 +418,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   h->HD = H * kHeadDim;
   h->U = O + K + h->n_win;
   h->res_words = (h->cand_cap + 31) / 32;
+  h->fused = c.rebuild_mode == SKV_REBUILD_FUSED ||
+             (c.rebuild_mode == SKV_REBUILD_AUTO && c.value_placement == SKV_VALUES_DEVICE);
   h->v_dev = v_dev;
   const int P = h->P, G = h->G, n_c = h->n_c, cap = h->cand_cap, HD = h->HD;
   // scratch sized for the largest candidate count the handle can reach (the
@@ -437,6 +467,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const size_t oMch = cv.take<int32_t>((size_t)P * K);
   const size_t oMca = cv.take<int32_t>((size_t)P * K);
   const size_t oFs = cv.take<int32_t>((size_t)P * K);
+  const size_t oHs = cv.take<int32_t>((size_t)P * K);
   const size_t oNm = cv.take<int32_t>(P);
   const size_t oHl = cv.take<int32_t>(P);
   const size_t oRes = cv.take<uint32_t>((size_t)P * h->res_words);
@@ -454,8 +485,12 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     t.merge_idx = tc.take<int32_t>((size_t)P * n_merge_cap * K);
     t.logits = tc.take<float>((size_t)P * G * ncp_cap);
     t.lse_part = tc.take<float>((size_t)P * nb_cap * G * 2);
+    t.tile_max = tc.take<float>((size_t)P * ((cap + 15) / 16) * G);
     const int n_split_max = (h->U + (c.max_new_tokens + C - 1) / C + h->upw - 1) / h->upw;
-    t.attn_part = tc.take<float>((size_t)P * n_split_max * G * kPartStride);
+    // fused rebuild: one more partial per tile of kRebuildRows rows of misses
+    const int mpb = kRebuildRows / C;
+    h->n_part_att = n_split_max + (h->fused ? (K + mpb - 1) / mpb : 0);
+    t.attn_part = tc.take<float>((size_t)P * h->n_part_att * G * kPartStride);
     t.bytes = (tc.off + kAlign - 1) / kAlign * kAlign;
   }
   const size_t oXs = cv.take<uint8_t>(h->xs_layout.bytes);
@@ -509,6 +544,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->miss_chunk = (int32_t*)(base + oMch);
     h->miss_cand = (int32_t*)(base + oMca);
     h->free_slot = (int32_t*)(base + oFs);
+    h->hit_slot = (int32_t*)(base + oHs);
     h->n_miss = (int32_t*)(base + oNm);
     h->hits_last = (int32_t*)(base + oHl);
     h->resident = (uint32_t*)(base + oRes);

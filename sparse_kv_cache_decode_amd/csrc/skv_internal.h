@@ -11,9 +11,11 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxTopK = 4096;
 constexpr int kSelLdsMax = 150 * 1024;   // dynamic LDS of the select kernel
 constexpr int kMaxSplits = 4096;         // attention workgroups per pair
+constexpr int kMaxPartials = kMaxSplits + 512;   // attention partials per pair (splits + miss tiles)
 constexpr int kScoreRows = 128;          // candidate landmarks per score workgroup (bf16)
 constexpr int kScoreRows8 = 256;         // the same for FP8 landmarks (the same 32 KB)
 constexpr int kPartStride = kHeadDim + 4; // floats per attention partial row: o[d], m, l, 2 pad (16-B rows)
+constexpr int kRebuildRows = 128;        // key rows rebuilt per workgroup (128 / C missed chunks)
 
 // Everything a decode step touches, by value into the kernels.
 struct DecodeArgs {
@@ -30,6 +32,8 @@ struct DecodeArgs {
   int nb_score, cpb;          // score workgroups per pair, candidates per workgroup
   int ncp;                    // logits row stride (n_cand rounded up to 4)
   int n_split, upw;           // attention workgroups per pair, units per workgroup
+  int n_part_att;             // attention partial rows per pair (splits, then miss tiles when fused)
+  int rebuild_fused;          // 1: misses rebuilt and attended in one launch with the rest (tail_kernel)
   int temporal, host_values;
   float scale;                // 1/sqrt(d)
   const double* inv_freq;     // [64]
@@ -57,6 +61,7 @@ struct DecodeArgs {
   int32_t* miss_slot;         // [P][K]
   int32_t* miss_chunk;        // [P][K]
   int32_t* miss_cand;         // [P][K]
+  int32_t* hit_slot;          // [P][K] slots that kept their chunk this step, ascending (K - n_miss)
   int32_t* free_slot;         // [P][K]
   int32_t* n_miss;            // [P]
   int32_t* hits_last;         // [P]
@@ -65,13 +70,18 @@ struct DecodeArgs {
   // scratch
   float* logits;              // [P][G][ncp]
   float* lse_part;            // [P][nb_score][G][2]
+  float* tile_max;            // [P][n_ctiles][G] largest logit of each 16-candidate tile and head
+  int n_ctiles;               // 16-candidate tiles per pair: ceil(n_cand / 16)
+  int n_ctiles_cap;           // tile rows per pair of tile_max (candidate capacity / 16)
+  int sel_two_level;          // 1: select2_kernel (tile keys, then the candidates of the hot tiles)
+  int sel_tpt, sel_ipt;       // its tiles and level-2 items (4 candidates) per thread
   uint32_t* keys;             // [P][n_cand]
   int n_part, part_size;      // selection stage 1: candidate parts per pair and their size
   uint32_t* part_keys;        // [P][n_part][K] each part's top-K keys, ascending candidate index
   int32_t* part_idx;          // [P][n_part][K] their candidate indices
   uint32_t* merge_keys;       // [P][<= n_part / 2][K] lists of a merge-tree level
   int32_t* merge_idx;
-  float* attn_part;           // [P][n_split][G][kPartStride]
+  float* attn_part;           // [P][n_part_att][G][kPartStride]
   // outputs
   float* out;                 // [b][Hq][d]
   int32_t* chunk_ids;         // [P][K]
@@ -81,13 +91,14 @@ struct DecodeArgs {
 // (nothing in it has to start at zero: every step writes each part before it
 // reads it).  Computed at build for the handle's largest candidate count.
 struct TransientLayout {
-  size_t logits = 0, lse_part = 0, part_keys = 0, part_idx = 0, merge_keys = 0, merge_idx = 0,
+  size_t logits = 0, lse_part = 0, tile_max = 0, part_keys = 0, part_idx = 0, merge_keys = 0, merge_idx = 0,
          attn_part = 0, bytes = 0;
 };
 
 inline void apply_transient(DecodeArgs& a, const TransientLayout& t, char* base) {
   a.logits = reinterpret_cast<float*>(base + t.logits);
   a.lse_part = reinterpret_cast<float*>(base + t.lse_part);
+  a.tile_max = reinterpret_cast<float*>(base + t.tile_max);
   a.part_keys = reinterpret_cast<uint32_t*>(base + t.part_keys);
   a.part_idx = reinterpret_cast<int32_t*>(base + t.part_idx);
   a.merge_keys = reinterpret_cast<uint32_t*>(base + t.merge_keys);
@@ -142,6 +153,8 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
 // top-K are taken by separate workgroups (stage 1), then merged per pair (stage 2).
 void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, int* part_size);
 int merge_groups(int top_k);   // part lists merged per workgroup of the merge tree
+// Two-level selection: tiles and level-2 items per thread, or 0 where it does not apply.
+int select2_shape(int n_ctiles_cap, int top_k, int res_words, int* tpt, int* ipt);
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
 // Append token t (position S + t) of every batch element: exact post-RoPE key
 // and value into key_new / val_new; lowrank: also its row a' = k' Psi of A.
@@ -152,7 +165,11 @@ hipError_t launch_append(const DecodeArgs& a, const uint16_t* k_new, const uint1
 // pair, its landmark the bf16 mean of its stored keys.
 hipError_t launch_fold(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
-hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);   // separate rebuild: every slot
+// fused rebuild + attention: the miss tiles, and with_splits the attention splits
+// in the same launch (else launch_attention runs them, e.g. on another stream)
+hipError_t launch_tail(const DecodeArgs& a, bool with_splits, hipStream_t st);
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t st);     // merge of the partials
 int attn_units_per_wave(int chunk);   // 16-token tiles per wave * 16 / C
 
 // ---- host eigensolver (eig_host.cpp)

@@ -161,14 +161,16 @@ __device__ void block_topk(Get get, int n, int k, int* hist, int* sh, Emit emit)
   block_topk<NT>(get, n, k, lo, hi, hist, sh, emit);
 }
 
-// block_topk over keys held in registers: thread t owns elements [t*PT, t*PT + nv)
-// of the array (nv <= PT valid entries in key[]), so the sweeps touch no memory.
-// emit(pos, e) receives the thread's local element index e.  If hist_cleared,
-// hist[0, 2048) is already zero and visible to every thread.
-template <int NT, int PT, class Emit>
-__device__ void block_topk_reg(const uint32_t (&key)[PT], int nv, int k, uint32_t kmin, uint32_t kmax,
-                               int* hist, int* sh, bool hist_cleared, Emit emit) {
+// The k-th largest of keys held in registers (radix select on 11-bit digits of
+// key - kmin; element e of a thread counts when bit e of vmask is set; [kmin, kmax]
+// bound the counted keys, as block_range gives them).  Returns the k-th largest
+// key T and, in *kk_eq, how many of the keys equal to T are among the k largest.
+// If hist_cleared, hist[0, 2048) is already zero and visible to every thread.
+template <int NT, int PT>
+__device__ uint32_t block_kth_reg(const uint32_t (&key)[PT], uint64_t vmask, int k, uint32_t kmin, uint32_t kmax,
+                                  int* hist, int* sh, bool hist_cleared, int* kk_eq) {
   static_assert(NT % 64 == 0 && 2048 % NT == 0 && NT / 64 + 8 <= 32 && NT >= kTopkSmall, "block size");
+  static_assert(PT <= 64, "validity mask");
   constexpr int PER = 2048 / NT;
   const uint32_t range = kmax - kmin;
   const int nbits = range == 0u ? 1 : 32 - __clz(range);
@@ -187,7 +189,7 @@ __device__ void block_topk_reg(const uint32_t (&key)[PT], int nv, int k, uint32_
 #pragma unroll
     for (int e = 0; e < PT; e++) {
       const uint32_t rel = key[e] - kmin;
-      if (e < nv && (rel & mask) == prefix) atomicAdd(&hist[(rel >> shift) & dmask], 1);
+      if (((vmask >> e) & 1) && (rel & mask) == prefix) atomicAdd(&hist[(rel >> shift) & dmask], 1);
     }
     __syncthreads();
     // bins in descending order; thread t owns bins 2047 - PER*t - (0..PER-1)
@@ -220,7 +222,7 @@ __device__ void block_topk_reg(const uint32_t (&key)[PT], int nv, int k, uint32_
 #pragma unroll
       for (int e = 0; e < PT; e++) {
         const uint32_t rel = key[e] - kmin;
-        if (e < nv && (rel & mask) == prefix) small[atomicAdd(&sh[NT / 64 + 3], 1)] = (int)rel;
+        if (((vmask >> e) & 1) && (rel & mask) == prefix) small[atomicAdd(&sh[NT / 64 + 3], 1)] = (int)rel;
       }
       __syncthreads();
       if ((int)threadIdx.x < bcount) {
@@ -242,13 +244,26 @@ __device__ void block_topk_reg(const uint32_t (&key)[PT], int nv, int k, uint32_
       done = true;
     }
   }
+  __syncthreads();   // sh and hist are free for the caller
+  *kk_eq = kk;
+  return prefix + kmin;
+}
+
+// block_topk over keys held in registers: thread t owns elements [t*PT, t*PT + PT)
+// of the array, element e counting when bit e of vmask is set, so the sweeps touch
+// no memory.  emit(pos, e) receives the thread's local element index e.  If
+// hist_cleared, hist[0, 2048) is already zero and visible to every thread.
+template <int NT, int PT, class Emit>
+__device__ void block_topk_reg(const uint32_t (&key)[PT], uint64_t vmask, int k, uint32_t kmin, uint32_t kmax,
+                               int* hist, int* sh, bool hist_cleared, Emit emit) {
+  int kk;
+  const uint32_t T = block_kth_reg<NT, PT>(key, vmask, k, kmin, kmax, hist, sh, hist_cleared, &kk);
   // every key > T is taken plus the kk lowest-index keys equal to T; one block
   // scan of the (greater, equal) counts places the selections in index order
-  const uint32_t T = prefix + kmin;
   int gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < PT; e++) {
-    if (e < nv) {
+    if ((vmask >> e) & 1) {
       gt += key[e] > T;
       eq += key[e] == T;
     }
@@ -259,7 +274,7 @@ __device__ void block_topk_reg(const uint32_t (&key)[PT], int nv, int k, uint32_
   int eq_seen = ex >> 13;
 #pragma unroll
   for (int e = 0; e < PT; e++) {
-    if (e < nv) {
+    if ((vmask >> e) & 1) {
       if (key[e] > T) {
         emit(pos++, e);
       } else if (key[e] == T) {
@@ -270,5 +285,8 @@ __device__ void block_topk_reg(const uint32_t (&key)[PT], int nv, int k, uint32_
   }
   __syncthreads();
 }
+
+// The first nv elements valid.
+__device__ __forceinline__ uint64_t prefix_mask(int nv) { return nv >= 64 ? ~0ull : ((1ull << nv) - 1ull); }
 
 }  // namespace skv

@@ -22,6 +22,10 @@ SKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 SKV_VALUES_DEVICE, SKV_VALUES_HOST = 0, 1
 SKV_NEW_EXACT, SKV_NEW_LOWRANK = 0, 1
 SKV_FORMAT_BF16, SKV_FORMAT_FP8_E5M2 = 0, 1
+SKV_REBUILD_AUTO, SKV_REBUILD_FUSED, SKV_REBUILD_SEPARATE = 0, 1, 2
+REBUILD_MODES = {"auto": SKV_REBUILD_AUTO, "fused": SKV_REBUILD_FUSED, "separate": SKV_REBUILD_SEPARATE}
+SKV_SELECT_AUTO, SKV_SELECT_FULL = 0, 1
+SELECT_MODES = {"auto": SKV_SELECT_AUTO, "full": SKV_SELECT_FULL}
 FORMATS = {"bf16": SKV_FORMAT_BF16, "e5m2": SKV_FORMAT_FP8_E5M2}
 
 EXPORTED = ["skv_build", "skv_decode_step", "skv_decode_step_noalloc", "skv_append_token", "skv_get_stats", "skv_reset_temporal_cache",
@@ -38,7 +42,8 @@ class SkvConfig(ctypes.Structure):
                 ("value_placement", ctypes.c_int32), ("rope_theta", ctypes.c_double),
                 ("temporal_cache", ctypes.c_int32), ("landmark_format", ctypes.c_int32),
                 ("max_new_tokens", ctypes.c_int32), ("new_token_mode", ctypes.c_int32),
-                ("a_format", ctypes.c_int32), ("b_format", ctypes.c_int32)]
+                ("a_format", ctypes.c_int32), ("b_format", ctypes.c_int32),
+                ("rebuild_mode", ctypes.c_int32), ("select_mode", ctypes.c_int32)]
 
 
 class SkvStats(ctypes.Structure):
@@ -106,7 +111,8 @@ def skv_abi_version() -> int:
 
 
 def make_config(shape, value_placement: int = SKV_VALUES_DEVICE, temporal_cache: int = 1,
-                max_new_tokens: int = 0, new_token_mode: int = SKV_NEW_EXACT) -> SkvConfig:
+                max_new_tokens: int = 0, new_token_mode: int = SKV_NEW_EXACT,
+                rebuild_mode: int = SKV_REBUILD_AUTO, select_mode: int = SKV_SELECT_AUTO) -> SkvConfig:
     """skv_config from any object with the ShadowKV shape fields (storage of
     the landmarks, of A and of B from its optional ``landmark_format``,
     ``a_format`` and ``b_format``: "bf16" or "e5m2")."""
@@ -116,7 +122,7 @@ def make_config(shape, value_placement: int = SKV_VALUES_DEVICE, temporal_cache:
     return SkvConfig(shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                      shape.seq_len, shape.rank, shape.chunk, shape.top_k, shape.n_outlier,
                      shape.window, value_placement, float(shape.rope_theta), temporal_cache, lfmt,
-                     max_new_tokens, new_token_mode, afmt, bfmt)
+                     max_new_tokens, new_token_mode, afmt, bfmt, rebuild_mode, select_mode)
 
 
 def _ptr(t) -> int | None:
@@ -214,8 +220,10 @@ class Layer:
     """Owning wrapper of one built layer."""
 
     def __init__(self, shape, k_pre, v, value_placement=SKV_VALUES_DEVICE, temporal_cache=1,
-                 stream=None, max_new_tokens=0, new_token_mode=SKV_NEW_EXACT):
-        self.cfg = make_config(shape, value_placement, temporal_cache, max_new_tokens, new_token_mode)
+                 stream=None, max_new_tokens=0, new_token_mode=SKV_NEW_EXACT, rebuild_mode=SKV_REBUILD_AUTO,
+                 select_mode=SKV_SELECT_AUTO):
+        self.cfg = make_config(shape, value_placement, temporal_cache, max_new_tokens, new_token_mode,
+                               rebuild_mode, select_mode)
         self.shape = shape
         self.h = skv_build(self.cfg, k_pre, v, stream)
         self._v = v   # the value store is borrowed by the library: keep it alive

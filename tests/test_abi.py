@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings_and_version():
-    assert skv.skv_abi_version() == 7
+    assert skv.skv_abi_version() == 8
     seen = set()
     for code in range(9):
         s = skv.skv_status_string(code)
@@ -75,6 +75,9 @@ def _cfg(**kw):
     (dict(batch=0), skv.SKV_ERR_SHAPE),
     (dict(max_new_tokens=-1), skv.SKV_ERR_SHAPE),
     (dict(new_token_mode=2), skv.SKV_ERR_INVALID_ARG),
+    (dict(rebuild_mode=3), skv.SKV_ERR_INVALID_ARG),
+    (dict(select_mode=2), skv.SKV_ERR_INVALID_ARG),
+    (dict(rebuild_mode=skv.SKV_REBUILD_FUSED, value_placement=skv.SKV_VALUES_HOST), skv.SKV_ERR_UNSUPPORTED),
 ])
 def test_build_validation(kw, expect):
     st, h = _build_status(_cfg(**kw))
@@ -124,7 +127,7 @@ int main(void) {
          sizeof(skv_stats), sizeof(skv_state_host));
   P(skv_config, seq_len) P(skv_config, rope_theta) P(skv_config, temporal_cache)
   P(skv_config, landmark_format) P(skv_config, max_new_tokens) P(skv_config, new_token_mode)
-  P(skv_config, a_format) P(skv_config, b_format)
+  P(skv_config, a_format) P(skv_config, b_format) P(skv_config, rebuild_mode) P(skv_config, select_mode)
   P(skv_stats, last_alpha) P(skv_stats, last_host_bytes) P(skv_stats, new_tokens)
   P(skv_state_host, eigvals)
   return 0;
@@ -148,6 +151,8 @@ int main(void) {
                               "skv_config.new_token_mode": (skv.SkvConfig, "new_token_mode"),
                               "skv_config.a_format": (skv.SkvConfig, "a_format"),
                               "skv_config.b_format": (skv.SkvConfig, "b_format"),
+                              "skv_config.rebuild_mode": (skv.SkvConfig, "rebuild_mode"),
+                              "skv_config.select_mode": (skv.SkvConfig, "select_mode"),
                               "skv_stats.new_tokens": (skv.SkvStats, "new_tokens"),
                               "skv_stats.last_alpha": (skv.SkvStats, "last_alpha"),
                               "skv_stats.last_host_bytes": (skv.SkvStats, "last_host_bytes"),

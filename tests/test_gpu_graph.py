@@ -14,13 +14,14 @@ from oracle import shadowkv as O
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("placement,fmt", [(skv.SKV_VALUES_DEVICE, "bf16"), (skv.SKV_VALUES_HOST, "bf16"),
-                                           (skv.SKV_VALUES_DEVICE, "e5m2")])
-def test_graph_replays_match_eager(placement, fmt):
+@pytest.mark.parametrize("placement,fmt,rebuild", [
+    (skv.SKV_VALUES_DEVICE, "bf16", skv.SKV_REBUILD_AUTO), (skv.SKV_VALUES_HOST, "bf16", skv.SKV_REBUILD_AUTO),
+    (skv.SKV_VALUES_DEVICE, "e5m2", skv.SKV_REBUILD_AUTO), (skv.SKV_VALUES_DEVICE, "bf16", skv.SKV_REBUILD_SEPARATE)])
+def test_graph_replays_match_eager(placement, fmt, rebuild):
     shape = synth.Shape("graph", batch=8, n_q_heads=16, n_kv_heads=4, head_dim=128, seq_len=4096,
                         rank=64, chunk=8, top_k=8, n_outlier=2, window=32, latent_rank=64,
                         landmark_format=fmt, a_format=fmt, b_format=fmt)
-    print(f"[graph] pairs={shape.pairs} placement={placement} storage={fmt}", flush=True)
+    print(f"[graph] pairs={shape.pairs} placement={placement} storage={fmt} rebuild={rebuild}", flush=True)
     steps = 6
     k, v = synth.layer_cache_np(shape, 0, 0)
     q = synth.queries_np(shape, k, 0, steps, 0)
@@ -29,8 +30,8 @@ def test_graph_replays_match_eager(placement, fmt):
         vd.copy_(v)
     else:
         vd = v.cuda()
-    eager = skv.Layer(shape, k.cuda(), vd, placement)
-    graphed = skv.Layer(shape, k.cuda(), vd, placement)
+    eager = skv.Layer(shape, k.cuda(), vd, placement, rebuild_mode=rebuild)
+    graphed = skv.Layer(shape, k.cuda(), vd, placement, rebuild_mode=rebuild)
     qbuf = q[0].cuda()
     out_g = torch.empty((shape.batch, shape.n_q_heads, shape.head_dim), device="cuda")
     ids_g = torch.empty((shape.batch, shape.n_kv_heads, shape.top_k), dtype=torch.int32, device="cuda")

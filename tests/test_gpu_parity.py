@@ -13,13 +13,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(shape, steps, placement=skv.SKV_VALUES_DEVICE, temporal=1, seed=0, mode="drift",
-         check_state=True, keep=False):
+         check_state=True, keep=False, rebuild=skv.SKV_REBUILD_AUTO, select=skv.SKV_SELECT_AUTO, q=None):
     print(f"[parity] {shape.name} b={shape.batch} S={shape.seq_len} G={shape.group} "
           f"C={shape.chunk} K={shape.top_k} O={shape.n_outlier} r={shape.rank} "
-          f"landmarks={shape.landmark_format} placement={placement} temporal={temporal} steps={steps}",
-          flush=True)
+          f"landmarks={shape.landmark_format} placement={placement} temporal={temporal} "
+          f"rebuild={rebuild} select={select} steps={steps}", flush=True)
     k, v = synth.layer_cache_np(shape, 0, seed)
-    q = synth.queries_np(shape, k, 0, steps, seed, mode=mode)
+    if q is None:
+        q = synth.queries_np(shape, k, 0, steps, seed, mode=mode)
     st = O.build(O.config_from(shape), bits(k), bits(v))
     kd = k.cuda()
     if placement == skv.SKV_VALUES_HOST:
@@ -27,7 +28,7 @@ def _run(shape, steps, placement=skv.SKV_VALUES_DEVICE, temporal=1, seed=0, mode
         vd.copy_(v)
     else:
         vd = v.cuda()
-    layer = skv.Layer(shape, kd, vd, placement, temporal)
+    layer = skv.Layer(shape, kd, vd, placement, temporal, rebuild_mode=rebuild, select_mode=select)
     del kd
     ex = layer.export()
     if check_state:
@@ -65,6 +66,37 @@ def _run(shape, steps, placement=skv.SKV_VALUES_DEVICE, temporal=1, seed=0, mode
 
 def test_tiny_8k_end_to_end():
     _run(synth.SHAPES["tiny_8k"], steps=4)
+
+
+# The rebuild as its own launch before the attention (SKV_REBUILD_SEPARATE) on the
+# shapes the fused default covers above: tiles, chunk sizes, group sizes, a
+# budget of one, the temporal cache off, the split selection
+@pytest.mark.parametrize("case", ["tiny", "ragged", "chunk4", "chunk16", "g16", "k1", "temporal_off", "split"])
+def test_separate_rebuild(case):
+    sep = skv.SKV_REBUILD_SEPARATE
+    if case == "tiny":
+        _run(synth.SHAPES["tiny_8k"], steps=4, rebuild=sep)
+    elif case == "ragged":
+        _run(_small(), steps=3, rebuild=sep)
+    elif case in ("chunk4", "chunk16"):
+        c = 4 if case == "chunk4" else 16
+        _run(_small(chunk=c, seq_len=8192, top_k=8192 // (64 * c), n_outlier=3, batch=1), steps=3, rebuild=sep)
+    elif case == "g16":
+        _run(_small(n_q_heads=32, n_kv_heads=2, batch=1, seq_len=4096, top_k=9, n_outlier=2, rank=48,
+                    latent_rank=48), steps=2, rebuild=sep)
+    elif case == "k1":
+        _run(_small(top_k=1, batch=1), steps=3, rebuild=sep)
+    elif case == "temporal_off":
+        _run(_small(), steps=3, temporal=0, rebuild=sep)
+    else:
+        _run(_small(batch=1, n_q_heads=16, n_kv_heads=2, seq_len=69632, rank=32, latent_rank=32, top_k=136,
+                    n_outlier=26), steps=2, rebuild=sep)
+
+
+def test_fused_rebuild_explicit_and_many_tiles():
+    # K = 400 at C = 4: 13 tiles of 32 missed chunks per pair on the first step
+    _run(_small(chunk=4, seq_len=102400, top_k=400, n_outlier=30, batch=1, n_q_heads=8, n_kv_heads=2),
+         steps=3, rebuild=skv.SKV_REBUILD_FUSED)
 
 
 def _small(**kw):
@@ -109,19 +141,29 @@ def test_budget_of_one():
     _run(_small(top_k=1, batch=1), steps=3)
 
 
-def test_reset_and_identical_query():
+@pytest.mark.parametrize("rebuild", [skv.SKV_REBUILD_SEPARATE, skv.SKV_REBUILD_FUSED])
+def test_reset_and_identical_query(rebuild):
     shape = _small(batch=1)
-    print(f"[parity] reset/identical query on {shape}", flush=True)
+    print(f"[parity] reset/identical query on {shape}, rebuild {rebuild}", flush=True)
     k, v = synth.layer_cache_np(shape, 0, 0)
     q = synth.queries_np(shape, k, 0, 2, 0)
-    layer = skv.Layer(shape, k.cuda(), v.cuda())
+    layer = skv.Layer(shape, k.cuda(), v.cuda(), rebuild_mode=rebuild)
     q0 = q[0].cuda()
     out0, ids0 = [x.clone() for x in layer.decode(q0)]
     out1, ids1 = [x.clone() for x in layer.decode(q0)]
     torch.cuda.synchronize()
     s = layer.stats()
     assert s["last_hits"] == shape.pairs * shape.top_k and s["last_misses"] == 0
-    assert torch.equal(ids0, ids1) and torch.equal(out0, out1)      # bitwise identical
+    assert torch.equal(ids0, ids1)
+    if rebuild == skv.SKV_REBUILD_SEPARATE:
+        assert torch.equal(out0, out1)      # the same units in the same splits: bitwise identical
+    else:
+        # the misses of the first step were attended by the tiles that rebuilt them,
+        # the hits of the second by attention splits: the same keys and values,
+        # summed in another grouping, with the softmax weights carried at 16 bits
+        # relative to another running maximum (2^-16 of each weight)
+        err = (out0 - out1).abs().max().item()
+        assert err <= 1e-4, err
     layer.decode(q[1].cuda())
     layer.reset()
     out2, ids2 = layer.decode(q0)
@@ -184,3 +226,39 @@ def test_rank_deficient_prefill():
     s = _small(batch=1, n_q_heads=4, n_kv_heads=2, seq_len=64, rank=64, latent_rank=64, top_k=2,
                n_outlier=1, window=0)
     _run(s, steps=3)
+
+
+# The selection as one full pass over every candidate's score (SKV_SELECT_FULL):
+# one workgroup per pair, and the parts / merge-tree path beyond 32K candidates
+@pytest.mark.parametrize("case", ["tiny", "ragged", "many_candidates", "group_of_eight", "tree_one", "tree_two"])
+def test_full_pass_selection(case):
+    full = skv.SKV_SELECT_FULL
+    if case == "tiny":
+        _run(synth.SHAPES["tiny_8k"], steps=3, select=full)
+    elif case == "ragged":
+        _run(_small(), steps=3, select=full)
+    elif case == "many_candidates":
+        _run(_small(batch=1, n_q_heads=2, n_kv_heads=1, seq_len=278528, rank=16, latent_rank=16, top_k=64,
+                    n_outlier=3), steps=2, select=full)
+    elif case == "group_of_eight":
+        _run(_small(batch=1, n_q_heads=16, n_kv_heads=2, seq_len=69632, rank=32, latent_rank=32, top_k=136,
+                    n_outlier=26), steps=2, select=full)
+    elif case == "tree_one":
+        _run(_small(batch=1, n_q_heads=16, n_kv_heads=1, seq_len=393216, rank=16, latent_rank=16, top_k=2048,
+                    n_outlier=3), steps=2, select=full)
+    else:
+        _run(_small(batch=1, n_q_heads=4, n_kv_heads=1, seq_len=557104, chunk=4, rank=16, latent_rank=16,
+                    top_k=4096, n_outlier=3), steps=2, select=full)
+
+
+@pytest.mark.parametrize("select", [skv.SKV_SELECT_AUTO, skv.SKV_SELECT_FULL])
+def test_equal_scores_take_lowest_chunks(select):
+    # zero queries: every logit is 0 and every chunk scores the same, so the K
+    # lowest chunk ids are selected; in the two-level selection every one of the
+    # 512 tiles is "hot", more than the 256 its registers hold at K = 60, so the
+    # second level runs from memory
+    s = _small(batch=2, n_q_heads=32, n_kv_heads=8, seq_len=65536, top_k=60, n_outlier=10)
+    assert (s.n_cand + 15) // 16 > 256
+    q = torch.zeros((2, s.batch, s.n_q_heads, s.head_dim), dtype=torch.bfloat16)
+    _run(s, steps=2, select=select, q=q)
+
