@@ -306,7 +306,7 @@ def main():
                     help="storage of the rows of A: bf16 (the pages' precision) or FP8 E5M2")
     ap.add_argument("--b-format", choices=["bf16", "e5m2"], default="bf16",
                     help="storage of B (Psi^T): bf16 (the pages' precision) or FP8 E5M2")
-    ap.add_argument("--rebuild", choices=["auto", "fused", "separate"], default="auto",
+    ap.add_argument("--rebuild", choices=["auto", "fused", "separate", "overlap"], default="auto",
                     help="missed chunks rebuilt and attended in one launch with the rest of the attention "
                          "(fused; auto with values in HBM) or rebuilt by their own launch before it (separate)")
     ap.add_argument("--graph", choices=["on", "off"], default="off",
@@ -543,7 +543,7 @@ def main():
         "phase_timing": f"HIP events around each phase on the decode stream, layers {sampled}, {PH} eager steps "
                         f"after the timed region",
         "launch": "one captured HIP graph per step (all layers), replayed" if graph is not None else "eager launches",
-        "rebuild": "fused" if (args.rebuild == "fused" or (args.rebuild == "auto" and not host)) else "separate",
+        "rebuild": args.rebuild if args.rebuild != "auto" else ("separate" if host else "fused"),
         "layer_us": round(layer_us, 2),
         "build_ms_per_layer": {"mean": round(1000.0 * sum(build_s[1:] or build_s) / len(build_s[1:] or build_s), 1),
                                "first": round(1000.0 * build_s[0], 1),

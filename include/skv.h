@@ -106,6 +106,10 @@ typedef int32_t skv_status;
                                   hit and the window; values in HBM only            */
 #define SKV_REBUILD_SEPARATE 2 /* a rebuild launch refreshes the missed key slots, then
                                   an attention launch reads every slot               */
+#define SKV_REBUILD_OVERLAP 3  /* one launch rebuilds the missed chunks into their
+                                  slots beside the attention over the outliers, the
+                                  slots that hit and the window; a second attends to
+                                  the missed slots; values in HBM only              */
 
 /* How the top-K of the chunk scores is found (the same chunks either way). */
 #define SKV_SELECT_AUTO 0      /* two levels where they fit: the largest score of every
@@ -148,8 +152,9 @@ typedef struct skv_config {
   int32_t a_format;        /* SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2 (rows of A,
                               also those appended in SKV_NEW_LOWRANK mode)        */
   int32_t b_format;        /* SKV_FORMAT_BF16 or SKV_FORMAT_FP8_E5M2 (B = Psi^T)   */
-  int32_t rebuild_mode;    /* SKV_REBUILD_AUTO, _FUSED or _SEPARATE; FUSED with
-                              SKV_VALUES_HOST gives SKV_ERR_UNSUPPORTED             */
+  int32_t rebuild_mode;    /* SKV_REBUILD_AUTO, _FUSED, _SEPARATE or _OVERLAP; FUSED
+                              or OVERLAP with SKV_VALUES_HOST gives
+                              SKV_ERR_UNSUPPORTED                                  */
   int32_t select_mode;     /* SKV_SELECT_AUTO or SKV_SELECT_FULL                   */
 } skv_config;
 

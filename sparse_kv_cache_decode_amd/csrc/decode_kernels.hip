@@ -317,12 +317,13 @@ static size_t select_lds_bytes(const DecodeArgs& a) {
 }
 
 // LSE_g of the pair's G heads from the score workgroups' (max, sum) partials, by
-// waves 0..G-1: one pass, each lane folding its blocks into a running (max, sum)
-// with four independent 8-byte loads in flight, then a butterfly over the wave.
-template <int G>
+// the NT / 64 waves of the workgroup, head g by wave g mod (NT / 64): one pass,
+// each lane folding its blocks into a running (max, sum) with four independent
+// 8-byte loads in flight, then across the wave.
+template <int G, int NT = kSelThreads>
 __device__ __forceinline__ void pair_lse(const DecodeArgs& a, int p, float* lse) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (w < G) {
+  const int lane = threadIdx.x & 63;
+  for (int w = threadIdx.x >> 6; w < G; w += NT / 64) {
     const float* src = a.lse_part + (int64_t)p * a.nb_score * G * 2;
     float M = kNegBig, S = 0.f;
     for (int k0 = lane; k0 < a.nb_score; k0 += 4 * 64) {
@@ -339,20 +340,33 @@ __device__ __forceinline__ void pair_lse(const DecodeArgs& a, int p, float* lse)
         M = Mn;
       }
     }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float Mo = __shfl_xor(M, o), So = __shfl_xor(S, o);
+    // fold the lanes: DPP within each row of 16, then the four rows as scalars
+    auto fold = [&](float Mo, float So) {
       const float Mn = fmaxf(M, Mo);
       S = S * __expf(M - Mn) + So * __expf(Mo - Mn);
       M = Mn;
+    };
+    fold(dpp<SKV_DPP_QP_XOR1>(M), dpp<SKV_DPP_QP_XOR1>(S));
+    fold(dpp<SKV_DPP_QP_XOR2>(M), dpp<SKV_DPP_QP_XOR2>(S));
+    fold(dpp<SKV_DPP_ROW_HALF_MIRROR>(M), dpp<SKV_DPP_ROW_HALF_MIRROR>(S));
+    fold(dpp<SKV_DPP_ROW_MIRROR>(M), dpp<SKV_DPP_ROW_MIRROR>(S));
+    float Mr[4], Sr[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      Mr[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), 16 * r));
+      Sr[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 16 * r));
     }
-    if (lane == 0) lse[w] = M + __logf(S);
+    float Mt = fmaxf(fmaxf(Mr[0], Mr[1]), fmaxf(Mr[2], Mr[3])), St = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; r++) St += Sr[r] * __expf(Mr[r] - Mt);
+    if (lane == 0) lse[w] = Mt + __logf(St);
   }
 }
 
 // Index scan of pair p against the chunks its slots hold, given the selection
 // sel[0, K) (ascending candidate indices): chunk ids out, hits / misses, slot
 // reassignment, miss list, list of the slots that hit, counters.
+template <int NT = kSelThreads>
 __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* selch, int* freel, int* missp,
                            int* scl, uint32_t* resl) {
   const int K = a.top_k, RW = a.res_words;
@@ -360,14 +374,14 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
   int32_t* sch = a.slot_chunk + (int64_t)p * K;
   uint32_t* res = a.resident + (int64_t)p * RW;
   const int32_t* cmap = a.cand_map + (int64_t)p * a.cand_stride;
-  for (int i = threadIdx.x; i < K; i += kSelThreads) {
+  for (int i = threadIdx.x; i < K; i += NT) {
     const int ch = cmap[sel[i]];
     selch[i] = ch;
     a.chunk_ids[(int64_t)p * K + i] = ch;
   }
   const bool has_prev = a.temporal && scl[0] >= 0;
   int n_free = 0, n_miss = 0;
-  for (int t0 = 0; t0 < K; t0 += kSelThreads) {
+  for (int t0 = 0; t0 < K; t0 += NT) {
     const int s = t0 + threadIdx.x;
     int fr = 0, ms = 0;
     if (s < K) {
@@ -377,7 +391,7 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
       ms = !(has_prev && ((resl[ci >> 5] >> (ci & 31)) & 1u));
     }
     int tot;
-    const int ex = block_exclusive_scan<kSelThreads>(fr | (ms << 16), sh, &tot);
+    const int ex = block_exclusive_scan<NT>(fr | (ms << 16), sh, &tot);
     if (fr) freel[n_free + (ex & 0xffff)] = s;
     if (ms) missp[n_miss + (ex >> 16)] = s;
     // a slot that keeps its chunk is a hit: listed in ascending slot order
@@ -388,7 +402,7 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
   __syncthreads();
   // n_free == n_miss: every missed chunk takes the next evicted slot.  The miss
   // list is written in full, -1 past n_miss, so its readers need not load n_miss.
-  for (int j = threadIdx.x; j < K; j += kSelThreads) {
+  for (int j = threadIdx.x; j < K; j += NT) {
     int slot = -1, ch = -1;
     if (j < n_miss) {
       slot = freel[j];
@@ -404,7 +418,7 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
     a.miss_chunk[(int64_t)p * K + j] = ch;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < RW; i += kSelThreads) res[i] = resl[i];
+  for (int i = threadIdx.x; i < RW; i += NT) res[i] = resl[i];
   if (threadIdx.x == 0) {
     a.n_miss[p] = n_miss;
     a.hits_last[p] = has_prev ? K - n_miss : 0;
@@ -679,10 +693,10 @@ __device__ __forceinline__ uint32_t cand_key(const DecodeArgs& a, int p, int c, 
   return float_key(best - 1.0f);
 }
 
-template <int G, int TPT, int IPT>
-__global__ __launch_bounds__(kSelThreads) void select2_kernel(DecodeArgs a) {
+template <int G, int NT, int TPT, int IPT>
+__global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
   extern __shared__ int smem[];
-  const int K = a.top_k, RW = a.res_words, NT = a.n_ctiles, n = a.n_cand;
+  const int K = a.top_k, RW = a.res_words, n_tiles = a.n_ctiles, n = a.n_cand;
   int* hist = smem;
   int* sh = smem + kHist;
   int* sel = sh + 32;        // selected candidate indices, ascending
@@ -697,12 +711,12 @@ __global__ __launch_bounds__(kSelThreads) void select2_kernel(DecodeArgs a) {
   // ---- level 1: tile keys of tiles [t*TPT, t*TPT + TPT); their maxima are
   // loaded before the LSE is reduced when they fit in 32 registers, else after
   const int t0 = threadIdx.x * TPT;
-  const int ntv = max(0, min(TPT, NT - t0));   // this thread's tiles
-  const float* tm = a.tile_max + (int64_t)p * NT * G;
+  const int ntv = max(0, min(TPT, n_tiles - t0));   // this thread's tiles
+  const float* tm = a.tile_max + (int64_t)p * n_tiles * G;
   constexpr bool kPrefetch = TPT * G <= 32;
   float mg[kPrefetch ? TPT : 1][G];
   auto load_tile = [&](int e, float (&m)[G]) {
-    const int tile = min(t0 + e, NT - 1);   // past the tiles: re-read the last, not counted
+    const int tile = min(t0 + e, n_tiles - 1);   // past the tiles: re-read the last, not counted
     if constexpr (G % 4 == 0) {
 #pragma unroll
       for (int g = 0; g < G; g += 4) {
@@ -722,11 +736,11 @@ __global__ __launch_bounds__(kSelThreads) void select2_kernel(DecodeArgs a) {
   {
     const int32_t* sc = a.slot_cand + (int64_t)p * K;
     const uint32_t* res = a.resident + (int64_t)p * RW;
-    for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
-    for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
+    for (int i = threadIdx.x; i < K; i += NT) scl[i] = sc[i];
+    for (int i = threadIdx.x; i < RW; i += NT) resl[i] = res[i];
   }
-  for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
-  pair_lse<G>(a, p, lse);
+  for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0;
+  pair_lse<G, NT>(a, p, lse);
   __syncthreads();
   uint32_t tk[TPT];
   uint32_t lo = 0xffffffffu, hi = 0u;
@@ -748,26 +762,27 @@ __global__ __launch_bounds__(kSelThreads) void select2_kernel(DecodeArgs a) {
       hi = max(hi, tk[e]);
     }
   }
-  block_range<kSelThreads>(lo, hi, sh);
+  block_range<NT>(lo, hi, sh);
+  const uint32_t hi1 = hi;   // the pair's largest key
   uint32_t beta = 0u;   // every key passes when K exceeds the tile count
-  if (K <= NT) {
+  if (K <= n_tiles) {
     int kk;
-    beta = block_kth_reg<kSelThreads, TPT>(tk, prefix_mask(ntv), K, lo, hi, hist, sh, true, &kk);
+    beta = block_kth_reg<NT, TPT>(tk, prefix_mask(ntv), K, lo, hi, hist, sh, true, &kk);
   }
   // hot tiles, compacted in ascending order
   int nh = 0;
 #pragma unroll
   for (int e = 0; e < TPT; e++) nh += (e < ntv && tk[e] >= beta);
   int n_hot;
-  int off = block_exclusive_scan<kSelThreads>(nh, sh, &n_hot);
+  int off = block_exclusive_scan<NT>(nh, sh, &n_hot);
 #pragma unroll
   for (int e = 0; e < TPT; e++)
     if (e < ntv && tk[e] >= beta) hot[off++] = t0 + e;
-  for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
+  for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0;
   __syncthreads();
   // ---- level 2: the candidates of the hot tiles, items of 4 candidates
   const int n_items = n_hot * 4;
-  if (n_items <= kSelThreads * IPT) {
+  if (n_items <= NT * IPT) {
     const int i0 = threadIdx.x * IPT;
     uint32_t key[IPT * 4];
     uint64_t vmask = 0;
@@ -800,17 +815,10 @@ __global__ __launch_bounds__(kSelThreads) void select2_kernel(DecodeArgs a) {
         if (i0 + it < n_items && cb + c < n && kv >= beta) vmask |= 1ull << (it * 4 + c);
       }
     }
-    lo = 0xffffffffu;
-    hi = 0u;
-#pragma unroll
-    for (int e = 0; e < IPT * 4; e++) {
-      if ((vmask >> e) & 1) {
-        lo = min(lo, key[e]);
-        hi = max(hi, key[e]);
-      }
-    }
-    block_range<kSelThreads>(lo, hi, sh);
-    block_topk_reg<kSelThreads, IPT * 4>(key, vmask, K, lo, hi, hist, sh, true, [&](int pos, int e) {
+    // the keys that pass lie in [beta, the largest tile key]; a version that
+    // ranked each passing key against all others (one per thread, from LDS)
+    // took 18.7 us per pair at the Llama-3.1-8B shape against 3.6 us for this
+    block_topk_reg<NT, IPT * 4>(key, vmask, K, beta, hi1, hist, sh, true, [&](int pos, int e) {
       const int item = i0 + e / 4;
       sel[pos] = hot[item >> 2] * 16 + (item & 3) * 4 + (e & 3);
     });
@@ -818,65 +826,77 @@ __global__ __launch_bounds__(kSelThreads) void select2_kernel(DecodeArgs a) {
     // many equal tile keys: the hot tiles' candidates from memory (candidates
     // past n_cand get key 0, below every real key, and are never taken)
     const int m = n_hot * 16;
-    block_topk<kSelThreads>(
+    block_topk<NT>(
         [&](int i) {
           const int c = hot[i >> 4] * 16 + (i & 15);
           return c < n ? cand_key<G>(a, p, c, lse) : 0u;
         },
         m, K, hist, sh, [&](int pos, int i) { sel[pos] = hot[i >> 4] * 16 + (i & 15); });
   }
-  index_scan(a, p, sh, sel, selch, freel, missp, scl, resl);
+  index_scan<NT>(a, p, sh, sel, selch, freel, missp, scl, resl);
 }
 
 static size_t select2_lds_bytes(const DecodeArgs& a) {
   return (size_t)(kHist + 32 + 5 * a.top_k + a.res_words + a.n_ctiles_cap) * sizeof(int);
 }
 
-// Tiles and level-2 items per thread of the two-level selection, or 0 when it
-// does not apply (more than 16K tiles per pair, or its LDS would not fit).
-int select2_shape(int n_ctiles_cap, int top_k, int res_words, int* tpt, int* ipt) {
-  const int t = (n_ctiles_cap + kSelThreads - 1) / kSelThreads;
-  if (t > 16) return 0;
+// Workgroup size, tiles and level-2 items per thread of the two-level selection,
+// or 0 when it does not apply (more tiles per thread than 16, or LDS that would
+// not fit).  1024 threads: 256 (one wave per SIMD) made every block-wide step
+// cheaper but the per-thread loops longer, 20.8 against 15.2 us per pair at the
+// Llama-3.1-8B shape (phase stamps).
+int select2_shape(int n_ctiles_cap, int top_k, int res_words, int* nt, int* tpt, int* ipt) {
   if ((size_t)(kHist + 32 + 5 * top_k + res_words + n_ctiles_cap) * sizeof(int) > (size_t)kSelLdsMax) return 0;
-  *tpt = t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 16;
-  // hot tiles are about K (more only on equal tile keys): room for 1.25 K, at
-  // most 8 items (32 keys) per thread, past which the registers spill
-  const int need = (5 * top_k + kSelThreads - 1) / kSelThreads;   // 4 items per tile
-  *ipt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-  return 1;
+  for (int threads : {kSelThreads}) {
+    const int t = (n_ctiles_cap + threads - 1) / threads;
+    // hot tiles are about K (more only on equal tile keys): room for 1.25 K, at
+    // most 8 items (32 keys) per thread, past which the registers spill
+    const int need = (5 * top_k + threads - 1) / threads;   // 4 items per tile
+    if (t > 16 || (threads == 256 && need > 8)) continue;
+    *nt = threads;
+    *tpt = t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 16;
+    *ipt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+    return 1;
+  }
+  return 0;
 }
 
-template <int G, int TPT, int IPT>
+template <int G, int NT, int TPT, int IPT>
 static hipError_t launch_select2_i(const DecodeArgs& a, hipStream_t st) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = allow_lds(&select2_kernel<G, TPT, IPT>);
+    hipError_t e = allow_lds(&select2_kernel<G, NT, TPT, IPT>);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  select2_kernel<G, TPT, IPT><<<a.batch * a.n_kv, kSelThreads, select2_lds_bytes(a), st>>>(a);
+  select2_kernel<G, NT, TPT, IPT><<<a.batch * a.n_kv, NT, select2_lds_bytes(a), st>>>(a);
   return hipGetLastError();
 }
 
-template <int G, int TPT>
+template <int G, int NT, int TPT>
 static hipError_t launch_select2_t(const DecodeArgs& a, hipStream_t st) {
   switch (a.sel_ipt) {
-    case 1: return launch_select2_i<G, TPT, 1>(a, st);
-    case 2: return launch_select2_i<G, TPT, 2>(a, st);
-    case 4: return launch_select2_i<G, TPT, 4>(a, st);
-    default: return launch_select2_i<G, TPT, 8>(a, st);
+    case 1: return launch_select2_i<G, NT, TPT, 1>(a, st);
+    case 2: return launch_select2_i<G, NT, TPT, 2>(a, st);
+    case 4: return launch_select2_i<G, NT, TPT, 4>(a, st);
+    default: return launch_select2_i<G, NT, TPT, 8>(a, st);
+  }
+}
+
+template <int G, int NT>
+static hipError_t launch_select2_n(const DecodeArgs& a, hipStream_t st) {
+  switch (a.sel_tpt) {
+    case 1: return launch_select2_t<G, NT, 1>(a, st);
+    case 2: return launch_select2_t<G, NT, 2>(a, st);
+    case 4: return launch_select2_t<G, NT, 4>(a, st);
+    case 8: return launch_select2_t<G, NT, 8>(a, st);
+    default: return launch_select2_t<G, NT, 16>(a, st);
   }
 }
 
 template <int G>
 static hipError_t launch_select2_g(const DecodeArgs& a, hipStream_t st) {
-  switch (a.sel_tpt) {
-    case 1: return launch_select2_t<G, 1>(a, st);
-    case 2: return launch_select2_t<G, 2>(a, st);
-    case 4: return launch_select2_t<G, 4>(a, st);
-    case 8: return launch_select2_t<G, 8>(a, st);
-    default: return launch_select2_t<G, 16>(a, st);
-  }
+  return a.sel_nt == 256 ? launch_select2_n<G, 256>(a, st) : launch_select2_n<G, kSelThreads>(a, st);
 }
 
 template <int G, int PT>
@@ -1068,13 +1088,20 @@ constexpr int rebuild_stage_bytes() {
 // into their slots.  Called by all 256 threads of a workgroup with mchunk in LDS
 // (written before a barrier) and `stage` an LDS buffer of
 // rebuild_stage_bytes<NSTEP>(); returns after a barrier, with the rows in place.
+// `pre` is called once the RoPE frequencies have arrived, before the operand
+// loads are issued (the fused tail issues its query and value loads there).
 // A8: rows of A stored as FP8 E5M2 (r bytes per row) instead of bf16.  B8: B^T
 // stored as FP8 E5M2; its operand fragments (8 bytes per lane and column tile,
 // 20 KB per pair at r = 160, read by every wave from L2) are then loaded straight
 // into registers and widened to bf16, with one k-step per iteration, instead of
 // the staged direct-to-LDS slices of the bf16 path.
-template <int C, int NSTEP, bool A8, bool B8>
-__device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const int* mchunk, u32x4* stage) {
+struct NoPrefetch {
+  __device__ void operator()() const {}
+};
+
+template <int C, int NSTEP, bool A8, bool B8, class Pre = NoPrefetch>
+__device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const int* mchunk, u32x4* stage,
+                                             Pre pre = Pre()) {
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int r = a.rank;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1111,6 +1138,9 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) ang[mt][nt] = rope_angle(pos0[mt], ffreq[nt]);
   }
+  // the caller's own loads go out here: after the frequencies (whose wait would
+  // otherwise also wait for them) and before the operand loads
+  pre();
   f32x4 acc[2][8];
 #pragma unroll
   for (int mt = 0; mt < 2; mt++)
@@ -1502,11 +1532,12 @@ __device__ __forceinline__ int slot_units(const DecodeArgs& a, int p) {
   return a.rebuild_fused ? a.top_k - a.n_miss[p] : a.top_k;
 }
 
-// Key / value rows of unit u of pair p; ns selected-chunk units, `slot` and `ch`
-// the slot and chunk id of u when it is one of them.
+// Key / value rows of unit u of pair p: O outlier units, then ns selected-chunk
+// units, then the exact region; `slot` and `ch` the slot and chunk id of u when it
+// is a selected chunk.
 template <int C>
-__device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, int u, int ns, int slot) {
-  const int O = a.n_outlier, K = a.top_k, Wu = a.n_win_units;
+__device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, int u, int O, int ns, int slot) {
+  const int K = a.top_k, Wu = a.n_win_units;
   if (u < O) return a.k_out + ((int64_t)p * O + u) * C * kHeadDim;
   if (u < O + ns) return a.key_slots + ((int64_t)p * K + slot) * C * kHeadDim;
   const int x = u - O - ns + a.n_fold;
@@ -1515,9 +1546,9 @@ __device__ __forceinline__ const uint16_t* unit_key(const DecodeArgs& a, int p, 
 }
 
 template <int C>
-__device__ __forceinline__ const uint16_t* unit_value(const DecodeArgs& a, int p, int b, int h, int u, int ns,
+__device__ __forceinline__ const uint16_t* unit_value(const DecodeArgs& a, int p, int b, int h, int u, int O, int ns,
                                                       int slot, int ch) {
-  const int O = a.n_outlier, K = a.top_k;
+  const int K = a.top_k;
   if (u < O) return a.v_out + ((int64_t)p * O + u) * C * kHeadDim;
   if (u < O + ns)
     return a.host_values ? a.val_slots + ((int64_t)p * K + slot) * C * kHeadDim : chunk_values(a, p, b, h, ch);
@@ -1677,20 +1708,25 @@ __device__ __forceinline__ void merge_waves(int G, int lane, float m, float l, c
 // pair's [outliers; selected-chunk units; exact region] (the exact region being
 // the window units and appended units not yet folded into the candidates; its
 // last unit may be partly filled: tokens past it are masked like a wave's tail).
-// A split past the pair's units writes nothing (the merge skips it).
-template <int NT, int C>
+// With MISSES, the units are the slots of the step's misses alone (the overlapped
+// rebuild attends to them after their keys are stored) and the partial goes to
+// row n_split + split.  A split past the pair's units writes nothing (the merge
+// skips it).
+template <int NT, int C, bool MISSES = false>
 __device__ __forceinline__ void attend_split(const DecodeArgs& a, int p, int split, AttnMerge& mg) {
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;   // (row|head|dim, kq)
-  const int O = a.n_outlier, K = a.top_k;
-  const int ns = slot_units(a, p);
-  const int U = O + ns + a.n_win_units + a.n_new_units - a.n_fold;
+  const int K = a.top_k;
+  const int O = MISSES ? 0 : a.n_outlier;
+  const int ns = MISSES ? a.n_miss[p] : slot_units(a, p);
+  const int U = O + ns + (MISSES ? 0 : a.n_win_units + a.n_new_units - a.n_fold);
   if (split * a.upw >= U) return;            // workgroup-uniform
   const int per_wave = (a.upw + 3) / 4;
   const int uw0 = min(U, split * a.upw + w * per_wave);
   const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
-  const int valid = (O + ns + a.n_win_units - a.n_fold) * C + a.n_new_tokens;   // tokens in units [0, U)
+  // tokens in units [0, U)
+  const int valid = MISSES ? ns * C : (O + ns + a.n_win_units - a.n_fold) * C + a.n_new_tokens;
   const int ntok = max(0, min((uw1 - uw0) * C, valid - uw0 * C));
 
   float m = kNegBig, l = 0.f;   // head lr
@@ -1705,7 +1741,8 @@ __device__ __forceinline__ void attend_split(const DecodeArgs& a, int p, int spl
     if (lane < uw1 - uw0) {
       const int sidx = uw0 + lane - O;
       if (sidx >= 0 && sidx < ns) {
-        my_slot = a.rebuild_fused ? a.hit_slot[(int64_t)p * K + sidx] : sidx;
+        my_slot = MISSES ? a.miss_slot[(int64_t)p * K + sidx]
+                         : (a.rebuild_fused ? a.hit_slot[(int64_t)p * K + sidx] : sidx);
         my_ch = max(a.slot_chunk[(int64_t)p * K + my_slot], 0);
       }
     }
@@ -1725,31 +1762,34 @@ __device__ __forceinline__ void attend_split(const DecodeArgs& a, int p, int spl
     for (int t = 0; t < NT; t++) {
       const int tk = min(t * 16 + lr, tlast);
       const int ks = __shfl(my_slot, tk / C);
-      const uint16_t* kp = unit_key<C>(a, p, uw0 + tk / C, ns, ks) + (tk % C) * kHeadDim + lq * 8;
+      const uint16_t* kp = unit_key<C>(a, p, uw0 + tk / C, O, ns, ks) + (tk % C) * kHeadDim + lq * 8;
 #pragma unroll
       for (int j = 0; j < 4; j++) kf[t][j] = *reinterpret_cast<const u32x4*>(kp + j * 32);
       const int tv = min(t * 16 + 4 * lq + (lr & 3), tlast);
       const int vs = __shfl(my_slot, tv / C), vc = __shfl(my_ch, tv / C);
-      const uint16_t* vp = unit_value<C>(a, p, b, h, uw0 + tv / C, ns, vs, vc) + (tv % C) * kHeadDim + (lr >> 2) * 8;
+      const uint16_t* vp =
+          unit_value<C>(a, p, b, h, uw0 + tv / C, O, ns, vs, vc) + (tv % C) * kHeadDim + (lr >> 2) * 8;
 #pragma unroll
       for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
     }
     wave_attend<NT>(kf, vf, bq, ntok, a.scale * kLog2e, lane, m, l, o);
   }
-  merge_waves(a.group, lane, m, l, o, mg, a.attn_part + ((int64_t)p * a.n_part_att + split) * a.group * kPartStride);
+  const int row = MISSES ? a.n_split + split : split;
+  merge_waves(a.group, lane, m, l, o, mg, a.attn_part + ((int64_t)p * a.n_part_att + row) * a.group * kPartStride);
 }
 
-template <int NT, int C>
+template <int NT, int C, bool MISSES>
 __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) AttnMerge mg;
   // pairs fastest: workgroups go to the 8 XCDs round-robin by linear id, so each
   // XCD gets whole pairs (all splits of pairs p = x mod 8) and equal work even
   // when the last split of a pair is short
-  attend_split<NT, C>(a, blockIdx.x, blockIdx.y, mg);
+  attend_split<NT, C, MISSES>(a, blockIdx.x, blockIdx.y, mg);
 }
 
 // Merge the partials of one (pair, head) that hold tokens: the attention splits
-// [0, ns) and, with the fused rebuild, the tiles of misses [0, nt) (partials
+// [0, ns) and, when the misses are attended on their own (fused or overlapped
+// rebuild), the partials of their miss_part_units-unit groups [0, nt) (rows
 // n_split + t):  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 // 512 threads: 32 lanes cover one partial row (4 dims each, 16-byte loads) and
 // the 16 row groups take every 16th partial, then sum their rows through LDS, so
@@ -1769,7 +1809,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
     const int nm = a.n_miss[p];
     const int units = a.n_outlier + (a.top_k - nm) + a.n_win_units + a.n_new_units - a.n_fold;
     ns = (units + a.upw - 1) / a.upw;
-    nt = (nm + kRebuildRows / a.chunk - 1) / (kRebuildRows / a.chunk);
+    nt = (nm + a.miss_part_units - 1) / a.miss_part_units;
   }
   const int n = ns + nt;
   const int64_t stride = (int64_t)G * kPartStride;
@@ -1827,17 +1867,21 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
   }
 }
 
-hipError_t launch_attention(const DecodeArgs& a, hipStream_t st) {
+template <bool MISSES>
+static hipError_t launch_attention_m(const DecodeArgs& a, hipStream_t st) {
   if (a.group < 1 || a.group > kAttnMaxHeads) return hipErrorInvalidValue;
-  const dim3 grid(a.batch * a.n_kv, a.n_split);
+  const dim3 grid(a.batch * a.n_kv, MISSES ? (a.top_k + a.upw - 1) / a.upw : a.n_split);
   switch (a.chunk) {
-    case 4: attn_kernel<kAttnTiles, 4><<<grid, 256, 0, st>>>(a); break;
-    case 8: attn_kernel<kAttnTiles, 8><<<grid, 256, 0, st>>>(a); break;
-    case 16: attn_kernel<kAttnTiles, 16><<<grid, 256, 0, st>>>(a); break;
+    case 4: attn_kernel<kAttnTiles, 4, MISSES><<<grid, 256, 0, st>>>(a); break;
+    case 8: attn_kernel<kAttnTiles, 8, MISSES><<<grid, 256, 0, st>>>(a); break;
+    case 16: attn_kernel<kAttnTiles, 16, MISSES><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
+
+hipError_t launch_attention(const DecodeArgs& a, hipStream_t st) { return launch_attention_m<false>(a, st); }
+hipError_t launch_attention_misses(const DecodeArgs& a, hipStream_t st) { return launch_attention_m<true>(a, st); }
 
 // ---------------------------------------------------------------------------
 // Fused tail of a decode step: one launch whose first P * n_tiles workgroups
@@ -1880,8 +1924,8 @@ __device__ __forceinline__ void attend_tile(const DecodeArgs& a, int n_rows, con
   merge_waves(a.group, lane, m, l, o, mg, part);
 }
 
-template <int C, int NSTEP, bool A8, bool B8>
-__global__ __launch_bounds__(256, 2) void tail_kernel(DecodeArgs a) {
+template <int C, int NSTEP, bool A8, bool B8, bool ATTEND>
+__global__ __launch_bounds__(256, ATTEND ? 2 : 3) void tail_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
   constexpr int kStage = rebuild_stage_bytes<NSTEP>() > (int)sizeof(AttnMerge) ? rebuild_stage_bytes<NSTEP>()
                                                                                 : (int)sizeof(AttnMerge);
@@ -1890,14 +1934,21 @@ __global__ __launch_bounds__(256, 2) void tail_kernel(DecodeArgs a) {
   AttnMerge& mg = *reinterpret_cast<AttnMerge*>(stage);   // used once the stage is read
   const int P = a.batch * a.n_kv;
   const int n_tiles = (a.top_k + MPB - 1) / MPB;
+  // Miss tiles first, the empty ones (past a pair's misses: the misses are a
+  // prefix of its list) first of all, so they leave at once and the tiles with
+  // work start right behind them; the attention splits follow.  Dispatching the
+  // two kinds interleaved (tile s and split s of every pair, stage by stage) was
+  // slower, 34 against 31 us per launch at the Llama-3.1-8B shape: the tiles
+  // (two per CU) still held the slots and the splits waited behind them.
   const int bid = blockIdx.x;
   if (bid >= P * n_tiles) {
     const int x = bid - P * n_tiles;
     attend_split<kAttnTiles, C>(a, x % P, x / P, mg);
     return;
   }
+  const int p = bid % P, idx = n_tiles - 1 - bid / P;
   // miss tile T of pair p: misses [T*MPB, T*MPB + MPB) of the pair's list
-  const int p = bid % P, T = n_tiles - 1 - bid / P;
+  const int T = idx;
   const int j0 = T * MPB, K = a.top_k;
   for (int i = threadIdx.x; i < MPB; i += 256) {
     const bool ok = j0 + i < K;
@@ -1906,69 +1957,78 @@ __global__ __launch_bounds__(256, 2) void tail_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
+  if constexpr (!ATTEND) {     // overlapped rebuild: the keys only, attended by the next launch
+    rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage);
+    store_tile<C>(a, p, mslot, reinterpret_cast<const uint16_t*>(stage));
+    return;
+  }
   int nmiss = 0;               // misses in this tile (a prefix of mchunk)
   for (int i = 0; i < MPB; i++) nmiss += mchunk[i] >= 0;
   const int n_rows = nmiss * C;
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  // q and this wave's values first: they arrive while the keys are rebuilt
+  // q and this wave's values go out with the rebuild's operand loads and arrive
+  // while the keys are rebuilt
   bf16x8 bq[4];
-  load_q(a, p, lr, lq, bq);
   u32x4 vf[2][4];
   const int ntok = max(0, min(32, n_rows - w * 32));
-  if (ntok > 0) {   // wave-uniform
+  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage, [&] {
+    load_q(a, p, lr, lq, bq);
+    if (ntok > 0) {   // wave-uniform
 #pragma unroll
-    for (int t = 0; t < 2; t++) {
-      const int row = w * 32 + min(t * 16 + 4 * lq + (lr & 3), ntok - 1);
-      const uint16_t* vp = chunk_values(a, p, b, h, mchunk[row / C]) + (row % C) * kHeadDim + (lr >> 2) * 8;
+      for (int t = 0; t < 2; t++) {
+        const int row = w * 32 + min(t * 16 + 4 * lq + (lr & 3), ntok - 1);
+        const uint16_t* vp = chunk_values(a, p, b, h, mchunk[row / C]) + (row % C) * kHeadDim + (lr >> 2) * 8;
 #pragma unroll
-      for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
+        for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) vf[t][c] = (u32x4){0u, 0u, 0u, 0u};
     }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 2; t++)
-#pragma unroll
-      for (int c = 0; c < 4; c++) vf[t][c] = (u32x4){0u, 0u, 0u, 0u};
-  }
-  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage);
+  });
   const uint16_t* otile = reinterpret_cast<const uint16_t*>(stage);
   if (a.temporal) store_tile<C>(a, p, mslot, otile);   // kept for the next steps' hits
   attend_tile<C>(a, n_rows, otile, vf, bq,
                  a.attn_part + ((int64_t)p * a.n_part_att + a.n_split + T) * a.group * kPartStride, mg);
 }
 
-template <int C, bool A8>
+template <int C, bool A8, bool ATTEND>
 static hipError_t launch_tail_c(const DecodeArgs& a, dim3 grid, hipStream_t st) {
   if (a.b_format == SKV_FORMAT_FP8_E5M2) {
-    tail_kernel<C, 1, A8, true><<<grid, 256, 0, st>>>(a);   // one k-step per iteration
+    tail_kernel<C, 1, A8, true, ATTEND><<<grid, 256, 0, st>>>(a);   // one k-step per iteration
     return hipGetLastError();
   }
   switch (min(kMaxSteps, (a.rank + 31) / 32)) {
-    case 1: tail_kernel<C, 1, A8, false><<<grid, 256, 0, st>>>(a); break;
-    case 2: tail_kernel<C, 2, A8, false><<<grid, 256, 0, st>>>(a); break;
-    case 3: tail_kernel<C, 3, A8, false><<<grid, 256, 0, st>>>(a); break;
-    case 4: tail_kernel<C, 4, A8, false><<<grid, 256, 0, st>>>(a); break;
-    default: tail_kernel<C, kMaxSteps, A8, false><<<grid, 256, 0, st>>>(a); break;
+    case 1: tail_kernel<C, 1, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
+    case 2: tail_kernel<C, 2, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
+    case 3: tail_kernel<C, 3, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
+    case 4: tail_kernel<C, 4, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
+    default: tail_kernel<C, kMaxSteps, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
   }
   return hipGetLastError();
 }
 
-template <bool A8>
+template <bool A8, bool ATTEND>
 static hipError_t launch_tail_a(const DecodeArgs& a, dim3 grid, hipStream_t st) {
   switch (a.chunk) {
-    case 4: return launch_tail_c<4, A8>(a, grid, st);
-    case 8: return launch_tail_c<8, A8>(a, grid, st);
-    case 16: return launch_tail_c<16, A8>(a, grid, st);
+    case 4: return launch_tail_c<4, A8, ATTEND>(a, grid, st);
+    case 8: return launch_tail_c<8, A8, ATTEND>(a, grid, st);
+    case 16: return launch_tail_c<16, A8, ATTEND>(a, grid, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_tail(const DecodeArgs& a, bool with_splits, hipStream_t st) {
+hipError_t launch_tail(const DecodeArgs& a, bool attend_tiles, hipStream_t st) {
   if (a.group < 1 || a.group > kAttnMaxHeads) return hipErrorInvalidValue;
   const int P = a.batch * a.n_kv, mpb = kRebuildRows / a.chunk;
-  const dim3 grid(P * ((a.top_k + mpb - 1) / mpb) + (with_splits ? P * a.n_split : 0));
-  return a.a_format == SKV_FORMAT_FP8_E5M2 ? launch_tail_a<true>(a, grid, st) : launch_tail_a<false>(a, grid, st);
+  const dim3 grid(P * ((a.top_k + mpb - 1) / mpb) + P * a.n_split);
+  const bool a8 = a.a_format == SKV_FORMAT_FP8_E5M2;
+  if (attend_tiles) return a8 ? launch_tail_a<true, true>(a, grid, st) : launch_tail_a<false, true>(a, grid, st);
+  return a8 ? launch_tail_a<true, false>(a, grid, st) : launch_tail_a<false, false>(a, grid, st);
 }
 
 }  // namespace skv

@@ -61,7 +61,7 @@ struct skv_layer {
   int64_t a_rows = 0;                // rows of A per batch element
   int upw = 0, res_words = 0;
   int n_part_att = 0;                // attention partial rows per pair
-  bool fused = false;                // misses rebuilt and attended in one launch (tail_kernel)
+  int rebuild = SKV_REBUILD_SEPARATE; // resolved rebuild mode (FUSED, SEPARATE or OVERLAP)
   bool poisoned = false;
   bool need_reset = false;
   const uint16_t* v_dev = nullptr;   // device-visible address of the value store
@@ -152,9 +152,11 @@ skv_status validate(const skv_config* c) {
   if (c->max_new_tokens < 0) return SKV_ERR_SHAPE;
   if (c->new_token_mode != SKV_NEW_EXACT && c->new_token_mode != SKV_NEW_LOWRANK) return SKV_ERR_INVALID_ARG;
   if (c->rebuild_mode != SKV_REBUILD_AUTO && c->rebuild_mode != SKV_REBUILD_FUSED &&
-      c->rebuild_mode != SKV_REBUILD_SEPARATE)
+      c->rebuild_mode != SKV_REBUILD_SEPARATE && c->rebuild_mode != SKV_REBUILD_OVERLAP)
     return SKV_ERR_INVALID_ARG;
-  if (c->rebuild_mode == SKV_REBUILD_FUSED && c->value_placement == SKV_VALUES_HOST) return SKV_ERR_UNSUPPORTED;
+  if ((c->rebuild_mode == SKV_REBUILD_FUSED || c->rebuild_mode == SKV_REBUILD_OVERLAP) &&
+      c->value_placement == SKV_VALUES_HOST)
+    return SKV_ERR_UNSUPPORTED;
   if (c->select_mode != SKV_SELECT_AUTO && c->select_mode != SKV_SELECT_FULL) return SKV_ERR_INVALID_ARG;
   // attention splits: at most kMaxSplits per pair with every appended token present
   const int64_t units = c->n_outlier + c->top_k + c->window / c->chunk +
@@ -243,7 +245,8 @@ DecodeArgs decode_args(skv_layer* h) {
   a.n_split = (h->U + a.n_new_units - h->n_fold + h->upw - 1) / h->upw;
   a.upw = h->upw;
   a.n_part_att = h->n_part_att;
-  a.rebuild_fused = h->fused ? 1 : 0;
+  a.rebuild_fused = h->rebuild != SKV_REBUILD_SEPARATE;
+  a.miss_part_units = h->rebuild == SKV_REBUILD_FUSED ? kRebuildRows / c.chunk : h->upw;
   a.temporal = c.temporal_cache;
   a.host_values = c.value_placement == SKV_VALUES_HOST;
   a.scale = 1.0f / std::sqrt((float)c.head_dim);
@@ -278,7 +281,7 @@ DecodeArgs decode_args(skv_layer* h) {
   a.n_ctiles = (h->n_cand + 15) / 16;
   a.n_ctiles_cap = (h->cand_cap + 15) / 16;
   a.sel_two_level = c.select_mode != SKV_SELECT_FULL &&
-                    select2_shape(a.n_ctiles_cap, c.top_k, h->res_words, &a.sel_tpt, &a.sel_ipt);
+                    select2_shape(a.n_ctiles_cap, c.top_k, h->res_words, &a.sel_nt, &a.sel_tpt, &a.sel_ipt);
   apply_transient(a, h->xs_layout, h->xs);
   return a;
 }
@@ -320,8 +323,9 @@ skv_status decode_enqueue(skv_layer* h, const uint16_t* q, float* out, int32_t* 
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
     HIP_TRY(launch_select(a, s));
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
-    if (h->fused) {
-      HIP_TRY(launch_tail(a, true, s));
+    if (h->rebuild != SKV_REBUILD_SEPARATE) {
+      HIP_TRY(launch_tail(a, h->rebuild == SKV_REBUILD_FUSED, s));
+      if (h->rebuild == SKV_REBUILD_OVERLAP) HIP_TRY(launch_attention_misses(a, s));
       if (ev) HIP_TRY(hipEventRecord(ev[3], s));
       HIP_TRY(launch_combine(a, s));
       if (ev) {
@@ -418,8 +422,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   h->HD = H * kHeadDim;
   h->U = O + K + h->n_win;
   h->res_words = (h->cand_cap + 31) / 32;
-  h->fused = c.rebuild_mode == SKV_REBUILD_FUSED ||
-             (c.rebuild_mode == SKV_REBUILD_AUTO && c.value_placement == SKV_VALUES_DEVICE);
+  h->rebuild = c.rebuild_mode != SKV_REBUILD_AUTO ? c.rebuild_mode
+              : c.value_placement == SKV_VALUES_DEVICE ? SKV_REBUILD_FUSED : SKV_REBUILD_SEPARATE;
   h->v_dev = v_dev;
   const int P = h->P, G = h->G, n_c = h->n_c, cap = h->cand_cap, HD = h->HD;
   // scratch sized for the largest candidate count the handle can reach (the
@@ -489,7 +493,9 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     const int n_split_max = (h->U + (c.max_new_tokens + C - 1) / C + h->upw - 1) / h->upw;
     // fused rebuild: one more partial per tile of kRebuildRows rows of misses
     const int mpb = kRebuildRows / C;
-    h->n_part_att = n_split_max + (h->fused ? (K + mpb - 1) / mpb : 0);
+    h->n_part_att = n_split_max + (h->rebuild == SKV_REBUILD_FUSED     ? (K + mpb - 1) / mpb
+                                   : h->rebuild == SKV_REBUILD_OVERLAP ? (K + h->upw - 1) / h->upw
+                                                                       : 0);
     t.attn_part = tc.take<float>((size_t)P * h->n_part_att * G * kPartStride);
     t.bytes = (tc.off + kAlign - 1) / kAlign * kAlign;
   }

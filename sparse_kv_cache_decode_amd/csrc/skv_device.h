@@ -104,6 +104,9 @@ __device__ __forceinline__ float rope_angle(int64_t pos, double inv_freq) {
 #define SKV_DPP_QP_XOR2 0x4E     // quad_perm [2,3,0,1]
 #define SKV_DPP_ROW_HALF_MIRROR 0x141
 #define SKV_DPP_ROW_MIRROR 0x140
+#define SKV_DPP_ROW_SHR(n) (0x110 + (n))
+#define SKV_DPP_ROW_BCAST15 0x142  // lane 15 of each row to the next row (gfx9)
+#define SKV_DPP_ROW_BCAST31 0x143  // lane 31 to rows 2 and 3 (gfx9)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -141,6 +144,43 @@ __device__ __forceinline__ float wave_min(float v) {
   return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Wave-uniform minimum / maximum of a uint32: DPP within each row of 16 lanes,
+// then the four rows' results read as scalars (no LDS round trips).
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  v = min(v, dppu<SKV_DPP_QP_XOR1>(v));
+  v = min(v, dppu<SKV_DPP_QP_XOR2>(v));
+  v = min(v, dppu<SKV_DPP_ROW_HALF_MIRROR>(v));
+  v = min(v, dppu<SKV_DPP_ROW_MIRROR>(v));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, dppu<SKV_DPP_QP_XOR1>(v));
+  v = max(v, dppu<SKV_DPP_QP_XOR2>(v));
+  v = max(v, dppu<SKV_DPP_ROW_HALF_MIRROR>(v));
+  v = max(v, dppu<SKV_DPP_ROW_MIRROR>(v));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts by 1, 2, 4, 8
+// (lanes shifted in from outside a row add 0), then lane 15 of rows 0 and 2
+// into rows 1 and 3, then lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, SKV_DPP_ROW_SHR(1), 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, SKV_DPP_ROW_SHR(2), 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, SKV_DPP_ROW_SHR(4), 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, SKV_DPP_ROW_SHR(8), 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, SKV_DPP_ROW_BCAST15, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, SKV_DPP_ROW_BCAST31, 0xC, 0xF, false);
+  return x;
+}
+
 // ---------------------------------------------------------------- keys
 
 // Order-preserving map of a finite float to uint32 (larger float, larger key).
@@ -156,12 +196,7 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_inclusive_sum(v);
   if (lane == 63) tmp[wid] = x;
   __syncthreads();
   int base = 0, tot = 0;

@@ -33,7 +33,8 @@ struct DecodeArgs {
   int ncp;                    // logits row stride (n_cand rounded up to 4)
   int n_split, upw;           // attention workgroups per pair, units per workgroup
   int n_part_att;             // attention partial rows per pair (splits, then miss tiles when fused)
-  int rebuild_fused;          // 1: misses rebuilt and attended in one launch with the rest (tail_kernel)
+  int rebuild_fused;          // 1: misses attended apart from the hits (fused or overlapped rebuild)
+  int miss_part_units;        // missed chunks per partial of theirs (a tile, or a split's units)
   int temporal, host_values;
   float scale;                // 1/sqrt(d)
   const double* inv_freq;     // [64]
@@ -74,7 +75,7 @@ struct DecodeArgs {
   int n_ctiles;               // 16-candidate tiles per pair: ceil(n_cand / 16)
   int n_ctiles_cap;           // tile rows per pair of tile_max (candidate capacity / 16)
   int sel_two_level;          // 1: select2_kernel (tile keys, then the candidates of the hot tiles)
-  int sel_tpt, sel_ipt;       // its tiles and level-2 items (4 candidates) per thread
+  int sel_nt, sel_tpt, sel_ipt;   // its workgroup size, tiles and level-2 items (4 candidates) per thread
   uint32_t* keys;             // [P][n_cand]
   int n_part, part_size;      // selection stage 1: candidate parts per pair and their size
   uint32_t* part_keys;        // [P][n_part][K] each part's top-K keys, ascending candidate index
@@ -153,8 +154,9 @@ hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
 // top-K are taken by separate workgroups (stage 1), then merged per pair (stage 2).
 void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, int* part_size);
 int merge_groups(int top_k);   // part lists merged per workgroup of the merge tree
-// Two-level selection: tiles and level-2 items per thread, or 0 where it does not apply.
-int select2_shape(int n_ctiles_cap, int top_k, int res_words, int* tpt, int* ipt);
+// Two-level selection: workgroup size, tiles and level-2 items per thread, or 0
+// where it does not apply.
+int select2_shape(int n_ctiles_cap, int top_k, int res_words, int* nt, int* tpt, int* ipt);
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t st);
 // Append token t (position S + t) of every batch element: exact post-RoPE key
 // and value into key_new / val_new; lowrank: also its row a' = k' Psi of A.
@@ -166,9 +168,11 @@ hipError_t launch_append(const DecodeArgs& a, const uint16_t* k_new, const uint1
 hipError_t launch_fold(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_attention(const DecodeArgs& a, hipStream_t st);   // separate rebuild: every slot
-// fused rebuild + attention: the miss tiles, and with_splits the attention splits
-// in the same launch (else launch_attention runs them, e.g. on another stream)
-hipError_t launch_tail(const DecodeArgs& a, bool with_splits, hipStream_t st);
+// One launch: tiles of missed chunks rebuilt (and, with attend_tiles, attended
+// from LDS) beside the attention splits over outliers, hits and window.
+hipError_t launch_tail(const DecodeArgs& a, bool attend_tiles, hipStream_t st);
+// The attention over the missed chunks' slots alone (after an overlapped rebuild).
+hipError_t launch_attention_misses(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t st);     // merge of the partials
 int attn_units_per_wave(int chunk);   // 16-token tiles per wave * 16 / C
 

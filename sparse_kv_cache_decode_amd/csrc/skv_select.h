@@ -12,11 +12,8 @@ namespace skv {
 template <int NT>
 __device__ __forceinline__ void block_range(uint32_t& lo, uint32_t& hi, int* sh) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
-  }
+  lo = wave_umin(lo);
+  hi = wave_umax(hi);
   __syncthreads();
   if (lane == 0) {
     sh[wid] = (int)lo;

@@ -22,8 +22,9 @@ SKV_NOALLOC_SCRATCH_BYTES = 64 << 20
 SKV_VALUES_DEVICE, SKV_VALUES_HOST = 0, 1
 SKV_NEW_EXACT, SKV_NEW_LOWRANK = 0, 1
 SKV_FORMAT_BF16, SKV_FORMAT_FP8_E5M2 = 0, 1
-SKV_REBUILD_AUTO, SKV_REBUILD_FUSED, SKV_REBUILD_SEPARATE = 0, 1, 2
-REBUILD_MODES = {"auto": SKV_REBUILD_AUTO, "fused": SKV_REBUILD_FUSED, "separate": SKV_REBUILD_SEPARATE}
+SKV_REBUILD_AUTO, SKV_REBUILD_FUSED, SKV_REBUILD_SEPARATE, SKV_REBUILD_OVERLAP = 0, 1, 2, 3
+REBUILD_MODES = {"auto": SKV_REBUILD_AUTO, "fused": SKV_REBUILD_FUSED, "separate": SKV_REBUILD_SEPARATE,
+                 "overlap": SKV_REBUILD_OVERLAP}
 SKV_SELECT_AUTO, SKV_SELECT_FULL = 0, 1
 SELECT_MODES = {"auto": SKV_SELECT_AUTO, "full": SKV_SELECT_FULL}
 FORMATS = {"bf16": SKV_FORMAT_BF16, "e5m2": SKV_FORMAT_FP8_E5M2}

@@ -75,7 +75,8 @@ def _cfg(**kw):
     (dict(batch=0), skv.SKV_ERR_SHAPE),
     (dict(max_new_tokens=-1), skv.SKV_ERR_SHAPE),
     (dict(new_token_mode=2), skv.SKV_ERR_INVALID_ARG),
-    (dict(rebuild_mode=3), skv.SKV_ERR_INVALID_ARG),
+    (dict(rebuild_mode=4), skv.SKV_ERR_INVALID_ARG),
+    (dict(rebuild_mode=skv.SKV_REBUILD_OVERLAP, value_placement=skv.SKV_VALUES_HOST), skv.SKV_ERR_UNSUPPORTED),
     (dict(select_mode=2), skv.SKV_ERR_INVALID_ARG),
     (dict(rebuild_mode=skv.SKV_REBUILD_FUSED, value_placement=skv.SKV_VALUES_HOST), skv.SKV_ERR_UNSUPPORTED),
 ])

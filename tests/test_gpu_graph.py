@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("placement,fmt,rebuild", [
     (skv.SKV_VALUES_DEVICE, "bf16", skv.SKV_REBUILD_AUTO), (skv.SKV_VALUES_HOST, "bf16", skv.SKV_REBUILD_AUTO),
-    (skv.SKV_VALUES_DEVICE, "e5m2", skv.SKV_REBUILD_AUTO), (skv.SKV_VALUES_DEVICE, "bf16", skv.SKV_REBUILD_SEPARATE)])
+    (skv.SKV_VALUES_DEVICE, "e5m2", skv.SKV_REBUILD_AUTO), (skv.SKV_VALUES_DEVICE, "bf16", skv.SKV_REBUILD_SEPARATE),
+    (skv.SKV_VALUES_DEVICE, "bf16", skv.SKV_REBUILD_OVERLAP)])
 def test_graph_replays_match_eager(placement, fmt, rebuild):
     shape = synth.Shape("graph", batch=8, n_q_heads=16, n_kv_heads=4, head_dim=128, seq_len=4096,
                         rank=64, chunk=8, top_k=8, n_outlier=2, window=32, latent_rank=64,

@@ -68,12 +68,14 @@ def test_tiny_8k_end_to_end():
     _run(synth.SHAPES["tiny_8k"], steps=4)
 
 
-# The rebuild as its own launch before the attention (SKV_REBUILD_SEPARATE) on the
-# shapes the fused default covers above: tiles, chunk sizes, group sizes, a
-# budget of one, the temporal cache off, the split selection
+# The rebuild as its own launch before the attention (SKV_REBUILD_SEPARATE), and
+# beside the attention over the hits with the misses attended by a second launch
+# (SKV_REBUILD_OVERLAP), on the shapes the fused default covers above: tiles,
+# chunk sizes, group sizes, a budget of one, the temporal cache off, the split
+# selection
 @pytest.mark.parametrize("case", ["tiny", "ragged", "chunk4", "chunk16", "g16", "k1", "temporal_off", "split"])
-def test_separate_rebuild(case):
-    sep = skv.SKV_REBUILD_SEPARATE
+@pytest.mark.parametrize("sep", [skv.SKV_REBUILD_SEPARATE, skv.SKV_REBUILD_OVERLAP])
+def test_other_rebuild_modes(case, sep):
     if case == "tiny":
         _run(synth.SHAPES["tiny_8k"], steps=4, rebuild=sep)
     elif case == "ragged":
