@@ -39,6 +39,14 @@
  *   - Streams are passed as void* holding a hipStream_t (NULL = default stream).
  *   - A handle (one model layer) is not thread-safe; distinct handles are
  *     independent.
+ *   - Environment switches read by skv_build, for tests and debugging:
+ *     SKV_INJECT_FAIL="alloc:N" makes the N-th device allocation of the build
+ *     report failure (SKV_ERR_OOM, everything allocated before it freed);
+ *     SKV_INJECT_FAIL="hip:N" makes the N-th HIP call of the handle's later
+ *     decode steps and appends report failure without being issued
+ *     (SKV_ERR_HIP, then SKV_ERR_STATE); SKV_POISON_SLOTS=1 fills the slot
+ *     caches with bf16 NaN at build, so that a read of a slot no step wrote
+ *     shows in the output.
  */
 #ifndef SKV_H
 #define SKV_H
@@ -83,7 +91,9 @@ typedef int32_t skv_status;
                                   Landmarks (128 bytes each) are widened to fp16
                                   exactly and scored with q in fp16 (q's bf16 values
                                   are exact there in fp16's normal range,
-                                  |q| <= 65504); rows of A (r bytes each) and B are
+                                  2^-14 <= |q| <= 65504; larger ones saturate at
+                                  +-65504, smaller ones lose bits down to fp16's
+                                  subnormal step 2^-24); rows of A (r bytes each) and B are
                                   widened to bf16 exactly for the key rebuild and
                                   the low-rank append                              */
 
@@ -216,7 +226,7 @@ typedef struct skv_state_host {
  *           until skv_destroy (the value store is never copied whole).
  *   stream: work is enqueued there; the call returns after it has completed
  *           (host-synchronous).
- *   out   : receives the new handle; untouched on failure.
+ *   out   : receives the new handle; set to NULL on any failure.
  * Computes post-RoPE keys (angles in float64), landmarks, per-chunk min-cosine,
  * outliers among the non-window chunks (lowest min-cos, lower id on ties), the
  * exact outlier and window K/V, and the rank-r factors from the top-r

@@ -5,6 +5,8 @@
 // "ShadowKV ..." (papercache deep notes, section A2, pre-fill algorithm; the
 // paper-graph-ui summary, section 3.4, "Landmark Construction and Outlier
 // Detection" and "Low-Rank Key Cache Compression via Online SVD").
+#include <algorithm>
+
 #include "skv_internal.h"
 #include "skv_select.h"
 
@@ -466,6 +468,21 @@ hipError_t launch_project(const uint16_t* k_pre, const double* psi, int b, int64
                           int64_t a_rows, bool fp8, void* A, hipStream_t st) {
   dim3 grid((r + 63) / 64, (unsigned)((S + 63) / 64), b);
   project_f64_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, a_rows, fp8, A);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fill of a 16-bit array (the optional NaN poisoning of the slot caches).
+
+__global__ void fill_u16_kernel(uint16_t* __restrict__ p, size_t n, uint16_t value) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = value;
+}
+
+hipError_t launch_fill_u16(uint16_t* p, size_t n, uint16_t value, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 65536);
+  fill_u16_kernel<<<(unsigned)blocks, 256, 0, st>>>(p, n, value);
   return hipGetLastError();
 }
 

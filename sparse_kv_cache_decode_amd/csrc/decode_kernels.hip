@@ -182,7 +182,8 @@ __global__ __launch_bounds__(256) void score_kernel(DecodeArgs a) {
 // (16x16x32 fp16) takes dims kq*32 + j*8 .. +7, and q's operand follows the same
 // assignment (a dot product does not depend on the order of the dims).  An E5M2
 // byte is the high byte of the fp16 with the same value, so widening is a shift;
-// q's bf16 values convert to fp16 exactly in fp16's normal range.
+// q's bf16 values convert to fp16 exactly in fp16's normal range; beyond it they
+// saturate at +-65504 (no inf, so no NaN logits), below 2^-14 they lose bits.
 
 __device__ __forceinline__ u32x4 e5m2x8_to_f16x8(uint32_t lo, uint32_t hi) {
   return (u32x4){((lo & 0xffu) << 8) | ((lo & 0xff00u) << 16), ((lo >> 8) & 0xff00u) | (lo & 0xff000000u),
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(DecodeArgs a) {
     float x[8];
     unpack8(*reinterpret_cast<const u32x4*>(qp + j * 8), x);
 #pragma unroll
-    for (int k = 0; k < 8; k++) bq[j][k] = (_Float16)x[k];
+    for (int k = 0; k < 8; k++) bq[j][k] = (_Float16)fminf(fmaxf(x[k], -65504.0f), 65504.0f);   // saturate
   }
   float* lg = a.logits + ((int64_t)p * G + (col < G ? col : 0)) * a.ncp;
   float* tmax = a.tile_max + (int64_t)p * a.n_ctiles * G;

@@ -6,6 +6,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -25,27 +27,50 @@ struct DeviceStreams {
   hipStream_t side = nullptr;
 };
 
+constexpr int kMaxDevices = 64;
 std::mutex g_streams_mu;
-std::vector<DeviceStreams*> g_streams;   // by device ordinal
+DeviceStreams g_streams[kMaxDevices];   // by device ordinal
 
 hipError_t device_streams(DeviceStreams** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_streams_mu);
-  if ((int)g_streams.size() <= dev) g_streams.resize(dev + 1, nullptr);
-  if (!g_streams[dev]) {
-    DeviceStreams* ds = new (std::nothrow) DeviceStreams();
-    if (!ds) return hipErrorOutOfMemory;
-    e = hipStreamCreateWithFlags(&ds->side, hipStreamNonBlocking);
+  if (!g_streams[dev].side) {
+    e = hipStreamCreateWithFlags(&g_streams[dev].side, hipStreamNonBlocking);
     if (e != hipSuccess) {
-      delete ds;
+      g_streams[dev].side = nullptr;
       return e;
     }
-    g_streams[dev] = ds;
   }
-  *out = g_streams[dev];
+  *out = &g_streams[dev];
   return hipSuccess;
+}
+
+// Failure injection for the tests of the error paths.  SKV_INJECT_FAIL="alloc:N"
+// makes the N-th device allocation of each skv_build report failure (as if
+// memory were exhausted); "hip:N" makes the N-th HIP call of a built handle's
+// decode steps and appends report failure instead of being issued.  Only return
+// codes are injected: the work before stays valid, nothing after is enqueued.
+struct Injection {
+  int alloc = 0, hip = 0;
+};
+
+Injection read_injection() {
+  Injection j;
+  const char* e = std::getenv("SKV_INJECT_FAIL");
+  int n = 0;
+  if (e && std::sscanf(e, "alloc:%d", &n) == 1) j.alloc = n;
+  else if (e && std::sscanf(e, "hip:%d", &n) == 1) j.hip = n;
+  return j;
+}
+
+// SKV_POISON_SLOTS=1: skv_build fills the key (and host-value) slot caches with
+// bf16 NaN, so that a read of a slot no step has written shows as NaN output.
+bool poison_slots() {
+  const char* e = std::getenv("SKV_POISON_SLOTS");
+  return e && e[0] == '1';
 }
 
 }  // namespace
@@ -64,6 +89,7 @@ struct skv_layer {
   int rebuild = SKV_REBUILD_SEPARATE; // resolved rebuild mode (FUSED, SEPARATE or OVERLAP)
   bool poisoned = false;
   bool need_reset = false;
+  int inject_hip = 0;                // failure injection: the HIP call that reports failure (0: none)
   const uint16_t* v_dev = nullptr;   // device-visible address of the value store
   void* pool = nullptr;
   // carved from pool
@@ -292,6 +318,13 @@ DecodeArgs decode_args(skv_layer* h) {
     if (e_ != hipSuccess) goto hip_fail; \
   } while (0)
 
+// HIP_TRY for a built handle's decode and append calls, with failure injection
+#define HIP_TRY_H(expr)                                              \
+  do {                                                               \
+    if (h->inject_hip > 0 && --h->inject_hip == 0) goto hip_fail;     \
+    HIP_TRY(expr);                                                   \
+  } while (0)
+
 }  // namespace
 
 namespace skv {
@@ -315,21 +348,21 @@ skv_status decode_enqueue(skv_layer* h, const uint16_t* q, float* out, int32_t* 
   {
     hipEvent_t* ev = h->t_n < h->t_cap ? &h->tev[(size_t)h->t_n * kEv] : nullptr;
     if (h->need_reset) {
-      HIP_TRY(launch_reset_cache(a, s));
+      HIP_TRY_H(launch_reset_cache(a, s));
       h->need_reset = false;
     }
-    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
-    HIP_TRY(launch_score(a, s));
-    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
-    HIP_TRY(launch_select(a, s));
-    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    if (ev) HIP_TRY_H(hipEventRecord(ev[0], s));
+    HIP_TRY_H(launch_score(a, s));
+    if (ev) HIP_TRY_H(hipEventRecord(ev[1], s));
+    HIP_TRY_H(launch_select(a, s));
+    if (ev) HIP_TRY_H(hipEventRecord(ev[2], s));
     if (h->rebuild != SKV_REBUILD_SEPARATE) {
-      HIP_TRY(launch_tail(a, h->rebuild == SKV_REBUILD_FUSED, s));
-      if (h->rebuild == SKV_REBUILD_OVERLAP) HIP_TRY(launch_attention_misses(a, s));
-      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
-      HIP_TRY(launch_combine(a, s));
+      HIP_TRY_H(launch_tail(a, h->rebuild == SKV_REBUILD_FUSED, s));
+      if (h->rebuild == SKV_REBUILD_OVERLAP) HIP_TRY_H(launch_attention_misses(a, s));
+      if (ev) HIP_TRY_H(hipEventRecord(ev[3], s));
+      HIP_TRY_H(launch_combine(a, s));
       if (ev) {
-        HIP_TRY(hipEventRecord(ev[4], s));
+        HIP_TRY_H(hipEventRecord(ev[4], s));
         h->t_n++;
       }
       h->steps++;
@@ -337,23 +370,23 @@ skv_status decode_enqueue(skv_layer* h, const uint16_t* q, float* out, int32_t* 
       return SKV_OK;
     }
     if (a.host_values) {
-      HIP_TRY(hipEventRecord(h->ev_fork, s));
-      HIP_TRY(hipStreamWaitEvent(h->side, h->ev_fork, 0));
-      if (ev) HIP_TRY(hipEventRecord(ev[5], h->side));
-      HIP_TRY(launch_value_gather(a, h->side));
-      if (ev) HIP_TRY(hipEventRecord(ev[6], h->side));
-      HIP_TRY(hipEventRecord(h->ev_join, h->side));
-      HIP_TRY(launch_rebuild(a, s));
-      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
-      HIP_TRY(hipStreamWaitEvent(s, h->ev_join, 0));
+      HIP_TRY_H(hipEventRecord(h->ev_fork, s));
+      HIP_TRY_H(hipStreamWaitEvent(h->side, h->ev_fork, 0));
+      if (ev) HIP_TRY_H(hipEventRecord(ev[5], h->side));
+      HIP_TRY_H(launch_value_gather(a, h->side));
+      if (ev) HIP_TRY_H(hipEventRecord(ev[6], h->side));
+      HIP_TRY_H(hipEventRecord(h->ev_join, h->side));
+      HIP_TRY_H(launch_rebuild(a, s));
+      if (ev) HIP_TRY_H(hipEventRecord(ev[3], s));
+      HIP_TRY_H(hipStreamWaitEvent(s, h->ev_join, 0));
     } else {
-      HIP_TRY(launch_rebuild(a, s));
-      if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+      HIP_TRY_H(launch_rebuild(a, s));
+      if (ev) HIP_TRY_H(hipEventRecord(ev[3], s));
     }
-    HIP_TRY(launch_attention(a, s));
-    HIP_TRY(launch_combine(a, s));
+    HIP_TRY_H(launch_attention(a, s));
+    HIP_TRY_H(launch_combine(a, s));
     if (ev) {
-      HIP_TRY(hipEventRecord(ev[4], s));
+      HIP_TRY_H(hipEventRecord(ev[4], s));
       h->t_n++;
     }
   }
@@ -389,6 +422,7 @@ const char* skv_status_string(skv_status s) {
 
 skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_t* v, void* stream,
                      skv_layer** out) {
+  if (out) *out = nullptr;
   skv_status st = validate(cfg);
   if (st != SKV_OK) return st;
   if (!k_pre || !v || !out) return SKV_ERR_INVALID_ARG;
@@ -515,15 +549,25 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   int rc;
   hipError_t herr = hipSuccess;
 
-  if (hipMalloc(&h->pool, pool_bytes) != hipSuccess) {
+  // device allocations of this build, the injected one reporting failure
+  const Injection inj = read_injection();
+  int n_alloc = 0;
+  auto dev_alloc = [&](void** ptr, size_t bytes) {
+    if (inj.alloc > 0 && ++n_alloc == inj.alloc) {
+      *ptr = nullptr;
+      return false;
+    }
+    return hipMalloc(ptr, bytes) == hipSuccess;
+  };
+  h->inject_hip = inj.hip;
+  if (!dev_alloc(&h->pool, pool_bytes)) {
     (void)hipGetLastError();
     h->pool = nullptr;
     release(h);
     return SKV_ERR_OOM;
   }
-  if (hipMalloc(&L_full, (size_t)P * n_c * lrow) != hipSuccess ||
-      hipMalloc(&gpart, (size_t)b * nseg * HD * HD * 8) != hipSuccess ||
-      hipMalloc(&gram, (size_t)b * HD * HD * 8) != hipSuccess) {
+  if (!dev_alloc(&L_full, (size_t)P * n_c * lrow) || !dev_alloc((void**)&gpart, (size_t)b * nseg * HD * HD * 8) ||
+      !dev_alloc((void**)&gram, (size_t)b * HD * HD * 8)) {
     (void)hipGetLastError();
     if (L_full) (void)hipFree(L_full);
     if (gpart) (void)hipFree(gpart);
@@ -573,6 +617,10 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   HIP_TRY(hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming));
   HIP_TRY(hipMemsetAsync(h->pool, 0, pool_bytes, s));
+  if (poison_slots()) {
+    HIP_TRY(launch_fill_u16(h->key_slots, (size_t)P * K * C * kHeadDim, 0x7fc0u, s));   // bf16 NaN
+    if (h->val_slots) HIP_TRY(launch_fill_u16(h->val_slots, (size_t)P * K * C * kHeadDim, 0x7fc0u, s));
+  }
   HIP_TRY(hipMemcpyAsync(h->inv_freq, invf.data(), invf.size() * 8, hipMemcpyHostToDevice, s));
   // post-RoPE keys -> landmarks and min-cos; outliers; candidates; exact caches
   HIP_TRY(launch_rope_landmark(k_pre, b, S, H, C, h->inv_freq, fp8, L_full, h->min_cos, s));
@@ -632,12 +680,12 @@ skv_status skv_append_token(skv_layer* h, const uint16_t* k_new, const uint16_t*
   hipStream_t s = static_cast<hipStream_t>(stream);
   {
     const bool lowrank = h->cfg.new_token_mode == SKV_NEW_LOWRANK;
-    HIP_TRY(launch_append(decode_args(h), k_new, v_new, h->n_new, lowrank, s));
+    HIP_TRY_H(launch_append(decode_args(h), k_new, v_new, h->n_new, lowrank, s));
     h->n_new++;
     h->last_stream = s;
     if (lowrank && h->n_new % h->cfg.chunk == 0) {
       // the chunk just completed pushes the oldest exact chunk into the candidates
-      HIP_TRY(launch_fold(decode_args(h), s));
+      HIP_TRY_H(launch_fold(decode_args(h), s));
       h->n_cand++;
       h->n_fold++;
     }

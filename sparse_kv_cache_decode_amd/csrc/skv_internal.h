@@ -146,6 +146,9 @@ hipError_t launch_round_psi(const double* psi, int b, int HD, int r, bool b8, vo
 hipError_t launch_project(const uint16_t* k_pre, const double* psi, int b, int64_t S, int HD, int r,
                           int64_t a_rows, bool fp8, void* A, hipStream_t st);
 
+// n 16-bit words at p set to `value` (debug poisoning of the slot caches)
+hipError_t launch_fill_u16(uint16_t* p, size_t n, uint16_t value, hipStream_t st);
+
 // ---- decode launchers (decode_kernels.hip)
 hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_score(const DecodeArgs& a, hipStream_t st);

@@ -2,10 +2,10 @@
 means with the same format (the precision-sensitivity study in section 5 of the
 paper-graph-ui summary of ShadowKV, Tables 9 and 10, runs the method in
 torch.float8_e5m2).  Build: every landmark the
-oracle's value or one E5M2 spacing away; decode: the usual bars with the oracle
-scoring the landmarks the GPU built (the rule and its reason are in
-tests/parity.py)."""
+oracle's rounding of the same float64 chunk mean; decode: the usual bars."""
+import numpy as np
 import pytest
+import torch
 
 from sparse_kv_cache_decode_amd import skv, synth
 from tests.test_gpu_append import _run_append
@@ -107,4 +107,27 @@ def test_fp8_b_lowrank_appended_rows():
     # the appended rows of A are projected with the FP8 B
     layer, _, _ = _run_append(_small(window=16, b_format="e5m2"), skv.SKV_NEW_LOWRANK, [0, 9, 20, 15],
                               max_new=48)
+    layer.close()
+
+
+def test_fp8_query_beyond_fp16_range_saturates():
+    # FP8 landmarks are scored with q in fp16: query values past 65504 saturate
+    # there instead of becoming inf (which would make the logits NaN); the step
+    # stays finite and selects valid, ascending candidate chunks
+    shape = synth.SHAPES["tiny_8k"].replace(landmark_format="e5m2")
+    k, v = synth.layer_cache_np(shape, 0, 0)
+    q = synth.queries_np(shape, k, 0, 2, 0).float()
+    q[:, :, 0, :4] = 2.0e5
+    q[:, :, 1, 5] = -3.0e6
+    q = q.to(torch.bfloat16)
+    layer = skv.Layer(shape, k.cuda(), v.cuda())
+    cand = layer.export()["cand_ids"]
+    for t in range(2):
+        out, ids = layer.decode(q[t].cuda())
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        g = ids.cpu().numpy()
+        assert np.all(np.diff(g, axis=-1) > 0)
+        for h in range(shape.n_kv_heads):
+            assert np.isin(g[0, h], cand[0, h]).all()
     layer.close()

@@ -7,7 +7,9 @@ library in the launch configuration the benchmark times:
 * GLM-4-9B-1M shape: batch 4, 1 048 576 tokens, 32 q / 2 KV heads, r = 48,
   K = 2048 (selection in 32 parts and a merge tree; attention in two head
   groups of 8);
-* the Llama-3.1-8B shape again with FP8 (E5M2) landmarks, rows of A and B.
+* the Llama-3.1-8B shape again with FP8 (E5M2) landmarks, rows of A and B;
+* the Llama-3.1-8B shape again with the value store in pinned host memory
+  (missed chunks' values gathered over PCIe).
 
 The oracle cannot afford the whole batch in float64, so it builds and decodes
 sampled batch elements from the very same bf16 bits the GPU consumed; every
@@ -33,14 +35,21 @@ def _slice_state(ex: dict, b: int) -> dict:
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,sampled,fmt", [("llama3_8b_122k", (0, 7), "bf16"), ("yi_9b_200k", (0,), "bf16"),
-                                              ("glm4_9b_1m", (3,), "bf16"), ("llama3_8b_122k", (5,), "e5m2")])
-def test_one_layer_sampled(name, sampled, fmt):
+@pytest.mark.parametrize("name,sampled,fmt,placement", [
+    ("llama3_8b_122k", (0, 7), "bf16", skv.SKV_VALUES_DEVICE), ("yi_9b_200k", (0,), "bf16", skv.SKV_VALUES_DEVICE),
+    ("glm4_9b_1m", (3,), "bf16", skv.SKV_VALUES_DEVICE), ("llama3_8b_122k", (5,), "e5m2", skv.SKV_VALUES_DEVICE),
+    ("llama3_8b_122k", (2,), "bf16", skv.SKV_VALUES_HOST)])
+def test_one_layer_sampled(name, sampled, fmt, placement):
     shape = synth.SHAPES[name].replace(landmark_format=fmt, a_format=fmt, b_format=fmt)
-    print(f"[fullsize] {shape}", flush=True)
+    print(f"[fullsize] {shape} placement {placement}", flush=True)
     k, v = synth.layer_cache_torch(shape, 0, 0, "cuda")
     q = synth.queries_torch(shape, k, 0, STEPS, 0)
-    layer = skv.Layer(shape, k, v)
+    if placement == skv.SKV_VALUES_HOST:   # the value store in pinned host memory (2 GB at this shape)
+        vh = torch.empty(v.shape, dtype=v.dtype, pin_memory=True)
+        vh.copy_(v)
+        del v
+        v = vh
+    layer = skv.Layer(shape, k, v, placement)
     ex = layer.export()
     outs, idss, stats = [], [], []
     for t in range(STEPS):
