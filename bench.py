@@ -196,6 +196,63 @@ def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> str:
     return "\n".join(lines)
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4          # 256 CUs of 4 SIMDs
+XCDS = 8                 # GRBM_GUI_ACTIVE per dispatch comes summed over the 8 XCDs
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def summarize_mfma(pmc_csv: str, stats_csv: str, command: str) -> str:
+    """Markdown summary of one rocprofv3 --pmc run with MFMA_COUNTERS (per-dispatch
+    means per kernel), with the kernels' mean durations from a kernel-trace run of
+    the same command: MFMA busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE
+    / XCDS x SIMDs) (the per-dispatch GRBM_GUI_ACTIVE is the sum of the XCDs' busy
+    cycles: about 8 x 2.3 cycles per ns on long kernels), bf16 MFMA rate =
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops / duration."""
+    vals = {}
+    with open(pmc_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            c = row.get("Counter_Name")
+            if c in MFMA_COUNTERS:
+                k = _short_kernel_name(row["Kernel_Name"])
+                vals.setdefault(k, {}).setdefault(c, []).append(float(row["Counter_Value"]))
+    dur = {}
+    with open(stats_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            dur[_short_kernel_name(row["Name"])] = float(row["AverageNs"]) / 1e3
+    lines = ["# MFMA counters per kernel launch: ShadowKV decode", "",
+             "Commands (repo root on the GPU box, `export TMPDIR=/tmp` first):", "", "```",
+             f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d /tmp/pmc_mfma -o pmc -- {command}",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/prof_mfma -o bench -- {command}",
+             "```", "",
+             f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} x {SIMDS} SIMDs), the "
+             f"dispatch's GRBM_GUI_ACTIVE being the sum over the {XCDS} XCDs; bf16 rate = "
+             f"SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / mean duration (kernel trace), against "
+             f"{MFMA_BF16_PEAK_TFLOPS:.0f} TFLOP/s dense bf16.", "",
+             "| kernel | dispatches | MFMA busy | bf16 MFMA GFLOP per launch | mean us | bf16 TFLOP/s | of peak |",
+             "|---|---|---|---|---|---|---|"]
+    blob = {}
+    for k in sorted(vals):
+        if not k.startswith("skv::"):
+            continue
+        v = {c: sum(x) / len(x) for c, x in vals[k].items()}
+        if not all(c in v for c in MFMA_COUNTERS):
+            continue
+        busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, v["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
+        gflop = v["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9
+        us = dur.get(k)
+        rate = gflop / (us * 1e-6) / 1e3 if us else None
+        n = len(vals[k]["GRBM_GUI_ACTIVE"])
+        lines.append(f"| `{k}` | {n} | {busy:.4f} | {gflop:.3f} | {us if us is not None else float('nan'):.2f} | "
+                     f"{rate if rate is not None else float('nan'):.1f} | "
+                     f"{(rate or 0) / MFMA_BF16_PEAK_TFLOPS:.4f} |")
+        blob[k] = {"mfma_busy": round(busy, 5), "bf16_gflop_per_launch": round(gflop, 4), "mean_us": us,
+                   "bf16_tflops": round(rate, 2) if rate else None}
+    lines += ["", "```json", json.dumps({"kernel_source_digest": kernel_source_digest(), "kernels": blob}, indent=1),
+              "```", ""]
+    return "\n".join(lines)
+
+
 def summarize_trace(stats_csv: str, command: str, shape=None) -> str:
     """Markdown table of the library's kernels from a rocprofv3 kernel_stats.csv,
     with the score kernel's rate at its algorithmic bytes per launch for `shape`
@@ -325,6 +382,8 @@ def main():
     ap.add_argument("--rebuild", choices=["auto", "fused", "separate", "overlap"], default="auto",
                     help="missed chunks rebuilt and attended in one launch with the rest of the attention "
                          "(fused; auto with values in HBM) or rebuilt by their own launch before it (separate)")
+    ap.add_argument("--select", choices=["auto", "full"], default="auto",
+                    help="top-K selection: the library's choice, or a pass over every candidate's score")
     ap.add_argument("--temporal", choices=["on", "off"], default="on",
                     help="temporal cache on (rebuild only the chunks missed against the previous step) or off "
                          "(rebuild every selected chunk; with the fused rebuild, no key slot cache at all)")
@@ -343,11 +402,16 @@ def main():
                     help="print the traffic summary of two rocprofv3 --pmc runs (no GPU needed)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="print the per-kernel summary of a rocprofv3 --kernel-trace --stats run (no GPU needed)")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "STATS_CSV", "COMMAND"),
+                    help="print the MFMA counter summary of a rocprofv3 --pmc run (no GPU needed)")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
 
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters))
+        return 0
+    if args.summarize_mfma:
+        print(summarize_mfma(*args.summarize_mfma))
         return 0
     if args.summarize_trace:
         from sparse_kv_cache_decode_amd import synth
@@ -404,11 +468,12 @@ def main():
         tb = time.perf_counter()
         rb = skv.REBUILD_MODES[args.rebuild]
         tc = 1 if args.temporal == "on" else 0
+        sm = skv.SELECT_MODES[args.select]
         if new_mode is None:
-            layers.append(skv.Layer(shape, k_pre, v, placement, tc, rebuild_mode=rb))
+            layers.append(skv.Layer(shape, k_pre, v, placement, tc, rebuild_mode=rb, select_mode=sm))
         else:
             layers.append(skv.Layer(shape, k_pre, v, placement, tc, max_new_tokens=total, new_token_mode=new_mode,
-                                    rebuild_mode=rb))
+                                    rebuild_mode=rb, select_mode=sm))
         torch.cuda.synchronize()
         build_s.append(time.perf_counter() - tb)
         if new_mode is not None:
@@ -574,6 +639,7 @@ def main():
                         f"after the timed region",
         "launch": "one captured HIP graph per step (all layers), replayed" if graph is not None else "eager launches",
         "rebuild": args.rebuild if args.rebuild != "auto" else ("separate" if host else "fused"),
+        "select": args.select,
         "layer_us": round(layer_us, 2),
         "build_ms_per_layer": {"mean": round(1000.0 * sum(build_s[1:] or build_s) / len(build_s[1:] or build_s), 1),
                                "first": round(1000.0 * build_s[0], 1),

@@ -126,7 +126,8 @@ typedef int32_t skv_status;
                                   16-chunk tile first (from per-tile maxima of the
                                   logits), the K-th largest of those as a threshold,
                                   then the top-K among the chunks of the tiles that
-                                  reach it; a full pass otherwise                    */
+                                  reach it (one workgroup per KV head and batch
+                                  element, for K <= 512); a full pass otherwise     */
 #define SKV_SELECT_FULL 1      /* a pass over every candidate's score                */
 
 /*

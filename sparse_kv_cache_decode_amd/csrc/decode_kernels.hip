@@ -842,11 +842,19 @@ static size_t select2_lds_bytes(const DecodeArgs& a) {
 }
 
 // Workgroup size, tiles and level-2 items per thread of the two-level selection,
-// or 0 when it does not apply (more tiles per thread than 16, or LDS that would
-// not fit).  1024 threads: 256 (one wave per SIMD) made every block-wide step
-// cheaper but the per-thread loops longer, 20.8 against 15.2 us per pair at the
-// Llama-3.1-8B shape (phase stamps).
+// or 0 when it does not apply (a budget above kSelect2MaxTopK, more tiles per
+// thread than 16, or LDS that would not fit).  1024 threads: 256 (one wave per
+// SIMD) made every block-wide step cheaper but the per-thread loops longer, 20.8
+// against 15.2 us per pair at the Llama-3.1-8B shape (phase stamps).  The budget
+// bound: one workgroup per pair takes about 5 K hot candidates through level 2,
+// which at K = 1024 and 2048 (few pairs, long contexts) was three times slower
+// than the selection in parts over all candidates (182 against 60 us per layer
+// at the GLM-4-9B-1M shape); at K = 240 and 400 it was faster (17 against 20,
+// 22 against 27 us).
+constexpr int kSelect2MaxTopK = 512;
+
 int select2_shape(int n_ctiles_cap, int top_k, int res_words, int* nt, int* tpt, int* ipt) {
+  if (top_k > kSelect2MaxTopK) return 0;
   if ((size_t)(kHist + 32 + 5 * top_k + res_words + n_ctiles_cap) * sizeof(int) > (size_t)kSelLdsMax) return 0;
   for (int threads : {kSelThreads}) {
     const int t = (n_ctiles_cap + threads - 1) / threads;
@@ -1893,7 +1901,8 @@ hipError_t launch_attention_misses(const DecodeArgs& a, hipStream_t st) { return
 // slots that hit and the exact region (attend_split).  Miss tiles go first, the
 // empty ones (past a pair's misses) first of all, so the tiles with work start
 // at once and the attention workgroups fill in behind them.
-// Two workgroups per CU (the rebuild's registers plus the tile's values).
+// Three workgroups per CU: the tile's values and query are loaded after the
+// rebuild, not beside it.
 
 // Attention of a miss tile: its n_rows rebuilt keys in LDS (rows of kOutW bf16),
 // values vf loaded by this wave (rows w*32 + t*16 + 4lq + lr%4, clamped to the
@@ -1926,7 +1935,7 @@ __device__ __forceinline__ void attend_tile(const DecodeArgs& a, int n_rows, con
 }
 
 template <int C, int NSTEP, bool A8, bool B8, bool ATTEND>
-__global__ __launch_bounds__(256, ATTEND ? 2 : 3) void tail_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
   constexpr int kStage = rebuild_stage_bytes<NSTEP>() > (int)sizeof(AttnMerge) ? rebuild_stage_bytes<NSTEP>()
                                                                                 : (int)sizeof(AttnMerge);
@@ -1969,32 +1978,51 @@ __global__ __launch_bounds__(256, ATTEND ? 2 : 3) void tail_kernel(DecodeArgs a)
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  // q and this wave's values go out with the rebuild's operand loads and arrive
-  // while the keys are rebuilt
+  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage);
+  // q and this wave's values go out once the rebuild's accumulators are dead (held
+  // across the rebuild they cost the third workgroup per CU), and arrive while the
+  // keys are stored to their slots
   bf16x8 bq[4];
   u32x4 vf[2][4];
   const int ntok = max(0, min(32, n_rows - w * 32));
-  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage, [&] {
-    load_q(a, p, lr, lq, bq);
-    if (ntok > 0) {   // wave-uniform
+  load_q(a, p, lr, lq, bq);
+  if (ntok > 0) {   // wave-uniform
 #pragma unroll
-      for (int t = 0; t < 2; t++) {
-        const int row = w * 32 + min(t * 16 + 4 * lq + (lr & 3), ntok - 1);
-        const uint16_t* vp = chunk_values(a, p, b, h, mchunk[row / C]) + (row % C) * kHeadDim + (lr >> 2) * 8;
+    for (int t = 0; t < 2; t++) {
+      const int row = w * 32 + min(t * 16 + 4 * lq + (lr & 3), ntok - 1);
+      const uint16_t* vp = chunk_values(a, p, b, h, mchunk[row / C]) + (row % C) * kHeadDim + (lr >> 2) * 8;
 #pragma unroll
-        for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; t++)
-#pragma unroll
-        for (int c = 0; c < 4; c++) vf[t][c] = (u32x4){0u, 0u, 0u, 0u};
+      for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
     }
-  });
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) vf[t][c] = (u32x4){0u, 0u, 0u, 0u};
+  }
   const uint16_t* otile = reinterpret_cast<const uint16_t*>(stage);
   if (a.temporal) store_tile<C>(a, p, mslot, otile);   // kept for the next steps' hits
   attend_tile<C>(a, n_rows, otile, vf, bq,
                  a.attn_part + ((int64_t)p * a.n_part_att + a.n_split + T) * a.group * kPartStride, mg);
+}
+
+// k-steps per staged slice of the bf16 path: the whole of r = 160 in one slice
+// where the registers allow it.  Attending from the tile keeps the attention's
+// state beside the rebuild's, and three workgroups per CU (168 registers) hold
+// only with slices of 4 k-steps (2 at C = 4); the fourth k-step slice costs one
+// more LDS round, the second and third workgroup per CU take the ~580 miss
+// tiles of the Llama-3.1-8B shape in one round instead of two.
+template <int C, bool ATTEND>
+constexpr int tail_max_steps() {
+  return !ATTEND ? kMaxSteps : C == 4 ? 2 : 4;
+}
+
+template <int C, int NS, bool A8, bool ATTEND>
+static void launch_tail_s(const DecodeArgs& a, dim3 grid, int want, hipStream_t st) {
+  if constexpr (NS < tail_max_steps<C, ATTEND>()) {
+    if (want > NS) return launch_tail_s<C, NS + 1, A8, ATTEND>(a, grid, want, st);
+  }
+  tail_kernel<C, NS, A8, false, ATTEND><<<grid, 256, 0, st>>>(a);
 }
 
 template <int C, bool A8, bool ATTEND>
@@ -2003,13 +2031,7 @@ static hipError_t launch_tail_c(const DecodeArgs& a, dim3 grid, hipStream_t st) 
     tail_kernel<C, 1, A8, true, ATTEND><<<grid, 256, 0, st>>>(a);   // one k-step per iteration
     return hipGetLastError();
   }
-  switch (min(kMaxSteps, (a.rank + 31) / 32)) {
-    case 1: tail_kernel<C, 1, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
-    case 2: tail_kernel<C, 2, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
-    case 3: tail_kernel<C, 3, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
-    case 4: tail_kernel<C, 4, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
-    default: tail_kernel<C, kMaxSteps, A8, false, ATTEND><<<grid, 256, 0, st>>>(a); break;
-  }
+  launch_tail_s<C, 1, A8, ATTEND>(a, grid, (a.rank + 31) / 32, st);
   return hipGetLastError();
 }
 
