@@ -326,16 +326,28 @@ def measure_h2d_gbps(nbytes: int = 256 << 20, reps: int = 8) -> float:
 # ----------------------------------------------------------------------------
 
 
-def algorithmic_bytes(shape, misses_per_layer_step: float) -> dict:
-    """Bytes the method must move per layer-step (HBM-resident values)."""
+def algorithmic_bytes(shape, rebuilt_per_layer_step: float, fused: bool = False, temporal: bool = True) -> dict:
+    """Bytes the method must move per layer-step (HBM-resident values), given the
+    chunks rebuilt per layer-step (the misses with the temporal cache, every
+    selected chunk without it):
+    - score: the candidates' landmarks and the queries;
+    - rebuild: the rebuilt chunks' rows of A, B once per pair, and the rebuilt keys
+      written to their slots (kept for later hits, or handed to a separate attention
+      launch; a fused rebuild without the temporal cache writes none);
+    - attention: the values of every attended token, the keys of every attended
+      token that is read from memory (a fused rebuild attends its rebuilt keys where
+      it made them), and the output."""
     d, C, r = shape.head_dim, shape.chunk, shape.rank
     P = shape.pairs
     landmarks = P * shape.n_cand * d * FORMAT_BYTES[shape.landmark_format]
     q_bytes = shape.batch * shape.n_q_heads * d * 2
     out_bytes = shape.batch * shape.n_q_heads * d * 4
-    rebuild = misses_per_layer_step * C * (r * FORMAT_BYTES[shape.a_format] + d * 2) + \
+    slot_writes = rebuilt_per_layer_step * C * d * 2 if (temporal or not fused) else 0.0
+    rebuild = rebuilt_per_layer_step * C * r * FORMAT_BYTES[shape.a_format] + slot_writes + \
         P * r * d * FORMAT_BYTES[shape.b_format]
-    attn = P * shape.tokens_attended * d * 2 * 2
+    tokens = P * shape.tokens_attended
+    key_tokens = tokens - (rebuilt_per_layer_step * C if fused else 0.0)
+    attn = tokens * d * 2 + key_tokens * d * 2
     return {"score": landmarks + q_bytes, "rebuild": rebuild, "attention": attn + out_bytes,
             "total": landmarks + q_bytes + rebuild + attn + out_bytes}
 
@@ -544,7 +556,11 @@ def main():
     alpha_timed = hits / (shape.pairs * shape.top_k)
     # hits over steps 1.. of the warm-up and timed steps (device counters)
     alpha_all = sum(a["total_hits"] for a in after) / (L * shape.pairs * shape.top_k * (W + K - 1))
-    by = algorithmic_bytes(shape, misses)
+    # chunks rebuilt per layer-step: the misses, or every selected chunk without
+    # the temporal cache (whose hit / miss counters then stay at zero)
+    rebuilt = misses if args.temporal == "on" else float(shape.pairs * shape.top_k)
+    fused = (args.rebuild if args.rebuild != "auto" else ("separate" if host else "fused")) == "fused"
+    by = algorithmic_bytes(shape, rebuilt, fused=fused, temporal=args.temporal == "on")
 
     ms_per_step = ms_total / K
     tok_s = shape.batch * K / (ms_total / 1000.0)

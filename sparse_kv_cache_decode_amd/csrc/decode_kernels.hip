@@ -1097,20 +1097,19 @@ constexpr int rebuild_stage_bytes() {
 // into their slots.  Called by all 256 threads of a workgroup with mchunk in LDS
 // (written before a barrier) and `stage` an LDS buffer of
 // rebuild_stage_bytes<NSTEP>(); returns after a barrier, with the rows in place.
-// `pre` is called once the RoPE frequencies have arrived, before the operand
-// loads are issued (the fused tail issues its query and value loads there).
+// With `park` (an LDS buffer of kParkFloats floats), the RoPE angles are parked
+// there across the MFMAs instead of held in 12 registers per lane (the fused
+// tail's attention state otherwise costs it its single k-step slice).
 // A8: rows of A stored as FP8 E5M2 (r bytes per row) instead of bf16.  B8: B^T
 // stored as FP8 E5M2; its operand fragments (8 bytes per lane and column tile,
 // 20 KB per pair at r = 160, read by every wave from L2) are then loaded straight
 // into registers and widened to bf16, with one k-step per iteration, instead of
 // the staged direct-to-LDS slices of the bf16 path.
-struct NoPrefetch {
-  __device__ void operator()() const {}
-};
+constexpr int kParkFloats = 12 * 256;
 
-template <int C, int NSTEP, bool A8, bool B8, class Pre = NoPrefetch>
+template <int C, int NSTEP, bool A8, bool B8, bool PARK = false>
 __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const int* mchunk, u32x4* stage,
-                                             Pre pre = Pre()) {
+                                             float* park = nullptr) {
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int r = a.rank;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1147,9 +1146,14 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) ang[mt][nt] = rope_angle(pos0[mt], ffreq[nt]);
   }
-  // the caller's own loads go out here: after the frequencies (whose wait would
-  // otherwise also wait for them) and before the operand loads
-  pre();
+  if constexpr (PARK) {
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) {
+      park[nt * 256 + threadIdx.x] = ff[nt];
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) park[(4 + mt * 4 + nt) * 256 + threadIdx.x] = ang[mt][nt];
+    }
+  }
   f32x4 acc[2][8];
 #pragma unroll
   for (int mt = 0; mt < 2; mt++)
@@ -1216,6 +1220,14 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
   }
   }
   __syncthreads();
+  if constexpr (PARK) {
+#pragma unroll
+    for (int nt = 0; nt < 4; nt++) {
+      ff[nt] = park[nt * 256 + threadIdx.x];
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) ang[mt][nt] = park[(4 + mt * 4 + nt) * 256 + threadIdx.x];
+    }
+  }
   // epilogue: RoPE on (col, col + 64) pairs, bf16 rows staged in LDS
   uint16_t* otile = reinterpret_cast<uint16_t*>(stage);
 #pragma unroll
@@ -1902,7 +1914,7 @@ hipError_t launch_attention_misses(const DecodeArgs& a, hipStream_t st) { return
 // empty ones (past a pair's misses) first of all, so the tiles with work start
 // at once and the attention workgroups fill in behind them.
 // Three workgroups per CU: the tile's values and query are loaded after the
-// rebuild, not beside it.
+// rebuild, not beside it, and the RoPE angles wait in LDS across the MFMAs.
 
 // Attention of a miss tile: its n_rows rebuilt keys in LDS (rows of kOutW bf16),
 // values vf loaded by this wave (rows w*32 + t*16 + 4lq + lr%4, clamped to the
@@ -1940,6 +1952,7 @@ __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   constexpr int kStage = rebuild_stage_bytes<NSTEP>() > (int)sizeof(AttnMerge) ? rebuild_stage_bytes<NSTEP>()
                                                                                 : (int)sizeof(AttnMerge);
   __shared__ u32x4 stage[kStage / 16];
+  __shared__ float park[ATTEND ? kParkFloats : 1];
   __shared__ int mchunk[MPB], mslot[MPB];
   AttnMerge& mg = *reinterpret_cast<AttnMerge*>(stage);   // used once the stage is read
   const int P = a.batch * a.n_kv;
@@ -1978,7 +1991,7 @@ __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage);
+  rebuild_tile<C, NSTEP, A8, B8, true>(a, p, mchunk, stage, park);
   // q and this wave's values go out once the rebuild's accumulators are dead (held
   // across the rebuild they cost the third workgroup per CU), and arrive while the
   // keys are stored to their slots
@@ -2007,14 +2020,14 @@ __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
 }
 
 // k-steps per staged slice of the bf16 path: the whole of r = 160 in one slice
-// where the registers allow it.  Attending from the tile keeps the attention's
-// state beside the rebuild's, and three workgroups per CU (168 registers) hold
-// only with slices of 4 k-steps (2 at C = 4); the fourth k-step slice costs one
-// more LDS round, the second and third workgroup per CU take the ~580 miss
-// tiles of the Llama-3.1-8B shape in one round instead of two.
+// (one round of operand loads) where three workgroups per CU (168 registers)
+// still hold without spills.  With the RoPE angles parked in LDS that is every
+// chunk size but C = 4 with the tile attended, which takes slices of 3.  At the
+// Llama-3.1-8B shape: slices of 4 (two load rounds), 32.0 us per launch; one
+// slice, 30.4 us; two workgroups per CU (all operands in registers), 34.2 us.
 template <int C, bool ATTEND>
 constexpr int tail_max_steps() {
-  return !ATTEND ? kMaxSteps : C == 4 ? 2 : 4;
+  return ATTEND && C == 4 ? 3 : kMaxSteps;
 }
 
 template <int C, int NS, bool A8, bool ATTEND>

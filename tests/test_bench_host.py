@@ -37,7 +37,24 @@ def test_algorithmic_bytes_llama_shape():
     r8 = bench.algorithmic_bytes(s.replace(a_format="e5m2"), m)["rebuild"]
     assert r16 - r8 == m * s.chunk * s.rank
     # attention: K and V of every attended token
-    assert by["attention"] == s.pairs * s.tokens_attended * s.head_dim * 4 + s.batch * s.n_q_heads * s.head_dim * 4
+    out = s.batch * s.n_q_heads * s.head_dim * 4
+    assert by["attention"] == s.pairs * s.tokens_attended * s.head_dim * 4 + out
+    # rebuilt keys go to their slots (A rows + key per token), and B once per pair
+    assert bench.algorithmic_bytes(s, m)["rebuild"] == m * s.chunk * (s.rank * 2 + s.head_dim * 2) + \
+        s.pairs * s.rank * s.head_dim * 2
+    # a fused rebuild attends the keys it rebuilt where it made them: those keys are
+    # not read back; without the temporal cache it stores none either
+    f = bench.algorithmic_bytes(s, m, fused=True)
+    assert by_attn_keys_saved(bench.algorithmic_bytes(s, m), f) == m * s.chunk * s.head_dim * 2
+    assert f["rebuild"] == bench.algorithmic_bytes(s, m)["rebuild"]
+    every = s.pairs * s.top_k
+    f3 = bench.algorithmic_bytes(s, every, fused=True, temporal=False)
+    assert f3["rebuild"] == every * s.chunk * s.rank * 2 + s.pairs * s.rank * s.head_dim * 2
+    assert f3["attention"] == s.pairs * s.tokens_attended * s.head_dim * 4 - every * s.chunk * s.head_dim * 2 + out
+
+
+def by_attn_keys_saved(plain, fused):
+    return plain["attention"] - fused["attention"]
 
 
 def _counter_csv(path, counter, rows):
