@@ -179,7 +179,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, command: str) -> str:
             "calibration_bytes": CALIB_BYTES, "fetch_factor": round(f_fac, 4),
             "write_factor": round(w_fac, 4), "kernels": kernels}
     lines = ["# HBM traffic per kernel launch: ShadowKV decode, Llama-3.1-8B shape (122 880 tokens, batch 8)",
-             "", "Commands (repo root on the GPU box, `export TMPDIR=/tmp` first):", "", "```"]
+             "", "Commands (repository root on the MI355X host, `export TMPDIR=/tmp` first):", "", "```"]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         lines.append(f"rocprofv3 --pmc {c} --output-format csv -d /tmp/pmc_{c.lower()} -o pmc -- {command}")
     lines += ["```", "",
@@ -221,7 +221,7 @@ def summarize_mfma(pmc_csv: str, stats_csv: str, command: str) -> str:
         for row in csv.DictReader(f):
             dur[_short_kernel_name(row["Name"])] = float(row["AverageNs"]) / 1e3
     lines = ["# MFMA counters per kernel launch: ShadowKV decode", "",
-             "Commands (repo root on the GPU box, `export TMPDIR=/tmp` first):", "", "```",
+             "Commands (repository root on the MI355X host, `export TMPDIR=/tmp` first):", "", "```",
              f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d /tmp/pmc_mfma -o pmc -- {command}",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/prof_mfma -o bench -- {command}",
              "```", "",
@@ -269,7 +269,7 @@ def summarize_trace(stats_csv: str, command: str, shape=None) -> str:
     rows.sort(key=lambda r: -r[5])
     lines = [f"# Kernel timing: ShadowKV decode, {shape.name} (S = {shape.seq_len}, batch {shape.batch}, "
              f"G = {shape.group}, C = {shape.chunk}, K = {shape.top_k}, {shape.layers} layers)", "",
-             "Command (repo root on the GPU box, `export TMPDIR=/tmp` first):", "", "```",
+             "Command (repository root on the MI355X host, `export TMPDIR=/tmp` first):", "", "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d /tmp/prof_bench -o bench -- {command}",
              "```", "",
              "Per-kernel summary from `bench_kernel_stats.csv` (library kernels only). The build kernels run "

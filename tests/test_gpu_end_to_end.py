@@ -3,7 +3,7 @@ build and decode of the same seeded bf16 inputs.  Nothing the GPU computed is
 handed to the oracle: the oracle factorises, builds landmarks and outliers, and
 decodes by itself, in float64.
 
-Bars (the spec rule): selected chunk ids bit-exact except chunks whose
+Bars: selected chunk ids bit-exact except chunks whose
 oracle score lies within 1e-3 relative of the K-th score; outputs within
 max |err| <= 2e-2 and relative L2 <= 5e-3; build state as check_build states it,
 with every landmark value and every exact outlier / window key equal to the
