@@ -403,7 +403,7 @@ def main():
                     help="replay each timed step (all layers) as one captured HIP graph; off: launch eagerly")
     ap.add_argument("--phase-steps", type=int, default=16,
                     help="eager steps after the timed region that record per-phase events on sampled layers")
-    ap.add_argument("--phase-every", type=int, default=16,
+    ap.add_argument("--phase-every", type=int, default=1,
                     help="record per-phase HIP events on every n-th layer during the phase-timing steps "
                          "(an event record between kernels costs a few microseconds)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -651,8 +651,9 @@ def main():
                           "meets_target": step_gbps / HBM_PEAK_GBPS >= 0.60},
         "phase_rates_GBps": phase_rates(by, phase_avg_us),
         "phase_us_per_layer": {p: round(v, 2) for p, v in phase_avg_us.items()},
-        "phase_timing": f"HIP events around each phase on the decode stream, layers {sampled}, {PH} eager steps "
-                        f"after the timed region",
+        "phase_timing": f"score: the kernel's own start and end, recorded into HIP events by its launch "
+                        f"(hipExtLaunchKernel); the other phases: HIP events between launches on the decode stream; "
+                        f"layers {sampled}, {PH} eager steps after the timed region",
         "launch": "one captured HIP graph per step (all layers), replayed" if graph is not None else "eager launches",
         "rebuild": args.rebuild if args.rebuild != "auto" else ("separate" if host else "fused"),
         "select": args.select,

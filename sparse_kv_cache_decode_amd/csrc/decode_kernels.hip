@@ -21,6 +21,8 @@
 // Workgroups never wait on one another inside a kernel: device-scope fences on
 // gfx950 write back and invalidate the whole L2, so every cross-workgroup
 // hand-off goes through a kernel boundary instead.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -237,15 +239,30 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(DecodeArgs a) {
   score_lse_out<G>(a, p, blk, w, col, kq, m_run, s_run, red);
 }
 
-hipError_t launch_score(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.nb_score, a.batch * a.n_kv);
+// With t0 / t1, the launch itself records the kernel's start and end in those
+// events (hipExtLaunchKernel: the dispatch's own timestamps, not event packets
+// around it, whose barriers add a few microseconds to the measured span).
+template <int G>
+static void launch_score_g(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
   const bool fp8 = a.landmark_format == SKV_FORMAT_FP8_E5M2;
+  if (t0 || t1) {
+    if (fp8) hipExtLaunchKernelGGL(score_fp8_kernel<G>, grid, dim3(256), 0, st, t0, t1, 0u, a);
+    else hipExtLaunchKernelGGL(score_kernel<G>, grid, dim3(256), 0, st, t0, t1, 0u, a);
+  } else if (fp8) {
+    score_fp8_kernel<G><<<grid, 256, 0, st>>>(a);
+  } else {
+    score_kernel<G><<<grid, 256, 0, st>>>(a);
+  }
+}
+
+hipError_t launch_score(const DecodeArgs& a, hipStream_t st, hipEvent_t t0, hipEvent_t t1) {
+  const dim3 grid(a.nb_score, a.batch * a.n_kv);
   switch (a.group) {
-    case 1: fp8 ? score_fp8_kernel<1><<<grid, 256, 0, st>>>(a) : score_kernel<1><<<grid, 256, 0, st>>>(a); break;
-    case 2: fp8 ? score_fp8_kernel<2><<<grid, 256, 0, st>>>(a) : score_kernel<2><<<grid, 256, 0, st>>>(a); break;
-    case 4: fp8 ? score_fp8_kernel<4><<<grid, 256, 0, st>>>(a) : score_kernel<4><<<grid, 256, 0, st>>>(a); break;
-    case 8: fp8 ? score_fp8_kernel<8><<<grid, 256, 0, st>>>(a) : score_kernel<8><<<grid, 256, 0, st>>>(a); break;
-    case 16: fp8 ? score_fp8_kernel<16><<<grid, 256, 0, st>>>(a) : score_kernel<16><<<grid, 256, 0, st>>>(a); break;
+    case 1: launch_score_g<1>(a, grid, st, t0, t1); break;
+    case 2: launch_score_g<2>(a, grid, st, t0, t1); break;
+    case 4: launch_score_g<4>(a, grid, st, t0, t1); break;
+    case 8: launch_score_g<8>(a, grid, st, t0, t1); break;
+    case 16: launch_score_g<16>(a, grid, st, t0, t1); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

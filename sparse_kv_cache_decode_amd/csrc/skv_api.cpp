@@ -351,9 +351,8 @@ skv_status decode_enqueue(skv_layer* h, const uint16_t* q, float* out, int32_t* 
       HIP_TRY_H(launch_reset_cache(a, s));
       h->need_reset = false;
     }
-    if (ev) HIP_TRY_H(hipEventRecord(ev[0], s));
-    HIP_TRY_H(launch_score(a, s));
-    if (ev) HIP_TRY_H(hipEventRecord(ev[1], s));
+    // the score phase is the kernel's own start and end (recorded by its launch)
+    HIP_TRY_H(launch_score(a, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr));
     HIP_TRY_H(launch_select(a, s));
     if (ev) HIP_TRY_H(hipEventRecord(ev[2], s));
     if (h->rebuild != SKV_REBUILD_SEPARATE) {

@@ -151,7 +151,8 @@ hipError_t launch_fill_u16(uint16_t* p, size_t n, uint16_t value, hipStream_t st
 
 // ---- decode launchers (decode_kernels.hip)
 hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t st);
-hipError_t launch_score(const DecodeArgs& a, hipStream_t st);
+// t0 / t1 (optional): events that receive the kernel's own start and end
+hipError_t launch_score(const DecodeArgs& a, hipStream_t st, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_select(const DecodeArgs& a, hipStream_t st);
 // Two-stage top-K: the candidates of a pair are cut into n_part parts whose
 // top-K are taken by separate workgroups (stage 1), then merged per pair (stage 2).

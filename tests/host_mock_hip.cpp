@@ -324,7 +324,11 @@ int select2_shape(int, int, int, int* nt, int* tpt, int* ipt) {
 }
 int attn_units_per_wave(int chunk) { return 64 / chunk; }
 hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t) { return decode_stub(a, false); }
-hipError_t launch_score(const DecodeArgs& a, hipStream_t) { return decode_stub(a); }
+hipError_t launch_score(const DecodeArgs& a, hipStream_t, hipEvent_t t0, hipEvent_t t1) {
+  if (t0) (void)hipEventRecord(t0, nullptr);
+  if (t1) (void)hipEventRecord(t1, nullptr);
+  return decode_stub(a);
+}
 hipError_t launch_select(const DecodeArgs& a, hipStream_t) { return decode_stub(a); }
 hipError_t launch_rebuild(const DecodeArgs& a, hipStream_t) { return decode_stub(a); }
 hipError_t launch_value_gather(const DecodeArgs& a, hipStream_t) { return decode_stub(a); }
