@@ -7,14 +7,20 @@
 //                 with the G query heads of its KV head; the d = 128 contraction
 //                 runs on MFMA 16x16x32 bf16 (16 landmarks x 16 head columns per
 //                 tile, fp32 accumulation) so the vector ALUs only run the softmax
-//                 epilogue.  Writes fp32 logits and per-head log-sum-exp partials.
+//                 epilogue.  Writes fp32 logits, per-head log-sum-exp partials
+//                 and the largest logit of every 16-candidate tile and head.
 //  select       : one workgroup per (batch, KV head) pair combines the LSE, forms
 //                 the chunk score max_g(l_g - LSE_g) (log of the group max of the
-//                 softmax probabilities), selects the top-K chunks with a radix
-//                 select in LDS and runs the temporal-cache index scan (hits,
-//                 misses, slot assignment).
-//  rebuild      : keys of the missed chunks, RoPE(Gather(A, I_miss) B), as bf16
-//                 MFMA 16x16x32 tiles with the rotation fused into the epilogue.
+//                 softmax probabilities), selects the top-K chunks with radix
+//                 selects in LDS (first over the tiles' maxima, then over the
+//                 chunks of the tiles that can hold a selected chunk; or over
+//                 every chunk, in parts for long contexts) and runs the
+//                 temporal-cache index scan (hits, misses, slot assignment).
+//  tail         : one launch that rebuilds the keys of the missed chunks,
+//                 RoPE(Gather(A, I_miss) B), as bf16 MFMA 16x16x32 tiles with the
+//                 rotation in the epilogue, and attends them from LDS, while its
+//                 other workgroups attend the outliers, the slots that hit and
+//                 the window (rebuild and attention are also separate kernels).
 //  value_gather : missed chunks' values from pinned host memory (side stream).
 //  attention    : split-K flash-decode over [outliers; selected; window] with an
 //                 online softmax in fp32, then a per-(pair, head) merge of splits.
@@ -292,13 +298,14 @@ hipError_t launch_score(const DecodeArgs& a, hipStream_t st, hipEvent_t t0, hipE
 constexpr int kSelThreads = 1024;
 constexpr int kHist = 2048 + kTopkSmall;
 
-__device__ __forceinline__ bool sorted_contains(const int* v, int n, int x) {
+// position of x in the ascending v[0, n), or -1
+__device__ __forceinline__ int sorted_find(const int* v, int n, int x) {
   int lo = 0, hi = n;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (v[mid] < x) lo = mid + 1; else hi = mid;
   }
-  return lo < n && v[lo] == x;
+  return lo < n && v[lo] == x ? lo : -1;
 }
 
 void select_partition(int n_cand, int top_k, int group, int pairs, int* n_part, int* part_size) {
@@ -401,10 +408,11 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
   int n_free = 0, n_miss = 0;
   for (int t0 = 0; t0 < K; t0 += NT) {
     const int s = t0 + threadIdx.x;
-    int fr = 0, ms = 0;
+    int fr = 0, ms = 0, at = -1;   // at: where the slot's chunk sits in the selection
     if (s < K) {
       const int old = scl[s];
-      fr = !(has_prev && old >= 0 && sorted_contains(sel, K, old));
+      if (has_prev && old >= 0) at = sorted_find(sel, K, old);
+      fr = at < 0;
       const int ci = sel[s];
       ms = !(has_prev && ((resl[ci >> 5] >> (ci & 31)) & 1u));
     }
@@ -412,8 +420,13 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
     const int ex = block_exclusive_scan<NT>(fr | (ms << 16), sh, &tot);
     if (fr) freel[n_free + (ex & 0xffff)] = s;
     if (ms) missp[n_miss + (ex >> 16)] = s;
-    // a slot that keeps its chunk is a hit: listed in ascending slot order
-    if (s < K && !fr) a.hit_slot[(int64_t)p * K + s - n_free - (ex & 0xffff)] = s;
+    // a slot that keeps its chunk is a hit: listed in ascending slot order, with
+    // its chunk id (from the selection, written before the scan's barriers)
+    if (s < K && !fr) {
+      const int64_t hi = (int64_t)p * K + s - n_free - (ex & 0xffff);
+      a.hit_slot[hi] = s;
+      a.hit_chunk[hi] = selch[at];
+    }
     n_free += tot & 0xffff;
     n_miss += tot >> 16;
   }
@@ -1779,9 +1792,11 @@ __device__ __forceinline__ void attend_split(const DecodeArgs& a, int p, int spl
     if (lane < uw1 - uw0) {
       const int sidx = uw0 + lane - O;
       if (sidx >= 0 && sidx < ns) {
-        my_slot = MISSES ? a.miss_slot[(int64_t)p * K + sidx]
-                         : (a.rebuild_fused ? a.hit_slot[(int64_t)p * K + sidx] : sidx);
-        my_ch = max(a.slot_chunk[(int64_t)p * K + my_slot], 0);
+        // the chunk id comes from the list that gives the slot (not through it),
+        // so the value loads wait for one dependent load, not two
+        const int64_t li = (int64_t)p * K + sidx;
+        my_slot = MISSES ? a.miss_slot[li] : (a.rebuild_fused ? a.hit_slot[li] : sidx);
+        my_ch = max(MISSES ? a.miss_chunk[li] : (a.rebuild_fused ? a.hit_chunk[li] : a.slot_chunk[li]), 0);
       }
     }
     // q first (every tile needs it; vector-memory loads complete in issue order),
@@ -1979,7 +1994,8 @@ __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   // work start right behind them; the attention splits follow.  Dispatching the
   // two kinds interleaved (tile s and split s of every pair, stage by stage) was
   // slower, 34 against 31 us per launch at the Llama-3.1-8B shape: the tiles
-  // (two per CU) still held the slots and the splits waited behind them.
+  // still held the slots and the splits waited behind them; dispatching every
+  // split first, so that the tiles start behind them, took 37.5 against 32 us.
   const int bid = blockIdx.x;
   if (bid >= P * n_tiles) {
     const int x = bid - P * n_tiles;

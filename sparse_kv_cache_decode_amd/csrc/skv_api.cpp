@@ -98,7 +98,7 @@ struct skv_layer {
            *key_new = nullptr, *val_new = nullptr;
   int32_t *cand_map = nullptr, *outlier_ids = nullptr, *slot_cand = nullptr, *slot_chunk = nullptr,
           *miss_slot = nullptr, *miss_chunk = nullptr, *miss_cand = nullptr, *free_slot = nullptr,
-          *hit_slot = nullptr,
+          *hit_slot = nullptr, *hit_chunk = nullptr,
           *n_miss = nullptr, *hits_last = nullptr;
   uint32_t *resident = nullptr, *keys = nullptr;
   long long *hits_total = nullptr, *miss_total = nullptr;
@@ -298,6 +298,7 @@ DecodeArgs decode_args(skv_layer* h) {
   a.miss_cand = h->miss_cand;
   a.free_slot = h->free_slot;
   a.hit_slot = h->hit_slot;
+  a.hit_chunk = h->hit_chunk;
   a.n_miss = h->n_miss;
   a.hits_last = h->hits_last;
   a.hits_total = h->hits_total;
@@ -505,6 +506,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const size_t oMca = cv.take<int32_t>((size_t)P * K);
   const size_t oFs = cv.take<int32_t>((size_t)P * K);
   const size_t oHs = cv.take<int32_t>((size_t)P * K);
+  const size_t oHc = cv.take<int32_t>((size_t)P * K);
   const size_t oNm = cv.take<int32_t>(P);
   const size_t oHl = cv.take<int32_t>(P);
   const size_t oRes = cv.take<uint32_t>((size_t)P * h->res_words);
@@ -594,6 +596,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     h->miss_cand = (int32_t*)(base + oMca);
     h->free_slot = (int32_t*)(base + oFs);
     h->hit_slot = (int32_t*)(base + oHs);
+    h->hit_chunk = (int32_t*)(base + oHc);
     h->n_miss = (int32_t*)(base + oNm);
     h->hits_last = (int32_t*)(base + oHl);
     h->resident = (uint32_t*)(base + oRes);

@@ -63,6 +63,7 @@ struct DecodeArgs {
   int32_t* miss_chunk;        // [P][K]
   int32_t* miss_cand;         // [P][K]
   int32_t* hit_slot;          // [P][K] slots that kept their chunk this step, ascending (K - n_miss)
+  int32_t* hit_chunk;         // [P][K] the chunk id each of those slots holds
   int32_t* free_slot;         // [P][K]
   int32_t* n_miss;            // [P]
   int32_t* hits_last;         // [P]

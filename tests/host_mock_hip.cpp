@@ -191,7 +191,7 @@ void check_decode(const DecodeArgs& a, bool step_io = true) {
   CHECK(inside(a.key_slots, P * K * C * d * 2));
   CHECK(inside(a.slot_cand, P * K * 4) && inside(a.slot_chunk, P * K * 4));
   CHECK(inside(a.miss_slot, P * K * 4) && inside(a.miss_chunk, P * K * 4) && inside(a.miss_cand, P * K * 4));
-  CHECK(inside(a.hit_slot, P * K * 4) && inside(a.free_slot, P * K * 4));
+  CHECK(inside(a.hit_slot, P * K * 4) && inside(a.hit_chunk, P * K * 4) && inside(a.free_slot, P * K * 4));
   CHECK(inside(a.n_miss, P * 4) && inside(a.hits_last, P * 4));
   CHECK(inside(a.hits_total, P * 8) && inside(a.miss_total, P * 8));
   CHECK(inside(a.resident, P * a.res_words * 4));
