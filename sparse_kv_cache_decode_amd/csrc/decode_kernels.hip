@@ -848,7 +848,9 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
     }
     // the keys that pass lie in [beta, the largest tile key]; a version that
     // ranked each passing key against all others (one per thread, from LDS)
-    // took 18.7 us per pair at the Llama-3.1-8B shape against 3.6 us for this
+    // took 18.7 us per pair at the Llama-3.1-8B shape against 3.6 us for this.
+    // Loading the hot candidates' chunk ids here (so that the index scan need
+    // not look up the selected ones) made the launch slower, 18.9 against 16.8 us.
     block_topk_reg<NT, IPT * 4>(key, vmask, K, beta, hi1, hist, sh, true, [&](int pos, int e) {
       const int item = i0 + e / 4;
       sel[pos] = hot[item >> 2] * 16 + (item & 3) * 4 + (e & 3);
@@ -886,18 +888,16 @@ constexpr int kSelect2MaxTopK = 512;
 int select2_shape(int n_ctiles_cap, int top_k, int res_words, int* nt, int* tpt, int* ipt) {
   if (top_k > kSelect2MaxTopK) return 0;
   if ((size_t)(kHist + 32 + 5 * top_k + res_words + n_ctiles_cap) * sizeof(int) > (size_t)kSelLdsMax) return 0;
-  for (int threads : {kSelThreads}) {
-    const int t = (n_ctiles_cap + threads - 1) / threads;
-    // hot tiles are about K (more only on equal tile keys): room for 1.25 K, at
-    // most 8 items (32 keys) per thread, past which the registers spill
-    const int need = (5 * top_k + threads - 1) / threads;   // 4 items per tile
-    if (t > 16 || (threads == 256 && need > 8)) continue;
-    *nt = threads;
-    *tpt = t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 16;
-    *ipt = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
-    return 1;
-  }
-  return 0;
+  const int threads = kSelThreads;
+  const int t = (n_ctiles_cap + threads - 1) / threads;
+  // hot tiles are about K (more only on equal tile keys): room for 1.25 K, 4
+  // candidates per item, at most 4 items per thread (K <= 512)
+  const int need = (5 * top_k + threads - 1) / threads;
+  if (t > 16 || need > 4) return 0;
+  *nt = threads;
+  *tpt = t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : t <= 8 ? 8 : 16;
+  *ipt = need <= 1 ? 1 : need <= 2 ? 2 : 4;
+  return 1;
 }
 
 template <int G, int NT, int TPT, int IPT>
@@ -917,8 +917,7 @@ static hipError_t launch_select2_t(const DecodeArgs& a, hipStream_t st) {
   switch (a.sel_ipt) {
     case 1: return launch_select2_i<G, NT, TPT, 1>(a, st);
     case 2: return launch_select2_i<G, NT, TPT, 2>(a, st);
-    case 4: return launch_select2_i<G, NT, TPT, 4>(a, st);
-    default: return launch_select2_i<G, NT, TPT, 8>(a, st);
+    default: return launch_select2_i<G, NT, TPT, 4>(a, st);
   }
 }
 
@@ -935,7 +934,7 @@ static hipError_t launch_select2_n(const DecodeArgs& a, hipStream_t st) {
 
 template <int G>
 static hipError_t launch_select2_g(const DecodeArgs& a, hipStream_t st) {
-  return a.sel_nt == 256 ? launch_select2_n<G, 256>(a, st) : launch_select2_n<G, kSelThreads>(a, st);
+  return launch_select2_n<G, kSelThreads>(a, st);
 }
 
 template <int G, int PT>
