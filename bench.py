@@ -253,6 +253,57 @@ def summarize_mfma(pmc_csv: str, stats_csv: str, command: str) -> str:
     return "\n".join(lines)
 
 
+def summarize_overlap(trace_csv: str, command: str) -> str:
+    """Markdown summary of how the host-value gather (side stream) overlaps the
+    main stream's kernels, from a rocprofv3 --kernel-trace kernel_trace.csv: per
+    decode step and layer, the gather's span against the rebuild that runs beside
+    it and the attention that waits for it."""
+    rows = []
+    with open(trace_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            name = _short_kernel_name(row["Kernel_Name"])
+            if name.startswith("skv::"):
+                rows.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]), name))
+    rows.sort()
+    spans = []   # (gather, rebuild, attention) per step: the gather and the main-stream kernels around it
+    last_rebuild = None
+    pending = None
+    for st, en, name in rows:
+        if name.startswith("skv::rebuild_kernel"):
+            last_rebuild = (st, en)
+            if pending is not None and pending[2] is None:
+                pending[2] = (st, en)
+        elif name == "skv::value_gather_kernel":
+            pending = [(st, en), None, None]
+            if last_rebuild and last_rebuild[1] > st:
+                pending[2] = last_rebuild
+        elif name.startswith("skv::attn_kernel") and pending is not None:
+            pending[1] = (st, en)
+            if pending[2] is not None:
+                spans.append(tuple(pending))
+            pending = None
+    if not spans:
+        return "no gather / rebuild / attention triples found\n"
+    ov, gap, gat, reb = [], [], [], []
+    for (gs, ge), (as_, ae), (rs, re) in spans:
+        gat.append((ge - gs) / 1e3)
+        reb.append((re - rs) / 1e3)
+        ov.append(max(0, min(ge, re) - max(gs, rs)) / 1e3)
+        gap.append((as_ - ge) / 1e3)
+    med = lambda v: sorted(v)[len(v) // 2]
+    lines = ["# Side-stream overlap: host-value gather beside the key rebuild (Llama-3.1-8B shape, values in pinned host memory)",
+             "", "Command (repository root on the MI355X host, `export TMPDIR=/tmp` first):", "", "```",
+             f"rocprofv3 --kernel-trace --output-format csv -d /tmp/trace_overlap -o bench -- {command}", "```", "",
+             "From `bench_kernel_trace.csv`: for every decode step of every layer, the zero-copy gather of the missed",
+             "chunks' values (`value_gather_kernel`, side stream) against the key rebuild of the same step",
+             "(`rebuild_kernel`, decode stream) and the attention (`attn_kernel`), which waits for the gather.", "",
+             f"| steps x layers | gather us (median) | rebuild us (median) | rebuild time inside the gather (median) | attention start after gather end, us (median) |",
+             "|---|---|---|---|---|",
+             f"| {len(spans)} | {med(gat):.1f} | {med(reb):.1f} | {med(ov):.1f} ({100 * med(ov) / max(1e-9, med(reb)):.0f} % of the rebuild) | {med(gap):.1f} |",
+             ""]
+    return "\n".join(lines)
+
+
 def summarize_trace(stats_csv: str, command: str, shape=None) -> str:
     """Markdown table of the library's kernels from a rocprofv3 kernel_stats.csv,
     with the score kernel's rate at its algorithmic bytes per launch for `shape`
@@ -414,6 +465,8 @@ def main():
                     help="print the traffic summary of two rocprofv3 --pmc runs (no GPU needed)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="print the per-kernel summary of a rocprofv3 --kernel-trace --stats run (no GPU needed)")
+    ap.add_argument("--summarize-overlap", nargs=2, metavar=("TRACE_CSV", "COMMAND"),
+                    help="print the side-stream overlap of a rocprofv3 --kernel-trace run (no GPU needed)")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_CSV", "STATS_CSV", "COMMAND"),
                     help="print the MFMA counter summary of a rocprofv3 --pmc run (no GPU needed)")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
@@ -421,6 +474,9 @@ def main():
 
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters))
+        return 0
+    if args.summarize_overlap:
+        print(summarize_overlap(*args.summarize_overlap))
         return 0
     if args.summarize_mfma:
         print(summarize_mfma(*args.summarize_mfma))
