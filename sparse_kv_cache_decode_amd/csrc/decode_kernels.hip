@@ -1289,7 +1289,11 @@ __device__ __forceinline__ void store_tile(const DecodeArgs& a, int p, const int
     const int slot = mslot[m / C];
     if (slot < 0) continue;
     uint16_t* dst = a.key_slots + (((int64_t)p * a.top_k + slot) * C + (m % C)) * kHeadDim + piece * 8;
-    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&otile[m * kOutW + piece * 8]);
+    // non-temporal: the slots are read at the earliest by the next step's attention,
+    // long after these lines would have left the L2 (tail 29.4 -> 29.0 us at the
+    // Llama-3.1-8B shape)
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&otile[m * kOutW + piece * 8]),
+                                reinterpret_cast<u32x4*>(dst));
   }
 }
 
