@@ -323,9 +323,11 @@ skv_status skv_export_state(const skv_layer* h, const skv_state_host* dst);
 
 /*
  * Per-phase device timing.  With capacity > 0 the next `capacity` decode steps
- * record HIP events on the decode stream around each kernel (and on the side
- * stream around the host value gather); capacity 0 stops recording.  The events
- * add one marker per phase and no host synchronisation.
+ * record HIP events on the decode stream (and on the side stream around the host
+ * value gather); capacity 0 stops recording.  The score phase is the score
+ * kernel's own start and end, recorded by its launch (hipExtLaunchKernel); the
+ * other phases run from one event to the next, each recorded after its kernels.
+ * No host synchronisation.
  */
 #define SKV_PHASE_SCORE 0         /* landmark GEMV: logits + per-head LSE partials */
 #define SKV_PHASE_SELECT 1        /* LSE, chunk scores, top-K, index scan          */
