@@ -264,3 +264,27 @@ def test_equal_scores_take_lowest_chunks(select):
     q = torch.zeros((2, s.batch, s.n_q_heads, s.head_dim), dtype=torch.bfloat16)
     _run(s, steps=2, select=select, q=q)
 
+
+
+@pytest.mark.parametrize("top_k", [512, 513])
+def test_two_level_budget_limit(top_k):
+    """The two-level selection serves budgets up to 512 chunks, a full pass the
+    ones above: on either side of the limit both selection modes pick the same
+    chunks bit for bit, and the oracle agrees."""
+    shape = _small(batch=1, n_q_heads=8, n_kv_heads=2, seq_len=65536, rank=32, latent_rank=32, top_k=top_k,
+                   n_outlier=20)
+    k, v = synth.layer_cache_np(shape, 0, 0)
+    q = synth.queries_np(shape, k, 0, 3, 0)
+    ids = {}
+    for sel in (skv.SKV_SELECT_AUTO, skv.SKV_SELECT_FULL):
+        layer = skv.Layer(shape, k.cuda(), v.cuda(), select_mode=sel)
+        got = []
+        for t in range(3):
+            _, i = layer.decode(q[t].cuda())
+            torch.cuda.synchronize()
+            got.append(i.cpu().numpy())
+        layer.close()
+        ids[sel] = got
+    for t in range(3):
+        assert np.array_equal(ids[skv.SKV_SELECT_AUTO][t], ids[skv.SKV_SELECT_FULL][t]), t
+    _run(shape, steps=3)
