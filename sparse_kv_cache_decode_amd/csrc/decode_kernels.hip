@@ -1281,19 +1281,21 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
 
 // The rebuilt rows of a tile (in LDS, as rebuild_tile left them) into the key
 // slots mslot[] of their chunks (-1: none).  The caller orders the stores against
-// later readers.
-template <int C>
+// later readers.  NT: non-temporal stores, for keys read at the earliest by the
+// next step (the fused tail attends them from LDS), long after these lines would
+// have left the L2 (tail 29.4 -> 29.0 us at the Llama-3.1-8B shape); keys that
+// the next launch attends keep plain stores (non-temporal ones cost the separate
+// and overlapped modes 3 % and 1.5 % of the step).
+template <int C, bool NT = false>
 __device__ __forceinline__ void store_tile(const DecodeArgs& a, int p, const int* mslot, const uint16_t* otile) {
   for (int e = threadIdx.x; e < kRebuildRows * 16; e += 256) {
     const int m = e >> 4, piece = e & 15;
     const int slot = mslot[m / C];
     if (slot < 0) continue;
     uint16_t* dst = a.key_slots + (((int64_t)p * a.top_k + slot) * C + (m % C)) * kHeadDim + piece * 8;
-    // non-temporal: the slots are read at the earliest by the next step's attention,
-    // long after these lines would have left the L2 (tail 29.4 -> 29.0 us at the
-    // Llama-3.1-8B shape)
-    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&otile[m * kOutW + piece * 8]),
-                                reinterpret_cast<u32x4*>(dst));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(&otile[m * kOutW + piece * 8]);
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+    else *reinterpret_cast<u32x4*>(dst) = v;
   }
 }
 
@@ -2050,7 +2052,7 @@ __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
       for (int c = 0; c < 4; c++) vf[t][c] = (u32x4){0u, 0u, 0u, 0u};
   }
   const uint16_t* otile = reinterpret_cast<const uint16_t*>(stage);
-  if (a.temporal) store_tile<C>(a, p, mslot, otile);   // kept for the next steps' hits
+  if (a.temporal) store_tile<C, true>(a, p, mslot, otile);   // kept for the next steps' hits
   attend_tile<C>(a, n_rows, otile, vf, bq,
                  a.attn_part + ((int64_t)p * a.n_part_att + a.n_split + T) * a.group * kPartStride, mg);
 }
