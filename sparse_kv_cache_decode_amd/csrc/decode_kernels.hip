@@ -724,9 +724,25 @@ __device__ __forceinline__ uint32_t cand_key(const DecodeArgs& a, int p, int c, 
   return float_key(best - 1.0f);
 }
 
+template <int G, int C>
+__device__ void attend_static(const DecodeArgs& a, int p, int s, float* lds);
+
+// Workgroups P .. P + P * n_static - 1 of the launch attend to the units that do
+// not depend on the selection (attend_static), on CUs the selection leaves idle.
 template <int G, int NT, int TPT, int IPT>
 __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
   extern __shared__ int smem[];
+  if ((int)blockIdx.x >= a.batch * a.n_kv) {   // workgroup-uniform
+    static_assert(NT == kStaticWaves * 64, "one wave per static attention wave");
+    const int P = a.batch * a.n_kv, x = blockIdx.x - P;
+    float* lds = reinterpret_cast<float*>(smem);
+    switch (a.chunk) {
+      case 4: attend_static<G, 4>(a, x % P, x / P, lds); break;
+      case 8: attend_static<G, 8>(a, x % P, x / P, lds); break;
+      default: attend_static<G, 16>(a, x % P, x / P, lds); break;
+    }
+    return;
+  }
   const int K = a.top_k, RW = a.res_words, n_tiles = a.n_ctiles, n = a.n_cand;
   int* hist = smem;
   int* sh = smem + kHist;
@@ -873,6 +889,9 @@ static size_t select2_lds_bytes(const DecodeArgs& a) {
   return (size_t)(kHist + 32 + 5 * a.top_k + a.res_words + a.n_ctiles_cap) * sizeof(int);
 }
 
+// LDS of a static attention workgroup: every wave's o[G][d], m[G] and l[G]
+static size_t static_lds_bytes(int G) { return (size_t)kStaticWaves * G * (kHeadDim + 2) * sizeof(float); }
+
 // Workgroup size, tiles and level-2 items per thread of the two-level selection,
 // or 0 when it does not apply (a budget above kSelect2MaxTopK, more tiles per
 // thread than 16, or LDS that would not fit).  1024 threads: 256 (one wave per
@@ -908,7 +927,8 @@ static hipError_t launch_select2_i(const DecodeArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  select2_kernel<G, NT, TPT, IPT><<<a.batch * a.n_kv, NT, select2_lds_bytes(a), st>>>(a);
+  const size_t lds = std::max(select2_lds_bytes(a), a.n_static > 0 ? static_lds_bytes(G) : (size_t)0);
+  select2_kernel<G, NT, TPT, IPT><<<a.batch * a.n_kv * (1 + a.n_static), NT, lds, st>>>(a);
   return hipGetLastError();
 }
 
@@ -1764,10 +1784,12 @@ __device__ __forceinline__ void merge_waves(int G, int lane, float m, float l, c
 // pair's [outliers; selected-chunk units; exact region] (the exact region being
 // the window units and appended units not yet folded into the candidates; its
 // last unit may be partly filled: tokens past it are masked like a wave's tail).
-// With MISSES, the units are the slots of the step's misses alone (the overlapped
-// rebuild attends to them after their keys are stored) and the partial goes to
-// row n_split + split.  A split past the pair's units writes nothing (the merge
-// skips it).
+// With a.n_static > 0 (the outliers and the exact region attended in the
+// selection launch) the splits cover the selected-chunk units alone, and split s
+// writes row n_static + s.  With MISSES, the units are the slots of the step's
+// misses alone (the overlapped rebuild attends to them after their keys are
+// stored) and the partial goes to row tile_row0 + split.  A split past the
+// pair's units writes nothing (the merge skips it).
 template <int NT, int C, bool MISSES = false>
 __device__ __forceinline__ void attend_split(const DecodeArgs& a, int p, int split, AttnMerge& mg) {
   const int b = p / a.n_kv, h = p % a.n_kv;
@@ -1776,13 +1798,15 @@ __device__ __forceinline__ void attend_split(const DecodeArgs& a, int p, int spl
   const int K = a.top_k;
   const int O = MISSES ? 0 : a.n_outlier;
   const int ns = MISSES ? a.n_miss[p] : slot_units(a, p);
-  const int U = O + ns + (MISSES ? 0 : a.n_win_units + a.n_new_units - a.n_fold);
-  if (split * a.upw >= U) return;            // workgroup-uniform
+  const bool hits_only = !MISSES && a.n_static > 0;
+  const int u_lo = hits_only ? O : 0;        // first unit of split 0
+  const int U = O + ns + (MISSES || hits_only ? 0 : a.n_win_units + a.n_new_units - a.n_fold);
+  if (u_lo + split * a.upw >= U) return;     // workgroup-uniform
   const int per_wave = (a.upw + 3) / 4;
-  const int uw0 = min(U, split * a.upw + w * per_wave);
-  const int uw1 = min(min(U, split * a.upw + a.upw), uw0 + per_wave);
+  const int uw0 = min(U, u_lo + split * a.upw + w * per_wave);
+  const int uw1 = min(min(U, u_lo + split * a.upw + a.upw), uw0 + per_wave);
   // tokens in units [0, U)
-  const int valid = MISSES ? ns * C : (O + ns + a.n_win_units - a.n_fold) * C + a.n_new_tokens;
+  const int valid = MISSES || hits_only ? (O + ns) * C : (O + ns + a.n_win_units - a.n_fold) * C + a.n_new_tokens;
   const int ntok = max(0, min((uw1 - uw0) * C, valid - uw0 * C));
 
   float m = kNegBig, l = 0.f;   // head lr
@@ -1832,8 +1856,89 @@ __device__ __forceinline__ void attend_split(const DecodeArgs& a, int p, int spl
     }
     wave_attend<NT>(kf, vf, bq, ntok, a.scale * kLog2e, lane, m, l, o);
   }
-  const int row = MISSES ? a.n_split + split : split;
+  const int row = MISSES ? a.tile_row0 + split : hits_only ? a.n_static + split : split;
   merge_waves(a.group, lane, m, l, o, mg, a.attn_part + ((int64_t)p * a.n_part_att + row) * a.group * kPartStride);
+}
+
+// Static-unit attention workgroup s of pair p (kStaticWaves waves, in the
+// two-level selection launch): the pair's outlier units and exact region, which
+// do not depend on the step's selection, kStaticWaves * 32 / C units per
+// workgroup, 32 / C per wave; the waves' (m, l, o) merge through `lds`
+// (static_lds_bytes(G)) into partial row s.
+static_assert((size_t)kStaticWaves * kAttnMaxHeads * (kHeadDim + 2) * sizeof(float) <= (size_t)kSelLdsMax,
+              "static attention LDS");
+
+template <int G, int C>
+__device__ void attend_static(const DecodeArgs& a, int p, int s, float* lds) {
+  constexpr int NUW = kAttnTiles * 16 / C;
+  const int b = p / a.n_kv, h = p % a.n_kv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int O = a.n_outlier;
+  const int U = O + a.n_win_units + a.n_new_units - a.n_fold;   // the static units (none selected)
+  const int valid = (O + a.n_win_units - a.n_fold) * C + a.n_new_tokens;
+  const int u0 = min(U, (s * kStaticWaves + w) * NUW), u1 = min(U, u0 + NUW);
+  const int ntok = max(0, min((u1 - u0) * C, valid - u0 * C));
+  float m = kNegBig, l = 0.f;
+  f32x4 o[4][2];
+#pragma unroll
+  for (int c = 0; c < 4; c++)
+#pragma unroll
+    for (int e = 0; e < 2; e++) o[c][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (ntok > 0) {   // wave-uniform; loads as in attend_split (no slot units: ns = 0)
+    bf16x8 bq[4];
+    load_q(a, p, lr, lq, bq);
+    const int tlast = ntok - 1;
+    u32x4 kf[kAttnTiles][4], vf[kAttnTiles][4];
+#pragma unroll
+    for (int t = 0; t < kAttnTiles; t++) {
+      const int tk = min(t * 16 + lr, tlast);
+      const uint16_t* kp = unit_key<C>(a, p, u0 + tk / C, O, 0, 0) + (tk % C) * kHeadDim + lq * 8;
+#pragma unroll
+      for (int j = 0; j < 4; j++) kf[t][j] = *reinterpret_cast<const u32x4*>(kp + j * 32);
+      const int tv = min(t * 16 + 4 * lq + (lr & 3), tlast);
+      const uint16_t* vp = unit_value<C>(a, p, b, h, u0 + tv / C, O, 0, 0, 0) + (tv % C) * kHeadDim + (lr >> 2) * 8;
+#pragma unroll
+      for (int c = 0; c < 4; c++) vf[t][c] = *reinterpret_cast<const u32x4*>(vp + c * 32);
+    }
+    wave_attend<kAttnTiles>(kf, vf, bq, ntok, a.scale * kLog2e, lane, m, l, o);
+  }
+  // merge: wo[wave][head][d], then wm[wave][head], wl[wave][head]
+  float* wo = lds;
+  float* wm = lds + kStaticWaves * G * kHeadDim;
+  float* wl = wm + kStaticWaves * G;
+  if (lr < G) {
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      float* dst = wo + (w * G + lr) * kHeadDim + c * 32 + 8 * lq;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{o[c][0][0], o[c][1][0], o[c][0][1], o[c][1][1]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[c][0][2], o[c][1][2], o[c][0][3], o[c][1][3]};
+    }
+    if (lq == 0) {
+      wm[w * G + lr] = m;
+      wl[w * G + lr] = l;
+    }
+  }
+  __syncthreads();
+  float* part = a.attn_part + ((int64_t)p * a.n_part_att + s) * G * kPartStride;
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kStaticWaves * 64) {
+    const int g = idx / kHeadDim, dim = idx % kHeadDim;
+    float M = kNegBig;
+#pragma unroll
+    for (int ww = 0; ww < kStaticWaves; ww++) M = fmaxf(M, wm[ww * G + g]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kStaticWaves; ww++) {
+      const float c = __builtin_amdgcn_exp2f(wm[ww * G + g] - M);
+      num += wo[(ww * G + g) * kHeadDim + dim] * c;
+      den += wl[ww * G + g] * c;
+    }
+    part[g * kPartStride + dim] = num;
+    if (dim == 0) {
+      part[g * kPartStride + kHeadDim] = M;
+      part[g * kPartStride + kHeadDim + 1] = den;
+    }
+  }
 }
 
 template <int NT, int C, bool MISSES>
@@ -1848,7 +1953,7 @@ __global__ __launch_bounds__(256) void attn_kernel(DecodeArgs a) {
 // Merge the partials of one (pair, head) that hold tokens: the attention splits
 // [0, ns) and, when the misses are attended on their own (fused or overlapped
 // rebuild), the partials of their miss_part_units-unit groups [0, nt) (rows
-// n_split + t):  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// tile_row0 + t):  out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 // 512 threads: 32 lanes cover one partial row (4 dims each, 16-byte loads) and
 // the 16 row groups take every 16th partial, then sum their rows through LDS, so
 // a long list is read 16 rows at a time.
@@ -1865,14 +1970,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) 
   int ns = a.n_split, nt = 0;
   if (a.rebuild_fused) {
     const int nm = a.n_miss[p];
-    const int units = a.n_outlier + (a.top_k - nm) + a.n_win_units + a.n_new_units - a.n_fold;
-    ns = (units + a.upw - 1) / a.upw;
+    if (a.n_static > 0) {   // static rows, then the splits over the hits
+      ns = a.n_static + (a.top_k - nm + a.upw - 1) / a.upw;
+    } else {
+      const int units = a.n_outlier + (a.top_k - nm) + a.n_win_units + a.n_new_units - a.n_fold;
+      ns = (units + a.upw - 1) / a.upw;
+    }
     nt = (nm + a.miss_part_units - 1) / a.miss_part_units;
   }
   const int n = ns + nt;
   const int64_t stride = (int64_t)G * kPartStride;
   const float* base = a.attn_part + (int64_t)p * a.n_part_att * stride + g * kPartStride;
-  auto row = [&](int s) { return base + (int64_t)(s < ns ? s : a.n_split + (s - ns)) * stride; };
+  auto row = [&](int s) { return base + (int64_t)(s < ns ? s : a.tile_row0 + (s - ns)) * stride; };
   for (int s = threadIdx.x; s < n; s += kCombineThreads) cw[s] = row(s)[kHeadDim];
   __syncthreads();
   if (threadIdx.x < 64) {   // wave 0: partial weights 2^(m_s - M) and the denominator
@@ -2054,7 +2163,7 @@ __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   const uint16_t* otile = reinterpret_cast<const uint16_t*>(stage);
   if (a.temporal) store_tile<C, true>(a, p, mslot, otile);   // kept for the next steps' hits
   attend_tile<C>(a, n_rows, otile, vf, bq,
-                 a.attn_part + ((int64_t)p * a.n_part_att + a.n_split + T) * a.group * kPartStride, mg);
+                 a.attn_part + ((int64_t)p * a.n_part_att + a.tile_row0 + T) * a.group * kPartStride, mg);
 }
 
 // k-steps per staged slice of the bf16 path: the whole of r = 160 in one slice

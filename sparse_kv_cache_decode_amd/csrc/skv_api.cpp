@@ -309,6 +309,18 @@ DecodeArgs decode_args(skv_layer* h) {
   a.n_ctiles_cap = (h->cand_cap + 15) / 16;
   a.sel_two_level = c.select_mode != SKV_SELECT_FULL &&
                     select2_shape(a.n_ctiles_cap, c.top_k, h->res_words, &a.sel_nt, &a.sel_tpt, &a.sel_ipt);
+  // fused rebuild with the two-level selection: the units that do not depend on
+  // the selection (outliers, exact region) are attended inside the selection's
+  // launch, on the CUs its one workgroup per pair leaves idle
+  a.n_static = 0;
+  a.tile_row0 = a.n_split;
+  if (h->rebuild == SKV_REBUILD_FUSED && a.sel_two_level) {
+    const int static_units = c.n_outlier + a.n_win_units + a.n_new_units - h->n_fold;
+    const int per_wg = kStaticWaves * attn_units_per_wave(c.chunk);
+    a.n_static = (static_units + per_wg - 1) / per_wg;
+    // n_static + ceil(hits / upw) <= n_split + 1 (n_static <= ceil(static_units / upw))
+    if (a.n_static > 0) a.tile_row0 = a.n_split + 1;
+  }
   apply_transient(a, h->xs_layout, h->xs);
   return a;
 }
@@ -528,7 +540,8 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     const int n_split_max = (h->U + (c.max_new_tokens + C - 1) / C + h->upw - 1) / h->upw;
     // fused rebuild: one more partial per tile of kRebuildRows rows of misses
     const int mpb = kRebuildRows / C;
-    h->n_part_att = n_split_max + (h->rebuild == SKV_REBUILD_FUSED     ? (K + mpb - 1) / mpb
+    // (fused: one more row, for the selection launch's static partials; see decode_args)
+    h->n_part_att = n_split_max + (h->rebuild == SKV_REBUILD_FUSED     ? 1 + (K + mpb - 1) / mpb
                                    : h->rebuild == SKV_REBUILD_OVERLAP ? (K + h->upw - 1) / h->upw
                                                                        : 0);
     t.attn_part = tc.take<float>((size_t)P * h->n_part_att * G * kPartStride);

@@ -15,6 +15,7 @@ constexpr int kMaxPartials = kMaxSplits + 512;   // attention partials per pair 
 constexpr int kScoreRows = 128;          // candidate landmarks per score workgroup (bf16)
 constexpr int kScoreRows8 = 256;         // the same for FP8 landmarks (the same 32 KB)
 constexpr int kPartStride = kHeadDim + 4; // floats per attention partial row: o[d], m, l, 2 pad (16-B rows)
+constexpr int kStaticWaves = 16;          // waves of a static-unit attention workgroup (selection launch)
 constexpr int kRebuildRows = 128;        // key rows rebuilt per workgroup (128 / C missed chunks)
 
 // Everything a decode step touches, by value into the kernels.
@@ -33,6 +34,10 @@ struct DecodeArgs {
   int ncp;                    // logits row stride (n_cand rounded up to 4)
   int n_split, upw;           // attention workgroups per pair, units per workgroup
   int n_part_att;             // attention partial rows per pair (splits, then miss tiles when fused)
+  int n_static;               // >0: the outliers and the exact region are attended by n_static extra
+                              // workgroups per pair of the two-level selection launch (partial rows
+                              // [0, n_static)); the splits then cover the slots that hit alone
+  int tile_row0;              // partial row of miss tile (or miss split) 0
   int rebuild_fused;          // 1: misses attended apart from the hits (fused or overlapped rebuild)
   int miss_part_units;        // missed chunks per partial of theirs (a tile, or a split's units)
   int temporal, host_values;

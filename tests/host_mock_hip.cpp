@@ -181,6 +181,8 @@ hipError_t hipEventElapsedTime(float* ms, hipEvent_t a, hipEvent_t b) {
 
 namespace skv {
 
+int g_static_steps = 0;   // launches that saw static-unit attention in the selection launch
+
 void check_decode(const DecodeArgs& a, bool step_io = true) {
   const size_t P = (size_t)a.batch * a.n_kv, K = a.top_k, G = a.group, C = a.chunk, d = kHeadDim;
   const size_t lbytes = a.landmark_format == SKV_FORMAT_FP8_E5M2 ? 1 : 2;
@@ -203,7 +205,15 @@ void check_decode(const DecodeArgs& a, bool step_io = true) {
   CHECK(inside(a.tile_max, P * a.n_ctiles_cap * G * 4));
   CHECK(a.n_ctiles <= a.n_ctiles_cap && (size_t)a.n_ctiles * 16 >= (size_t)a.n_cand);
   CHECK(inside(a.part_keys, P * a.n_part * K * 4) && inside(a.part_idx, P * a.n_part * K * 4));
-  CHECK(a.n_part_att >= a.n_split);
+  CHECK(a.n_part_att >= a.n_split && a.tile_row0 >= a.n_split);
+  if (a.n_static > 0) {   // static rows, then the hit splits' rows, below the first miss row
+    g_static_steps++;
+    CHECK(a.rebuild_fused && a.sel_two_level);
+    CHECK(a.n_static + (K + a.upw - 1) / a.upw <= a.tile_row0);
+    const int static_units = a.n_outlier + a.n_win_units + a.n_new_units - a.n_fold;
+    CHECK(static_units > 0 && a.n_static * kStaticWaves * (32 / C) >= static_units);
+  }
+  if (a.rebuild_fused) CHECK(a.tile_row0 + (K + a.miss_part_units - 1) / a.miss_part_units <= a.n_part_att);
   CHECK(inside(a.attn_part, P * a.n_part_att * G * kPartStride * 4));
   if (step_io) CHECK(inside(a.out, (size_t)a.batch * a.n_kv * G * d * 4) && inside(a.chunk_ids, P * K * 4));
   CHECK(inside(a.k_out, P * a.n_outlier * C * d * 2) || a.n_outlier == 0);
@@ -318,11 +328,13 @@ void select_partition(int n_cand, int, int, int, int* n_part, int* part_size) {
   *n_part = 1;
   *part_size = n_cand;
 }
-int select2_shape(int, int, int, int* nt, int* tpt, int* ipt) {
-  *nt = *tpt = *ipt = 0;
-  return 0;
+int select2_shape(int, int top_k, int, int* nt, int* tpt, int* ipt) {
+  // the kernels' rule on the budget (two levels up to K = 512); the shape values only size launches
+  *nt = 1024;
+  *tpt = *ipt = 1;
+  return top_k <= 512;
 }
-int attn_units_per_wave(int chunk) { return 64 / chunk; }
+int attn_units_per_wave(int chunk) { return 32 / chunk; }   // two 16-token tiles per wave
 hipError_t launch_reset_cache(const DecodeArgs& a, hipStream_t) { return decode_stub(a, false); }
 hipError_t launch_score(const DecodeArgs& a, hipStream_t, hipEvent_t t0, hipEvent_t t1) {
   if (t0) (void)hipEventRecord(t0, nullptr);
@@ -588,6 +600,7 @@ int main() {
   c.max_new_tokens = 8;
   c.new_token_mode = SKV_NEW_LOWRANK;
   hip_failures(c);
-  std::printf("launches %d failures %d live blocks %zu\n", skv::g_launches, g_failures, g_blocks.size());
+  std::printf("launches %d failures %d live blocks %zu static-split launches %d\n", skv::g_launches, g_failures,
+              g_blocks.size(), skv::g_static_steps);
   return g_failures == 0 ? 0 : 1;
 }

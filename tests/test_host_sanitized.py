@@ -46,3 +46,4 @@ def test_host_code_under_sanitizers(tmp_path):
     print(r.stderr[-4000:])
     assert r.returncode == 0, r.stderr[-4000:]
     assert "failures 0 live blocks 0" in r.stdout
+    assert "static-split launches 0" not in r.stdout
