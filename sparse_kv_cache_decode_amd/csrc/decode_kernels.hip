@@ -399,20 +399,30 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
   int32_t* sch = a.slot_chunk + (int64_t)p * K;
   uint32_t* res = a.resident + (int64_t)p * RW;
   const int32_t* cmap = a.cand_map + (int64_t)p * a.cand_stride;
-  for (int i = threadIdx.x; i < K; i += NT) {
-    const int ch = cmap[sel[i]];
-    selch[i] = ch;
-    a.chunk_ids[(int64_t)p * K + i] = ch;
+  // chunk ids of this thread's selected candidates and of its slots' chunks (the
+  // ones they keep if they hit), loaded before the scan and used after it, so
+  // that their latency hides behind it; K <= 4 * NT
+  constexpr int kPer = 4;
+  static_assert(kMaxTopK <= kPer * NT, "selection entries per thread");
+  int my_sel[kPer], my_slot[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int i = threadIdx.x + j * NT;
+    if (i < K) {
+      my_sel[j] = cmap[sel[i]];
+      my_slot[j] = sch[i];
+    }
   }
   const bool has_prev = a.temporal && scl[0] >= 0;
   int n_free = 0, n_miss = 0;
-  for (int t0 = 0; t0 < K; t0 += NT) {
-    const int s = t0 + threadIdx.x;
-    int fr = 0, ms = 0, at = -1;   // at: where the slot's chunk sits in the selection
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    if (j * NT >= K) break;      // block-uniform
+    const int s = j * NT + threadIdx.x;
+    int fr = 0, ms = 0;
     if (s < K) {
       const int old = scl[s];
-      if (has_prev && old >= 0) at = sorted_find(sel, K, old);
-      fr = at < 0;
+      fr = !(has_prev && old >= 0 && sorted_find(sel, K, old) >= 0);
       const int ci = sel[s];
       ms = !(has_prev && ((resl[ci >> 5] >> (ci & 31)) & 1u));
     }
@@ -421,14 +431,22 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
     if (fr) freel[n_free + (ex & 0xffff)] = s;
     if (ms) missp[n_miss + (ex >> 16)] = s;
     // a slot that keeps its chunk is a hit: listed in ascending slot order, with
-    // its chunk id (from the selection, written before the scan's barriers)
+    // the chunk id it holds (slot_chunk[s] is the chunk of slot_cand[s])
     if (s < K && !fr) {
       const int64_t hi = (int64_t)p * K + s - n_free - (ex & 0xffff);
       a.hit_slot[hi] = s;
-      a.hit_chunk[hi] = selch[at];
+      a.hit_chunk[hi] = my_slot[j];
     }
     n_free += tot & 0xffff;
     n_miss += tot >> 16;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int i = threadIdx.x + j * NT;
+    if (i < K) {
+      selch[i] = my_sel[j];
+      a.chunk_ids[(int64_t)p * K + i] = my_sel[j];
+    }
   }
   __syncthreads();
   // n_free == n_miss: every missed chunk takes the next evicted slot.  The miss
