@@ -2226,7 +2226,10 @@ static hipError_t launch_tail_a(const DecodeArgs& a, dim3 grid, hipStream_t st) 
 hipError_t launch_tail(const DecodeArgs& a, bool attend_tiles, hipStream_t st) {
   if (a.group < 1 || a.group > kAttnMaxHeads) return hipErrorInvalidValue;
   const int P = a.batch * a.n_kv, mpb = kRebuildRows / a.chunk;
-  const dim3 grid(P * ((a.top_k + mpb - 1) / mpb) + P * a.n_split);
+  // with the static units attended in the selection launch, the splits cover at
+  // most the K selected chunks
+  const int n_split = a.n_static > 0 ? (a.top_k + a.upw - 1) / a.upw : a.n_split;
+  const dim3 grid(P * ((a.top_k + mpb - 1) / mpb) + P * n_split);
   const bool a8 = a.a_format == SKV_FORMAT_FP8_E5M2;
   if (attend_tiles) return a8 ? launch_tail_a<true, true>(a, grid, st) : launch_tail_a<false, true>(a, grid, st);
   return a8 ? launch_tail_a<true, false>(a, grid, st) : launch_tail_a<false, false>(a, grid, st);
