@@ -827,7 +827,7 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
       hi = max(hi, tk[e]);
     }
   }
-  block_range<NT>(lo, hi, sh);
+  block_range<NT, false>(lo, hi, sh);   // nothing has touched sh yet
   const uint32_t hi1 = hi;   // the pair's largest key
   uint32_t beta = 0u;   // every key passes when K exceeds the tile count
   if (K <= n_tiles) {
@@ -850,11 +850,13 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
   if (n_items <= NT * IPT) {
     const int i0 = threadIdx.x * IPT;
     uint32_t key[IPT * 4];
+    int cbs[IPT];   // first candidate of each item (kept for the emission)
     uint64_t vmask = 0;
 #pragma unroll
     for (int it = 0; it < IPT; it++) {
       const int item = min(i0 + it, n_items - 1);
       const int cb = hot[item >> 2] * 16 + (item & 3) * 4;
+      cbs[it] = cb;
       const int cl = min(cb, a.ncp - 4);     // past the candidates: re-read the last row's end, not counted
       // the G heads in groups of (at most) 4 loads
       constexpr int GB = G < 4 ? G : 4;
@@ -885,10 +887,8 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
     // took 18.7 us per pair at the Llama-3.1-8B shape against 3.6 us for this.
     // Loading the hot candidates' chunk ids here (so that the index scan need
     // not look up the selected ones) made the launch slower, 18.9 against 16.8 us.
-    block_topk_reg<NT, IPT * 4>(key, vmask, K, beta, hi1, hist, sh, true, [&](int pos, int e) {
-      const int item = i0 + e / 4;
-      sel[pos] = hot[item >> 2] * 16 + (item & 3) * 4 + (e & 3);
-    });
+    block_topk_reg<NT, IPT * 4>(key, vmask, K, beta, hi1, hist, sh, true,
+                                [&](int pos, int e) { sel[pos] = cbs[e / 4] + (e & 3); });
   } else {
     // many equal tile keys: the hot tiles' candidates from memory (candidates
     // past n_cand get key 0, below every real key, and are never taken)

@@ -8,13 +8,14 @@
 namespace skv {
 
 // Largest key range start: every thread passes its own partial min / max of the
-// keys it produced; block_range combines them (needs sh[32]).
-template <int NT>
+// keys it produced; block_range combines them (needs sh[32]).  SH_BUSY: sh may
+// still be read by another thread (wait for it before writing).
+template <int NT, bool SH_BUSY = true>
 __device__ __forceinline__ void block_range(uint32_t& lo, uint32_t& hi, int* sh) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   lo = wave_umin(lo);
   hi = wave_umax(hi);
-  __syncthreads();
+  if constexpr (SH_BUSY) __syncthreads();
   if (lane == 0) {
     sh[wid] = (int)lo;
     sh[16 + wid] = (int)hi;

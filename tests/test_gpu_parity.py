@@ -108,6 +108,21 @@ def _small(**kw):
     return synth.Shape(**base)
 
 
+@pytest.mark.parametrize("chunk", [4, 8, 16])
+def test_static_units_over_several_selection_workgroups(chunk):
+    """Fused rebuild with the two-level selection: the outlier chunks and the
+    window are attended by extra workgroups of the selection launch, each 16
+    waves of 32 tokens (16 * 32 / C units).  Here they need four such workgroups
+    per pair, the last one partly filled, and the outputs still match the
+    oracle."""
+    per_wg = 16 * 32 // chunk
+    shape = _small(chunk=chunk, seq_len=16384, n_outlier=3 * per_wg + 5, top_k=40, batch=2, n_q_heads=8,
+                   n_kv_heads=2)
+    static_units = shape.n_outlier + shape.window // chunk
+    assert 3 * per_wg < static_units <= 4 * per_wg
+    _run(shape, steps=3)
+
+
 def test_ragged_tiles_two_batches():
     # n_cand = 1021 - 5 - 4 = 1012: not a multiple of the 16/256-landmark tiles
     _run(_small(), steps=3)
