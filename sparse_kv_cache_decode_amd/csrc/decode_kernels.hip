@@ -827,12 +827,18 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
       hi = max(hi, tk[e]);
     }
   }
-  block_range<NT, false>(lo, hi, sh);   // nothing has touched sh yet
+  // (no barrier before: nothing has touched sh yet; none after: the selection's
+  // histogram barrier, or the one below, comes before the next write to sh)
+  block_range<NT, false, false>(lo, hi, sh);
   const uint32_t hi1 = hi;   // the pair's largest key
   uint32_t beta = 0u;   // every key passes when K exceeds the tile count
-  if (K <= n_tiles) {
+  if (K <= n_tiles) {   // block-uniform
     int kk;
-    beta = block_kth_reg<NT, TPT>(tk, prefix_mask(ntv), K, lo, hi, hist, sh, true, &kk);
+    // lean: its last reads of sh[0, 16) and of hist precede a barrier inside; the
+    // hot-tile scan below writes only sh[0, 16), and hist after a barrier
+    beta = block_kth_reg<NT, TPT, true>(tk, prefix_mask(ntv), K, lo, hi, hist, sh, true, &kk);
+  } else {
+    __syncthreads();
   }
   // hot tiles, compacted in ascending order
   int nh = 0;
@@ -887,8 +893,10 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
     // took 18.7 us per pair at the Llama-3.1-8B shape against 3.6 us for this.
     // Loading the hot candidates' chunk ids here (so that the index scan need
     // not look up the selected ones) made the launch slower, 18.9 against 16.8 us.
-    block_topk_reg<NT, IPT * 4>(key, vmask, K, beta, hi1, hist, sh, true,
-                                [&](int pos, int e) { sel[pos] = cbs[e / 4] + (e & 3); });
+    // lean: it ends with the barrier that publishes sel, before the index scan
+    // writes sh again
+    block_topk_reg<NT, IPT * 4, true>(key, vmask, K, beta, hi1, hist, sh, true,
+                                      [&](int pos, int e) { sel[pos] = cbs[e / 4] + (e & 3); });
   } else {
     // many equal tile keys: the hot tiles' candidates from memory (candidates
     // past n_cand get key 0, below every real key, and are never taken)

@@ -193,7 +193,9 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 // Exclusive prefix sum over a block of NT threads (NT multiple of 64, <= 1024).
 // `tmp` needs NT/64 ints of LDS.  Returns the exclusive prefix, writes the total.
-template <int NT>
+// TRAIL = false leaves out the closing barrier: the caller passes another barrier
+// before anything writes tmp again.
+template <int NT, bool TRAIL = true>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int x = wave_inclusive_sum(v);
@@ -206,7 +208,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
     if (w < wid) base += t;
     tot += t;
   }
-  __syncthreads();
+  if constexpr (TRAIL) __syncthreads();
   *total = tot;
   return base + x - v;
 }

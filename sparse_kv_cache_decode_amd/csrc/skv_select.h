@@ -9,8 +9,9 @@ namespace skv {
 
 // Largest key range start: every thread passes its own partial min / max of the
 // keys it produced; block_range combines them (needs sh[32]).  SH_BUSY: sh may
-// still be read by another thread (wait for it before writing).
-template <int NT, bool SH_BUSY = true>
+// still be read by another thread (wait for it before writing).  TRAIL = false:
+// no closing barrier; the caller passes one before anything writes sh again.
+template <int NT, bool SH_BUSY = true, bool TRAIL = true>
 __device__ __forceinline__ void block_range(uint32_t& lo, uint32_t& hi, int* sh) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   lo = wave_umin(lo);
@@ -28,7 +29,7 @@ __device__ __forceinline__ void block_range(uint32_t& lo, uint32_t& hi, int* sh)
     lo = min(lo, (uint32_t)sh[w]);
     hi = max(hi, (uint32_t)sh[16 + w]);
   }
-  __syncthreads();
+  if constexpr (TRAIL) __syncthreads();
 }
 
 // Boundary buckets at most this large are finished by counting ranks directly.
@@ -164,7 +165,11 @@ __device__ void block_topk(Get get, int n, int k, int* hist, int* sh, Emit emit)
 // bound the counted keys, as block_range gives them).  Returns the k-th largest
 // key T and, in *kk_eq, how many of the keys equal to T are among the k largest.
 // If hist_cleared, hist[0, 2048) is already zero and visible to every thread.
-template <int NT, int PT>
+// LEAN: no barrier that only guards sh[0, NT/64) or hist against the caller's next
+// writes (the last reads of sh[0, NT/64) and of hist end before a barrier inside;
+// sh[NT/64, NT/64 + 6) may still be read on return): for a caller whose next
+// write to sh[NT/64, ...) or to small (hist + 2048) follows a barrier of its own.
+template <int NT, int PT, bool LEAN = false>
 __device__ uint32_t block_kth_reg(const uint32_t (&key)[PT], uint64_t vmask, int k, uint32_t kmin, uint32_t kmax,
                                   int* hist, int* sh, bool hist_cleared, int* kk_eq) {
   static_assert(NT % 64 == 0 && 2048 % NT == 0 && NT / 64 + 8 <= 32 && NT >= kTopkSmall, "block size");
@@ -195,8 +200,8 @@ __device__ uint32_t block_kth_reg(const uint32_t (&key)[PT], uint64_t vmask, int
     const int tb = 2047 - PER * threadIdx.x;
 #pragma unroll
     for (int j = 0; j < PER; j++) local += hist[tb - j];
-    int tot;
-    int above = block_exclusive_scan<NT>(local, sh, &tot);
+    int tot;   // (the barrier after `find` below orders the scan's reads before later writes)
+    int above = block_exclusive_scan<NT, !LEAN>(local, sh, &tot);
 #pragma unroll
     for (int j = 0; j < PER; j++) {
       const int hcount = hist[tb - j];
@@ -242,7 +247,7 @@ __device__ uint32_t block_kth_reg(const uint32_t (&key)[PT], uint64_t vmask, int
       done = true;
     }
   }
-  __syncthreads();   // sh and hist are free for the caller
+  if constexpr (!LEAN) __syncthreads();   // sh and hist are free for the caller
   *kk_eq = kk;
   return prefix + kmin;
 }
@@ -251,11 +256,11 @@ __device__ uint32_t block_kth_reg(const uint32_t (&key)[PT], uint64_t vmask, int
 // of the array, element e counting when bit e of vmask is set, so the sweeps touch
 // no memory.  emit(pos, e) receives the thread's local element index e.  If
 // hist_cleared, hist[0, 2048) is already zero and visible to every thread.
-template <int NT, int PT, class Emit>
+template <int NT, int PT, bool LEAN = false, class Emit>
 __device__ void block_topk_reg(const uint32_t (&key)[PT], uint64_t vmask, int k, uint32_t kmin, uint32_t kmax,
                                int* hist, int* sh, bool hist_cleared, Emit emit) {
   int kk;
-  const uint32_t T = block_kth_reg<NT, PT>(key, vmask, k, kmin, kmax, hist, sh, hist_cleared, &kk);
+  const uint32_t T = block_kth_reg<NT, PT, LEAN>(key, vmask, k, kmin, kmax, hist, sh, hist_cleared, &kk);
   // every key > T is taken plus the kk lowest-index keys equal to T; one block
   // scan of the (greater, equal) counts places the selections in index order
   int gt = 0, eq = 0;
@@ -266,8 +271,8 @@ __device__ void block_topk_reg(const uint32_t (&key)[PT], uint64_t vmask, int k,
       eq += key[e] == T;
     }
   }
-  int tot;
-  const int ex = block_exclusive_scan<NT>(gt | (eq << 13), sh, &tot);
+  int tot;   // (LEAN: the closing barrier below orders the scan's reads before later writes)
+  const int ex = block_exclusive_scan<NT, !LEAN>(gt | (eq << 13), sh, &tot);
   int pos = (ex & 0x1fff) + min(ex >> 13, kk);
   int eq_seen = ex >> 13;
 #pragma unroll
