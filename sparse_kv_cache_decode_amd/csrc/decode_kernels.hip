@@ -427,7 +427,10 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
       ms = !(has_prev && ((resl[ci >> 5] >> (ci & 31)) & 1u));
     }
     int tot;
-    const int ex = block_exclusive_scan<NT>(fr | (ms << 16), sh, &tot);
+    // closing barrier only where another round of the scan follows (the last
+    // round's reads of sh are ordered by the barrier after the loop)
+    const int ex = block_exclusive_scan<NT, false>(fr | (ms << 16), sh, &tot);
+    if ((j + 1) * NT < K) __syncthreads();   // block-uniform
     if (fr) freel[n_free + (ex & 0xffff)] = s;
     if (ms) missp[n_miss + (ex >> 16)] = s;
     // a slot that keeps its chunk is a hit: listed in ascending slot order, with
@@ -845,7 +848,8 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < TPT; e++) nh += (e < ntv && tk[e] >= beta);
   int n_hot;
-  int off = block_exclusive_scan<NT>(nh, sh, &n_hot);
+  // (no closing barrier: the one after the histogram clear below comes first)
+  int off = block_exclusive_scan<NT, false>(nh, sh, &n_hot);
 #pragma unroll
   for (int e = 0; e < TPT; e++)
     if (e < ntv && tk[e] >= beta) hot[off++] = t0 + e;
