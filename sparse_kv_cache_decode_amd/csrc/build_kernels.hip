@@ -402,6 +402,27 @@ hipError_t launch_round_psi(const double* psi, int b, int HD, int r, bool b8, vo
   return hipGetLastError();
 }
 
+// B^T of pair p (rows p*128 .. p*128 + 127 of bt, r each) in the rebuild's stage
+// order: element ((p*n_kq + q)*128 + n)*32 + s*8 + j is k = q*32 + (s ^ ((n >> 2) &
+// 3))*8 + j of row n, or 0 past r.  One thread per element.
+__global__ void stage_bt_kernel(const uint16_t* __restrict__ bt, int64_t n_el, int r, int n_kq,
+                                uint16_t* __restrict__ bst) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_el) return;
+  const int j = (int)(idx & 7), sl = (int)((idx >> 3) & 3), n = (int)((idx >> 5) & 127);
+  const int64_t pq = idx >> 12;   // p * n_kq + q
+  const int q = (int)(pq % n_kq);
+  const int64_t p = pq / n_kq;
+  const int k = q * 32 + ((sl ^ ((n >> 2) & 3)) * 8) + j;
+  bst[idx] = k < r ? bt[(p * 128 + n) * r + k] : (uint16_t)0;
+}
+
+hipError_t launch_stage_bt(const uint16_t* bt, int P, int r, int n_kq, uint16_t* bst, hipStream_t st) {
+  const int64_t n = (int64_t)P * n_kq * 4096;
+  stage_bt_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(bt, n, r, n_kq, bst);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Projection A[b] = K_b Psi_b (S x HD times HD x r) in float64: K's bf16 values are
 // exact in float64, Psi is the eigensolver's float64 basis, and every product is

@@ -1196,7 +1196,6 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
   double ffreq[4];
 #pragma unroll
   for (int nt = 0; nt < 4; nt++) ffreq[nt] = a.inv_freq[nt * 16 + lr];
-  const uint16_t* Bt = a.Bt + ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
   const int64_t Ab = (int64_t)b * a.a_rows * r;   // element offset of the batch element's A
   // A operand rows of this lane: row m = w*32 + mt*16 + lr (rows past the misses
   // read row 0 of the batch element; their outputs are not stored)
@@ -1280,9 +1279,11 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
       for (int u = 0; u < 2; u++) {
         const int i = w * 2 + u;                 // instruction 0..7 of the step
         const int e = i * 64 + lane;
-        const int n = e >> 2, c = (e & 3) ^ ((n >> 2) & 3);
-        const int kk = q * 32 + c * 8 < kn ? ks + q * 32 + c * 8 : ks;
-        __builtin_amdgcn_global_load_lds(Bt + (int64_t)n * r + kk,
+        // B^T pre-arranged in stage order (the pieces already swizzled, zero past
+        // r): one contiguous 1 KB per instruction; a k-step past the rank (the
+        // last slice of a split contraction) re-reads the last one, masked below
+        const int qg = min(ks / 32 + q, a.n_kq - 1);
+        __builtin_amdgcn_global_load_lds(a.Bst + ((int64_t)(p * a.n_kq + qg) * kStepPieces + e) * 8,
             (__attribute__((address_space(3))) void*)(stage + q * kStepPieces + i * 64), 16, 0, 0);
       }
 #pragma unroll

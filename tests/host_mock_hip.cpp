@@ -223,6 +223,10 @@ void check_decode(const DecodeArgs& a, bool step_io = true) {
   if (a.max_new) CHECK(inside(a.key_new, P * a.max_new * d * 2) && inside(a.val_new, P * a.max_new * d * 2));
   const size_t abytes = a.a_format == SKV_FORMAT_FP8_E5M2 ? 1 : 2;
   CHECK(inside(a.A, (size_t)a.batch * a.a_rows * a.rank * abytes));
+  if (a.b_format != SKV_FORMAT_FP8_E5M2) {   // the rebuild's stage-order copy of B^T
+    CHECK(a.n_kq * 32 >= a.rank && (a.n_kq - 1) * 32 < a.rank);
+    CHECK(inside(a.Bst, P * a.n_kq * kHeadDim * 32 * 2));
+  }
   CHECK(inside(a.inv_freq, kHeadDim / 2 * 8));
 }
 
@@ -310,6 +314,11 @@ hipError_t launch_gemm_f64_tn(const double* A, const double* B, double* C, int b
 }
 hipError_t launch_round_psi(const double* psi, int b, int HD, int r, bool b8, void* bt, hipStream_t) {
   CHECK(inside(psi, (size_t)b * HD * r * 8) && inside(bt, (size_t)b * HD * r * (b8 ? 1 : 2)));
+  return hipSuccess;
+}
+hipError_t launch_stage_bt(const uint16_t* bt, int P, int r, int n_kq, uint16_t* bst, hipStream_t) {
+  CHECK(n_kq * 32 >= r && (n_kq - 1) * 32 < r);
+  CHECK(inside(bt, (size_t)P * kHeadDim * r * 2) && inside(bst, (size_t)P * n_kq * kHeadDim * 32 * 2));
   return hipSuccess;
 }
 hipError_t launch_project(const uint16_t* k, const double* psi, int b, int64_t S, int HD, int r, int64_t a_rows,
