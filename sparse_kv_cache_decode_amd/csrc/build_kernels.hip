@@ -433,7 +433,8 @@ hipError_t launch_stage_bt(const uint16_t* bt, int P, int r, int n_kq, uint16_t*
 
 __global__ __launch_bounds__(256) void project_f64_kernel(const uint16_t* __restrict__ k_pre,
                                                           const double* __restrict__ psi, int64_t S, int HD,
-                                                          int r, int64_t a_rows, bool fp8, void* __restrict__ A) {
+                                                          int r, int C, int64_t a_rows, bool fp8,
+                                                          void* __restrict__ A) {
   __shared__ double ta[16][64 + 1];   // K tile, [k][row]
   __shared__ double tb[16][64 + 1];   // Psi tile, [k][column]
   const int b = blockIdx.z;
@@ -475,20 +476,23 @@ __global__ __launch_bounds__(256) void project_f64_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int col = n0 + tx * 4 + j;
-      if (col >= r) continue;
-      const int64_t at = ((int64_t)b * a_rows + row) * r + col;
+      const int r_pad = (r + 31) / 32 * 32;   // the grid's columns cover it: 64-column tiles
+      if (col >= r_pad) continue;
+      const int64_t at = a_tiled(b, a_rows, r_pad, C, row, col);
+      const double v = col < r ? acc[i][j] : 0.0;   // columns past r stay zero
       if (fp8)
-        static_cast<uint8_t*>(A)[at] = f64_to_e5m2_rne(acc[i][j]);
+        static_cast<uint8_t*>(A)[at] = f64_to_e5m2_rne(v);
       else
-        static_cast<uint16_t*>(A)[at] = f64_to_bf16_rne(acc[i][j]);
+        static_cast<uint16_t*>(A)[at] = f64_to_bf16_rne(v);
     }
   }
 }
 
-hipError_t launch_project(const uint16_t* k_pre, const double* psi, int b, int64_t S, int HD, int r,
+hipError_t launch_project(const uint16_t* k_pre, const double* psi, int b, int64_t S, int HD, int r, int C,
                           int64_t a_rows, bool fp8, void* A, hipStream_t st) {
+  if (a_rows % C != 0 || S % C != 0) return hipErrorInvalidValue;
   dim3 grid((r + 63) / 64, (unsigned)((S + 63) / 64), b);
-  project_f64_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, a_rows, fp8, A);
+  project_f64_kernel<<<grid, 256, 0, st>>>(k_pre, psi, S, HD, r, C, a_rows, fp8, A);
   return hipGetLastError();
 }
 

@@ -1196,16 +1196,17 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
   double ffreq[4];
 #pragma unroll
   for (int nt = 0; nt < 4; nt++) ffreq[nt] = a.inv_freq[nt * 16 + lr];
-  const int64_t Ab = (int64_t)b * a.a_rows * r;   // element offset of the batch element's A
-  // A operand rows of this lane: row m = w*32 + mt*16 + lr (rows past the misses
-  // read row 0 of the batch element; their outputs are not stored)
+  const int r_pad = a.n_kq * 32;
+  // A operand rows of this lane: row m = w*32 + mt*16 + lr, element offset of its
+  // k-step 0 in the chunk-tiled A (k-step q adds q * C * 32); rows past the
+  // misses read chunk 0 of the batch element, their outputs not stored
   int64_t arow[2];
   int64_t pos0[2];   // position of this lane's first output row of each tile
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
     const int m = w * 32 + mt * 16 + lr;
     const int ch = mchunk[m / C];
-    arow[mt] = ch >= 0 ? Ab + ((int64_t)ch * C + (m % C)) * r : Ab;   // element offsets
+    arow[mt] = a_tiled(b, a.a_rows, r_pad, C, (int64_t)max(ch, 0) * C + (m % C), 0);
     const int m0 = w * 32 + mt * 16 + lk * 4;
     pos0[mt] = (int64_t)max(mchunk[m0 / C], 0) * C + (m0 % C);
   }
@@ -1245,14 +1246,16 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
       // lanes whose k-group lies past r (r % 32 == 16) read group 0 and zero B
       const bool kin = ks + lk * 8 < r;
       const int kk = kin ? ks + lk * 8 : ks;
+      // A: this k-step's block of the chunk (columns past r are zero there)
       u32x4 av[2], bw[8];
 #pragma unroll
       for (int mt = 0; mt < 2; mt++) {
+        const int64_t at = arow[mt] + (int64_t)(ks >> 5) * (C * 32) + lk * 8;
         if constexpr (A8) {
-          const uint2 w8 = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.A) + arow[mt] + kk);
+          const uint2 w8 = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.A) + at);
           av[mt] = e5m2x8_to_bf16x8(w8.x, w8.y);
         } else {
-          av[mt] = *reinterpret_cast<const u32x4*>(a.A + arow[mt] + kk);
+          av[mt] = *reinterpret_cast<const u32x4*>(a.A + at);
         }
       }
 #pragma unroll
@@ -1288,11 +1291,14 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
       }
 #pragma unroll
       for (int mt = 0; mt < 2; mt++) {
-        const int kk = q * 32 + lk * 8 < kn ? ks + q * 32 + lk * 8 : ks;
+        // the chunk's block of k-step qg: its C rows' 32 columns contiguous (zero
+        // past r); a k-step past the rank re-reads the last one (B is masked there)
+        const int qg = min(ks / 32 + q, a.n_kq - 1);
+        const int64_t at = arow[mt] + (int64_t)qg * (C * 32) + lk * 8;
         if constexpr (A8)
-          af[q][mt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.A) + arow[mt] + kk);
+          af[q][mt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.A) + at);
         else
-          af[q][mt] = *reinterpret_cast<const u32x4*>(a.A + arow[mt] + kk);
+          af[q][mt] = *reinterpret_cast<const u32x4*>(a.A + at);
       }
       __builtin_amdgcn_sched_barrier(0);         // keep the groups in issue order
     }
@@ -1517,13 +1523,20 @@ __global__ __launch_bounds__(kAppendThreads) void append_project_kernel(DecodeAr
       double sum = 0.0;
       for (int pt = 0; pt < parts; pt++) sum += red2[pt * R2 + jj];
       const int j = (jj >> 2) * 8 + hf * 4 + (jj & 3);
-      const int64_t at = ((int64_t)b * a.a_rows + a.seq_len + t) * r + j;
+      const int64_t at = a_tiled(b, a.a_rows, a.n_kq * 32, a.chunk, a.seq_len + t, j);
       if (a.a_format == SKV_FORMAT_FP8_E5M2)
         reinterpret_cast<uint8_t*>(A)[at] = f64_to_e5m2_rne(sum);
       else
         A[at] = f64_to_bf16_rne(sum);
     }
     __syncthreads();   // red and red2 are rewritten by the next round
+  }
+  for (int j = r + tid; j < a.n_kq * 32; j += kAppendThreads) {   // the row's columns past r stay zero
+    const int64_t at = a_tiled(b, a.a_rows, a.n_kq * 32, a.chunk, a.seq_len + t, j);
+    if (a.a_format == SKV_FORMAT_FP8_E5M2)
+      reinterpret_cast<uint8_t*>(A)[at] = 0;
+    else
+      A[at] = 0;
   }
 }
 

@@ -466,7 +466,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   h->n_cand0 = h->n_cand = h->n_c - O - h->n_win;
   // low rank: every completed chunk of appended tokens adds one candidate
   h->cand_cap = h->n_cand0 + (lowrank ? c.max_new_tokens / C : 0);
-  h->a_rows = S + (lowrank ? c.max_new_tokens : 0);
+  h->a_rows = (S + (lowrank ? c.max_new_tokens : 0) + C - 1) / C * C;   // whole chunks (A is chunk-tiled)
   h->P = b * H;
   h->HD = H * kHeadDim;
   h->U = O + K + h->n_win;
@@ -502,7 +502,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   // persistent state, one allocation
   Carver cv;
   const bool a8 = c.a_format == SKV_FORMAT_FP8_E5M2;
-  const size_t oA = cv.take<uint8_t>((size_t)b * h->a_rows * r * (a8 ? 1 : 2));
+  const size_t oA = cv.take<uint8_t>((size_t)b * h->a_rows * ((r + 31) / 32 * 32) * (a8 ? 1 : 2));
   const bool b8 = c.b_format == SKV_FORMAT_FP8_E5M2;
   const size_t oBt = cv.take<uint8_t>((size_t)b * HD * r * (b8 ? 1 : 2));
   const int n_kq = (r + 31) / 32;
@@ -667,7 +667,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   HIP_TRY(hipMemcpyAsync(gpart, psi.data(), psi.size() * 8, hipMemcpyHostToDevice, s));
   HIP_TRY(launch_round_psi(gpart, b, HD, r, b8, h->Bt, s));
   if (!b8) HIP_TRY(launch_stage_bt(h->Bt, P, r, n_kq, h->Bst, s));
-  HIP_TRY(launch_project(k_pre, gpart, b, S, HD, r, h->a_rows, a8, h->A, s));
+  HIP_TRY(launch_project(k_pre, gpart, b, S, HD, r, C, h->a_rows, a8, h->A, s));
   HIP_TRY(launch_reset_cache(decode_args(h), s));
   HIP_TRY(hipStreamSynchronize(s));
   (void)hipFree(L_full);
@@ -773,14 +773,20 @@ skv_status skv_export_state(const skv_layer* hc, const skv_state_host* d) {
   const int64_t S = c.seq_len;
   const int P = h->P, HD = h->HD;
   HIP_TRY(hipStreamSynchronize(h->last_stream));
-  if (d->A && c.a_format == SKV_FORMAT_FP8_E5M2) {
-    std::vector<uint8_t> a8((size_t)b * S * r);
-    HIP_TRY(hipMemcpy2D(a8.data(), (size_t)S * r, h->A, (size_t)h->a_rows * r, (size_t)S * r, b,
-                        hipMemcpyDeviceToHost));
-    for (size_t i = 0; i < a8.size(); i++) d->A[i] = e5m2_to_bf16(a8[i]);
-  } else if (d->A)
-    HIP_TRY(hipMemcpy2D(d->A, (size_t)S * r * 2, h->A, (size_t)h->a_rows * r * 2, (size_t)S * r * 2, b,
-                        hipMemcpyDeviceToHost));
+  if (d->A) {   // rows 0..S-1 out of the chunk-tiled layout
+    const int r_pad = (r + 31) / 32 * 32;
+    const bool a8 = c.a_format == SKV_FORMAT_FP8_E5M2;
+    const size_t n = (size_t)b * h->a_rows * r_pad;
+    std::vector<uint8_t> raw(n * (a8 ? 1 : 2));
+    HIP_TRY(hipMemcpy(raw.data(), h->A, raw.size(), hipMemcpyDeviceToHost));
+    const uint16_t* r16 = reinterpret_cast<const uint16_t*>(raw.data());
+    for (int bi = 0; bi < b; bi++)
+      for (int64_t row = 0; row < S; row++)
+        for (int k = 0; k < r; k++) {
+          const int64_t at = a_tiled(bi, h->a_rows, r_pad, C, row, k);
+          d->A[((size_t)bi * S + row) * r + k] = a8 ? e5m2_to_bf16(raw[at]) : r16[at];
+        }
+  }
   if (d->B) {
     std::vector<uint16_t> bt((size_t)b * HD * r);
     if (c.b_format == SKV_FORMAT_FP8_E5M2) {   // FP8 bytes widened to bf16

@@ -18,6 +18,16 @@ constexpr int kPartStride = kHeadDim + 4; // floats per attention partial row: o
 constexpr int kStaticWaves = 16;          // waves of a static-unit attention workgroup (selection launch)
 constexpr int kRebuildRows = 128;        // key rows rebuilt per workgroup (128 / C missed chunks)
 
+// Element offset of column k of row `row` of A (batch element b) in its chunk-tiled
+// layout: every chunk of C rows is one run of n_kq = r_pad / 32 blocks of C x 32
+// elements (k-step, then row, then the step's 32 columns), columns r .. r_pad - 1
+// zero.  The rebuild's load of one k-step of a chunk's rows then reads C * 32
+// contiguous elements instead of C pieces 2r bytes apart.  a_rows is a multiple of C.
+constexpr int64_t a_tiled(int64_t b, int64_t a_rows, int r_pad, int C, int64_t row, int k) {
+  return b * a_rows * r_pad + (row / C) * ((int64_t)C * r_pad) + (int64_t)(k >> 5) * (C * 32) + (row % C) * 32 +
+         (k & 31);
+}
+
 // Everything a decode step touches, by value into the kernels.
 struct DecodeArgs {
   int batch, n_kv, group, chunk, top_k, n_outlier, n_win_units, n_cand;
@@ -29,7 +39,8 @@ struct DecodeArgs {
   int n_new_tokens, n_new_units, max_new;   // appended tokens, their units, capacity
   int n_fold;                 // appended chunks folded into the candidates (low-rank mode)
   int64_t seq_len;
-  int64_t a_rows;             // rows of A per batch element (S, plus max_new in low-rank mode)
+  int64_t a_rows;             // rows of A per batch element (S, plus max_new in low-rank mode, rounded
+                              // up to a multiple of C)
   int nb_score, cpb;          // score workgroups per pair, candidates per workgroup
   int ncp;                    // logits row stride (n_cand rounded up to 4)
   int n_split, upw;           // attention workgroups per pair, units per workgroup
@@ -47,7 +58,7 @@ struct DecodeArgs {
   const uint16_t* q;          // [b][Hq][d]
   const uint16_t* L;          // [P][cand_stride][d] bf16 (bytes for FP8), first n_cand rows in use
   const int32_t* cand_map;    // [P][cand_stride]
-  const uint16_t* A;          // [b][a_rows][r] bf16 (bytes for FP8)
+  const uint16_t* A;          // bf16 (bytes for FP8), chunk-tiled: element a_tiled(b, a_rows, 32 n_kq, C, row, k)
   const uint16_t* Bt;         // [b][HD][r] bf16 (bytes for FP8)         // [b][Hkv*d][r]
   const uint16_t* Bst;        // bf16 B only: [P][n_kq][128][32] B^T in the rebuild's LDS stage order
   int n_kq;                   // k-steps of 32 over the rank: ceil(r / 32)
@@ -154,9 +165,10 @@ hipError_t launch_round_psi(const double* psi, int b, int HD, int r, bool b8, vo
 // s ^ ((n >> 2) & 3) in slot s), zero past r, so that a stage load reads 1 KB
 // contiguous
 hipError_t launch_stage_bt(const uint16_t* bt, int P, int r, int n_kq, uint16_t* bst, hipStream_t st);
-// Rows 0..S-1 of A [b][a_rows][r] = K_b Psi_b in float64, each rounded once to
+// Rows 0..S-1 of A (chunk-tiled, a_tiled with chunk C and r_pad columns, those past
+// r zero) = K_b Psi_b in float64, each rounded once to
 // bf16, or FP8 E5M2 bytes with fp8; psi [b][HD][r] float64
-hipError_t launch_project(const uint16_t* k_pre, const double* psi, int b, int64_t S, int HD, int r,
+hipError_t launch_project(const uint16_t* k_pre, const double* psi, int b, int64_t S, int HD, int r, int C,
                           int64_t a_rows, bool fp8, void* A, hipStream_t st);
 
 // n 16-bit words at p set to `value` (debug poisoning of the slot caches)

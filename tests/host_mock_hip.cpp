@@ -222,7 +222,8 @@ void check_decode(const DecodeArgs& a, bool step_io = true) {
   if (a.host_values) CHECK(inside(a.val_slots, P * K * C * d * 2));
   if (a.max_new) CHECK(inside(a.key_new, P * a.max_new * d * 2) && inside(a.val_new, P * a.max_new * d * 2));
   const size_t abytes = a.a_format == SKV_FORMAT_FP8_E5M2 ? 1 : 2;
-  CHECK(inside(a.A, (size_t)a.batch * a.a_rows * a.rank * abytes));
+  CHECK(a.a_rows % C == 0 && a.n_kq * 32 >= a.rank);   // chunk-tiled A, whole chunks and k-steps
+  CHECK(inside(a.A, (size_t)a.batch * a.a_rows * a.n_kq * 32 * abytes));
   if (a.b_format != SKV_FORMAT_FP8_E5M2) {   // the rebuild's stage-order copy of B^T
     CHECK(a.n_kq * 32 >= a.rank && (a.n_kq - 1) * 32 < a.rank);
     CHECK(inside(a.Bst, P * a.n_kq * kHeadDim * 32 * 2));
@@ -321,11 +322,11 @@ hipError_t launch_stage_bt(const uint16_t* bt, int P, int r, int n_kq, uint16_t*
   CHECK(inside(bt, (size_t)P * kHeadDim * r * 2) && inside(bst, (size_t)P * n_kq * kHeadDim * 32 * 2));
   return hipSuccess;
 }
-hipError_t launch_project(const uint16_t* k, const double* psi, int b, int64_t S, int HD, int r, int64_t a_rows,
-                          bool a8, void* A, hipStream_t) {
-  CHECK(a_rows >= S);
+hipError_t launch_project(const uint16_t* k, const double* psi, int b, int64_t S, int HD, int r, int C,
+                          int64_t a_rows, bool a8, void* A, hipStream_t) {
+  CHECK(a_rows >= S && a_rows % C == 0 && S % C == 0);
   CHECK(inside(k, (size_t)b * S * HD * 2) && inside(psi, (size_t)b * HD * r * 8));
-  CHECK(inside(A, (size_t)b * a_rows * r * (a8 ? 1 : 2)));
+  CHECK(inside(A, (size_t)b * a_rows * ((r + 31) / 32 * 32) * (a8 ? 1 : 2)));
   return hipSuccess;
 }
 hipError_t launch_fill_u16(uint16_t* p, size_t n, uint16_t value, hipStream_t) {
