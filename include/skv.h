@@ -112,8 +112,10 @@ typedef int32_t skv_status;
                                   attended from on-chip memory by one workgroup (and
                                   stored to the key slots for later hits, with the
                                   temporal cache on), while the other workgroups of
-                                  the launch attend to the outliers, the slots that
-                                  hit and the window; values in HBM only            */
+                                  the launch attend to the slots that hit; the
+                                  outliers and the window are attended there too, or,
+                                  with the two-level selection, by extra workgroups
+                                  of the selection launch; values in HBM only       */
 #define SKV_REBUILD_SEPARATE 2 /* a rebuild launch refreshes the missed key slots, then
                                   an attention launch reads every slot               */
 #define SKV_REBUILD_OVERLAP 3  /* one launch rebuilds the missed chunks into their
