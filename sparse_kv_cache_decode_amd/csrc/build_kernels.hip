@@ -404,8 +404,9 @@ hipError_t launch_round_psi(const double* psi, int b, int HD, int r, bool b8, vo
 
 // B^T of pair p (rows p*128 .. p*128 + 127 of bt, r each) in the rebuild's stage
 // order: element ((p*n_kq + q)*128 + n)*32 + s*8 + j is k = q*32 + (s ^ ((n >> 2) &
-// 3))*8 + j of row n, or 0 past r.  One thread per element.
-__global__ void stage_bt_kernel(const uint16_t* __restrict__ bt, int64_t n_el, int r, int n_kq,
+// 3))*8 + j of row n, or 0 past r; FP8 E5M2 values (b8) widened to bf16 exactly
+// (the byte is the high byte of the equal fp16).  One thread per element.
+__global__ void stage_bt_kernel(const void* __restrict__ bt, int64_t n_el, int r, int n_kq, bool b8,
                                 uint16_t* __restrict__ bst) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= n_el) return;
@@ -414,12 +415,22 @@ __global__ void stage_bt_kernel(const uint16_t* __restrict__ bt, int64_t n_el, i
   const int q = (int)(pq % n_kq);
   const int64_t p = pq / n_kq;
   const int k = q * 32 + ((sl ^ ((n >> 2) & 3)) * 8) + j;
-  bst[idx] = k < r ? bt[(p * 128 + n) * r + k] : (uint16_t)0;
+  uint16_t v = 0;
+  if (k < r) {
+    const int64_t at = (p * 128 + n) * r + k;
+    if (b8) {
+      const float f = (float)__builtin_bit_cast(_Float16, (uint16_t)(static_cast<const uint8_t*>(bt)[at] << 8));
+      v = (uint16_t)(__float_as_uint(f) >> 16);
+    } else {
+      v = static_cast<const uint16_t*>(bt)[at];
+    }
+  }
+  bst[idx] = v;
 }
 
-hipError_t launch_stage_bt(const uint16_t* bt, int P, int r, int n_kq, uint16_t* bst, hipStream_t st) {
+hipError_t launch_stage_bt(const void* bt, int P, int r, int n_kq, bool b8, uint16_t* bst, hipStream_t st) {
   const int64_t n = (int64_t)P * n_kq * 4096;
-  stage_bt_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(bt, n, r, n_kq, bst);
+  stage_bt_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(bt, n, r, n_kq, b8, bst);
   return hipGetLastError();
 }
 

@@ -1179,17 +1179,16 @@ constexpr int rebuild_stage_bytes() {
 // With `park` (an LDS buffer of kParkFloats floats), the RoPE angles are parked
 // there across the MFMAs instead of held in 12 registers per lane (the fused
 // tail's attention state otherwise costs it its single k-step slice).
-// A8: rows of A stored as FP8 E5M2 (r bytes per row) instead of bf16.  B8: B^T
-// stored as FP8 E5M2; its operand fragments (8 bytes per lane and column tile,
-// 20 KB per pair at r = 160, read by every wave from L2) are then loaded straight
-// into registers and widened to bf16, with one k-step per iteration, instead of
-// the staged direct-to-LDS slices of the bf16 path.
+// A8: rows of A stored as FP8 E5M2 (r bytes per row) instead of bf16, widened to
+// bf16 exactly after the loads.  B^T is always read from its bf16 stage-order copy
+// (with B stored as FP8 E5M2, the build widens it into that copy exactly, so the
+// MFMA inputs are the FP8 values either way).
 constexpr int kParkFloats = 12 * 256;
 
-template <int C, int NSTEP, bool A8, bool B8, bool PARK = false>
+template <int C, int NSTEP, bool A8, bool PARK = false>
 __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const int* mchunk, u32x4* stage,
                                              float* park = nullptr) {
-  const int b = p / a.n_kv, h = p % a.n_kv;
+  const int b = p / a.n_kv;
   const int r = a.rank;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lk = lane >> 4;
@@ -1239,38 +1238,6 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
 #pragma unroll
     for (int nt = 0; nt < 8; nt++) acc[mt][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (B8) {
-    const uint8_t* Bt8 = reinterpret_cast<const uint8_t*>(a.Bt) +
-                         ((int64_t)b * a.n_kv * kHeadDim + (int64_t)h * kHeadDim) * r;
-    for (int ks = 0; ks < r; ks += 32) {
-      // lanes whose k-group lies past r (r % 32 == 16) read group 0 and zero B
-      const bool kin = ks + lk * 8 < r;
-      const int kk = kin ? ks + lk * 8 : ks;
-      // A: this k-step's block of the chunk (columns past r are zero there)
-      u32x4 av[2], bw[8];
-#pragma unroll
-      for (int mt = 0; mt < 2; mt++) {
-        const int64_t at = arow[mt] + (int64_t)(ks >> 5) * (C * 32) + lk * 8;
-        if constexpr (A8) {
-          const uint2 w8 = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(a.A) + at);
-          av[mt] = e5m2x8_to_bf16x8(w8.x, w8.y);
-        } else {
-          av[mt] = *reinterpret_cast<const u32x4*>(a.A + at);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 8; t++) {
-        const uint2 w8 = *reinterpret_cast<const uint2*>(Bt8 + (int64_t)(t * 16 + lr) * r + kk);
-        bw[t] = kin ? e5m2x8_to_bf16x8(w8.x, w8.y) : (u32x4){0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int t = 0; t < 8; t++)
-#pragma unroll
-        for (int mt = 0; mt < 2; mt++)
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[mt]),
-                                                               __builtin_bit_cast(bf16x8, bw[t]), acc[mt][t], 0, 0, 0);
-    }
-  } else {
   for (int ks = 0; ks < r; ks += NSTEP * 32) {
     const int kn = min(NSTEP * 32, r - ks);
     if (ks > 0) __syncthreads();                 // previous slice fully consumed
@@ -1303,7 +1270,6 @@ __device__ __forceinline__ void rebuild_tile(const DecodeArgs& a, int p, const i
       __builtin_amdgcn_sched_barrier(0);         // keep the groups in issue order
     }
     mfma_steps<NSTEP, 0, AFrag>(af, kn, lk, baddr, acc);
-  }
   }
   __syncthreads();
   if constexpr (PARK) {
@@ -1356,7 +1322,7 @@ __device__ __forceinline__ void store_tile(const DecodeArgs& a, int p, const int
   }
 }
 
-template <int C, int NSTEP, bool A8, bool B8>
+template <int C, int NSTEP, bool A8>
 __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
   __shared__ u32x4 stage[rebuild_stage_bytes<NSTEP>() / 16];
@@ -1378,23 +1344,19 @@ __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
-  rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage);
+  rebuild_tile<C, NSTEP, A8>(a, p, mchunk, stage);
   store_tile<C>(a, p, mslot, reinterpret_cast<const uint16_t*>(stage));
 }
 
 template <int C, bool A8>
 static hipError_t launch_rebuild_c(const DecodeArgs& a, dim3 grid, hipStream_t st) {
-  if (a.b_format == SKV_FORMAT_FP8_E5M2) {
-    rebuild_kernel<C, 1, A8, true><<<grid, 256, 0, st>>>(a);   // one k-step per iteration
-    return hipGetLastError();
-  }
   switch (min(kMaxSteps, (a.rank + 31) / 32)) {
-    case 1: rebuild_kernel<C, 1, A8, false><<<grid, 256, 0, st>>>(a); break;
-    case 2: rebuild_kernel<C, 2, A8, false><<<grid, 256, 0, st>>>(a); break;
-    case 3: rebuild_kernel<C, 3, A8, false><<<grid, 256, 0, st>>>(a); break;
-    case 4: rebuild_kernel<C, 4, A8, false><<<grid, 256, 0, st>>>(a); break;
-    case 5: rebuild_kernel<C, 5, A8, false><<<grid, 256, 0, st>>>(a); break;
-    default: rebuild_kernel<C, kMaxSteps, A8, false><<<grid, 256, 0, st>>>(a); break;
+    case 1: rebuild_kernel<C, 1, A8><<<grid, 256, 0, st>>>(a); break;
+    case 2: rebuild_kernel<C, 2, A8><<<grid, 256, 0, st>>>(a); break;
+    case 3: rebuild_kernel<C, 3, A8><<<grid, 256, 0, st>>>(a); break;
+    case 4: rebuild_kernel<C, 4, A8><<<grid, 256, 0, st>>>(a); break;
+    case 5: rebuild_kernel<C, 5, A8><<<grid, 256, 0, st>>>(a); break;
+    default: rebuild_kernel<C, kMaxSteps, A8><<<grid, 256, 0, st>>>(a); break;
   }
   return hipGetLastError();
 }
@@ -2136,7 +2098,7 @@ __device__ __forceinline__ void attend_tile(const DecodeArgs& a, int n_rows, con
   merge_waves(a.group, lane, m, l, o, mg, part);
 }
 
-template <int C, int NSTEP, bool A8, bool B8, bool ATTEND>
+template <int C, int NSTEP, bool A8, bool ATTEND>
 __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
   constexpr int kStage = rebuild_stage_bytes<NSTEP>() > (int)sizeof(AttnMerge) ? rebuild_stage_bytes<NSTEP>()
@@ -2172,7 +2134,7 @@ __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   __syncthreads();
   if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
   if constexpr (!ATTEND) {     // overlapped rebuild: the keys only, attended by the next launch
-    rebuild_tile<C, NSTEP, A8, B8>(a, p, mchunk, stage);
+    rebuild_tile<C, NSTEP, A8>(a, p, mchunk, stage);
     store_tile<C>(a, p, mslot, reinterpret_cast<const uint16_t*>(stage));
     return;
   }
@@ -2182,7 +2144,7 @@ __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   const int b = p / a.n_kv, h = p % a.n_kv;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int lr = lane & 15, lq = lane >> 4;
-  rebuild_tile<C, NSTEP, A8, B8, true>(a, p, mchunk, stage, park);
+  rebuild_tile<C, NSTEP, A8, true>(a, p, mchunk, stage, park);
   // q and this wave's values go out once the rebuild's accumulators are dead (held
   // across the rebuild they cost the third workgroup per CU), and arrive while the
   // keys are stored to their slots
@@ -2226,15 +2188,11 @@ static void launch_tail_s(const DecodeArgs& a, dim3 grid, int want, hipStream_t 
   if constexpr (NS < tail_max_steps<C, ATTEND>()) {
     if (want > NS) return launch_tail_s<C, NS + 1, A8, ATTEND>(a, grid, want, st);
   }
-  tail_kernel<C, NS, A8, false, ATTEND><<<grid, 256, 0, st>>>(a);
+  tail_kernel<C, NS, A8, ATTEND><<<grid, 256, 0, st>>>(a);
 }
 
 template <int C, bool A8, bool ATTEND>
 static hipError_t launch_tail_c(const DecodeArgs& a, dim3 grid, hipStream_t st) {
-  if (a.b_format == SKV_FORMAT_FP8_E5M2) {
-    tail_kernel<C, 1, A8, true, ATTEND><<<grid, 256, 0, st>>>(a);   // one k-step per iteration
-    return hipGetLastError();
-  }
   launch_tail_s<C, 1, A8, ATTEND>(a, grid, (a.rank + 31) / 32, st);
   return hipGetLastError();
 }

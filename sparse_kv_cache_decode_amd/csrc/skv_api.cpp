@@ -93,7 +93,7 @@ struct skv_layer {
   const uint16_t* v_dev = nullptr;   // device-visible address of the value store
   void* pool = nullptr;
   // carved from pool
-  uint16_t* Bst = nullptr;   // B^T in the rebuild's stage order (bf16 B)
+  uint16_t* Bst = nullptr;   // B^T in the rebuild's stage order (bf16; widened from FP8 B)
   uint16_t *A = nullptr, *Bt = nullptr, *L = nullptr, *k_out = nullptr, *v_out = nullptr,
            *k_win = nullptr, *v_win = nullptr, *key_slots = nullptr, *val_slots = nullptr,
            *key_new = nullptr, *val_new = nullptr;
@@ -506,7 +506,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   const bool b8 = c.b_format == SKV_FORMAT_FP8_E5M2;
   const size_t oBt = cv.take<uint8_t>((size_t)b * HD * r * (b8 ? 1 : 2));
   const int n_kq = (r + 31) / 32;
-  const size_t oBst = cv.take<uint16_t>(b8 ? 0 : (size_t)P * n_kq * kHeadDim * 32);
+  const size_t oBst = cv.take<uint16_t>((size_t)P * n_kq * kHeadDim * 32);
   const size_t oL = cv.take<uint8_t>((size_t)P * cap * lrow);
   const size_t oKo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
   const size_t oVo = cv.take<uint16_t>((size_t)P * O * C * kHeadDim);
@@ -598,7 +598,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
     char* base = static_cast<char*>(h->pool);
     h->A = (uint16_t*)(base + oA);
     h->Bt = (uint16_t*)(base + oBt);
-    h->Bst = b8 ? nullptr : (uint16_t*)(base + oBst);
+    h->Bst = (uint16_t*)(base + oBst);
     h->L = (uint16_t*)(base + oL);
     h->k_out = (uint16_t*)(base + oKo);
     h->v_out = (uint16_t*)(base + oVo);
@@ -666,7 +666,7 @@ skv_status skv_build(const skv_config* cfg, const uint16_t* k_pre, const uint16_
   // doubles; B^T is rounded from it and A = K Psi projected from it in float64
   HIP_TRY(hipMemcpyAsync(gpart, psi.data(), psi.size() * 8, hipMemcpyHostToDevice, s));
   HIP_TRY(launch_round_psi(gpart, b, HD, r, b8, h->Bt, s));
-  if (!b8) HIP_TRY(launch_stage_bt(h->Bt, P, r, n_kq, h->Bst, s));
+  HIP_TRY(launch_stage_bt(h->Bt, P, r, n_kq, b8, h->Bst, s));
   HIP_TRY(launch_project(k_pre, gpart, b, S, HD, r, C, h->a_rows, a8, h->A, s));
   HIP_TRY(launch_reset_cache(decode_args(h), s));
   HIP_TRY(hipStreamSynchronize(s));

@@ -60,7 +60,7 @@ struct DecodeArgs {
   const int32_t* cand_map;    // [P][cand_stride]
   const uint16_t* A;          // bf16 (bytes for FP8), chunk-tiled: element a_tiled(b, a_rows, 32 n_kq, C, row, k)
   const uint16_t* Bt;         // [b][HD][r] bf16 (bytes for FP8)         // [b][Hkv*d][r]
-  const uint16_t* Bst;        // bf16 B only: [P][n_kq][128][32] B^T in the rebuild's LDS stage order
+  const uint16_t* Bst;        // [P][n_kq][128][32] bf16 B^T (widened from FP8 B) in the rebuild's stage order
   int n_kq;                   // k-steps of 32 over the rank: ceil(r / 32)
   int rank;
   const uint16_t* k_out;      // [P][O*C][d]
@@ -160,11 +160,11 @@ hipError_t launch_gemm_f64_tn(const double* A, const double* B, double* C, int b
 // psi [b][HD][r] fp64 -> bt = bf16(psi), or FP8 E5M2 bytes with b8 (same layout),
 // each value rounded once to nearest even from the fp64 value
 hipError_t launch_round_psi(const double* psi, int b, int HD, int r, bool b8, void* bt, hipStream_t st);
-// bst [P][n_kq][128][32] from the bf16 bt [P*128][r]: for each k-step of 32, row n's
-// four 8-element pieces in the slots the rebuild stages them to in LDS (piece
-// s ^ ((n >> 2) & 3) in slot s), zero past r, so that a stage load reads 1 KB
-// contiguous
-hipError_t launch_stage_bt(const uint16_t* bt, int P, int r, int n_kq, uint16_t* bst, hipStream_t st);
+// bst [P][n_kq][128][32] bf16 from bt [P*128][r] (bf16, or FP8 E5M2 bytes with b8,
+// widened exactly): for each k-step of 32, row n's four 8-element pieces in the
+// slots the rebuild stages them to in LDS (piece s ^ ((n >> 2) & 3) in slot s),
+// zero past r, so that a stage load reads 1 KB contiguous
+hipError_t launch_stage_bt(const void* bt, int P, int r, int n_kq, bool b8, uint16_t* bst, hipStream_t st);
 // Rows 0..S-1 of A (chunk-tiled, a_tiled with chunk C and r_pad columns, those past
 // r zero) = K_b Psi_b in float64, each rounded once to
 // bf16, or FP8 E5M2 bytes with fp8; psi [b][HD][r] float64

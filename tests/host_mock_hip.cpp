@@ -224,10 +224,8 @@ void check_decode(const DecodeArgs& a, bool step_io = true) {
   const size_t abytes = a.a_format == SKV_FORMAT_FP8_E5M2 ? 1 : 2;
   CHECK(a.a_rows % C == 0 && a.n_kq * 32 >= a.rank);   // chunk-tiled A, whole chunks and k-steps
   CHECK(inside(a.A, (size_t)a.batch * a.a_rows * a.n_kq * 32 * abytes));
-  if (a.b_format != SKV_FORMAT_FP8_E5M2) {   // the rebuild's stage-order copy of B^T
-    CHECK(a.n_kq * 32 >= a.rank && (a.n_kq - 1) * 32 < a.rank);
-    CHECK(inside(a.Bst, P * a.n_kq * kHeadDim * 32 * 2));
-  }
+  CHECK(a.n_kq * 32 >= a.rank && (a.n_kq - 1) * 32 < a.rank);   // the rebuild's stage-order copy of B^T
+  CHECK(inside(a.Bst, P * a.n_kq * kHeadDim * 32 * 2));
   CHECK(inside(a.inv_freq, kHeadDim / 2 * 8));
 }
 
@@ -317,9 +315,9 @@ hipError_t launch_round_psi(const double* psi, int b, int HD, int r, bool b8, vo
   CHECK(inside(psi, (size_t)b * HD * r * 8) && inside(bt, (size_t)b * HD * r * (b8 ? 1 : 2)));
   return hipSuccess;
 }
-hipError_t launch_stage_bt(const uint16_t* bt, int P, int r, int n_kq, uint16_t* bst, hipStream_t) {
+hipError_t launch_stage_bt(const void* bt, int P, int r, int n_kq, bool b8, uint16_t* bst, hipStream_t) {
   CHECK(n_kq * 32 >= r && (n_kq - 1) * 32 < r);
-  CHECK(inside(bt, (size_t)P * kHeadDim * r * 2) && inside(bst, (size_t)P * n_kq * kHeadDim * 32 * 2));
+  CHECK(inside(bt, (size_t)P * kHeadDim * r * (b8 ? 1 : 2)) && inside(bst, (size_t)P * n_kq * kHeadDim * 32 * 2));
   return hipSuccess;
 }
 hipError_t launch_project(const uint16_t* k, const double* psi, int b, int64_t S, int HD, int r, int C,
