@@ -1325,6 +1325,7 @@ __device__ __forceinline__ void store_tile(const DecodeArgs& a, int p, const int
 template <int C, int NSTEP, bool A8>
 __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
+  static_assert(MPB <= 256, "one miss entry per thread");
   __shared__ u32x4 stage[rebuild_stage_bytes<NSTEP>() / 16];
   __shared__ int mchunk[MPB], mslot[MPB];
   const int P = a.batch * a.n_kv;
@@ -1337,13 +1338,22 @@ __global__ __launch_bounds__(256, 3) void rebuild_kernel(DecodeArgs a) {
   const int n_tiles = (a.top_k + MPB - 1) / MPB;
   const int p = blockIdx.x % P, j0 = (n_tiles - 1 - (int)(blockIdx.x / P)) * MPB;
   const int K = a.top_k;
-  for (int i = threadIdx.x; i < MPB; i += 256) {
-    const bool ok = j0 + i < K;
-    mchunk[i] = ok ? a.miss_chunk[(int64_t)p * K + j0 + i] : -1;
-    mslot[i] = ok ? a.miss_slot[(int64_t)p * K + j0 + i] : -1;
+  // The tile's first miss says whether it has work (the misses are a prefix of
+  // the list, which is written in full): every thread reads it beside its own
+  // entry, so an empty tile leaves before the barrier and a working one waits for
+  // no extra load.  MPB <= 32 entries, one per thread.
+  const int64_t l0 = (int64_t)p * K + j0;   // j0 < K: the tiles cover [0, K)
+  int mc = -1, ms = -1;
+  if ((int)threadIdx.x < MPB && j0 + (int)threadIdx.x < K) {
+    mc = a.miss_chunk[l0 + threadIdx.x];
+    ms = a.miss_slot[l0 + threadIdx.x];
+  }
+  if (a.miss_chunk[l0] < 0) return;   // workgroup-uniform: nothing here
+  if ((int)threadIdx.x < MPB) {
+    mchunk[threadIdx.x] = mc;
+    mslot[threadIdx.x] = ms;
   }
   __syncthreads();
-  if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
   rebuild_tile<C, NSTEP, A8>(a, p, mchunk, stage);
   store_tile<C>(a, p, mslot, reinterpret_cast<const uint16_t*>(stage));
 }
@@ -2101,6 +2111,7 @@ __device__ __forceinline__ void attend_tile(const DecodeArgs& a, int n_rows, con
 template <int C, int NSTEP, bool A8, bool ATTEND>
 __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   constexpr int MPB = kRebuildRows / C;
+  static_assert(MPB <= 256, "one miss entry per thread");
   constexpr int kStage = rebuild_stage_bytes<NSTEP>() > (int)sizeof(AttnMerge) ? rebuild_stage_bytes<NSTEP>()
                                                                                 : (int)sizeof(AttnMerge);
   __shared__ u32x4 stage[kStage / 16];
@@ -2126,13 +2137,22 @@ __global__ __launch_bounds__(256, 3) void tail_kernel(DecodeArgs a) {
   // miss tile T of pair p: misses [T*MPB, T*MPB + MPB) of the pair's list
   const int T = idx;
   const int j0 = T * MPB, K = a.top_k;
-  for (int i = threadIdx.x; i < MPB; i += 256) {
-    const bool ok = j0 + i < K;
-    mchunk[i] = ok ? a.miss_chunk[(int64_t)p * K + j0 + i] : -1;
-    mslot[i] = ok ? a.miss_slot[(int64_t)p * K + j0 + i] : -1;
+  // The tile's first miss says whether it has work (the misses are a prefix of
+  // the list, which is written in full): every thread reads it beside its own
+  // entry, so an empty tile leaves before the barrier and a working one waits for
+  // no extra load.  MPB <= 32 entries, one per thread.
+  const int64_t l0 = (int64_t)p * K + j0;   // j0 < K: the tiles cover [0, K)
+  int mc = -1, ms = -1;
+  if ((int)threadIdx.x < MPB && j0 + (int)threadIdx.x < K) {
+    mc = a.miss_chunk[l0 + threadIdx.x];
+    ms = a.miss_slot[l0 + threadIdx.x];
+  }
+  if (a.miss_chunk[l0] < 0) return;   // workgroup-uniform: nothing here
+  if ((int)threadIdx.x < MPB) {
+    mchunk[threadIdx.x] = mc;
+    mslot[threadIdx.x] = ms;
   }
   __syncthreads();
-  if (mchunk[0] < 0) return;   // misses form a prefix of the list: nothing here
   if constexpr (!ATTEND) {     // overlapped rebuild: the keys only, attended by the next launch
     rebuild_tile<C, NSTEP, A8>(a, p, mchunk, stage);
     store_tile<C>(a, p, mslot, reinterpret_cast<const uint16_t*>(stage));
