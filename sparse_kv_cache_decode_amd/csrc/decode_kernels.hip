@@ -717,9 +717,10 @@ static hipError_t allow_lds(F* kernel) {
 // maxima of each head's logits: max_g(M_g - LSE_g) is the same fp32 arithmetic
 // as each candidate's max_g(l_g - LSE_g) applied to the tile's largest logits,
 // and every later step (- 1, the order-preserving map) is monotone.
-//  1. beta = the K-th largest tile key.  K tiles each hold a candidate whose key
-//     is >= beta, so the pair's K-th largest key is >= beta: every selected
-//     candidate has key >= beta and lies in a tile whose key is >= beta ("hot").
+//  1. beta = a lower bound of the K-th largest tile key (the lower edge of its
+//     radix bucket).  At least K tiles hold a candidate whose key is >= beta,
+//     so the pair's K-th largest key is >= beta: every selected candidate has
+//     key >= beta and lies in a tile whose key is >= beta ("hot").
 //  2. The candidates of the hot tiles (4 per item, items in ascending candidate
 //     order) form the keys; those below beta are left out, which changes
 //     nothing, since every candidate left out is smaller than every selected one
@@ -838,8 +839,11 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
   if (K <= n_tiles) {   // block-uniform
     int kk;
     // lean: its last reads of sh[0, 16) and of hist precede a barrier inside; the
-    // hot-tile scan below writes only sh[0, 16), and hist after a barrier
-    beta = block_kth_reg<NT, TPT, true>(tk, prefix_mask(ntv), K, lo, hi, hist, sh, true, &kk);
+    // hot-tile scan below writes only sh[0, 16), and hist after a barrier.
+    // beta need only be a lower bound of the K-th largest tile key (a lower one
+    // adds hot tiles, never drops a selected chunk): the edge of the first digit
+    // pass's boundary bucket, without the passes that would pin it exactly
+    beta = block_kth_reg<NT, TPT, true, true>(tk, prefix_mask(ntv), K, lo, hi, hist, sh, true, &kk);
   } else {
     __syncthreads();
   }

@@ -169,7 +169,11 @@ __device__ void block_topk(Get get, int n, int k, int* hist, int* sh, Emit emit)
 // writes (the last reads of sh[0, NT/64) and of hist end before a barrier inside;
 // sh[NT/64, NT/64 + 6) may still be read on return): for a caller whose next
 // write to sh[NT/64, ...) or to small (hist + 2048) follows a barrier of its own.
-template <int NT, int PT, bool LEAN = false>
+// BOUND: stop after the first digit pass and return the lower edge of the bucket
+// that holds the k-th largest key (its key - kmin with the digits below zero): a
+// value <= the k-th largest key with at least k keys >= it (*kk_eq is then not
+// meaningful).  Exact when one digit covers the range.
+template <int NT, int PT, bool LEAN = false, bool BOUND = false>
 __device__ uint32_t block_kth_reg(const uint32_t (&key)[PT], uint64_t vmask, int k, uint32_t kmin, uint32_t kmax,
                                   int* hist, int* sh, bool hist_cleared, int* kk_eq) {
   static_assert(NT % 64 == 0 && 2048 % NT == 0 && NT / 64 + 8 <= 32 && NT >= kTopkSmall, "block size");
@@ -219,6 +223,10 @@ __device__ uint32_t block_kth_reg(const uint32_t (&key)[PT], uint64_t vmask, int
     const int bcount = sh[NT / 64 + 2];
     prefix |= dv << shift;
     mask |= dmask << shift;
+    if constexpr (BOUND) {
+      done = true;   // (loop exit; the lower digits of prefix stay zero)
+      continue;
+    }
     if (shift > 0 && bcount <= kTopkSmall) {
       // few keys share the boundary bucket: gather them and find the kk-th
       // largest of them by counting, instead of more histogram passes
