@@ -393,7 +393,7 @@ __device__ __forceinline__ void pair_lse(const DecodeArgs& a, int p, float* lse)
 // reassignment, miss list, list of the slots that hit, counters.
 template <int NT = kSelThreads>
 __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* selch, int* freel, int* missp,
-                           int* scl, uint32_t* resl) {
+                           int* scl, uint32_t* resl, const uint32_t* selbits = nullptr) {
   const int K = a.top_k, RW = a.res_words;
   int32_t* sc = a.slot_cand + (int64_t)p * K;
   int32_t* sch = a.slot_chunk + (int64_t)p * K;
@@ -422,7 +422,11 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
     int fr = 0, ms = 0;
     if (s < K) {
       const int old = scl[s];
-      fr = !(has_prev && old >= 0 && sorted_find(sel, K, old) >= 0);
+      // is the slot's chunk still selected: the selection's bitmap when the
+      // caller built one (one LDS read), else a binary search of sel
+      const bool kept = has_prev && old >= 0 &&
+                        (selbits ? ((selbits[old >> 5] >> (old & 31)) & 1u) != 0u : sorted_find(sel, K, old) >= 0);
+      fr = !kept;
       const int ci = sel[s];
       ms = !(has_prev && ((resl[ci >> 5] >> (ci & 31)) & 1u));
     }
@@ -734,7 +738,9 @@ static hipError_t allow_lds(F* kernel) {
 // register budget (IPT items of 4 candidates per thread; only with many equal
 // tile keys), the second level runs over them from memory instead.
 // LDS layout (ints): hist[2048 + kTopkSmall] | sh[32] | sel[K] | selch[K] |
-// freel[K] | missp[K] | scl[K] | resl[res_words] | hot tile list[n_ctiles].
+// freel[K] | missp[K] | scl[K] | resl[res_words] | hot tile list[n_ctiles] |
+// selbits[res_words] (the selection as a bitmap over candidate indices, for the
+// index scan's "is the slot's chunk still selected").
 
 // key of candidate c (< n_cand) of pair p from its G logits
 template <int G>
@@ -775,6 +781,7 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
   int* scl = missp + K;      // slot -> candidate index (copy of the pair's slot map)
   uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);   // resident bitmap copy
   int* hot = reinterpret_cast<int*>(resl + RW);            // hot tiles, ascending
+  uint32_t* selbits = reinterpret_cast<uint32_t*>(hot + a.n_ctiles_cap);   // the selection as a bitmap
   __shared__ float lse[16];
   const int p = blockIdx.x;
   // ---- level 1: tile keys of tiles [t*TPT, t*TPT + TPT); their maxima are
@@ -858,6 +865,7 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
   for (int e = 0; e < TPT; e++)
     if (e < ntv && tk[e] >= beta) hot[off++] = t0 + e;
   for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0;
+  for (int i = threadIdx.x; i < RW; i += NT) selbits[i] = 0u;
   __syncthreads();
   // ---- level 2: the candidates of the hot tiles, items of 4 candidates
   const int n_items = n_hot * 4;
@@ -903,8 +911,11 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
     // not look up the selected ones) made the launch slower, 18.9 against 16.8 us.
     // lean: it ends with the barrier that publishes sel, before the index scan
     // writes sh again
-    block_topk_reg<NT, IPT * 4, true>(key, vmask, K, beta, hi1, hist, sh, true,
-                                      [&](int pos, int e) { sel[pos] = cbs[e / 4] + (e & 3); });
+    block_topk_reg<NT, IPT * 4, true>(key, vmask, K, beta, hi1, hist, sh, true, [&](int pos, int e) {
+      const int c = cbs[e / 4] + (e & 3);
+      sel[pos] = c;
+      atomicOr(&selbits[c >> 5], 1u << (c & 31));
+    });
   } else {
     // many equal tile keys: the hot tiles' candidates from memory (candidates
     // past n_cand get key 0, below every real key, and are never taken)
@@ -914,13 +925,17 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
           const int c = hot[i >> 4] * 16 + (i & 15);
           return c < n ? cand_key<G>(a, p, c, lse) : 0u;
         },
-        m, K, hist, sh, [&](int pos, int i) { sel[pos] = hot[i >> 4] * 16 + (i & 15); });
+        m, K, hist, sh, [&](int pos, int i) {
+          const int c = hot[i >> 4] * 16 + (i & 15);
+          sel[pos] = c;
+          atomicOr(&selbits[c >> 5], 1u << (c & 31));
+        });
   }
-  index_scan<NT>(a, p, sh, sel, selch, freel, missp, scl, resl);
+  index_scan<NT>(a, p, sh, sel, selch, freel, missp, scl, resl, selbits);
 }
 
 static size_t select2_lds_bytes(const DecodeArgs& a) {
-  return (size_t)(kHist + 32 + 5 * a.top_k + a.res_words + a.n_ctiles_cap) * sizeof(int);
+  return (size_t)(kHist + 32 + 5 * a.top_k + 2 * a.res_words + a.n_ctiles_cap) * sizeof(int);
 }
 
 // LDS of a static attention workgroup: every wave's o[G][d], m[G] and l[G]
@@ -940,7 +955,7 @@ constexpr int kSelect2MaxTopK = 512;
 
 int select2_shape(int n_ctiles_cap, int top_k, int res_words, int* nt, int* tpt, int* ipt) {
   if (top_k > kSelect2MaxTopK) return 0;
-  if ((size_t)(kHist + 32 + 5 * top_k + res_words + n_ctiles_cap) * sizeof(int) > (size_t)kSelLdsMax) return 0;
+  if ((size_t)(kHist + 32 + 5 * top_k + 2 * res_words + n_ctiles_cap) * sizeof(int) > (size_t)kSelLdsMax) return 0;
   const int threads = kSelThreads;
   const int t = (n_ctiles_cap + threads - 1) / threads;
   // hot tiles are about K (more only on equal tile keys): room for 1.25 K, 4
