@@ -809,14 +809,20 @@ __global__ __launch_bounds__(NT) void select2_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < TPT; e++) load_tile(e, mg[e]);
   }
-  {
-    const int32_t* sc = a.slot_cand + (int64_t)p * K;
-    const uint32_t* res = a.resident + (int64_t)p * RW;
-    for (int i = threadIdx.x; i < K; i += NT) scl[i] = sc[i];
-    for (int i = threadIdx.x; i < RW; i += NT) resl[i] = res[i];
-  }
+  // the slot map and the resident bitmap (read by the index scan) are loaded
+  // now and written to LDS after the LSE, so their latency overlaps the LSE
+  // partials' (the first NT entries through registers)
+  const int32_t* sc = a.slot_cand + (int64_t)p * K;
+  const uint32_t* res = a.resident + (int64_t)p * RW;
+  const int i0 = threadIdx.x;
+  const int sc0 = i0 < K ? sc[i0] : 0;
+  const uint32_t rs0 = i0 < RW ? res[i0] : 0u;
   for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0;
   pair_lse<G, NT>(a, p, lse);
+  if (i0 < K) scl[i0] = sc0;
+  if (i0 < RW) resl[i0] = rs0;
+  for (int i = i0 + NT; i < K; i += NT) scl[i] = sc[i];
+  for (int i = i0 + NT; i < RW; i += NT) resl[i] = res[i];
   __syncthreads();
   uint32_t tk[TPT];
   uint32_t lo = 0xffffffffu, hi = 0u;
