@@ -496,6 +496,38 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
 // the top of the distribution.  On the score itself a pair with one dominant
 // chunk (score 0) stretched the range over every tiny negative value, and its
 // selection took three digit passes instead of one (11.5 against 6.3 us).
+// The pair's slot map (K entries) and resident bitmap (RW words), read by the
+// index scan, copied to LDS in two halves: issue() loads this thread's first
+// kSlotRegs entries of each into registers, so that their latency overlaps
+// whatever the caller loads next; finish() writes them (and loads and writes any
+// further entries) to LDS; a later barrier publishes them.
+constexpr int kSlotRegs = 4;   // K <= kMaxTopK = 4 * kSelThreads
+struct SlotStage {
+  int sc[kSlotRegs];
+  uint32_t rs[kSlotRegs];
+  __device__ __forceinline__ void issue(const DecodeArgs& a, int p) {
+    const int K = a.top_k, RW = a.res_words;
+#pragma unroll
+    for (int j = 0; j < kSlotRegs; j++) {
+      const int i = threadIdx.x + j * kSelThreads;
+      sc[j] = i < K ? a.slot_cand[(int64_t)p * K + i] : 0;
+      rs[j] = i < RW ? a.resident[(int64_t)p * RW + i] : 0u;
+    }
+  }
+  __device__ __forceinline__ void finish(const DecodeArgs& a, int p, int* scl, uint32_t* resl) const {
+    const int K = a.top_k, RW = a.res_words;
+#pragma unroll
+    for (int j = 0; j < kSlotRegs; j++) {
+      const int i = threadIdx.x + j * kSelThreads;
+      if (i < K) scl[i] = sc[j];
+      if (i < RW) resl[i] = rs[j];
+    }
+    for (int i = threadIdx.x + kSlotRegs * kSelThreads; i < RW; i += kSelThreads)
+      resl[i] = a.resident[(int64_t)p * RW + i];
+  }
+};
+static_assert(kMaxTopK <= kSlotRegs * kSelThreads, "slot map entries per thread");
+
 template <int G, int PT, class Stage>
 __device__ __forceinline__ int reg_keys(const DecodeArgs& a, int p, int c0, int n, float* lse, int* hist,
                                         uint32_t (&key)[PT], uint32_t& lo, uint32_t& hi, Stage stage) {
@@ -567,13 +599,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(DecodeArgs a) {
   uint32_t* resl = reinterpret_cast<uint32_t*>(scl + K);   // resident bitmap copy
   __shared__ float lse[16];
   const int p = blockIdx.x;
-  const int32_t* sc = a.slot_cand + (int64_t)p * K;
-  const uint32_t* res = a.resident + (int64_t)p * RW;
   uint32_t key[PT], lo, hi;
-  const int nv = reg_keys<G, PT>(a, p, 0, a.n_cand, lse, hist, key, lo, hi, [&] {
-    for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
-    for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
-  });
+  int nv;
+  if constexpr (G * PT <= 64) {
+    SlotStage ss;   // loads issued beside the logits', stored to LDS after the LSE
+    nv = reg_keys<G, PT>(a, p, 0, a.n_cand, lse, hist, key, lo, hi, [&] { ss.issue(a, p); });
+    ss.finish(a, p, scl, resl);   // published by the barriers below
+  } else {          // the logits fill the registers: load and store in place
+    nv = reg_keys<G, PT>(a, p, 0, a.n_cand, lse, hist, key, lo, hi, [&] {
+      for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = a.slot_cand[(int64_t)p * K + i];
+      for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = a.resident[(int64_t)p * RW + i];
+    });
+  }
   block_range<kSelThreads>(lo, hi, sh);
   const int i0 = threadIdx.x * PT;
   block_topk_reg<kSelThreads, PT>(key, prefix_mask(nv), K, lo, hi, hist, sh, true,
@@ -698,11 +735,10 @@ __global__ __launch_bounds__(kSelThreads) void merged_select_kernel(DecodeArgs a
   const int p = blockIdx.x;
   uint32_t key[PT], lo, hi;
   int idx[PT];
+  SlotStage ss;   // loads issued before the lists', stored to LDS after them
+  ss.issue(a, p);
   const int nv = load_entries<PT>(ls, K, p, 0, ls.m, key, idx, lo, hi);
-  const int32_t* sc = a.slot_cand + (int64_t)p * K;
-  const uint32_t* res = a.resident + (int64_t)p * RW;
-  for (int i = threadIdx.x; i < K; i += kSelThreads) scl[i] = sc[i];
-  for (int i = threadIdx.x; i < RW; i += kSelThreads) resl[i] = res[i];
+  ss.finish(a, p, scl, resl);
   for (int i = threadIdx.x; i < 2048; i += kSelThreads) hist[i] = 0;
   block_range<kSelThreads>(lo, hi, sh);   // its barriers also publish the cleared histogram
   block_topk_reg<kSelThreads, PT>(key, prefix_mask(nv), K, lo, hi, hist, sh, true, [&](int pos, int e) { sel[pos] = idx[e]; });
