@@ -405,6 +405,17 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
   constexpr int kPer = 4;
   static_assert(kMaxTopK <= kPer * NT, "selection entries per thread");
   int my_sel[kPer], my_slot[kPer];
+  // the running hit / miss totals, read now and written at the end, so the end
+  // waits for no load
+  long long hits_run = 0, miss_run = 0;
+  if (threadIdx.x == 0) {
+    hits_run = a.hits_total[p];
+    miss_run = a.miss_total[p];
+  }
+  // after the step the slots hold exactly the selection: with its bitmap at hand
+  // the resident bitmap is written now, off the end of the launch
+  if (selbits)
+    for (int i = threadIdx.x; i < RW; i += NT) res[i] = selbits[i];
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     const int i = threadIdx.x + j * NT;
@@ -464,23 +475,27 @@ __device__ void index_scan(const DecodeArgs& a, int p, int* sh, int* sel, int* s
       slot = freel[j];
       const int ci = sel[missp[j]];
       ch = selch[missp[j]];
-      const int old = scl[slot];
-      if (old >= 0) atomicAnd(&resl[old >> 5], ~(1u << (old & 31)));
-      atomicOr(&resl[ci >> 5], 1u << (ci & 31));
+      if (!selbits) {   // the resident bitmap follows the slots' changes
+        const int old = scl[slot];
+        if (old >= 0) atomicAnd(&resl[old >> 5], ~(1u << (old & 31)));
+        atomicOr(&resl[ci >> 5], 1u << (ci & 31));
+      }
       sc[slot] = ci;
       sch[slot] = ch;
     }
     a.miss_slot[(int64_t)p * K + j] = slot;
     a.miss_chunk[(int64_t)p * K + j] = ch;
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < RW; i += NT) res[i] = resl[i];
+  if (!selbits) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < RW; i += NT) res[i] = resl[i];
+  }
   if (threadIdx.x == 0) {
     a.n_miss[p] = n_miss;
     a.hits_last[p] = has_prev ? K - n_miss : 0;
     if (has_prev) {
-      a.hits_total[p] += K - n_miss;
-      a.miss_total[p] += n_miss;
+      a.hits_total[p] = hits_run + (K - n_miss);
+      a.miss_total[p] = miss_run + n_miss;
     }
   }
 }
